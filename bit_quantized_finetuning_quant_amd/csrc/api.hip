@@ -1,0 +1,225 @@
+// C ABI of the QLoRA linear layer library (declared in include/qlora.h):
+// argument validation, workspace plans and kernel launches.  Host code only.
+
+#include <math.h>
+#include <string.h>
+
+#include <algorithm>
+#include <cmath>
+
+#include "../../include/qlora.h"
+#include "common.hpp"
+#include "launch.hpp"
+
+using namespace qlora;
+
+namespace {
+
+// ---- NF4 levels, computed on the host from the definition ------------------
+// Standard-normal quantiles at equal probability steps on each side of 1/2:
+// 8 positive levels up to probability delta and 7 negative levels down to
+// 1 - delta, plus an exact zero, all divided by the largest quantile so that
+// the range is [-1, 1]; delta = 1 - (1/32 + 1/30)/2 is the mean of the
+// half-bin offsets of a 16-level and a 15-level equal-probability grid.
+double normal_cdf(double z) { return 0.5 * std::erfc(-z / std::sqrt(2.0)); }
+double normal_pdf(double z) { return std::exp(-0.5 * z * z) / std::sqrt(2.0 * M_PI); }
+
+// Phi^-1(p) for p in (1/2, 1): bisection to full double resolution, then two
+// Newton steps on the upper-tail form 1 - Phi(z) = erfc(z/sqrt2)/2.
+double normal_quantile_upper(double p) {
+  double lo = 0.0, hi = 40.0;
+  for (int i = 0; i < 200 && hi - lo > 0; ++i) {
+    const double mid = 0.5 * (lo + hi);
+    if (mid == lo || mid == hi) break;
+    if (normal_cdf(mid) < p) lo = mid; else hi = mid;
+  }
+  double z = 0.5 * (lo + hi);
+  const double q = 1.0 - p;  // exact for the probabilities used here
+  for (int i = 0; i < 2; ++i) z += (0.5 * std::erfc(z / std::sqrt(2.0)) - q) / normal_pdf(z);
+  return z;
+}
+
+struct Tables {
+  Codebook cb;
+  Midpoints mid;
+  Tables() {
+    const double delta = 1.0 - 0.5 * (1.0 / 32.0 + 1.0 / 30.0);
+    const double top = normal_quantile_upper(delta);
+    double lv[16];
+    for (int j = 1; j <= 7; ++j) lv[7 - j] = -normal_quantile_upper(0.5 + j * (delta - 0.5) / 7.0) / top;
+    lv[7] = 0.0;
+    for (int j = 1; j <= 8; ++j) lv[7 + j] = normal_quantile_upper(0.5 + j * (delta - 0.5) / 8.0) / top;
+    lv[0] = -1.0;
+    lv[15] = 1.0;
+    for (int k = 0; k < 16; ++k) cb.v[k] = (float)lv[k];
+    for (int j = 0; j < 15; ++j) mid.m[j] = ((double)cb.v[j] + (double)cb.v[j + 1]) * 0.5;  // exact
+  }
+};
+
+const Tables &tables() {
+  static const Tables t;
+  return t;
+}
+
+constexpr int64_t kMaxNumel = (int64_t)1 << 37;
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+bool shape_ok(int64_t n_out, int64_t n_in) {
+  return n_out > 0 && n_in > 0 && n_out <= kMaxNumel && n_in <= kMaxNumel && n_out * n_in <= kMaxNumel;
+}
+
+qlora_status check_weight(const qlora_nf4_weight *q) {
+  if (!q) return QLORA_ERR_NULL;
+  if (!shape_ok(q->n_out, q->n_in)) return QLORA_ERR_SHAPE;
+  if (!q->codes || !q->absmax_fp8 || !q->absmax_scale || !q->absmax_mean) return QLORA_ERR_NULL;
+  if (!aligned16(q->codes) || !aligned16(q->absmax_fp8) || !aligned16(q->absmax_scale) ||
+      !aligned16(q->absmax_mean))
+    return QLORA_ERR_ALIGN;
+  return QLORA_OK;
+}
+
+QWeight qweight(const qlora_nf4_weight *q) {
+  return QWeight{q->codes, q->absmax_fp8, q->absmax_scale, q->absmax_mean, q->n_out, q->n_in};
+}
+
+qlora_status check_linear(int64_t T, const qlora_nf4_weight *q, int r, float scale) {
+  qlora_status s = check_weight(q);
+  if (s != QLORA_OK) return s;
+  if (T < 1 || T > kMaxNumel || q->n_in % kBlock != 0 || r < 1 || r > 256) return QLORA_ERR_SHAPE;
+  if (T * q->n_in > kMaxNumel || T * q->n_out > kMaxNumel) return QLORA_ERR_SHAPE;
+  if (!std::isfinite(scale)) return QLORA_ERR_VALUE;
+  return QLORA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+qlora_status qlora_nf4_sizes(int64_t n_out, int64_t n_in, int64_t *codes_bytes, int64_t *nblocks,
+                             int64_t *ngroups) {
+  if (!shape_ok(n_out, n_in)) return QLORA_ERR_SHAPE;
+  const int64_t numel = n_out * n_in;
+  const int64_t nb = (numel + kBlock - 1) / kBlock;
+  if (codes_bytes) *codes_bytes = (numel + 1) / 2;
+  if (nblocks) *nblocks = nb;
+  if (ngroups) *ngroups = (nb + kGroup - 1) / kGroup;
+  return QLORA_OK;
+}
+
+size_t qlora_nf4_bytes(int64_t n_out, int64_t n_in) {
+  int64_t cb, nb, ng;
+  if (qlora_nf4_sizes(n_out, n_in, &cb, &nb, &ng) != QLORA_OK) return 0;
+  return (size_t)(cb + nb + 4 * ng + 4);
+}
+
+size_t qlora_quantize_workspace_bytes(int64_t n_out, int64_t n_in) {
+  int64_t nb;
+  if (qlora_nf4_sizes(n_out, n_in, nullptr, &nb, nullptr) != QLORA_OK) return 0;
+  // status (256 B) + 256 u64 exponent bins (2 KiB) + fp32 block absmax
+  return 256 + 2048 + (size_t)nb * 4;
+}
+
+size_t qlora_linear_workspace_bytes(int64_t T, int64_t n_out, int64_t n_in, int r) {
+  if (T < 1 || !shape_ok(n_out, n_in) || n_in % kBlock != 0 || r < 1 || r > 256) return 0;
+  return plan_linear(T, n_out, n_in, r).total;
+}
+
+void qlora_nf4_codebook(float out[16]) {
+  if (!out) return;
+  memcpy(out, tables().cb.v, sizeof(float) * 16);
+}
+
+const char *qlora_status_string(qlora_status s) {
+  switch (s) {
+    case QLORA_OK: return "ok";
+    case QLORA_ERR_NULL: return "a required pointer is NULL";
+    case QLORA_ERR_SHAPE: return "a dimension is out of range";
+    case QLORA_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case QLORA_ERR_WORKSPACE: return "workspace too small";
+    case QLORA_ERR_DTYPE: return "unknown dtype";
+    case QLORA_ERR_HIP: return "HIP runtime error at launch";
+    case QLORA_ERR_NONFINITE: return "NaN or Inf in the quantized weight";
+    case QLORA_ERR_VALUE: return "a scalar argument is not finite";
+  }
+  return "unknown status";
+}
+
+const char *qlora_version(void) { return "qlora-gfx950 0.1"; }
+
+qlora_status qlora_quantize(const void *w, qlora_dtype w_dtype, const qlora_nf4_weight *q, void *ws,
+                            size_t ws_bytes, void *stream) {
+  qlora_status s = check_weight(q);
+  if (s != QLORA_OK) return s;
+  if (!w || !ws) return QLORA_ERR_NULL;
+  if (!aligned16(w) || !aligned16(ws)) return QLORA_ERR_ALIGN;
+  if (w_dtype != QLORA_F32 && w_dtype != QLORA_BF16) return QLORA_ERR_DTYPE;
+  if (ws_bytes < qlora_quantize_workspace_bytes(q->n_out, q->n_in)) return QLORA_ERR_WORKSPACE;
+  char *base = (char *)ws;
+  hipError_t e = launch_quantize(w, w_dtype == QLORA_BF16, q->n_out * q->n_in, q->codes, q->absmax_fp8,
+                                 q->absmax_scale, q->absmax_mean, (uint32_t *)base,
+                                 (unsigned long long *)(base + 256), (float *)(base + 256 + 2048),
+                                 tables().mid, (hipStream_t)stream);
+  return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP;
+}
+
+qlora_status qlora_dequantize(const qlora_nf4_weight *q, uint16_t *w_bf16, void *stream) {
+  qlora_status s = check_weight(q);
+  if (s != QLORA_OK) return s;
+  if (!w_bf16) return QLORA_ERR_NULL;
+  if (!aligned16(w_bf16)) return QLORA_ERR_ALIGN;
+  hipError_t e = launch_dequantize(q->codes, q->absmax_fp8, q->absmax_scale, q->absmax_mean,
+                                   q->n_out * q->n_in, w_bf16, tables().cb, (hipStream_t)stream);
+  return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP;
+}
+
+qlora_status qlora_linear_fwd(const uint16_t *x, int64_t T, const qlora_nf4_weight *q, const uint16_t *A,
+                              const uint16_t *B, int r, float scale, uint16_t *y, uint16_t *u_out, void *ws,
+                              size_t ws_bytes, void *stream) {
+  qlora_status s = check_linear(T, q, r, scale);
+  if (s != QLORA_OK) return s;
+  if (!x || !A || !B || !y || !ws) return QLORA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(A) || !aligned16(B) || !aligned16(y) || !aligned16(ws) ||
+      (u_out && !aligned16(u_out)))
+    return QLORA_ERR_ALIGN;
+  const LinearPlan p = plan_linear(T, q->n_out, q->n_in, r);
+  if (ws_bytes < p.total) return QLORA_ERR_WORKSPACE;
+  hipError_t e = launch_linear_fwd(p, x, qweight(q), A, B, scale, y, u_out, (char *)ws, tables().cb,
+                                   (hipStream_t)stream);
+  return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP;
+}
+
+qlora_status qlora_linear_bwd(const uint16_t *dy, const uint16_t *x, int64_t T, const qlora_nf4_weight *q,
+                              const uint16_t *A, const uint16_t *B, int r, float scale, const uint16_t *u,
+                              uint16_t *grad_x, float *grad_A, float *grad_B, void *ws, size_t ws_bytes,
+                              void *stream) {
+  qlora_status s = check_linear(T, q, r, scale);
+  if (s != QLORA_OK) return s;
+  if (!dy || !x || !A || !B || !grad_A || !grad_B || !ws) return QLORA_ERR_NULL;
+  if (!aligned16(dy) || !aligned16(x) || !aligned16(A) || !aligned16(B) || !aligned16(grad_A) ||
+      !aligned16(grad_B) || !aligned16(ws) || (u && !aligned16(u)) || (grad_x && !aligned16(grad_x)))
+    return QLORA_ERR_ALIGN;
+  const LinearPlan p = plan_linear(T, q->n_out, q->n_in, r);
+  if (ws_bytes < p.total) return QLORA_ERR_WORKSPACE;
+  hipError_t e = launch_linear_bwd(p, dy, x, qweight(q), A, B, scale, u, grad_x, grad_A, grad_B, (char *)ws,
+                                   tables().cb, (hipStream_t)stream);
+  return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP;
+}
+
+void qlora_gemm_timing_enable(int enable) { gemm_timing_enable(enable != 0); }
+
+qlora_status qlora_gemm_timing_read(int64_t *fwd_launches, double *fwd_ms, int64_t *dx_launches,
+                                    double *dx_ms) {
+  return gemm_timing_read(fwd_launches, fwd_ms, dx_launches, dx_ms) ? QLORA_OK : QLORA_ERR_HIP;
+}
+
+qlora_status qlora_status_read(const void *ws, void *stream) {
+  if (!ws) return QLORA_ERR_NULL;
+  if (!aligned16(ws)) return QLORA_ERR_ALIGN;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return QLORA_ERR_HIP;
+  uint32_t word = 0;
+  if (hipMemcpy(&word, ws, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess) return QLORA_ERR_HIP;
+  return (word & 1u) ? QLORA_ERR_NONFINITE : QLORA_OK;
+}
+
+}  // extern "C"

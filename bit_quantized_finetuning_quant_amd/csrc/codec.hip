@@ -1,0 +1,293 @@
+// NF4 + FP8 double-quantization codec kernels for gfx950.
+//
+// Method: the "qlora" encyclopedia entry (tonho.wtf), section "como funciona":
+// 4-bit levels from standard-normal quantiles with an exact zero, one absmax
+// constant per 64-element block, constants quantized to FP8 in blocks of 256.
+//
+// Kernels
+//   zero_words        clears the status word and the exponent bins
+//   quantize_blocks   absmax, nearest code by exact thresholds, nibble packing,
+//                     exact exponent-binned partial sums of the absmax values
+//   mean_from_bins    one thread: exact sum -> fp32 mean (round to nearest even)
+//   double_quantize   one workgroup per 256-block group: fp32 scale, e4m3 codes
+//   dequantize_bf16   streaming decode to bf16 (HBM bound)
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace qlora {
+
+__global__ void zero_words(uint32_t *p, int n) {
+  int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+// Largest fp32 strictly below f (f finite).
+__device__ __forceinline__ float next_down(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) == 0u) return __uint_as_float(0x80000001u);
+  return __uint_as_float((u & 0x80000000u) ? u + 1u : u - 1u);
+}
+
+// 8 lanes own one 64-element block (8 elements each); a 256-thread workgroup
+// covers 32 blocks per pass and strides over the tensor.
+template <bool kBf16Src>
+__global__ __launch_bounds__(256) void quantize_blocks(const void *__restrict__ src, int64_t numel,
+                                                       int64_t nblocks, uint8_t *__restrict__ codes,
+                                                       int64_t codes_bytes, float *__restrict__ c1_out,
+                                                       unsigned long long *__restrict__ bins,
+                                                       uint32_t *__restrict__ status, Midpoints mid) {
+  __shared__ unsigned long long sbins[256];
+  sbins[threadIdx.x] = 0ull;
+  __syncthreads();
+  const int sub = threadIdx.x & 7;
+  bool bad = false;
+  for (int64_t b = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3); b < nblocks; b += (int64_t)gridDim.x * 32) {
+    const int64_t e0 = b * kBlock + sub * 8;
+    float x[8];
+    if (e0 + 8 <= numel) {
+      if (kBf16Src) {
+        u32x4 v = *(const u32x4 *)((const uint16_t *)src + e0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[2 * i] = bf16_lo(v[i]);
+          x[2 * i + 1] = bf16_hi(v[i]);
+        }
+      } else {
+        f32x4 v0 = *(const f32x4 *)((const float *)src + e0);
+        f32x4 v1 = *(const f32x4 *)((const float *)src + e0 + 4);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[i] = v0[i];
+          x[4 + i] = v1[i];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float v = 0.f;
+        if (e0 + i < numel) {
+          v = kBf16Src ? __uint_as_float((uint32_t)((const uint16_t *)src)[e0 + i] << 16)
+                       : ((const float *)src)[e0 + i];
+        }
+        x[i] = v;
+      }
+    }
+    // block absmax: max of |x| bit patterns (monotone for non-negative floats)
+    uint32_t am = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) am = max(am, __float_as_uint(x[i]) & 0x7FFFFFFFu);
+    am = max(am, (uint32_t)__shfl_xor((int)am, 1, 8));
+    am = max(am, (uint32_t)__shfl_xor((int)am, 2, 8));
+    am = max(am, (uint32_t)__shfl_xor((int)am, 4, 8));
+    if (am >= 0x7F800000u) bad = true;
+    const float c1 = __uint_as_float(am);
+    // thresholds: x is above midpoint j exactly when x > tau_j (fp32 compare)
+    const double cd = (double)c1;
+    float tau[15];
+#pragma unroll
+    for (int j = 0; j < 15; ++j) {
+      const double t = mid.m[j] * cd;  // exact in fp64
+      float f = (float)t;
+      const double fd = (double)f;
+      // round down; an exact tie on the negative side counts as "above" (toward zero)
+      if (fd > t || (fd == t && j < 7)) f = next_down(f);
+      tau[j] = f;
+    }
+    uint32_t packed = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t c = 0u;
+#pragma unroll
+      for (int j = 0; j < 15; ++j) c += (x[i] > tau[j]) ? 1u : 0u;
+      packed |= c << (4 * i);
+    }
+    const int64_t byte0 = e0 >> 1;
+    if (byte0 + 4 <= codes_bytes) {
+      *(uint32_t *)(codes + byte0) = packed;
+    } else {
+      for (int i = 0; i < 4; ++i)
+        if (byte0 + i < codes_bytes) codes[byte0 + i] = (uint8_t)(packed >> (8 * i));
+    }
+    if (sub == 0) {
+      c1_out[b] = c1;
+      const uint32_t ex = am >> 23;
+      if (ex < 255u) {
+        const uint32_t frac = am & 0x7FFFFFu;
+        const unsigned long long mant = ex ? (frac | 0x800000u) : frac;
+        if (mant) atomicAdd(&sbins[ex ? ex : 1u], mant);
+      }
+    }
+  }
+  if (bad) atomicOr(status, 1u);
+  __syncthreads();
+  const unsigned long long s = sbins[threadIdx.x];
+  if (s) atomicAdd(&bins[threadIdx.x], s);
+}
+
+// Exact mean of the block constants.  bins[e] holds the sum of the 24-bit
+// significands of all constants with biased exponent e (subnormals in bin 1),
+// so the exact sum is Z * 2^-149 with Z = sum_e bins[e] << (e - 1).  The mean
+// Z * 2^-149 / n is rounded to the nearest fp32 (ties to even) by long
+// division of Z * 2^64 by n and inspection of the quotient's bits.
+__global__ void mean_from_bins(const unsigned long long *__restrict__ bins, int64_t nblocks,
+                               float *__restrict__ mu) {
+  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+  uint32_t w[12];
+  for (int k = 0; k < 12; ++k) w[k] = 0u;
+  for (int e = 1; e < 255; ++e) {
+    const unsigned long long v = bins[e];
+    if (!v) continue;
+    const int sh = e - 1 + 64;
+    const int wo = sh >> 5, bo = sh & 31;
+    const uint32_t add[3] = {(uint32_t)(v << bo), (uint32_t)((v << bo) >> 32),
+                             bo ? (uint32_t)(v >> (64 - bo)) : 0u};
+    uint64_t carry = 0;
+    for (int k = wo; k < 12; ++k) {
+      const uint64_t a = (k - wo < 3) ? add[k - wo] : 0u;
+      const uint64_t s = (uint64_t)w[k] + a + carry;
+      w[k] = (uint32_t)s;
+      carry = s >> 32;
+      if (k - wo >= 2 && carry == 0) break;
+    }
+  }
+  const uint64_t n = (uint64_t)nblocks;
+  uint32_t q[12];
+  uint64_t rem = 0;
+  for (int k = 11; k >= 0; --k) {
+    const uint64_t cur = (rem << 32) | w[k];
+    q[k] = (uint32_t)(cur / n);
+    rem = cur % n;
+  }
+  int top = -1;
+  for (int k = 11; k >= 0; --k)
+    if (q[k]) {
+      top = k;
+      break;
+    }
+  if (top < 0) {  // zero sum
+    *mu = 0.f;
+    return;
+  }
+  const int L = 32 * top + (32 - __clz(q[top]));
+  const int s = max(L - 24, 64);
+  auto bit = [&](int i) -> uint32_t { return (i < 0 || i >= 384) ? 0u : (q[i >> 5] >> (i & 31)) & 1u; };
+  uint32_t m = 0;
+  for (int i = 0; i < 25; ++i) m |= bit(s + i) << i;
+  const uint32_t guard = bit(s - 1);
+  bool sticky = rem != 0;
+  for (int i = 0; i < s - 1 && !sticky; ++i) sticky = bit(i) != 0;
+  if (guard && (sticky || (m & 1u))) ++m;
+  *mu = __uint_as_float(((uint32_t)(s - 64) << 23) + m);
+}
+
+// e4m3 code of the real value v (given as an fp64 quotient of two fp32
+// numbers): nearest value, ties to the even mantissa, saturating at 448.
+__device__ __forceinline__ uint32_t e4m3_rne(double v) {
+  const uint32_t sign = (__double_as_longlong(v) < 0) ? 0x80u : 0u;
+  const double a = fabs(v);
+  uint32_t mag;
+  if (a >= 448.0) {
+    mag = 0x7Eu;
+  } else if (a < 0x1p-6) {
+    mag = (uint32_t)__builtin_rint(a * 512.0);  // subnormal grid 2^-9; 8 -> smallest normal
+  } else {
+    const int e = (int)((__double_as_longlong(a) >> 52) & 0x7FF) - 1023;
+    const double scaled = a * __longlong_as_double((long long)(1023 + 3 - e) << 52);  // a * 2^(3-e), exact
+    mag = (uint32_t)((e + 7) << 3) + ((uint32_t)__builtin_rint(scaled) - 8u);  // carry moves into the exponent
+  }
+  return sign | mag;
+}
+
+__global__ __launch_bounds__(256) void double_quantize(const float *__restrict__ c1, int64_t nblocks,
+                                                       const float *__restrict__ mu_p,
+                                                       uint8_t *__restrict__ q_out,
+                                                       float *__restrict__ s2_out) {
+  __shared__ uint32_t wmax[4];
+  const int64_t b = (int64_t)blockIdx.x * kGroup + threadIdx.x;
+  const float mu = *mu_p;
+  const float d = (b < nblocks) ? __fsub_rn(c1[b], mu) : 0.f;
+  uint32_t a = __float_as_uint(d) & 0x7FFFFFFFu;
+  for (int off = 32; off >= 1; off >>= 1) a = max(a, (uint32_t)__shfl_xor((int)a, off, 64));
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = a;
+  __syncthreads();
+  a = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+  const float s2 = __fdiv_rn(__uint_as_float(a), 448.0f);
+  if (threadIdx.x == 0) s2_out[blockIdx.x] = s2;
+  if (b < nblocks) q_out[b] = (s2 > 0.f) ? (uint8_t)e4m3_rne((double)d / (double)s2) : (uint8_t)0;
+}
+
+// One thread decodes 8 consecutive elements (4 code bytes) per pass.
+__global__ __launch_bounds__(256) void dequantize_bf16(const uint8_t *__restrict__ codes,
+                                                       const uint8_t *__restrict__ fp8,
+                                                       const float *__restrict__ s2,
+                                                       const float *__restrict__ mu_p, int64_t numel,
+                                                       uint16_t *__restrict__ out, Codebook cb) {
+  __shared__ float lut[16];
+  if (threadIdx.x < 16) lut[threadIdx.x] = cb.v[threadIdx.x];
+  __syncthreads();
+  const float mu = *mu_p;
+  const int64_t nchunks = (numel + 7) >> 3;
+  const int64_t codes_bytes = (numel + 1) >> 1;
+  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nchunks; c += (int64_t)gridDim.x * 256) {
+    const int64_t e0 = c << 3;
+    const bool full = e0 + 8 <= numel;
+    uint32_t packed;
+    if (full) {
+      packed = *(const uint32_t *)(codes + (c << 2));
+    } else {
+      packed = 0x77777777u;
+      for (int i = 0; i < 4; ++i)
+        if ((c << 2) + i < codes_bytes) packed = (packed & ~(0xFFu << (8 * i))) | ((uint32_t)codes[(c << 2) + i] << (8 * i));
+    }
+    const int64_t blk = e0 >> 6;
+    const float ch = decode_constant(fp8[blk], s2[blk >> 8], mu);
+    u32x4 o;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float lo = decode_product(lut[(packed >> (8 * i)) & 15u], ch);
+      const float hi = decode_product(lut[(packed >> (8 * i + 4)) & 15u], ch);
+      o[i] = pack_bf16x2(lo, hi);
+    }
+    if (full) {
+      *(u32x4 *)(out + e0) = o;
+    } else {
+      for (int i = 0; i < 8; ++i)
+        if (e0 + i < numel) out[e0 + i] = (uint16_t)(o[i >> 1] >> (16 * (i & 1)));
+    }
+  }
+}
+
+static inline int grid_for(int64_t items, int64_t per_wg, int64_t cap) {
+  int64_t g = (items + per_wg - 1) / per_wg;
+  if (g > cap) g = cap;
+  return (int)(g < 1 ? 1 : g);
+}
+
+hipError_t launch_quantize(const void *w, bool bf16_src, int64_t numel, uint8_t *codes, uint8_t *fp8,
+                           float *s2, float *mu, uint32_t *status, unsigned long long *bins, float *c1,
+                           const Midpoints &mid, hipStream_t st) {
+  const int64_t nblocks = (numel + kBlock - 1) / kBlock;
+  const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
+  const int64_t codes_bytes = (numel + 1) / 2;
+  // status word + padding (64 words) followed by 256 u64 bins = 576 words
+  zero_words<<<3, 256, 0, st>>>(status, 64 + 512);
+  const int g = grid_for(nblocks, 32, 8192);
+  if (bf16_src)
+    quantize_blocks<true><<<g, 256, 0, st>>>(w, numel, nblocks, codes, codes_bytes, c1, bins, status, mid);
+  else
+    quantize_blocks<false><<<g, 256, 0, st>>>(w, numel, nblocks, codes, codes_bytes, c1, bins, status, mid);
+  mean_from_bins<<<1, 64, 0, st>>>(bins, nblocks, mu);
+  double_quantize<<<(unsigned)ngroups, 256, 0, st>>>(c1, nblocks, mu, fp8, s2);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequantize(const uint8_t *codes, const uint8_t *fp8, const float *s2, const float *mu,
+                             int64_t numel, uint16_t *out, const Codebook &cb, hipStream_t st) {
+  const int64_t nchunks = (numel + 7) / 8;
+  const int g = grid_for(nchunks, 256, 256 * 32);
+  dequantize_bf16<<<g, 256, 0, st>>>(codes, fp8, s2, mu, numel, out, cb);
+  return hipGetLastError();
+}
+
+}  // namespace qlora

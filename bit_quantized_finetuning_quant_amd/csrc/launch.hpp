@@ -1,0 +1,51 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.hpp"
+
+namespace qlora {
+
+// Packed weight as the kernels see it.
+struct QWeight {
+  const uint8_t *codes;
+  const uint8_t *fp8;
+  const float *s2;
+  const float *mu;
+  int64_t n_out, n_in;
+};
+
+hipError_t launch_quantize(const void *w, bool bf16_src, int64_t numel, uint8_t *codes, uint8_t *fp8,
+                           float *s2, float *mu, uint32_t *status, unsigned long long *bins, float *c1,
+                           const Midpoints &mid, hipStream_t st);
+
+hipError_t launch_dequantize(const uint8_t *codes, const uint8_t *fp8, const float *s2, const float *mu,
+                             int64_t numel, uint16_t *out, const Codebook &cb, hipStream_t st);
+
+// Workspace plan of the linear calls (byte offsets into the caller's buffer).
+struct LinearPlan {
+  int64_t T, N, K;
+  int r;
+  int s_u, s_v;       // K-splits of x A^T and dy B
+  int s_ga, s_gb;     // T-splits of grad_A and grad_B
+  size_t off_status, off_u, off_v, off_bt, off_at, off_part, total;
+};
+
+LinearPlan plan_linear(int64_t T, int64_t N, int64_t K, int r);
+
+// Optional event bracketing of the fused GEMM launches (diagnostics).
+void gemm_timing_enable(bool on);
+bool gemm_timing_read(int64_t *fwd_n, double *fwd_ms, int64_t *dx_n, double *dx_ms);
+
+hipError_t launch_linear_fwd(const LinearPlan &p, const uint16_t *x, const QWeight &w, const uint16_t *A,
+                             const uint16_t *B, float scale, uint16_t *y, uint16_t *u_out, char *ws,
+                             const Codebook &cb, hipStream_t st);
+
+hipError_t launch_linear_bwd(const LinearPlan &p, const uint16_t *dy, const uint16_t *x, const QWeight &w,
+                             const uint16_t *A, const uint16_t *B, float scale, const uint16_t *u,
+                             uint16_t *grad_x, float *grad_A, float *grad_B, char *ws, const Codebook &cb,
+                             hipStream_t st);
+
+}  // namespace qlora

@@ -1,0 +1,244 @@
+"""ctypes binding of the gfx950 QLoRA library (``libqlora_gfx950.so``).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI declared in ``include/qlora.h``.  PyTorch supplies
+device memory (``data_ptr()``) and the stream (``cuda_stream``).  There is no
+fallback: if the library is missing, every call raises.
+"""
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libqlora_gfx950.so")
+
+QLORA_F32, QLORA_BF16 = 0, 1
+STATUS_NAMES = {0: "QLORA_OK", 1: "QLORA_ERR_NULL", 2: "QLORA_ERR_SHAPE", 3: "QLORA_ERR_ALIGN",
+                4: "QLORA_ERR_WORKSPACE", 5: "QLORA_ERR_DTYPE", 6: "QLORA_ERR_HIP",
+                7: "QLORA_ERR_NONFINITE", 8: "QLORA_ERR_VALUE"}
+
+
+class QloraError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)} ({status_string(status)})")
+
+
+class NF4WeightStruct(ctypes.Structure):
+    _fields_ = [("n_out", ctypes.c_int64), ("n_in", ctypes.c_int64), ("codes", ctypes.c_void_p),
+                ("absmax_fp8", ctypes.c_void_p), ("absmax_scale", ctypes.c_void_p),
+                ("absmax_mean", ctypes.c_void_p)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+_I64 = ctypes.c_int64
+_SZ = ctypes.c_size_t
+
+_SIGNATURES = {
+    "qlora_nf4_sizes": (ctypes.c_int, [_I64, _I64, _P, _P, _P]),
+    "qlora_nf4_bytes": (_SZ, [_I64, _I64]),
+    "qlora_quantize_workspace_bytes": (_SZ, [_I64, _I64]),
+    "qlora_linear_workspace_bytes": (_SZ, [_I64, _I64, _I64, ctypes.c_int]),
+    "qlora_nf4_codebook": (None, [_P]),
+    "qlora_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "qlora_version": (ctypes.c_char_p, []),
+    "qlora_quantize": (ctypes.c_int, [_P, ctypes.c_int, _P, _P, _SZ, _P]),
+    "qlora_dequantize": (ctypes.c_int, [_P, _P, _P]),
+    "qlora_linear_fwd": (ctypes.c_int, [_P, _I64, _P, _P, _P, ctypes.c_int, ctypes.c_float, _P, _P, _P, _SZ, _P]),
+    "qlora_linear_bwd": (ctypes.c_int, [_P, _P, _I64, _P, _P, _P, ctypes.c_int, ctypes.c_float, _P, _P, _P, _P,
+                                        _P, _SZ, _P]),
+    "qlora_status_read": (ctypes.c_int, [_P, _P]),
+    "qlora_gemm_timing_enable": (None, [ctypes.c_int]),
+    "qlora_gemm_timing_read": (ctypes.c_int, [_P, _P, _P, _P]),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m bit_quantized_finetuning_quant_amd.build`")
+        l = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGNATURES.items():
+            f = getattr(l, name)
+            f.restype = res
+            f.argtypes = args
+        _lib = l
+    return _lib
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise QloraError(status, where)
+
+
+# ---------------------------------------------------------------- host helpers
+def status_string(status: int) -> str:
+    return lib().qlora_status_string(int(status)).decode()
+
+
+def version() -> str:
+    return lib().qlora_version().decode()
+
+
+def nf4_sizes(n_out: int, n_in: int):
+    cb, nb, ng = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(lib().qlora_nf4_sizes(n_out, n_in, ctypes.byref(cb), ctypes.byref(nb), ctypes.byref(ng)), "nf4_sizes")
+    return cb.value, nb.value, ng.value
+
+
+def nf4_bytes(n_out: int, n_in: int) -> int:
+    return int(lib().qlora_nf4_bytes(n_out, n_in))
+
+
+def quantize_workspace_bytes(n_out: int, n_in: int) -> int:
+    return int(lib().qlora_quantize_workspace_bytes(n_out, n_in))
+
+
+def linear_workspace_bytes(tokens: int, n_out: int, n_in: int, r: int) -> int:
+    return int(lib().qlora_linear_workspace_bytes(tokens, n_out, n_in, r))
+
+
+def gemm_timing_enable(on: bool) -> None:
+    """Bracket every fused-GEMM launch with HIP events on its stream (diagnostics)."""
+    lib().qlora_gemm_timing_enable(1 if on else 0)
+
+
+def gemm_timing_read():
+    """-> {"fwd": (launches, ms), "dx": (launches, ms)} for the launches timed so far (then cleared)."""
+    fn, fm, dn, dm = ctypes.c_int64(), ctypes.c_double(), ctypes.c_int64(), ctypes.c_double()
+    _check(lib().qlora_gemm_timing_read(ctypes.byref(fn), ctypes.byref(fm), ctypes.byref(dn), ctypes.byref(dm)),
+           "gemm_timing_read")
+    return {"fwd": (fn.value, fm.value), "dx": (dn.value, dm.value)}
+
+
+def nf4_codebook():
+    buf = (ctypes.c_float * 16)()
+    lib().qlora_nf4_codebook(buf)
+    return list(buf)
+
+
+# ------------------------------------------------------------- device helpers
+def _torch():
+    import torch
+
+    return torch
+
+
+def _stream(stream=None) -> int:
+    torch = _torch()
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return int(s.cuda_stream)
+
+
+def _ptr(t) -> int:
+    return 0 if t is None else int(t.data_ptr())
+
+
+@dataclass
+class NF4Weight:
+    """Device buffers of a packed weight (allocated by torch, owned by this object)."""
+    n_out: int
+    n_in: int
+    codes: "object"
+    absmax_fp8: "object"
+    absmax_scale: "object"
+    absmax_mean: "object"
+
+    @classmethod
+    def empty(cls, n_out: int, n_in: int, device="cuda"):
+        torch = _torch()
+        cb, nb, ng = nf4_sizes(n_out, n_in)
+        return cls(n_out, n_in, torch.empty(cb, dtype=torch.uint8, device=device),
+                   torch.empty(nb, dtype=torch.uint8, device=device),
+                   torch.empty(ng, dtype=torch.float32, device=device),
+                   torch.empty(1, dtype=torch.float32, device=device))
+
+    def struct(self) -> NF4WeightStruct:
+        return NF4WeightStruct(self.n_out, self.n_in, _ptr(self.codes), _ptr(self.absmax_fp8),
+                               _ptr(self.absmax_scale), _ptr(self.absmax_mean))
+
+    def nbytes(self) -> int:
+        return sum(t.numel() * t.element_size() for t in
+                   (self.codes, self.absmax_fp8, self.absmax_scale, self.absmax_mean))
+
+
+def _bits(t):
+    """bf16 tensor -> the same memory viewed as int16 (no copy)."""
+    torch = _torch()
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
+
+
+def quantize(w, out: NF4Weight = None, workspace=None, stream=None) -> NF4Weight:
+    """Quantize a [n_out x n_in] fp32 or bf16 CUDA tensor to NF4 + FP8 double quantization."""
+    torch = _torch()
+    if w.dim() != 2 or not w.is_contiguous():
+        raise ValueError("w must be a contiguous 2-D tensor")
+    dtype = {torch.float32: QLORA_F32, torch.bfloat16: QLORA_BF16}.get(w.dtype)
+    if dtype is None:
+        raise ValueError("w must be float32 or bfloat16")
+    n_out, n_in = w.shape
+    q = out if out is not None else NF4Weight.empty(n_out, n_in, w.device)
+    wsb = quantize_workspace_bytes(n_out, n_in)
+    ws = workspace if workspace is not None else torch.empty(wsb, dtype=torch.uint8, device=w.device)
+    st = q.struct()
+    _check(lib().qlora_quantize(_ptr(w), dtype, ctypes.byref(st), _ptr(ws), ws.numel() * ws.element_size(),
+                                _stream(stream)), "qlora_quantize")
+    q.last_workspace = ws
+    return q
+
+
+def status_read(workspace, stream=None) -> int:
+    """Synchronise and return the status word a call left in `workspace` (0 = ok)."""
+    return int(lib().qlora_status_read(_ptr(workspace), _stream(stream)))
+
+
+def dequantize(q: NF4Weight, out=None, stream=None):
+    torch = _torch()
+    y = out if out is not None else torch.empty((q.n_out, q.n_in), dtype=torch.bfloat16, device=q.codes.device)
+    st = q.struct()
+    _check(lib().qlora_dequantize(ctypes.byref(st), _ptr(y), _stream(stream)), "qlora_dequantize")
+    return y
+
+
+def linear_fwd(x, q: NF4Weight, A, B, scale: float, y=None, u_out=None, save_u=True, workspace=None,
+               stream=None):
+    """y = x W_hat^T + scale (x A^T) B^T (bf16); returns (y, u or None)."""
+    torch = _torch()
+    T = x.shape[0]
+    r = A.shape[0]
+    y = y if y is not None else torch.empty((T, q.n_out), dtype=torch.bfloat16, device=x.device)
+    if save_u and u_out is None:
+        u_out = torch.empty((T, r), dtype=torch.bfloat16, device=x.device)
+    wsb = linear_workspace_bytes(T, q.n_out, q.n_in, r)
+    ws = workspace if workspace is not None else torch.empty(max(wsb, 1), dtype=torch.uint8, device=x.device)
+    st = q.struct()
+    _check(lib().qlora_linear_fwd(_ptr(x), T, ctypes.byref(st), _ptr(A), _ptr(B), r, float(scale), _ptr(y),
+                                  _ptr(u_out), _ptr(ws), ws.numel(), _stream(stream)), "qlora_linear_fwd")
+    return y, u_out
+
+
+def linear_bwd(dy, x, q: NF4Weight, A, B, scale: float, u=None, need_grad_x=True, grad_x=None, grad_A=None,
+               grad_B=None, workspace=None, stream=None):
+    """Returns (grad_x bf16 or None, grad_A fp32, grad_B fp32)."""
+    torch = _torch()
+    T = x.shape[0]
+    r = A.shape[0]
+    dev = x.device
+    if need_grad_x and grad_x is None:
+        grad_x = torch.empty((T, q.n_in), dtype=torch.bfloat16, device=dev)
+    if not need_grad_x:
+        grad_x = None
+    grad_A = grad_A if grad_A is not None else torch.empty((r, q.n_in), dtype=torch.float32, device=dev)
+    grad_B = grad_B if grad_B is not None else torch.empty((q.n_out, r), dtype=torch.float32, device=dev)
+    wsb = linear_workspace_bytes(T, q.n_out, q.n_in, r)
+    ws = workspace if workspace is not None else torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    st = q.struct()
+    _check(lib().qlora_linear_bwd(_ptr(dy), _ptr(x), T, ctypes.byref(st), _ptr(A), _ptr(B), r, float(scale),
+                                  _ptr(u), _ptr(grad_x), _ptr(grad_A), _ptr(grad_B), _ptr(ws), ws.numel(),
+                                  _stream(stream)), "qlora_linear_bwd")
+    return grad_x, grad_A, grad_B

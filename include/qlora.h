@@ -1,0 +1,175 @@
+/*
+ * qlora.h -- C ABI of the QLoRA linear layer for MI355X (gfx950).
+ *
+ * The method (the "qlora" encyclopedia entry on tonho.wtf, sections "a ideia"
+ * and "como funciona"; the LoRA formula from the nexusinovation tutorial
+ * "Tutorial fine-tuning LLM LoRA/QLoRA", section "LoRA: O Padrão Ouro de
+ * Eficiência"):
+ *   - a frozen base weight W [n_out x n_in] is stored in a 4-bit type (NF4)
+ *     built from standard-normal quantiles, normalised to [-1, 1] by the
+ *     absolute maximum of each 64-element block, with an exact zero;
+ *   - the per-block constants are quantized again, to FP8 (e4m3) in groups of
+ *     256, with one fp32 scale per group and one fp32 mean per tensor
+ *     (double quantization: 4.127 bits per parameter in total);
+ *   - every use of the weight dequantizes it to BFloat16 inside the matrix
+ *     product; a 16-bit LoRA adapter path is added, W' = W + s.B.A with
+ *     A [r x n_in] and B [n_out x r];
+ *   - the backward pass sends the gradient through the frozen weight into the
+ *     adapters only (grad_x, grad_A, grad_B; never a gradient for W).
+ *
+ * Conventions for every call:
+ *   - Tensor pointers are DEVICE pointers (memory the caller allocated on the
+ *     current HIP device), 16-byte aligned, row-major and densely packed.
+ *     bf16 tensors are passed as uint16_t bit patterns.
+ *   - The caller owns every buffer, including the workspace.  The library
+ *     allocates and frees no device memory and keeps no mutable global state.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Calls validate
+ *     their arguments on the host, enqueue kernels on `stream` and return
+ *     without waiting.  Buffers must stay alive until the stream has run the
+ *     work.  Calls on different streams are independent; two calls that share
+ *     a workspace must be ordered by the caller.
+ *   - Host-checkable problems return a non-zero qlora_status BEFORE anything
+ *     is enqueued.  A launch failure returns QLORA_ERR_HIP.  Data-dependent
+ *     problems (a NaN or Inf in the weight given to qlora_quantize) set a flag
+ *     in the workspace that qlora_status_read reports.  Nothing throws.
+ *   - Outputs are overwritten, never accumulated into.
+ */
+#ifndef QLORA_H
+#define QLORA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  QLORA_OK = 0,
+  QLORA_ERR_NULL = 1,       /* a required pointer is NULL                          */
+  QLORA_ERR_SHAPE = 2,      /* a dimension is out of range (see each call)          */
+  QLORA_ERR_ALIGN = 3,      /* a pointer is not 16-byte aligned                     */
+  QLORA_ERR_WORKSPACE = 4,  /* workspace smaller than the size helper returns      */
+  QLORA_ERR_DTYPE = 5,      /* unknown dtype code                                   */
+  QLORA_ERR_HIP = 6,        /* the HIP runtime reported an error at launch          */
+  QLORA_ERR_NONFINITE = 7,  /* (deferred) NaN or Inf met while quantizing           */
+  QLORA_ERR_VALUE = 8       /* a scalar argument is not finite                      */
+} qlora_status;
+
+typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
+
+/* Packed NF4 weight.  All four buffers are device memory owned by the caller.
+ * Element e of the row-major [n_out x n_in] weight belongs to block e/64 and
+ * to double-quantization group (e/64)/256; a partial last block or group is
+ * zero padded.                                                                */
+typedef struct {
+  int64_t n_out;         /* rows of W (output features)                        */
+  int64_t n_in;          /* columns of W (input features), contiguous          */
+  uint8_t *codes;        /* ceil(numel/2) bytes: element 2i in the low nibble,
+                            element 2i+1 in the high nibble; an odd tail's high
+                            nibble is the zero code 7                           */
+  uint8_t *absmax_fp8;   /* nblocks = ceil(numel/64) e4m3 bytes, q_b          */
+  float *absmax_scale;   /* ngroups = ceil(nblocks/256) fp32 scales, s2_g      */
+  float *absmax_mean;    /* 1 fp32, the mean mu of the block absmax values     */
+} qlora_nf4_weight;
+
+/* ---- host-only helpers (no GPU needed) ----------------------------------- */
+
+/* Sizes of the four buffers of a packed [n_out x n_in] weight; any out-pointer
+ * may be NULL.  Returns QLORA_ERR_SHAPE for a non-positive dimension or more
+ * than 2^37 elements.                                                          */
+qlora_status qlora_nf4_sizes(int64_t n_out, int64_t n_in, int64_t *codes_bytes,
+                             int64_t *nblocks, int64_t *ngroups);
+
+/* Total bytes of the packed format (codes + constants + scales + mean): the
+ * storage cost is 8 * this / numel bits per parameter.  0 on a bad shape.     */
+size_t qlora_nf4_bytes(int64_t n_out, int64_t n_in);
+
+/* Workspace bytes needed by qlora_quantize for a weight of this shape.        */
+size_t qlora_quantize_workspace_bytes(int64_t n_out, int64_t n_in);
+
+/* Workspace bytes needed by qlora_linear_fwd and qlora_linear_bwd for T
+ * tokens, this weight shape and adapter rank r (one size covers both calls). */
+size_t qlora_linear_workspace_bytes(int64_t T, int64_t n_out, int64_t n_in, int r);
+
+/* The library's 16 NF4 levels (fp32, code k -> out[k]), computed on the host
+ * from the definition: standard-normal quantiles at equal probability steps,
+ * 8 positive and 7 negative levels plus an exact zero, divided by the largest
+ * quantile; see "como funciona" in the qlora entry.                          */
+void qlora_nf4_codebook(float out[16]);
+
+const char *qlora_status_string(qlora_status s);
+
+/* Library version string.                                                    */
+const char *qlora_version(void);
+
+/* ---- device calls (enqueue on `stream`) ---------------------------------- */
+
+/* Quantize W (fp32 or bf16, [q->n_out x q->n_in], device) into *q.
+ *   c1_b  = max |x| over block b (exact);
+ *   code  = index of the NF4 level nearest to the exact real x / c1_b, ties
+ *           toward the level of smaller magnitude (c1_b = 0 gives code 7);
+ *   mu    = fp32 round-to-nearest of the exact mean of all c1_b;
+ *   per group g: s2_g = fl32(max_b |fl32(c1_b - mu)| / 448) and
+ *   q_b   = e4m3 nearest to the exact real fl32(c1_b - mu) / s2_g (ties to
+ *           the even mantissa, saturating at 448; q_b = 0 when s2_g = 0).
+ * Any numel up to 2^37 is accepted.  ws: qlora_quantize_workspace_bytes, 16-B
+ * aligned; after the call it holds the status word read by qlora_status_read.
+ * A NaN/Inf in W raises QLORA_ERR_NONFINITE there; that block's codes are
+ * then unspecified.                                                           */
+qlora_status qlora_quantize(const void *w, qlora_dtype w_dtype, const qlora_nf4_weight *q,
+                            void *ws, size_t ws_bytes, void *stream);
+
+/* Dequantize *q to bf16 w_bf16 [n_out x n_in] (device):
+ *   c1hat_b = fl32(fl32(e4m3(q_b) * s2_g) + mu)     (no fused multiply-add)
+ *   w_hat   = bf16_round_nearest_even(fl32(CB[code] * c1hat_b))
+ * This is the same decode the fused linear calls apply on the fly.           */
+qlora_status qlora_dequantize(const qlora_nf4_weight *q, uint16_t *w_bf16, void *stream);
+
+/* Forward of the adapted linear layer for T tokens:
+ *   u = x A^T                      (bf16, [T x r]; written to u_out if non-NULL)
+ *   y = bf16( x W_hat^T + scale * u B^T )          [T x n_out]
+ * x [T x n_in] bf16, A [r x n_in] bf16, B [n_out x r] bf16, all device.
+ * Requires n_in % 64 == 0, T >= 1, 1 <= r <= 256, finite scale.  W_hat is
+ * never written to memory: it is decoded tile by tile inside the product.
+ * ws: qlora_linear_workspace_bytes(T, n_out, n_in, r), 16-B aligned.        */
+qlora_status qlora_linear_fwd(const uint16_t *x, int64_t T, const qlora_nf4_weight *q,
+                              const uint16_t *A, const uint16_t *B, int r, float scale,
+                              uint16_t *y, uint16_t *u_out, void *ws, size_t ws_bytes,
+                              void *stream);
+
+/* Backward of the adapted linear layer (the weight is frozen):
+ *   v      = dy B                                   (bf16, internal)
+ *   grad_x = bf16( dy W_hat + scale * v A )         [T x n_in]   (skipped if NULL)
+ *   grad_A = scale * v^T x                          [r x n_in]   fp32
+ *   grad_B = scale * dy^T u                         [n_out x r]  fp32
+ * dy [T x n_out] bf16.  u is the forward's u_out; pass NULL to recompute it.
+ * Same shape rules and workspace as qlora_linear_fwd.                         */
+qlora_status qlora_linear_bwd(const uint16_t *dy, const uint16_t *x, int64_t T,
+                              const qlora_nf4_weight *q, const uint16_t *A, const uint16_t *B,
+                              int r, float scale, const uint16_t *u, uint16_t *grad_x,
+                              float *grad_A, float *grad_B, void *ws, size_t ws_bytes,
+                              void *stream);
+
+/* ---- diagnostics ---------------------------------------------------------- */
+
+/* Kernel timing for benchmarks.  While enabled (non-zero), every launch of the
+ * dequant-fused GEMM kernels (forward: x W_hat^T, backward: dy W_hat) is
+ * bracketed by two HIP events recorded on the call's stream.  The events are
+ * created by the library (no device memory is allocated).  Not thread-safe. */
+void qlora_gemm_timing_enable(int enable);
+
+/* Synchronise the recorded events and return, per kernel, the number of timed
+ * launches and their summed duration in milliseconds; then forget them.
+ * Any out-pointer may be NULL.                                               */
+qlora_status qlora_gemm_timing_read(int64_t *fwd_launches, double *fwd_ms, int64_t *dx_launches,
+                                    double *dx_ms);
+
+/* Wait for `stream`, then read the status word a previous call left in `ws`:
+ * QLORA_OK or QLORA_ERR_NONFINITE (the word is not cleared).                  */
+qlora_status qlora_status_read(const void *ws, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* QLORA_H */

@@ -1,0 +1,117 @@
+"""The C-ABI library: it loads, exports every declared symbol, and its host-only helpers and
+argument validation behave as documented.  No call here reaches the GPU: every validation
+case fails before anything is enqueued."""
+
+import ctypes
+import math
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from bit_quantized_finetuning_quant_amd import qlora
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "qlora.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qlora_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = qlora.lib()
+    names = _declared_functions()
+    assert len(names) >= 12
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(qlora._SIGNATURES)
+
+
+def test_codebook_matches_oracle_bit_for_bit():
+    lib_cb = np.array(qlora.nf4_codebook(), dtype=np.float32)
+    assert np.array_equal(lib_cb.view(np.uint32), oracle.nf4_codebook().view(np.uint32))
+
+
+@pytest.mark.parametrize("shape", [(1, 1), (1, 63), (1, 65), (3, 100), (512, 256), (4096, 11008), (22016, 8192)])
+def test_size_helpers_match_the_format(shape):
+    n_out, n_in = shape
+    numel = n_out * n_in
+    cb, nb, ng = qlora.nf4_sizes(n_out, n_in)
+    assert cb == math.ceil(numel / 2) and nb == math.ceil(numel / 64) and ng == math.ceil(nb / 256)
+    total = qlora.nf4_bytes(n_out, n_in)
+    assert total == cb + nb + 4 * ng + 4
+    assert 8 * total / numel == pytest.approx(oracle.bits_per_param(n_out, n_in), abs=1e-12)
+    assert qlora.quantize_workspace_bytes(n_out, n_in) >= 4 * nb
+
+
+def test_bits_per_param_of_the_65b_store():
+    from bit_quantized_finetuning_quant_amd.workloads import SHAPES_65B
+
+    params = sum(n * k for _, n, k in SHAPES_65B) * 80
+    total = sum(qlora.nf4_bytes(n, k) for _, n, k in SHAPES_65B) * 80
+    assert params == 64_760_053_760
+    assert round(8 * total / params, 3) == 4.127
+    assert 33.0e9 < total < 33.5e9
+
+
+def test_bad_shapes_and_sizes():
+    with pytest.raises(qlora.QloraError):
+        qlora.nf4_sizes(0, 5)
+    assert qlora.nf4_bytes(-1, 5) == 0
+    assert qlora.linear_workspace_bytes(16, 512, 100, 8) == 0  # n_in % 64
+    assert qlora.linear_workspace_bytes(16, 512, 256, 0) == 0
+    assert qlora.linear_workspace_bytes(16, 512, 256, 257) == 0
+    assert qlora.linear_workspace_bytes(0, 512, 256, 8) == 0
+    assert qlora.linear_workspace_bytes(16, 512, 256, 8) > 0
+    assert qlora.status_string(7).startswith("NaN")
+
+
+def _fake_weight(n_out=512, n_in=256, align=True):
+    off = 0 if align else 4
+    return qlora.NF4WeightStruct(n_out, n_in, 0x10000 + off, 0x20000, 0x30000, 0x40000)
+
+
+def _fwd(w, x=0x50000, T=16, a=0x60000, b=0x70000, r=8, scale=2.0, y=0x80000, ws=0x90000, ws_bytes=0):
+    return qlora.lib().qlora_linear_fwd(x, T, ctypes.byref(w), a, b, r, scale, y, None, ws, ws_bytes, None)
+
+
+def test_validation_errors_before_any_launch():
+    L = qlora.lib()
+    w = _fake_weight()
+    assert _fwd(w, x=None) == 1  # NULL
+    assert _fwd(w, x=0x50002) == 3  # misaligned
+    assert _fwd(_fake_weight(align=False)) == 3
+    assert _fwd(_fake_weight(512, 100)) == 2  # n_in % 64
+    assert _fwd(w, T=0) == 2
+    assert _fwd(w, r=0) == 2 and _fwd(w, r=257) == 2
+    assert _fwd(w, scale=float("nan")) == 8 and _fwd(w, scale=float("inf")) == 8
+    assert _fwd(w, ws_bytes=16) == 4  # workspace too small
+    null_w = qlora.NF4WeightStruct(512, 256, None, 0x20000, 0x30000, 0x40000)
+    assert _fwd(null_w) == 1
+    # backward
+    assert L.qlora_linear_bwd(0x50000, 0x50000, 16, ctypes.byref(w), 0x60000, 0x70000, 8, 1.0, None, None,
+                              None, 0x80000, 0x90000, 1 << 30, None) == 1  # grad_A NULL
+    assert L.qlora_linear_bwd(0x50000, 0x50000, 16, ctypes.byref(w), 0x60000, 0x70000, 8, 1.0, None, None,
+                              0x80000, 0x80000, 0x90000, 8, None) == 4
+    # quantize
+    assert L.qlora_quantize(0x50000, 2, ctypes.byref(w), 0x90000, 1 << 30, None) == 5  # dtype
+    assert L.qlora_quantize(0x50000, 0, ctypes.byref(w), 0x90000, 8, None) == 4
+    assert L.qlora_quantize(None, 0, ctypes.byref(w), 0x90000, 1 << 30, None) == 1
+    assert L.qlora_quantize(0x50008, 0, ctypes.byref(w), 0x90000, 1 << 30, None) == 3
+    bad = qlora.NF4WeightStruct(0, 256, 0x10000, 0x20000, 0x30000, 0x40000)
+    assert L.qlora_quantize(0x50000, 0, ctypes.byref(bad), 0x90000, 1 << 30, None) == 2
+    assert L.qlora_dequantize(ctypes.byref(w), None, None) == 1
+    assert L.qlora_dequantize(ctypes.byref(w), 0x50001, None) == 3
+    assert L.qlora_status_read(None, None) == 1
+
+
+def test_product_path_has_no_fallback(monkeypatch, tmp_path):
+    """Without the built library every call raises instead of computing elsewhere."""
+    monkeypatch.setattr(qlora, "_lib", None)
+    monkeypatch.setattr(qlora, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="missing"):
+        qlora.nf4_codebook()
