@@ -33,6 +33,11 @@ struct LinearPlan {
   size_t off_status, off_u, off_v, off_bt, off_at, off_part, total;
 };
 
+// Dequant-fused GEMM: out = scale * la lb^T + act W_op (see qgemm.hip).
+hipError_t launch_qgemm(bool trans_w, const uint16_t *act, int64_t M, int64_t Ncols, int64_t Kc, const QWeight &w,
+                        const uint16_t *la, const uint16_t *lb, int r, float scale, uint16_t *out,
+                        const Codebook &cb, hipStream_t st);
+
 LinearPlan plan_linear(int64_t T, int64_t N, int64_t K, int r);
 
 // Optional event bracketing of the fused GEMM launches (diagnostics).

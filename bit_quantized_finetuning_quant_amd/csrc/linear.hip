@@ -7,8 +7,8 @@
 // into the 16-bit adapters only.  Adapter algebra from the nexusinovation
 // tutorial, section "LoRA: O Padrão Ouro de Eficiência": W' = W + s.B.A.
 //
-//   y      = x W_hat^T + s (x A^T) B^T        qgemm<false> (+ nt_splitk for u)
-//   grad_x = dy W_hat + s (dy B) A            qgemm<true>  (+ nt_splitk for v)
+//   y      = x W_hat^T + s (x A^T) B^T        qgemm.hip (forward form) + nt_splitk for u
+//   grad_x = dy W_hat + s (dy B) A            qgemm.hip (transposed form) + nt_splitk for v
 //   grad_A = s (dy B)^T x                     tn_split + reduce_splits
 //   grad_B = s dy^T (x A^T)                   tn_split + reduce_splits
 //
@@ -35,198 +35,6 @@ __device__ __forceinline__ u32x4 load8(const uint16_t *row, int64_t c, int64_t n
 
 __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
-}
-
-// ---------------------------------------------------------------------------
-// Dequant-fused GEMM.  out[M x Ncols] = scale * la lb^T + act W_op, where the
-// contraction runs over Kc and the weight operand W_op is
-//   kTransW = false: W_hat^T (weight rows are output columns), Kc = n_in
-//   kTransW = true : W_hat   (weight rows are the contraction),  Kc = n_out
-// la [M x r], lb [Ncols x r] are the LoRA factors of the epilogue.
-// Workgroup tile 256 x 128, contraction step 64 (one NF4 block per weight row
-// in the non-transposed case), 4 waves of 128 x 64, LDS double buffered.  The
-// weight tile is decoded once per workgroup into LDS as bf16 and shared by all
-// 256 rows of the activation tile.
-constexpr int GBM = 256, GBN = 128, GBK = 64, GLD = 72;  // GLD: padded LDS row (bf16)
-
-template <bool kTransW>
-__global__ __launch_bounds__(256) void qgemm(const uint16_t *__restrict__ act, int64_t M, int64_t Ncols,
-                                             int64_t Kc, QWeight w, const uint16_t *__restrict__ la,
-                                             const uint16_t *__restrict__ lb, int r, float scale,
-                                             uint16_t *__restrict__ out, Codebook cb) {
-  __shared__ __attribute__((aligned(16))) uint16_t sa[2][GBM * GLD];
-  __shared__ __attribute__((aligned(16))) uint16_t sb[2][GBN * GLD];
-  __shared__ float lut[16];
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int l32 = lane & 31, lhi = lane >> 5;
-  const int64_t m0 = (int64_t)blockIdx.x * GBM, c0 = (int64_t)blockIdx.y * GBN;
-  if (tid < 16) lut[tid] = cb.v[tid];
-  const float mu = *w.mu;
-  const int64_t K = w.n_in, N = w.n_out;
-  const int64_t kblk_row = K / kBlock;
-  const bool act_vec = (Kc % 8) == 0;
-  const bool lora_vec = (r % 8) == 0;
-
-  f32x16 acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-
-  // ---- LoRA term: acc = scale * la lb^T (r padded to a multiple of 16 with zeros)
-  for (int j0 = 0; j0 < r; j0 += 16) {
-    u32x4 af[4], bfr[2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t row = m0 + wm * 128 + i * 32 + l32;
-      af[i] = (row < M) ? load8(la + row * r, j0 + 8 * lhi, r, lora_vec) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = c0 + wn * 64 + j * 32 + l32;
-      bfr[j] = (col < Ncols) ? load8(lb + col * r, j0 + 8 * lhi, r, lora_vec) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] *= scale;
-
-  // ---- staging registers
-  const int a_row = tid >> 3, a_col = 8 * (tid & 7);  // activation: rows a_row + 32 i
-  u32x4 areg[8];
-  // weight, not transposed: one weight row (output column), 32 contraction elements
-  const int f_row = tid >> 1, f_half = tid & 1;
-  // weight, transposed: 4 weight rows (contraction) x 8 output columns
-  const int t_cg = tid & 15, t_rg = tid >> 4;
-  u32x4 wcodes;
-  uint32_t wq[4];
-  float ws2[4];
-  bool wvalid[4];
-
-  const int64_t nk = (Kc + GBK - 1) / GBK;
-
-  auto load_stage = [&](int64_t kt) {
-    const int64_t k0 = kt * GBK;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int64_t row = m0 + a_row + 32 * i;
-      areg[i] = (row < M) ? load8(act + row * Kc, k0 + a_col, Kc, act_vec) : u32x4{0u, 0u, 0u, 0u};
-    }
-    if (!kTransW) {
-      const int64_t n = c0 + f_row;
-      wvalid[0] = n < N;
-      if (wvalid[0]) {
-        wcodes = *(const u32x4 *)(w.codes + n * (K / 2) + k0 / 2 + 16 * f_half);
-        const int64_t blk = n * kblk_row + kt;
-        wq[0] = w.fp8[blk];
-        ws2[0] = w.s2[blk >> 8];
-      }
-    } else {
-      const int64_t kcol = c0 + 8 * t_cg;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t n = k0 + 4 * t_rg + i;
-        wvalid[i] = (n < N) && (kcol < K);
-        if (wvalid[i]) {
-          wcodes[i] = *(const uint32_t *)(w.codes + n * (K / 2) + kcol / 2);
-          const int64_t blk = n * kblk_row + kcol / kBlock;
-          wq[i] = w.fp8[blk];
-          ws2[i] = w.s2[blk >> 8];
-        }
-      }
-    }
-  };
-
-  auto store_stage = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *(u32x4 *)&sa[buf][(a_row + 32 * i) * GLD + a_col] = areg[i];
-    if (!kTransW) {
-      const float ch = wvalid[0] ? decode_constant(wq[0], ws2[0], mu) : 0.f;
-      const u32x4 cw = wvalid[0] ? wcodes : u32x4{0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        u32x4 o;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          const uint32_t word = cw[v];
-          const float lo = decode_product(lut[(word >> (8 * d)) & 15u], ch);
-          const float hi = decode_product(lut[(word >> (8 * d + 4)) & 15u], ch);
-          o[d] = pack_bf16x2(lo, hi);
-        }
-        *(u32x4 *)&sb[buf][f_row * GLD + 32 * f_half + 8 * v] = o;
-      }
-    } else {
-      float ch[4];
-      uint32_t cw[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ch[i] = wvalid[i] ? decode_constant(wq[i], ws2[i], mu) : 0.f;
-        cw[i] = wvalid[i] ? wcodes[i] : 0x77777777u;
-      }
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        float v[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = decode_product(lut[(cw[i] >> (4 * c)) & 15u], ch[i]);
-        uint2 o;
-        o.x = pack_bf16x2(v[0], v[1]);
-        o.y = pack_bf16x2(v[2], v[3]);
-        *(uint2 *)&sb[buf][(8 * t_cg + c) * GLD + 4 * t_rg] = o;
-      }
-    }
-  };
-
-  load_stage(0);
-  __syncthreads();  // lut ready
-  store_stage(0);
-  __syncthreads();
-
-  for (int64_t kt = 0; kt < nk; ++kt) {
-    const int buf = (int)(kt & 1);
-    if (kt + 1 < nk) load_stage(kt + 1);
-#pragma unroll
-    for (int kk = 0; kk < GBK / 16; ++kk) {
-      u32x4 af[4], bfr[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = *(const u32x4 *)&sa[buf][(wm * 128 + i * 32 + l32) * GLD + kk * 16 + 8 * lhi];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) bfr[j] = *(const u32x4 *)&sb[buf][(wn * 64 + j * 32 + l32) * GLD + kk * 16 + 8 * lhi];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(af[i], bfr[j], acc[i][j]);
-    }
-    if (kt + 1 < nk) store_stage(buf ^ 1);
-    __syncthreads();
-  }
-
-  // ---- epilogue: round to bf16 and store
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = c0 + wn * 64 + j * 32 + l32;
-      if (col >= Ncols) continue;
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int64_t row = m0 + wm * 128 + i * 32 + 8 * (q >> 2) + 4 * lhi + (q & 3);
-        if (row < M) {
-          __bf16 h = (__bf16)acc[i][j][q];
-          out[row * Ncols + col] = __builtin_bit_cast(uint16_t, h);
-        }
-      }
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -476,12 +284,11 @@ hipError_t launch_linear_fwd(const LinearPlan &p, const uint16_t *x, const QWeig
   float *part = (float *)(ws + p.off_part);
   set_word<<<1, 64, 0, st>>>((uint32_t *)(ws + p.off_status), 0u);
   launch_u(p, x, A, u, part, st);
-  dim3 g((unsigned)cdiv(p.T, GBM), (unsigned)cdiv(p.N, GBN));
   TimedLaunch tl;
   const bool timed = timing_begin(st, tl, false);
-  qgemm<false><<<g, 256, 0, st>>>(x, p.T, p.N, p.K, w, u, B, p.r, scale, y, cb);
+  const hipError_t e = launch_qgemm(false, x, p.T, p.N, p.K, w, u, B, p.r, scale, y, cb, st);
   if (timed) timing_end(st, tl);
-  return hipGetLastError();
+  return e != hipSuccess ? e : hipGetLastError();
 }
 
 hipError_t launch_linear_bwd(const LinearPlan &p, const uint16_t *dy, const uint16_t *x, const QWeight &w,
@@ -491,7 +298,6 @@ hipError_t launch_linear_bwd(const LinearPlan &p, const uint16_t *dy, const uint
   float *part = (float *)(ws + p.off_part);
   uint16_t *v = (uint16_t *)(ws + p.off_v);
   uint16_t *bt = (uint16_t *)(ws + p.off_bt);
-  uint16_t *at = (uint16_t *)(ws + p.off_at);
   set_word<<<1, 64, 0, st>>>((uint32_t *)(ws + p.off_status), 0u);
   if (!u) {
     uint16_t *uw = (uint16_t *)(ws + p.off_u);
@@ -507,12 +313,11 @@ hipError_t launch_linear_bwd(const LinearPlan &p, const uint16_t *dy, const uint
     launch_reduce(part, p.s_v, p.T * p.r, 1.0f, v, true, st);
   }
   if (grad_x) {
-    transpose_bf16<<<dim3((unsigned)cdiv(p.K, 32), (unsigned)cdiv(p.r, 32)), 256, 0, st>>>(A, p.r, p.K, at);
-    dim3 g((unsigned)cdiv(p.T, GBM), (unsigned)cdiv(p.K, GBN));
     TimedLaunch tl;
     const bool timed = timing_begin(st, tl, true);
-    qgemm<true><<<g, 256, 0, st>>>(dy, p.T, p.K, p.N, w, v, at, p.r, scale, grad_x, cb);
+    const hipError_t e = launch_qgemm(true, dy, p.T, p.K, p.N, w, v, A, p.r, scale, grad_x, cb, st);
     if (timed) timing_end(st, tl);
+    if (e != hipSuccess) return e;
   }
   {  // grad_A = s v^T x   [r x K]
     const int64_t tchunk = chunk_of(p.T, p.s_ga, 32);
