@@ -32,10 +32,15 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 // e4m3 ("fn") byte -> its exact value: bias 7, 3 mantissa bits, exponent
 // field 0 = subnormal m * 2^-9.  NaN patterns never occur in stored data.
 __device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-  uint32_t e = (b >> 3) & 0xFu;
-  uint32_t m = b & 7u;
-  float mag = e ? __uint_as_float(((e + 120u) << 23) | (m << 20)) : (float)m * 0x1p-9f;
-  return (b & 0x80u) ? -mag : mag;
+  // Branch-free: both the normal and the subnormal encodings are formed and
+  // one is selected, and the sign is OR-ed in (a divergent branch here would
+  // make the compiler drain outstanding loads at the join).
+  const uint32_t e = (b >> 3) & 0xFu;
+  const uint32_t m = b & 7u;
+  const uint32_t normal = ((e + 120u) << 23) | (m << 20);
+  const uint32_t subnormal = __float_as_uint((float)m * 0x1p-9f);  // exact
+  const uint32_t mag = e ? normal : subnormal;
+  return __uint_as_float(mag | ((b & 0x80u) << 24));
 }
 
 // Block constant decode: fl32(fl32(e4m3(q) * s2) + mu), two roundings.  The

@@ -11,16 +11,20 @@
 //   grad_x  : act = dy [T x n_out], W_op = W_hat,   Kc = n_out, la = v, lb = A^T
 //
 // Workgroup = 8 waves on a 256 x 128 output tile, contraction step 64:
-//   waves 0-3 (consumers) each own a 128 x 64 sub-tile and only read LDS and
-//     issue v_mfma_f32_32x32x16_bf16;
-//   waves 4-7 (producers) fetch the activation tile and the packed weight tile
-//     two steps ahead into registers, decode the nibbles through the 16-entry
-//     level table into bf16 (weight tile decoded once per workgroup, shared by
-//     all 256 activation rows) and write the next LDS stage.
+//   waves 0-3 (consumers) each own a 128 x 64 sub-tile: they read LDS, issue
+//     v_mfma_f32_32x32x16_bf16, and (full tiles) move the activation tile of
+//     stage k+2 from global memory straight into a 3-stage LDS ring with
+//     global_load_lds_dwordx4, so no register ever holds it;
+//   waves 4-7 (producers) fetch the packed weight codes two steps ahead into
+//     registers, decode the nibbles through the 16-entry level table into bf16
+//     (the weight tile is decoded once per workgroup and shared by all 256
+//     activation rows) and write the next weight stage to LDS.  For partial
+//     tiles they also carry the activation tile, masked, through registers.
 // One consumer and one producer wave share each SIMD, so the decode's vector
-// ALU work issues alongside the matrix-core work.  Two LDS stages, one
-// workgroup barrier per contraction step; both roles execute the same number
-// of barriers.
+// ALU work issues alongside the matrix-core work.  One workgroup barrier per
+// contraction step; both roles execute the same number of barriers.  The DMA
+// is kept in the consumer waves because a wave that has issued LDS-DMA gets
+// conservative full waits on every later use of a loaded register.
 //
 // MFMA lane layouts (l = lane): A operand lane l holds A[l%32][8(l/32)..+7],
 // B operand lane l holds B[8(l/32)..+7][l%32], result register q of lane l is
@@ -33,7 +37,11 @@ namespace qlora {
 
 namespace {
 
-constexpr int QBM = 256, QBN = 128, QBK = 64, QLD = 72;  // QLD: padded LDS row length (bf16)
+constexpr int QBM = 256, QBN = 128, QBK = 64, QLD = 72;  // QLD: padded LDS row of the weight tile (bf16)
+constexpr int kActStages = 3;                            // activation tile LDS ring
+
+typedef __attribute__((address_space(1))) const void gptr_t;
+typedef __attribute__((address_space(3))) void lptr_t;
 
 __device__ __forceinline__ u32x4 ld8(const uint16_t *row, int64_t c, int64_t ncols, bool vec) {
   if (vec && c + 8 <= ncols) return *(const u32x4 *)(row + c);
@@ -47,8 +55,60 @@ __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+// Activation tile in LDS: 256 rows of 64 bf16 (128 B, eight 16-byte chunks),
+// unpadded; chunk c of row r sits at position c ^ (r & 7), so that the MFMA
+// fragment reads of 8 consecutive rows hit distinct banks.
+__device__ __forceinline__ int act_off(int row, int chunk) { return row * 64 + ((chunk ^ (row & 7)) << 3); }
+
+// Workgroup barrier without the memory fences of __syncthreads(): those would
+// wait for every outstanding load, including the LDS-DMA of stages that are
+// deliberately still in flight.  Each caller first waits for exactly what the
+// other waves need (s_waitcnt), and the empty asm statements keep the compiler
+// from moving memory accesses across the barrier.
+__device__ __forceinline__ void wg_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// s_waitcnt immediate (gfx9 encoding): vmcnt in bits 3:0 and 15:14, expcnt in
+// 6:4 (left at its maximum), lgkmcnt in 11:8.
+constexpr int waitcnt_imm(int vm, int lgkm) { return (vm & 15) | (7 << 4) | ((lgkm & 15) << 8) | ((vm >> 4) << 14); }
+
+// One 16-byte-per-lane LDS-DMA: lane l reads 16 bytes at sbase + voff and
+// writes them at LDS byte address lds + 16 l.  Written as inline asm so that
+// the compiler does not treat the whole LDS as possibly being written by it:
+// the builtin makes every later LDS read of the wave wait for all outstanding
+// loads, including stages that are meant to stay in flight.  The instruction
+// has no register result; its waits are issued explicitly by the caller, and
+// voff must stay unmodified until they have been.
+__device__ __forceinline__ void dma16(const char *sbase, uint32_t voff, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(sbase), "s"(lds)
+      : "memory", "m0");
+}
+
+__device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)(lptr_t *)p; }
+
+// Full tiles: consumer wave cw (0..3) moves rows [64 cw, 64 cw + 64) of the
+// activation tile of stage kt into LDS buffer dst with 8 DMA instructions of 8
+// rows each (lane l writes the 16 bytes at dst + 16 l: row 8 j + l/8 of the
+// range, the chunk whose swizzled position is l % 8).  The per-lane byte
+// offset is loop-invariant and everything else is scalar.
+__device__ __forceinline__ void dma_act(const uint16_t *act, int64_t Kc, int64_t row0, int64_t kt,
+                                        uint32_t lane_off, uint16_t *dst) {
+  const char *base = (const char *)(act + row0 * Kc + kt * QBK);
+  const uint32_t l0 = lds_addr(dst);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) dma16(base + (int64_t)(16 * j) * Kc, lane_off, l0 + 8 * j * 64 * 2);
+}
+
 struct Stage {
-  u32x4 a[8];   // activation: 8 rows x 8 contraction elements
+  u32x4 a[8];   // activation (register path only): 8 rows x 8 contraction elements
   u32x4 code;   // weight codes (see Producer)
   uint32_t q[4];
   float s2[4];
@@ -63,45 +123,31 @@ struct Producer {
   int ptid;
   bool act_vec;
 
-  // kFull: the whole tile and every contraction step are in range and rows are
-  // 16-byte aligned, so every load is unconditional (no branches, so the
-  // compiler can keep two steps of loads in flight).
-  template <bool kFull>
-  __device__ __forceinline__ void load(int64_t kt, Stage &s) const {
+  // Partial tiles: the activation tile goes through registers with masking.
+  __device__ __forceinline__ void load_act(int64_t kt, Stage &s) const {
     const int64_t k0 = kt * QBK;
     const int a_row = ptid >> 3, a_col = 8 * (ptid & 7);
-    if (kFull) {
-      const uint16_t *base = act + (m0 + a_row) * Kc + k0 + a_col;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) s.a[i] = *(const u32x4 *)(base + (int64_t)(32 * i) * Kc);
-      if (!kTransW) {
-        const int64_t n = c0 + (ptid >> 1);
-        s.code = *(const u32x4 *)(w.codes + n * (K / 2) + k0 / 2 + 16 * (ptid & 1));
-        const int64_t blk = n * kblk_row + kt;
-        s.q[0] = w.fp8[blk];
-        s.s2[0] = w.s2[blk >> 8];
-      } else {
-        const int64_t kcol = c0 + 8 * (ptid >> 4);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t n = k0 + 4 * (ptid & 15) + i;
-          s.code[i] = *(const uint32_t *)(w.codes + n * (K / 2) + kcol / 2);
-          const int64_t blk = n * kblk_row + kcol / kBlock;
-          s.q[i] = w.fp8[blk];
-          s.s2[i] = w.s2[blk >> 8];
-        }
-      }
-      return;
-    }
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int64_t row = m0 + a_row + 32 * i;
       s.a[i] = (row < M) ? ld8(act + row * Kc, k0 + a_col, Kc, act_vec) : u32x4{0u, 0u, 0u, 0u};
     }
+  }
+
+  __device__ __forceinline__ void store_act(const Stage &s, uint16_t *dst) const {
+    const int a_row = ptid >> 3, chunk = ptid & 7;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) *(u32x4 *)&dst[act_off(a_row + 32 * i, chunk)] = s.a[i];
+  }
+
+  // Packed weight codes, FP8 constants and group scales of stage kt.
+  template <bool kFull>
+  __device__ __forceinline__ void load_w(int64_t kt, Stage &s) const {
+    const int64_t k0 = kt * QBK;
     if (!kTransW) {
       // one weight row (an output column), 32 consecutive contraction elements
       const int64_t n = c0 + (ptid >> 1);
-      if (n < N) {
+      if (kFull || n < N) {
         s.code = *(const u32x4 *)(w.codes + n * (K / 2) + k0 / 2 + 16 * (ptid & 1));
         const int64_t blk = n * kblk_row + kt;
         s.q[0] = w.fp8[blk];
@@ -119,7 +165,7 @@ struct Producer {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int64_t n = k0 + 4 * (ptid & 15) + i;
-        if (n < N && kcol < K) {
+        if (kFull || (n < N && kcol < K)) {
           s.code[i] = *(const uint32_t *)(w.codes + n * (K / 2) + kcol / 2);
           const int64_t blk = n * kblk_row + kcol / kBlock;
           s.q[i] = w.fp8[blk];
@@ -133,12 +179,9 @@ struct Producer {
     }
   }
 
-  // Decode one stage into LDS.  All 32 level-table reads are issued before any
-  // of the arithmetic that consumes them, so their LDS latency is paid once.
-  __device__ __forceinline__ void store(const Stage &s, uint16_t *sa, uint16_t *sb, const float *lut) const {
-    const int a_row = ptid >> 3, a_col = 8 * (ptid & 7);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) *(u32x4 *)&sa[(a_row + 32 * i) * QLD + a_col] = s.a[i];
+  // Decode one weight stage into LDS.  All 32 level-table reads are issued
+  // before any of the arithmetic that consumes them.
+  __device__ __forceinline__ void store_w(const Stage &s, uint16_t *sb, const float *lut) const {
     float lv[32];
     if (!kTransW) {
       // element e = 8 v + j of this lane's 32: nibble j of code word v
@@ -180,35 +223,48 @@ struct Producer {
   }
 };
 
-// Producer side of the pipeline: stage k+2 is fetched into registers while
-// stage k+1 is decoded into LDS and the consumers multiply stage k.  Three
-// register sets rotate; the loop is unrolled by three so that each set is a
-// fixed group of registers.
+// Producer side of the pipeline: at step k the weight codes of stage k+2 are
+// fetched into registers while stage k+1 is decoded into LDS and the
+// consumers multiply stage k (partial tiles: the activation tile rides along
+// in the same registers).  Three register sets rotate; the main loop is
+// unrolled by three with no conditions inside, so each set keeps fixed
+// registers.
 template <bool kFull, bool kTransW>
-__device__ __forceinline__ void producer_loop(const Producer<kTransW> &p, int64_t nk, uint16_t (*sa)[QBM * QLD],
-                                              uint16_t (*sb)[QBN * QLD], const float *lut) {
+__device__ __forceinline__ void producer_loop(const Producer<kTransW> &p, int64_t nk,
+                                              uint16_t (*sa)[QBM * 64], uint16_t (*sb)[QBN * QLD],
+                                              const float *lut) {
   Stage s0, s1, s2;
-  p.template load<kFull>(0, s0);
-  p.template load<kFull>(min((int64_t)1, nk - 1), s1);
-  __syncthreads();  // level table in LDS
-  p.store(s0, sa[0], sb[0], lut);
-  __syncthreads();  // stage 0 ready
-  // The step body is unconditional: past the end it re-fetches the last stage
-  // and writes the LDS buffer nobody reads any more, which keeps the loop free
-  // of branches so that the fetch of stage k+2 stays in flight while stage k+1
-  // is decoded.
-#define QGEMM_PRODUCER_STEP(K_, CUR_NEXT, NEXT2)                                    \
-  if ((K_) < nk) {                                                                  \
-    p.template load<kFull>(min((K_) + 2, nk - 1), NEXT2);                           \
-    __builtin_amdgcn_sched_barrier(0);                                              \
-    p.store(CUR_NEXT, sa[((K_) + 1) & 1], sb[((K_) + 1) & 1], lut);                 \
-    __syncthreads();                                                                \
+  if (!kFull) {
+    p.load_act(0, s0);
+    p.load_act(min((int64_t)1, nk - 1), s1);
   }
-  for (int64_t kt = 0; kt < nk; kt += 3) {
+  p.template load_w<kFull>(0, s0);
+  p.template load_w<kFull>(min((int64_t)1, nk - 1), s1);
+  __syncthreads();  // level table in LDS
+  if (!kFull) p.store_act(s0, sa[0]);
+  p.store_w(s0, sb[0], lut);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+  wg_barrier();  // stage 0 ready
+#define QGEMM_PRODUCER_STEP(K_, CUR_NEXT, NEXT2)                                      \
+  if ((K_) < nk) {                                                                    \
+    const int64_t k2 = min((K_) + 2, nk - 1);                                         \
+    if (!kFull) p.load_act(k2, NEXT2);                                                \
+    p.template load_w<kFull>(k2, NEXT2);                                              \
+    __builtin_amdgcn_sched_barrier(0);                                                \
+    if (!kFull) p.store_act(CUR_NEXT, sa[((K_) + 1) % kActStages]);                   \
+    p.store_w(CUR_NEXT, sb[((K_) + 1) & 1], lut);                                     \
+    __builtin_amdgcn_sched_barrier(0);                                                \
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));                                   \
+    wg_barrier();                                                                     \
+  }
+  int64_t kt = 0;
+  for (; kt + 3 <= nk; kt += 3) {
     QGEMM_PRODUCER_STEP(kt, s1, s2)
     QGEMM_PRODUCER_STEP(kt + 1, s2, s0)
     QGEMM_PRODUCER_STEP(kt + 2, s0, s1)
   }
+  QGEMM_PRODUCER_STEP(kt, s1, s2)
+  QGEMM_PRODUCER_STEP(kt + 1, s2, s0)
 #undef QGEMM_PRODUCER_STEP
 }
 
@@ -217,13 +273,15 @@ __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act
                                                 int64_t Kc, QWeight w, const uint16_t *__restrict__ la,
                                                 const uint16_t *__restrict__ lb, int r, float scale,
                                                 uint16_t *__restrict__ out, Codebook cb) {
-  __shared__ __attribute__((aligned(16))) uint16_t sa[2][QBM * QLD];
+  __shared__ __attribute__((aligned(16))) uint16_t sa[kActStages][QBM * 64];
   __shared__ __attribute__((aligned(16))) uint16_t sb[2][QBN * QLD];
   __shared__ float lut[16];
 
   const int tid = threadIdx.x;
   const int64_t m0 = (int64_t)blockIdx.x * QBM, c0 = (int64_t)blockIdx.y * QBN;
   const int64_t nk = (Kc + QBK - 1) / QBK;
+  // full: every row, column and contraction step of the tile is in range and
+  // activation rows are 16-byte aligned
   const bool full = (m0 + QBM <= M) && (c0 + QBN <= Ncols) && (Kc % QBK == 0);
 
   if (tid >= 256) {
@@ -298,17 +356,33 @@ __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] *= scale;
 
+  // full tiles: stages 0 and 1 of the activation ring
+  const int cw = __builtin_amdgcn_readfirstlane(wave);
+  const int64_t dma_row0 = m0 + 64 * cw;
+  const uint32_t dma_lane_off = (uint32_t)(((lane >> 3) * Kc + 8 * ((lane & 7) ^ (lane >> 3))) * 2);
+  if (full) {
+    dma_act(act, Kc, dma_row0, 0, dma_lane_off, sa[0] + 64 * cw * 64);
+    dma_act(act, Kc, dma_row0, min((int64_t)1, nk - 1), dma_lane_off, sa[1] + 64 * cw * 64);
+  }
   __syncthreads();  // level table in LDS
-  __syncthreads();  // stage 0 ready
+  // stage 0's DMA has landed (stage 1's 8 may still be in flight)
+  if (full) __builtin_amdgcn_s_waitcnt(waitcnt_imm(8, 0));
+  wg_barrier();     // stage 0 ready
 
   for (int64_t kt = 0; kt < nk; ++kt) {
-    const uint16_t *A = sa[kt & 1];
+    // Stage k+2 of the activation ring (past the end: the last stage again,
+    // into a buffer nobody reads).  Exactly 8 DMAs per step, so waiting for
+    // at most 8 outstanding before the barrier means stage k+1 has landed.
+    if (full)
+      dma_act(act, Kc, dma_row0, min(kt + 2, nk - 1), dma_lane_off, sa[(kt + 2) % kActStages] + 64 * cw * 64);
+    const uint16_t *A = sa[kt % kActStages];
     const uint16_t *B = sb[kt & 1];
 #pragma unroll
     for (int kk = 0; kk < QBK / 16; ++kk) {
       u32x4 af[4], bf[2];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = *(const u32x4 *)&A[(wm * 128 + i * 32 + l32) * QLD + kk * 16 + 8 * lhi];
+      for (int i = 0; i < 4; ++i)
+        af[i] = *(const u32x4 *)&A[act_off(wm * 128 + i * 32 + l32, 2 * kk + lhi)];
 #pragma unroll
       for (int j = 0; j < 2; ++j) bf[j] = *(const u32x4 *)&B[(wn * 64 + j * 32 + l32) * QLD + kk * 16 + 8 * lhi];
 #pragma unroll
@@ -316,8 +390,17 @@ __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act
 #pragma unroll
         for (int j = 0; j < 2; ++j) acc[i][j] = mfma(af[i], bf[j], acc[i][j]);
     }
-    __syncthreads();
+    // every LDS read of this stage has returned (the MFMAs consumed them), and
+    // this wave's DMA of stage k+1 has landed
+    if (full)
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(8, 0));
+    else
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    wg_barrier();
   }
+  // No LDS-DMA may still be writing when the workgroup's LDS is released; the
+  // wait names dma_lane_off so that its register stays untouched until then.
+  asm volatile("s_waitcnt vmcnt(0)" ::"v"(dma_lane_off) : "memory");
 
   // epilogue: round to bf16 and store
 #pragma unroll
