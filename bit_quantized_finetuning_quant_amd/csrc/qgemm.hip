@@ -37,7 +37,13 @@ namespace qlora {
 
 namespace {
 
-constexpr int QBM = 256, QBN = 128, QBK = 64, QLD = 72;  // QLD: padded LDS row of the weight tile (bf16)
+constexpr int QBM = 256, QBN = 128, QBK = 64;
+// Weight tile in LDS, always with the weight's own contiguous axis (n_in)
+// along LDS rows: forward 128 weight rows x 64 (row length QLD), grad_x 64
+// weight rows x 128 (row length TLD).  Both are padded for conflict-free
+// fragment reads.
+constexpr int QLD = 72, TLD = 144;
+static_assert(128 * QLD == 64 * TLD, "both weight-tile layouts fill the same LDS stage");
 constexpr int kActStages = 3;                            // activation tile LDS ring
 
 typedef __attribute__((address_space(1))) const void gptr_t;
@@ -109,7 +115,7 @@ __device__ __forceinline__ void dma_act(const uint16_t *act, int64_t Kc, int64_t
 
 struct Stage {
   u32x4 a[8];   // activation (register path only): 8 rows x 8 contraction elements
-  u32x4 code;   // weight codes (see Producer)
+  u32x4 code;   // 32 weight codes: one weight row, 32 consecutive n_in positions
   uint32_t q[4];
   float s2[4];
 };
@@ -140,42 +146,24 @@ struct Producer {
     for (int i = 0; i < 8; ++i) *(u32x4 *)&dst[act_off(a_row + 32 * i, chunk)] = s.a[i];
   }
 
-  // Packed weight codes, FP8 constants and group scales of stage kt.
+  // Packed weight codes, FP8 constant and group scale of stage kt.  Each lane
+  // owns one weight row and 32 consecutive n_in positions (half an NF4 block):
+  //   forward: weight rows c0 .. c0+127 (2 lanes a row), n_in = k0 .. k0+63
+  //   grad_x : weight rows k0 .. k0+63 (4 lanes a row), n_in = c0 .. c0+127
   template <bool kFull>
   __device__ __forceinline__ void load_w(int64_t kt, Stage &s) const {
     const int64_t k0 = kt * QBK;
-    if (!kTransW) {
-      // one weight row (an output column), 32 consecutive contraction elements
-      const int64_t n = c0 + (ptid >> 1);
-      if (kFull || n < N) {
-        s.code = *(const u32x4 *)(w.codes + n * (K / 2) + k0 / 2 + 16 * (ptid & 1));
-        const int64_t blk = n * kblk_row + kt;
-        s.q[0] = w.fp8[blk];
-        s.s2[0] = w.s2[blk >> 8];
-      } else {
-        s.code = u32x4{0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
-        s.q[0] = 0u;
-        s.s2[0] = 0.f;
-      }
+    const int64_t n = kTransW ? k0 + (ptid >> 2) : c0 + (ptid >> 1);
+    const int64_t col = kTransW ? c0 + 32 * (ptid & 3) : k0 + 32 * (ptid & 1);
+    if (kFull || (n < N && col < K)) {
+      s.code = *(const u32x4 *)(w.codes + n * (K / 2) + col / 2);
+      const int64_t blk = n * kblk_row + col / kBlock;
+      s.q[0] = w.fp8[blk];
+      s.s2[0] = w.s2[blk >> 8];
     } else {
-      // 4 consecutive weight rows (contraction) x 8 consecutive output columns;
-      // the row group runs fastest across lanes so that the transposed LDS
-      // writes of a wave land in consecutive banks
-      const int64_t kcol = c0 + 8 * (ptid >> 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t n = k0 + 4 * (ptid & 15) + i;
-        if (kFull || (n < N && kcol < K)) {
-          s.code[i] = *(const uint32_t *)(w.codes + n * (K / 2) + kcol / 2);
-          const int64_t blk = n * kblk_row + kcol / kBlock;
-          s.q[i] = w.fp8[blk];
-          s.s2[i] = w.s2[blk >> 8];
-        } else {
-          s.code[i] = 0x77777777u;
-          s.q[i] = 0u;
-          s.s2[i] = 0.f;
-        }
-      }
+      s.code = u32x4{0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
+      s.q[0] = 0u;
+      s.s2[0] = 0.f;
     }
   }
 
@@ -183,42 +171,22 @@ struct Producer {
   // before any of the arithmetic that consumes them.
   __device__ __forceinline__ void store_w(const Stage &s, uint16_t *sb, const float *lut) const {
     float lv[32];
-    if (!kTransW) {
-      // element e = 8 v + j of this lane's 32: nibble j of code word v
+    // element e = 8 v + j of this lane's 32: nibble j of code word v
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
+    for (int v = 0; v < 4; ++v)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) lv[8 * v + j] = lut[(s.code[v] >> (4 * j)) & 15u];
-      __builtin_amdgcn_sched_barrier(0);
-      // q = 0 with s2 = 0 decodes to c1hat = mu; masked rows carry the zero code, so they decode to 0
-      const float ch = decode_constant(s.q[0], s.s2[0], mu);
-      const int row = ptid >> 1, half = ptid & 1;
+      for (int j = 0; j < 8; ++j) lv[8 * v + j] = lut[(s.code[v] >> (4 * j)) & 15u];
+    __builtin_amdgcn_sched_barrier(0);
+    // q = 0 with s2 = 0 decodes to c1hat = mu; masked rows carry the zero code, so they decode to 0
+    const float ch = decode_constant(s.q[0], s.s2[0], mu);
+    uint16_t *dst = kTransW ? &sb[(ptid >> 2) * TLD + 32 * (ptid & 3)] : &sb[(ptid >> 1) * QLD + 32 * (ptid & 1)];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        u32x4 o;
+    for (int v = 0; v < 4; ++v) {
+      u32x4 o;
 #pragma unroll
-        for (int d = 0; d < 4; ++d)
-          o[d] = pack_bf16x2(decode_product(lv[8 * v + 2 * d], ch), decode_product(lv[8 * v + 2 * d + 1], ch));
-        *(u32x4 *)&sb[row * QLD + 32 * half + 8 * v] = o;
-      }
-    } else {
-      // element (row i, column c): nibble c of code word i
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) lv[8 * i + c] = lut[(s.code[i] >> (4 * c)) & 15u];
-      __builtin_amdgcn_sched_barrier(0);
-      float ch[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ch[i] = decode_constant(s.q[i], s.s2[i], mu);
-      const int cg = ptid >> 4, rg = ptid & 15;
-#pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        uint2 o;
-        o.x = pack_bf16x2(decode_product(lv[c], ch[0]), decode_product(lv[8 + c], ch[1]));
-        o.y = pack_bf16x2(decode_product(lv[16 + c], ch[2]), decode_product(lv[24 + c], ch[3]));
-        *(uint2 *)&sb[(8 * cg + c) * QLD + 4 * rg] = o;
-      }
+      for (int d = 0; d < 4; ++d)
+        o[d] = pack_bf16x2(decode_product(lv[8 * v + 2 * d], ch), decode_product(lv[8 * v + 2 * d + 1], ch));
+      *(u32x4 *)&dst[8 * v] = o;
     }
   }
 };
@@ -274,7 +242,7 @@ __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act
                                                 const uint16_t *__restrict__ lb, int r, float scale,
                                                 uint16_t *__restrict__ out, Codebook cb) {
   __shared__ __attribute__((aligned(16))) uint16_t sa[kActStages][QBM * 64];
-  __shared__ __attribute__((aligned(16))) uint16_t sb[2][QBN * QLD];
+  __shared__ __attribute__((aligned(16))) uint16_t sb[2][QBN * QLD];  // = 64 * TLD
   __shared__ float lut[16];
 
   const int tid = threadIdx.x;
@@ -377,18 +345,40 @@ __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act
       dma_act(act, Kc, dma_row0, min(kt + 2, nk - 1), dma_lane_off, sa[(kt + 2) % kActStages] + 64 * cw * 64);
     const uint16_t *A = sa[kt % kActStages];
     const uint16_t *B = sb[kt & 1];
+    u32x4 af[2][4], bf[2][2];
+    auto load_frags = [&](int kk, u32x4 (&a)[4], u32x4 (&b)[2]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) a[i] = *(const u32x4 *)&A[act_off(wm * 128 + i * 32 + l32, 2 * kk + lhi)];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (!kTransW) {
+          b[j] = *(const u32x4 *)&B[(wn * 64 + j * 32 + l32) * QLD + kk * 16 + 8 * lhi];
+        } else {
+          // LDS transpose read (16-lane groups): source lane s of group g
+          // points at weight row 16 kk + 8 (g/2) + s/4 (+4), n_in column
+          // 16 (g%2) + 4 (s%4) of this 32-column sub-tile; lane l then holds
+          // 4 consecutive weight rows of column l%32.
+          const int sl = lane & 15, g = lane >> 4;
+          const int nrow = 16 * kk + 8 * (g >> 1) + (sl >> 2);
+          const int ncol = wn * 64 + j * 32 + 16 * (g & 1) + 4 * (sl & 3);
+          typedef short v4s __attribute__((ext_vector_type(4)));
+          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (v4s __attribute__((address_space(3))) *)(lptr_t *)&B[nrow * TLD + ncol]);
+          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+              (v4s __attribute__((address_space(3))) *)(lptr_t *)&B[(nrow + 4) * TLD + ncol]);
+          const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+          b[j] = u32x4{l2.x, l2.y, h2.x, h2.y};
+        }
+      }
+    };
+    load_frags(0, af[0], bf[0]);
 #pragma unroll
     for (int kk = 0; kk < QBK / 16; ++kk) {
-      u32x4 af[4], bf[2];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        af[i] = *(const u32x4 *)&A[act_off(wm * 128 + i * 32 + l32, 2 * kk + lhi)];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) bf[j] = *(const u32x4 *)&B[(wn * 64 + j * 32 + l32) * QLD + kk * 16 + 8 * lhi];
+      if (kk + 1 < QBK / 16) load_frags(kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma(af[i], bf[j], acc[i][j]);
+        for (int j = 0; j < 2; ++j) acc[i][j] = mfma(af[kk & 1][i], bf[kk & 1][j], acc[i][j]);
     }
     // every LDS read of this stage has returned (the MFMAs consumed them), and
     // this wave's DMA of stage k+1 has landed
