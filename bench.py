@@ -79,7 +79,7 @@ class LinearStep:
         self.gx = torch.empty((T, K), dtype=bf, device="cuda")
         self.ga = torch.empty((r, K), dtype=f32, device="cuda")
         self.gb = torch.empty((N, r), dtype=f32, device="cuda")
-        self.ws = torch.empty(qlora.linear_workspace_bytes(T, N, K, r), dtype=torch.uint8, device="cuda")
+        self.ws = qlora.linear_workspace(T, N, K, r)
         self.qlora = qlora
 
     def __call__(self):
@@ -164,7 +164,7 @@ def extra_measurements(torch, qlora, steps):
     gx = torch.empty((1, K), dtype=torch.bfloat16, device="cuda")
     ga = torch.empty((r, K), dtype=torch.float32, device="cuda")
     gb = torch.empty((N, r), dtype=torch.float32, device="cuda")
-    ws = torch.empty(qlora.linear_workspace_bytes(1, N, K, r), dtype=torch.uint8, device="cuda")
+    ws = qlora.linear_workspace(1, N, K, r)
 
     def gemv():
         for q in weights:

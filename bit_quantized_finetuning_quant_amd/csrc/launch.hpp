@@ -28,10 +28,16 @@ hipError_t launch_dequantize(const uint8_t *codes, const uint8_t *fp8, const flo
 struct LinearPlan {
   int64_t T, N, K;
   int r;
-  int s_u, s_v;       // K-splits of x A^T and dy B
-  int s_ga, s_gb;     // T-splits of grad_A and grad_B
-  size_t off_status, off_u, off_v, off_bt, off_at, off_part, total;
+  size_t off_status, off_u, off_v, off_part, total;
 };
+
+// Adapter-side products (lora.hip).
+enum class LoraKind { kU, kV, kGrad };
+int lora_splits(int64_t tiles, int64_t kc);
+int64_t lora_tiles(int64_t m, int64_t n);
+size_t lora_part_floats(int64_t m, int64_t n, int64_t kc);
+hipError_t launch_lora(LoraKind kind, const uint16_t *P, int64_t ldp, const uint16_t *Q, int64_t ldq, int64_t M,
+                       int64_t Nc, int64_t Kc, float scale, void *out, float *part, hipStream_t st);
 
 // Dequant-fused GEMM: out = scale * la lb^T + act W_op (see qgemm.hip).
 hipError_t launch_qgemm(bool trans_w, const uint16_t *act, int64_t M, int64_t Ncols, int64_t Kc, const QWeight &w,

@@ -1,0 +1,284 @@
+// The adapter-side products of the QLoRA linear layer (gfx950), one kernel
+// family for all four of them.
+//
+// Adapter algebra: W' = W + s.B.A with A [r x n_in], B [n_out x r] (the LoRA
+// formula of the nexusinovation tutorial, section "LoRA: O Padrão Ouro de
+// Eficiência"); only the adapters receive gradients ("qlora" encyclopedia
+// entry, tonho.wtf, section "a ideia").
+//
+//   u      = x A^T        [T x r]      A op: x (rows)          B op: A (rows)
+//   v      = dy B         [T x r]      A op: dy (rows)         B op: B (columns)
+//   grad_A = s v^T x      [r x n_in]   A op: v (columns)       B op: x (columns)
+//   grad_B = s dy^T u     [n_out x r]  A op: dy (columns)      B op: u (columns)
+//
+// C[M x Nc] = scale * sum_k Aop(m, k) Bop(k, n), where an operand is either
+// "row" (its contraction index is contiguous: Aop(m, k) = P[m ld + k]) or
+// "column" (the contraction index strides: Aop(m, k) = P[k ld + m]).  Tiles of
+// both operands are staged in LDS in their natural layout; "column" operands
+// reach the MFMA through LDS transpose reads (ds_read_b64_tr_b16).  The
+// contraction is split over the grid's z dimension; every split writes an
+// fp32 partial tile and a second kernel adds the partials in split order (so
+// the result is deterministic) and writes the scaled output.
+
+#include "common.hpp"
+#include "launch.hpp"
+
+namespace qlora {
+
+namespace {
+
+constexpr int LT = 64;   // output tile (M and N) and contraction step
+constexpr int LLD = 72;  // LDS row length (bf16), padded
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef short v4s __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ u32x4 ld8(const uint16_t *row, int64_t c, int64_t ncols, bool vec) {
+  if (vec && c + 8 <= ncols) return *(const u32x4 *)(row + c);
+  u32x4 v = {0u, 0u, 0u, 0u};
+  for (int i = 0; i < 8; ++i)
+    if (c + i < ncols) v[i >> 1] |= (uint32_t)row[c + i] << (16 * (i & 1));
+  return v;
+}
+
+// Tile rows [r0, r0 + 64) x columns [c0, c0 + 64) of a row-major [nrows x ld]
+// bf16 matrix (columns >= ncols and rows >= nrows read as zero); thread t
+// fetches row t/4, columns 16 (t%4) .. +15.  kFull: the tile is known to be in
+// range and 16-byte aligned, so the loads are unconditional.
+struct TileRegs {
+  u32x4 v[2];
+};
+
+template <bool kFull>
+__device__ __forceinline__ void load_tile(const uint16_t *src, int64_t ld, int64_t nrows, int64_t ncols,
+                                          int64_t r0, int64_t c0, bool vec, int tid, TileRegs &t) {
+  const int64_t row = r0 + (tid >> 2);
+  const int64_t col = c0 + 16 * (tid & 3);
+  if (kFull) {
+    const uint16_t *p = src + row * ld + col;
+    t.v[0] = *(const u32x4 *)p;
+    t.v[1] = *(const u32x4 *)(p + 8);
+    return;
+  }
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+    t.v[h] = (row < nrows) ? ld8(src + row * ld, col + 8 * h, ncols, vec) : u32x4{0u, 0u, 0u, 0u};
+}
+
+__device__ __forceinline__ void store_tile(const TileRegs &t, uint16_t *lds, int tid) {
+#pragma unroll
+  for (int h = 0; h < 2; ++h) *(u32x4 *)&lds[(tid >> 2) * LLD + 16 * (tid & 3) + 8 * h] = t.v[h];
+}
+
+// MFMA operand fragment for output rows/cols [base, base + 32), contraction
+// sub-step kk (16 wide).  kTrans = false: the LDS tile is [out][contraction];
+// kTrans = true: the LDS tile is [contraction][out] and is read transposed
+// (in each 16-lane group, source lane s points at contraction row
+// 16 kk + 8 (g/2) + s/4 (and +4) and output column 16 (g%2) + 4 (s%4); lane l
+// then holds 4 consecutive contraction rows of output column l%32).
+template <bool kTrans>
+__device__ __forceinline__ u32x4 frag(const uint16_t *lds, int base, int kk, int lane) {
+  if (!kTrans) return *(const u32x4 *)&lds[(base + (lane & 31)) * LLD + 16 * kk + 8 * (lane >> 5)];
+  const int s = lane & 15, g = lane >> 4;
+  const int row = 16 * kk + 8 * (g >> 1) + (s >> 2);
+  const int col = base + 16 * (g & 1) + 4 * (s & 3);
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4s __attribute__((address_space(3))) *)(lds_void_t *)&lds[row * LLD + col]);
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((v4s __attribute__((address_space(3))) *)(lds_void_t *)&lds[(row + 4) * LLD + col]);
+  const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+  return u32x4{l2.x, l2.y, h2.x, h2.y};
+}
+
+__host__ __device__ constexpr int64_t cdiv_d(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+constexpr int kGroupSteps = 4;  // contraction steps fetched at once (a group of 256)
+
+template <bool kAT, bool kBT, bool kBf16Out, bool kFull>
+__device__ __forceinline__ void lora_body(const uint16_t *__restrict__ P, int64_t ldp,
+                                          const uint16_t *__restrict__ Q, int64_t ldq, int64_t M, int64_t Nc,
+                                          int64_t kb, int64_t ke, int64_t m0, int64_t n0, uint16_t (*sA)[LT * LLD],
+                                          uint16_t (*sB)[LT * LLD], f32x16 &acc) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const bool vp = (ldp % 8) == 0, vq = (ldq % 8) == 0;
+  // Operand tiles in natural layout: a row operand as [out rows][contraction],
+  // a column operand as [contraction rows][out columns].  A group of four
+  // contraction steps is fetched at once (64 KB per workgroup in flight); the
+  // next group's loads reuse the registers as soon as the current group is in
+  // LDS, so they overlap with its MFMAs.
+  TileRegs ta[kGroupSteps], tb[kGroupSteps];
+  auto fetch = [&](int64_t g0) {
+#pragma unroll
+    for (int st = 0; st < kGroupSteps; ++st) {
+      const int64_t k0 = g0 + LT * st;
+      if (!kAT)
+        load_tile<kFull>(P, ldp, M, ke, m0, k0, vp, tid, ta[st]);
+      else
+        load_tile<kFull>(P, ldp, ke, M, k0, m0, vp, tid, ta[st]);
+      if (!kBT)
+        load_tile<kFull>(Q, ldq, Nc, ke, n0, k0, vq, tid, tb[st]);
+      else
+        load_tile<kFull>(Q, ldq, ke, Nc, k0, n0, vq, tid, tb[st]);
+    }
+  };
+  const int64_t last = kb + ((ke - kb - 1) / (LT * kGroupSteps)) * (LT * kGroupSteps);
+  fetch(kb);
+  for (int64_t g0 = kb; g0 < ke; g0 += LT * kGroupSteps) {
+#pragma unroll
+    for (int st = 0; st < kGroupSteps; ++st) {
+      store_tile(ta[st], sA[st], tid);
+      store_tile(tb[st], sB[st], tid);
+    }
+    __syncthreads();
+    // next group (past the end: the last group again, unused), no branch
+    fetch(min(g0 + LT * kGroupSteps, last));
+#pragma unroll
+    for (int st = 0; st < kGroupSteps; ++st)
+#pragma unroll
+      for (int kk = 0; kk < LT / 16; ++kk) {
+        const u32x4 a = frag<kAT>(sA[st], wm * 32, kk, lane);
+        const u32x4 b = frag<kBT>(sB[st], wn * 32, kk, lane);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), acc, 0, 0, 0);
+      }
+    __syncthreads();
+  }
+}
+
+template <bool kBf16Out>
+__device__ __forceinline__ void emit_out(void *out, int64_t idx, float v) {
+  if (kBf16Out) {
+    __bf16 h = (__bf16)v;
+    ((uint16_t *)out)[idx] = __builtin_bit_cast(uint16_t, h);
+  } else {
+    ((float *)out)[idx] = v;
+  }
+}
+
+template <bool kAT, bool kBT, bool kBf16Out>
+__global__ __launch_bounds__(256) void lora_gemm(const uint16_t *__restrict__ P, int64_t ldp,
+                                                 const uint16_t *__restrict__ Q, int64_t ldq, int64_t M, int64_t Nc,
+                                                 int64_t Kc, int64_t chunk, float scale, void *__restrict__ out,
+                                                 float *__restrict__ part) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[kGroupSteps][LT * LLD];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[kGroupSteps][LT * LLD];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t m0 = (int64_t)blockIdx.x * LT, n0 = (int64_t)blockIdx.y * LT;
+  const int S = gridDim.z, s = blockIdx.z;
+  const int64_t kb = (int64_t)s * chunk, ke = min(Kc, kb + chunk);
+
+  f32x16 acc;
+#pragma unroll
+  for (int q = 0; q < 16; ++q) acc[q] = 0.f;
+  // full: both operand tiles in range and aligned, and the chunk is whole groups
+  const bool full = (m0 + LT <= M) && (n0 + LT <= Nc) && ((ke - kb) % (LT * kGroupSteps) == 0) &&
+                    (ldp % 8 == 0) && (ldq % 8 == 0);
+  if (full)
+    lora_body<kAT, kBT, kBf16Out, true>(P, ldp, Q, ldq, M, Nc, kb, ke, m0, n0, sA, sB, acc);
+  else
+    lora_body<kAT, kBT, kBf16Out, false>(P, ldp, Q, ldq, M, Nc, kb, ke, m0, n0, sA, sB, acc);
+
+  // result element q of this lane: tile row wm*32 + 8(q/4) + 4(lane/32) + q%4, column wn*32 + lane%32
+  const int col = wn * 32 + (lane & 31);
+  if (S == 1) {
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int64_t gm = m0 + wm * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3), gn = n0 + col;
+      if (gm < M && gn < Nc) emit_out<kBf16Out>(out, gm * Nc + gn, acc[q] * scale);
+    }
+    return;
+  }
+  // partial tile, row-major 64 x 64, at part[((tile * S) + s) * 4096]
+  const int64_t tile = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
+  float *mine = part + (tile * S + s) * (LT * LT);
+#pragma unroll
+  for (int q = 0; q < 16; ++q) mine[(wm * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)) * LT + col] = acc[q];
+}
+
+// out = scale * (sum over splits, in split order) of the partial tiles; one
+// thread per 4 consecutive columns of a tile row.
+template <bool kBf16Out>
+__global__ __launch_bounds__(256) void lora_reduce(const float *__restrict__ part, int S, int64_t M, int64_t Nc,
+                                                   int64_t tiles_m, float scale, void *__restrict__ out) {
+  const int64_t quads = cdiv_d(M, LT) * cdiv_d(Nc, LT) * (LT * LT / 4);
+  for (int64_t qd = (int64_t)blockIdx.x * 256 + threadIdx.x; qd < quads; qd += (int64_t)gridDim.x * 256) {
+    const int64_t tile = qd / (LT * LT / 4);
+    const int local = (int)(qd % (LT * LT / 4)) * 4;
+    const int64_t gm = (tile % tiles_m) * LT + local / LT;
+    const int64_t gn = (tile / tiles_m) * LT + local % LT;
+    if (gm >= M || gn >= Nc) continue;
+    const f32x4 *p = (const f32x4 *)(part + tile * S * (LT * LT) + local);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // eight loads in flight at a time; the additions stay in split order
+    for (int k0 = 0; k0 < S; k0 += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) v[k] = (k0 + k < S) ? p[(int64_t)(k0 + k) * (LT * LT / 4)] : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        acc[0] += v[k][0];
+        acc[1] += v[k][1];
+        acc[2] += v[k][2];
+        acc[3] += v[k][3];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (gn + e < Nc) emit_out<kBf16Out>(out, gm * Nc + gn + e, acc[e] * scale);
+  }
+}
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace
+
+// Contraction splits: about 256 workgroups in all, chunks of whole groups.
+static int64_t lora_chunk(int64_t tiles, int64_t kc) {
+  const int64_t grp = LT * kGroupSteps;
+  int64_t s = cdiv(256, tiles);
+  const int64_t max_s = cdiv(kc, grp);
+  if (s > max_s) s = max_s;
+  if (s < 1) s = 1;
+  return cdiv(cdiv(kc, s), grp) * grp;
+}
+
+int lora_splits(int64_t tiles, int64_t kc) { return (int)cdiv(kc, lora_chunk(tiles, kc)); }
+
+int64_t lora_tiles(int64_t m, int64_t n) { return cdiv(m, LT) * cdiv(n, LT); }
+
+size_t lora_part_floats(int64_t m, int64_t n, int64_t kc) {
+  const int64_t tiles = lora_tiles(m, n);
+  const int S = lora_splits(tiles, kc);
+  return S > 1 ? (size_t)tiles * S * LT * LT : 0;
+}
+
+hipError_t launch_lora(LoraKind kind, const uint16_t *P, int64_t ldp, const uint16_t *Q, int64_t ldq, int64_t M,
+                       int64_t Nc, int64_t Kc, float scale, void *out, float *part, hipStream_t st) {
+  const int64_t tiles = lora_tiles(M, Nc);
+  const int64_t chunk = lora_chunk(tiles, Kc);
+  const int S = (int)cdiv(Kc, chunk);
+  const float sc = S == 1 ? scale : 1.0f;  // with splits the scale is applied by the reduction
+  dim3 g((unsigned)cdiv(M, LT), (unsigned)cdiv(Nc, LT), (unsigned)S);
+  switch (kind) {
+    case LoraKind::kU:  // x A^T
+      lora_gemm<false, false, true><<<g, 256, 0, st>>>(P, ldp, Q, ldq, M, Nc, Kc, chunk, sc, out, part);
+      break;
+    case LoraKind::kV:  // dy B
+      lora_gemm<false, true, true><<<g, 256, 0, st>>>(P, ldp, Q, ldq, M, Nc, Kc, chunk, sc, out, part);
+      break;
+    case LoraKind::kGrad:  // v^T x, dy^T u
+      lora_gemm<true, true, false><<<g, 256, 0, st>>>(P, ldp, Q, ldq, M, Nc, Kc, chunk, sc, out, part);
+      break;
+  }
+  if (S > 1) {
+    const int64_t quads = tiles * (LT * LT / 4);
+    int64_t blocks = cdiv(quads, 256);
+    if (blocks > 2048) blocks = 2048;
+    if (kind == LoraKind::kGrad)
+      lora_reduce<false><<<(unsigned)blocks, 256, 0, st>>>(part, S, M, Nc, cdiv(M, LT), scale, out);
+    else
+      lora_reduce<true><<<(unsigned)blocks, 256, 0, st>>>(part, S, M, Nc, cdiv(M, LT), scale, out);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace qlora

@@ -205,6 +205,12 @@ def dequantize(q: NF4Weight, out=None, stream=None):
     return y
 
 
+def linear_workspace(tokens: int, n_out: int, n_in: int, r: int, device="cuda"):
+    """A workspace for the linear calls (reusable by successive calls on one stream)."""
+    torch = _torch()
+    return torch.empty(max(linear_workspace_bytes(tokens, n_out, n_in, r), 1), dtype=torch.uint8, device=device)
+
+
 def linear_fwd(x, q: NF4Weight, A, B, scale: float, y=None, u_out=None, save_u=True, workspace=None,
                stream=None):
     """y = x W_hat^T + scale (x A^T) B^T (bf16); returns (y, u or None)."""
@@ -214,8 +220,7 @@ def linear_fwd(x, q: NF4Weight, A, B, scale: float, y=None, u_out=None, save_u=T
     y = y if y is not None else torch.empty((T, q.n_out), dtype=torch.bfloat16, device=x.device)
     if save_u and u_out is None:
         u_out = torch.empty((T, r), dtype=torch.bfloat16, device=x.device)
-    wsb = linear_workspace_bytes(T, q.n_out, q.n_in, r)
-    ws = workspace if workspace is not None else torch.empty(max(wsb, 1), dtype=torch.uint8, device=x.device)
+    ws = workspace if workspace is not None else linear_workspace(T, q.n_out, q.n_in, r, x.device)
     st = q.struct()
     _check(lib().qlora_linear_fwd(_ptr(x), T, ctypes.byref(st), _ptr(A), _ptr(B), r, float(scale), _ptr(y),
                                   _ptr(u_out), _ptr(ws), ws.numel(), _stream(stream)), "qlora_linear_fwd")
@@ -235,8 +240,7 @@ def linear_bwd(dy, x, q: NF4Weight, A, B, scale: float, u=None, need_grad_x=True
         grad_x = None
     grad_A = grad_A if grad_A is not None else torch.empty((r, q.n_in), dtype=torch.float32, device=dev)
     grad_B = grad_B if grad_B is not None else torch.empty((q.n_out, r), dtype=torch.float32, device=dev)
-    wsb = linear_workspace_bytes(T, q.n_out, q.n_in, r)
-    ws = workspace if workspace is not None else torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    ws = workspace if workspace is not None else linear_workspace(T, q.n_out, q.n_in, r, dev)
     st = q.struct()
     _check(lib().qlora_linear_bwd(_ptr(dy), _ptr(x), T, ctypes.byref(st), _ptr(A), _ptr(B), r, float(scale),
                                   _ptr(u), _ptr(grad_x), _ptr(grad_A), _ptr(grad_B), _ptr(ws), ws.numel(),

@@ -89,7 +89,9 @@ size_t qlora_nf4_bytes(int64_t n_out, int64_t n_in);
 size_t qlora_quantize_workspace_bytes(int64_t n_out, int64_t n_in);
 
 /* Workspace bytes needed by qlora_linear_fwd and qlora_linear_bwd for T
- * tokens, this weight shape and adapter rank r (one size covers both calls). */
+ * tokens, this weight shape and adapter rank r (one size covers both calls).
+ * Its contents need no initialisation; calls that may overlap in time must
+ * not share a workspace.                                                     */
 size_t qlora_linear_workspace_bytes(int64_t T, int64_t n_out, int64_t n_in, int r);
 
 /* The library's 16 NF4 levels (fp32, code k -> out[k]), computed on the host
