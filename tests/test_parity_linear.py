@@ -65,6 +65,17 @@ def test_ragged_multi_tile_shapes(shape):
     _check_case(case)
 
 
+@pytest.mark.parametrize("shape", [(300, 320, 1, 24), (77, 192, 2, 5), (64, 64, 2, 256), (1000, 11008, 1, 64),
+                                   (11008, 4096, 2, 64)])
+def test_few_token_path(shape):
+    """T <= 2 runs the HBM-bound few-token kernels; same bar as the GEMM path."""
+    n_out, n_in, T, r = shape
+    announce(f"linear few-token n_out={n_out} n_in={n_in} T={T} r={r}")
+    case = workloads.custom_case(n_out, n_in, T, r, 16.0, seed=n_out + 3 * T)
+    _check_case(case)
+    _check_case(case, scale=1.5, need_u=False)
+
+
 def test_one_hot_rows_return_decoded_weight_bit_exactly():
     """x rows one-hot with A = 0: y row t is column k_t of W_hat; dy rows one-hot with B = 0:
     grad_x row t is row n_t of W_hat.  A single product is exact in fp32, so this checks the
