@@ -24,24 +24,24 @@ hipError_t launch_quantize(const void *w, bool bf16_src, int64_t numel, uint8_t 
 hipError_t launch_dequantize(const uint8_t *codes, const uint8_t *fp8, const float *s2, const float *mu,
                              int64_t numel, uint16_t *out, const Codebook &cb, hipStream_t st);
 
-// Few-token path (gemv.hip): T <= kGemvMaxT and x of all tokens fits in LDS.
-constexpr int64_t kGemvMaxT = 2;
+// Few-token path (gemv.hip): 1 <= T <= kGemvMaxT.  `part` is fp32 scratch of
+// gemv_part_floats(T, N, K, r) floats.  launch_gemv_fwd with y == nullptr only
+// computes u; launch_gemv_bwd with grad_x == nullptr skips the weight pass.
+constexpr int64_t kGemvMaxT = 4;
 bool gemv_applies(int64_t T, int64_t K);
-int64_t gemv_chunks(int64_t N, int64_t K);
-hipError_t launch_gemv_u(int64_t T, const uint16_t *x, int64_t K, const uint16_t *A, int r, uint16_t *u,
-                         hipStream_t st);
+size_t gemv_part_floats(int64_t T, int64_t N, int64_t K, int r);
 hipError_t launch_gemv_fwd(int64_t T, const uint16_t *x, const QWeight &w, const uint16_t *A, const uint16_t *B,
-                           int r, float scale, uint16_t *y, uint16_t *u, const Codebook &cb, hipStream_t st);
+                           int r, float scale, uint16_t *y, uint16_t *u, float *part, const Codebook &cb,
+                           hipStream_t st);
 hipError_t launch_gemv_bwd(int64_t T, const uint16_t *dy, const uint16_t *x, const QWeight &w, const uint16_t *A,
                            const uint16_t *B, int r, float scale, const uint16_t *u, uint16_t *grad_x,
-                           float *grad_A, float *grad_B, float *gx_part, float *v, const Codebook &cb,
-                           hipStream_t st);
+                           float *grad_A, float *grad_B, float *part, const Codebook &cb, hipStream_t st);
 
 // Workspace plan of the linear calls (byte offsets into the caller's buffer).
 struct LinearPlan {
   int64_t T, N, K;
   int r;
-  size_t off_status, off_u, off_v, off_gx, off_part, total;
+  size_t off_status, off_u, off_v, off_part, total;
 };
 
 // Adapter-side products (lora.hip).

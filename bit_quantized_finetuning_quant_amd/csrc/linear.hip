@@ -90,7 +90,7 @@ LinearPlan plan_linear(int64_t T, int64_t N, int64_t K, int r) {
   const int64_t shapes[4][3] = {{T, r, K}, {T, r, N}, {r, K, T}, {N, r, T}};
   size_t part = 0;
   for (const auto &sh : shapes) part = std::max(part, lora_part_floats(sh[0], sh[1], sh[2]));
-  if (gemv_applies(T, K)) part = std::max(part, (size_t)(gemv_chunks(N, K) * T * K + T * r));
+  if (gemv_applies(T, K)) part = std::max(part, gemv_part_floats(T, N, K, r));
   size_t off = 0;
   p.off_status = off;  // status word (never written by the linear calls)
   off = 256;
@@ -98,8 +98,6 @@ LinearPlan plan_linear(int64_t T, int64_t N, int64_t K, int r) {
   off += align256((size_t)T * r * 2);
   p.off_v = off;
   off += align256((size_t)T * r * 2);
-  p.off_gx = off;  // few-token path: grad_x scratch when the caller passes none
-  off += gemv_applies(T, K) ? align256((size_t)T * K * 2) : 0;
   p.off_part = off;
   off += align256(part * 4);
   p.total = off;
@@ -111,7 +109,7 @@ hipError_t launch_linear_fwd(const LinearPlan &p, const uint16_t *x, const QWeig
                              const Codebook &cb, hipStream_t st) {
   uint16_t *u = u_out ? u_out : (uint16_t *)(ws + p.off_u);
   float *part = (float *)(ws + p.off_part);
-  if (gemv_applies(p.T, p.K)) return launch_gemv_fwd(p.T, x, w, A, B, p.r, scale, y, u, cb, st);
+  if (gemv_applies(p.T, p.K)) return launch_gemv_fwd(p.T, x, w, A, B, p.r, scale, y, u, part, cb, st);
   hipError_t e = launch_lora(LoraKind::kU, x, p.K, A, p.K, p.T, p.r, p.K, 1.0f, u, part, st);
   if (e != hipSuccess) return e;
   TimedLaunch tl;
@@ -129,19 +127,13 @@ hipError_t launch_linear_bwd(const LinearPlan &p, const uint16_t *dy, const uint
   uint16_t *v = (uint16_t *)(ws + p.off_v);
   hipError_t e;
   if (gemv_applies(p.T, p.K)) {
-    if (!u) {
+    if (!u) {  // recompute u = x A^T
       uint16_t *uw = (uint16_t *)(ws + p.off_u);
-      e = launch_gemv_u(p.T, x, p.K, A, p.r, uw, st);
+      e = launch_gemv_fwd(p.T, x, w, A, B, p.r, scale, nullptr, uw, part, cb, st);
       if (e != hipSuccess) return e;
       u = uw;
     }
-    // grad_x is needed by the few-token path's own pass; write it to the partial area's tail when
-    // the caller does not want it
-    const int64_t chunks = gemv_chunks(p.N, p.K);
-    float *gx_part = part;
-    float *vf = part + chunks * p.T * p.K;
-    uint16_t *gx = grad_x ? grad_x : (uint16_t *)(ws + p.off_gx);
-    return launch_gemv_bwd(p.T, dy, x, w, A, B, p.r, scale, u, gx, grad_A, grad_B, gx_part, vf, cb, st);
+    return launch_gemv_bwd(p.T, dy, x, w, A, B, p.r, scale, u, grad_x, grad_A, grad_B, part, cb, st);
   }
   if (!u) {  // recompute u = x A^T
     uint16_t *uw = (uint16_t *)(ws + p.off_u);

@@ -66,14 +66,30 @@ def test_ragged_multi_tile_shapes(shape):
 
 
 @pytest.mark.parametrize("shape", [(300, 320, 1, 24), (77, 192, 2, 5), (64, 64, 2, 256), (1000, 11008, 1, 64),
-                                   (11008, 4096, 2, 64)])
+                                   (11008, 4096, 2, 64), (130, 2112, 3, 13), (515, 4160, 4, 64), (8, 64, 4, 1)])
 def test_few_token_path(shape):
-    """T <= 2 runs the HBM-bound few-token kernels; same bar as the GEMM path."""
+    """T <= 4 runs the HBM-bound few-token kernels; same bar as the GEMM path.  The shapes cover
+    ragged row groups and spans, r not a multiple of 8, and the largest adapter rank."""
     n_out, n_in, T, r = shape
     announce(f"linear few-token n_out={n_out} n_in={n_in} T={T} r={r}")
     case = workloads.custom_case(n_out, n_in, T, r, 16.0, seed=n_out + 3 * T)
     _check_case(case)
     _check_case(case, scale=1.5, need_u=False)
+
+
+@pytest.mark.parametrize("T", [1, 3, 2048 // 16])
+def test_backward_without_grad_x(T):
+    """grad_A and grad_B alone (the first adapted layer needs no grad_x)."""
+    announce(f"linear bwd without grad_x T={T}")
+    case = workloads.custom_case(384, 640, T, 16, 16.0, seed=40 + T)
+    q = qlora.quantize(dev_f32(case.w))
+    x, a, b, dy = dev_bf16(case.x), dev_bf16(case.a), dev_bf16(case.b), dev_bf16(case.dy)
+    gx, ga, gb = qlora.linear_bwd(dy, x, q, a, b, case.scale, need_grad_x=False)
+    assert gx is None
+    wh = oracle.dequantize(oracle.quantize(case.w, case.n_out, case.n_in))
+    _, ga_ref, gb_ref = oracle.backward(case.dy, case.x, wh, case.a, case.b, case.scale)
+    assert normwise_rel(host(ga), ga_ref) <= NORMWISE_TOL
+    assert normwise_rel(host(gb), gb_ref) <= NORMWISE_TOL
 
 
 def test_one_hot_rows_return_decoded_weight_bit_exactly():
