@@ -125,9 +125,13 @@ def padded_tokens_x(rng, tokens: int, n_in: int, seq: int = 512, pad: int = 26) 
     return x
 
 
-def layer65b_cases(tokens: int = 4096, shapes=None):
+def layer65b_cases(tokens: int = 4096, shapes=None, names=None):
+    """The 65B linears (seed 4, one child seed per linear).  `names` keeps only those
+    linears (each keeps its own seed); `shapes` replaces the shape list."""
     seeds = np.random.SeedSequence(4).spawn(len(SHAPES_65B))
     for (name, n, k), ss in zip(shapes or SHAPES_65B, seeds):
+        if names is not None and name not in names:
+            continue
         streams = [np.random.default_rng(s) for s in ss.spawn(5)]
         w = student_t_weight(streams[0], n, k)
         a = _normal(streams[1], (64, k), 0.01)

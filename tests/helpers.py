@@ -4,6 +4,8 @@ import sys
 
 import numpy as np
 
+import oracle
+
 
 def torch_mod():
     import torch
@@ -56,3 +58,22 @@ def normwise_rel(got: np.ndarray, want: np.ndarray) -> float:
 # The bar for floating-point outputs of the linear layer: normwise relative
 # error against the fp64 evaluation on the dequantized weight.
 NORMWISE_TOL = 1e-2
+
+
+def oracle_blocks(flat: np.ndarray, c1: np.ndarray, mu, blocks: np.ndarray) -> np.ndarray:
+    """bf16 bits [len(blocks), 64] of the given NF4 blocks, from the oracle's own quantization."""
+    blocks = np.asarray(blocks, dtype=np.int64)
+    out = np.empty((blocks.size, 64), dtype=np.uint16)
+    order = np.argsort(blocks, kind="stable")
+    sb = blocks[order]
+    groups = sb // 256
+    bounds = np.flatnonzero(np.diff(groups)) + 1
+    for part, idx in zip(np.split(sb, bounds), np.split(order, bounds)):
+        g = int(part[0] // 256)
+        b0, b1 = g * 256, min((g + 1) * 256, c1.size)
+        qg, s2g = oracle.double_quantize(c1[b0:b1], mu)
+        seg = flat[(part[:, None] * 64 + np.arange(64)).reshape(-1)]
+        codes = oracle.nearest_codes(seg, c1[part]).reshape(-1)
+        ref = oracle.NF4Quantized(1, seg.size, oracle.pack_codes(codes, seg.size), qg[part - b0], s2g, mu, c1[part])
+        out[idx] = oracle.dequantize(ref).reshape(-1, 64)
+    return out

@@ -205,3 +205,18 @@ def test_quantized_sizes_and_decode_of_a_c1_weight():
         assert np.array_equal(table[codes[b]], wh.reshape(-1, BLOCK)[b])
     err = oracle.nf4.relative_error(case.w, wh)
     assert 0.05 < err < 0.15  # NF4 on N(0, 0.02): about 0.09 (informational bound)
+
+
+def test_sampled_block_decode_matches_full_dequantization():
+    """The sampled-output tests decode chosen blocks group by group; that must equal the full
+    oracle dequantization at those blocks (ragged last group included)."""
+    from helpers import oracle_blocks
+    rng = np.random.default_rng(12)
+    n_out, n_in = 96, 704  # 1056 blocks: four full groups and a ragged fifth
+    w = (rng.standard_t(5, size=(n_out, n_in)) * 0.02).astype(np.float32)
+    full = oracle.dequantize(oracle.quantize(w, n_out, n_in)).reshape(-1, 64)
+    flat = w.reshape(-1)
+    c1 = oracle.block_absmax(flat)
+    mu = oracle.exact_mean_f32(c1)
+    blocks = np.concatenate([rng.integers(0, full.shape[0], 40), [0, full.shape[0] - 1, 255, 256, 1024]])
+    assert np.array_equal(oracle_blocks(flat, c1, mu, blocks), full[blocks])
