@@ -6,10 +6,17 @@ projection: W 4096 x 4096 in NF4 + FP8 double quantization, r = 64,
 alpha = 16, 2048 tokens (batch 4 x seq 512).  Inputs are synthetic and
 already resident in HBM when the timed region starts.  Prints one JSON line.
 
-Also measured in the same run (field "extra"): the few-token (T = 1) path
-and the bulk dequantization, each rotating over more than 1 GB of distinct
-packed weights so that the 256 MB last-level cache cannot hold them, and
-the quantizer.
+Also measured in the same run (field "extra"), each on synthetic inputs
+generated on the device with the distributions of the tests' workloads:
+  - layers_7b: the seven LLaMA-7B linears (q/k/v/o, gate/up, down), 2048
+    tokens, fwd + bwd through all seven;
+  - layers_65b: the seven LLaMA-65B linears, 4096 tokens, Student-t(5)
+    weights with 0.1% outliers x20 and 5% zero-padding token rows;
+  - bulk_65b: the whole 65B weight set (80 layers x 7 linears) quantized into
+    one packed store in HBM, then streamed back to bf16 layer by layer;
+  - gemv_T1: the few-token path at T = 1 and dequant_bulk, each rotating over
+    more than 1 GB of distinct packed weights so that the 256 MB last-level
+    cache cannot hold them; quantize on one 4096 x 4096 weight.
 
   python bench.py [--gpus 1] [--steps 50] [--warmup 10] [--workload 7b_attn]
                   [--no-cpu-baseline] [--no-extra]
@@ -127,6 +134,140 @@ def rotating_weights(torch, qlora, n_out, n_in, total_bytes):
         ws.append(qlora.quantize(w))
     torch.cuda.synchronize()
     return ws
+
+
+def _bf16_normal(torch, g, shape, std):
+    return torch.empty(shape, dtype=torch.float32, device="cuda").normal_(0.0, std, generator=g).to(torch.bfloat16)
+
+
+def _student_t_weight(torch, g, n, k, out):
+    """0.02 * Student-t(5) (a normal over the root of a chi-square with 5 degrees of freedom, itself a
+    sum of 5 squared normals) with 0.1% of positions scaled by 20, into the fp32 tensor out."""
+    out.normal_(0.0, 1.0, generator=g)
+    chi = torch.zeros_like(out)
+    z = torch.empty_like(out)
+    for _ in range(5):
+        z.normal_(0.0, 1.0, generator=g)
+        chi.addcmul_(z, z)
+    out.div_(torch.sqrt(chi / 5.0)).mul_(0.02)
+    del chi, z
+    flat = out.view(-1)
+    idx = torch.randint(0, flat.numel(), (round(0.001 * flat.numel()),), device="cuda", generator=g)
+    flat[idx] *= 20.0
+
+
+class LayerSet:
+    """fwd + bwd through a list of linears sharing one token count (preallocated)."""
+
+    def __init__(self, torch, qlora, shapes, tokens, weight, pad_rows=False, seed=0):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed)
+        self.steps = []
+        self.flops = 0
+        r = 64
+        w = None
+        for _, n, k in shapes:
+            if w is None or w.shape != (n, k):
+                w = torch.empty((n, k), dtype=torch.float32, device="cuda")
+            weight(g, n, k, w)
+            q = qlora.quantize(w)
+            x = _bf16_normal(torch, g, (tokens, k), 1.0)
+            if pad_rows:  # the last 26 tokens of every 512-token sequence are padding
+                x.view(tokens // 512, 512, k)[:, 512 - 26:] = 0
+            a = _bf16_normal(torch, g, (r, k), 0.01)
+            b = _bf16_normal(torch, g, (n, r), 0.01)
+            dy = _bf16_normal(torch, g, (tokens, n), 1.0)
+            bf, f32 = torch.bfloat16, torch.float32
+            bufs = dict(y=torch.empty((tokens, n), dtype=bf, device="cuda"),
+                        u=torch.empty((tokens, r), dtype=bf, device="cuda"),
+                        gx=torch.empty((tokens, k), dtype=bf, device="cuda"),
+                        ga=torch.empty((r, k), dtype=f32, device="cuda"),
+                        gb=torch.empty((n, r), dtype=f32, device="cuda"))
+            self.steps.append((q, x, a, b, dy, bufs))
+            self.flops += linear_flops(tokens, n, k, r)
+        del w
+        self.ws = qlora.linear_workspace(tokens, max(s[1] for s in shapes), max(s[2] for s in shapes), r)
+        self.qlora = qlora
+        torch.cuda.synchronize()
+
+    def __call__(self):
+        ql = self.qlora
+        for q, x, a, b, dy, o in self.steps:
+            ql.linear_fwd(x, q, a, b, 0.25, y=o["y"], u_out=o["u"], workspace=self.ws)
+            ql.linear_bwd(dy, x, q, a, b, 0.25, u=o["u"], grad_x=o["gx"], grad_A=o["ga"], grad_B=o["gb"],
+                          workspace=self.ws)
+
+
+def extra_layers(torch, qlora, workloads, steps):
+    out = {}
+    normal = lambda g, n, k, w: w.normal_(0.0, 0.02, generator=g)
+    student = lambda g, n, k, w: _student_t_weight(torch, g, n, k, w)
+    for tag, shapes, tokens, weight, pad in (("layers_7b", workloads.SHAPES_7B, 2048, normal, False),
+                                             ("layers_65b", workloads.SHAPES_65B, 4096, student, True)):
+        log(f"extra: {tag} ({len(shapes)} linears, {tokens} tokens)")
+        ls = LayerSet(torch, qlora, shapes, tokens, weight, pad_rows=pad, seed=len(tag))
+        for _ in range(2):
+            ls()
+        n = max(2, steps // 5)
+        t, _ = time_region(torch, ls, n)
+        out[tag] = {"TFLOP/s": ls.flops * n / t / 1e12, "frac_mfma": ls.flops * n / t / 1e12 / PEAK_BF16_TFLOPS,
+                    "ms_per_layer_step": t / n * 1e3, "tokens": tokens, "r": 64, "alpha": 16,
+                    "linears": [list(s) for s in shapes], "flops_per_layer_step": ls.flops, "steps": n}
+        del ls
+        torch.cuda.empty_cache()
+    return out
+
+
+def extra_bulk_65b(torch, qlora, workloads, layers=80):
+    """Quantize the 65B weight set (layers x 7 linears, N(0, 0.02)) into one packed store in HBM, then
+    stream it back to bf16 one layer at a time."""
+    shapes = workloads.SHAPES_65B
+    log(f"extra: bulk_65b ({layers} layers x {len(shapes)} linears)")
+    store = [[qlora.NF4Weight.empty(n, k) for _, n, k in shapes] for _ in range(layers)]
+    params = layers * sum(n * k for _, n, k in shapes)
+    packed = layers * sum(qlora.nf4_bytes(n, k) for _, n, k in shapes)
+    big = max(n * k for _, n, k in shapes)
+    src = torch.empty(big, dtype=torch.float32, device="cuda")
+    wsq = torch.empty(max(qlora.quantize_workspace_bytes(n, k) for _, n, k in shapes), dtype=torch.uint8,
+                      device="cuda")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(65)
+    torch.cuda.synchronize()
+    tq = 0.0
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for layer in store:
+        for (_, n, k), q in zip(shapes, layer):
+            w = src[: n * k].view(n, k)
+            w.normal_(0.0, 0.02, generator=g)
+            e0.record()
+            qlora.quantize(w, out=q, workspace=wsq)
+            e1.record()
+            e1.synchronize()
+            tq += e0.elapsed_time(e1) / 1e3
+    del src
+    layer_elems = sum(n * k for _, n, k in shapes)
+    bf = torch.empty(layer_elems, dtype=torch.bfloat16, device="cuda")
+    views = []
+    off = 0
+    for _, n, k in shapes:
+        views.append(bf[off: off + n * k].view(n, k))
+        off += n * k
+
+    def stream():
+        for layer in store:
+            for q, v in zip(layer, views):
+                qlora.dequantize(q, out=v)
+
+    stream()
+    t, _ = time_region(torch, stream, 2)
+    deq_bytes = 2 * (packed + 2 * params)
+    res = {"params": params, "packed_bytes": packed, "bits_per_param": packed * 8 / params,
+           "quantize_s": tq, "quantize_GB/s": (4 * params + packed) / tq / 1e9,
+           "dequant_stream_GB/s": deq_bytes / t / 1e9, "dequant_frac_hbm": deq_bytes / t / 1e9 / PEAK_HBM_GBS,
+           "dequant_s_per_pass": t / 2, "layers": layers}
+    del store, bf, views
+    torch.cuda.empty_cache()
+    return res
 
 
 def extra_measurements(torch, qlora, steps):
@@ -293,8 +434,11 @@ def main():
         "roofline": roofline,
     }
     if not args.no_extra:
-        log("extra measurements: bulk dequant, T=1 path, quantize")
-        result["extra"] = extra_measurements(torch, qlora, args.steps)
+        log("extra measurements: layer sets, bulk 65B store, bulk dequant, T=1 path, quantize")
+        extra = extra_layers(torch, qlora, workloads, args.steps)
+        extra["bulk_65b"] = extra_bulk_65b(torch, qlora, workloads)
+        extra.update(extra_measurements(torch, qlora, args.steps))
+        result["extra"] = extra
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on host cores")
         result["cpu_baseline"] = cpu_baseline(case)
