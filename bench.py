@@ -63,7 +63,7 @@ def measured_traffic(kernel_tag):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("source_sha") != source_sha("linear.hip"):
+    if fields.get("source_sha") != source_sha("qgemm.hip"):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
@@ -360,14 +360,65 @@ def cpu_baseline(case, budget_s=12.0):
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+class RotatingStep:
+    """The same step, each call on the next of a list of distinct packed weights."""
+
+    def __init__(self, step, weights):
+        self.step, self.weights, self.i = step, weights, 0
+
+    def __call__(self):
+        self.step.q = self.weights[self.i % len(self.weights)]
+        self.i += 1
+        self.step()
+
+
+def roofline_of(timing, T, N, K, r, packed):
+    """Roofline of the dominant main kernel (largest summed time) from the live HIP-event timing.
+    Fused GEMMs count algorithmic flops (MFMA bound); the few-token weight passes count
+    algorithmic bytes (HBM bound): the packed weight with its constants, the activations and
+    adapters read, the outputs written."""
+    units = {
+        "qgemm_fwd": ("mfma", 2 * T * N * K + 2 * T * r * N),
+        "qgemm_dx": ("mfma", 2 * T * N * K + 2 * T * r * K),
+        "gemv_fwd": ("hbm", packed + 2 * T * K + 2 * r * K),
+        "gemv_bwd": ("hbm", packed + 2 * T * N + 2 * r * N + 2 * T * r + 4 * r * N),
+    }
+    live = {k: v for k, v in timing.items() if v[0] > 0}
+    dom = max(live, key=lambda k: live[k][1])
+    n_launch, ms = live[dom]
+    avg_s = ms / n_launch / 1e3
+    bound, per_launch = units[dom]
+    if bound == "mfma":
+        achieved, peak, unit = per_launch / avg_s / 1e12, PEAK_BF16_TFLOPS, "TFLOP/s"
+    else:
+        achieved, peak, unit = per_launch / avg_s / 1e9, PEAK_HBM_GBS, "GB/s"
+    roof = {"bound": bound, "kernel": dom, "achieved": achieved, "peak": peak, "unit": unit,
+            "frac": achieved / peak, "traffic": measured_traffic(dom), "avg_us": avg_s * 1e6,
+            "launches": n_launch, ("flops_per_launch" if bound == "mfma" else "bytes_per_launch"): per_launch}
+    others = {}
+    for k, (n, t) in live.items():
+        if k != dom:
+            b, u = units[k]
+            a = u / (t / n / 1e3)
+            others[k] = {"avg_us": t / n * 1e3, "achieved": a / (1e12 if b == "mfma" else 1e9),
+                         "unit": "TFLOP/s" if b == "mfma" else "GB/s"}
+    roof["other_kernels"] = others
+    return roof
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="7b_attn", choices=["7b_attn"])
+    ap.add_argument("--workload", default="7b_attn", choices=["7b_attn", "7b_attn_T1"],
+                    help="7b_attn: 2048 tokens (the headline); 7b_attn_T1: one token on the few-token "
+                         "path, rotating over more than 1 GB of distinct packed weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="before the steps, copy 256 MiB device to device three times (untimed): the "
+                         "reference kernel that scales the HBM byte counters of a profiled run")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
@@ -380,41 +431,32 @@ def main():
 
     torch.cuda.set_device(0)
     dev_bf16, dev_f32 = dev_helpers(torch)
-    log("generating the 7B projection workload (4096x4096, T=2048, r=64)")
-    case = workloads.attn7b_case(2048)
+    tokens = 2048 if args.workload == "7b_attn" else 1
+    log(f"generating the 7B projection workload (4096x4096, T={tokens}, r=64)")
+    case = workloads.attn7b_case(tokens)
     step = LinearStep(case, torch, qlora, dev_bf16, dev_f32)
+    if tokens == 1:
+        step = RotatingStep(step, rotating_weights(torch, qlora, case.n_out, case.n_in, 1.1e9))
     T, N, K, r = case.tokens, case.n_out, case.n_in, case.r
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    qlora.gemm_timing_read()  # discard
-    qlora.gemm_timing_enable(True)
+    qlora.kernel_timing_read()  # discard
+    qlora.kernel_timing_enable(True)
     elapsed, wall = time_region(torch, step, args.steps)
-    qlora.gemm_timing_enable(False)
-    timing = qlora.gemm_timing_read()
+    qlora.kernel_timing_enable(False)
+    timing = qlora.kernel_timing_read()
     flops = linear_flops(T, N, K, r)
     value = flops * args.steps / elapsed / 1e12
-    log(f"{args.steps} steps: {elapsed * 1e3 / args.steps:.3f} ms/step, {value:.1f} TFLOP/s")
-
-    # dominant kernel: the fused GEMM with the larger total time
-    kernels = {
-        "fwd": ("qgemm_fwd", 2 * T * N * K + 2 * T * r * N),
-        "dx": ("qgemm_dx", 2 * T * N * K + 2 * T * r * K),
-    }
-    dom = max(timing, key=lambda k: timing[k][1])
-    n_launch, ms = timing[dom]
-    avg_s = ms / max(n_launch, 1) / 1e3
-    name, kflops = kernels[dom]
-    achieved = kflops / avg_s / 1e12
-    roofline = {"bound": "mfma", "kernel": name, "achieved": achieved, "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_TFLOPS,
-                "traffic": measured_traffic(name), "avg_us": avg_s * 1e6, "launches": n_launch,
-                "flops_per_launch": kflops}
-    other = "dx" if dom == "fwd" else "fwd"
-    if timing[other][0]:
-        o_avg = timing[other][1] / timing[other][0] / 1e3
-        roofline["other_fused_gemm"] = {"kernel": kernels[other][0], "avg_us": o_avg * 1e6,
-                                        "achieved": kernels[other][1] / o_avg / 1e12}
+    log(f"{args.steps} steps: {elapsed * 1e3 / args.steps:.3f} ms/step, {value:.3f} TFLOP/s")
+    roofline = roofline_of(timing, T, N, K, r, qlora.nf4_bytes(N, K))
 
     result = {
         "metric": "QLoRA linear fwd+bwd TFLOP/s (7B/65B shapes); NF4 dequant GB/s",
@@ -429,11 +471,11 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,0.02) weight, N(0,0.01) adapters, N(0,1) activations)",
-        "config": {"workload": "7b_attn_T2048", "n_out": N, "n_in": K, "tokens": T, "r": r, "alpha": 16,
+        "config": {"workload": f"7b_attn_T{T}", "n_out": N, "n_in": K, "tokens": T, "r": r, "alpha": 16,
                    "flops_per_step": flops, "parallelism": "single GPU"},
         "roofline": roofline,
     }
-    if not args.no_extra:
+    if not args.no_extra and tokens > 1:
         log("extra measurements: layer sets, bulk 65B store, bulk dequant, T=1 path, quantize")
         extra = extra_layers(torch, qlora, workloads, args.steps)
         extra["bulk_65b"] = extra_bulk_65b(torch, qlora, workloads)

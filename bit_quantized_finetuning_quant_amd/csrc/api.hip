@@ -206,11 +206,17 @@ qlora_status qlora_linear_bwd(const uint16_t *dy, const uint16_t *x, int64_t T, 
   return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP;
 }
 
-void qlora_gemm_timing_enable(int enable) { gemm_timing_enable(enable != 0); }
+void qlora_kernel_timing_enable(int enable) { kernel_timing_enable(enable != 0); }
 
-qlora_status qlora_gemm_timing_read(int64_t *fwd_launches, double *fwd_ms, int64_t *dx_launches,
-                                    double *dx_ms) {
-  return gemm_timing_read(fwd_launches, fwd_ms, dx_launches, dx_ms) ? QLORA_OK : QLORA_ERR_HIP;
+qlora_status qlora_kernel_timing_read(int64_t *launches, double *total_ms) {
+  int64_t n[kTimedKinds];
+  double ms[kTimedKinds];
+  const bool ok = kernel_timing_read(n, ms);
+  for (int k = 0; k < kTimedKinds; ++k) {
+    if (launches) launches[k] = n[k];
+    if (total_ms) total_ms[k] = ms[k];
+  }
+  return ok ? QLORA_OK : QLORA_ERR_HIP;
 }
 
 qlora_status qlora_status_read(const void *ws, void *stream) {

@@ -602,8 +602,11 @@ hipError_t gemv_fwd_impl(const uint16_t *x, const QWeight &w, const uint16_t *A,
   const int64_t fblocks = rows ? g.fblocks : 0;
   float *y_part = part, *u_part = part + g.fspans * T * N;
   const size_t lds = (size_t)T * kXStride * 2;
+  TimedLaunch tl;
+  const bool timed = rows && timing_begin(st, tl, kTimedGemvFwd);
   gemv_fwd_main<<<(unsigned)(fblocks + g.ablocks), 256, lds, st>>>(x, T, w, A, r, y_part, u_part, g.fspans, fblocks,
                                                                    cb);
+  if (timed) timing_end(st, tl);
   const int64_t out_rows = rows ? N : 0;
   const unsigned fg = (unsigned)std::max<int64_t>(1, cdiv(out_rows, 64));
   gemv_fwd_finish<T><<<fg, 256, 0, st>>>(y_part, u_part, g.fspans, B, r, scale, out_rows, y, u);
@@ -625,12 +628,15 @@ hipError_t gemv_bwd_impl(const uint16_t *dy, const uint16_t *x, const QWeight &w
     if (e != hipSuccess) return e;
   }
   const unsigned grid = (unsigned)(nf4_wgs + g.bparts);
+  TimedLaunch tl;
+  const bool timed = grad_x && timing_begin(st, tl, kTimedGemvBwd);
   if (T == 1)
     gemv_bwd_main_t1<<<grid, 512, lds, st>>>(dy, w, B, u, r, scale, gx_part, v_part, grad_B, g.bspans, nf4_wgs,
                                              (int)g.groups, (int)g.bsub, cb);
   else
     gemv_bwd_main<T><<<grid, 512, lds, st>>>(dy, w, B, u, r, scale, gx_part, v_part, grad_B, g.bspans, nf4_wgs,
                                              (int)g.groups, (int)g.bsub, cb);
+  if (timed) timing_end(st, tl);
   gemv_bwd_finish<T><<<(unsigned)cdiv(K, 64), 256, 0, st>>>(gx_part, g.chunks, v_part, g.bparts, x, A, r, K, scale,
                                                             grad_x, grad_A);
   return hipGetLastError();

@@ -60,8 +60,16 @@ hipError_t launch_qgemm(bool trans_w, const uint16_t *act, int64_t M, int64_t Nc
 LinearPlan plan_linear(int64_t T, int64_t N, int64_t K, int r);
 
 // Optional event bracketing of the fused GEMM launches (diagnostics).
-void gemm_timing_enable(bool on);
-bool gemm_timing_read(int64_t *fwd_n, double *fwd_ms, int64_t *dx_n, double *dx_ms);
+// Diagnostics: HIP events around the main kernel of each kind (linear.hip).
+enum TimedKind : int { kTimedQgemmFwd = 0, kTimedQgemmDx = 1, kTimedGemvFwd = 2, kTimedGemvBwd = 3, kTimedKinds = 4 };
+struct TimedLaunch {
+  hipEvent_t start, stop;
+  int kind;
+};
+bool timing_begin(hipStream_t st, TimedLaunch &t, int kind);  // false when timing is off
+void timing_end(hipStream_t st, TimedLaunch &t);
+void kernel_timing_enable(bool on);
+bool kernel_timing_read(int64_t *launches, double *ms);  // arrays of kTimedKinds
 
 hipError_t launch_linear_fwd(const LinearPlan &p, const uint16_t *x, const QWeight &w, const uint16_t *A,
                              const uint16_t *B, float scale, uint16_t *y, uint16_t *u_out, char *ws,

@@ -29,23 +29,20 @@ namespace qlora {
 
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// ---- diagnostics: HIP events around the fused GEMM launches
+// ---- diagnostics: HIP events around the main kernel launches
 namespace {
-struct TimedLaunch {
-  hipEvent_t start, stop;
-  bool dx;
-};
 bool g_timing = false;
 std::vector<TimedLaunch> g_timed;
+}  // namespace
 
-bool timing_begin(hipStream_t st, TimedLaunch &t, bool dx) {
+bool timing_begin(hipStream_t st, TimedLaunch &t, int kind) {
   if (!g_timing) return false;
   if (hipEventCreate(&t.start) != hipSuccess) return false;
   if (hipEventCreate(&t.stop) != hipSuccess) {
     (void)hipEventDestroy(t.start);
     return false;
   }
-  t.dx = dx;
+  t.kind = kind;
   (void)hipEventRecord(t.start, st);
   return true;
 }
@@ -54,30 +51,28 @@ void timing_end(hipStream_t st, TimedLaunch &t) {
   (void)hipEventRecord(t.stop, st);
   g_timed.push_back(t);
 }
-}  // namespace
 
-void gemm_timing_enable(bool on) { g_timing = on; }
+void kernel_timing_enable(bool on) { g_timing = on; }
 
-bool gemm_timing_read(int64_t *fwd_n, double *fwd_ms, int64_t *dx_n, double *dx_ms) {
-  int64_t n[2] = {0, 0};
-  double ms[2] = {0.0, 0.0};
+bool kernel_timing_read(int64_t *launches, double *ms) {
+  for (int k = 0; k < kTimedKinds; ++k) {
+    launches[k] = 0;
+    ms[k] = 0.0;
+  }
   bool ok = true;
   for (auto &t : g_timed) {
     float e = 0.f;
     if (hipEventSynchronize(t.stop) != hipSuccess || hipEventElapsedTime(&e, t.start, t.stop) != hipSuccess)
       ok = false;
-    n[t.dx] += 1;
-    ms[t.dx] += e;
+    launches[t.kind] += 1;
+    ms[t.kind] += e;
     (void)hipEventDestroy(t.start);
     (void)hipEventDestroy(t.stop);
   }
   g_timed.clear();
-  if (fwd_n) *fwd_n = n[0];
-  if (fwd_ms) *fwd_ms = ms[0];
-  if (dx_n) *dx_n = n[1];
-  if (dx_ms) *dx_ms = ms[1];
   return ok;
 }
+
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 LinearPlan plan_linear(int64_t T, int64_t N, int64_t K, int r) {
@@ -113,7 +108,7 @@ hipError_t launch_linear_fwd(const LinearPlan &p, const uint16_t *x, const QWeig
   hipError_t e = launch_lora(LoraKind::kU, x, p.K, A, p.K, p.T, p.r, p.K, 1.0f, u, part, st);
   if (e != hipSuccess) return e;
   TimedLaunch tl;
-  const bool timed = timing_begin(st, tl, false);
+  const bool timed = timing_begin(st, tl, kTimedQgemmFwd);
   e = launch_qgemm(false, x, p.T, p.N, p.K, w, u, B, p.r, scale, y, cb, st);
   if (timed) timing_end(st, tl);
   return e != hipSuccess ? e : hipGetLastError();
@@ -146,7 +141,7 @@ hipError_t launch_linear_bwd(const LinearPlan &p, const uint16_t *dy, const uint
   if (e != hipSuccess) return e;
   if (grad_x) {  // grad_x = dy W_hat + s v A
     TimedLaunch tl;
-    const bool timed = timing_begin(st, tl, true);
+    const bool timed = timing_begin(st, tl, kTimedQgemmDx);
     e = launch_qgemm(true, dy, p.T, p.K, p.N, w, v, A, p.r, scale, grad_x, cb, st);
     if (timed) timing_end(st, tl);
     if (e != hipSuccess) return e;

@@ -50,8 +50,8 @@ _SIGNATURES = {
     "qlora_linear_bwd": (ctypes.c_int, [_P, _P, _I64, _P, _P, _P, ctypes.c_int, ctypes.c_float, _P, _P, _P, _P,
                                         _P, _SZ, _P]),
     "qlora_status_read": (ctypes.c_int, [_P, _P]),
-    "qlora_gemm_timing_enable": (None, [ctypes.c_int]),
-    "qlora_gemm_timing_read": (ctypes.c_int, [_P, _P, _P, _P]),
+    "qlora_kernel_timing_enable": (None, [ctypes.c_int]),
+    "qlora_kernel_timing_read": (ctypes.c_int, [_P, _P]),
 }
 
 
@@ -103,17 +103,20 @@ def linear_workspace_bytes(tokens: int, n_out: int, n_in: int, r: int) -> int:
     return int(lib().qlora_linear_workspace_bytes(tokens, n_out, n_in, r))
 
 
-def gemm_timing_enable(on: bool) -> None:
-    """Bracket every fused-GEMM launch with HIP events on its stream (diagnostics)."""
-    lib().qlora_gemm_timing_enable(1 if on else 0)
+TIMED_KINDS = ("qgemm_fwd", "qgemm_dx", "gemv_fwd", "gemv_bwd")
 
 
-def gemm_timing_read():
-    """-> {"fwd": (launches, ms), "dx": (launches, ms)} for the launches timed so far (then cleared)."""
-    fn, fm, dn, dm = ctypes.c_int64(), ctypes.c_double(), ctypes.c_int64(), ctypes.c_double()
-    _check(lib().qlora_gemm_timing_read(ctypes.byref(fn), ctypes.byref(fm), ctypes.byref(dn), ctypes.byref(dm)),
-           "gemm_timing_read")
-    return {"fwd": (fn.value, fm.value), "dx": (dn.value, dm.value)}
+def kernel_timing_enable(on: bool) -> None:
+    """Bracket every main-kernel launch with HIP events on its stream (diagnostics)."""
+    lib().qlora_kernel_timing_enable(1 if on else 0)
+
+
+def kernel_timing_read():
+    """-> {kind: (launches, total ms)} for the launches timed so far (then cleared)."""
+    n = (ctypes.c_int64 * len(TIMED_KINDS))()
+    ms = (ctypes.c_double * len(TIMED_KINDS))()
+    _check(lib().qlora_kernel_timing_read(n, ms), "kernel_timing_read")
+    return {k: (n[i], ms[i]) for i, k in enumerate(TIMED_KINDS)}
 
 
 def nf4_codebook():

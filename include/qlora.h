@@ -155,17 +155,24 @@ qlora_status qlora_linear_bwd(const uint16_t *dy, const uint16_t *x, int64_t T,
 
 /* ---- diagnostics ---------------------------------------------------------- */
 
-/* Kernel timing for benchmarks.  While enabled (non-zero), every launch of the
- * dequant-fused GEMM kernels (forward: x W_hat^T, backward: dy W_hat) is
- * bracketed by two HIP events recorded on the call's stream.  The events are
- * created by the library (no device memory is allocated).  Not thread-safe. */
-void qlora_gemm_timing_enable(int enable);
+/* Kernel timing for benchmarks.  While enabled (non-zero), every launch of
+ * the main kernel of each kind below is bracketed by two HIP events recorded
+ * on the call's stream.  The events are created by the library (no device
+ * memory is allocated).  Not thread-safe: one host thread at a time.        */
+enum {
+  QLORA_TIMED_QGEMM_FWD = 0, /* dequant-fused GEMM, forward: x W_hat^T (+ LoRA)       */
+  QLORA_TIMED_QGEMM_DX = 1,  /* dequant-fused GEMM, grad_x: dy W_hat (+ LoRA)         */
+  QLORA_TIMED_GEMV_FWD = 2,  /* few-token forward, weight pass (T <= 4)                */
+  QLORA_TIMED_GEMV_BWD = 3,  /* few-token backward, weight and adapter pass (T <= 4)   */
+  QLORA_TIMED_KINDS = 4
+};
+void qlora_kernel_timing_enable(int enable);
 
-/* Synchronise the recorded events and return, per kernel, the number of timed
- * launches and their summed duration in milliseconds; then forget them.
- * Any out-pointer may be NULL.                                               */
-qlora_status qlora_gemm_timing_read(int64_t *fwd_launches, double *fwd_ms, int64_t *dx_launches,
-                                    double *dx_ms);
+/* Synchronise the recorded events and write, for each kind k, the number of
+ * timed launches to launches[k] and their summed duration in milliseconds to
+ * total_ms[k] (arrays of QLORA_TIMED_KINDS; either may be NULL); then forget
+ * them.  QLORA_ERR_HIP if an event could not be read.                       */
+qlora_status qlora_kernel_timing_read(int64_t *launches, double *total_ms);
 
 /* Wait for `stream`, then read the status word a previous call left in `ws`:
  * QLORA_OK or QLORA_ERR_NONFINITE (the word is not cleared).                  */
