@@ -241,6 +241,85 @@ __device__ __forceinline__ void producer_loop(const Producer<kTransW> &p, int64_
 #undef QGEMM_PRODUCER_STEP
 }
 
+// The four 16-wide contraction slices of one stage for a consumer wave's
+// 128 x 64 sub-tile: fragments of slice kk+1 are read while slice kk
+// multiplies.
+template <bool kTransW>
+__device__ __forceinline__ void consumer_slices(const uint16_t *A, const uint16_t *B, int wm, int wn, int lane,
+                                                f32x16 (&acc)[4][2]) {
+  const int l32 = lane & 31, lhi = lane >> 5;
+  u32x4 af[2][4], bf[2][2];
+  auto load_frags = [&](int kk, u32x4 (&a)[4], u32x4 (&b)[2]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) a[i] = *(const u32x4 *)&A[act_off(wm * 128 + i * 32 + l32, 2 * kk + lhi)];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      if (!kTransW) {
+        b[j] = *(const u32x4 *)&B[(wn * 64 + j * 32 + l32) * QLD + kk * 16 + 8 * lhi];
+      } else {
+        // LDS transpose read (16-lane groups): source lane s of group g
+        // points at weight row 16 kk + 8 (g/2) + s/4 (+4), n_in column
+        // 16 (g%2) + 4 (s%4) of this 32-column sub-tile; lane l then holds
+        // 4 consecutive weight rows of column l%32.
+        const int sl = lane & 15, g = lane >> 4;
+        const int nrow = 16 * kk + 8 * (g >> 1) + (sl >> 2);
+        const int ncol = wn * 64 + j * 32 + 16 * (g & 1) + 4 * (sl & 3);
+        typedef short v4s __attribute__((ext_vector_type(4)));
+        const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (v4s __attribute__((address_space(3))) *)(lptr_t *)&B[nrow * TLD + ncol]);
+        const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (v4s __attribute__((address_space(3))) *)(lptr_t *)&B[(nrow + 4) * TLD + ncol]);
+        const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+        b[j] = u32x4{l2.x, l2.y, h2.x, h2.y};
+      }
+    }
+  };
+  load_frags(0, af[0], bf[0]);
+#pragma unroll
+  for (int kk = 0; kk < QBK / 16; ++kk) {
+    if (kk + 1 < QBK / 16) load_frags(kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = mfma(af[kk & 1][i], bf[kk & 1][j], acc[i][j]);
+  }
+}
+
+// LoRA term of the output tile, staged through LDS in the same layouts as the
+// main contraction (one 64-wide chunk of the rank r at a time, zero past r):
+// the left factor la [M x r] as an activation tile, the right factor as a
+// weight tile (forward: lb = B [Ncols x r], rows = output columns; grad_x:
+// lb = A [r x Ncols], rows = the rank).  All 512 threads stage with 16-byte
+// loads where the rank allows it.
+template <bool kTransW>
+__device__ __forceinline__ void stage_lora(const uint16_t *la, const uint16_t *lb, int r, int j0, int64_t M,
+                                           int64_t Ncols, int64_t m0, int64_t c0, int tid, uint16_t *sa_dst,
+                                           uint16_t *sb_dst) {
+  const bool vec = (r % 8) == 0;
+  for (int idx = tid; idx < QBM * 8; idx += 512) {  // 256 rows x 8 chunks
+    const int row = idx >> 3, ch = idx & 7;
+    const int64_t grow = m0 + row;
+    const u32x4 v = grow < M ? ld8(la + grow * r, j0 + 8 * ch, r, vec) : u32x4{0u, 0u, 0u, 0u};
+    *(u32x4 *)&sa_dst[act_off(row, ch)] = v;
+  }
+  if (!kTransW) {
+    for (int idx = tid; idx < QBN * 8; idx += 512) {  // 128 output columns x 8 chunks of the rank
+      const int row = idx >> 3, ch = idx & 7;
+      const int64_t col = c0 + row;
+      const u32x4 v = col < Ncols ? ld8(lb + col * r, j0 + 8 * ch, r, vec) : u32x4{0u, 0u, 0u, 0u};
+      *(u32x4 *)&sb_dst[row * QLD + 8 * ch] = v;
+    }
+  } else {
+    const bool cvec = (Ncols % 8) == 0;
+    for (int idx = tid; idx < 64 * 16; idx += 512) {  // 64 rank rows x 16 chunks of 8 columns
+      const int jr = idx >> 4, ch = idx & 15;
+      const int j = j0 + jr;
+      const u32x4 v = j < r ? ld8(lb + (int64_t)j * Ncols, c0 + 8 * ch, Ncols, cvec) : u32x4{0u, 0u, 0u, 0u};
+      *(u32x4 *)&sb_dst[jr * TLD + 8 * ch] = v;
+    }
+  }
+}
+
 template <bool kTransW>
 __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act, int64_t M, int64_t Ncols,
                                                 int64_t Kc, QWeight w, const uint16_t *__restrict__ la,
@@ -256,6 +335,34 @@ __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act
   // full: every row, column and contraction step of the tile is in range and
   // activation rows are 16-byte aligned
   const bool full = (m0 + QBM <= M) && (c0 + QBN <= Ncols) && (Kc % QBK == 0);
+
+  // LoRA term first, scaled: acc = scale * la lb^T, staged chunk by chunk in
+  // buffers the pipeline does not touch before its first barrier (activation
+  // stage 2, weight stage 1); the consumer waves multiply, everyone stages.
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int l32 = lane & 31, lhi = lane >> 5;
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+  for (int j0 = 0; j0 < r; j0 += QBK) {
+    stage_lora<kTransW>(la, lb, r, j0, M, Ncols, m0, c0, tid, sa[2], sb[1]);
+    __syncthreads();
+    if (tid < 256) consumer_slices<kTransW>(sa[2], sb[1], wm, wn, lane, acc);
+    __syncthreads();
+  }
+  if (tid < 256) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] *= scale;
+  }
 
   if (tid >= 256) {
     // ------------------------------------------------------------ producers
@@ -281,53 +388,6 @@ __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act
 
   // -------------------------------------------------------------- consumers
   if (tid < 16) lut[tid] = cb.v[tid];
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int l32 = lane & 31, lhi = lane >> 5;
-  const bool lora_vec = (r % 8) == 0;
-
-  f32x16 acc[4][2];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-
-  // LoRA term first: acc = scale * la lb^T (r zero-padded to a multiple of 16)
-  for (int j0 = 0; j0 < r; j0 += 16) {
-    u32x4 af[4], bf[2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t row = m0 + wm * 128 + i * 32 + l32;
-      af[i] = (row < M) ? ld8(la + row * r, j0 + 8 * lhi, r, lora_vec) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = c0 + wn * 64 + j * 32 + l32;
-      if (!kTransW) {
-        bf[j] = (col < Ncols) ? ld8(lb + col * r, j0 + 8 * lhi, r, lora_vec) : u32x4{0u, 0u, 0u, 0u};
-      } else {
-        // lb is A [r x Ncols]: gather 8 adapter rows of one column
-        u32x4 v = {0u, 0u, 0u, 0u};
-        for (int e = 0; e < 8; ++e) {
-          const int jr = j0 + 8 * lhi + e;
-          if (jr < r && col < Ncols) v[e >> 1] |= (uint32_t)lb[(int64_t)jr * Ncols + col] << (16 * (e & 1));
-        }
-        bf[j] = v;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) acc[i][j] = mfma(af[i], bf[j], acc[i][j]);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] *= scale;
 
   // full tiles: stages 0 and 1 of the activation ring
   const int cw = __builtin_amdgcn_readfirstlane(wave);
@@ -348,43 +408,7 @@ __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act
     // at most 8 outstanding before the barrier means stage k+1 has landed.
     if (full)
       dma_act(act, Kc, dma_row0, min(kt + 2, nk - 1), dma_lane_off, sa[(kt + 2) % kActStages] + 64 * cw * 64);
-    const uint16_t *A = sa[kt % kActStages];
-    const uint16_t *B = sb[kt & 1];
-    u32x4 af[2][4], bf[2][2];
-    auto load_frags = [&](int kk, u32x4 (&a)[4], u32x4 (&b)[2]) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = *(const u32x4 *)&A[act_off(wm * 128 + i * 32 + l32, 2 * kk + lhi)];
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        if (!kTransW) {
-          b[j] = *(const u32x4 *)&B[(wn * 64 + j * 32 + l32) * QLD + kk * 16 + 8 * lhi];
-        } else {
-          // LDS transpose read (16-lane groups): source lane s of group g
-          // points at weight row 16 kk + 8 (g/2) + s/4 (+4), n_in column
-          // 16 (g%2) + 4 (s%4) of this 32-column sub-tile; lane l then holds
-          // 4 consecutive weight rows of column l%32.
-          const int sl = lane & 15, g = lane >> 4;
-          const int nrow = 16 * kk + 8 * (g >> 1) + (sl >> 2);
-          const int ncol = wn * 64 + j * 32 + 16 * (g & 1) + 4 * (sl & 3);
-          typedef short v4s __attribute__((ext_vector_type(4)));
-          const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (v4s __attribute__((address_space(3))) *)(lptr_t *)&B[nrow * TLD + ncol]);
-          const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-              (v4s __attribute__((address_space(3))) *)(lptr_t *)&B[(nrow + 4) * TLD + ncol]);
-          const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
-          b[j] = u32x4{l2.x, l2.y, h2.x, h2.y};
-        }
-      }
-    };
-    load_frags(0, af[0], bf[0]);
-#pragma unroll
-    for (int kk = 0; kk < QBK / 16; ++kk) {
-      if (kk + 1 < QBK / 16) load_frags(kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma(af[kk & 1][i], bf[kk & 1][j], acc[i][j]);
-    }
+    consumer_slices<kTransW>(sa[kt % kActStages], sb[kt & 1], wm, wn, lane, acc);
     // every LDS read of this stage has returned (the MFMAs consumed them), and
     // this wave's DMA of stage k+1 has landed
     if (full)
@@ -397,22 +421,36 @@ __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act
   // wait names dma_lane_off so that its register stays untouched until then.
   asm volatile("s_waitcnt vmcnt(0)" ::"v"(dma_lane_off) : "memory");
 
-  // epilogue: round to bf16 and store
+  // Epilogue through LDS: the tile is rounded to bf16 into [256][136] (the
+  // activation ring's storage), then written out as 16-byte row chunks.  The
+  // barrier (consumers only; the producers have ended and no longer count)
+  // also waits for every consumer's last DMA.
+  __syncthreads();
+  constexpr int OLD = QBN + 8;
+  uint16_t *ot = &sa[0][0];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int64_t col = c0 + wn * 64 + j * 32 + l32;
-      if (col >= Ncols) continue;
+    for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
-        const int64_t row = m0 + wm * 128 + i * 32 + 8 * (q >> 2) + 4 * lhi + (q & 3);
-        if (row < M) {
-          __bf16 h = (__bf16)acc[i][j][q];
-          out[row * Ncols + col] = __builtin_bit_cast(uint16_t, h);
-        }
+        const int row = wm * 128 + i * 32 + 8 * (q >> 2) + 4 * lhi + (q & 3);
+        __bf16 h = (__bf16)acc[i][j][q];
+        ot[row * OLD + wn * 64 + j * 32 + l32] = __builtin_bit_cast(uint16_t, h);
       }
+  __syncthreads();
+  const bool out_vec = (Ncols % 8) == 0;
+  for (int idx = tid; idx < QBM * (QBN / 8); idx += 256) {
+    const int row = idx >> 4, ch = idx & 15;
+    const int64_t grow = m0 + row, gcol = c0 + 8 * ch;
+    if (grow >= M || gcol >= Ncols) continue;
+    const u32x4 v = *(const u32x4 *)&ot[row * OLD + 8 * ch];
+    if (out_vec && gcol + 8 <= Ncols) {
+      *(u32x4 *)&out[grow * Ncols + gcol] = v;
+    } else {
+      for (int e = 0; e < 8 && gcol + e < Ncols; ++e) out[grow * Ncols + gcol + e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
     }
+  }
 }
 
 }  // namespace
