@@ -90,9 +90,11 @@ __device__ __forceinline__ u32x4 frag(const uint16_t *lds, int base, int kk, int
 
 __host__ __device__ constexpr int64_t cdiv_d(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-constexpr int kGroupSteps = 4;  // contraction steps fetched at once (a group of 256)
+// Contraction steps fetched at once: 4 (a group of 256) or, when a split is
+// exactly 512 long, all 8 of it, so that the whole split arrives in one round
+// trip (128 KB per workgroup in flight, 147 KB of LDS).
 
-template <bool kAT, bool kBT, bool kBf16Out, bool kFull>
+template <bool kAT, bool kBT, bool kBf16Out, bool kFull, int kGroupSteps>
 __device__ __forceinline__ void lora_body(const uint16_t *__restrict__ P, int64_t ldp,
                                           const uint16_t *__restrict__ Q, int64_t ldq, int64_t M, int64_t Nc,
                                           int64_t kb, int64_t ke, int64_t m0, int64_t n0, uint16_t (*sA)[LT * LLD],
@@ -101,10 +103,10 @@ __device__ __forceinline__ void lora_body(const uint16_t *__restrict__ P, int64_
   const int wm = wave >> 1, wn = wave & 1;
   const bool vp = (ldp % 8) == 0, vq = (ldq % 8) == 0;
   // Operand tiles in natural layout: a row operand as [out rows][contraction],
-  // a column operand as [contraction rows][out columns].  A group of four
-  // contraction steps is fetched at once (64 KB per workgroup in flight); the
-  // next group's loads reuse the registers as soon as the current group is in
-  // LDS, so they overlap with its MFMAs.
+  // a column operand as [contraction rows][out columns].  A group of
+  // contraction steps is fetched at once; the next group's loads reuse the
+  // registers as soon as the current group is in LDS, so they overlap with its
+  // MFMAs.
   TileRegs ta[kGroupSteps], tb[kGroupSteps];
   auto fetch = [&](int64_t g0) {
 #pragma unroll
@@ -120,7 +122,6 @@ __device__ __forceinline__ void lora_body(const uint16_t *__restrict__ P, int64_
         load_tile<kFull>(Q, ldq, ke, Nc, k0, n0, vq, tid, tb[st]);
     }
   };
-  const int64_t last = kb + ((ke - kb - 1) / (LT * kGroupSteps)) * (LT * kGroupSteps);
   fetch(kb);
   for (int64_t g0 = kb; g0 < ke; g0 += LT * kGroupSteps) {
 #pragma unroll
@@ -129,8 +130,9 @@ __device__ __forceinline__ void lora_body(const uint16_t *__restrict__ P, int64_
       store_tile(tb[st], sB[st], tid);
     }
     __syncthreads();
-    // next group (past the end: the last group again, unused), no branch
-    fetch(min(g0 + LT * kGroupSteps, last));
+    // next group while this one multiplies (a uniform branch: the registers
+    // are next needed by the LDS store above, which waits for them anyway)
+    if (g0 + LT * kGroupSteps < ke) fetch(g0 + LT * kGroupSteps);
 #pragma unroll
     for (int st = 0; st < kGroupSteps; ++st)
 #pragma unroll
@@ -153,7 +155,7 @@ __device__ __forceinline__ void emit_out(void *out, int64_t idx, float v) {
   }
 }
 
-template <bool kAT, bool kBT, bool kBf16Out>
+template <bool kAT, bool kBT, bool kBf16Out, int kGroupSteps>
 __global__ __launch_bounds__(256) void lora_gemm(const uint16_t *__restrict__ P, int64_t ldp,
                                                  const uint16_t *__restrict__ Q, int64_t ldq, int64_t M, int64_t Nc,
                                                  int64_t Kc, int64_t chunk, float scale, void *__restrict__ out,
@@ -173,9 +175,9 @@ __global__ __launch_bounds__(256) void lora_gemm(const uint16_t *__restrict__ P,
   const bool full = (m0 + LT <= M) && (n0 + LT <= Nc) && ((ke - kb) % (LT * kGroupSteps) == 0) &&
                     (ldp % 8 == 0) && (ldq % 8 == 0);
   if (full)
-    lora_body<kAT, kBT, kBf16Out, true>(P, ldp, Q, ldq, M, Nc, kb, ke, m0, n0, sA, sB, acc);
+    lora_body<kAT, kBT, kBf16Out, true, kGroupSteps>(P, ldp, Q, ldq, M, Nc, kb, ke, m0, n0, sA, sB, acc);
   else
-    lora_body<kAT, kBT, kBf16Out, false>(P, ldp, Q, ldq, M, Nc, kb, ke, m0, n0, sA, sB, acc);
+    lora_body<kAT, kBT, kBf16Out, false, kGroupSteps>(P, ldp, Q, ldq, M, Nc, kb, ke, m0, n0, sA, sB, acc);
 
   // result element q of this lane: tile row wm*32 + 8(q/4) + 4(lane/32) + q%4, column wn*32 + lane%32
   const int col = wn * 32 + (lane & 31);
@@ -233,7 +235,7 @@ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Contraction splits: about 256 workgroups in all, chunks of whole groups.
 static int64_t lora_chunk(int64_t tiles, int64_t kc) {
-  const int64_t grp = LT * kGroupSteps;
+  const int64_t grp = LT * 4;
   int64_t s = cdiv(256, tiles);
   const int64_t max_s = cdiv(kc, grp);
   if (s > max_s) s = max_s;
@@ -258,17 +260,24 @@ hipError_t launch_lora(LoraKind kind, const uint16_t *P, int64_t ldp, const uint
   const int S = (int)cdiv(Kc, chunk);
   const float sc = S == 1 ? scale : 1.0f;  // with splits the scale is applied by the reduction
   dim3 g((unsigned)cdiv(M, LT), (unsigned)cdiv(Nc, LT), (unsigned)S);
+  const bool whole = chunk == LT * 8;
+#define QLORA_LORA_LAUNCH(AT, BT, BF)                                                                  \
+  if (whole)                                                                                        \
+    lora_gemm<AT, BT, BF, 8><<<g, 256, 0, st>>>(P, ldp, Q, ldq, M, Nc, Kc, chunk, sc, out, part);   \
+  else                                                                                              \
+    lora_gemm<AT, BT, BF, 4><<<g, 256, 0, st>>>(P, ldp, Q, ldq, M, Nc, Kc, chunk, sc, out, part);
   switch (kind) {
     case LoraKind::kU:  // x A^T
-      lora_gemm<false, false, true><<<g, 256, 0, st>>>(P, ldp, Q, ldq, M, Nc, Kc, chunk, sc, out, part);
+      QLORA_LORA_LAUNCH(false, false, true)
       break;
     case LoraKind::kV:  // dy B
-      lora_gemm<false, true, true><<<g, 256, 0, st>>>(P, ldp, Q, ldq, M, Nc, Kc, chunk, sc, out, part);
+      QLORA_LORA_LAUNCH(false, true, true)
       break;
     case LoraKind::kGrad:  // v^T x, dy^T u
-      lora_gemm<true, true, false><<<g, 256, 0, st>>>(P, ldp, Q, ldq, M, Nc, Kc, chunk, sc, out, part);
+      QLORA_LORA_LAUNCH(true, true, false)
       break;
   }
+#undef QLORA_LORA_LAUNCH
   if (S > 1) {
     const int64_t quads = tiles * (LT * LT / 4);
     int64_t blocks = cdiv(quads, 256);
