@@ -111,11 +111,11 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(
 // range, the chunk whose swizzled position is l % 8).  The per-lane byte
 // offset is loop-invariant and everything else is scalar.
 __device__ __forceinline__ void dma_act(const uint16_t *act, int64_t Kc, int64_t row0, int64_t kt,
-                                        uint32_t lane_off, uint16_t *dst) {
+                                        uint32_t lane_off, uint16_t *dst, int j0 = 0, int nj = 8) {
   const char *base = (const char *)(act + row0 * Kc + kt * QBK);
   const uint32_t l0 = lds_addr(dst);
 #pragma unroll
-  for (int j = 0; j < 8; ++j) dma16(base + (int64_t)(16 * j) * Kc, lane_off, l0 + 8 * j * 64 * 2);
+  for (int j = j0; j < j0 + nj; ++j) dma16(base + (int64_t)(16 * j) * Kc, lane_off, l0 + 8 * j * 64 * 2);
 }
 
 struct Stage {
@@ -244,9 +244,13 @@ __device__ __forceinline__ void producer_loop(const Producer<kTransW> &p, int64_
 // The four 16-wide contraction slices of one stage for a consumer wave's
 // 128 x 64 sub-tile: fragments of slice kk+1 are read while slice kk
 // multiplies.
-template <bool kTransW>
+struct NoHook {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
+template <bool kTransW, typename Hook = NoHook>
 __device__ __forceinline__ void consumer_slices(const uint16_t *A, const uint16_t *B, int wm, int wn, int lane,
-                                                f32x16 (&acc)[4][2]) {
+                                                f32x16 (&acc)[4][2], const Hook &hook = Hook()) {
   const int l32 = lane & 31, lhi = lane >> 5;
   u32x4 af[2][4], bf[2][2];
   auto load_frags = [&](int kk, u32x4 (&a)[4], u32x4 (&b)[2]) {
@@ -278,6 +282,7 @@ __device__ __forceinline__ void consumer_slices(const uint16_t *A, const uint16_
 #pragma unroll
   for (int kk = 0; kk < QBK / 16; ++kk) {
     if (kk + 1 < QBK / 16) load_frags(kk + 1, af[(kk + 1) & 1], bf[(kk + 1) & 1]);
+    hook(kk);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -406,9 +411,12 @@ __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act
     // Stage k+2 of the activation ring (past the end: the last stage again,
     // into a buffer nobody reads).  Exactly 8 DMAs per step, so waiting for
     // at most 8 outstanding before the barrier means stage k+1 has landed.
-    if (full)
-      dma_act(act, Kc, dma_row0, min(kt + 2, nk - 1), dma_lane_off, sa[(kt + 2) % kActStages] + 64 * cw * 64);
-    consumer_slices<kTransW>(sa[kt % kActStages], sb[kt & 1], wm, wn, lane, acc);
+    // the 8 DMAs of stage k+2 are spread over the four slices, two each
+    uint16_t *dma_dst = sa[(kt + 2) % kActStages] + 64 * cw * 64;
+    const int64_t dma_kt = min(kt + 2, nk - 1);
+    consumer_slices<kTransW>(sa[kt % kActStages], sb[kt & 1], wm, wn, lane, acc, [&](int kk) {
+      if (full) dma_act(act, Kc, dma_row0, dma_kt, dma_lane_off, dma_dst, 2 * kk, 2);
+    });
     // every LDS read of this stage has returned (the MFMAs consumed them), and
     // this wave's DMA of stage k+1 has landed
     if (full)
