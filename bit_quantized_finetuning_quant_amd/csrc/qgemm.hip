@@ -409,9 +409,9 @@ __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act
 
   for (int64_t kt = 0; kt < nk; ++kt) {
     // Stage k+2 of the activation ring (past the end: the last stage again,
-    // into a buffer nobody reads).  Exactly 8 DMAs per step, so waiting for
-    // at most 8 outstanding before the barrier means stage k+1 has landed.
-    // the 8 DMAs of stage k+2 are spread over the four slices, two each
+    // into a buffer nobody reads), its 8 DMAs spread over the four slices,
+    // two each.  Exactly 8 DMAs per step, so waiting for at most 8
+    // outstanding before the barrier means stage k+1 has landed.
     uint16_t *dma_dst = sa[(kt + 2) % kActStages] + 64 * cw * 64;
     const int64_t dma_kt = min(kt + 2, nk - 1);
     consumer_slices<kTransW>(sa[kt % kActStages], sb[kt & 1], wm, wn, lane, acc, [&](int kk) {
