@@ -116,8 +116,8 @@ size_t qlora_nf4_bytes(int64_t n_out, int64_t n_in) {
 size_t qlora_quantize_workspace_bytes(int64_t n_out, int64_t n_in) {
   int64_t nb;
   if (qlora_nf4_sizes(n_out, n_in, nullptr, &nb, nullptr) != QLORA_OK) return 0;
-  // status (256 B) + 256 u64 exponent bins (2 KiB) + fp32 block absmax
-  return 256 + 2048 + (size_t)nb * 4;
+  // status (256 B) + exponent bins + fp32 block absmax
+  return 256 + kQuantizeBinBytes + (size_t)nb * 4;
 }
 
 size_t qlora_linear_workspace_bytes(int64_t T, int64_t n_out, int64_t n_in, int r) {
@@ -158,7 +158,7 @@ qlora_status qlora_quantize(const void *w, qlora_dtype w_dtype, const qlora_nf4_
   char *base = (char *)ws;
   hipError_t e = launch_quantize(w, w_dtype == QLORA_BF16, q->n_out * q->n_in, q->codes, q->absmax_fp8,
                                  q->absmax_scale, q->absmax_mean, (uint32_t *)base,
-                                 (unsigned long long *)(base + 256), (float *)(base + 256 + 2048),
+                                 (unsigned long long *)(base + 256), (float *)(base + 256 + kQuantizeBinBytes),
                                  tables().mid, (hipStream_t)stream);
   return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP;
 }

@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void quantize_blocks(const void *__restrict__ 
   if (bad) atomicOr(status, 1u);
   __syncthreads();
   const unsigned long long s = sbins[threadIdx.x];
-  if (s) atomicAdd(&bins[threadIdx.x], s);
+  if (s) atomicAdd(&bins[(blockIdx.x % kBinCopies) * 256 + threadIdx.x], s);
 }
 
 // Exact mean of the block constants.  bins[e] holds the sum of the 24-bit
@@ -130,13 +130,23 @@ __global__ __launch_bounds__(256) void quantize_blocks(const void *__restrict__ 
 // so the exact sum is Z * 2^-149 with Z = sum_e bins[e] << (e - 1).  The mean
 // Z * 2^-149 / n is rounded to the nearest fp32 (ties to even) by long
 // division of Z * 2^64 by n and inspection of the quotient's bits.
-__global__ void mean_from_bins(const unsigned long long *__restrict__ bins, int64_t nblocks,
-                               float *__restrict__ mu) {
-  if (threadIdx.x != 0 || blockIdx.x != 0) return;
+__global__ __launch_bounds__(256) void mean_from_bins(const unsigned long long *__restrict__ bins, int64_t nblocks,
+                                                      float *__restrict__ mu) {
+  // the copies of each bin are added by 256 threads at once (each bin sum stays
+  // below nblocks * 2^24 <= 2^55), then one thread forms the exact quotient
+  __shared__ unsigned long long sb[256];
+  {
+    unsigned long long t = 0;
+#pragma unroll
+    for (int c = 0; c < kBinCopies; ++c) t += bins[c * 256 + threadIdx.x];
+    sb[threadIdx.x] = t;
+  }
+  __syncthreads();
+  if (threadIdx.x != 0) return;
   uint32_t w[12];
   for (int k = 0; k < 12; ++k) w[k] = 0u;
   for (int e = 1; e < 255; ++e) {
-    const unsigned long long v = bins[e];
+    const unsigned long long v = sb[e];
     if (!v) continue;
     const int sh = e - 1 + 64;
     const int wo = sh >> 5, bo = sh & 31;
@@ -270,14 +280,15 @@ hipError_t launch_quantize(const void *w, bool bf16_src, int64_t numel, uint8_t 
   const int64_t nblocks = (numel + kBlock - 1) / kBlock;
   const int64_t ngroups = (nblocks + kGroup - 1) / kGroup;
   const int64_t codes_bytes = (numel + 1) / 2;
-  // status word + padding (64 words) followed by 256 u64 bins = 576 words
-  zero_words<<<3, 256, 0, st>>>(status, 64 + 512);
+  // status word + padding (64 words) followed by the bin copies
+  const int words = 64 + (int)(kQuantizeBinBytes / 4);
+  zero_words<<<(words + 255) / 256, 256, 0, st>>>(status, words);
   const int g = grid_for(nblocks, 32, 8192);
   if (bf16_src)
     quantize_blocks<true><<<g, 256, 0, st>>>(w, numel, nblocks, codes, codes_bytes, c1, bins, status, mid);
   else
     quantize_blocks<false><<<g, 256, 0, st>>>(w, numel, nblocks, codes, codes_bytes, c1, bins, status, mid);
-  mean_from_bins<<<1, 64, 0, st>>>(bins, nblocks, mu);
+  mean_from_bins<<<1, 256, 0, st>>>(bins, nblocks, mu);
   double_quantize<<<(unsigned)ngroups, 256, 0, st>>>(c1, nblocks, mu, fp8, s2);
   return hipGetLastError();
 }

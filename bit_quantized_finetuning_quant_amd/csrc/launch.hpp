@@ -17,6 +17,13 @@ struct QWeight {
   int64_t n_out, n_in;
 };
 
+// Copies of the 256 exponent bins of the quantizer's exact mean: workgroup g
+// adds into copy g % kBinCopies, which keeps the global atomics on any one
+// address few.  Quantize workspace: status (256 B), the bins
+// (kBinCopies x 256 u64), fp32 block absmax.
+constexpr int kBinCopies = 16;
+constexpr size_t kQuantizeBinBytes = (size_t)kBinCopies * 256 * 8;
+
 hipError_t launch_quantize(const void *w, bool bf16_src, int64_t numel, uint8_t *codes, uint8_t *fp8,
                            float *s2, float *mu, uint32_t *status, unsigned long long *bins, float *c1,
                            const Midpoints &mid, hipStream_t st);
