@@ -142,32 +142,57 @@ __global__ __launch_bounds__(256) void mean_from_bins(const unsigned long long *
     sb[threadIdx.x] = t;
   }
   __syncthreads();
+  // Z = sum_e sb[e] << (e - 1), in 32-bit limbs: bin e adds three limbs at
+  // limb offset (e - 1 + 64) / 32 (the 64 extra bits keep the quotient's
+  // fraction); the 64-bit limb sums stay below 2^40, and integer addition in
+  // any order is exact
+  __shared__ unsigned long long limb[12];
+  if (threadIdx.x < 12) limb[threadIdx.x] = 0ull;
+  __syncthreads();
+  {
+    const int e = threadIdx.x;
+    const unsigned long long v = (e >= 1 && e < 255) ? sb[e] : 0ull;
+    if (v) {
+      const int sh = e - 1 + 64;
+      const int wo = sh >> 5, bo = sh & 31;
+      atomicAdd(&limb[wo], (unsigned long long)(uint32_t)(v << bo));
+      atomicAdd(&limb[wo + 1], (unsigned long long)(uint32_t)((v << bo) >> 32));
+      if (bo) atomicAdd(&limb[wo + 2], (unsigned long long)(uint32_t)(v >> (64 - bo)));
+    }
+  }
+  __syncthreads();
   if (threadIdx.x != 0) return;
-  uint32_t w[12];
-  for (int k = 0; k < 12; ++k) w[k] = 0u;
-  for (int e = 1; e < 255; ++e) {
-    const unsigned long long v = sb[e];
-    if (!v) continue;
-    const int sh = e - 1 + 64;
-    const int wo = sh >> 5, bo = sh & 31;
-    const uint32_t add[3] = {(uint32_t)(v << bo), (uint32_t)((v << bo) >> 32),
-                             bo ? (uint32_t)(v >> (64 - bo)) : 0u};
-    uint64_t carry = 0;
-    for (int k = wo; k < 12; ++k) {
-      const uint64_t a = (k - wo < 3) ? add[k - wo] : 0u;
-      const uint64_t s = (uint64_t)w[k] + a + carry;
-      w[k] = (uint32_t)s;
-      carry = s >> 32;
-      if (k - wo >= 2 && carry == 0) break;
+  // limbs and quotient digits live in LDS: they are indexed with run-time
+  // values, which would put a private array in scratch memory
+  __shared__ uint32_t w[12], q[12];
+  {
+    unsigned long long carry = 0;
+    for (int k = 0; k < 12; ++k) {
+      const unsigned long long t = limb[k] + carry;
+      w[k] = (uint32_t)t;
+      carry = t >> 32;
     }
   }
   const uint64_t n = (uint64_t)nblocks;
-  uint32_t q[12];
   uint64_t rem = 0;
+  // base-2^32 long division by n (n < 2^31, rem < n, so cur < n 2^32 < 2^63
+  // and the quotient digit is below 2^32): the fp64 quotient is within one of
+  // the digit (cur exact below 2^53; above, n >= 2^21 bounds the error), and
+  // an exact integer correction makes it the digit
   for (int k = 11; k >= 0; --k) {
     const uint64_t cur = (rem << 32) | w[k];
-    q[k] = (uint32_t)(cur / n);
-    rem = cur % n;
+    int64_t d = (int64_t)((double)cur / (double)n);
+    int64_t r = (int64_t)cur - d * (int64_t)n;
+    while (r < 0) {
+      --d;
+      r += (int64_t)n;
+    }
+    while (r >= (int64_t)n) {
+      ++d;
+      r -= (int64_t)n;
+    }
+    q[k] = (uint32_t)d;
+    rem = (uint64_t)r;
   }
   int top = -1;
   for (int k = 11; k >= 0; --k)
