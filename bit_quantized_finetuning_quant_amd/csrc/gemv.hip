@@ -12,16 +12,17 @@
 // Layout of the work.  A row of the weight is split into 16-byte units of 32
 // codes (half an NF4 block).
 //
-//   gemv_fwd_main    workgroup = (span of 32 units, 64 rows): x W_hat^T on
+//   gemv_fwd_main    workgroup = (span of 8 or 32 units, 64 rows): x W_hat^T on
 //                    v_mfma_f32_16x16x32_bf16 with the tokens padded to 16; a
 //                    lane decodes one unit per step straight into the B operand.
-//                    Extra workgroups do the same for the rows of A (partial u).
+//                    The first workgroups do the same for the rows of A
+//                    (partial u).
 //   gemv_fwd_finish  y = sum of span partials + s u B^T, u = bf16(sum of partials)
 //   gemv_bwd_main    workgroup = (span of 64 units, row chunk): a lane owns one
-//                    unit column and walks groups of eight rows, pairing rows in
+//                    unit column and walks groups of four rows, pairing rows in
 //                    v_dot2 against dy; the eight waves' column sums are added
-//                    through LDS in a fixed tree.  Extra workgroups own rows of
-//                    B: grad_B = s dy^T u and a partial v = dy B.
+//                    through LDS in a fixed tree.  The first workgroups own rows
+//                    of B: grad_B = s dy^T u and a partial v = dy B.
 //   gemv_bwd_finish  per 64 columns: grad_x = sum of chunk partials + s v A,
 //                    grad_A = s v^T x
 // Every sum runs in a fixed order, so results do not depend on scheduling.
@@ -36,13 +37,24 @@ namespace qlora {
 namespace {
 
 constexpr int kSpanUnits = 64;   // backward: units per span (one per lane)
-constexpr int kRowsPerWave = 8;  // backward: rows of one group
+constexpr int kRowsPerWave = 4;  // backward: rows of one group
 constexpr int kBwdWaves = 8;     // waves of a backward workgroup
+constexpr int kBwdThreads = kBwdWaves * 64;
+constexpr int64_t kBwdTargetWaves = 2048;  // backward: waves the row split aims for
 constexpr int kBRows = 64;       // rows of B staged at a time by an adapter workgroup
-constexpr int kFwdUnits = 32;    // forward: units per span
-constexpr int kFwdSteps = kFwdUnits / 4;
-constexpr int kFwdRows = 64;                    // forward: rows per workgroup (16 per wave)
-constexpr int kXStride = kFwdUnits * 32 + 8;    // bf16 per token row of the LDS x tile
+constexpr int kFwdRows = 64;     // forward: rows per workgroup (16 per wave)
+// Forward span (units per workgroup): short spans give small weights enough
+// waves to hide the load latency; large weights have waves to spare and take
+// long spans, which keep the span partials and per-workgroup set-up few.
+constexpr int kFwdUnitsSmall = 8, kFwdUnitsLarge = 32;
+constexpr int64_t kFwdShortSpanWaves = 8192;  // short spans while they give at most this many waves
+template <int kUnits>
+struct FwdShape {
+  static constexpr int kSteps = kUnits / 4;
+  static constexpr int kXStride = kUnits * 32 + 8;  // bf16 per token row of the LDS x tile
+  static constexpr int kASlice = kSteps < 4 ? kSteps : 4;
+  static_assert(kSteps % kASlice == 0, "A rows are read in whole slices");
+};
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -115,22 +127,26 @@ __device__ __forceinline__ f32x4 mfma16(const u32x4 &a, const u32x4 &b, f32x4 c)
 //
 // Workgroup (span, row block): x[:, span columns] is staged in LDS (zero past
 // n_in, so clamped units add nothing); wave w takes rows 64 block + 16 w +
-// 0..15 of the weight, or of A for the workgroups past the weight's (partial
-// u).
+// 0..15 of A (the first workgroups: partial u) or of the weight.  Each wave
+// issues the loads of its rows before x is staged, so the two overlap.
+template <int kSteps>
 struct FwdTile {
-  UnitLoad L[kFwdSteps];
+  UnitLoad L[kSteps];
 };
 
+template <int kSteps>
 __device__ __forceinline__ void fwd_load(const QWeight &w, int64_t n, int64_t unit0, int64_t U, int64_t kblk_row,
-                                         FwdTile &f) {
+                                         FwdTile<kSteps> &f) {
 #pragma unroll
-  for (int st = 0; st < kFwdSteps; ++st) load_unit(w, n, min(unit0 + 4 * st, U - 1), kblk_row, f.L[st]);
+  for (int st = 0; st < kSteps; ++st) load_unit(w, n, min(unit0 + 4 * st, U - 1), kblk_row, f.L[st]);
 }
 
-__device__ __forceinline__ f32x4 fwd_tile(const FwdTile &f, float mu, const float *lut, const uint16_t *xrow) {
+template <int kSteps>
+__device__ __forceinline__ f32x4 fwd_tile(const FwdTile<kSteps> &f, float mu, const float *lut,
+                                          const uint16_t *xrow) {
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int st = 0; st < kFwdSteps; ++st) {
+  for (int st = 0; st < kSteps; ++st) {
     uint32_t wv[16];
     decode_unit(f.L[st].c, decode_constant(f.L[st].q, f.L[st].s2, mu), lut, wv);
 #pragma unroll
@@ -142,6 +158,19 @@ __device__ __forceinline__ f32x4 fwd_tile(const FwdTile &f, float mu, const floa
   return acc;
 }
 
+// Rows of A: the same tile with bf16 values read directly, in slices of at
+// most four steps (16 registers a step).
+template <int kASlice>
+__device__ __forceinline__ void a_load(const uint16_t *A, int64_t K, int64_t n, int64_t unit0, int64_t U, int h,
+                                       u32x4 (&av)[kASlice][4]) {
+#pragma unroll
+  for (int st = 0; st < kASlice; ++st) {
+    const int64_t unit = min(unit0 + 4 * (st + h * kASlice), U - 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) av[st][j] = *(const u32x4 *)(A + n * K + 32 * unit + 8 * j);
+  }
+}
+
 __device__ __forceinline__ void fwd_store(const f32x4 &acc, float *dst, int64_t rows, int64_t row, int T, int g) {
   if (row < rows) {
 #pragma unroll
@@ -150,20 +179,36 @@ __device__ __forceinline__ void fwd_store(const f32x4 &acc, float *dst, int64_t 
   }
 }
 
+template <int kUnits>
 __global__ __launch_bounds__(256) void gemv_fwd_main(const uint16_t *__restrict__ x, int T, QWeight w,
                                                      const uint16_t *__restrict__ A, int r, float *__restrict__ y_part,
-                                                     float *__restrict__ u_part, int64_t spans, int64_t wblocks,
+                                                     float *__restrict__ u_part, int64_t spans, int64_t ablocks,
                                                      Codebook cb) {
+  typedef FwdShape<kUnits> S;
+  constexpr int kSteps = S::kSteps, kXStride = S::kXStride, kASlice = S::kASlice;
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];  // [T][kXStride]
   __shared__ float lut[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  if (tid < 16) lut[tid] = cb.v[tid];
   const int64_t K = w.n_in, N = w.n_out, U = K / 32, kblk_row = K / kBlock;
-  const bool a_rows = (int64_t)blockIdx.x >= wblocks;
-  const int64_t blk = a_rows ? (int64_t)blockIdx.x - wblocks : (int64_t)blockIdx.x;
+  const bool a_rows = (int64_t)blockIdx.x < ablocks;
+  const int64_t blk = a_rows ? (int64_t)blockIdx.x : (int64_t)blockIdx.x - ablocks;
   const int64_t span = blk % spans, p = blk / spans;
-  const int64_t col0 = span * kFwdUnits * 32;
-  constexpr int kChunks = kFwdUnits * 4;  // 16-byte chunks of a token row of the tile
+  const int64_t col0 = span * kUnits * 32;
+  const int rl = lane & 15, g = lane >> 4;
+  const int64_t unit0 = span * kUnits + g;
+  const int64_t row0 = p * kFwdRows + wave * 16, rows = a_rows ? r : N;
+  const bool active = row0 < rows;
+  const int64_t n = min(row0 + rl, rows - 1);
+  FwdTile<kSteps> f;
+  u32x4 av[kASlice][4];
+  if (active) {
+    if (a_rows)
+      a_load<kASlice>(A, K, n, unit0, U, 0, av);
+    else
+      fwd_load(w, n, unit0, U, kblk_row, f);
+  }
+  if (tid < 16) lut[tid] = cb.v[tid];
+  constexpr int kChunks = kUnits * 4;  // 16-byte chunks of a token row of the tile
   for (int i = tid; i < T * kChunks; i += 256) {
     const int t = i / kChunks, c8 = (i % kChunks) * 8;
     u32x4 v = {0u, 0u, 0u, 0u};
@@ -171,75 +216,113 @@ __global__ __launch_bounds__(256) void gemv_fwd_main(const uint16_t *__restrict_
     *(u32x4 *)(xs + t * kXStride + c8) = v;
   }
   __syncthreads();
-  const int rl = lane & 15, g = lane >> 4;
+  if (!active) return;
   const uint16_t *xrow = xs + min(rl, T - 1) * kXStride + 32 * g;
-  const int64_t unit0 = span * kFwdUnits + g;
   if (a_rows) {
-    const int64_t nrow0 = p * kFwdRows + wave * 16;
-    if (nrow0 >= r) return;
-    const int64_t n = min(nrow0 + rl, (int64_t)r - 1);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      u32x4 av[kFwdSteps / 2][4];
+    for (int h = 0; h < kSteps / kASlice; ++h) {
+      if (h > 0) a_load<kASlice>(A, K, n, unit0, U, h, av);
 #pragma unroll
-      for (int st = 0; st < kFwdSteps / 2; ++st) {
-        const int64_t unit = min(unit0 + 4 * (st + h * kFwdSteps / 2), U - 1);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) av[st][j] = *(const u32x4 *)(A + n * K + 32 * unit + 8 * j);
-      }
-#pragma unroll
-      for (int st = 0; st < kFwdSteps / 2; ++st)
+      for (int st = 0; st < kASlice; ++st)
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          const u32x4 xa = *(const u32x4 *)(xrow + 128 * (st + h * kFwdSteps / 2) + 8 * j);
+          const u32x4 xa = *(const u32x4 *)(xrow + 128 * (st + h * kASlice) + 8 * j);
           acc = mfma16(xa, av[st][j], acc);
         }
     }
-    fwd_store(acc, u_part + span * T * r, r, nrow0 + rl, T, g);
+    fwd_store(acc, u_part + span * T * r, r, row0 + rl, T, g);
     return;
   }
-  const int64_t row0 = p * kFwdRows + wave * 16;
-  if (row0 >= N) return;
-  FwdTile f;
-  fwd_load(w, min(row0 + rl, N - 1), unit0, U, kblk_row, f);
   fwd_store(fwd_tile(f, *w.mu, lut, xrow), y_part + span * T * N, N, row0 + rl, T, g);
 }
 
+// Sum of `count` fp32 values p[0], p[stride], ... in index order, fetched
+// kFinBatch at a time with every load of a batch issued before the adds.
+constexpr int kFinBatch = 16;
+
+__device__ __forceinline__ float strided_sum(const float *p, int64_t stride, int64_t count) {
+  float s = 0.f;
+  for (int64_t i0 = 0; i0 < count; i0 += kFinBatch) {
+    float v[kFinBatch];
+#pragma unroll
+    for (int i = 0; i < kFinBatch; ++i) v[i] = p[min(i0 + i, count - 1) * stride];
+#pragma unroll
+    for (int i = 0; i < kFinBatch; ++i) s += i0 + i < count ? v[i] : 0.f;
+  }
+  return s;
+}
+
 // Forward, pass 2: a workgroup per 64 output rows (N may be 0: u only).
-// Quarter q = tid / 64 sums s u B^T over the 8-column chunks q, q + 4, ... of
-// row 64 blockIdx.x + tid % 64 (eight loads in flight); quarter 0 adds the
-// four quarters in order to the span partials.
+// u = bf16(sum of the span partials of u): with E = T r entries, slice sl of
+// S = 256 / E thread groups sums spans sl, sl + S, ... and the slices are
+// added in order.  Thread (q, c) = (tid / 64, tid % 64) owns row
+// n = 64 blockIdx.x + c and its quarter q of the rest: span partials q,
+// q + 4, ... and the 8-wide rank chunks q, q + 4, ... of s u B^T; the four
+// quarters are added in order.  Every load that does not need u is issued
+// before u is reduced, so that one memory round trip covers them.
 template <int T>
 __global__ __launch_bounds__(256) void gemv_fwd_finish(const float *__restrict__ y_part,
                                                        const float *__restrict__ u_part, int64_t spans,
                                                        const uint16_t *__restrict__ B, int r, float scale, int64_t N,
                                                        uint16_t *__restrict__ y, uint16_t *__restrict__ u_out) {
   __shared__ float us[T * 256];
+  __shared__ float tmp[1024];
   __shared__ float red[4][T][64];
   const int tid = threadIdx.x;
-  for (int e = tid; e < T * r; e += 256) {
+  const int q = __builtin_amdgcn_readfirstlane(tid >> 6), c = tid & 63;
+  const int64_t n = (int64_t)blockIdx.x * 64 + c;
+  const int64_t nc = n < N ? n : (N > 0 ? N - 1 : 0);
+  const bool vec = (r & 7) == 0;
+  const int nch = r / 8;
+  const uint16_t *brow = B + nc * r;
+  // first batch of this thread's partials and B chunks
+  constexpr int kYB = kFinBatch / 2;
+  float yp[kYB][T];
+  u32x4 b[8];
+  if (N > 0) {
+#pragma unroll
+    for (int i = 0; i < kYB; ++i)
+#pragma unroll
+      for (int t = 0; t < T; ++t) yp[i][t] = y_part[(min((int64_t)(q + 4 * i), spans - 1) * T + t) * N + nc];
+    if (vec) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) b[i] = *(const u32x4 *)(brow + 8 * min(q + 4 * i, nch - 1));
+    }
+  }
+  const int E = T * r, S = E >= 256 ? 1 : 256 / E;
+  const int64_t per = (spans + S - 1) / S;
+  for (int idx = tid; idx < E * S; idx += 256) {
+    const int e = idx % E, sl = idx / E;
+    const int64_t cnt = max((int64_t)0, min(per, (spans - sl + S - 1) / S));
+    tmp[idx] = strided_sum(u_part + sl * (int64_t)E + e, (int64_t)S * E, cnt);
+  }
+  __syncthreads();
+  for (int e = tid; e < E; e += 256) {
     float s = 0.f;
-#pragma unroll 8
-    for (int64_t sp = 0; sp < spans; ++sp) s += u_part[sp * T * r + e];
+    for (int sl = 0; sl < S; ++sl) s += tmp[sl * E + e];
     const uint16_t h = to_bf16(s);
     us[e] = bf(h);
     if (blockIdx.x == 0) u_out[e] = h;
   }
   if (N == 0) return;
   __syncthreads();
-  const int q = __builtin_amdgcn_readfirstlane(tid >> 6), c = tid & 63;
-  const int64_t n = (int64_t)blockIdx.x * 64 + c;
-  const uint16_t *brow = B + (n < N ? n : N - 1) * r;
-  float lora[T];
+  float ys[T], lora[T];
 #pragma unroll
-  for (int t = 0; t < T; ++t) lora[t] = 0.f;
-  if ((r & 7) == 0) {
-    const int nch = r / 8;
-    for (int c0 = q; c0 < nch; c0 += 32) {
-      u32x4 b[8];
+  for (int t = 0; t < T; ++t) ys[t] = lora[t] = 0.f;
+  for (int64_t s0 = q;; s0 += 4 * kYB) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) b[i] = *(const u32x4 *)(brow + 8 * min(c0 + 4 * i, nch - 1));
+    for (int i = 0; i < kYB; ++i)
+#pragma unroll
+      for (int t = 0; t < T; ++t) ys[t] += s0 + 4 * i < spans ? yp[i][t] : 0.f;
+    if (s0 + 4 * kYB >= spans) break;
+#pragma unroll
+    for (int i = 0; i < kYB; ++i)
+#pragma unroll
+      for (int t = 0; t < T; ++t) yp[i][t] = y_part[(min(s0 + 4 * kYB + 4 * i, spans - 1) * T + t) * N + nc];
+  }
+  if (vec) {
+    for (int c0 = q;; c0 += 32) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int ch = c0 + 4 * i;
@@ -253,38 +336,36 @@ __global__ __launch_bounds__(256) void gemv_fwd_finish(const float *__restrict__
             }
         }
       }
+      if (c0 + 32 >= nch) break;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) b[i] = *(const u32x4 *)(brow + 8 * min(c0 + 32 + 4 * i, nch - 1));
     }
   } else {
     for (int j0 = q; j0 < r; j0 += 32) {
-      float b[8];
+      float bs[8];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) b[i] = bf(brow[min(j0 + 4 * i, r - 1)]);
+      for (int i = 0; i < 8; ++i) bs[i] = bf(brow[min(j0 + 4 * i, r - 1)]);
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const int j = j0 + 4 * i;
         if (j < r) {
 #pragma unroll
-          for (int t = 0; t < T; ++t) lora[t] = __builtin_fmaf(us[t * r + j], b[i], lora[t]);
+          for (int t = 0; t < T; ++t) lora[t] = __builtin_fmaf(us[t * r + j], bs[i], lora[t]);
         }
       }
     }
   }
 #pragma unroll
-  for (int t = 0; t < T; ++t) red[q][t][c] = lora[t];
+  for (int t = 0; t < T; ++t) red[q][t][c] = ys[t] + scale * lora[t];
   __syncthreads();
   if (q == 0 && n < N) {
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      float s = 0.f;
-#pragma unroll 8
-      for (int64_t sp = 0; sp < spans; ++sp) s += y_part[(sp * T + t) * N + n];
-      y[t * N + n] = to_bf16(s + scale * (red[0][t][c] + red[1][t][c] + red[2][t][c] + red[3][t][c]));
-    }
+    for (int t = 0; t < T; ++t) y[t * N + n] = to_bf16(red[0][t][c] + red[1][t][c] + red[2][t][c] + red[3][t][c]);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Eight rows of one unit column with dy of those rows (zero past N).
+// kRowsPerWave rows of one unit column with dy of those rows (zero past N).
 template <int T>
 struct BwdGroup {
   UnitLoad L[kRowsPerWave];
@@ -326,53 +407,56 @@ __device__ __forceinline__ void bwd_group(const BwdGroup<T> &g, float mu, const 
   }
 }
 
-// Backward, pass 1.  Workgroups below nf4_wgs: span = id % spans, chunk =
-// id / spans; wave w takes `groups` groups of eight rows starting at row
-// chunk * 8 groups * 8 + w * groups * 8 and accumulates 32 column sums per
-// token.  The eight waves' sums are added through LDS in a fixed tree
-// (4 + 4, 2 + 2, 1 + 1) and wave 0 writes the chunk's partial.  Later
-// workgroups each own `bsub` blocks of 64 rows of B: grad_B rows and a partial
-// v = dy B over their rows.
+// Backward, pass 1.  The first `awgs` workgroups each own `bsub` blocks of 64
+// rows of B: grad_B rows and a partial v = dy B over their rows.  The others,
+// id = blockIdx.x - awgs: span = id % spans, chunk = id / spans; wave w takes
+// `groups` groups of kRowsPerWave rows starting at row
+// (chunk * kBwdWaves + w) * groups * kRowsPerWave and accumulates 32 column
+// sums per token.  The waves' sums are added through LDS in a fixed tree
+// (halves added pairwise) and wave 0 writes the chunk's partial.
 template <int T>
 __device__ __forceinline__ void bwd_main_body(const uint16_t *__restrict__ dy, QWeight w,
                                               const uint16_t *__restrict__ B, const uint16_t *__restrict__ u, int r,
                                               float scale, float *__restrict__ gx_part, float *__restrict__ v_part,
-                                              float *__restrict__ grad_B, int64_t spans, int64_t nf4_wgs, int groups,
+                                              float *__restrict__ grad_B, int64_t spans, int64_t awgs, int groups,
                                               int bsub, const Codebook &cb, float *smem, float *lut) {
   static_assert(T <= 4, "adapter partials hold at most two entries per thread");
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t K = w.n_in, N = w.n_out;
-  if ((int64_t)blockIdx.x >= nf4_wgs) {
+  if ((int64_t)blockIdx.x < awgs) {
     // adapter rows [bid * bsub * 64, ...) of B, 64 at a time (r <= 256)
-    const int64_t bid = (int64_t)blockIdx.x - nf4_wgs;
+    const int64_t bid = blockIdx.x;
     float *us = smem;                          // [T][r]
     float *ds = us + T * 256;                  // [T][64]
     uint16_t *bt = (uint16_t *)(ds + T * 64);  // [64][r]
     float *vt = (float *)(bt + kBRows * 256);  // [S][E]
-    const int E = T * r, S = E >= 512 ? 1 : 512 / E;
-    for (int e = tid; e < T * r; e += 512) us[e] = bf(u[e]);
-    float vacc[2] = {0.f, 0.f};  // entries idx = tid and tid + 512 of the [S][E] slices
+    const int E = T * r, S = E >= kBwdThreads ? 1 : kBwdThreads / E;
+    for (int e = tid; e < T * r; e += kBwdThreads) us[e] = bf(u[e]);
+    constexpr int kV = (1024 + kBwdThreads - 1) / kBwdThreads;  // E * S <= max(E, threads) <= 1024
+    float vacc[kV];  // entries idx = tid + kBwdThreads k of the [S][E] slices
+#pragma unroll
+    for (int k = 0; k < kV; ++k) vacc[k] = 0.f;
     for (int sb = 0; sb < bsub; ++sb) {
       const int64_t n0 = (bid * bsub + sb) * kBRows;
       if (n0 >= N) break;
       const int rows = (int)min((int64_t)kBRows, N - n0);
       __syncthreads();  // the previous block's tile is no longer read
-      for (int e = tid; e < T * kBRows; e += 512) {
+      for (int e = tid; e < T * kBRows; e += kBwdThreads) {
         const int t = e / kBRows, i = e % kBRows;
         ds[e] = i < rows ? bf(dy[t * N + n0 + i]) : 0.f;
       }
       const uint16_t *bsrc = B + n0 * r;
       const int elems = rows * r;
-      for (int e0 = tid; e0 < elems; e0 += 512 * 8) {
+      for (int e0 = tid; e0 < elems; e0 += kBwdThreads * 8) {
         uint16_t b[8];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) b[i] = bsrc[min(e0 + 512 * i, elems - 1)];
+        for (int i = 0; i < 8; ++i) b[i] = bsrc[min(e0 + kBwdThreads * i, elems - 1)];
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-          if (e0 + 512 * i < elems) bt[e0 + 512 * i] = b[i];
+          if (e0 + kBwdThreads * i < elems) bt[e0 + kBwdThreads * i] = b[i];
       }
       __syncthreads();
-      for (int e = tid; e < elems; e += 512) {
+      for (int e = tid; e < elems; e += kBwdThreads) {
         const int i = e / r, j = e % r;
         float g = 0.f;
 #pragma unroll
@@ -381,8 +465,8 @@ __device__ __forceinline__ void bwd_main_body(const uint16_t *__restrict__ dy, Q
       }
       // slice sl of the threads takes rows sl, sl + S, ... of this block
 #pragma unroll
-      for (int k = 0; k < 2; ++k) {
-        const int idx = tid + 512 * k;
+      for (int k = 0; k < kV; ++k) {
+        const int idx = tid + kBwdThreads * k;
         if (idx < E * S) {
           const int e = idx % E, sl = idx / E, t = e / r, j = e % r;
           float s = vacc[k];
@@ -392,10 +476,10 @@ __device__ __forceinline__ void bwd_main_body(const uint16_t *__restrict__ dy, Q
       }
     }
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
-      if (tid + 512 * k < E * S) vt[tid + 512 * k] = vacc[k];
+    for (int k = 0; k < kV; ++k)
+      if (tid + kBwdThreads * k < E * S) vt[tid + kBwdThreads * k] = vacc[k];
     __syncthreads();
-    for (int e = tid; e < E; e += 512) {
+    for (int e = tid; e < E; e += kBwdThreads) {
       float s = 0.f;
       for (int sl = 0; sl < S; ++sl) s += vt[sl * E + e];
       v_part[bid * E + e] = s;
@@ -406,7 +490,8 @@ __device__ __forceinline__ void bwd_main_body(const uint16_t *__restrict__ dy, Q
   if (tid < 16) lut[tid] = cb.v[tid];
   __syncthreads();
   const int64_t U = K / 32, kblk_row = K / kBlock;
-  const int64_t span = blockIdx.x % spans, chunk = blockIdx.x / spans;
+  const int64_t id = (int64_t)blockIdx.x - awgs;
+  const int64_t span = id % spans, chunk = id / spans;
   const int64_t unit = span * kSpanUnits + lane;
   const bool valid = unit < U;
   const int64_t uc = valid ? unit : U - 1;
@@ -422,9 +507,9 @@ __device__ __forceinline__ void bwd_main_body(const uint16_t *__restrict__ dy, Q
     bwd_load(w, dy, n0, uc, kblk_row, g0);
     bwd_group(g0, mu, lut, acc);
   }
-  // fixed tree over the eight waves; smem holds [4][T * 32][64]
+  // fixed tree over the waves; smem holds [kBwdWaves / 2][T * 32][64]
 #pragma unroll
-  for (int half = 4; half >= 1; half >>= 1) {
+  for (int half = kBwdWaves / 2; half >= 1; half >>= 1) {
     if (wave >= half && wave < 2 * half) {
 #pragma unroll
       for (int t = 0; t < T; ++t)
@@ -452,32 +537,35 @@ __device__ __forceinline__ void bwd_main_body(const uint16_t *__restrict__ dy, Q
 }
 
 // One token fits in 128 registers, which keeps two workgroups on every CU.
-__global__ __launch_bounds__(512, 4) void gemv_bwd_main_t1(const uint16_t *__restrict__ dy, QWeight w,
+__global__ __launch_bounds__(kBwdThreads, 4) void gemv_bwd_main_t1(const uint16_t *__restrict__ dy, QWeight w,
                                                            const uint16_t *__restrict__ B,
                                                            const uint16_t *__restrict__ u, int r, float scale,
                                                            float *__restrict__ gx_part, float *__restrict__ v_part,
-                                                           float *__restrict__ grad_B, int64_t spans, int64_t nf4_wgs,
+                                                           float *__restrict__ grad_B, int64_t spans, int64_t awgs,
                                                            int groups, int bsub, Codebook cb) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ float lut[16];
-  bwd_main_body<1>(dy, w, B, u, r, scale, gx_part, v_part, grad_B, spans, nf4_wgs, groups, bsub, cb, smem, lut);
+  bwd_main_body<1>(dy, w, B, u, r, scale, gx_part, v_part, grad_B, spans, awgs, groups, bsub, cb, smem, lut);
 }
 
 template <int T>
-__global__ __launch_bounds__(512) void gemv_bwd_main(const uint16_t *__restrict__ dy, QWeight w,
+__global__ __launch_bounds__(kBwdThreads) void gemv_bwd_main(const uint16_t *__restrict__ dy, QWeight w,
                                                      const uint16_t *__restrict__ B, const uint16_t *__restrict__ u,
                                                      int r, float scale, float *__restrict__ gx_part,
                                                      float *__restrict__ v_part, float *__restrict__ grad_B,
-                                                     int64_t spans, int64_t nf4_wgs, int groups, int bsub,
+                                                     int64_t spans, int64_t awgs, int groups, int bsub,
                                                      Codebook cb) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ float lut[16];
-  bwd_main_body<T>(dy, w, B, u, r, scale, gx_part, v_part, grad_B, spans, nf4_wgs, groups, bsub, cb, smem, lut);
+  bwd_main_body<T>(dy, w, B, u, r, scale, gx_part, v_part, grad_B, spans, awgs, groups, bsub, cb, smem, lut);
 }
 
 // Backward, pass 2: a workgroup per 64 columns; thread (jg, c) = (tid / 64,
 // tid % 64) takes adapter rows j = jg, jg + 4, ... and chunk partials
-// jg, jg + 4, ...; the four groups are added in order through LDS.
+// jg, jg + 4, ...; the four groups are added in order through LDS.  v is the
+// sum of the adapter workgroups' partials, sliced like u in the forward pass.
+// Every load that does not need v (the first kFinBatch rows of A and chunk
+// partials of each thread, x) is issued before v is reduced.
 template <int T>
 __global__ __launch_bounds__(256) void gemv_bwd_finish(const float *__restrict__ gx_part, int64_t chunks,
                                                        const float *__restrict__ v_part, int64_t vparts,
@@ -488,21 +576,27 @@ __global__ __launch_bounds__(256) void gemv_bwd_finish(const float *__restrict__
   __shared__ float vs[T * 256];
   __shared__ float red[4][T][64];
   const int tid = threadIdx.x;
-  // v = sum of the adapter workgroups' partials: slice sl of the threads sums
-  // partials sl, sl + S, ...; the S slices are then added in order
-  const int E = T * r;
-  const int S = E >= 256 ? 1 : 256 / E;
+  const int jg = __builtin_amdgcn_readfirstlane(tid >> 6), c = tid & 63;
+  const int64_t col = (int64_t)blockIdx.x * 64 + c;
+  const bool valid = col < K;
+  const int64_t cc = valid ? col : K - 1;
+  float xv[T], a[kFinBatch], gv[kFinBatch][T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) xv[t] = bf(x[t * K + cc]);
+#pragma unroll
+  for (int i = 0; i < kFinBatch; ++i) a[i] = bf(A[(int64_t)min(jg + 4 * i, r - 1) * K + cc]);
+  if (grad_x) {
+#pragma unroll
+    for (int i = 0; i < kFinBatch; ++i)
+#pragma unroll
+      for (int t = 0; t < T; ++t) gv[i][t] = gx_part[(min((int64_t)(jg + 4 * i), chunks - 1) * T + t) * K + cc];
+  }
+  const int E = T * r, S = E >= 256 ? 1 : 256 / E;
+  const int64_t per = (vparts + S - 1) / S;
   for (int idx = tid; idx < E * S; idx += 256) {
     const int e = idx % E, sl = idx / E;
-    float s = 0.f;
-    for (int64_t p0 = sl; p0 < vparts; p0 += 8 * S) {
-      float pv[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) pv[i] = v_part[min(p0 + i * S, vparts - 1) * E + e];
-#pragma unroll
-      for (int i = 0; i < 8; ++i) s += p0 + i * S < vparts ? pv[i] : 0.f;
-    }
-    tmp[idx] = s;
+    const int64_t cnt = max((int64_t)0, min(per, (vparts - sl + S - 1) / S));
+    tmp[idx] = strided_sum(v_part + sl * (int64_t)E + e, (int64_t)S * E, cnt);
   }
   __syncthreads();
   for (int e = tid; e < E; e += 256) {
@@ -511,23 +605,12 @@ __global__ __launch_bounds__(256) void gemv_bwd_finish(const float *__restrict__
     vs[e] = s;
   }
   __syncthreads();
-  const int jg = __builtin_amdgcn_readfirstlane(tid >> 6), c = tid & 63;
-  const int64_t col = (int64_t)blockIdx.x * 64 + c;
-  const bool valid = col < K;
-  const int64_t cc = valid ? col : K - 1;
-  float xv[T], g[T], lora[T];
+  float g[T], lora[T];
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
-    xv[t] = bf(x[t * K + cc]);
-    g[t] = 0.f;
-    lora[t] = 0.f;
-  }
-  for (int j0 = jg; j0 < r; j0 += 32) {
-    float a[8];
+  for (int t = 0; t < T; ++t) g[t] = lora[t] = 0.f;
+  for (int j0 = jg;; j0 += 4 * kFinBatch) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) a[i] = bf(A[(int64_t)min(j0 + 4 * i, r - 1) * K + cc]);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
+    for (int i = 0; i < kFinBatch; ++i) {
       const int j = j0 + 4 * i;
       if (j < r) {
         float ga = 0.f;
@@ -539,18 +622,22 @@ __global__ __launch_bounds__(256) void gemv_bwd_finish(const float *__restrict__
         if (valid) grad_A[(int64_t)j * K + col] = scale * ga;
       }
     }
+    if (j0 + 4 * kFinBatch >= r) break;
+#pragma unroll
+    for (int i = 0; i < kFinBatch; ++i) a[i] = bf(A[(int64_t)min(j0 + 4 * kFinBatch + 4 * i, r - 1) * K + cc]);
   }
   if (grad_x) {
-    for (int64_t c0 = jg; c0 < chunks; c0 += 32) {
-      float gv[8][T];
+    for (int64_t c0 = jg;; c0 += 4 * kFinBatch) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int t = 0; t < T; ++t) gv[i][t] = gx_part[(min(c0 + 4 * i, chunks - 1) * T + t) * K + cc];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < kFinBatch; ++i)
 #pragma unroll
         for (int t = 0; t < T; ++t) g[t] += c0 + 4 * i < chunks ? gv[i][t] : 0.f;
+      if (c0 + 4 * kFinBatch >= chunks) break;
+#pragma unroll
+      for (int i = 0; i < kFinBatch; ++i)
+#pragma unroll
+        for (int t = 0; t < T; ++t)
+          gv[i][t] = gx_part[(min(c0 + 4 * kFinBatch + 4 * i, chunks - 1) * T + t) * K + cc];
     }
 #pragma unroll
     for (int t = 0; t < T; ++t) red[jg][t][c] = g[t] + scale * lora[t];
@@ -565,20 +652,22 @@ __global__ __launch_bounds__(256) void gemv_bwd_finish(const float *__restrict__
 
 // Work split of one call.  The backward takes enough rows per wave that the
 // chunk partials stay small next to the weight, and no more than keeps about
-// 2048 waves in flight.
+// kBwdTargetWaves waves in flight.
 struct GemvGeometry {
-  int64_t fspans, fblocks, ablocks;       // forward: spans, weight and A workgroups
+  int64_t funits, fspans, fblocks, ablocks;  // forward: span units, spans, weight and A workgroups
   int64_t bspans, groups, chunks;         // backward weight pass
   int64_t bsub, bparts;                   // backward adapter workgroups
 };
 
 GemvGeometry geometry(int64_t N, int64_t K, int r) {
   GemvGeometry g;
-  g.fspans = cdiv(K / 32, kFwdUnits);
+  const int64_t short_span_waves = cdiv(K / 32, kFwdUnitsSmall) * cdiv(N, 16);
+  g.funits = short_span_waves <= kFwdShortSpanWaves ? kFwdUnitsSmall : kFwdUnitsLarge;
+  g.fspans = cdiv(K / 32, g.funits);
   g.fblocks = g.fspans * cdiv(N, kFwdRows);
   g.ablocks = g.fspans * cdiv(r, kFwdRows);
   g.bspans = cdiv(K / 32, kSpanUnits);
-  const int64_t rows_per_wave = g.bspans * N / 2048;
+  const int64_t rows_per_wave = g.bspans * N / kBwdTargetWaves;
   g.groups = std::max<int64_t>(1, std::min<int64_t>(4, rows_per_wave / kRowsPerWave));
   g.chunks = cdiv(N, kBwdWaves * g.groups * kRowsPerWave);
   const int64_t blocks = cdiv(N, kBRows);
@@ -588,7 +677,7 @@ GemvGeometry geometry(int64_t N, int64_t K, int r) {
 }
 
 size_t bwd_lds_bytes(int T) {
-  const size_t tree = (size_t)4 * T * 32 * 64 * 4;
+  const size_t tree = (size_t)(kBwdWaves / 2) * T * 32 * 64 * 4;
   const size_t adapter = (size_t)T * 256 * 4 + (size_t)T * 64 * 4 + (size_t)kBRows * 256 * 2 + 1024 * 4;
   return std::max(tree, adapter);
 }
@@ -601,11 +690,14 @@ hipError_t gemv_fwd_impl(const uint16_t *x, const QWeight &w, const uint16_t *A,
   const bool rows = y != nullptr;
   const int64_t fblocks = rows ? g.fblocks : 0;
   float *y_part = part, *u_part = part + g.fspans * T * N;
-  const size_t lds = (size_t)T * kXStride * 2;
+  const size_t lds = (size_t)T * (g.funits * 32 + 8) * 2;
+  const unsigned grid = (unsigned)(fblocks + g.ablocks);
   TimedLaunch tl;
   const bool timed = rows && timing_begin(st, tl, kTimedGemvFwd);
-  gemv_fwd_main<<<(unsigned)(fblocks + g.ablocks), 256, lds, st>>>(x, T, w, A, r, y_part, u_part, g.fspans, fblocks,
-                                                                   cb);
+  if (g.funits == kFwdUnitsSmall)
+    gemv_fwd_main<kFwdUnitsSmall><<<grid, 256, lds, st>>>(x, T, w, A, r, y_part, u_part, g.fspans, g.ablocks, cb);
+  else
+    gemv_fwd_main<kFwdUnitsLarge><<<grid, 256, lds, st>>>(x, T, w, A, r, y_part, u_part, g.fspans, g.ablocks, cb);
   if (timed) timing_end(st, tl);
   const int64_t out_rows = rows ? N : 0;
   const unsigned fg = (unsigned)std::max<int64_t>(1, cdiv(out_rows, 64));
@@ -627,14 +719,14 @@ hipError_t gemv_bwd_impl(const uint16_t *dy, const uint16_t *x, const QWeight &w
     const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  const unsigned grid = (unsigned)(nf4_wgs + g.bparts);
+  const unsigned grid = (unsigned)(nf4_wgs + g.bparts);  // adapter workgroups first
   TimedLaunch tl;
   const bool timed = grad_x && timing_begin(st, tl, kTimedGemvBwd);
   if (T == 1)
-    gemv_bwd_main_t1<<<grid, 512, lds, st>>>(dy, w, B, u, r, scale, gx_part, v_part, grad_B, g.bspans, nf4_wgs,
+    gemv_bwd_main_t1<<<grid, kBwdThreads, lds, st>>>(dy, w, B, u, r, scale, gx_part, v_part, grad_B, g.bspans, g.bparts,
                                              (int)g.groups, (int)g.bsub, cb);
   else
-    gemv_bwd_main<T><<<grid, 512, lds, st>>>(dy, w, B, u, r, scale, gx_part, v_part, grad_B, g.bspans, nf4_wgs,
+    gemv_bwd_main<T><<<grid, kBwdThreads, lds, st>>>(dy, w, B, u, r, scale, gx_part, v_part, grad_B, g.bspans, g.bparts,
                                              (int)g.groups, (int)g.bsub, cb);
   if (timed) timing_end(st, tl);
   gemv_bwd_finish<T><<<(unsigned)cdiv(K, 64), 256, 0, st>>>(gx_part, g.chunks, v_part, g.bparts, x, A, r, K, scale,
