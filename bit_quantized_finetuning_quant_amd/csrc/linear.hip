@@ -29,17 +29,28 @@ namespace qlora {
 
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// ---- diagnostics: HIP events around the main kernel launches
+// ---- diagnostics: HIP events around the main kernel launches (events are
+// pooled, so a timed launch costs two event records and no event creation)
 namespace {
 bool g_timing = false;
 std::vector<TimedLaunch> g_timed;
+std::vector<hipEvent_t> g_event_pool;
+
+bool pooled_event(hipEvent_t &e) {
+  if (!g_event_pool.empty()) {
+    e = g_event_pool.back();
+    g_event_pool.pop_back();
+    return true;
+  }
+  return hipEventCreate(&e) == hipSuccess;
+}
 }  // namespace
 
 bool timing_begin(hipStream_t st, TimedLaunch &t, int kind) {
   if (!g_timing) return false;
-  if (hipEventCreate(&t.start) != hipSuccess) return false;
-  if (hipEventCreate(&t.stop) != hipSuccess) {
-    (void)hipEventDestroy(t.start);
+  if (!pooled_event(t.start)) return false;
+  if (!pooled_event(t.stop)) {
+    g_event_pool.push_back(t.start);
     return false;
   }
   t.kind = kind;
@@ -66,8 +77,8 @@ bool kernel_timing_read(int64_t *launches, double *ms) {
       ok = false;
     launches[t.kind] += 1;
     ms[t.kind] += e;
-    (void)hipEventDestroy(t.start);
-    (void)hipEventDestroy(t.stop);
+    g_event_pool.push_back(t.start);
+    g_event_pool.push_back(t.stop);
   }
   g_timed.clear();
   return ok;
