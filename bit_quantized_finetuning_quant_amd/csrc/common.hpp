@@ -65,6 +65,60 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, v);
 }
 
+// Decode without a memory lookup.  The 16 decoded values of one block,
+// t[k] = bf16_rne(fl32(CB[k] * c1hat)), are built once per block in registers
+// as byte tables: lo[j] holds the low bytes of t[4j .. 4j+3], hi[j] the high
+// bytes.  A code then selects its two bytes with v_perm_b32 (which picks
+// bytes 0..7 of the 64-bit pair {S0, S1}, S1 the low word): one permute
+// over each half of a table and a per-byte select on the code's bit 3.
+// Every decoded value is computed exactly as in the lookup form, so the two
+// are bit-identical.
+struct DecodeTable {
+  uint32_t lo[4], hi[4];
+};
+
+__device__ __forceinline__ DecodeTable decode_table(const Codebook &cb, float c1hat) {
+  uint32_t p[8];  // p[m] = t[2m] | t[2m+1] << 16
+#pragma unroll
+  for (int m = 0; m < 8; ++m)
+    p[m] = pack_bf16x2(decode_product(cb.v[2 * m], c1hat), decode_product(cb.v[2 * m + 1], c1hat));
+  DecodeTable t;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    t.lo[j] = __builtin_amdgcn_perm(p[2 * j + 1], p[2 * j], 0x06040200u);
+    t.hi[j] = __builtin_amdgcn_perm(p[2 * j + 1], p[2 * j], 0x07050301u);
+  }
+  return t;
+}
+
+// Byte b of the result is byte (code_b) of a 16-byte table, for four codes
+// given as the bytes of sel (low 3 bits) and mask (0xFF where the code's bit 3
+// is set).
+__device__ __forceinline__ uint32_t table_bytes(const uint32_t (&tb)[4], uint32_t sel, uint32_t mask) {
+  const uint32_t a = __builtin_amdgcn_perm(tb[1], tb[0], sel), b = __builtin_amdgcn_perm(tb[3], tb[2], sel);
+  return (b & mask) | (a & ~mask);
+}
+
+// One word of 8 codes (low nibble first) -> 4 words of bf16 pairs; word d
+// holds element 2d in its low half and element 2d + 1 in its high half.
+__device__ __forceinline__ void decode_word(uint32_t c, const DecodeTable &t, uint32_t (&o)[4]) {
+  const uint32_t c4 = c >> 4;
+  // bytes of c: even codes n0, n2, n4, n6 in bits 0..3; bytes of c4: odd codes
+  const uint32_t se = c & 0x07070707u, so = c4 & 0x07070707u;
+  const uint32_t xe = c & 0x08080808u, xo = c4 & 0x08080808u;
+  const uint32_t me = (xe << 5) - (xe >> 3), mo = (xo << 5) - (xo >> 3);  // 0x08 -> 0xFF per byte
+  const uint32_t le = table_bytes(t.lo, se, me), he = table_bytes(t.hi, se, me);
+  const uint32_t lq = table_bytes(t.lo, so, mo), hq = table_bytes(t.hi, so, mo);
+  const uint32_t x0 = __builtin_amdgcn_perm(he, le, 0x05010400u);  // t[n0] | t[n2] << 16
+  const uint32_t y0 = __builtin_amdgcn_perm(hq, lq, 0x05010400u);  // t[n1] | t[n3] << 16
+  const uint32_t x1 = __builtin_amdgcn_perm(he, le, 0x07030602u);  // t[n4] | t[n6] << 16
+  const uint32_t y1 = __builtin_amdgcn_perm(hq, lq, 0x07030602u);  // t[n5] | t[n7] << 16
+  o[0] = __builtin_amdgcn_perm(y0, x0, 0x05040100u);
+  o[1] = __builtin_amdgcn_perm(y0, x0, 0x07060302u);
+  o[2] = __builtin_amdgcn_perm(y1, x1, 0x05040100u);
+  o[3] = __builtin_amdgcn_perm(y1, x1, 0x07060302u);
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t p) { return __uint_as_float(p << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t p) { return __uint_as_float(p & 0xFFFF0000u); }
 

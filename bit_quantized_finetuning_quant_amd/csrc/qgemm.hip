@@ -16,10 +16,11 @@
 //     stage k+2 from global memory straight into a 3-stage LDS ring with
 //     global_load_lds_dwordx4, so no register ever holds it;
 //   waves 4-7 (producers) fetch the packed weight codes two steps ahead into
-//     registers, decode the nibbles through the 16-entry level table into bf16
-//     (the weight tile is decoded once per workgroup and shared by all 256
-//     activation rows) and write the next weight stage to LDS.  For partial
-//     tiles they also carry the activation tile, masked, through registers.
+//     registers, decode the nibbles into bf16 by byte permutes from the
+//     block's 16 decoded values held in registers (the weight tile is decoded
+//     once per workgroup and shared by all 256 activation rows) and write the
+//     next weight stage to LDS.  For partial tiles they also carry the
+//     activation tile, masked, through registers.
 // One consumer and one producer wave share each SIMD, so the decode's vector
 // ALU work issues alongside the matrix-core work.  One workgroup barrier per
 // contraction step; both roles execute the same number of barriers.  The DMA
@@ -62,9 +63,11 @@ __device__ __forceinline__ f32x16 mfma(u32x4 a, u32x4 b, f32x16 c) {
 }
 
 // Activation tile in LDS: 256 rows of 64 bf16 (128 B, eight 16-byte chunks),
-// unpadded; chunk c of row r sits at position c ^ (r & 7), so that the MFMA
-// fragment reads of 8 consecutive rows hit distinct banks.
-__device__ __forceinline__ int act_off(int row, int chunk) { return row * 64 + ((chunk ^ (row & 7)) << 3); }
+// unpadded; chunk c of row r sits at position c ^ ((r >> 1) & 7).  The LDS
+// serves the 16-byte reads of 16 lanes at a time from 64 four-byte banks
+// (256 B), i.e. two consecutive rows; under this swizzle the 16 rows of one
+// fragment read fill the 64 banks exactly once.
+__device__ __forceinline__ int act_off(int row, int chunk) { return row * 64 + ((chunk ^ ((row >> 1) & 7)) << 3); }
 
 // Workgroup barrier without the memory fences of __syncthreads(): those would
 // wait for every outstanding load, including the LDS-DMA of stages that are
@@ -108,14 +111,21 @@ __device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(
 // Full tiles: consumer wave cw (0..3) moves rows [64 cw, 64 cw + 64) of the
 // activation tile of stage kt into LDS buffer dst with 8 DMA instructions of 8
 // rows each (lane l writes the 16 bytes at dst + 16 l: row 8 j + l/8 of the
-// range, the chunk whose swizzled position is l % 8).  The per-lane byte
-// offset is loop-invariant and everything else is scalar.
+// range, the chunk whose swizzled position is l % 8).  The swizzle of those
+// rows depends on the parity of j only, so the per-lane byte offset takes two
+// loop-invariant values (lane_off[j & 1]) and everything else is scalar.
+__device__ __forceinline__ uint32_t dma_lane_offset(int lane, int64_t Kc, int parity) {
+  const int row = lane >> 3, pos = lane & 7;
+  const int chunk = pos ^ (4 * parity + (row >> 1));  // ((8 j + row) >> 1) & 7 for j of this parity
+  return (uint32_t)((row * Kc + 8 * chunk) * 2);
+}
+
 __device__ __forceinline__ void dma_act(const uint16_t *act, int64_t Kc, int64_t row0, int64_t kt,
-                                        uint32_t lane_off, uint16_t *dst, int j0 = 0, int nj = 8) {
+                                        const uint32_t (&lane_off)[2], uint16_t *dst, int j0 = 0, int nj = 8) {
   const char *base = (const char *)(act + row0 * Kc + kt * QBK);
   const uint32_t l0 = lds_addr(dst);
 #pragma unroll
-  for (int j = j0; j < j0 + nj; ++j) dma16(base + (int64_t)(16 * j) * Kc, lane_off, l0 + 8 * j * 64 * 2);
+  for (int j = j0; j < j0 + nj; ++j) dma16(base + (int64_t)(16 * j) * Kc, lane_off[j & 1], l0 + 8 * j * 64 * 2);
 }
 
 struct Stage {
@@ -172,26 +182,18 @@ struct Producer {
     }
   }
 
-  // Decode one weight stage into LDS.  All 32 level-table reads are issued
-  // before any of the arithmetic that consumes them.
-  __device__ __forceinline__ void store_w(const Stage &s, uint16_t *sb, const float *lut) const {
-    float lv[32];
-    // element e = 8 v + j of this lane's 32: nibble j of code word v
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) lv[8 * v + j] = lut[(s.code[v] >> (4 * j)) & 15u];
-    __builtin_amdgcn_sched_barrier(0);
+  // Decode one weight stage into LDS: the block's 16 decoded values are built
+  // in registers and the 32 codes select from them (no level-table reads, so
+  // the decode adds no LDS traffic and no LDS latency).
+  __device__ __forceinline__ void store_w(const Stage &s, uint16_t *sb, const Codebook &cb) const {
     // q = 0 with s2 = 0 decodes to c1hat = mu; masked rows carry the zero code, so they decode to 0
-    const float ch = decode_constant(s.q[0], s.s2[0], mu);
+    const DecodeTable t = decode_table(cb, decode_constant(s.q[0], s.s2[0], mu));
     uint16_t *dst = kTransW ? &sb[(ptid >> 2) * TLD + 32 * (ptid & 3)] : &sb[(ptid >> 1) * QLD + 32 * (ptid & 1)];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      u32x4 o;
-#pragma unroll
-      for (int d = 0; d < 4; ++d)
-        o[d] = pack_bf16x2(decode_product(lv[8 * v + 2 * d], ch), decode_product(lv[8 * v + 2 * d + 1], ch));
-      *(u32x4 *)&dst[8 * v] = o;
+      uint32_t o[4];
+      decode_word(s.code[v], t, o);
+      *(u32x4 *)&dst[8 * v] = u32x4{o[0], o[1], o[2], o[3]};
     }
   }
 };
@@ -205,7 +207,7 @@ struct Producer {
 template <bool kFull, bool kTransW>
 __device__ __forceinline__ void producer_loop(const Producer<kTransW> &p, int64_t nk,
                                               uint16_t (*sa)[QBM * 64], uint16_t (*sb)[QBN * QLD],
-                                              const float *lut) {
+                                              const Codebook &cb) {
   Stage s0, s1, s2;
   if (!kFull) {
     p.load_act(0, s0);
@@ -213,9 +215,8 @@ __device__ __forceinline__ void producer_loop(const Producer<kTransW> &p, int64_
   }
   p.template load_w<kFull>(0, s0);
   p.template load_w<kFull>(min((int64_t)1, nk - 1), s1);
-  __syncthreads();  // level table in LDS
   if (!kFull) p.store_act(s0, sa[0]);
-  p.store_w(s0, sb[0], lut);
+  p.store_w(s0, sb[0], cb);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
   wg_barrier();  // stage 0 ready
 #define QGEMM_PRODUCER_STEP(K_, CUR_NEXT, NEXT2)                                      \
@@ -225,7 +226,7 @@ __device__ __forceinline__ void producer_loop(const Producer<kTransW> &p, int64_
     p.template load_w<kFull>(k2, NEXT2);                                              \
     __builtin_amdgcn_sched_barrier(0);                                                \
     if (!kFull) p.store_act(CUR_NEXT, sa[((K_) + 1) % kActStages]);                   \
-    p.store_w(CUR_NEXT, sb[((K_) + 1) & 1], lut);                                     \
+    p.store_w(CUR_NEXT, sb[((K_) + 1) & 1], cb);                                      \
     __builtin_amdgcn_sched_barrier(0);                                                \
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));                                   \
     wg_barrier();                                                                     \
@@ -332,7 +333,6 @@ __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act
                                                 uint16_t *__restrict__ out, Codebook cb) {
   __shared__ __attribute__((aligned(16))) uint16_t sa[kActStages][QBM * 64];
   __shared__ __attribute__((aligned(16))) uint16_t sb[2][QBN * QLD];  // = 64 * TLD
-  __shared__ float lut[16];
 
   const int tid = threadIdx.x;
   const int64_t m0 = (int64_t)blockIdx.x * QBM, c0 = (int64_t)blockIdx.y * QBN;
@@ -385,24 +385,21 @@ __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act
     p.ptid = tid - 256;
     p.act_vec = (Kc % 8) == 0;
     if (full)
-      producer_loop<true>(p, nk, sa, sb, lut);
+      producer_loop<true>(p, nk, sa, sb, cb);
     else
-      producer_loop<false>(p, nk, sa, sb, lut);
+      producer_loop<false>(p, nk, sa, sb, cb);
     return;
   }
 
   // -------------------------------------------------------------- consumers
-  if (tid < 16) lut[tid] = cb.v[tid];
-
   // full tiles: stages 0 and 1 of the activation ring
   const int cw = __builtin_amdgcn_readfirstlane(wave);
   const int64_t dma_row0 = m0 + 64 * cw;
-  const uint32_t dma_lane_off = (uint32_t)(((lane >> 3) * Kc + 8 * ((lane & 7) ^ (lane >> 3))) * 2);
+  const uint32_t dma_lane_off[2] = {dma_lane_offset(lane, Kc, 0), dma_lane_offset(lane, Kc, 1)};
   if (full) {
     dma_act(act, Kc, dma_row0, 0, dma_lane_off, sa[0] + 64 * cw * 64);
     dma_act(act, Kc, dma_row0, min((int64_t)1, nk - 1), dma_lane_off, sa[1] + 64 * cw * 64);
   }
-  __syncthreads();  // level table in LDS
   // stage 0's DMA has landed (stage 1's 8 may still be in flight)
   if (full) __builtin_amdgcn_s_waitcnt(waitcnt_imm(8, 0));
   wg_barrier();     // stage 0 ready
@@ -426,8 +423,8 @@ __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act
     wg_barrier();
   }
   // No LDS-DMA may still be writing when the workgroup's LDS is released; the
-  // wait names dma_lane_off so that its register stays untouched until then.
-  asm volatile("s_waitcnt vmcnt(0)" ::"v"(dma_lane_off) : "memory");
+  // wait names the lane offsets so that their registers stay untouched until then.
+  asm volatile("s_waitcnt vmcnt(0)" ::"v"(dma_lane_off[0]), "v"(dma_lane_off[1]) : "memory");
 
   // Epilogue through LDS: the tile is rounded to bf16 into [256][136] (the
   // activation ring's storage), then written out as 16-byte row chunks.  The
