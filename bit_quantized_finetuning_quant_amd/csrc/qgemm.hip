@@ -128,11 +128,21 @@ __device__ __forceinline__ void dma_act(const uint16_t *act, int64_t Kc, int64_t
   for (int j = j0; j < j0 + nj; ++j) dma16(base + (int64_t)(16 * j) * Kc, lane_off[j & 1], l0 + 8 * j * 64 * 2);
 }
 
+// One stage of a producer lane: its 32 weight codes (one weight row, 32
+// consecutive n_in positions) with the block's FP8 constant and group scale,
+// and for partial tiles its share of the activation tile.
 struct Stage {
-  u32x4 a[8];   // activation (register path only): 8 rows x 8 contraction elements
-  u32x4 code;   // 32 weight codes: one weight row, 32 consecutive n_in positions
-  uint32_t q[4];
-  float s2[4];
+  u32x4 a[8];  // activation (register path only): 8 rows x 8 contraction elements
+  u32x4 code;
+  uint32_t q;
+  float s2;
+};
+
+// The 32 levels of a stage's codes and its block constant, read one step
+// before the products that use them.
+struct Levels {
+  float lv[32];
+  float ch;
 };
 
 template <bool kTransW>
@@ -165,80 +175,190 @@ struct Producer {
   // owns one weight row and 32 consecutive n_in positions (half an NF4 block):
   //   forward: weight rows c0 .. c0+127 (2 lanes a row), n_in = k0 .. k0+63
   //   grad_x : weight rows k0 .. k0+63 (4 lanes a row), n_in = c0 .. c0+127
+  // Full tiles address them from the lane's stage-0 position plus a per-stage
+  // stride (code_step bytes, blk_step blocks).
+  const uint8_t *code0;
+  int64_t code_step, blk0, blk_step;
+
+  __device__ __forceinline__ void init_addressing() {
+    const int64_t n = kTransW ? (ptid >> 2) : c0 + (ptid >> 1);
+    const int64_t col = kTransW ? c0 + 32 * (ptid & 3) : 32 * (ptid & 1);
+    code0 = w.codes + n * (K / 2) + col / 2;
+    code_step = kTransW ? QBK * (K / 2) : QBK / 2;
+    blk0 = n * kblk_row + col / kBlock;
+    blk_step = kTransW ? QBK * kblk_row : 1;
+  }
+
   template <bool kFull>
   __device__ __forceinline__ void load_w(int64_t kt, Stage &s) const {
+    if (kFull) {
+      s.code = *(const u32x4 *)(code0 + kt * code_step);
+      const int64_t blk = blk0 + kt * blk_step;
+      s.q = w.fp8[blk];
+      s.s2 = w.s2[blk >> 8];
+      return;
+    }
     const int64_t k0 = kt * QBK;
     const int64_t n = kTransW ? k0 + (ptid >> 2) : c0 + (ptid >> 1);
     const int64_t col = kTransW ? c0 + 32 * (ptid & 3) : k0 + 32 * (ptid & 1);
-    if (kFull || (n < N && col < K)) {
+    if (n < N && col < K) {
       s.code = *(const u32x4 *)(w.codes + n * (K / 2) + col / 2);
       const int64_t blk = n * kblk_row + col / kBlock;
-      s.q[0] = w.fp8[blk];
-      s.s2[0] = w.s2[blk >> 8];
+      s.q = w.fp8[blk];
+      s.s2 = w.s2[blk >> 8];
     } else {
       s.code = u32x4{0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
-      s.q[0] = 0u;
-      s.s2[0] = 0.f;
+      s.q = 0u;
+      s.s2 = 0.f;
     }
   }
 
-  // Decode one weight stage into LDS: the block's 16 decoded values are built
-  // in registers and the 32 codes select from them (no level-table reads, so
-  // the decode adds no LDS traffic and no LDS latency).
-  __device__ __forceinline__ void store_w(const Stage &s, uint16_t *sb, const Codebook &cb) const {
+  // The levels of a stage's 32 codes from the 16-entry table in LDS, and its
+  // block constant.  Each byte of the masked words (c << 2) & 0x3C3C3C3C and
+  // (c >> 2) & 0x3C3C3C3C is four times a code (even and odd elements), i.e.
+  // the byte offset of its level, so one extract per code forms its address.
+  __device__ __forceinline__ void read_levels(const Stage &s, const float *lut, Levels &L) const {
+    const char *base = (const char *)lut;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      uint32_t ev = (s.code[v] << 2) & 0x3C3C3C3Cu, od = (s.code[v] >> 2) & 0x3C3C3C3Cu;
+      // opaque to the optimizer, which would otherwise rebuild a shift and a mask per code
+      asm("" : "+v"(ev), "+v"(od));
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        L.lv[8 * v + 2 * k] = *(const float *)(base + __builtin_amdgcn_ubfe(ev, 8 * k, 8));
+        L.lv[8 * v + 2 * k + 1] = *(const float *)(base + __builtin_amdgcn_ubfe(od, 8 * k, 8));
+      }
+    }
     // q = 0 with s2 = 0 decodes to c1hat = mu; masked rows carry the zero code, so they decode to 0
-    const DecodeTable t = decode_table(cb, decode_constant(s.q[0], s.s2[0], mu));
+    L.ch = decode_constant(s.q, s.s2, mu);
+  }
+
+  // The decoded stage into LDS: fl32 products rounded to bf16, 16-byte stores.
+  __device__ __forceinline__ void store_w(const Levels &L, uint16_t *sb) const {
     uint16_t *dst = kTransW ? &sb[(ptid >> 2) * TLD + 32 * (ptid & 3)] : &sb[(ptid >> 1) * QLD + 32 * (ptid & 1)];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      uint32_t o[4];
-      decode_word(s.code[v], t, o);
-      *(u32x4 *)&dst[8 * v] = u32x4{o[0], o[1], o[2], o[3]};
+      u32x4 o;
+#pragma unroll
+      for (int d = 0; d < 4; ++d)
+        o[d] = pack_bf16x2(decode_product(L.lv[8 * v + 2 * d], L.ch), decode_product(L.lv[8 * v + 2 * d + 1], L.ch));
+      *(u32x4 *)&dst[8 * v] = o;
     }
   }
 };
 
-// Producer side of the pipeline: at step k the weight codes of stage k+2 are
-// fetched into registers while stage k+1 is decoded into LDS and the
-// consumers multiply stage k (partial tiles: the activation tile rides along
-// in the same registers).  Three register sets rotate; the main loop is
-// unrolled by three with no conditions inside, so each set keeps fixed
+// Producer side of the pipeline: at step k the consumers multiply stage k
+// (from registers) and read stage k+1 from LDS, while the producers write
+// stage k+2 into the buffers of stage k (read during step k-1).  Stages 0 and
+// 1 are written before the loop, each followed by a barrier.  Past the end the
+// last stage is repeated, into buffers nobody reads.  The loops are unrolled
+// over their register sets with no conditions inside, so each set keeps fixed
 // registers.
-template <bool kFull, bool kTransW>
-__device__ __forceinline__ void producer_loop(const Producer<kTransW> &p, int64_t nk,
-                                              uint16_t (*sa)[QBM * 64], uint16_t (*sb)[QBN * QLD],
-                                              const Codebook &cb) {
-  Stage s0, s1, s2;
-  if (!kFull) {
-    p.load_act(0, s0);
-    p.load_act(min((int64_t)1, nk - 1), s1);
-  }
-  p.template load_w<kFull>(0, s0);
-  p.template load_w<kFull>(min((int64_t)1, nk - 1), s1);
-  if (!kFull) p.store_act(s0, sa[0]);
-  p.store_w(s0, sb[0], cb);
+//
+// Full tiles: at step k the producers
+//   - read the levels of stage k+3 from the LDS table (codes fetched two
+//     steps earlier), to be used at the next step,
+//   - fetch the codes of stage k+5,
+//   - form the products of stage k+2 (levels read at the previous step) and
+//     write them to LDS.
+// Code sets rotate by three and level sets by two (unrolled by six).
+template <bool kTransW>
+__device__ __forceinline__ void producer_loop_full(const Producer<kTransW> &p, int64_t nk, uint16_t (*sb)[QBN * QLD],
+                                                   const float *lut) {
+  auto st = [nk](int64_t k) { return min(k, nk - 1); };
+  Stage c0, c1, c2;
+  Levels l0, l1;
+  p.template load_w<true>(0, c0);
+  p.template load_w<true>(st(1), c1);
+  p.template load_w<true>(st(2), c2);
+  p.read_levels(c0, lut, l0);
+  p.store_w(l0, sb[0]);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
   wg_barrier();  // stage 0 ready
-#define QGEMM_PRODUCER_STEP(K_, CUR_NEXT, NEXT2)                                      \
+  p.read_levels(c1, lut, l1);
+  p.store_w(l1, sb[1]);
+  p.read_levels(c2, lut, l0);  // stage 2, used at step 0
+  p.template load_w<true>(st(3), c0);
+  p.template load_w<true>(st(4), c1);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+  wg_barrier();  // stage 1 ready; the consumers hold stage 0 in registers
+  // step K_: LCUR = levels of stage K_+2, LNEXT <- levels of stage K_+3 (codes
+  // in CREAD), CLOAD (codes of stage K_+2, levels already read) <- stage K_+5
+#define QGEMM_PRODUCER_STEP(K_, LCUR, LNEXT, CREAD, CLOAD)                           \
   if ((K_) < nk) {                                                                    \
-    const int64_t k2 = min((K_) + 2, nk - 1);                                         \
-    if (!kFull) p.load_act(k2, NEXT2);                                                \
-    p.template load_w<kFull>(k2, NEXT2);                                              \
+    p.read_levels(CREAD, lut, LNEXT);                                                 \
     __builtin_amdgcn_sched_barrier(0);                                                \
-    if (!kFull) p.store_act(CUR_NEXT, sa[((K_) + 1) % kActStages]);                   \
-    p.store_w(CUR_NEXT, sb[((K_) + 1) & 1], cb);                                      \
+    p.template load_w<true>(st((K_) + 5), CLOAD);                                     \
+    __builtin_amdgcn_sched_barrier(0);                                                \
+    p.store_w(LCUR, sb[(K_) & 1]);                                                    \
     __builtin_amdgcn_sched_barrier(0);                                                \
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));                                   \
     wg_barrier();                                                                     \
   }
   int64_t kt = 0;
-  for (; kt + 3 <= nk; kt += 3) {
-    QGEMM_PRODUCER_STEP(kt, s1, s2)
-    QGEMM_PRODUCER_STEP(kt + 1, s2, s0)
-    QGEMM_PRODUCER_STEP(kt + 2, s0, s1)
+  for (; kt + 6 <= nk; kt += 6) {
+    QGEMM_PRODUCER_STEP(kt, l0, l1, c0, c2)
+    QGEMM_PRODUCER_STEP(kt + 1, l1, l0, c1, c0)
+    QGEMM_PRODUCER_STEP(kt + 2, l0, l1, c2, c1)
+    QGEMM_PRODUCER_STEP(kt + 3, l1, l0, c0, c2)
+    QGEMM_PRODUCER_STEP(kt + 4, l0, l1, c1, c0)
+    QGEMM_PRODUCER_STEP(kt + 5, l1, l0, c2, c1)
   }
-  QGEMM_PRODUCER_STEP(kt, s1, s2)
-  QGEMM_PRODUCER_STEP(kt + 1, s2, s0)
+  QGEMM_PRODUCER_STEP(kt, l0, l1, c0, c2)
+  QGEMM_PRODUCER_STEP(kt + 1, l1, l0, c1, c0)
+  QGEMM_PRODUCER_STEP(kt + 2, l0, l1, c2, c1)
+  QGEMM_PRODUCER_STEP(kt + 3, l1, l0, c0, c2)
+  QGEMM_PRODUCER_STEP(kt + 4, l0, l1, c1, c0)
+#undef QGEMM_PRODUCER_STEP
+}
+
+// Partial tiles: the activation tile rides along with the codes, masked; at
+// step k the producers read the levels of stage k+2 and write it (codes and
+// activation fetched two steps earlier), then fetch stage k+4.  Sets rotate
+// by three (unrolled by three).
+template <bool kTransW>
+__device__ __forceinline__ void producer_loop_partial(const Producer<kTransW> &p, int64_t nk,
+                                                      uint16_t (*sa)[QBM * 64], uint16_t (*sb)[QBN * QLD],
+                                                      const float *lut) {
+  auto st = [nk](int64_t k) { return min(k, nk - 1); };
+  Stage c0, c1, c2;
+  Levels l;
+  auto load = [&](int64_t k, Stage &c) {
+    p.load_act(k, c);
+    p.template load_w<false>(k, c);
+  };
+  auto store = [&](const Stage &c, int64_t k) {
+    p.read_levels(c, lut, l);
+    p.store_act(c, sa[k % kActStages]);
+    p.store_w(l, sb[k & 1]);
+  };
+  load(0, c0);
+  load(st(1), c1);
+  load(st(2), c2);
+  store(c0, 0);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+  wg_barrier();  // stage 0 ready
+  store(c1, 1);
+  load(st(3), c0);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+  wg_barrier();  // stage 1 ready
+#define QGEMM_PRODUCER_STEP(K_, CSTORE, CLOAD)                                        \
+  if ((K_) < nk) {                                                                    \
+    store(CSTORE, (K_) + 2);                                                          \
+    __builtin_amdgcn_sched_barrier(0);                                                \
+    load(st((K_) + 4), CLOAD);                                                        \
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));                                   \
+    wg_barrier();                                                                     \
+  }
+  int64_t kt = 0;
+  for (; kt + 3 <= nk; kt += 3) {
+    QGEMM_PRODUCER_STEP(kt, c2, c1)
+    QGEMM_PRODUCER_STEP(kt + 1, c0, c2)
+    QGEMM_PRODUCER_STEP(kt + 2, c1, c0)
+  }
+  QGEMM_PRODUCER_STEP(kt, c2, c1)
+  QGEMM_PRODUCER_STEP(kt + 1, c0, c2)
 #undef QGEMM_PRODUCER_STEP
 }
 
@@ -291,6 +411,31 @@ __device__ __forceinline__ void consumer_slices(const uint16_t *A, const uint16_
   }
 }
 
+// Fragments of slice kk of one stage for a consumer wave's 128 x 64
+// sub-tile (the same addressing as consumer_slices).
+struct StageFrags {
+  u32x4 a[QBK / 16][4], b[QBK / 16][2];
+};
+
+__device__ __forceinline__ u32x4 load_a_frag(const uint16_t *A, int wm, int lane, int kk, int i) {
+  return *(const u32x4 *)&A[act_off(wm * 128 + i * 32 + (lane & 31), 2 * kk + (lane >> 5))];
+}
+
+template <bool kTransW>
+__device__ __forceinline__ u32x4 load_b_frag(const uint16_t *B, int wn, int lane, int kk, int j) {
+  if (!kTransW) return *(const u32x4 *)&B[(wn * 64 + j * 32 + (lane & 31)) * QLD + kk * 16 + 8 * (lane >> 5)];
+  const int sl = lane & 15, g = lane >> 4;
+  const int nrow = 16 * kk + 8 * (g >> 1) + (sl >> 2);
+  const int ncol = wn * 64 + j * 32 + 16 * (g & 1) + 4 * (sl & 3);
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (v4s __attribute__((address_space(3))) *)(lptr_t *)&B[nrow * TLD + ncol]);
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (v4s __attribute__((address_space(3))) *)(lptr_t *)&B[(nrow + 4) * TLD + ncol]);
+  const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+  return u32x4{l2.x, l2.y, h2.x, h2.y};
+}
+
 // LoRA term of the output tile, staged through LDS in the same layouts as the
 // main contraction (one 64-wide chunk of the rank r at a time, zero past r):
 // the left factor la [M x r] as an activation tile, the right factor as a
@@ -333,6 +478,7 @@ __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act
                                                 uint16_t *__restrict__ out, Codebook cb) {
   __shared__ __attribute__((aligned(16))) uint16_t sa[kActStages][QBM * 64];
   __shared__ __attribute__((aligned(16))) uint16_t sb[2][QBN * QLD];  // = 64 * TLD
+  __shared__ float lut[16];
 
   const int tid = threadIdx.x;
   const int64_t m0 = (int64_t)blockIdx.x * QBM, c0 = (int64_t)blockIdx.y * QBN;
@@ -341,9 +487,14 @@ __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act
   // activation rows are 16-byte aligned
   const bool full = (m0 + QBM <= M) && (c0 + QBN <= Ncols) && (Kc % QBK == 0);
 
+  // Level table for the producers' decode.
+  if (tid < 16) lut[tid] = cb.v[tid];
+  __syncthreads();
+
   // LoRA term first, scaled: acc = scale * la lb^T, staged chunk by chunk in
-  // buffers the pipeline does not touch before its first barrier (activation
-  // stage 2, weight stage 1); the consumer waves multiply, everyone stages.
+  // activation stage 2 and weight stage 1 (the loop's last barrier ends their
+  // use before the pipeline starts); the consumer waves multiply, everyone
+  // stages.
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, lhi = lane >> 5;
@@ -384,38 +535,74 @@ __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act
     p.mu = *w.mu;
     p.ptid = tid - 256;
     p.act_vec = (Kc % 8) == 0;
+    p.init_addressing();
     if (full)
-      producer_loop<true>(p, nk, sa, sb, cb);
+      producer_loop_full(p, nk, sb, lut);
     else
-      producer_loop<false>(p, nk, sa, sb, cb);
+      producer_loop_partial(p, nk, sa, sb, lut);
     return;
   }
 
   // -------------------------------------------------------------- consumers
-  // full tiles: stages 0 and 1 of the activation ring
+  // full tiles: stages 0, 1 and 2 of the activation ring
   const int cw = __builtin_amdgcn_readfirstlane(wave);
   const int64_t dma_row0 = m0 + 64 * cw;
   const uint32_t dma_lane_off[2] = {dma_lane_offset(lane, Kc, 0), dma_lane_offset(lane, Kc, 1)};
   if (full) {
     dma_act(act, Kc, dma_row0, 0, dma_lane_off, sa[0] + 64 * cw * 64);
     dma_act(act, Kc, dma_row0, min((int64_t)1, nk - 1), dma_lane_off, sa[1] + 64 * cw * 64);
+    dma_act(act, Kc, dma_row0, min((int64_t)2, nk - 1), dma_lane_off, sa[2] + 64 * cw * 64);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(16, 0));  // stage 0 has landed
   }
-  // stage 0's DMA has landed (stage 1's 8 may still be in flight)
-  if (full) __builtin_amdgcn_s_waitcnt(waitcnt_imm(8, 0));
-  wg_barrier();     // stage 0 ready
+  wg_barrier();  // stage 0 ready
+  StageFrags f;
+#pragma unroll
+  for (int kk = 0; kk < QBK / 16; ++kk) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.a[kk][i] = load_a_frag(sa[0], wm, lane, kk, i);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) f.b[kk][j] = load_b_frag<kTransW>(sb[0], wn, lane, kk, j);
+  }
+  // stage 0 is in registers, and this wave's DMA of stage 1 has landed
+  if (full)
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(8, 0));
+  else
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+  wg_barrier();  // stage 1 ready
 
+  // Step k: the 32 MFMAs of stage k run from registers; each fragment register
+  // is reloaded with the same fragment of stage k+1 (in LDS since the previous
+  // barrier) right after the last MFMA that reads it, so the MFMAs never wait
+  // for LDS within a step.  One load, DMA or nothing follows each MFMA, so the
+  // wave keeps the matrix core fed while it issues them: A fragment i of
+  // slice kk after MFMA (kk, i, 1); the two B fragments of slice kk early in
+  // slice kk+1 (after the last slice: after the loop); the two DMAs of a slice
+  // after its MFMAs (kk, 2, 0) and (kk, 3, 0).  Stage k+3 of the activation
+  // ring goes by DMA into the buffer of stage k (read during step k-1).  At the
+  // last step the loads read a stage nobody uses.  Exactly 8 DMAs per step, so
+  // waiting for at most 8 outstanding before the barrier means stage k+2 has
+  // landed; every read of stage k+1 has returned by then too.
   for (int64_t kt = 0; kt < nk; ++kt) {
-    // Stage k+2 of the activation ring (past the end: the last stage again,
-    // into a buffer nobody reads), its 8 DMAs spread over the four slices,
-    // two each.  Exactly 8 DMAs per step, so waiting for at most 8
-    // outstanding before the barrier means stage k+1 has landed.
-    uint16_t *dma_dst = sa[(kt + 2) % kActStages] + 64 * cw * 64;
-    const int64_t dma_kt = min(kt + 2, nk - 1);
-    consumer_slices<kTransW>(sa[kt % kActStages], sb[kt & 1], wm, wn, lane, acc, [&](int kk) {
-      if (full) dma_act(act, Kc, dma_row0, dma_kt, dma_lane_off, dma_dst, 2 * kk, 2);
-    });
-    // every LDS read of this stage has returned (the MFMAs consumed them), and
-    // this wave's DMA of stage k+1 has landed
+    uint16_t *dma_dst = sa[kt % kActStages] + 64 * cw * 64;
+    const int64_t dma_kt = min(kt + 3, nk - 1);
+    const uint16_t *na = sa[(kt + 1) % kActStages], *nb = sb[(kt + 1) & 1];
+#pragma unroll
+    for (int kk = 0; kk < QBK / 16; ++kk) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        acc[i][0] = mfma(f.a[kk][i], f.b[kk][0], acc[i][0]);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kk > 0 && i < 2) f.b[kk - 1][i] = load_b_frag<kTransW>(nb, wn, lane, kk - 1, i);
+        if (i >= 2 && full) dma_act(act, Kc, dma_row0, dma_kt, dma_lane_off, dma_dst, 2 * kk + i - 2, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        acc[i][1] = mfma(f.a[kk][i], f.b[kk][1], acc[i][1]);
+        __builtin_amdgcn_sched_barrier(0);
+        f.a[kk][i] = load_a_frag(na, wm, lane, kk, i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) f.b[QBK / 16 - 1][j] = load_b_frag<kTransW>(nb, wn, lane, QBK / 16 - 1, j);
     if (full)
       __builtin_amdgcn_s_waitcnt(waitcnt_imm(8, 0));
     else
