@@ -186,7 +186,10 @@ class LayerSet:
             self.steps.append((q, x, a, b, dy, bufs))
             self.flops += linear_flops(tokens, n, k, r)
         del w
-        self.ws = qlora.linear_workspace(tokens, max(s[1] for s in shapes), max(s[2] for s in shapes), r)
+        # one workspace for all the linears: the largest any of them needs (the size is not
+        # monotone in the shape: the contraction splits depend on the tile count)
+        ws_bytes = max(qlora.linear_workspace_bytes(tokens, n, k, r) for _, n, k in shapes)
+        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
         self.qlora = qlora
         torch.cuda.synchronize()
 

@@ -58,6 +58,11 @@ int64_t lora_tiles(int64_t m, int64_t n);
 size_t lora_part_floats(int64_t m, int64_t n, int64_t kc);
 hipError_t launch_lora(LoraKind kind, const uint16_t *P, int64_t ldp, const uint16_t *Q, int64_t ldq, int64_t M,
                        int64_t Nc, int64_t Kc, float scale, void *out, float *part, hipStream_t st);
+// grad_A = s v^T x and grad_B = s dy^T u in one launch (plus one reduction); the
+// partials of grad_A take the first part_a_floats of `part`, those of grad_B follow.
+hipError_t launch_lora_grads(const uint16_t *v, const uint16_t *x, const uint16_t *dy, const uint16_t *u, int64_t T,
+                             int64_t N, int64_t K, int r, float scale, float *grad_A, float *grad_B, float *part,
+                             size_t part_a_floats, hipStream_t st);
 
 // Dequant-fused GEMM: out = scale * la lb^T + act W_op (see qgemm.hip).
 hipError_t launch_qgemm(bool trans_w, const uint16_t *act, int64_t M, int64_t Ncols, int64_t Kc, const QWeight &w,

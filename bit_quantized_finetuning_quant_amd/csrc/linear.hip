@@ -96,6 +96,8 @@ LinearPlan plan_linear(int64_t T, int64_t N, int64_t K, int r) {
   const int64_t shapes[4][3] = {{T, r, K}, {T, r, N}, {r, K, T}, {N, r, T}};
   size_t part = 0;
   for (const auto &sh : shapes) part = std::max(part, lora_part_floats(sh[0], sh[1], sh[2]));
+  // grad_A and grad_B are formed together
+  part = std::max(part, lora_part_floats(r, K, T) + lora_part_floats(N, r, T));
   if (gemv_applies(T, K)) part = std::max(part, gemv_part_floats(T, N, K, r));
   size_t off = 0;
   p.off_status = off;  // status word (never written by the linear calls)
@@ -157,11 +159,9 @@ hipError_t launch_linear_bwd(const LinearPlan &p, const uint16_t *dy, const uint
     if (timed) timing_end(st, tl);
     if (e != hipSuccess) return e;
   }
-  // grad_A = s v^T x   [r x K]
-  e = launch_lora(LoraKind::kGrad, v, p.r, x, p.K, p.r, p.K, p.T, scale, grad_A, part, st);
-  if (e != hipSuccess) return e;
-  // grad_B = s dy^T u  [N x r]
-  return launch_lora(LoraKind::kGrad, dy, p.N, u, p.r, p.N, p.r, p.T, scale, grad_B, part, st);
+  // grad_A = s v^T x [r x K] and grad_B = s dy^T u [N x r], one launch (and one reduction) for both
+  return launch_lora_grads(v, x, dy, u, p.T, p.N, p.K, p.r, scale, grad_A, grad_B, part,
+                           lora_part_floats(p.r, p.K, p.T), st);
 }
 
 }  // namespace qlora

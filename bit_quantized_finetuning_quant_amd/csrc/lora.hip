@@ -155,77 +155,110 @@ __device__ __forceinline__ void emit_out(void *out, int64_t idx, float v) {
   }
 }
 
+// One adapter product of a launch: C[M x Nc] = scale * Aop Bop over a
+// contraction of Kc, split in chunks of `chunk` (S splits); tiles are numbered
+// column-major (tile = n-tile * tiles_m + m-tile).
+struct LoraProblem {
+  const uint16_t *P;
+  int64_t ldp;
+  const uint16_t *Q;
+  int64_t ldq;
+  int64_t M, Nc, Kc, chunk, tiles_m;
+  int S;
+  float scale;  // applied here when S == 1, else by the reduction
+  void *out;
+  float *part;
+};
+
 template <bool kAT, bool kBT, bool kBf16Out, int kGroupSteps>
-__global__ __launch_bounds__(256) void lora_gemm(const uint16_t *__restrict__ P, int64_t ldp,
-                                                 const uint16_t *__restrict__ Q, int64_t ldq, int64_t M, int64_t Nc,
-                                                 int64_t Kc, int64_t chunk, float scale, void *__restrict__ out,
-                                                 float *__restrict__ part) {
-  __shared__ __attribute__((aligned(16))) uint16_t sA[kGroupSteps][LT * LLD];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[kGroupSteps][LT * LLD];
+__device__ __forceinline__ void lora_tile(const LoraProblem &pr, int64_t tile, int s, uint16_t (*sA)[LT * LLD],
+                                          uint16_t (*sB)[LT * LLD]) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.x * LT, n0 = (int64_t)blockIdx.y * LT;
-  const int S = gridDim.z, s = blockIdx.z;
-  const int64_t kb = (int64_t)s * chunk, ke = min(Kc, kb + chunk);
+  const int64_t m0 = (tile % pr.tiles_m) * LT, n0 = (tile / pr.tiles_m) * LT;
+  const int64_t kb = (int64_t)s * pr.chunk, ke = min(pr.Kc, kb + pr.chunk);
 
   f32x16 acc;
 #pragma unroll
   for (int q = 0; q < 16; ++q) acc[q] = 0.f;
   // full: both operand tiles in range and aligned, and the chunk is whole groups
-  const bool full = (m0 + LT <= M) && (n0 + LT <= Nc) && ((ke - kb) % (LT * kGroupSteps) == 0) &&
-                    (ldp % 8 == 0) && (ldq % 8 == 0);
+  const bool full = (m0 + LT <= pr.M) && (n0 + LT <= pr.Nc) && ((ke - kb) % (LT * kGroupSteps) == 0) &&
+                    (pr.ldp % 8 == 0) && (pr.ldq % 8 == 0);
   if (full)
-    lora_body<kAT, kBT, kBf16Out, true, kGroupSteps>(P, ldp, Q, ldq, M, Nc, kb, ke, m0, n0, sA, sB, acc);
+    lora_body<kAT, kBT, kBf16Out, true, kGroupSteps>(pr.P, pr.ldp, pr.Q, pr.ldq, pr.M, pr.Nc, kb, ke, m0, n0, sA, sB,
+                                                      acc);
   else
-    lora_body<kAT, kBT, kBf16Out, false, kGroupSteps>(P, ldp, Q, ldq, M, Nc, kb, ke, m0, n0, sA, sB, acc);
+    lora_body<kAT, kBT, kBf16Out, false, kGroupSteps>(pr.P, pr.ldp, pr.Q, pr.ldq, pr.M, pr.Nc, kb, ke, m0, n0, sA,
+                                                       sB, acc);
 
   // result element q of this lane: tile row wm*32 + 8(q/4) + 4(lane/32) + q%4, column wn*32 + lane%32
   const int col = wn * 32 + (lane & 31);
-  if (S == 1) {
+  if (pr.S == 1) {
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int64_t gm = m0 + wm * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3), gn = n0 + col;
-      if (gm < M && gn < Nc) emit_out<kBf16Out>(out, gm * Nc + gn, acc[q] * scale);
+      if (gm < pr.M && gn < pr.Nc) emit_out<kBf16Out>(pr.out, gm * pr.Nc + gn, acc[q] * pr.scale);
     }
     return;
   }
   // partial tile, row-major 64 x 64, at part[((tile * S) + s) * 4096]
-  const int64_t tile = (int64_t)blockIdx.y * gridDim.x + blockIdx.x;
-  float *mine = part + (tile * S + s) * (LT * LT);
+  float *mine = pr.part + (tile * pr.S + s) * (LT * LT);
 #pragma unroll
   for (int q = 0; q < 16; ++q) mine[(wm * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3)) * LT + col] = acc[q];
 }
 
+// One or two products of the same operand forms in one launch: workgroups
+// below `first` take problem a (tile-major, splits innermost), the rest
+// problem b.
+template <bool kAT, bool kBT, bool kBf16Out, int kGroupSteps>
+__global__ __launch_bounds__(256) void lora_gemm(LoraProblem a, LoraProblem b, int64_t first) {
+  __shared__ __attribute__((aligned(16))) uint16_t sA[kGroupSteps][LT * LLD];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[kGroupSteps][LT * LLD];
+  const int64_t id = blockIdx.x;
+  const bool in_a = id < first;
+  const LoraProblem &pr = in_a ? a : b;
+  const int64_t j = in_a ? id : id - first;
+  lora_tile<kAT, kBT, kBf16Out, kGroupSteps>(pr, j / pr.S, (int)(j % pr.S), sA, sB);
+}
+
 // out = scale * (sum over splits, in split order) of the partial tiles; one
-// thread per 4 consecutive columns of a tile row.
+// thread per 4 consecutive columns of a tile row.  Quads below `first` belong
+// to problem a, the rest to problem b.
 template <bool kBf16Out>
-__global__ __launch_bounds__(256) void lora_reduce(const float *__restrict__ part, int S, int64_t M, int64_t Nc,
-                                                   int64_t tiles_m, float scale, void *__restrict__ out) {
-  const int64_t quads = cdiv_d(M, LT) * cdiv_d(Nc, LT) * (LT * LT / 4);
-  for (int64_t qd = (int64_t)blockIdx.x * 256 + threadIdx.x; qd < quads; qd += (int64_t)gridDim.x * 256) {
-    const int64_t tile = qd / (LT * LT / 4);
-    const int local = (int)(qd % (LT * LT / 4)) * 4;
-    const int64_t gm = (tile % tiles_m) * LT + local / LT;
-    const int64_t gn = (tile / tiles_m) * LT + local % LT;
-    if (gm >= M || gn >= Nc) continue;
-    const f32x4 *p = (const f32x4 *)(part + tile * S * (LT * LT) + local);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    // eight loads in flight at a time; the additions stay in split order
-    for (int k0 = 0; k0 < S; k0 += 8) {
-      f32x4 v[8];
+__device__ __forceinline__ void reduce_quad(const LoraProblem &pr, int64_t qd) {
+  const int64_t tile = qd / (LT * LT / 4);
+  const int local = (int)(qd % (LT * LT / 4)) * 4;
+  const int64_t gm = (tile % pr.tiles_m) * LT + local / LT;
+  const int64_t gn = (tile / pr.tiles_m) * LT + local % LT;
+  if (gm >= pr.M || gn >= pr.Nc) return;
+  const int S = pr.S;
+  const f32x4 *p = (const f32x4 *)(pr.part + tile * S * (LT * LT) + local);
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  // eight loads in flight at a time; the additions stay in split order
+  for (int k0 = 0; k0 < S; k0 += 8) {
+    f32x4 v[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) v[k] = (k0 + k < S) ? p[(int64_t)(k0 + k) * (LT * LT / 4)] : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < 8; ++k) v[k] = (k0 + k < S) ? p[(int64_t)(k0 + k) * (LT * LT / 4)] : f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        acc[0] += v[k][0];
-        acc[1] += v[k][1];
-        acc[2] += v[k][2];
-        acc[3] += v[k][3];
-      }
+    for (int k = 0; k < 8; ++k) {
+      acc[0] += v[k][0];
+      acc[1] += v[k][1];
+      acc[2] += v[k][2];
+      acc[3] += v[k][3];
     }
+  }
 #pragma unroll
-    for (int e = 0; e < 4; ++e)
-      if (gn + e < Nc) emit_out<kBf16Out>(out, gm * Nc + gn + e, acc[e] * scale);
+  for (int e = 0; e < 4; ++e)
+    if (gn + e < pr.Nc) emit_out<kBf16Out>(pr.out, gm * pr.Nc + gn + e, acc[e] * pr.scale);
+}
+
+template <bool kBf16Out>
+__global__ __launch_bounds__(256) void lora_reduce(LoraProblem a, LoraProblem b, int64_t first, int64_t quads) {
+  for (int64_t qd = (int64_t)blockIdx.x * 256 + threadIdx.x; qd < quads; qd += (int64_t)gridDim.x * 256) {
+    if (qd < first)
+      reduce_quad<kBf16Out>(a, qd);
+    else
+      reduce_quad<kBf16Out>(b, qd - first);
   }
 }
 
@@ -253,41 +286,76 @@ size_t lora_part_floats(int64_t m, int64_t n, int64_t kc) {
   return S > 1 ? (size_t)tiles * S * LT * LT : 0;
 }
 
-hipError_t launch_lora(LoraKind kind, const uint16_t *P, int64_t ldp, const uint16_t *Q, int64_t ldq, int64_t M,
-                       int64_t Nc, int64_t Kc, float scale, void *out, float *part, hipStream_t st) {
+namespace {
+
+LoraProblem make_problem(const uint16_t *P, int64_t ldp, const uint16_t *Q, int64_t ldq, int64_t M, int64_t Nc,
+                         int64_t Kc, float scale, void *out, float *part) {
+  LoraProblem pr;
+  pr.P = P;
+  pr.ldp = ldp;
+  pr.Q = Q;
+  pr.ldq = ldq;
+  pr.M = M;
+  pr.Nc = Nc;
+  pr.Kc = Kc;
+  pr.tiles_m = cdiv(M, LT);
   const int64_t tiles = lora_tiles(M, Nc);
-  const int64_t chunk = lora_chunk(tiles, Kc);
-  const int S = (int)cdiv(Kc, chunk);
-  const float sc = S == 1 ? scale : 1.0f;  // with splits the scale is applied by the reduction
-  dim3 g((unsigned)cdiv(M, LT), (unsigned)cdiv(Nc, LT), (unsigned)S);
-  const bool whole = chunk == LT * 8;
-#define QLORA_LORA_LAUNCH(AT, BT, BF)                                                                  \
-  if (whole)                                                                                        \
-    lora_gemm<AT, BT, BF, 8><<<g, 256, 0, st>>>(P, ldp, Q, ldq, M, Nc, Kc, chunk, sc, out, part);   \
-  else                                                                                              \
-    lora_gemm<AT, BT, BF, 4><<<g, 256, 0, st>>>(P, ldp, Q, ldq, M, Nc, Kc, chunk, sc, out, part);
-  switch (kind) {
-    case LoraKind::kU:  // x A^T
-      QLORA_LORA_LAUNCH(false, false, true)
-      break;
-    case LoraKind::kV:  // dy B
-      QLORA_LORA_LAUNCH(false, true, true)
-      break;
-    case LoraKind::kGrad:  // v^T x, dy^T u
-      QLORA_LORA_LAUNCH(true, true, false)
-      break;
-  }
-#undef QLORA_LORA_LAUNCH
-  if (S > 1) {
-    const int64_t quads = tiles * (LT * LT / 4);
-    int64_t blocks = cdiv(quads, 256);
+  pr.chunk = lora_chunk(tiles, Kc);
+  pr.S = (int)cdiv(Kc, pr.chunk);
+  pr.scale = scale;
+  pr.out = out;
+  pr.part = part;
+  return pr;
+}
+
+int64_t problem_blocks(const LoraProblem &pr) { return lora_tiles(pr.M, pr.Nc) * pr.S; }
+int64_t problem_quads(const LoraProblem &pr) { return pr.S > 1 ? lora_tiles(pr.M, pr.Nc) * (LT * LT / 4) : 0; }
+
+// Launches one product (nb == nullptr) or two of the same operand forms; the
+// two must agree on the group length (8 when a split is exactly 512 long).
+template <bool kAT, bool kBT, bool kBf16Out>
+hipError_t launch_pair(const LoraProblem &a, const LoraProblem *nb, hipStream_t st) {
+  const LoraProblem b = nb ? *nb : a;
+  const int64_t wa = problem_blocks(a), wb = nb ? problem_blocks(b) : 0;
+  const bool whole = a.chunk == LT * 8;
+  if (whole)
+    lora_gemm<kAT, kBT, kBf16Out, 8><<<(unsigned)(wa + wb), 256, 0, st>>>(a, b, wa);
+  else
+    lora_gemm<kAT, kBT, kBf16Out, 4><<<(unsigned)(wa + wb), 256, 0, st>>>(a, b, wa);
+  const int64_t qa = problem_quads(a), qb = nb ? problem_quads(b) : 0;
+  if (qa + qb > 0) {
+    int64_t blocks = cdiv(qa + qb, 256);
     if (blocks > 2048) blocks = 2048;
-    if (kind == LoraKind::kGrad)
-      lora_reduce<false><<<(unsigned)blocks, 256, 0, st>>>(part, S, M, Nc, cdiv(M, LT), scale, out);
-    else
-      lora_reduce<true><<<(unsigned)blocks, 256, 0, st>>>(part, S, M, Nc, cdiv(M, LT), scale, out);
+    lora_reduce<kBf16Out><<<(unsigned)blocks, 256, 0, st>>>(a, b, qa, qa + qb);
   }
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_lora(LoraKind kind, const uint16_t *P, int64_t ldp, const uint16_t *Q, int64_t ldq, int64_t M,
+                       int64_t Nc, int64_t Kc, float scale, void *out, float *part, hipStream_t st) {
+  const LoraProblem pr = make_problem(P, ldp, Q, ldq, M, Nc, Kc, scale, out, part);
+  switch (kind) {
+    case LoraKind::kU:  // x A^T
+      return launch_pair<false, false, true>(pr, nullptr, st);
+    case LoraKind::kV:  // dy B
+      return launch_pair<false, true, true>(pr, nullptr, st);
+    case LoraKind::kGrad:  // v^T x, dy^T u
+      return launch_pair<true, true, false>(pr, nullptr, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_lora_grads(const uint16_t *v, const uint16_t *x, const uint16_t *dy, const uint16_t *u, int64_t T,
+                             int64_t N, int64_t K, int r, float scale, float *grad_A, float *grad_B, float *part,
+                             size_t part_a_floats, hipStream_t st) {
+  // grad_A = s v^T x [r x K] and grad_B = s dy^T u [N x r], contraction over the tokens
+  const LoraProblem a = make_problem(v, r, x, K, r, K, T, scale, grad_A, part);
+  const LoraProblem b = make_problem(dy, N, u, r, N, r, T, scale, grad_B, part + part_a_floats);
+  if ((a.chunk == LT * 8) == (b.chunk == LT * 8)) return launch_pair<true, true, false>(a, &b, st);
+  const hipError_t e = launch_pair<true, true, false>(a, nullptr, st);
+  return e != hipSuccess ? e : launch_pair<true, true, false>(b, nullptr, st);
 }
 
 }  // namespace qlora
