@@ -234,6 +234,43 @@ struct Producer {
     L.ch = decode_constant(s.q, s.s2, mu);
   }
 
+  // Levels of word v (8 codes) of a stage.
+  __device__ __forceinline__ void read_word(const Stage &s, int v, const float *lut, Levels &L) const {
+    const char *base = (const char *)lut;
+    uint32_t ev = (s.code[v] << 2) & 0x3C3C3C3Cu, od = (s.code[v] >> 2) & 0x3C3C3C3Cu;
+    asm("" : "+v"(ev), "+v"(od));
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      L.lv[8 * v + 2 * k] = *(const float *)(base + __builtin_amdgcn_ubfe(ev, 8 * k, 8));
+      L.lv[8 * v + 2 * k + 1] = *(const float *)(base + __builtin_amdgcn_ubfe(od, 8 * k, 8));
+    }
+  }
+
+  // Products of word v of a stage, rounded to bf16, as one 16-byte store.
+  __device__ __forceinline__ void write_word(const Levels &L, int v, uint16_t *sb) const {
+    uint16_t *dst = kTransW ? &sb[(ptid >> 2) * TLD + 32 * (ptid & 3)] : &sb[(ptid >> 1) * QLD + 32 * (ptid & 1)];
+    u32x4 o;
+#pragma unroll
+    for (int d = 0; d < 4; ++d)
+      o[d] = pack_bf16x2(decode_product(L.lv[8 * v + 2 * d], L.ch), decode_product(L.lv[8 * v + 2 * d + 1], L.ch));
+    *(u32x4 *)&dst[8 * v] = o;
+  }
+
+  // One steady-state decode step: the levels of the next stage (codes in
+  // `next`) word by word, each group of eight reads followed by the products
+  // of a word of the current stage, so that at most nine LDS operations are
+  // in flight (the counter tracks fifteen) and the products cover the reads'
+  // latency.
+  __device__ __forceinline__ void step_decode(const Stage &next, const float *lut, Levels &Lnext,
+                                              const Levels &Lcur, uint16_t *sb) const {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      read_word(next, v, lut, Lnext);
+      write_word(Lcur, v, sb);
+    }
+    Lnext.ch = decode_constant(next.q, next.s2, mu);
+  }
+
   // The decoded stage into LDS: fl32 products rounded to bf16, 16-byte stores.
   __device__ __forceinline__ void store_w(const Levels &L, uint16_t *sb) const {
     uint16_t *dst = kTransW ? &sb[(ptid >> 2) * TLD + 32 * (ptid & 3)] : &sb[(ptid >> 1) * QLD + 32 * (ptid & 1)];
@@ -287,11 +324,9 @@ __device__ __forceinline__ void producer_loop_full(const Producer<kTransW> &p, i
   // in CREAD), CLOAD (codes of stage K_+2, levels already read) <- stage K_+5
 #define QGEMM_PRODUCER_STEP(K_, LCUR, LNEXT, CREAD, CLOAD)                           \
   if ((K_) < nk) {                                                                    \
-    p.read_levels(CREAD, lut, LNEXT);                                                 \
-    __builtin_amdgcn_sched_barrier(0);                                                \
     p.template load_w<true>(st((K_) + 5), CLOAD);                                     \
     __builtin_amdgcn_sched_barrier(0);                                                \
-    p.store_w(LCUR, sb[(K_) & 1]);                                                    \
+    p.step_decode(CREAD, lut, LNEXT, LCUR, sb[(K_) & 1]);                             \
     __builtin_amdgcn_sched_barrier(0);                                                \
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));                                   \
     wg_barrier();                                                                     \
@@ -582,10 +617,13 @@ __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act
   // last step the loads read a stage nobody uses.  Exactly 8 DMAs per step, so
   // waiting for at most 8 outstanding before the barrier means stage k+2 has
   // landed; every read of stage k+1 has returned by then too.
+  int ring = 0;  // kt % kActStages, kept by rotation (a 64-bit remainder costs the scalar unit dozens of instructions)
   for (int64_t kt = 0; kt < nk; ++kt) {
-    uint16_t *dma_dst = sa[kt % kActStages] + 64 * cw * 64;
+    const int ring1 = ring + 1 == kActStages ? 0 : ring + 1;
+    uint16_t *dma_dst = sa[ring] + 64 * cw * 64;
     const int64_t dma_kt = min(kt + 3, nk - 1);
-    const uint16_t *na = sa[(kt + 1) % kActStages], *nb = sb[(kt + 1) & 1];
+    const uint16_t *na = sa[ring1], *nb = sb[(kt + 1) & 1];
+    ring = ring1;
 #pragma unroll
     for (int kk = 0; kk < QBK / 16; ++kk) {
 #pragma unroll
