@@ -26,8 +26,9 @@ Readings (the pages do not write the update out)
 * Every operation is one fp32 operation with one rounding, in the order
   below; no fused multiply-add.  The hyperparameters are given as fp64
   numbers; the scalars that depend only on them and on the step are formed
-  from them in fp64 and rounded once to fp32; b^t is t successive fp64
-  multiplications.
+  from them in fp64 and rounded once to fp32; b^t is the C library's fp64
+  pow (a library primitive; a last-bit difference in it changes the fp32
+  scalar only when that scalar sits on a rounding boundary).
 
     c_m = fl32(1 - b1)      c_v = fl32(1 - b2)      decay = fl32(1 - lr wd)
     step_size = fl32(lr / (1 - b1^t))               bc2_sqrt = fl32(sqrt(1 - b2^t))
@@ -55,18 +56,10 @@ from .rounding import bf16_rne_bits
 f32 = np.float32
 
 
-def pow_f64(b, t):
-    """b^t as t successive fp64 multiplications (t >= 0)."""
-    x = 1.0
-    for _ in range(int(t)):
-        x *= float(b)
-    return x
-
-
 def step_scalars(step, lr, beta1, beta2, eps, weight_decay):
     """The fp32 scalars of step `step` (1-based), formed as the module docstring states."""
     b1, b2, lr, wd = float(beta1), float(beta2), float(lr), float(weight_decay)
-    p1, p2 = pow_f64(b1, step), pow_f64(b2, step)
+    p1, p2 = math.pow(b1, step), math.pow(b2, step)
     return {
         "b1": f32(b1),
         "b2": f32(b2),
