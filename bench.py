@@ -336,6 +336,53 @@ def extra_measurements(torch, qlora, steps):
     return out
 
 
+def extra_adamw(torch, qlora, workloads, steps):
+    """AdamW over the adapters of the 7B layer set at r = 64, 32 layers in one
+    flat buffer (159,907,840 values): 16 B read and 14 B written per value with
+    the states in HBM; then one layer's adapters with both moments in pinned
+    host memory (16 B per value cross the host link)."""
+    out = {}
+    n = workloads.adapter_numel(workloads.SHAPES_7B, 64, 32)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    p = torch.empty(n, dtype=torch.float32, device="cuda").normal_(0.0, 0.01, generator=g)
+    pb = torch.empty(n, dtype=torch.bfloat16, device="cuda")
+    gr = torch.empty(n, dtype=torch.float32, device="cuda").normal_(0.0, 1e-3, generator=g)
+    m = torch.zeros(n, dtype=torch.float32, device="cuda")
+    v = torch.zeros(n, dtype=torch.float32, device="cuda")
+    it = iter(range(1, 1 << 30))
+    run = lambda: qlora.adamw_step(p, pb, gr, m, v, next(it), lr=2e-4, weight_decay=0.01)
+    for _ in range(3):
+        run()
+    reps = max(5, steps // 5)
+    t, _ = time_region(torch, run, reps)
+    qlora.kernel_timing_read()
+    qlora.kernel_timing_enable(True)
+    time_region(torch, run, reps)
+    qlora.kernel_timing_enable(False)
+    launches, ms = qlora.kernel_timing_read()["adamw"]
+    per = 30 * n
+    kern_us = ms / max(launches, 1) * 1e3
+    out["adamw_7b_adapters"] = {"GB/s": per * reps / t / 1e9, "frac_hbm": per * reps / t / 1e9 / PEAK_HBM_GBS,
+                                "us_per_step": t / reps * 1e6, "kernel_us": kern_us,
+                                "kernel_GB/s": per / (kern_us * 1e-6) / 1e9 if launches else None,
+                                "values": n, "bytes_per_value": 30, "layers": 32, "r": 64}
+    del p, pb, gr, m, v
+    n1 = workloads.adapter_numel(workloads.SHAPES_7B, 64)
+    p = torch.empty(n1, dtype=torch.float32, device="cuda").normal_(0.0, 0.01, generator=g)
+    pb = torch.empty(n1, dtype=torch.bfloat16, device="cuda")
+    gr = torch.empty(n1, dtype=torch.float32, device="cuda").normal_(0.0, 1e-3, generator=g)
+    m = torch.zeros(n1, dtype=torch.float32).pin_memory()
+    v = torch.zeros(n1, dtype=torch.float32).pin_memory()
+    run = lambda: qlora.adamw_step(p, pb, gr, m, v, next(it), lr=2e-4, weight_decay=0.01)
+    run()
+    reps = 5
+    t, _ = time_region(torch, run, reps)
+    out["adamw_paged_7b_layer"] = {"us_per_step": t / reps * 1e6, "host_link_GB/s": 16 * n1 * reps / t / 1e9,
+                                   "values": n1, "host_bytes_per_value": 16, "device_bytes_per_value": 14}
+    return out
+
+
 def cpu_baseline(case, budget_s=12.0):
     """The oracle (dequantize + fp64 forward + backward) timed on this host's cores."""
     import oracle
@@ -419,6 +466,8 @@ def main():
                          "path, rotating over more than 1 GB of distinct packed weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
+    ap.add_argument("--extra-only", choices=["adamw"], default=None,
+                    help="run only this extra measurement and print its JSON (for profiling it alone)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before the steps, copy 256 MiB device to device three times (untimed): the "
                          "reference kernel that scales the HBM byte counters of a profiled run")
@@ -433,6 +482,16 @@ def main():
     from bit_quantized_finetuning_quant_amd import qlora, workloads
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+    if args.extra_only == "adamw":
+        print(json.dumps(extra_adamw(torch, qlora, workloads, args.steps)), flush=True)
+        return
     dev_bf16, dev_f32 = dev_helpers(torch)
     tokens = 2048 if args.workload == "7b_attn" else 1
     log(f"generating the 7B projection workload (4096x4096, T={tokens}, r=64)")
@@ -441,13 +500,6 @@ def main():
     if tokens == 1:
         step = RotatingStep(step, rotating_weights(torch, qlora, case.n_out, case.n_in, 1.1e9))
     T, N, K, r = case.tokens, case.n_out, case.n_in, case.r
-    if args.copy_calibration:
-        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -484,10 +536,11 @@ def main():
         "roofline": roofline,
     }
     if not args.no_extra and tokens > 1:
-        log("extra measurements: layer sets, bulk 65B store, bulk dequant, T=1 path, quantize")
+        log("extra measurements: layer sets, bulk 65B store, bulk dequant, T=1 path, quantize, adapter AdamW")
         extra = extra_layers(torch, qlora, workloads, args.steps)
         extra["bulk_65b"] = extra_bulk_65b(torch, qlora, workloads)
         extra.update(extra_measurements(torch, qlora, args.steps))
+        extra.update(extra_adamw(torch, qlora, workloads, args.steps))
         result["extra"] = extra
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on host cores")

@@ -92,6 +92,30 @@ qlora_status check_linear(int64_t T, const qlora_nf4_weight *q, int r, float sca
   return QLORA_OK;
 }
 
+// The address a kernel uses for p: p itself for device or managed memory, the
+// mapped device address for pinned host memory (hipHostMalloc), and false for
+// memory the GPU cannot reach (pageable host memory, unknown pointers).
+bool device_address(const void *p, void **dev) {
+  hipPointerAttribute_t a;
+  if (hipPointerGetAttributes(&a, p) != hipSuccess) {
+    (void)hipGetLastError();
+    return false;
+  }
+  switch (a.type) {
+    case hipMemoryTypeDevice:
+    case hipMemoryTypeManaged:
+    case hipMemoryTypeUnified:
+      *dev = const_cast<void *>(p);
+      return true;
+    case hipMemoryTypeHost:
+      if (!a.devicePointer || !a.hostPointer) return false;
+      *dev = (char *)a.devicePointer + ((const char *)p - (const char *)a.hostPointer);
+      return true;
+    default:
+      return false;
+  }
+}
+
 }  // namespace
 
 extern "C" {
@@ -140,7 +164,8 @@ const char *qlora_status_string(qlora_status s) {
     case QLORA_ERR_DTYPE: return "unknown dtype";
     case QLORA_ERR_HIP: return "HIP runtime error at launch";
     case QLORA_ERR_NONFINITE: return "NaN or Inf in the quantized weight";
-    case QLORA_ERR_VALUE: return "a scalar argument is not finite";
+    case QLORA_ERR_VALUE: return "a scalar argument is not finite or out of range";
+    case QLORA_ERR_MEMORY: return "a buffer is not reachable by the GPU (pageable host memory?)";
   }
   return "unknown status";
 }
@@ -203,6 +228,40 @@ qlora_status qlora_linear_bwd(const uint16_t *dy, const uint16_t *x, int64_t T, 
   if (ws_bytes < p.total) return QLORA_ERR_WORKSPACE;
   hipError_t e = launch_linear_bwd(p, dy, x, qweight(q), A, B, scale, u, grad_x, grad_A, grad_B, (char *)ws,
                                    tables().cb, (hipStream_t)stream);
+  return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP;
+}
+
+qlora_status qlora_adamw_step(float *param, uint16_t *param_bf16, const float *grad, float *exp_avg,
+                              float *exp_avg_sq, int64_t n, int64_t step, double lr, double beta1, double beta2,
+                              double eps, double weight_decay, void *stream) {
+  if (n < 0 || n > kMaxNumel) return QLORA_ERR_SHAPE;
+  if (step < 1 || !std::isfinite(lr) || !std::isfinite(eps) || !std::isfinite(weight_decay) || lr < 0 ||
+      eps < 0 || weight_decay < 0 || !(beta1 >= 0 && beta1 < 1) || !(beta2 >= 0 && beta2 < 1))
+    return QLORA_ERR_VALUE;
+  if (n == 0) return QLORA_OK;
+  if (!param || !param_bf16 || !grad || !exp_avg || !exp_avg_sq) return QLORA_ERR_NULL;
+  if (!aligned16(param) || !aligned16(param_bf16) || !aligned16(grad) || !aligned16(exp_avg) ||
+      !aligned16(exp_avg_sq))
+    return QLORA_ERR_ALIGN;
+  void *d[5];
+  const void *h[5] = {param, param_bf16, grad, exp_avg, exp_avg_sq};
+  for (int i = 0; i < 5; ++i)
+    if (!device_address(h[i], &d[i]) || !aligned16(d[i])) return QLORA_ERR_MEMORY;
+  // Scalars of this step: fp64 from the hyperparameters, one rounding to fp32.
+  const double bc1 = 1.0 - std::pow(beta1, (double)step);
+  const double bc2 = 1.0 - std::pow(beta2, (double)step);
+  AdamwScalars sc;
+  sc.b1 = (float)beta1;
+  sc.b2 = (float)beta2;
+  sc.c_m = (float)(1.0 - beta1);
+  sc.c_v = (float)(1.0 - beta2);
+  sc.decay = (float)(1.0 - lr * weight_decay);
+  sc.step_size = (float)(lr / bc1);
+  sc.bc2_sqrt = (float)std::sqrt(bc2);
+  sc.eps = (float)eps;
+  if (!std::isfinite(sc.step_size) || !(sc.bc2_sqrt > 0.0f)) return QLORA_ERR_VALUE;
+  hipError_t e = launch_adamw((float *)d[0], (uint16_t *)d[1], (const float *)d[2], (float *)d[3], (float *)d[4], n,
+                              sc, (hipStream_t)stream);
   return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP;
 }
 

@@ -73,7 +73,14 @@ LinearPlan plan_linear(int64_t T, int64_t N, int64_t K, int r);
 
 // Optional event bracketing of the fused GEMM launches (diagnostics).
 // Diagnostics: HIP events around the main kernel of each kind (linear.hip).
-enum TimedKind : int { kTimedQgemmFwd = 0, kTimedQgemmDx = 1, kTimedGemvFwd = 2, kTimedGemvBwd = 3, kTimedKinds = 4 };
+enum TimedKind : int {
+  kTimedQgemmFwd = 0,
+  kTimedQgemmDx = 1,
+  kTimedGemvFwd = 2,
+  kTimedGemvBwd = 3,
+  kTimedAdamw = 4,
+  kTimedKinds = 5
+};
 struct TimedLaunch {
   hipEvent_t start, stop;
   int kind;
@@ -91,5 +98,19 @@ hipError_t launch_linear_bwd(const LinearPlan &p, const uint16_t *dy, const uint
                              const uint16_t *A, const uint16_t *B, float scale, const uint16_t *u,
                              uint16_t *grad_x, float *grad_A, float *grad_B, char *ws, const Codebook &cb,
                              hipStream_t st);
+
+// AdamW update of a flat fp32 adapter buffer (optim.hip).  The scalars that
+// depend only on the hyperparameters and the step, each formed in fp64 and
+// rounded once to fp32 on the host.
+struct AdamwScalars {
+  float b1, b2;        // fl32(beta1), fl32(beta2)
+  float c_m, c_v;      // fl32(1 - beta1), fl32(1 - beta2)
+  float decay;         // fl32(1 - lr * weight_decay)
+  float step_size;     // fl32(lr / (1 - beta1^t))
+  float bc2_sqrt;      // fl32(sqrt(1 - beta2^t))
+  float eps;           // fl32(eps)
+};
+hipError_t launch_adamw(float *param, uint16_t *param_bf16, const float *grad, float *exp_avg, float *exp_avg_sq,
+                        int64_t n, const AdamwScalars &s, hipStream_t st);
 
 }  // namespace qlora

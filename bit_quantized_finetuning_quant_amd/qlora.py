@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_PKG, "libqlora_gfx950.so")
 QLORA_F32, QLORA_BF16 = 0, 1
 STATUS_NAMES = {0: "QLORA_OK", 1: "QLORA_ERR_NULL", 2: "QLORA_ERR_SHAPE", 3: "QLORA_ERR_ALIGN",
                 4: "QLORA_ERR_WORKSPACE", 5: "QLORA_ERR_DTYPE", 6: "QLORA_ERR_HIP",
-                7: "QLORA_ERR_NONFINITE", 8: "QLORA_ERR_VALUE"}
+                7: "QLORA_ERR_NONFINITE", 8: "QLORA_ERR_VALUE", 9: "QLORA_ERR_MEMORY"}
 
 
 class QloraError(RuntimeError):
@@ -49,6 +49,8 @@ _SIGNATURES = {
     "qlora_linear_fwd": (ctypes.c_int, [_P, _I64, _P, _P, _P, ctypes.c_int, ctypes.c_float, _P, _P, _P, _SZ, _P]),
     "qlora_linear_bwd": (ctypes.c_int, [_P, _P, _I64, _P, _P, _P, ctypes.c_int, ctypes.c_float, _P, _P, _P, _P,
                                         _P, _SZ, _P]),
+    "qlora_adamw_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, ctypes.c_double, ctypes.c_double,
+                                        ctypes.c_double, ctypes.c_double, ctypes.c_double, _P]),
     "qlora_status_read": (ctypes.c_int, [_P, _P]),
     "qlora_kernel_timing_enable": (None, [ctypes.c_int]),
     "qlora_kernel_timing_read": (ctypes.c_int, [_P, _P]),
@@ -103,7 +105,7 @@ def linear_workspace_bytes(tokens: int, n_out: int, n_in: int, r: int) -> int:
     return int(lib().qlora_linear_workspace_bytes(tokens, n_out, n_in, r))
 
 
-TIMED_KINDS = ("qgemm_fwd", "qgemm_dx", "gemv_fwd", "gemv_bwd")
+TIMED_KINDS = ("qgemm_fwd", "qgemm_dx", "gemv_fwd", "gemv_bwd", "adamw")
 
 
 def kernel_timing_enable(on: bool) -> None:
@@ -249,3 +251,25 @@ def linear_bwd(dy, x, q: NF4Weight, A, B, scale: float, u=None, need_grad_x=True
                                   _ptr(u), _ptr(grad_x), _ptr(grad_A), _ptr(grad_B), _ptr(ws), ws.numel(),
                                   _stream(stream)), "qlora_linear_bwd")
     return grad_x, grad_A, grad_B
+
+
+def adamw_step(param, param_bf16, grad, exp_avg, exp_avg_sq, step: int, lr: float, beta1: float = 0.9,
+               beta2: float = 0.999, eps: float = 1e-8, weight_decay: float = 0.0, stream=None) -> None:
+    """One AdamW update of a flat fp32 adapter buffer, in place (see qlora_adamw_step).
+
+    param, grad, exp_avg, exp_avg_sq: contiguous float32 tensors of n elements;
+    param_bf16: bfloat16 (or int16) tensor of n elements.  The states may be
+    pinned host tensors (``pin_memory=True``): the kernel reads them in place.
+    """
+    torch = _torch()
+    n = param.numel()
+    for name, t, dt in (("param", param, torch.float32), ("grad", grad, torch.float32),
+                        ("exp_avg", exp_avg, torch.float32), ("exp_avg_sq", exp_avg_sq, torch.float32)):
+        if t.dtype != dt or not t.is_contiguous() or t.numel() != n:
+            raise ValueError(f"{name} must be a contiguous float32 tensor of {n} elements")
+    if param_bf16.dtype not in (torch.bfloat16, torch.int16) or not param_bf16.is_contiguous() \
+            or param_bf16.numel() != n:
+        raise ValueError(f"param_bf16 must be a contiguous bfloat16 tensor of {n} elements")
+    _check(lib().qlora_adamw_step(_ptr(param), _ptr(param_bf16), _ptr(grad), _ptr(exp_avg), _ptr(exp_avg_sq), n,
+                                  int(step), float(lr), float(beta1), float(beta2), float(eps), float(weight_decay),
+                                  _stream(stream)), "qlora_adamw_step")

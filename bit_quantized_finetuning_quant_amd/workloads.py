@@ -26,6 +26,13 @@ models and datasets are not needed, these stand in for them):
                 sequence zero (5.08% padding rows); seed 4.
 * ``65b_bulk``  80 layers of the 65B shapes, W ~N(0, 0.02), one child seed per
                 layer from SeedSequence(5).
+* ``adamw``     a flat adapter buffer of n values: master weights ~N(0, 0.01)
+                with the B half of each adapter (here: every second 4096-run)
+                zero, as LoRA starts B at zero; gradients ~N(0, 1) times
+                10^U(-6, -1) (six decades, as adapter gradients spread), with
+                1% exact zeros; states start at zero; one child stream per
+                step from SeedSequence(seed).  The 7B layer set's adapters at
+                r = 64 hold 32 x 4,997,120 values (``adapter_numel``).
 """
 
 from dataclasses import dataclass
@@ -183,3 +190,28 @@ def crafted_weight(seed: int, n_out: int, n_in: int) -> np.ndarray:
         elif kind == 6:  # tiny normal block
             blk[:] = (blk * 1e-30).astype(np.float32)
     return w.reshape(n_out, n_in)
+
+
+def adapter_numel(shapes, r: int, layers: int = 1) -> int:
+    """Values in the A [r x n_in] and B [n_out x r] adapters of `layers` copies of `shapes`."""
+    return layers * sum(r * k + n * r for _, n, k in shapes)
+
+
+def adamw_params(seed: int, n: int) -> np.ndarray:
+    """Initial fp32 master copy of n adapter values (see ``adamw`` above)."""
+    rng = np.random.default_rng(np.random.SeedSequence(seed).spawn(1)[0])
+    p = _normal(rng, (n,), 0.01)
+    idx = np.arange(n)
+    p[(idx // 4096) % 2 == 1] = 0.0
+    return p
+
+
+def adamw_grads(seed: int, n: int, steps: int):
+    """`steps` fp32 gradient vectors of n values, one child stream per step."""
+    out = []
+    for ss in np.random.SeedSequence(seed).spawn(steps + 1)[1:]:
+        rng = np.random.default_rng(ss)
+        g = rng.standard_normal(n) * 10.0 ** rng.uniform(-6.0, -1.0, n)
+        g[rng.random(n) < 0.01] = 0.0
+        out.append(g.astype(np.float32))
+    return out

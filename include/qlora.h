@@ -53,7 +53,8 @@ typedef enum {
   QLORA_ERR_DTYPE = 5,      /* unknown dtype code                                   */
   QLORA_ERR_HIP = 6,        /* the HIP runtime reported an error at launch          */
   QLORA_ERR_NONFINITE = 7,  /* (deferred) NaN or Inf met while quantizing           */
-  QLORA_ERR_VALUE = 8       /* a scalar argument is not finite                      */
+  QLORA_ERR_VALUE = 8,      /* a scalar argument is not finite or out of range      */
+  QLORA_ERR_MEMORY = 9      /* a buffer is neither device nor pinned host memory    */
 } qlora_status;
 
 typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
@@ -153,6 +154,36 @@ qlora_status qlora_linear_bwd(const uint16_t *dy, const uint16_t *x, int64_t T,
                               float *grad_A, float *grad_B, void *ws, size_t ws_bytes,
                               void *stream);
 
+/* AdamW update of n adapter values held in one flat buffer (the caller lays
+ * the A and B matrices of its adapters out back to back).  Only the adapters
+ * train, and the optimizer keeps two moments per trained value ("LoRA vs.
+ * QLoRA vs. Full Fine-Tuning", section "Quanta VRAM cada método precisa?").
+ * For step t >= 1, with the scalars formed in fp64 and rounded once to fp32
+ *   c_m = 1 - beta1, c_v = 1 - beta2, decay = 1 - lr * weight_decay,
+ *   step_size = lr / (1 - beta1^t), bc2_sqrt = sqrt(1 - beta2^t)   (C pow),
+ * every element is updated with one fp32 rounding per operation, no fused
+ * multiply-add, in this order:
+ *   m <- fl32(beta1) m + c_m g;       v <- fl32(beta2) v + c_v (g g);
+ *   d  = sqrt(v) / bc2_sqrt + eps;     p <- p decay;
+ *   p <- p - step_size (m / d);        param_bf16 = bf16_round_nearest_even(p).
+ * param (fp32 master copy), exp_avg (m) and exp_avg_sq (v) are updated in
+ * place; param_bf16 receives the copy the linear calls read; grad is fp32
+ * (e.g. the grad_A / grad_B of qlora_linear_bwd).  All five are 16-B aligned
+ * and hold n elements; they must not overlap.
+ * Paged states ("qlora" entry, section "como funciona"): exp_avg and
+ * exp_avg_sq (and any other buffer) may be pinned host memory allocated with
+ * hipHostMalloc instead of device memory; the kernel then reads and writes
+ * them in place across the host link, and nothing is copied beforehand.
+ * Pageable host memory (plain malloc) is rejected with QLORA_ERR_MEMORY.
+ * Errors: QLORA_ERR_SHAPE if n < 0 or n > 2^37; QLORA_ERR_VALUE if step < 1,
+ * a beta is outside [0, 1), lr, eps or weight_decay is negative or not finite,
+ * or step_size is not finite; n == 0 enqueues nothing.  A NaN or Inf in grad
+ * or in the states propagates into the outputs of that element only.          */
+qlora_status qlora_adamw_step(float *param, uint16_t *param_bf16, const float *grad,
+                              float *exp_avg, float *exp_avg_sq, int64_t n, int64_t step,
+                              double lr, double beta1, double beta2, double eps,
+                              double weight_decay, void *stream);
+
 /* ---- diagnostics ---------------------------------------------------------- */
 
 /* Kernel timing for benchmarks.  While enabled (non-zero), every launch of
@@ -164,7 +195,8 @@ enum {
   QLORA_TIMED_QGEMM_DX = 1,  /* dequant-fused GEMM, grad_x: dy W_hat (+ LoRA)         */
   QLORA_TIMED_GEMV_FWD = 2,  /* few-token forward, weight pass (T <= 4)                */
   QLORA_TIMED_GEMV_BWD = 3,  /* few-token backward, weight and adapter pass (T <= 4)   */
-  QLORA_TIMED_KINDS = 4
+  QLORA_TIMED_ADAMW = 4,     /* adapter AdamW update, whole 4096-element tiles          */
+  QLORA_TIMED_KINDS = 5
 };
 void qlora_kernel_timing_enable(int enable);
 

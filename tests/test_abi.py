@@ -115,3 +115,20 @@ def test_product_path_has_no_fallback(monkeypatch, tmp_path):
     monkeypatch.setattr(qlora, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="missing"):
         qlora.nf4_codebook()
+
+
+def _adamw(n=4096, step=1, lr=1e-3, b1=0.9, b2=0.999, eps=1e-8, wd=0.0, p=0x10000, pb=0x20000, g=0x30000,
+           m=0x40000, v=0x50000):
+    return qlora.lib().qlora_adamw_step(p, pb, g, m, v, n, step, lr, b1, b2, eps, wd, None)
+
+
+def test_adamw_argument_validation_before_any_launch():
+    assert _adamw(n=-1) == 2  # QLORA_ERR_SHAPE
+    assert _adamw(n=(1 << 37) + 1) == 2
+    for bad in (dict(step=0), dict(b1=1.0), dict(b2=-0.1), dict(lr=float("nan")), dict(lr=-1e-3),
+                dict(eps=float("inf")), dict(wd=-0.1), dict(b1=float("nan"))):
+        assert _adamw(**bad) == 8, bad  # QLORA_ERR_VALUE
+    assert _adamw(n=0) == 0  # nothing to do, nothing enqueued
+    assert _adamw(p=None) == 1 and _adamw(v=None) == 1  # QLORA_ERR_NULL
+    assert _adamw(g=0x30004) == 3 and _adamw(pb=0x20002) == 3  # QLORA_ERR_ALIGN
+    assert qlora.status_string(9).startswith("a buffer is not reachable")
