@@ -40,6 +40,11 @@ constant decode (``dequantize_constants``)
     multiply-add.
 weight decode (``dequantize``)
     w_hat = bf16_RNE(fl32(CB[code] * c1hat_b)).
+without double quantization (``quantize(..., double_quant=False)``)
+    The page prices the fp32 constants before their FP8 quantization at
+    0.5 bit/param; the variant stores c1_b itself (fp32, one per block; no
+    mean, no FP8 bytes, no group scales) and decodes with c1hat_b = c1_b:
+    4.5 bits per parameter.
 
 Pins (tests/test_oracle_nf4.py): Fraction brute-force nearest code on tiny
 tensors and on crafted blocks (ties at the four fp32-representable
@@ -73,6 +78,7 @@ class NF4Quantized:
     absmax_scale: np.ndarray  # float32 [ngroups]
     absmax_mean: np.float32
     absmax: np.ndarray  # float32 [nblocks] first-level constants (not stored; kept for checks)
+    double_quant: bool = True  # False: absmax_scale holds the nblocks fp32 constants c1 themselves
 
     @property
     def numel(self) -> int:
@@ -163,8 +169,9 @@ def dequantize_constants(q: np.ndarray, s2: np.ndarray, mu: np.float32) -> np.nd
     return (prod + np.float32(mu)).astype(np.float32)
 
 
-def quantize(w, n_out: int, n_in: int, src: str = "f32") -> NF4Quantized:
-    """Quantize a [n_out x n_in] weight (fp32, or bf16 bit patterns) to NF4 + FP8 constants."""
+def quantize(w, n_out: int, n_in: int, src: str = "f32", double_quant: bool = True) -> NF4Quantized:
+    """Quantize a [n_out x n_in] weight (fp32, or bf16 bit patterns) to NF4 + FP8 constants
+    (or, with double_quant=False, NF4 + the fp32 block constants)."""
     flat = _as_f32(w, src)
     if flat.size != n_out * n_in:
         raise ValueError("shape mismatch")
@@ -173,6 +180,9 @@ def quantize(w, n_out: int, n_in: int, src: str = "f32") -> NF4Quantized:
     c1 = block_absmax(flat)
     codes = nearest_codes(flat, c1).reshape(-1)
     packed = pack_codes(codes, flat.size)
+    if not double_quant:
+        return NF4Quantized(n_out, n_in, packed, np.zeros(0, np.uint8), c1.copy(), np.float32(0.0), c1,
+                            double_quant=False)
     mu = exact_mean_f32(c1)
     q, s2 = double_quantize(c1, mu)
     return NF4Quantized(n_out, n_in, packed, q, s2, np.float32(mu), c1)
@@ -182,7 +192,10 @@ def dequantize(qw: NF4Quantized) -> np.ndarray:
     """Decode to bf16 bit patterns [n_out x n_in]: bf16_RNE(fl32(CB[code] * c1hat))."""
     cb = nf4_codebook()
     codes = unpack_codes(qw.codes, qw.numel)
-    c1hat = dequantize_constants(qw.absmax_fp8, qw.absmax_scale, qw.absmax_mean)
+    if qw.double_quant:
+        c1hat = dequantize_constants(qw.absmax_fp8, qw.absmax_scale, qw.absmax_mean)
+    else:
+        c1hat = np.asarray(qw.absmax_scale, dtype=np.float32)
     blk = np.arange(qw.numel) // BLOCK
     w32 = (cb[codes] * c1hat[blk]).astype(np.float32)
     return bf16_rne_bits(w32).reshape(qw.n_out, qw.n_in)

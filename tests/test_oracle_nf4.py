@@ -220,3 +220,66 @@ def test_sampled_block_decode_matches_full_dequantization():
     mu = oracle.exact_mean_f32(c1)
     blocks = np.concatenate([rng.integers(0, full.shape[0], 40), [0, full.shape[0] - 1, 255, 256, 1024]])
     assert np.array_equal(oracle_blocks(flat, c1, mu, blocks), full[blocks])
+
+
+# ---- without double quantization (fp32 block constants) --------------------------------------
+
+def test_fp32_constants_decode_by_exact_rationals():
+    """With the fp32 constants stored as they are, w_hat = bf16(RN32(CB[code] * c1)); the
+    product is formed here as an exact rational and rounded once, independently of numpy."""
+    rng = np.random.default_rng(31)
+    n_out, n_in = 5, 77  # ragged: 385 elements, a partial last block, an odd nibble count
+    w = (rng.standard_t(4, size=(n_out, n_in)) * 0.03).astype(np.float32)
+    w[1, :] = 0.0
+    q = oracle.quantize(w, n_out, n_in, double_quant=False)
+    assert not q.double_quant and q.absmax_fp8.size == 0
+    assert q.absmax_scale.dtype == np.float32 and q.absmax_scale.size == -(-w.size // BLOCK)
+    assert np.array_equal(q.absmax_scale.view(np.uint32), oracle.block_absmax(w.reshape(-1)).view(np.uint32))
+    cb = oracle.nf4_codebook()
+    codes = oracle.unpack_codes(q.codes, w.size)
+    got = oracle.dequantize(q).reshape(-1)
+    for e in range(w.size):
+        prod = Fraction(float(cb[codes[e]])) * Fraction(float(q.absmax_scale[e // BLOCK]))
+        want = oracle.bf16_rne_bits(np.array([oracle.rn32_from_fraction(prod)], np.float32))[0]
+        assert got[e] == want, e
+
+
+def test_fp32_constants_every_block_peaks_at_its_absmax():
+    """The absmax element of a block takes code 0 or 15 (level -1 or +1), so without double
+    quantization the largest decoded magnitude of every non-zero block is exactly bf16(c1)."""
+    w = workloads.custom_case(64, 512, 1, 8, 16.0, seed=32).w
+    q = oracle.quantize(w, 64, 512, double_quant=False)
+    wh = oracle.bf16_bits_to_f32(oracle.dequantize(q)).reshape(-1, BLOCK)
+    c1 = oracle.block_absmax(w.reshape(-1))
+    peak = np.abs(wh).max(axis=1)
+    want = oracle.bf16_bits_to_f32(oracle.bf16_rne_bits(c1))
+    assert np.array_equal(peak, want)
+
+
+def test_fp32_constants_agree_with_double_quant_where_it_is_exact():
+    """Codes depend on c1 only, so both variants store the same codes; where the FP8 stage
+    reproduces c1 exactly (here: every block of a group has the same absmax, so d = 0 and
+    c1hat = mu = c1) the two decodes are identical, elsewhere they differ."""
+    rng = np.random.default_rng(33)
+    n_out, n_in = 64, 512  # 512 blocks = 2 groups
+    w = (rng.standard_normal((n_out, n_in)) * 0.02).astype(np.float32)
+    blocks = w.reshape(-1, BLOCK)
+    blocks[:, 0] = np.float32(0.125)  # every block's absmax is exactly 0.125
+    blocks[:, 1:] = np.clip(blocks[:, 1:], -0.12, 0.12)
+    w = blocks.reshape(n_out, n_in)
+    qa = oracle.quantize(w, n_out, n_in)
+    qb = oracle.quantize(w, n_out, n_in, double_quant=False)
+    assert np.array_equal(qa.codes, qb.codes)
+    assert qa.absmax_mean == np.float32(0.125) and np.all(qa.absmax_fp8 == 0)
+    assert np.array_equal(oracle.dequantize(qa), oracle.dequantize(qb))
+    # a generic weight: same codes, different constants, different decodes somewhere
+    w2 = (rng.standard_normal((n_out, n_in)) * 0.02).astype(np.float32)
+    qa2, qb2 = oracle.quantize(w2, n_out, n_in), oracle.quantize(w2, n_out, n_in, double_quant=False)
+    assert np.array_equal(qa2.codes, qb2.codes)
+    assert not np.array_equal(oracle.dequantize(qa2), oracle.dequantize(qb2))
+
+
+def test_fp32_constants_bit_budget_is_four_and_a_half():
+    figs = json.load(open(GOLDEN))
+    for n_out, n_in in ((4096, 4096), (11008, 4096), (8192, 22016)):
+        assert oracle.bits_per_param(n_out, n_in, double_quant=False) == 4 + figs["fp32_constant_bits_per_param"]["value"]
