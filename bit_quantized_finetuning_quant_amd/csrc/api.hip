@@ -69,18 +69,23 @@ bool shape_ok(int64_t n_out, int64_t n_in) {
   return n_out > 0 && n_in > 0 && n_out <= kMaxNumel && n_in <= kMaxNumel && n_out * n_in <= kMaxNumel;
 }
 
+bool double_quantized(const qlora_nf4_weight *q) { return (q->flags & QLORA_NF4_FP32_CONSTANTS) == 0u; }
+
 qlora_status check_weight(const qlora_nf4_weight *q) {
   if (!q) return QLORA_ERR_NULL;
   if (!shape_ok(q->n_out, q->n_in)) return QLORA_ERR_SHAPE;
-  if (!q->codes || !q->absmax_fp8 || !q->absmax_scale || !q->absmax_mean) return QLORA_ERR_NULL;
-  if (!aligned16(q->codes) || !aligned16(q->absmax_fp8) || !aligned16(q->absmax_scale) ||
-      !aligned16(q->absmax_mean))
-    return QLORA_ERR_ALIGN;
+  if ((q->flags & ~QLORA_NF4_FP32_CONSTANTS) != 0u) return QLORA_ERR_VALUE;
+  if (!q->codes || !q->absmax_scale) return QLORA_ERR_NULL;
+  if (!aligned16(q->codes) || !aligned16(q->absmax_scale)) return QLORA_ERR_ALIGN;
+  if (double_quantized(q)) {
+    if (!q->absmax_fp8 || !q->absmax_mean) return QLORA_ERR_NULL;
+    if (!aligned16(q->absmax_fp8) || !aligned16(q->absmax_mean)) return QLORA_ERR_ALIGN;
+  }
   return QLORA_OK;
 }
 
 QWeight qweight(const qlora_nf4_weight *q) {
-  return QWeight{q->codes, q->absmax_fp8, q->absmax_scale, q->absmax_mean, q->n_out, q->n_in};
+  return QWeight{q->codes, q->absmax_fp8, q->absmax_scale, q->absmax_mean, q->n_out, q->n_in, double_quantized(q)};
 }
 
 qlora_status check_linear(int64_t T, const qlora_nf4_weight *q, int r, float scale) {
@@ -137,6 +142,14 @@ size_t qlora_nf4_bytes(int64_t n_out, int64_t n_in) {
   return (size_t)(cb + nb + 4 * ng + 4);
 }
 
+size_t qlora_nf4_bytes_flags(int64_t n_out, int64_t n_in, uint32_t flags) {
+  if ((flags & ~QLORA_NF4_FP32_CONSTANTS) != 0u) return 0;
+  if (!(flags & QLORA_NF4_FP32_CONSTANTS)) return qlora_nf4_bytes(n_out, n_in);
+  int64_t cb, nb;
+  if (qlora_nf4_sizes(n_out, n_in, &cb, &nb, nullptr) != QLORA_OK) return 0;
+  return (size_t)(cb + 4 * nb);
+}
+
 size_t qlora_quantize_workspace_bytes(int64_t n_out, int64_t n_in) {
   int64_t nb;
   if (qlora_nf4_sizes(n_out, n_in, nullptr, &nb, nullptr) != QLORA_OK) return 0;
@@ -181,10 +194,12 @@ qlora_status qlora_quantize(const void *w, qlora_dtype w_dtype, const qlora_nf4_
   if (w_dtype != QLORA_F32 && w_dtype != QLORA_BF16) return QLORA_ERR_DTYPE;
   if (ws_bytes < qlora_quantize_workspace_bytes(q->n_out, q->n_in)) return QLORA_ERR_WORKSPACE;
   char *base = (char *)ws;
-  hipError_t e = launch_quantize(w, w_dtype == QLORA_BF16, q->n_out * q->n_in, q->codes, q->absmax_fp8,
+  // without double quantization the block constants go straight to absmax_scale
+  const bool dq = double_quantized(q);
+  float *c1 = dq ? (float *)(base + 256 + kQuantizeBinBytes) : q->absmax_scale;
+  hipError_t e = launch_quantize(w, w_dtype == QLORA_BF16, dq, q->n_out * q->n_in, q->codes, q->absmax_fp8,
                                  q->absmax_scale, q->absmax_mean, (uint32_t *)base,
-                                 (unsigned long long *)(base + 256), (float *)(base + 256 + kQuantizeBinBytes),
-                                 tables().mid, (hipStream_t)stream);
+                                 (unsigned long long *)(base + 256), c1, tables().mid, (hipStream_t)stream);
   return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP;
 }
 
@@ -193,8 +208,7 @@ qlora_status qlora_dequantize(const qlora_nf4_weight *q, uint16_t *w_bf16, void 
   if (s != QLORA_OK) return s;
   if (!w_bf16) return QLORA_ERR_NULL;
   if (!aligned16(w_bf16)) return QLORA_ERR_ALIGN;
-  hipError_t e = launch_dequantize(q->codes, q->absmax_fp8, q->absmax_scale, q->absmax_mean,
-                                   q->n_out * q->n_in, w_bf16, tables().cb, (hipStream_t)stream);
+  hipError_t e = launch_dequantize(qweight(q), w_bf16, tables().cb, (hipStream_t)stream);
   return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP;
 }
 

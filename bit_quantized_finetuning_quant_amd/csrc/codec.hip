@@ -252,7 +252,10 @@ __global__ __launch_bounds__(256) void double_quantize(const float *__restrict__
   if (b < nblocks) q_out[b] = (s2 > 0.f) ? (uint8_t)e4m3_rne((double)d / (double)s2) : (uint8_t)0;
 }
 
-// One thread decodes 8 consecutive elements (4 code bytes) per pass.
+// One thread decodes 8 consecutive elements (4 code bytes) per pass.  kDQ:
+// FP8 constants with group scales and a mean; otherwise s2 holds the fp32
+// block constants themselves.
+template <bool kDQ>
 __global__ __launch_bounds__(256) void dequantize_bf16(const uint8_t *__restrict__ codes,
                                                        const uint8_t *__restrict__ fp8,
                                                        const float *__restrict__ s2,
@@ -261,7 +264,7 @@ __global__ __launch_bounds__(256) void dequantize_bf16(const uint8_t *__restrict
   __shared__ float lut[16];
   if (threadIdx.x < 16) lut[threadIdx.x] = cb.v[threadIdx.x];
   __syncthreads();
-  const float mu = *mu_p;
+  const float mu = kDQ ? *mu_p : 0.f;
   const int64_t nchunks = (numel + 7) >> 3;
   const int64_t codes_bytes = (numel + 1) >> 1;
   for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nchunks; c += (int64_t)gridDim.x * 256) {
@@ -276,7 +279,7 @@ __global__ __launch_bounds__(256) void dequantize_bf16(const uint8_t *__restrict
         if ((c << 2) + i < codes_bytes) packed = (packed & ~(0xFFu << (8 * i))) | ((uint32_t)codes[(c << 2) + i] << (8 * i));
     }
     const int64_t blk = e0 >> 6;
-    const float ch = decode_constant(fp8[blk], s2[blk >> 8], mu);
+    const float ch = kDQ ? decode_constant(fp8[blk], s2[blk >> 8], mu) : s2[blk];
     u32x4 o;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -299,7 +302,7 @@ static inline int grid_for(int64_t items, int64_t per_wg, int64_t cap) {
   return (int)(g < 1 ? 1 : g);
 }
 
-hipError_t launch_quantize(const void *w, bool bf16_src, int64_t numel, uint8_t *codes, uint8_t *fp8,
+hipError_t launch_quantize(const void *w, bool bf16_src, bool dq, int64_t numel, uint8_t *codes, uint8_t *fp8,
                            float *s2, float *mu, uint32_t *status, unsigned long long *bins, float *c1,
                            const Midpoints &mid, hipStream_t st) {
   const int64_t nblocks = (numel + kBlock - 1) / kBlock;
@@ -313,16 +316,21 @@ hipError_t launch_quantize(const void *w, bool bf16_src, int64_t numel, uint8_t 
     quantize_blocks<true><<<g, 256, 0, st>>>(w, numel, nblocks, codes, codes_bytes, c1, bins, status, mid);
   else
     quantize_blocks<false><<<g, 256, 0, st>>>(w, numel, nblocks, codes, codes_bytes, c1, bins, status, mid);
-  mean_from_bins<<<1, 256, 0, st>>>(bins, nblocks, mu);
-  double_quantize<<<(unsigned)ngroups, 256, 0, st>>>(c1, nblocks, mu, fp8, s2);
+  if (dq) {
+    mean_from_bins<<<1, 256, 0, st>>>(bins, nblocks, mu);
+    double_quantize<<<(unsigned)ngroups, 256, 0, st>>>(c1, nblocks, mu, fp8, s2);
+  }
   return hipGetLastError();
 }
 
-hipError_t launch_dequantize(const uint8_t *codes, const uint8_t *fp8, const float *s2, const float *mu,
-                             int64_t numel, uint16_t *out, const Codebook &cb, hipStream_t st) {
+hipError_t launch_dequantize(const QWeight &w, uint16_t *out, const Codebook &cb, hipStream_t st) {
+  const int64_t numel = w.n_out * w.n_in;
   const int64_t nchunks = (numel + 7) / 8;
   const int g = grid_for(nchunks, 256, 256 * 32);
-  dequantize_bf16<<<g, 256, 0, st>>>(codes, fp8, s2, mu, numel, out, cb);
+  if (w.dq)
+    dequantize_bf16<true><<<g, 256, 0, st>>>(w.codes, w.fp8, w.s2, w.mu, numel, out, cb);
+  else
+    dequantize_bf16<false><<<g, 256, 0, st>>>(w.codes, w.fp8, w.s2, w.mu, numel, out, cb);
   return hipGetLastError();
 }
 

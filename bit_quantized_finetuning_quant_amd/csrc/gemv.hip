@@ -71,7 +71,11 @@ __device__ __forceinline__ uint16_t to_bf16(float v) {
 
 __host__ __device__ __forceinline__ int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// One unit (32 codes) of one row with the constants of its NF4 block.
+// One unit (32 codes) of one row with the constants of its NF4 block.  With
+// fp32 block constants (no double quantization) the unit carries q = 0x38
+// (e4m3 1.0) and s2 = c1, and the decode runs with mu = 0: fl32(fl32(1 * c1)
+// + 0) = c1 exactly, so one decode serves both storage forms.
+constexpr uint32_t kE4m3One = 0x38u;
 struct UnitLoad {
   u32x4 c;
   uint32_t q;
@@ -81,8 +85,13 @@ struct UnitLoad {
 __device__ __forceinline__ void load_unit(const QWeight &w, int64_t n, int64_t unit, int64_t kblk_row, UnitLoad &L) {
   L.c = *(const u32x4 *)(w.codes + n * (w.n_in / 2) + 16 * unit);
   const int64_t blk = n * kblk_row + (unit >> 1);
-  L.q = w.fp8[blk];
-  L.s2 = w.s2[blk >> 8];
+  if (w.dq) {
+    L.q = w.fp8[blk];
+    L.s2 = w.s2[blk >> 8];
+  } else {
+    L.q = kE4m3One;
+    L.s2 = w.s2[blk];
+  }
 }
 
 // Codebook levels of the 32 codes of a unit.  Each byte of the masked words
@@ -234,7 +243,7 @@ __global__ __launch_bounds__(256) void gemv_fwd_main(const uint16_t *__restrict_
     fwd_store(acc, u_part + span * T * r, r, row0 + rl, T, g);
     return;
   }
-  fwd_store(fwd_tile(f, *w.mu, lut, xrow), y_part + span * T * N, N, row0 + rl, T, g);
+  fwd_store(fwd_tile(f, w.dq ? *w.mu : 0.f, lut, xrow), y_part + span * T * N, N, row0 + rl, T, g);
 }
 
 // Sum of `count` fp32 values p[0], p[stride], ... in index order, fetched
@@ -496,7 +505,7 @@ __device__ __forceinline__ void bwd_main_body(const uint16_t *__restrict__ dy, Q
   const bool valid = unit < U;
   const int64_t uc = valid ? unit : U - 1;
   const int64_t n_base = (chunk * kBwdWaves + wave) * (int64_t)groups * kRowsPerWave;
-  const float mu = *w.mu;
+  const float mu = w.dq ? *w.mu : 0.f;
   float acc[T][32];
 #pragma unroll
   for (int t = 0; t < T; ++t)

@@ -8,13 +8,16 @@
 
 namespace qlora {
 
-// Packed weight as the kernels see it.
+// Packed weight as the kernels see it.  dq: the block constants are FP8
+// codes (fp8) with fp32 group scales (s2) and a tensor mean (mu); otherwise
+// s2 holds one fp32 constant per block and fp8, mu are unused.
 struct QWeight {
   const uint8_t *codes;
   const uint8_t *fp8;
   const float *s2;
   const float *mu;
   int64_t n_out, n_in;
+  bool dq;
 };
 
 // Copies of the 256 exponent bins of the quantizer's exact mean: workgroup g
@@ -24,12 +27,13 @@ struct QWeight {
 constexpr int kBinCopies = 16;
 constexpr size_t kQuantizeBinBytes = (size_t)kBinCopies * 256 * 8;
 
-hipError_t launch_quantize(const void *w, bool bf16_src, int64_t numel, uint8_t *codes, uint8_t *fp8,
+// dq = false: the block constants go to c1 (the caller's fp32 constants) and
+// the mean and FP8 stages are skipped; fp8, s2 and mu are then unused.
+hipError_t launch_quantize(const void *w, bool bf16_src, bool dq, int64_t numel, uint8_t *codes, uint8_t *fp8,
                            float *s2, float *mu, uint32_t *status, unsigned long long *bins, float *c1,
                            const Midpoints &mid, hipStream_t st);
 
-hipError_t launch_dequantize(const uint8_t *codes, const uint8_t *fp8, const float *s2, const float *mu,
-                             int64_t numel, uint16_t *out, const Codebook &cb, hipStream_t st);
+hipError_t launch_dequantize(const QWeight &w, uint16_t *out, const Codebook &cb, hipStream_t st);
 
 // Few-token path (gemv.hip): 1 <= T <= kGemvMaxT.  `part` is fp32 scratch of
 // gemv_part_floats(T, N, K, r) floats.  launch_gemv_fwd with y == nullptr only

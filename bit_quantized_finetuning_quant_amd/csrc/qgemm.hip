@@ -145,7 +145,9 @@ struct Levels {
   float ch;
 };
 
-template <bool kTransW>
+// kDQ: the block constants are FP8 codes with group scales and a tensor mean
+// (double quantization); otherwise w.s2 holds one fp32 constant per block.
+template <bool kTransW, bool kDQ>
 struct Producer {
   const uint16_t *act;
   int64_t M, Kc, m0, c0, K, N, kblk_row;
@@ -194,8 +196,13 @@ struct Producer {
     if (kFull) {
       s.code = *(const u32x4 *)(code0 + kt * code_step);
       const int64_t blk = blk0 + kt * blk_step;
-      s.q = w.fp8[blk];
-      s.s2 = w.s2[blk >> 8];
+      if (kDQ) {
+        s.q = w.fp8[blk];
+        s.s2 = w.s2[blk >> 8];
+      } else {
+        s.q = 0u;
+        s.s2 = w.s2[blk];
+      }
       return;
     }
     const int64_t k0 = kt * QBK;
@@ -204,8 +211,13 @@ struct Producer {
     if (n < N && col < K) {
       s.code = *(const u32x4 *)(w.codes + n * (K / 2) + col / 2);
       const int64_t blk = n * kblk_row + col / kBlock;
-      s.q = w.fp8[blk];
-      s.s2 = w.s2[blk >> 8];
+      if (kDQ) {
+        s.q = w.fp8[blk];
+        s.s2 = w.s2[blk >> 8];
+      } else {
+        s.q = 0u;
+        s.s2 = w.s2[blk];
+      }
     } else {
       s.code = u32x4{0x77777777u, 0x77777777u, 0x77777777u, 0x77777777u};
       s.q = 0u;
@@ -231,7 +243,7 @@ struct Producer {
       }
     }
     // q = 0 with s2 = 0 decodes to c1hat = mu; masked rows carry the zero code, so they decode to 0
-    L.ch = decode_constant(s.q, s.s2, mu);
+    L.ch = kDQ ? decode_constant(s.q, s.s2, mu) : s.s2;
   }
 
   // Levels of word v (8 codes) of a stage.
@@ -268,7 +280,7 @@ struct Producer {
       read_word(next, v, lut, Lnext);
       write_word(Lcur, v, sb);
     }
-    Lnext.ch = decode_constant(next.q, next.s2, mu);
+    Lnext.ch = kDQ ? decode_constant(next.q, next.s2, mu) : next.s2;
   }
 
   // The decoded stage into LDS: fl32 products rounded to bf16, 16-byte stores.
@@ -300,8 +312,8 @@ struct Producer {
 //   - form the products of stage k+2 (levels read at the previous step) and
 //     write them to LDS.
 // Code sets rotate by three and level sets by two (unrolled by six).
-template <bool kTransW>
-__device__ __forceinline__ void producer_loop_full(const Producer<kTransW> &p, int64_t nk, uint16_t (*sb)[QBN * QLD],
+template <bool kTransW, bool kDQ>
+__device__ __forceinline__ void producer_loop_full(const Producer<kTransW, kDQ> &p, int64_t nk, uint16_t (*sb)[QBN * QLD],
                                                    const float *lut) {
   auto st = [nk](int64_t k) { return min(k, nk - 1); };
   Stage c0, c1, c2;
@@ -352,8 +364,8 @@ __device__ __forceinline__ void producer_loop_full(const Producer<kTransW> &p, i
 // step k the producers read the levels of stage k+2 and write it (codes and
 // activation fetched two steps earlier), then fetch stage k+4.  Sets rotate
 // by three (unrolled by three).
-template <bool kTransW>
-__device__ __forceinline__ void producer_loop_partial(const Producer<kTransW> &p, int64_t nk,
+template <bool kTransW, bool kDQ>
+__device__ __forceinline__ void producer_loop_partial(const Producer<kTransW, kDQ> &p, int64_t nk,
                                                       uint16_t (*sa)[QBM * 64], uint16_t (*sb)[QBN * QLD],
                                                       const float *lut) {
   auto st = [nk](int64_t k) { return min(k, nk - 1); };
@@ -506,7 +518,7 @@ __device__ __forceinline__ void stage_lora(const uint16_t *la, const uint16_t *l
   }
 }
 
-template <bool kTransW>
+template <bool kTransW, bool kDQ>
 __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act, int64_t M, int64_t Ncols,
                                                 int64_t Kc, QWeight w, const uint16_t *__restrict__ la,
                                                 const uint16_t *__restrict__ lb, int r, float scale,
@@ -557,7 +569,7 @@ __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act
 
   if (tid >= 256) {
     // ------------------------------------------------------------ producers
-    Producer<kTransW> p;
+    Producer<kTransW, kDQ> p;
     p.act = act;
     p.M = M;
     p.Kc = Kc;
@@ -567,7 +579,7 @@ __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act
     p.N = w.n_out;
     p.kblk_row = w.n_in / kBlock;
     p.w = w;
-    p.mu = *w.mu;
+    p.mu = kDQ ? *w.mu : 0.f;
     p.ptid = tid - 256;
     p.act_vec = (Kc % 8) == 0;
     p.init_addressing();
@@ -689,10 +701,17 @@ hipError_t launch_qgemm(bool trans_w, const uint16_t *act, int64_t M, int64_t Nc
                         const uint16_t *la, const uint16_t *lb, int r, float scale, uint16_t *out,
                         const Codebook &cb, hipStream_t st) {
   dim3 g((unsigned)((M + QBM - 1) / QBM), (unsigned)((Ncols + QBN - 1) / QBN));
-  if (trans_w)
-    qgemm_ws<true><<<g, 512, 0, st>>>(act, M, Ncols, Kc, w, la, lb, r, scale, out, cb);
-  else
-    qgemm_ws<false><<<g, 512, 0, st>>>(act, M, Ncols, Kc, w, la, lb, r, scale, out, cb);
+  if (w.dq) {
+    if (trans_w)
+      qgemm_ws<true, true><<<g, 512, 0, st>>>(act, M, Ncols, Kc, w, la, lb, r, scale, out, cb);
+    else
+      qgemm_ws<false, true><<<g, 512, 0, st>>>(act, M, Ncols, Kc, w, la, lb, r, scale, out, cb);
+  } else {
+    if (trans_w)
+      qgemm_ws<true, false><<<g, 512, 0, st>>>(act, M, Ncols, Kc, w, la, lb, r, scale, out, cb);
+    else
+      qgemm_ws<false, false><<<g, 512, 0, st>>>(act, M, Ncols, Kc, w, la, lb, r, scale, out, cb);
+  }
   return hipGetLastError();
 }
 

@@ -14,6 +14,7 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libqlora_gfx950.so")
 
 QLORA_F32, QLORA_BF16 = 0, 1
+QLORA_NF4_FP32_CONSTANTS = 1
 STATUS_NAMES = {0: "QLORA_OK", 1: "QLORA_ERR_NULL", 2: "QLORA_ERR_SHAPE", 3: "QLORA_ERR_ALIGN",
                 4: "QLORA_ERR_WORKSPACE", 5: "QLORA_ERR_DTYPE", 6: "QLORA_ERR_HIP",
                 7: "QLORA_ERR_NONFINITE", 8: "QLORA_ERR_VALUE", 9: "QLORA_ERR_MEMORY"}
@@ -28,7 +29,7 @@ class QloraError(RuntimeError):
 class NF4WeightStruct(ctypes.Structure):
     _fields_ = [("n_out", ctypes.c_int64), ("n_in", ctypes.c_int64), ("codes", ctypes.c_void_p),
                 ("absmax_fp8", ctypes.c_void_p), ("absmax_scale", ctypes.c_void_p),
-                ("absmax_mean", ctypes.c_void_p)]
+                ("absmax_mean", ctypes.c_void_p), ("flags", ctypes.c_uint32)]
 
 
 _lib = None
@@ -39,6 +40,7 @@ _SZ = ctypes.c_size_t
 _SIGNATURES = {
     "qlora_nf4_sizes": (ctypes.c_int, [_I64, _I64, _P, _P, _P]),
     "qlora_nf4_bytes": (_SZ, [_I64, _I64]),
+    "qlora_nf4_bytes_flags": (_SZ, [_I64, _I64, ctypes.c_uint32]),
     "qlora_quantize_workspace_bytes": (_SZ, [_I64, _I64]),
     "qlora_linear_workspace_bytes": (_SZ, [_I64, _I64, _I64, ctypes.c_int]),
     "qlora_nf4_codebook": (None, [_P]),
@@ -93,8 +95,10 @@ def nf4_sizes(n_out: int, n_in: int):
     return cb.value, nb.value, ng.value
 
 
-def nf4_bytes(n_out: int, n_in: int) -> int:
-    return int(lib().qlora_nf4_bytes(n_out, n_in))
+def nf4_bytes(n_out: int, n_in: int, double_quant: bool = True) -> int:
+    if double_quant:
+        return int(lib().qlora_nf4_bytes(n_out, n_in))
+    return int(lib().qlora_nf4_bytes_flags(n_out, n_in, QLORA_NF4_FP32_CONSTANTS))
 
 
 def quantize_workspace_bytes(n_out: int, n_in: int) -> int:
@@ -146,30 +150,37 @@ def _ptr(t) -> int:
 
 @dataclass
 class NF4Weight:
-    """Device buffers of a packed weight (allocated by torch, owned by this object)."""
+    """Device buffers of a packed weight (allocated by torch, owned by this object).
+
+    double_quant=False: absmax_scale holds the nblocks fp32 block constants and
+    absmax_fp8 / absmax_mean are None (QLORA_NF4_FP32_CONSTANTS)."""
     n_out: int
     n_in: int
     codes: "object"
     absmax_fp8: "object"
     absmax_scale: "object"
     absmax_mean: "object"
+    double_quant: bool = True
 
     @classmethod
-    def empty(cls, n_out: int, n_in: int, device="cuda"):
+    def empty(cls, n_out: int, n_in: int, device="cuda", double_quant: bool = True):
         torch = _torch()
         cb, nb, ng = nf4_sizes(n_out, n_in)
-        return cls(n_out, n_in, torch.empty(cb, dtype=torch.uint8, device=device),
-                   torch.empty(nb, dtype=torch.uint8, device=device),
+        codes = torch.empty(cb, dtype=torch.uint8, device=device)
+        if not double_quant:
+            return cls(n_out, n_in, codes, None, torch.empty(nb, dtype=torch.float32, device=device), None, False)
+        return cls(n_out, n_in, codes, torch.empty(nb, dtype=torch.uint8, device=device),
                    torch.empty(ng, dtype=torch.float32, device=device),
                    torch.empty(1, dtype=torch.float32, device=device))
 
     def struct(self) -> NF4WeightStruct:
         return NF4WeightStruct(self.n_out, self.n_in, _ptr(self.codes), _ptr(self.absmax_fp8),
-                               _ptr(self.absmax_scale), _ptr(self.absmax_mean))
+                               _ptr(self.absmax_scale), _ptr(self.absmax_mean),
+                               0 if self.double_quant else QLORA_NF4_FP32_CONSTANTS)
 
     def nbytes(self) -> int:
         return sum(t.numel() * t.element_size() for t in
-                   (self.codes, self.absmax_fp8, self.absmax_scale, self.absmax_mean))
+                   (self.codes, self.absmax_fp8, self.absmax_scale, self.absmax_mean) if t is not None)
 
 
 def _bits(t):
@@ -178,8 +189,10 @@ def _bits(t):
     return t.view(torch.int16) if t.dtype == torch.bfloat16 else t
 
 
-def quantize(w, out: NF4Weight = None, workspace=None, stream=None) -> NF4Weight:
-    """Quantize a [n_out x n_in] fp32 or bf16 CUDA tensor to NF4 + FP8 double quantization."""
+def quantize(w, out: NF4Weight = None, workspace=None, stream=None, double_quant: bool = True) -> NF4Weight:
+    """Quantize a [n_out x n_in] fp32 or bf16 CUDA tensor to NF4 + FP8 double quantization
+    (double_quant=False: NF4 + fp32 block constants; ignored when `out` is given, whose
+    storage form decides)."""
     torch = _torch()
     if w.dim() != 2 or not w.is_contiguous():
         raise ValueError("w must be a contiguous 2-D tensor")
@@ -187,7 +200,7 @@ def quantize(w, out: NF4Weight = None, workspace=None, stream=None) -> NF4Weight
     if dtype is None:
         raise ValueError("w must be float32 or bfloat16")
     n_out, n_in = w.shape
-    q = out if out is not None else NF4Weight.empty(n_out, n_in, w.device)
+    q = out if out is not None else NF4Weight.empty(n_out, n_in, w.device, double_quant=double_quant)
     wsb = quantize_workspace_bytes(n_out, n_in)
     ws = workspace if workspace is not None else torch.empty(wsb, dtype=torch.uint8, device=w.device)
     st = q.struct()

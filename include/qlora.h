@@ -59,10 +59,17 @@ typedef enum {
 
 typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
 
-/* Packed NF4 weight.  All four buffers are device memory owned by the caller.
+/* Packed NF4 weight.  All buffers are device memory owned by the caller.
  * Element e of the row-major [n_out x n_in] weight belongs to block e/64 and
  * to double-quantization group (e/64)/256; a partial last block or group is
- * zero padded.                                                                */
+ * zero padded.
+ * flags = 0 (the default): double quantization, the four buffers below.
+ * flags = QLORA_NF4_FP32_CONSTANTS: no double quantization ("qlora" entry,
+ * section "como funciona": the fp32 constants cost 0.5 bit/param before
+ * their FP8 stage); absmax_scale then holds nblocks fp32 block constants
+ * c1_b themselves, decoded as c1hat_b = c1_b, and absmax_fp8 / absmax_mean
+ * are unused (may be NULL): 4.5 bits per parameter.                          */
+#define QLORA_NF4_FP32_CONSTANTS 1u
 typedef struct {
   int64_t n_out;         /* rows of W (output features)                        */
   int64_t n_in;          /* columns of W (input features), contiguous          */
@@ -70,8 +77,11 @@ typedef struct {
                             element 2i+1 in the high nibble; an odd tail's high
                             nibble is the zero code 7                           */
   uint8_t *absmax_fp8;   /* nblocks = ceil(numel/64) e4m3 bytes, q_b          */
-  float *absmax_scale;   /* ngroups = ceil(nblocks/256) fp32 scales, s2_g      */
+  float *absmax_scale;   /* ngroups = ceil(nblocks/256) fp32 scales, s2_g
+                            (nblocks fp32 constants c1_b with FP32_CONSTANTS) */
   float *absmax_mean;    /* 1 fp32, the mean mu of the block absmax values     */
+  uint32_t flags;        /* 0 or QLORA_NF4_FP32_CONSTANTS; other bits are
+                            rejected with QLORA_ERR_VALUE                       */
 } qlora_nf4_weight;
 
 /* ---- host-only helpers (no GPU needed) ----------------------------------- */
@@ -85,6 +95,10 @@ qlora_status qlora_nf4_sizes(int64_t n_out, int64_t n_in, int64_t *codes_bytes,
 /* Total bytes of the packed format (codes + constants + scales + mean): the
  * storage cost is 8 * this / numel bits per parameter.  0 on a bad shape.     */
 size_t qlora_nf4_bytes(int64_t n_out, int64_t n_in);
+
+/* The same total for a storage form chosen by `flags` (0: as qlora_nf4_bytes;
+ * QLORA_NF4_FP32_CONSTANTS: codes + 4 * nblocks).  0 on a bad shape or flag. */
+size_t qlora_nf4_bytes_flags(int64_t n_out, int64_t n_in, uint32_t flags);
 
 /* Workspace bytes needed by qlora_quantize for a weight of this shape.        */
 size_t qlora_quantize_workspace_bytes(int64_t n_out, int64_t n_in);
@@ -116,6 +130,8 @@ const char *qlora_version(void);
  *   per group g: s2_g = fl32(max_b |fl32(c1_b - mu)| / 448) and
  *   q_b   = e4m3 nearest to the exact real fl32(c1_b - mu) / s2_g (ties to
  *           the even mantissa, saturating at 448; q_b = 0 when s2_g = 0).
+ * With q->flags = QLORA_NF4_FP32_CONSTANTS the mean and FP8 stages are
+ * skipped and c1_b is written to absmax_scale[b] as it is.
  * Any numel up to 2^37 is accepted.  ws: qlora_quantize_workspace_bytes, 16-B
  * aligned; after the call it holds the status word read by qlora_status_read.
  * A NaN/Inf in W raises QLORA_ERR_NONFINITE there; that block's codes are
@@ -124,7 +140,8 @@ qlora_status qlora_quantize(const void *w, qlora_dtype w_dtype, const qlora_nf4_
                             void *ws, size_t ws_bytes, void *stream);
 
 /* Dequantize *q to bf16 w_bf16 [n_out x n_in] (device):
- *   c1hat_b = fl32(fl32(e4m3(q_b) * s2_g) + mu)     (no fused multiply-add)
+ *   c1hat_b = fl32(fl32(e4m3(q_b) * s2_g) + mu)     (no fused multiply-add;
+ *             c1hat_b = c1_b with QLORA_NF4_FP32_CONSTANTS)
  *   w_hat   = bf16_round_nearest_even(fl32(CB[code] * c1hat_b))
  * This is the same decode the fused linear calls apply on the fly.           */
 qlora_status qlora_dequantize(const qlora_nf4_weight *q, uint16_t *w_bf16, void *stream);

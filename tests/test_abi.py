@@ -132,3 +132,23 @@ def test_adamw_argument_validation_before_any_launch():
     assert _adamw(p=None) == 1 and _adamw(v=None) == 1  # QLORA_ERR_NULL
     assert _adamw(g=0x30004) == 3 and _adamw(pb=0x20002) == 3  # QLORA_ERR_ALIGN
     assert qlora.status_string(9).startswith("a buffer is not reachable")
+
+
+def test_storage_flag_validation_and_sizes():
+    lib = qlora.lib()
+    # unknown flag bits are refused; the FP32-constant form needs no fp8 bytes and no mean
+    bad = qlora.NF4WeightStruct(512, 256, 0x10000, 0x20000, 0x30000, 0x40000, 2)
+    assert lib.qlora_dequantize(ctypes.byref(bad), 0x50000, None) == 8
+    fp32c = qlora.NF4WeightStruct(512, 256, 0x10000, None, 0x30000, None, qlora.QLORA_NF4_FP32_CONSTANTS)
+    assert lib.qlora_dequantize(ctypes.byref(fp32c), 0x50002, None) == 3  # weight accepted; output misaligned
+    dq = qlora.NF4WeightStruct(512, 256, 0x10000, None, 0x30000, None, 0)
+    assert lib.qlora_dequantize(ctypes.byref(dq), 0x50000, None) == 1  # double quantization needs them
+    fp32c_bad = qlora.NF4WeightStruct(512, 256, 0x10000, None, 0x30004, None, qlora.QLORA_NF4_FP32_CONSTANTS)
+    assert lib.qlora_dequantize(ctypes.byref(fp32c_bad), 0x50000, None) == 3
+    for n_out, n_in in ((512, 256), (3, 100), (4096, 11008)):
+        cb, nb, _ = qlora.nf4_sizes(n_out, n_in)
+        assert qlora.nf4_bytes(n_out, n_in, double_quant=False) == cb + 4 * nb
+        bits = 8 * qlora.nf4_bytes(n_out, n_in, double_quant=False) / (n_out * n_in)
+        assert bits == pytest.approx(oracle.bits_per_param(n_out, n_in, double_quant=False), abs=1e-12)
+    assert lib.qlora_nf4_bytes_flags(512, 256, 4) == 0
+    assert lib.qlora_nf4_bytes_flags(512, 256, 0) == qlora.nf4_bytes(512, 256)
