@@ -26,6 +26,7 @@ rounding  fp32 / bf16 / e4m3 rounding written from the IEEE-style definitions
 nf4       blocking, nearest code, packing, mean, double quantization, decode
 linear    forward and backward of the adapted linear layer in fp64
 adamw     the AdamW update of the adapters (fp32 states, fp32 master copy)
+dropout   LoRA dropout on the adapter input: Philox4x64-10 mask, forward and backward
 
 Parity status: every function here is pinned by a ``-m "not gpu"`` test in
 ``tests/test_oracle_*.py`` (see each module's docstring for its pins), except
@@ -55,4 +56,5 @@ from .nf4 import (  # noqa: F401
     unpack_codes,
 )
 from .linear import backward, backward_f64, forward, forward_f64  # noqa: F401
+from . import dropout  # noqa: F401
 from .adamw import adamw_step, step_scalars  # noqa: F401
