@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libqlora_gfx950.so")
-SOURCES = ["codec.hip", "qgemm.hip", "lora.hip", "gemv.hip", "linear.hip", "optim.hip", "api.hip"]
+SOURCES = ["codec.hip", "qgemm.hip", "lora.hip", "gemv.hip", "linear.hip", "optim.hip", "dropout.hip", "api.hip"]
 
 HIPCC_FLAGS = [
     "--offload-arch=gfx950",

@@ -97,6 +97,18 @@ qlora_status check_linear(int64_t T, const qlora_nf4_weight *q, int r, float sca
   return QLORA_OK;
 }
 
+// Dropout arguments: 0 <= p < 1 (finite); thresh = min(2^32 - 1, floor(p 2^32 + 1/2))
+// in fp64, and the fp32 factor 1 / (1 - p) of the kept values.
+bool make_dropout(double p, uint64_t seed, Dropout *d) {
+  if (!std::isfinite(p) || p < 0.0 || p >= 1.0) return false;
+  const double t = std::floor(p * 4294967296.0 + 0.5);
+  d->on = true;
+  d->thresh = t >= 4294967295.0 ? 0xFFFFFFFFu : (uint32_t)t;
+  d->seed = seed;
+  d->inv_keep = (float)(1.0 / (1.0 - p));
+  return true;
+}
+
 // The address a kernel uses for p: p itself for device or managed memory, the
 // mapped device address for pinned host memory (hipHostMalloc), and false for
 // memory the GPU cannot reach (pageable host memory, unknown pointers).
@@ -160,6 +172,12 @@ size_t qlora_quantize_workspace_bytes(int64_t n_out, int64_t n_in) {
 size_t qlora_linear_workspace_bytes(int64_t T, int64_t n_out, int64_t n_in, int r) {
   if (T < 1 || !shape_ok(n_out, n_in) || n_in % kBlock != 0 || r < 1 || r > 256) return 0;
   return plan_linear(T, n_out, n_in, r).total;
+}
+
+size_t qlora_linear_dropout_workspace_bytes(int64_t T, int64_t n_out, int64_t n_in, int r) {
+  if (T < 1 || !shape_ok(n_out, n_in) || n_in % kBlock != 0 || r < 1 || r > 256) return 0;
+  if (T * n_in > kMaxNumel) return 0;
+  return plan_linear(T, n_out, n_in, r, true).total;
 }
 
 void qlora_nf4_codebook(float out[16]) {
@@ -276,6 +294,54 @@ qlora_status qlora_adamw_step(float *param, uint16_t *param_bf16, const float *g
   if (!std::isfinite(sc.step_size) || !(sc.bc2_sqrt > 0.0f)) return QLORA_ERR_VALUE;
   hipError_t e = launch_adamw((float *)d[0], (uint16_t *)d[1], (const float *)d[2], (float *)d[3], (float *)d[4], n,
                               sc, (hipStream_t)stream);
+  return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP;
+}
+
+qlora_status qlora_linear_fwd_dropout(const uint16_t *x, int64_t T, const qlora_nf4_weight *q, const uint16_t *A,
+                                      const uint16_t *B, int r, float scale, double dropout_p, uint64_t seed,
+                                      uint16_t *y, uint16_t *u_out, void *ws, size_t ws_bytes, void *stream) {
+  qlora_status s = check_linear(T, q, r, scale);
+  if (s != QLORA_OK) return s;
+  Dropout d;
+  if (!make_dropout(dropout_p, seed, &d)) return QLORA_ERR_VALUE;
+  if (!x || !A || !B || !y || !ws) return QLORA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(A) || !aligned16(B) || !aligned16(y) || !aligned16(ws) ||
+      (u_out && !aligned16(u_out)))
+    return QLORA_ERR_ALIGN;
+  const LinearPlan p = plan_linear(T, q->n_out, q->n_in, r, true);
+  if (ws_bytes < p.total) return QLORA_ERR_WORKSPACE;
+  hipError_t e = launch_linear_fwd(p, x, qweight(q), A, B, scale, y, u_out, (char *)ws, tables().cb,
+                                   (hipStream_t)stream, d);
+  return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP;
+}
+
+qlora_status qlora_linear_bwd_dropout(const uint16_t *dy, const uint16_t *x, int64_t T, const qlora_nf4_weight *q,
+                                      const uint16_t *A, const uint16_t *B, int r, float scale, double dropout_p,
+                                      uint64_t seed, const uint16_t *u, uint16_t *grad_x, float *grad_A,
+                                      float *grad_B, void *ws, size_t ws_bytes, void *stream) {
+  qlora_status s = check_linear(T, q, r, scale);
+  if (s != QLORA_OK) return s;
+  Dropout d;
+  if (!make_dropout(dropout_p, seed, &d)) return QLORA_ERR_VALUE;
+  if (!dy || !x || !A || !B || !grad_A || !grad_B || !ws) return QLORA_ERR_NULL;
+  if (!aligned16(dy) || !aligned16(x) || !aligned16(A) || !aligned16(B) || !aligned16(grad_A) ||
+      !aligned16(grad_B) || !aligned16(ws) || (u && !aligned16(u)) || (grad_x && !aligned16(grad_x)))
+    return QLORA_ERR_ALIGN;
+  const LinearPlan p = plan_linear(T, q->n_out, q->n_in, r, true);
+  if (ws_bytes < p.total) return QLORA_ERR_WORKSPACE;
+  hipError_t e = launch_linear_bwd(p, dy, x, qweight(q), A, B, scale, u, grad_x, grad_A, grad_B, (char *)ws,
+                                   tables().cb, (hipStream_t)stream, d);
+  return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP;
+}
+
+qlora_status qlora_dropout_mask(const uint16_t *x, int64_t T, int64_t K, double dropout_p, uint64_t seed,
+                                uint32_t *keep_words, uint16_t *x_drop, void *stream) {
+  if (T < 1 || K < 1 || K % 8 != 0 || T > kMaxNumel || K > kMaxNumel || T * K > kMaxNumel) return QLORA_ERR_SHAPE;
+  Dropout d;
+  if (!make_dropout(dropout_p, seed, &d)) return QLORA_ERR_VALUE;
+  if (!x || !keep_words || !x_drop) return QLORA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(keep_words) || !aligned16(x_drop)) return QLORA_ERR_ALIGN;
+  hipError_t e = launch_dropout_mask(x, T, K, d.thresh, d.seed, keep_words, x_drop, (hipStream_t)stream);
   return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP;
 }
 

@@ -189,7 +189,8 @@ __device__ __forceinline__ void fwd_store(const f32x4 &acc, float *dst, int64_t 
 }
 
 template <int kUnits>
-__global__ __launch_bounds__(256) void gemv_fwd_main(const uint16_t *__restrict__ x, int T, QWeight w,
+__global__ __launch_bounds__(256) void gemv_fwd_main(const uint16_t *__restrict__ x,
+                                                     const uint16_t *__restrict__ xa, int T, QWeight w,
                                                      const uint16_t *__restrict__ A, int r, float *__restrict__ y_part,
                                                      float *__restrict__ u_part, int64_t spans, int64_t ablocks,
                                                      Codebook cb) {
@@ -218,10 +219,11 @@ __global__ __launch_bounds__(256) void gemv_fwd_main(const uint16_t *__restrict_
   }
   if (tid < 16) lut[tid] = cb.v[tid];
   constexpr int kChunks = kUnits * 4;  // 16-byte chunks of a token row of the tile
+  const uint16_t *xsrc = a_rows ? xa : x;  // the adapter rows read the adapter input
   for (int i = tid; i < T * kChunks; i += 256) {
     const int t = i / kChunks, c8 = (i % kChunks) * 8;
     u32x4 v = {0u, 0u, 0u, 0u};
-    if (col0 + c8 < K) v = *(const u32x4 *)(x + (int64_t)t * K + col0 + c8);
+    if (col0 + c8 < K) v = *(const u32x4 *)(xsrc + (int64_t)t * K + col0 + c8);
     *(u32x4 *)(xs + t * kXStride + c8) = v;
   }
   __syncthreads();
@@ -273,8 +275,9 @@ __device__ __forceinline__ float strided_sum(const float *p, int64_t stride, int
 template <int T>
 __global__ __launch_bounds__(256) void gemv_fwd_finish(const float *__restrict__ y_part,
                                                        const float *__restrict__ u_part, int64_t spans,
-                                                       const uint16_t *__restrict__ B, int r, float scale, int64_t N,
-                                                       uint16_t *__restrict__ y, uint16_t *__restrict__ u_out) {
+                                                       const uint16_t *__restrict__ B, int r, float scale,
+                                                       float u_scale, int64_t N, uint16_t *__restrict__ y,
+                                                       uint16_t *__restrict__ u_out) {
   __shared__ float us[T * 256];
   __shared__ float tmp[1024];
   __shared__ float red[4][T][64];
@@ -310,7 +313,7 @@ __global__ __launch_bounds__(256) void gemv_fwd_finish(const float *__restrict__
   for (int e = tid; e < E; e += 256) {
     float s = 0.f;
     for (int sl = 0; sl < S; ++sl) s += tmp[sl * E + e];
-    const uint16_t h = to_bf16(s);
+    const uint16_t h = to_bf16(s * u_scale);
     us[e] = bf(h);
     if (blockIdx.x == 0) u_out[e] = h;
   }
@@ -579,8 +582,8 @@ template <int T>
 __global__ __launch_bounds__(256) void gemv_bwd_finish(const float *__restrict__ gx_part, int64_t chunks,
                                                        const float *__restrict__ v_part, int64_t vparts,
                                                        const uint16_t *__restrict__ x, const uint16_t *__restrict__ A,
-                                                       int r, int64_t K, float scale, uint16_t *__restrict__ grad_x,
-                                                       float *__restrict__ grad_A) {
+                                                       int r, int64_t K, float scale, const uint32_t *__restrict__ keep,
+                                                       uint16_t *__restrict__ grad_x, float *__restrict__ grad_A) {
   __shared__ float tmp[1024];
   __shared__ float vs[T * 256];
   __shared__ float red[4][T][64];
@@ -648,8 +651,10 @@ __global__ __launch_bounds__(256) void gemv_bwd_finish(const float *__restrict__
         for (int t = 0; t < T; ++t)
           gv[i][t] = gx_part[(min(c0 + 4 * kFinBatch + 4 * i, chunks - 1) * T + t) * K + cc];
     }
+    // dropout: the adapter term of row t is kept where bit t of the column's word is set
+    const uint32_t kw = keep ? keep[cc] : 0xFFFFFFFFu;
 #pragma unroll
-    for (int t = 0; t < T; ++t) red[jg][t][c] = g[t] + scale * lora[t];
+    for (int t = 0; t < T; ++t) red[jg][t][c] = g[t] + (((kw >> t) & 1u) ? scale * lora[t] : 0.f);
     __syncthreads();
     if (jg == 0 && valid) {
 #pragma unroll
@@ -692,8 +697,9 @@ size_t bwd_lds_bytes(int T) {
 }
 
 template <int T>
-hipError_t gemv_fwd_impl(const uint16_t *x, const QWeight &w, const uint16_t *A, const uint16_t *B, int r,
-                         float scale, uint16_t *y, uint16_t *u, float *part, const Codebook &cb, hipStream_t st) {
+hipError_t gemv_fwd_impl(const uint16_t *x, const uint16_t *xa, const QWeight &w, const uint16_t *A, const uint16_t *B,
+                         int r, float scale, float u_scale, uint16_t *y, uint16_t *u, float *part, const Codebook &cb,
+                         hipStream_t st) {
   const int64_t N = w.n_out;
   const GemvGeometry g = geometry(N, w.n_in, r);
   const bool rows = y != nullptr;
@@ -704,20 +710,21 @@ hipError_t gemv_fwd_impl(const uint16_t *x, const QWeight &w, const uint16_t *A,
   TimedLaunch tl;
   const bool timed = rows && timing_begin(st, tl, kTimedGemvFwd);
   if (g.funits == kFwdUnitsSmall)
-    gemv_fwd_main<kFwdUnitsSmall><<<grid, 256, lds, st>>>(x, T, w, A, r, y_part, u_part, g.fspans, g.ablocks, cb);
+    gemv_fwd_main<kFwdUnitsSmall><<<grid, 256, lds, st>>>(x, xa, T, w, A, r, y_part, u_part, g.fspans, g.ablocks, cb);
   else
-    gemv_fwd_main<kFwdUnitsLarge><<<grid, 256, lds, st>>>(x, T, w, A, r, y_part, u_part, g.fspans, g.ablocks, cb);
+    gemv_fwd_main<kFwdUnitsLarge><<<grid, 256, lds, st>>>(x, xa, T, w, A, r, y_part, u_part, g.fspans, g.ablocks, cb);
   if (timed) timing_end(st, tl);
   const int64_t out_rows = rows ? N : 0;
   const unsigned fg = (unsigned)std::max<int64_t>(1, cdiv(out_rows, 64));
-  gemv_fwd_finish<T><<<fg, 256, 0, st>>>(y_part, u_part, g.fspans, B, r, scale, out_rows, y, u);
+  gemv_fwd_finish<T><<<fg, 256, 0, st>>>(y_part, u_part, g.fspans, B, r, scale, u_scale, out_rows, y, u);
   return hipGetLastError();
 }
 
 template <int T>
-hipError_t gemv_bwd_impl(const uint16_t *dy, const uint16_t *x, const QWeight &w, const uint16_t *A,
-                         const uint16_t *B, int r, float scale, const uint16_t *u, uint16_t *grad_x, float *grad_A,
-                         float *grad_B, float *part, const Codebook &cb, hipStream_t st) {
+hipError_t gemv_bwd_impl(const uint16_t *dy, const uint16_t *xa, const QWeight &w, const uint16_t *A,
+                         const uint16_t *B, int r, float scale, float scale_ax, const uint32_t *keep, const uint16_t *u,
+                         uint16_t *grad_x, float *grad_A, float *grad_B, float *part, const Codebook &cb,
+                         hipStream_t st) {
   const int64_t N = w.n_out, K = w.n_in;
   const GemvGeometry g = geometry(N, K, r);
   const int64_t nf4_wgs = grad_x ? g.bspans * g.chunks : 0;
@@ -738,8 +745,8 @@ hipError_t gemv_bwd_impl(const uint16_t *dy, const uint16_t *x, const QWeight &w
     gemv_bwd_main<T><<<grid, kBwdThreads, lds, st>>>(dy, w, B, u, r, scale, gx_part, v_part, grad_B, g.bspans, g.bparts,
                                              (int)g.groups, (int)g.bsub, cb);
   if (timed) timing_end(st, tl);
-  gemv_bwd_finish<T><<<(unsigned)cdiv(K, 64), 256, 0, st>>>(gx_part, g.chunks, v_part, g.bparts, x, A, r, K, scale,
-                                                            grad_x, grad_A);
+  gemv_bwd_finish<T><<<(unsigned)cdiv(K, 64), 256, 0, st>>>(gx_part, g.chunks, v_part, g.bparts, xa, A, r, K,
+                                                            scale_ax, keep, grad_x, grad_A);
   return hipGetLastError();
 }
 
@@ -754,26 +761,27 @@ size_t gemv_part_floats(int64_t T, int64_t N, int64_t K, int r) {
   return std::max(fwd, bwd);
 }
 
-hipError_t launch_gemv_fwd(int64_t T, const uint16_t *x, const QWeight &w, const uint16_t *A, const uint16_t *B,
-                           int r, float scale, uint16_t *y, uint16_t *u, float *part, const Codebook &cb,
-                           hipStream_t st) {
+hipError_t launch_gemv_fwd(int64_t T, const uint16_t *x, const uint16_t *xa, const QWeight &w, const uint16_t *A,
+                           const uint16_t *B, int r, float scale, float u_scale, uint16_t *y, uint16_t *u,
+                           float *part, const Codebook &cb, hipStream_t st) {
   switch (T) {
-    case 1: return gemv_fwd_impl<1>(x, w, A, B, r, scale, y, u, part, cb, st);
-    case 2: return gemv_fwd_impl<2>(x, w, A, B, r, scale, y, u, part, cb, st);
-    case 3: return gemv_fwd_impl<3>(x, w, A, B, r, scale, y, u, part, cb, st);
-    case 4: return gemv_fwd_impl<4>(x, w, A, B, r, scale, y, u, part, cb, st);
+    case 1: return gemv_fwd_impl<1>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 2: return gemv_fwd_impl<2>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 3: return gemv_fwd_impl<3>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 4: return gemv_fwd_impl<4>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
     default: return hipErrorInvalidValue;
   }
 }
 
-hipError_t launch_gemv_bwd(int64_t T, const uint16_t *dy, const uint16_t *x, const QWeight &w, const uint16_t *A,
-                           const uint16_t *B, int r, float scale, const uint16_t *u, uint16_t *grad_x,
-                           float *grad_A, float *grad_B, float *part, const Codebook &cb, hipStream_t st) {
+hipError_t launch_gemv_bwd(int64_t T, const uint16_t *dy, const uint16_t *xa, const QWeight &w, const uint16_t *A,
+                           const uint16_t *B, int r, float scale, float scale_ax, const uint32_t *keep,
+                           const uint16_t *u, uint16_t *grad_x, float *grad_A, float *grad_B, float *part,
+                           const Codebook &cb, hipStream_t st) {
   switch (T) {
-    case 1: return gemv_bwd_impl<1>(dy, x, w, A, B, r, scale, u, grad_x, grad_A, grad_B, part, cb, st);
-    case 2: return gemv_bwd_impl<2>(dy, x, w, A, B, r, scale, u, grad_x, grad_A, grad_B, part, cb, st);
-    case 3: return gemv_bwd_impl<3>(dy, x, w, A, B, r, scale, u, grad_x, grad_A, grad_B, part, cb, st);
-    case 4: return gemv_bwd_impl<4>(dy, x, w, A, B, r, scale, u, grad_x, grad_A, grad_B, part, cb, st);
+    case 1: return gemv_bwd_impl<1>(dy, xa, w, A, B, r, scale, scale_ax, keep, u, grad_x, grad_A, grad_B, part, cb, st);
+    case 2: return gemv_bwd_impl<2>(dy, xa, w, A, B, r, scale, scale_ax, keep, u, grad_x, grad_A, grad_B, part, cb, st);
+    case 3: return gemv_bwd_impl<3>(dy, xa, w, A, B, r, scale, scale_ax, keep, u, grad_x, grad_A, grad_B, part, cb, st);
+    case 4: return gemv_bwd_impl<4>(dy, xa, w, A, B, r, scale, scale_ax, keep, u, grad_x, grad_A, grad_B, part, cb, st);
     default: return hipErrorInvalidValue;
   }
 }

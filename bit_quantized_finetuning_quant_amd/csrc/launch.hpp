@@ -41,19 +41,36 @@ hipError_t launch_dequantize(const QWeight &w, uint16_t *out, const Codebook &cb
 constexpr int64_t kGemvMaxT = 4;
 bool gemv_applies(int64_t T, int64_t K);
 size_t gemv_part_floats(int64_t T, int64_t N, int64_t K, int r);
-hipError_t launch_gemv_fwd(int64_t T, const uint16_t *x, const QWeight &w, const uint16_t *A, const uint16_t *B,
-                           int r, float scale, uint16_t *y, uint16_t *u, float *part, const Codebook &cb,
-                           hipStream_t st);
-hipError_t launch_gemv_bwd(int64_t T, const uint16_t *dy, const uint16_t *x, const QWeight &w, const uint16_t *A,
-                           const uint16_t *B, int r, float scale, const uint16_t *u, uint16_t *grad_x,
-                           float *grad_A, float *grad_B, float *part, const Codebook &cb, hipStream_t st);
+// The adapter input xa (x, or the dropped-out x) feeds u = u_scale * xa A^T
+// and grad_A = scale_ax * v^T xa; scale_ax also scales the adapter term of
+// grad_x, which `keep` (nullptr: no dropout) masks element by element.
+hipError_t launch_gemv_fwd(int64_t T, const uint16_t *x, const uint16_t *xa, const QWeight &w, const uint16_t *A,
+                           const uint16_t *B, int r, float scale, float u_scale, uint16_t *y, uint16_t *u,
+                           float *part, const Codebook &cb, hipStream_t st);
+hipError_t launch_gemv_bwd(int64_t T, const uint16_t *dy, const uint16_t *xa, const QWeight &w, const uint16_t *A,
+                           const uint16_t *B, int r, float scale, float scale_ax, const uint32_t *keep,
+                           const uint16_t *u, uint16_t *grad_x, float *grad_A, float *grad_B, float *part,
+                           const Codebook &cb, hipStream_t st);
 
 // Workspace plan of the linear calls (byte offsets into the caller's buffer).
 struct LinearPlan {
   int64_t T, N, K;
   int r;
-  size_t off_status, off_u, off_v, off_part, total;
+  bool dropout;
+  size_t off_status, off_u, off_v, off_part, off_keep, off_xd, total;
 };
+
+// LoRA dropout of one linear call (dropout.hip): the mask of the adapter input
+// is regenerated from (thresh, seed) by the forward and by the backward.
+struct Dropout {
+  bool on;
+  uint32_t thresh;  // a uniform 32-bit word below it drops the element
+  uint64_t seed;
+  float inv_keep;   // fl32(1 / (1 - p))
+};
+size_t dropout_keep_words(int64_t T, int64_t K);
+hipError_t launch_dropout_mask(const uint16_t *x, int64_t T, int64_t K, uint32_t thresh, uint64_t seed,
+                               uint32_t *keep, uint16_t *xd, hipStream_t st);
 
 // Adapter-side products (lora.hip).
 enum class LoraKind { kU, kV, kGrad };
@@ -65,15 +82,16 @@ hipError_t launch_lora(LoraKind kind, const uint16_t *P, int64_t ldp, const uint
 // grad_A = s v^T x and grad_B = s dy^T u in one launch (plus one reduction); the
 // partials of grad_A take the first part_a_floats of `part`, those of grad_B follow.
 hipError_t launch_lora_grads(const uint16_t *v, const uint16_t *x, const uint16_t *dy, const uint16_t *u, int64_t T,
-                             int64_t N, int64_t K, int r, float scale, float *grad_A, float *grad_B, float *part,
-                             size_t part_a_floats, hipStream_t st);
+                             int64_t N, int64_t K, int r, float scale_a, float scale_b, float *grad_A, float *grad_B,
+                             float *part, size_t part_a_floats, hipStream_t st);
 
-// Dequant-fused GEMM: out = scale * la lb^T + act W_op (see qgemm.hip).
+// Dequant-fused GEMM: out = keep (.) (scale * la lb^T) + act W_op (see
+// qgemm.hip); keep (dropout words, [ceil(M/32)][Ncols]) may be nullptr.
 hipError_t launch_qgemm(bool trans_w, const uint16_t *act, int64_t M, int64_t Ncols, int64_t Kc, const QWeight &w,
                         const uint16_t *la, const uint16_t *lb, int r, float scale, uint16_t *out,
-                        const Codebook &cb, hipStream_t st);
+                        const Codebook &cb, hipStream_t st, const uint32_t *keep = nullptr);
 
-LinearPlan plan_linear(int64_t T, int64_t N, int64_t K, int r);
+LinearPlan plan_linear(int64_t T, int64_t N, int64_t K, int r, bool dropout = false);
 
 // Optional event bracketing of the fused GEMM launches (diagnostics).
 // Diagnostics: HIP events around the main kernel of each kind (linear.hip).
@@ -96,12 +114,12 @@ bool kernel_timing_read(int64_t *launches, double *ms);  // arrays of kTimedKind
 
 hipError_t launch_linear_fwd(const LinearPlan &p, const uint16_t *x, const QWeight &w, const uint16_t *A,
                              const uint16_t *B, float scale, uint16_t *y, uint16_t *u_out, char *ws,
-                             const Codebook &cb, hipStream_t st);
+                             const Codebook &cb, hipStream_t st, const Dropout &d = Dropout{false, 0u, 0ull, 1.f});
 
 hipError_t launch_linear_bwd(const LinearPlan &p, const uint16_t *dy, const uint16_t *x, const QWeight &w,
                              const uint16_t *A, const uint16_t *B, float scale, const uint16_t *u,
                              uint16_t *grad_x, float *grad_A, float *grad_B, char *ws, const Codebook &cb,
-                             hipStream_t st);
+                             hipStream_t st, const Dropout &d = Dropout{false, 0u, 0ull, 1.f});
 
 // AdamW update of a flat fp32 adapter buffer (optim.hip).  The scalars that
 // depend only on the hyperparameters and the step, each formed in fp64 and

@@ -86,12 +86,13 @@ bool kernel_timing_read(int64_t *launches, double *ms) {
 
 static size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
-LinearPlan plan_linear(int64_t T, int64_t N, int64_t K, int r) {
+LinearPlan plan_linear(int64_t T, int64_t N, int64_t K, int r, bool dropout) {
   LinearPlan p;
   p.T = T;
   p.N = N;
   p.K = K;
   p.r = r;
+  p.dropout = dropout;
   // the four adapter-side products (see lora.hip): M x Nc outputs, contraction Kc
   const int64_t shapes[4][3] = {{T, r, K}, {T, r, N}, {r, K, T}, {N, r, T}};
   size_t part = 0;
@@ -108,17 +109,47 @@ LinearPlan plan_linear(int64_t T, int64_t N, int64_t K, int r) {
   off += align256((size_t)T * r * 2);
   p.off_part = off;
   off += align256(part * 4);
+  // dropout: keep words [ceil(T/32)][K] and the dropped-out input [T x K] bf16
+  p.off_keep = p.off_xd = 0;
+  if (dropout) {
+    p.off_keep = off;
+    off += align256(dropout_keep_words(T, K) * 4);
+    p.off_xd = off;
+    off += align256((size_t)T * K * 2);
+  }
   p.total = off;
   return p;
 }
 
+// The adapter input of a call: x itself, or with dropout the masked copy the
+// mask kernel writes into the workspace (with its keep words).
+struct AdapterInput {
+  const uint16_t *xa;
+  const uint32_t *keep;
+  float inv_keep;
+  hipError_t err;
+};
+
+static AdapterInput adapter_input(const LinearPlan &p, const uint16_t *x, char *ws, const Dropout &d,
+                                  hipStream_t st) {
+  if (!d.on) return AdapterInput{x, nullptr, 1.0f, hipSuccess};
+  uint32_t *keep = (uint32_t *)(ws + p.off_keep);
+  uint16_t *xd = (uint16_t *)(ws + p.off_xd);
+  const hipError_t e = launch_dropout_mask(x, p.T, p.K, d.thresh, d.seed, keep, xd, st);
+  return AdapterInput{xd, keep, d.inv_keep, e};
+}
+
 hipError_t launch_linear_fwd(const LinearPlan &p, const uint16_t *x, const QWeight &w, const uint16_t *A,
                              const uint16_t *B, float scale, uint16_t *y, uint16_t *u_out, char *ws,
-                             const Codebook &cb, hipStream_t st) {
+                             const Codebook &cb, hipStream_t st, const Dropout &d) {
   uint16_t *u = u_out ? u_out : (uint16_t *)(ws + p.off_u);
   float *part = (float *)(ws + p.off_part);
-  if (gemv_applies(p.T, p.K)) return launch_gemv_fwd(p.T, x, w, A, B, p.r, scale, y, u, part, cb, st);
-  hipError_t e = launch_lora(LoraKind::kU, x, p.K, A, p.K, p.T, p.r, p.K, 1.0f, u, part, st);
+  const AdapterInput ai = adapter_input(p, x, ws, d, st);
+  if (ai.err != hipSuccess) return ai.err;
+  if (gemv_applies(p.T, p.K))
+    return launch_gemv_fwd(p.T, x, ai.xa, w, A, B, p.r, scale, ai.inv_keep, y, u, part, cb, st);
+  // u = bf16((1 / (1 - p)) xa A^T): the factor is exactly 1 without dropout
+  hipError_t e = launch_lora(LoraKind::kU, ai.xa, p.K, A, p.K, p.T, p.r, p.K, ai.inv_keep, u, part, st);
   if (e != hipSuccess) return e;
   TimedLaunch tl;
   const bool timed = timing_begin(st, tl, kTimedQgemmFwd);
@@ -130,37 +161,43 @@ hipError_t launch_linear_fwd(const LinearPlan &p, const uint16_t *x, const QWeig
 hipError_t launch_linear_bwd(const LinearPlan &p, const uint16_t *dy, const uint16_t *x, const QWeight &w,
                              const uint16_t *A, const uint16_t *B, float scale, const uint16_t *u,
                              uint16_t *grad_x, float *grad_A, float *grad_B, char *ws, const Codebook &cb,
-                             hipStream_t st) {
+                             hipStream_t st, const Dropout &d) {
   float *part = (float *)(ws + p.off_part);
   uint16_t *v = (uint16_t *)(ws + p.off_v);
+  const AdapterInput ai = adapter_input(p, x, ws, d, st);  // the forward's mask, regenerated
+  if (ai.err != hipSuccess) return ai.err;
+  // grad_A and the adapter term of grad_x carry s / (1 - p); grad_B = s dy^T u
+  const float scale_ax = scale * ai.inv_keep;
   hipError_t e;
   if (gemv_applies(p.T, p.K)) {
-    if (!u) {  // recompute u = x A^T
+    if (!u) {  // recompute u = (1 / (1 - p)) xa A^T
       uint16_t *uw = (uint16_t *)(ws + p.off_u);
-      e = launch_gemv_fwd(p.T, x, w, A, B, p.r, scale, nullptr, uw, part, cb, st);
+      e = launch_gemv_fwd(p.T, x, ai.xa, w, A, B, p.r, scale, ai.inv_keep, nullptr, uw, part, cb, st);
       if (e != hipSuccess) return e;
       u = uw;
     }
-    return launch_gemv_bwd(p.T, dy, x, w, A, B, p.r, scale, u, grad_x, grad_A, grad_B, part, cb, st);
+    return launch_gemv_bwd(p.T, dy, ai.xa, w, A, B, p.r, scale, scale_ax, ai.keep, u, grad_x, grad_A, grad_B, part,
+                           cb, st);
   }
-  if (!u) {  // recompute u = x A^T
+  if (!u) {  // recompute u = (1 / (1 - p)) xa A^T
     uint16_t *uw = (uint16_t *)(ws + p.off_u);
-    e = launch_lora(LoraKind::kU, x, p.K, A, p.K, p.T, p.r, p.K, 1.0f, uw, part, st);
+    e = launch_lora(LoraKind::kU, ai.xa, p.K, A, p.K, p.T, p.r, p.K, ai.inv_keep, uw, part, st);
     if (e != hipSuccess) return e;
     u = uw;
   }
   // v = dy B
   e = launch_lora(LoraKind::kV, dy, p.N, B, p.r, p.T, p.r, p.N, 1.0f, v, part, st);
   if (e != hipSuccess) return e;
-  if (grad_x) {  // grad_x = dy W_hat + s v A
+  if (grad_x) {  // grad_x = dy W_hat + keep (.) (s / (1 - p)) v A
     TimedLaunch tl;
     const bool timed = timing_begin(st, tl, kTimedQgemmDx);
-    e = launch_qgemm(true, dy, p.T, p.K, p.N, w, v, A, p.r, scale, grad_x, cb, st);
+    e = launch_qgemm(true, dy, p.T, p.K, p.N, w, v, A, p.r, scale_ax, grad_x, cb, st, ai.keep);
     if (timed) timing_end(st, tl);
     if (e != hipSuccess) return e;
   }
-  // grad_A = s v^T x [r x K] and grad_B = s dy^T u [N x r], one launch (and one reduction) for both
-  return launch_lora_grads(v, x, dy, u, p.T, p.N, p.K, p.r, scale, grad_A, grad_B, part,
+  // grad_A = (s / (1 - p)) v^T xa [r x K] and grad_B = s dy^T u [N x r], one launch (and one
+  // reduction) for both
+  return launch_lora_grads(v, ai.xa, dy, u, p.T, p.N, p.K, p.r, scale_ax, scale, grad_A, grad_B, part,
                            lora_part_floats(p.r, p.K, p.T), st);
 }
 

@@ -348,11 +348,11 @@ hipError_t launch_lora(LoraKind kind, const uint16_t *P, int64_t ldp, const uint
 }
 
 hipError_t launch_lora_grads(const uint16_t *v, const uint16_t *x, const uint16_t *dy, const uint16_t *u, int64_t T,
-                             int64_t N, int64_t K, int r, float scale, float *grad_A, float *grad_B, float *part,
-                             size_t part_a_floats, hipStream_t st) {
-  // grad_A = s v^T x [r x K] and grad_B = s dy^T u [N x r], contraction over the tokens
-  const LoraProblem a = make_problem(v, r, x, K, r, K, T, scale, grad_A, part);
-  const LoraProblem b = make_problem(dy, N, u, r, N, r, T, scale, grad_B, part + part_a_floats);
+                             int64_t N, int64_t K, int r, float scale_a, float scale_b, float *grad_A, float *grad_B,
+                             float *part, size_t part_a_floats, hipStream_t st) {
+  // grad_A = s_a v^T x [r x K] and grad_B = s_b dy^T u [N x r], contraction over the tokens
+  const LoraProblem a = make_problem(v, r, x, K, r, K, T, scale_a, grad_A, part);
+  const LoraProblem b = make_problem(dy, N, u, r, N, r, T, scale_b, grad_B, part + part_a_floats);
   if ((a.chunk == LT * 8) == (b.chunk == LT * 8)) return launch_pair<true, true, false>(a, &b, st);
   const hipError_t e = launch_pair<true, true, false>(a, nullptr, st);
   return e != hipSuccess ? e : launch_pair<true, true, false>(b, nullptr, st);

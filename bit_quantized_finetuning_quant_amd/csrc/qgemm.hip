@@ -9,18 +9,19 @@
 //   out[M x Ncols] = scale * la lb^T + act . W_op           (bf16 out, fp32 acc)
 //   forward : act = x  [T x n_in],  W_op = W_hat^T, Kc = n_in,  la = u, lb = B
 //   grad_x  : act = dy [T x n_out], W_op = W_hat,   Kc = n_out, la = v, lb = A^T
+//             (with LoRA dropout the adapter term is masked element by element)
 //
 // Workgroup = 8 waves on a 256 x 128 output tile, contraction step 64:
 //   waves 0-3 (consumers) each own a 128 x 64 sub-tile: they read LDS, issue
 //     v_mfma_f32_32x32x16_bf16, and (full tiles) move the activation tile of
 //     stage k+2 from global memory straight into a 3-stage LDS ring with
 //     global_load_lds_dwordx4, so no register ever holds it;
-//   waves 4-7 (producers) fetch the packed weight codes two steps ahead into
-//     registers, decode the nibbles into bf16 by byte permutes from the
-//     block's 16 decoded values held in registers (the weight tile is decoded
-//     once per workgroup and shared by all 256 activation rows) and write the
-//     next weight stage to LDS.  For partial tiles they also carry the
-//     activation tile, masked, through registers.
+//   waves 4-7 (producers) fetch the packed weight codes several steps ahead
+//     into registers, look each code's level up in a 16-entry table in LDS,
+//     multiply it by the block constant in fp32 and round to bf16 (the weight
+//     tile is decoded once per workgroup and shared by all 256 activation
+//     rows), and write the next weight stage to LDS.  For partial tiles they
+//     also carry the activation tile, masked, through registers.
 // One consumer and one producer wave share each SIMD, so the decode's vector
 // ALU work issues alongside the matrix-core work.  One workgroup barrier per
 // contraction step; both roles execute the same number of barriers.  The DMA
@@ -518,11 +519,13 @@ __device__ __forceinline__ void stage_lora(const uint16_t *la, const uint16_t *l
   }
 }
 
-template <bool kTransW, bool kDQ>
+// kDrop (grad_x only): the adapter term is masked by the LoRA dropout words.
+template <bool kTransW, bool kDQ, bool kDrop>
 __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act, int64_t M, int64_t Ncols,
                                                 int64_t Kc, QWeight w, const uint16_t *__restrict__ la,
                                                 const uint16_t *__restrict__ lb, int r, float scale,
-                                                uint16_t *__restrict__ out, Codebook cb) {
+                                                uint16_t *__restrict__ out, Codebook cb,
+                                                const uint32_t *__restrict__ keep) {
   __shared__ __attribute__((aligned(16))) uint16_t sa[kActStages][QBM * 64];
   __shared__ __attribute__((aligned(16))) uint16_t sb[2][QBN * QLD];  // = 64 * TLD
   __shared__ float lut[16];
@@ -559,12 +562,32 @@ __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act
     __syncthreads();
   }
   if (tid < 256) {
+    if (kTransW && kDrop) {
+      // LoRA dropout (grad_x): the adapter term of (row, column) is kept where
+      // bit row % 32 of word [row / 32][column] is set.  The 16 accumulators
+      // of a lane in a 32 x 32 sub-tile share one column and one 32-row block.
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        const int64_t rb = m0 + wm * 128 + i * 32;
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < 2; ++j) {
+          const int64_t col = c0 + wn * 64 + j * 32 + l32;
+          const uint32_t kw = (rb < M && col < Ncols) ? keep[(rb >> 5) * Ncols + col] : 0u;
 #pragma unroll
-        for (int q = 0; q < 16; ++q) acc[i][j][q] *= scale;
+          for (int q = 0; q < 16; ++q) {
+            const int bit = 8 * (q >> 2) + 4 * lhi + (q & 3);
+            acc[i][j][q] = ((kw >> bit) & 1u) ? acc[i][j][q] * scale : 0.f;
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 16; ++q) acc[i][j][q] *= scale;
+    }
   }
 
   if (tid >= 256) {
@@ -699,18 +722,23 @@ __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act
 
 hipError_t launch_qgemm(bool trans_w, const uint16_t *act, int64_t M, int64_t Ncols, int64_t Kc, const QWeight &w,
                         const uint16_t *la, const uint16_t *lb, int r, float scale, uint16_t *out,
-                        const Codebook &cb, hipStream_t st) {
+                        const Codebook &cb, hipStream_t st, const uint32_t *keep) {
   dim3 g((unsigned)((M + QBM - 1) / QBM), (unsigned)((Ncols + QBN - 1) / QBN));
-  if (w.dq) {
-    if (trans_w)
-      qgemm_ws<true, true><<<g, 512, 0, st>>>(act, M, Ncols, Kc, w, la, lb, r, scale, out, cb);
+  if (!trans_w) {  // the forward never takes a dropout mask
+    if (w.dq)
+      qgemm_ws<false, true, false><<<g, 512, 0, st>>>(act, M, Ncols, Kc, w, la, lb, r, scale, out, cb, nullptr);
     else
-      qgemm_ws<false, true><<<g, 512, 0, st>>>(act, M, Ncols, Kc, w, la, lb, r, scale, out, cb);
+      qgemm_ws<false, false, false><<<g, 512, 0, st>>>(act, M, Ncols, Kc, w, la, lb, r, scale, out, cb, nullptr);
+  } else if (keep) {
+    if (w.dq)
+      qgemm_ws<true, true, true><<<g, 512, 0, st>>>(act, M, Ncols, Kc, w, la, lb, r, scale, out, cb, keep);
+    else
+      qgemm_ws<true, false, true><<<g, 512, 0, st>>>(act, M, Ncols, Kc, w, la, lb, r, scale, out, cb, keep);
   } else {
-    if (trans_w)
-      qgemm_ws<true, false><<<g, 512, 0, st>>>(act, M, Ncols, Kc, w, la, lb, r, scale, out, cb);
+    if (w.dq)
+      qgemm_ws<true, true, false><<<g, 512, 0, st>>>(act, M, Ncols, Kc, w, la, lb, r, scale, out, cb, nullptr);
     else
-      qgemm_ws<false, false><<<g, 512, 0, st>>>(act, M, Ncols, Kc, w, la, lb, r, scale, out, cb);
+      qgemm_ws<true, false, false><<<g, 512, 0, st>>>(act, M, Ncols, Kc, w, la, lb, r, scale, out, cb, nullptr);
   }
   return hipGetLastError();
 }

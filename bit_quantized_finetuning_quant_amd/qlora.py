@@ -51,6 +51,12 @@ _SIGNATURES = {
     "qlora_linear_fwd": (ctypes.c_int, [_P, _I64, _P, _P, _P, ctypes.c_int, ctypes.c_float, _P, _P, _P, _SZ, _P]),
     "qlora_linear_bwd": (ctypes.c_int, [_P, _P, _I64, _P, _P, _P, ctypes.c_int, ctypes.c_float, _P, _P, _P, _P,
                                         _P, _SZ, _P]),
+    "qlora_linear_dropout_workspace_bytes": (_SZ, [_I64, _I64, _I64, ctypes.c_int]),
+    "qlora_linear_fwd_dropout": (ctypes.c_int, [_P, _I64, _P, _P, _P, ctypes.c_int, ctypes.c_float, ctypes.c_double,
+                                                ctypes.c_uint64, _P, _P, _P, _SZ, _P]),
+    "qlora_linear_bwd_dropout": (ctypes.c_int, [_P, _P, _I64, _P, _P, _P, ctypes.c_int, ctypes.c_float,
+                                                ctypes.c_double, ctypes.c_uint64, _P, _P, _P, _P, _P, _SZ, _P]),
+    "qlora_dropout_mask": (ctypes.c_int, [_P, _I64, _I64, ctypes.c_double, ctypes.c_uint64, _P, _P, _P]),
     "qlora_adamw_step": (ctypes.c_int, [_P, _P, _P, _P, _P, _I64, _I64, ctypes.c_double, ctypes.c_double,
                                         ctypes.c_double, ctypes.c_double, ctypes.c_double, _P]),
     "qlora_status_read": (ctypes.c_int, [_P, _P]),
@@ -286,3 +292,60 @@ def adamw_step(param, param_bf16, grad, exp_avg, exp_avg_sq, step: int, lr: floa
     _check(lib().qlora_adamw_step(_ptr(param), _ptr(param_bf16), _ptr(grad), _ptr(exp_avg), _ptr(exp_avg_sq), n,
                                   int(step), float(lr), float(beta1), float(beta2), float(eps), float(weight_decay),
                                   _stream(stream)), "qlora_adamw_step")
+
+
+# ------------------------------------------------------------------ LoRA dropout
+def linear_dropout_workspace_bytes(tokens: int, n_out: int, n_in: int, r: int) -> int:
+    return int(lib().qlora_linear_dropout_workspace_bytes(tokens, n_out, n_in, r))
+
+
+def linear_dropout_workspace(tokens: int, n_out: int, n_in: int, r: int, device="cuda"):
+    torch = _torch()
+    return torch.empty(max(linear_dropout_workspace_bytes(tokens, n_out, n_in, r), 1), dtype=torch.uint8,
+                       device=device)
+
+
+def linear_fwd_dropout(x, q: NF4Weight, A, B, scale: float, p: float, seed: int, y=None, u_out=None, save_u=True,
+                       workspace=None, stream=None):
+    """linear_fwd with LoRA dropout of probability p on the adapter input (mask from seed)."""
+    torch = _torch()
+    T, r = x.shape[0], A.shape[0]
+    y = y if y is not None else torch.empty((T, q.n_out), dtype=torch.bfloat16, device=x.device)
+    if save_u and u_out is None:
+        u_out = torch.empty((T, r), dtype=torch.bfloat16, device=x.device)
+    ws = workspace if workspace is not None else linear_dropout_workspace(T, q.n_out, q.n_in, r, x.device)
+    st = q.struct()
+    _check(lib().qlora_linear_fwd_dropout(_ptr(x), T, ctypes.byref(st), _ptr(A), _ptr(B), r, float(scale), float(p),
+                                          int(seed), _ptr(y), _ptr(u_out), _ptr(ws), ws.numel(), _stream(stream)),
+           "qlora_linear_fwd_dropout")
+    return y, u_out
+
+
+def linear_bwd_dropout(dy, x, q: NF4Weight, A, B, scale: float, p: float, seed: int, u=None, need_grad_x=True,
+                       grad_x=None, grad_A=None, grad_B=None, workspace=None, stream=None):
+    """linear_bwd with the forward's dropout mask (same p and seed)."""
+    torch = _torch()
+    T, r, dev = x.shape[0], A.shape[0], x.device
+    if need_grad_x and grad_x is None:
+        grad_x = torch.empty((T, q.n_in), dtype=torch.bfloat16, device=dev)
+    if not need_grad_x:
+        grad_x = None
+    grad_A = grad_A if grad_A is not None else torch.empty((r, q.n_in), dtype=torch.float32, device=dev)
+    grad_B = grad_B if grad_B is not None else torch.empty((q.n_out, r), dtype=torch.float32, device=dev)
+    ws = workspace if workspace is not None else linear_dropout_workspace(T, q.n_out, q.n_in, r, dev)
+    st = q.struct()
+    _check(lib().qlora_linear_bwd_dropout(_ptr(dy), _ptr(x), T, ctypes.byref(st), _ptr(A), _ptr(B), r, float(scale),
+                                          float(p), int(seed), _ptr(u), _ptr(grad_x), _ptr(grad_A), _ptr(grad_B),
+                                          _ptr(ws), ws.numel(), _stream(stream)), "qlora_linear_bwd_dropout")
+    return grad_x, grad_A, grad_B
+
+
+def dropout_mask(x, p: float, seed: int, stream=None):
+    """(keep_words [ceil(T/32) x K] int32, x_drop [T x K] bf16) for a [T x K] bf16 tensor."""
+    torch = _torch()
+    T, K = x.shape
+    keep = torch.empty(((T + 31) // 32, K), dtype=torch.int32, device=x.device)
+    xd = torch.empty((T, K), dtype=torch.bfloat16, device=x.device)
+    _check(lib().qlora_dropout_mask(_ptr(x), T, K, float(p), int(seed), _ptr(keep), _ptr(xd), _stream(stream)),
+           "qlora_dropout_mask")
+    return keep, xd

@@ -171,6 +171,49 @@ qlora_status qlora_linear_bwd(const uint16_t *dy, const uint16_t *x, int64_t T,
                               float *grad_A, float *grad_B, void *ws, size_t ws_bytes,
                               void *stream);
 
+/* ---- LoRA dropout -------------------------------------------------------- */
+
+/* The recipe sets a dropout probability p on the adapters ("Tutorial
+ * fine-tuning LLM LoRA/QLoRA", section "Código Completo", step "4.
+ * Configuração LoRA").  Dropout acts on the adapter input only, kept values
+ * scaled by 1 / (1 - p); the backward uses the same mask:
+ *   u      = bf16( (1 / (1 - p)) (keep (.) x) A^T )
+ *   y      = bf16( x W_hat^T + scale * u B^T )
+ *   grad_x = bf16( dy W_hat + (scale / (1 - p)) keep (.) (v A) ),  v = dy B
+ *   grad_A = (scale / (1 - p)) v^T (keep (.) x),   grad_B = scale * dy^T u
+ * The mask is a pure function of (seed, position): element e = t K + k of
+ * x [T x K] takes 32-bit word e mod 8 of the Philox4x64-10 block (Salmon et
+ * al., SC 2011) for counter (e div 8, 0, 0, 0) and key (seed, 0) -- the four
+ * 64-bit outputs in order, low half first -- and is kept iff that word is
+ * >= min(2^32 - 1, floor(p 2^32 + 1/2)).  The forward and the backward each
+ * regenerate it, so pass them the same seed (and a new seed per step).
+ * 0 <= dropout_p < 1 (QLORA_ERR_VALUE otherwise); p = 0 keeps everything
+ * (the results then equal those of the plain calls up to rounding order).   */
+
+/* Workspace of the two dropout calls: the plain one plus the mask words and
+ * the masked input (4 ceil(T/32) n_in + 2 T n_in bytes, 256-B aligned).     */
+size_t qlora_linear_dropout_workspace_bytes(int64_t T, int64_t n_out, int64_t n_in, int r);
+
+/* qlora_linear_fwd with LoRA dropout (same shapes, rules and errors).        */
+qlora_status qlora_linear_fwd_dropout(const uint16_t *x, int64_t T, const qlora_nf4_weight *q,
+                                      const uint16_t *A, const uint16_t *B, int r, float scale,
+                                      double dropout_p, uint64_t seed, uint16_t *y, uint16_t *u_out,
+                                      void *ws, size_t ws_bytes, void *stream);
+
+/* qlora_linear_bwd with LoRA dropout; u = NULL recomputes it with the mask.  */
+qlora_status qlora_linear_bwd_dropout(const uint16_t *dy, const uint16_t *x, int64_t T,
+                                      const qlora_nf4_weight *q, const uint16_t *A, const uint16_t *B,
+                                      int r, float scale, double dropout_p, uint64_t seed,
+                                      const uint16_t *u, uint16_t *grad_x, float *grad_A,
+                                      float *grad_B, void *ws, size_t ws_bytes, void *stream);
+
+/* The mask itself, as the linear calls form it, for x [T x K] bf16 (device,
+ * K % 8 == 0): keep_words [ceil(T/32) x K] uint32, bit b of word [tb][k] set
+ * iff (32 tb + b, k) is kept (0 past T); x_drop [T x K] bf16 = x where kept,
+ * +0 where dropped.  Device buffers, 16-B aligned, caller-owned.            */
+qlora_status qlora_dropout_mask(const uint16_t *x, int64_t T, int64_t K, double dropout_p,
+                                uint64_t seed, uint32_t *keep_words, uint16_t *x_drop, void *stream);
+
 /* AdamW update of n adapter values held in one flat buffer (the caller lays
  * the A and B matrices of its adapters out back to back).  Only the adapters
  * train, and the optimizer keeps two moments per trained value ("LoRA vs.

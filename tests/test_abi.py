@@ -152,3 +152,22 @@ def test_storage_flag_validation_and_sizes():
         assert bits == pytest.approx(oracle.bits_per_param(n_out, n_in, double_quant=False), abs=1e-12)
     assert lib.qlora_nf4_bytes_flags(512, 256, 4) == 0
     assert lib.qlora_nf4_bytes_flags(512, 256, 0) == qlora.nf4_bytes(512, 256)
+
+
+def test_dropout_argument_validation_before_any_launch():
+    lib = qlora.lib()
+    w = _fake_weight()
+    ws = qlora.linear_dropout_workspace_bytes(16, 512, 256, 8)
+    assert ws > qlora.linear_workspace_bytes(16, 512, 256, 8) + 2 * 16 * 256
+    for p in (-0.1, 1.0, float("nan")):
+        assert lib.qlora_linear_fwd_dropout(0x50000, 16, ctypes.byref(w), 0x60000, 0x70000, 8, 2.0, p, 1,
+                                            0x80000, None, 0x90000, ws, None) == 8
+        assert lib.qlora_dropout_mask(0x50000, 16, 64, p, 1, 0x60000, 0x70000, None) == 8
+    assert lib.qlora_linear_fwd_dropout(0x50000, 16, ctypes.byref(w), 0x60000, 0x70000, 8, 2.0, 0.05, 1,
+                                        0x80000, None, 0x90000, ws - 1, None) == 4
+    assert lib.qlora_linear_bwd_dropout(0x50000, 0x50000, 16, ctypes.byref(w), 0x60000, 0x70000, 8, 2.0, 0.05, 1,
+                                        None, None, 0x80000, 0x90000, 0xA0000, ws - 1, None) == 4
+    assert lib.qlora_dropout_mask(0x50000, 16, 60, 0.05, 1, 0x60000, 0x70000, None) == 2  # K % 8
+    assert lib.qlora_dropout_mask(0x50000, 0, 64, 0.05, 1, 0x60000, 0x70000, None) == 2
+    assert lib.qlora_dropout_mask(0x50000, 16, 64, 0.05, 1, None, 0x70000, None) == 1
+    assert lib.qlora_dropout_mask(0x50008, 16, 64, 0.05, 1, 0x60000, 0x70000, None) == 3
