@@ -96,6 +96,23 @@ class LinearStep:
                       grad_A=self.ga, grad_B=self.gb, workspace=self.ws)
 
 
+class DropoutStep(LinearStep):
+    """The same step with LoRA dropout p on the adapter input (a new seed every step)."""
+
+    def __init__(self, case, torch, qlora, dev_bf16, dev_f32, p=0.05):
+        super().__init__(case, torch, qlora, dev_bf16, dev_f32)
+        self.p, self.seed = p, 0
+        self.ws = qlora.linear_dropout_workspace(case.tokens, case.n_out, case.n_in, case.r)
+
+    def __call__(self):
+        c, ql = self.case, self.qlora
+        self.seed += 1
+        ql.linear_fwd_dropout(self.x, self.q, self.a, self.b, c.scale, self.p, self.seed, y=self.y, u_out=self.u,
+                              workspace=self.ws)
+        ql.linear_bwd_dropout(self.dy, self.x, self.q, self.a, self.b, c.scale, self.p, self.seed, u=self.u,
+                              grad_x=self.gx, grad_A=self.ga, grad_B=self.gb, workspace=self.ws)
+
+
 def dev_helpers(torch):
     def dev_bf16(bits):
         t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16)).cuda()
@@ -336,6 +353,21 @@ def extra_measurements(torch, qlora, steps):
     return out
 
 
+def extra_dropout(torch, qlora, case, dev_bf16, dev_f32, steps):
+    """The headline step with LoRA dropout 0.05 (mask regenerated in the forward and in the
+    backward), against the same step without it."""
+    plain = LinearStep(case, torch, qlora, dev_bf16, dev_f32)
+    drop = DropoutStep(case, torch, qlora, dev_bf16, dev_f32, p=0.05)
+    for _ in range(3):
+        plain()
+        drop()
+    t0, _ = time_region(torch, plain, steps)
+    t1, _ = time_region(torch, drop, steps)
+    flops = linear_flops(case.tokens, case.n_out, case.n_in, case.r)
+    return {"dropout_7b_attn_T2048": {"TFLOP/s": flops * steps / t1 / 1e12, "ms_per_step": t1 / steps * 1e3,
+                                      "ms_per_step_without": t0 / steps * 1e3, "p": 0.05, "steps": steps}}
+
+
 def extra_adamw(torch, qlora, workloads, steps):
     """AdamW over the adapters of the 7B layer set at r = 64, 32 layers in one
     flat buffer (159,907,840 values): 16 B read and 14 B written per value with
@@ -466,7 +498,7 @@ def main():
                          "path, rotating over more than 1 GB of distinct packed weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--extra-only", choices=["adamw"], default=None,
+    ap.add_argument("--extra-only", choices=["adamw", "dropout"], default=None,
                     help="run only this extra measurement and print its JSON (for profiling it alone)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before the steps, copy 256 MiB device to device three times (untimed): the "
@@ -493,6 +525,10 @@ def main():
         print(json.dumps(extra_adamw(torch, qlora, workloads, args.steps)), flush=True)
         return
     dev_bf16, dev_f32 = dev_helpers(torch)
+    if args.extra_only == "dropout":
+        case = workloads.attn7b_case(2048)
+        print(json.dumps(extra_dropout(torch, qlora, case, dev_bf16, dev_f32, args.steps)), flush=True)
+        return
     tokens = 2048 if args.workload == "7b_attn" else 1
     log(f"generating the 7B projection workload (4096x4096, T={tokens}, r=64)")
     case = workloads.attn7b_case(tokens)
@@ -536,11 +572,13 @@ def main():
         "roofline": roofline,
     }
     if not args.no_extra and tokens > 1:
-        log("extra measurements: layer sets, bulk 65B store, bulk dequant, T=1 path, quantize, adapter AdamW")
+        log("extra measurements: layer sets, bulk 65B store, bulk dequant, T=1 path, quantize, adapter AdamW, "
+            "LoRA dropout")
         extra = extra_layers(torch, qlora, workloads, args.steps)
         extra["bulk_65b"] = extra_bulk_65b(torch, qlora, workloads)
         extra.update(extra_measurements(torch, qlora, args.steps))
         extra.update(extra_adamw(torch, qlora, workloads, args.steps))
+        extra.update(extra_dropout(torch, qlora, case, dev_bf16, dev_f32, args.steps))
         result["extra"] = extra
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on host cores")
