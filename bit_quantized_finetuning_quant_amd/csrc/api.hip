@@ -133,6 +133,23 @@ bool device_address(const void *p, void **dev) {
   }
 }
 
+// A projection set: 1..kMaxSetMembers members sharing n_in and the storage
+// form, T above the few-token limit, adapter rank r per member.
+qlora_status check_set(int64_t T, int count, const qlora_nf4_weight *q, int r, float scale, int64_t *N) {
+  if (!q) return QLORA_ERR_NULL;
+  if (count < 1 || count > kMaxSetMembers) return QLORA_ERR_SHAPE;
+  for (int i = 0; i < count; ++i) {
+    const qlora_status s = check_linear(T, &q[i], r, scale);
+    if (s != QLORA_OK) return s;
+    if (q[i].n_in != q[0].n_in) return QLORA_ERR_SHAPE;
+    if (q[i].flags != q[0].flags) return QLORA_ERR_VALUE;
+    N[i] = q[i].n_out;
+  }
+  if (T <= kGemvMaxT) return QLORA_ERR_SHAPE;
+  if (T * (int64_t)count * r > kMaxNumel) return QLORA_ERR_SHAPE;
+  return QLORA_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -331,6 +348,59 @@ qlora_status qlora_linear_bwd_dropout(const uint16_t *dy, const uint16_t *x, int
   if (ws_bytes < p.total) return QLORA_ERR_WORKSPACE;
   hipError_t e = launch_linear_bwd(p, dy, x, qweight(q), A, B, scale, u, grad_x, grad_A, grad_B, (char *)ws,
                                    tables().cb, (hipStream_t)stream, d);
+  return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP;
+}
+
+size_t qlora_linear_set_workspace_bytes(int64_t T, int count, const int64_t *n_out, int64_t n_in, int r) {
+  if (!n_out || count < 1 || count > kMaxSetMembers || T <= kGemvMaxT || T > kMaxNumel) return 0;
+  if (n_in % kBlock != 0 || r < 1 || r > 256) return 0;
+  for (int i = 0; i < count; ++i)
+    if (!shape_ok(n_out[i], n_in)) return 0;
+  return plan_linear_set(T, count, n_out, n_in, r).total;
+}
+
+qlora_status qlora_linear_set_fwd(const uint16_t *x, int64_t T, int count, const qlora_nf4_weight *q,
+                                  const uint16_t *A_set, const uint16_t *const *B, int r, float scale,
+                                  uint16_t *const *y, uint16_t *u_out, void *ws, size_t ws_bytes, void *stream) {
+  int64_t N[kMaxSetMembers];
+  qlora_status s = check_set(T, count, q, r, scale, N);
+  if (s != QLORA_OK) return s;
+  if (!x || !A_set || !B || !y || !ws) return QLORA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(A_set) || !aligned16(ws) || (u_out && !aligned16(u_out))) return QLORA_ERR_ALIGN;
+  QWeight w[kMaxSetMembers];
+  for (int i = 0; i < count; ++i) {
+    if (!B[i] || !y[i]) return QLORA_ERR_NULL;
+    if (!aligned16(B[i]) || !aligned16(y[i])) return QLORA_ERR_ALIGN;
+    w[i] = qweight(&q[i]);
+  }
+  const SetPlan p = plan_linear_set(T, count, N, q[0].n_in, r);
+  if (ws_bytes < p.total) return QLORA_ERR_WORKSPACE;
+  hipError_t e = launch_linear_set_fwd(p, x, w, A_set, B, scale, y, u_out, (char *)ws, tables().cb,
+                                       (hipStream_t)stream);
+  return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP;
+}
+
+qlora_status qlora_linear_set_bwd(const uint16_t *const *dy, const uint16_t *x, int64_t T, int count,
+                                  const qlora_nf4_weight *q, const uint16_t *A_set, const uint16_t *const *B, int r,
+                                  float scale, const uint16_t *u, uint16_t *grad_x, float *grad_A_set,
+                                  float *const *grad_B, void *ws, size_t ws_bytes, void *stream) {
+  int64_t N[kMaxSetMembers];
+  qlora_status s = check_set(T, count, q, r, scale, N);
+  if (s != QLORA_OK) return s;
+  if (!dy || !x || !A_set || !B || !grad_A_set || !grad_B || !ws) return QLORA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(A_set) || !aligned16(grad_A_set) || !aligned16(ws) || (u && !aligned16(u)) ||
+      (grad_x && !aligned16(grad_x)))
+    return QLORA_ERR_ALIGN;
+  QWeight w[kMaxSetMembers];
+  for (int i = 0; i < count; ++i) {
+    if (!dy[i] || !B[i] || !grad_B[i]) return QLORA_ERR_NULL;
+    if (!aligned16(dy[i]) || !aligned16(B[i]) || !aligned16(grad_B[i])) return QLORA_ERR_ALIGN;
+    w[i] = qweight(&q[i]);
+  }
+  const SetPlan p = plan_linear_set(T, count, N, q[0].n_in, r);
+  if (ws_bytes < p.total) return QLORA_ERR_WORKSPACE;
+  hipError_t e = launch_linear_set_bwd(p, dy, x, w, A_set, B, scale, u, grad_x, grad_A_set, grad_B, (char *)ws,
+                                       tables().cb, (hipStream_t)stream);
   return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP;
 }
 

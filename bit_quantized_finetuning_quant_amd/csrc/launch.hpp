@@ -85,6 +85,37 @@ hipError_t launch_lora_grads(const uint16_t *v, const uint16_t *x, const uint16_
                              int64_t N, int64_t K, int r, float scale_a, float scale_b, float *grad_A, float *grad_B,
                              float *part, size_t part_a_floats, hipStream_t st);
 
+// A projection set: linears that share their input (q/k/v, gate/up), run as
+// one fused GEMM launch (qgemm.hip).  Members share n_in and the storage form.
+constexpr int kMaxSetMembers = 4;
+struct QgemmMember {
+  QWeight w;
+  const uint16_t *act;  // grad_x: this member's dy [M x n_out]
+  const uint16_t *lb;   // forward: this member's B [n_out x r]
+  uint16_t *out;        // forward: this member's y [M x n_out]
+  int64_t tile0;        // forward: first column tile (set by the launcher)
+};
+struct QgemmSet {
+  int count;
+  int64_t ld_la;  // row stride of the adapter left factor (u_set or v_set)
+  QgemmMember m[kMaxSetMembers];
+};
+// forward: x shared, la = u_set (member i reads columns [i r, i r + r)); grad_x:
+// gx = sum over members of dy_i W_hat_i + keep (.) (scale * la lb^T) with la =
+// v_set, lb = A_set and r the total rank.
+hipError_t launch_qgemm_set(bool trans_w, const QgemmSet &set, int64_t M, const uint16_t *x, const uint16_t *la,
+                            const uint16_t *lb, int r, float scale, uint16_t *gx, const Codebook &cb, hipStream_t st,
+                            const uint32_t *keep = nullptr);
+
+// Adapter products of a projection set (lora.hip); each product has its own
+// region of `part`, lora_set_part_floats in all.
+size_t lora_set_part_floats(int64_t T, int count, const int64_t *N, int64_t K, int r);
+hipError_t launch_lora_set_v(const uint16_t *const *dy, const uint16_t *const *B, const int64_t *N, int count,
+                             int64_t T, int r, uint16_t *v_set, float *part, hipStream_t st);
+hipError_t launch_lora_set_grads(const uint16_t *v_set, const uint16_t *x, const uint16_t *const *dy,
+                                 const uint16_t *u_set, const int64_t *N, int count, int64_t T, int64_t K, int r,
+                                 float scale, float *grad_A_set, float *const *grad_B, float *part, hipStream_t st);
+
 // Dequant-fused GEMM: out = keep (.) (scale * la lb^T) + act W_op (see
 // qgemm.hip); keep (dropout words, [ceil(M/32)][Ncols]) may be nullptr.
 hipError_t launch_qgemm(bool trans_w, const uint16_t *act, int64_t M, int64_t Ncols, int64_t Kc, const QWeight &w,
@@ -134,5 +165,23 @@ struct AdamwScalars {
 };
 hipError_t launch_adamw(float *param, uint16_t *param_bf16, const float *grad, float *exp_avg, float *exp_avg_sq,
                         int64_t n, const AdamwScalars &s, hipStream_t st);
+
+// Projection sets (linear.hip): members share x [T x K] and the adapter
+// rank r; A_set [count r x K] holds the members' A back to back, u_set and
+// v_set are [T x count r].  T > kGemvMaxT.
+struct SetPlan {
+  int64_t T, K;
+  int r, count;
+  int64_t N[kMaxSetMembers];
+  size_t off_u, off_v, off_part, total;
+};
+SetPlan plan_linear_set(int64_t T, int count, const int64_t *N, int64_t K, int r);
+hipError_t launch_linear_set_fwd(const SetPlan &p, const uint16_t *x, const QWeight *w, const uint16_t *A_set,
+                                 const uint16_t *const *B, float scale, uint16_t *const *y, uint16_t *u_out, char *ws,
+                                 const Codebook &cb, hipStream_t st);
+hipError_t launch_linear_set_bwd(const SetPlan &p, const uint16_t *const *dy, const uint16_t *x, const QWeight *w,
+                                 const uint16_t *A_set, const uint16_t *const *B, float scale, const uint16_t *u,
+                                 uint16_t *grad_x, float *grad_A_set, float *const *grad_B, char *ws,
+                                 const Codebook &cb, hipStream_t st);
 
 }  // namespace qlora

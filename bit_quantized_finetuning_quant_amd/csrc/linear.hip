@@ -201,4 +201,84 @@ hipError_t launch_linear_bwd(const LinearPlan &p, const uint16_t *dy, const uint
                            lora_part_floats(p.r, p.K, p.T), st);
 }
 
+// ---------------------------------------------------------------------------
+// Projection sets: linears that read the same input (q/k/v, gate/up).
+
+SetPlan plan_linear_set(int64_t T, int count, const int64_t *N, int64_t K, int r) {
+  SetPlan p;
+  p.T = T;
+  p.K = K;
+  p.r = r;
+  p.count = count;
+  for (int i = 0; i < kMaxSetMembers; ++i) p.N[i] = i < count ? N[i] : 0;
+  const size_t uv = align256((size_t)T * count * r * 2);
+  size_t off = 256;
+  p.off_u = off;
+  off += uv;
+  p.off_v = off;
+  off += uv;
+  p.off_part = off;
+  off += align256(lora_set_part_floats(T, count, N, K, r) * 4);
+  p.total = off;
+  return p;
+}
+
+hipError_t launch_linear_set_fwd(const SetPlan &p, const uint16_t *x, const QWeight *w, const uint16_t *A_set,
+                                 const uint16_t *const *B, float scale, uint16_t *const *y, uint16_t *u_out, char *ws,
+                                 const Codebook &cb, hipStream_t st) {
+  uint16_t *u = u_out ? u_out : (uint16_t *)(ws + p.off_u);
+  float *part = (float *)(ws + p.off_part);
+  const int64_t rt = (int64_t)p.count * p.r;
+  // u_set = x A_set^T: one product for every member's u
+  hipError_t e = launch_lora(LoraKind::kU, x, p.K, A_set, p.K, p.T, rt, p.K, 1.0f, u, part, st);
+  if (e != hipSuccess) return e;
+  QgemmSet s{};
+  s.count = p.count;
+  s.ld_la = rt;
+  for (int i = 0; i < p.count; ++i) {
+    s.m[i].w = w[i];
+    s.m[i].lb = B[i];
+    s.m[i].out = y[i];
+  }
+  TimedLaunch tl;
+  const bool timed = timing_begin(st, tl, kTimedQgemmFwd);
+  e = launch_qgemm_set(false, s, p.T, x, u, nullptr, p.r, scale, nullptr, cb, st);
+  if (timed) timing_end(st, tl);
+  return e;
+}
+
+hipError_t launch_linear_set_bwd(const SetPlan &p, const uint16_t *const *dy, const uint16_t *x, const QWeight *w,
+                                 const uint16_t *A_set, const uint16_t *const *B, float scale, const uint16_t *u,
+                                 uint16_t *grad_x, float *grad_A_set, float *const *grad_B, char *ws,
+                                 const Codebook &cb, hipStream_t st) {
+  float *part = (float *)(ws + p.off_part);
+  uint16_t *v = (uint16_t *)(ws + p.off_v);
+  const int64_t rt = (int64_t)p.count * p.r;
+  hipError_t e;
+  if (!u) {  // recompute u_set = x A_set^T
+    uint16_t *uw = (uint16_t *)(ws + p.off_u);
+    e = launch_lora(LoraKind::kU, x, p.K, A_set, p.K, p.T, rt, p.K, 1.0f, uw, part, st);
+    if (e != hipSuccess) return e;
+    u = uw;
+  }
+  // v_set: member i's columns = dy_i B_i
+  e = launch_lora_set_v(dy, B, p.N, p.count, p.T, p.r, v, part, st);
+  if (e != hipSuccess) return e;
+  if (grad_x) {  // grad_x = sum_i dy_i W_hat_i + s v_set A_set: one GEMM contracting over every member
+    QgemmSet s{};
+    s.count = p.count;
+    s.ld_la = rt;
+    for (int i = 0; i < p.count; ++i) {
+      s.m[i].w = w[i];
+      s.m[i].act = dy[i];
+    }
+    TimedLaunch tl;
+    const bool timed = timing_begin(st, tl, kTimedQgemmDx);
+    e = launch_qgemm_set(true, s, p.T, nullptr, v, A_set, (int)rt, scale, grad_x, cb, st);
+    if (timed) timing_end(st, tl);
+    if (e != hipSuccess) return e;
+  }
+  return launch_lora_set_grads(v, x, dy, u, p.N, p.count, p.T, p.K, p.r, scale, grad_A_set, grad_B, part, st);
+}
+
 }  // namespace qlora

@@ -20,6 +20,8 @@
 // fp32 partial tile and a second kernel adds the partials in split order (so
 // the result is deterministic) and writes the scaled output.
 
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -101,7 +103,9 @@ __device__ __forceinline__ void lora_body(const uint16_t *__restrict__ P, int64_
                                           uint16_t (*sB)[LT * LLD], f32x16 &acc) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const bool vp = (ldp % 8) == 0, vq = (ldq % 8) == 0;
+  // 16-byte loads need 16-byte aligned rows: the row stride and the base (a
+  // member's columns of a set's u may start mid-row)
+  const bool vp = (ldp % 8) == 0 && ((uintptr_t)P & 15u) == 0, vq = (ldq % 8) == 0 && ((uintptr_t)Q & 15u) == 0;
   // Operand tiles in natural layout: a row operand as [out rows][contraction],
   // a column operand as [contraction rows][out columns].  A group of
   // contraction steps is fetched at once; the next group's loads reuse the
@@ -167,6 +171,7 @@ struct LoraProblem {
   int S;
   float scale;  // applied here when S == 1, else by the reduction
   void *out;
+  int64_t ldo;  // row stride of out (Nc unless the product fills columns of a wider matrix)
   float *part;
 };
 
@@ -183,7 +188,8 @@ __device__ __forceinline__ void lora_tile(const LoraProblem &pr, int64_t tile, i
   for (int q = 0; q < 16; ++q) acc[q] = 0.f;
   // full: both operand tiles in range and aligned, and the chunk is whole groups
   const bool full = (m0 + LT <= pr.M) && (n0 + LT <= pr.Nc) && ((ke - kb) % (LT * kGroupSteps) == 0) &&
-                    (pr.ldp % 8 == 0) && (pr.ldq % 8 == 0);
+                    (pr.ldp % 8 == 0) && (pr.ldq % 8 == 0) && (((uintptr_t)pr.P & 15u) == 0) &&
+                    (((uintptr_t)pr.Q & 15u) == 0);
   if (full)
     lora_body<kAT, kBT, kBf16Out, true, kGroupSteps>(pr.P, pr.ldp, pr.Q, pr.ldq, pr.M, pr.Nc, kb, ke, m0, n0, sA, sB,
                                                       acc);
@@ -197,7 +203,7 @@ __device__ __forceinline__ void lora_tile(const LoraProblem &pr, int64_t tile, i
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int64_t gm = m0 + wm * 32 + 8 * (q >> 2) + 4 * (lane >> 5) + (q & 3), gn = n0 + col;
-      if (gm < pr.M && gn < pr.Nc) emit_out<kBf16Out>(pr.out, gm * pr.Nc + gn, acc[q] * pr.scale);
+      if (gm < pr.M && gn < pr.Nc) emit_out<kBf16Out>(pr.out, gm * pr.ldo + gn, acc[q] * pr.scale);
     }
     return;
   }
@@ -249,7 +255,7 @@ __device__ __forceinline__ void reduce_quad(const LoraProblem &pr, int64_t qd) {
   }
 #pragma unroll
   for (int e = 0; e < 4; ++e)
-    if (gn + e < pr.Nc) emit_out<kBf16Out>(pr.out, gm * pr.Nc + gn + e, acc[e] * pr.scale);
+    if (gn + e < pr.Nc) emit_out<kBf16Out>(pr.out, gm * pr.ldo + gn + e, acc[e] * pr.scale);
 }
 
 template <bool kBf16Out>
@@ -304,6 +310,7 @@ LoraProblem make_problem(const uint16_t *P, int64_t ldp, const uint16_t *Q, int6
   pr.S = (int)cdiv(Kc, pr.chunk);
   pr.scale = scale;
   pr.out = out;
+  pr.ldo = Nc;
   pr.part = part;
   return pr;
 }
@@ -356,6 +363,63 @@ hipError_t launch_lora_grads(const uint16_t *v, const uint16_t *x, const uint16_
   if ((a.chunk == LT * 8) == (b.chunk == LT * 8)) return launch_pair<true, true, false>(a, &b, st);
   const hipError_t e = launch_pair<true, true, false>(a, nullptr, st);
   return e != hipSuccess ? e : launch_pair<true, true, false>(b, nullptr, st);
+}
+
+// Adapter products of a projection set (members i < count, ranks r each).
+size_t lora_set_part_floats(int64_t T, int count, const int64_t *N, int64_t K, int r) {
+  size_t v = 0, g = lora_part_floats((int64_t)count * r, K, T);
+  for (int i = 0; i < count; ++i) {
+    v += lora_part_floats(T, r, N[i]);
+    g += lora_part_floats(N[i], r, T);
+  }
+  return std::max(lora_part_floats(T, (int64_t)count * r, K), std::max(v, g));
+}
+
+// Runs a list of products of one operand form, two per launch where their
+// group lengths agree.
+template <bool kAT, bool kBT, bool kBf16Out>
+static hipError_t launch_list(const LoraProblem *pr, int n, hipStream_t st) {
+  for (int i = 0; i < n;) {
+    hipError_t e;
+    if (i + 1 < n && (pr[i].chunk == LT * 8) == (pr[i + 1].chunk == LT * 8)) {
+      e = launch_pair<kAT, kBT, kBf16Out>(pr[i], &pr[i + 1], st);
+      i += 2;
+    } else {
+      e = launch_pair<kAT, kBT, kBf16Out>(pr[i], nullptr, st);
+      i += 1;
+    }
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+// v_set [T x count r]: columns [i r, i r + r) = dy_i B_i.
+hipError_t launch_lora_set_v(const uint16_t *const *dy, const uint16_t *const *B, const int64_t *N, int count,
+                             int64_t T, int r, uint16_t *v_set, float *part, hipStream_t st) {
+  LoraProblem pr[kMaxSetMembers];
+  size_t off = 0;
+  for (int i = 0; i < count; ++i) {
+    pr[i] = make_problem(dy[i], N[i], B[i], r, T, r, N[i], 1.0f, v_set + (int64_t)i * r, part + off);
+    pr[i].ldo = (int64_t)count * r;
+    off += lora_part_floats(T, r, N[i]);
+  }
+  return launch_list<false, true, true>(pr, count, st);
+}
+
+// grad_A_set = scale v_set^T x [count r x K] and grad_B_i = scale dy_i^T u_i [N_i x r]
+// (u_i = columns [i r, i r + r) of u_set).
+hipError_t launch_lora_set_grads(const uint16_t *v_set, const uint16_t *x, const uint16_t *const *dy,
+                                 const uint16_t *u_set, const int64_t *N, int count, int64_t T, int64_t K, int r,
+                                 float scale, float *grad_A_set, float *const *grad_B, float *part, hipStream_t st) {
+  LoraProblem pr[kMaxSetMembers + 1];
+  const int64_t rt = (int64_t)count * r;
+  pr[0] = make_problem(v_set, rt, x, K, rt, K, T, scale, grad_A_set, part);
+  size_t off = lora_part_floats(rt, K, T);
+  for (int i = 0; i < count; ++i) {
+    pr[i + 1] = make_problem(dy[i], N[i], u_set + (int64_t)i * r, rt, N[i], r, T, scale, grad_B[i], part + off);
+    off += lora_part_floats(N[i], r, T);
+  }
+  return launch_list<true, true, false>(pr, count + 1, st);
 }
 
 }  // namespace qlora

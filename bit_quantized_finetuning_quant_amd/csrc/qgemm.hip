@@ -486,19 +486,19 @@ __device__ __forceinline__ u32x4 load_b_frag(const uint16_t *B, int wn, int lane
 
 // LoRA term of the output tile, staged through LDS in the same layouts as the
 // main contraction (one 64-wide chunk of the rank r at a time, zero past r):
-// the left factor la [M x r] as an activation tile, the right factor as a
+// the left factor la [M x r] (row stride ld_la) as an activation tile, the right factor as a
 // weight tile (forward: lb = B [Ncols x r], rows = output columns; grad_x:
 // lb = A [r x Ncols], rows = the rank).  All 512 threads stage with 16-byte
 // loads where the rank allows it.
 template <bool kTransW>
-__device__ __forceinline__ void stage_lora(const uint16_t *la, const uint16_t *lb, int r, int j0, int64_t M,
+__device__ __forceinline__ void stage_lora(const uint16_t *la, int64_t ld_la, const uint16_t *lb, int r, int j0, int64_t M,
                                            int64_t Ncols, int64_t m0, int64_t c0, int tid, uint16_t *sa_dst,
                                            uint16_t *sb_dst) {
-  const bool vec = (r % 8) == 0;
+  const bool vec = (r % 8) == 0 && (ld_la % 8) == 0;
   for (int idx = tid; idx < QBM * 8; idx += 512) {  // 256 rows x 8 chunks
     const int row = idx >> 3, ch = idx & 7;
     const int64_t grow = m0 + row;
-    const u32x4 v = grow < M ? ld8(la + grow * r, j0 + 8 * ch, r, vec) : u32x4{0u, 0u, 0u, 0u};
+    const u32x4 v = grow < M ? ld8(la + grow * ld_la, j0 + 8 * ch, r, vec) : u32x4{0u, 0u, 0u, 0u};
     *(u32x4 *)&sa_dst[act_off(row, ch)] = v;
   }
   if (!kTransW) {
@@ -519,23 +519,45 @@ __device__ __forceinline__ void stage_lora(const uint16_t *la, const uint16_t *l
   }
 }
 
+__device__ __forceinline__ QgemmMember set_member(const QgemmSet &s, int i) {
+  return i == 0 ? s.m[0] : i == 1 ? s.m[1] : i == 2 ? s.m[2] : s.m[3];
+}
+
+// One launch covers a projection set (members sharing n_in; one member for a
+// single linear):
+//   forward: the grid's column tiles run over the members in order; tile y
+//     belongs to the last member whose tile0 <= y: out = its y, act = x, the
+//     weight is its W, la = columns [i r, i r + r) of u_set (row stride
+//     set.ld_la), lb = its B, r = the member rank.
+//   grad_x : every tile contracts over all members in order (the sum over the
+//     set), one pipeline run per member: act = its dy, the weight is its W;
+//     the adapter term uses la = v_set, lb = A_set and r = the set's total
+//     rank; out = grad_x.
 // kDrop (grad_x only): the adapter term is masked by the LoRA dropout words.
 template <bool kTransW, bool kDQ, bool kDrop>
-__global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act, int64_t M, int64_t Ncols,
-                                                int64_t Kc, QWeight w, const uint16_t *__restrict__ la,
-                                                const uint16_t *__restrict__ lb, int r, float scale,
-                                                uint16_t *__restrict__ out, Codebook cb,
+__global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const uint16_t *__restrict__ x,
+                                                const uint16_t *__restrict__ la, const uint16_t *__restrict__ lb,
+                                                int r, float scale, uint16_t *__restrict__ gx, Codebook cb,
                                                 const uint32_t *__restrict__ keep) {
   __shared__ __attribute__((aligned(16))) uint16_t sa[kActStages][QBM * 64];
   __shared__ __attribute__((aligned(16))) uint16_t sb[2][QBN * QLD];  // = 64 * TLD
   __shared__ float lut[16];
 
   const int tid = threadIdx.x;
-  const int64_t m0 = (int64_t)blockIdx.x * QBM, c0 = (int64_t)blockIdx.y * QBN;
-  const int64_t nk = (Kc + QBK - 1) / QBK;
-  // full: every row, column and contraction step of the tile is in range and
-  // activation rows are 16-byte aligned
-  const bool full = (m0 + QBM <= M) && (c0 + QBN <= Ncols) && (Kc % QBK == 0);
+  const int64_t m0 = (int64_t)blockIdx.x * QBM;
+  int mf = 0;  // forward: the member of this column tile
+  if (!kTransW)
+    for (int i = 1; i < set.count; ++i)
+      if ((int64_t)blockIdx.y >= set_member(set, i).tile0) mf = i;
+  const QgemmMember fm = set_member(set, mf);
+  const int64_t Ncols = kTransW ? set.m[0].w.n_in : fm.w.n_out;
+  const int64_t c0 = ((int64_t)blockIdx.y - (kTransW ? 0 : fm.tile0)) * QBN;
+  const uint16_t *la_t = kTransW ? la : la + (int64_t)mf * r;
+  const uint16_t *lb_t = kTransW ? lb : fm.lb;
+  uint16_t *out = kTransW ? gx : fm.out;
+  const int m_begin = kTransW ? 0 : mf, m_end = kTransW ? set.count : mf + 1;
+  // full (per member): every row, column and contraction step of the tile is
+  // in range and activation rows are 16-byte aligned
 
   // Level table for the producers' decode.
   if (tid < 16) lut[tid] = cb.v[tid];
@@ -556,7 +578,7 @@ __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
   for (int j0 = 0; j0 < r; j0 += QBK) {
-    stage_lora<kTransW>(la, lb, r, j0, M, Ncols, m0, c0, tid, sa[2], sb[1]);
+    stage_lora<kTransW>(la_t, set.ld_la, lb_t, r, j0, M, Ncols, m0, c0, tid, sa[2], sb[1]);
     __syncthreads();
     if (tid < 256) consumer_slices<kTransW>(sa[2], sb[1], wm, wn, lane, acc);
     __syncthreads();
@@ -592,24 +614,31 @@ __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act
 
   if (tid >= 256) {
     // ------------------------------------------------------------ producers
-    Producer<kTransW, kDQ> p;
-    p.act = act;
-    p.M = M;
-    p.Kc = Kc;
-    p.m0 = m0;
-    p.c0 = c0;
-    p.K = w.n_in;
-    p.N = w.n_out;
-    p.kblk_row = w.n_in / kBlock;
-    p.w = w;
-    p.mu = kDQ ? *w.mu : 0.f;
-    p.ptid = tid - 256;
-    p.act_vec = (Kc % 8) == 0;
-    p.init_addressing();
-    if (full)
-      producer_loop_full(p, nk, sb, lut);
-    else
-      producer_loop_partial(p, nk, sa, sb, lut);
+    for (int mi = m_begin; mi < m_end; ++mi) {
+      const QgemmMember mm = set_member(set, mi);
+      const int64_t Kc = kTransW ? mm.w.n_out : mm.w.n_in;
+      const int64_t nk = (Kc + QBK - 1) / QBK;
+      const bool full = (m0 + QBM <= M) && (c0 + QBN <= Ncols) && (Kc % QBK == 0);
+      if (mi > m_begin) wg_barrier();  // the previous member's pipeline has drained
+      Producer<kTransW, kDQ> p;
+      p.act = kTransW ? mm.act : x;
+      p.M = M;
+      p.Kc = Kc;
+      p.m0 = m0;
+      p.c0 = c0;
+      p.K = mm.w.n_in;
+      p.N = mm.w.n_out;
+      p.kblk_row = mm.w.n_in / kBlock;
+      p.w = mm.w;
+      p.mu = kDQ ? *mm.w.mu : 0.f;
+      p.ptid = tid - 256;
+      p.act_vec = (Kc % 8) == 0;
+      p.init_addressing();
+      if (full)
+        producer_loop_full(p, nk, sb, lut);
+      else
+        producer_loop_partial(p, nk, sa, sb, lut);
+    }
     return;
   }
 
@@ -617,6 +646,13 @@ __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act
   // full tiles: stages 0, 1 and 2 of the activation ring
   const int cw = __builtin_amdgcn_readfirstlane(wave);
   const int64_t dma_row0 = m0 + 64 * cw;
+  for (int mi = m_begin; mi < m_end; ++mi) {
+  const QgemmMember mm = set_member(set, mi);
+  const uint16_t *act = kTransW ? mm.act : x;
+  const int64_t Kc = kTransW ? mm.w.n_out : mm.w.n_in;
+  const int64_t nk = (Kc + QBK - 1) / QBK;
+  const bool full = (m0 + QBM <= M) && (c0 + QBN <= Ncols) && (Kc % QBK == 0);
+  if (mi > m_begin) wg_barrier();  // every wave is done with the previous member's LDS stages
   const uint32_t dma_lane_off[2] = {dma_lane_offset(lane, Kc, 0), dma_lane_offset(lane, Kc, 1)};
   if (full) {
     dma_act(act, Kc, dma_row0, 0, dma_lane_off, sa[0] + 64 * cw * 64);
@@ -682,9 +718,11 @@ __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act
       __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
     wg_barrier();
   }
-  // No LDS-DMA may still be writing when the workgroup's LDS is released; the
-  // wait names the lane offsets so that their registers stay untouched until then.
+  // No LDS-DMA may still be writing when the next member's stages start or the
+  // workgroup's LDS is released; the wait names the lane offsets so that their
+  // registers stay untouched until then.
   asm volatile("s_waitcnt vmcnt(0)" ::"v"(dma_lane_off[0]), "v"(dma_lane_off[1]) : "memory");
+  }  // members
 
   // Epilogue through LDS: the tile is rounded to bf16 into [256][136] (the
   // activation ring's storage), then written out as 16-byte row chunks.  The
@@ -720,27 +758,58 @@ __global__ __launch_bounds__(512) void qgemm_ws(const uint16_t *__restrict__ act
 
 }  // namespace
 
+hipError_t launch_qgemm_set(bool trans_w, const QgemmSet &set, int64_t M, const uint16_t *x, const uint16_t *la,
+                            const uint16_t *lb, int r, float scale, uint16_t *gx, const Codebook &cb, hipStream_t st,
+                            const uint32_t *keep) {
+  if (set.count < 1 || set.count > kMaxSetMembers) return hipErrorInvalidValue;
+  QgemmSet s = set;
+  int64_t ytiles = 0;
+  if (!trans_w) {
+    for (int i = 0; i < s.count; ++i) {
+      s.m[i].tile0 = ytiles;
+      ytiles += (s.m[i].w.n_out + QBN - 1) / QBN;
+    }
+  } else {
+    ytiles = (s.m[0].w.n_in + QBN - 1) / QBN;
+  }
+  for (int i = s.count; i < kMaxSetMembers; ++i) s.m[i] = s.m[0];
+  const dim3 g((unsigned)((M + QBM - 1) / QBM), (unsigned)ytiles);
+  const bool dq = s.m[0].w.dq;
+  if (!trans_w) {  // the forward never takes a dropout mask
+    if (dq)
+      qgemm_ws<false, true, false><<<g, 512, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, nullptr);
+    else
+      qgemm_ws<false, false, false><<<g, 512, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, nullptr);
+  } else if (keep) {
+    if (dq)
+      qgemm_ws<true, true, true><<<g, 512, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, keep);
+    else
+      qgemm_ws<true, false, true><<<g, 512, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, keep);
+  } else {
+    if (dq)
+      qgemm_ws<true, true, false><<<g, 512, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, nullptr);
+    else
+      qgemm_ws<true, false, false><<<g, 512, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, nullptr);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_qgemm(bool trans_w, const uint16_t *act, int64_t M, int64_t Ncols, int64_t Kc, const QWeight &w,
                         const uint16_t *la, const uint16_t *lb, int r, float scale, uint16_t *out,
                         const Codebook &cb, hipStream_t st, const uint32_t *keep) {
-  dim3 g((unsigned)((M + QBM - 1) / QBM), (unsigned)((Ncols + QBN - 1) / QBN));
-  if (!trans_w) {  // the forward never takes a dropout mask
-    if (w.dq)
-      qgemm_ws<false, true, false><<<g, 512, 0, st>>>(act, M, Ncols, Kc, w, la, lb, r, scale, out, cb, nullptr);
-    else
-      qgemm_ws<false, false, false><<<g, 512, 0, st>>>(act, M, Ncols, Kc, w, la, lb, r, scale, out, cb, nullptr);
-  } else if (keep) {
-    if (w.dq)
-      qgemm_ws<true, true, true><<<g, 512, 0, st>>>(act, M, Ncols, Kc, w, la, lb, r, scale, out, cb, keep);
-    else
-      qgemm_ws<true, false, true><<<g, 512, 0, st>>>(act, M, Ncols, Kc, w, la, lb, r, scale, out, cb, keep);
-  } else {
-    if (w.dq)
-      qgemm_ws<true, true, false><<<g, 512, 0, st>>>(act, M, Ncols, Kc, w, la, lb, r, scale, out, cb, nullptr);
-    else
-      qgemm_ws<true, false, false><<<g, 512, 0, st>>>(act, M, Ncols, Kc, w, la, lb, r, scale, out, cb, nullptr);
+  (void)Ncols;
+  (void)Kc;
+  QgemmSet s{};
+  s.count = 1;
+  s.ld_la = r;
+  s.m[0].w = w;
+  if (trans_w) {
+    s.m[0].act = act;
+    return launch_qgemm_set(true, s, M, nullptr, la, lb, r, scale, out, cb, st, keep);
   }
-  return hipGetLastError();
+  s.m[0].lb = lb;
+  s.m[0].out = out;
+  return launch_qgemm_set(false, s, M, act, la, nullptr, r, scale, nullptr, cb, st, nullptr);
 }
 
 }  // namespace qlora

@@ -51,6 +51,11 @@ _SIGNATURES = {
     "qlora_linear_fwd": (ctypes.c_int, [_P, _I64, _P, _P, _P, ctypes.c_int, ctypes.c_float, _P, _P, _P, _SZ, _P]),
     "qlora_linear_bwd": (ctypes.c_int, [_P, _P, _I64, _P, _P, _P, ctypes.c_int, ctypes.c_float, _P, _P, _P, _P,
                                         _P, _SZ, _P]),
+    "qlora_linear_set_workspace_bytes": (_SZ, [_I64, ctypes.c_int, _P, _I64, ctypes.c_int]),
+    "qlora_linear_set_fwd": (ctypes.c_int, [_P, _I64, ctypes.c_int, _P, _P, _P, ctypes.c_int, ctypes.c_float, _P, _P,
+                                            _P, _SZ, _P]),
+    "qlora_linear_set_bwd": (ctypes.c_int, [_P, _P, _I64, ctypes.c_int, _P, _P, _P, ctypes.c_int, ctypes.c_float,
+                                            _P, _P, _P, _P, _P, _SZ, _P]),
     "qlora_linear_dropout_workspace_bytes": (_SZ, [_I64, _I64, _I64, ctypes.c_int]),
     "qlora_linear_fwd_dropout": (ctypes.c_int, [_P, _I64, _P, _P, _P, ctypes.c_int, ctypes.c_float, ctypes.c_double,
                                                 ctypes.c_uint64, _P, _P, _P, _SZ, _P]),
@@ -349,3 +354,57 @@ def dropout_mask(x, p: float, seed: int, stream=None):
     _check(lib().qlora_dropout_mask(_ptr(x), T, K, float(p), int(seed), _ptr(keep), _ptr(xd), _stream(stream)),
            "qlora_dropout_mask")
     return keep, xd
+
+
+# ------------------------------------------------------------ projection sets
+def _ptrs(ts):
+    return (ctypes.c_void_p * len(ts))(*[_ptr(t) for t in ts])
+
+
+def linear_set_workspace_bytes(tokens: int, n_outs, n_in: int, r: int) -> int:
+    arr = (ctypes.c_int64 * len(n_outs))(*n_outs)
+    return int(lib().qlora_linear_set_workspace_bytes(tokens, len(n_outs), arr, n_in, r))
+
+
+def linear_set_workspace(tokens: int, n_outs, n_in: int, r: int, device="cuda"):
+    torch = _torch()
+    return torch.empty(max(linear_set_workspace_bytes(tokens, n_outs, n_in, r), 1), dtype=torch.uint8, device=device)
+
+
+def linear_set_fwd(x, qs, A_set, Bs, scale: float, ys=None, u_out=None, save_u=True, workspace=None, stream=None):
+    """Projection set forward: y_i = x W_hat_i^T + scale (x A_i^T) B_i^T for every member, with
+    A_set [count r x n_in] the members' A matrices back to back.  Returns (ys, u_set or None)."""
+    torch = _torch()
+    T, count = x.shape[0], len(qs)
+    r = A_set.shape[0] // count
+    ys = ys if ys is not None else [torch.empty((T, q.n_out), dtype=torch.bfloat16, device=x.device) for q in qs]
+    if save_u and u_out is None:
+        u_out = torch.empty((T, count * r), dtype=torch.bfloat16, device=x.device)
+    ws = workspace if workspace is not None else linear_set_workspace(T, [q.n_out for q in qs], qs[0].n_in, r,
+                                                                      x.device)
+    st = (NF4WeightStruct * count)(*[q.struct() for q in qs])
+    _check(lib().qlora_linear_set_fwd(_ptr(x), T, count, st, _ptr(A_set), _ptrs(Bs), r, float(scale), _ptrs(ys),
+                                      _ptr(u_out), _ptr(ws), ws.numel(), _stream(stream)), "qlora_linear_set_fwd")
+    return ys, u_out
+
+
+def linear_set_bwd(dys, x, qs, A_set, Bs, scale: float, u=None, need_grad_x=True, grad_x=None, grad_A_set=None,
+                   grad_Bs=None, workspace=None, stream=None):
+    """Projection set backward: (grad_x summed over the members or None, grad_A_set, [grad_B_i])."""
+    torch = _torch()
+    T, count, dev = x.shape[0], len(qs), x.device
+    r = A_set.shape[0] // count
+    if need_grad_x and grad_x is None:
+        grad_x = torch.empty((T, qs[0].n_in), dtype=torch.bfloat16, device=dev)
+    if not need_grad_x:
+        grad_x = None
+    grad_A_set = grad_A_set if grad_A_set is not None else torch.empty((count * r, qs[0].n_in), dtype=torch.float32,
+                                                                       device=dev)
+    grad_Bs = grad_Bs if grad_Bs is not None else [torch.empty((q.n_out, r), dtype=torch.float32, device=dev)
+                                                   for q in qs]
+    ws = workspace if workspace is not None else linear_set_workspace(T, [q.n_out for q in qs], qs[0].n_in, r, dev)
+    st = (NF4WeightStruct * count)(*[q.struct() for q in qs])
+    _check(lib().qlora_linear_set_bwd(_ptrs(dys), _ptr(x), T, count, st, _ptr(A_set), _ptrs(Bs), r, float(scale),
+                                      _ptr(u), _ptr(grad_x), _ptr(grad_A_set), _ptrs(grad_Bs), _ptr(ws), ws.numel(),
+                                      _stream(stream)), "qlora_linear_set_bwd")
+    return grad_x, grad_A_set, grad_Bs

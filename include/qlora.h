@@ -171,6 +171,40 @@ qlora_status qlora_linear_bwd(const uint16_t *dy, const uint16_t *x, int64_t T,
                               float *grad_A, float *grad_B, void *ws, size_t ws_bytes,
                               void *stream);
 
+/* ---- projection sets --------------------------------------------------------- */
+
+/* The adapters go on every linear layer, not only on query and value ("qlora"
+ * entry, section "como funciona"; "LoRA vs. QLoRA vs. Full Fine-Tuning",
+ * section "Um LoRA Rank Mais Alto Sempre Melhora a Qualidade?"), so linears
+ * that read the same input -- the attention projections q, k, v, or the
+ * MLP's gate and up -- each carry an adapter.  A set runs them together:
+ *   u_set = x A_set^T                      one adapter product for all members
+ *   y_i   = bf16( x W_hat_i^T + scale * u_i B_i^T )     one fused GEMM launch
+ *   grad_x = bf16( sum_i dy_i W_hat_i + scale * v_set A_set ),  v_i = dy_i B_i
+ *                                          one GEMM over every member's rows
+ *   grad_A_set = scale * v_set^T x,        grad_B_i = scale * dy_i^T u_i
+ * count = 1..4 members; q[i] is member i's weight [n_out_i x n_in] (the same
+ * n_in and the same flags for all); A_set [count r x n_in] holds the members'
+ * A matrices back to back (member i: rows i r .. i r + r - 1), and u_set,
+ * v_set [T x count r] the members' u / v side by side (member i: columns
+ * i r ..).  B[i] [n_out_i x r], y[i] [T x n_out_i], dy[i] [T x n_out_i] and
+ * grad_B[i] [n_out_i x r] are arrays of count device pointers; grad_x is the
+ * gradient of x summed over the members (NULL skips it).  T must be above 4:
+ * few-token calls go per linear (QLORA_ERR_SHAPE).  No dropout here: each
+ * adapter draws its own mask, so sets with dropout go per linear.           */
+size_t qlora_linear_set_workspace_bytes(int64_t T, int count, const int64_t *n_out, int64_t n_in, int r);
+
+qlora_status qlora_linear_set_fwd(const uint16_t *x, int64_t T, int count, const qlora_nf4_weight *q,
+                                  const uint16_t *A_set, const uint16_t *const *B, int r, float scale,
+                                  uint16_t *const *y, uint16_t *u_out, void *ws, size_t ws_bytes,
+                                  void *stream);
+
+qlora_status qlora_linear_set_bwd(const uint16_t *const *dy, const uint16_t *x, int64_t T, int count,
+                                  const qlora_nf4_weight *q, const uint16_t *A_set,
+                                  const uint16_t *const *B, int r, float scale, const uint16_t *u,
+                                  uint16_t *grad_x, float *grad_A_set, float *const *grad_B, void *ws,
+                                  size_t ws_bytes, void *stream);
+
 /* ---- LoRA dropout -------------------------------------------------------- */
 
 /* The recipe sets a dropout probability p on the adapters ("Tutorial

@@ -171,3 +171,32 @@ def test_dropout_argument_validation_before_any_launch():
     assert lib.qlora_dropout_mask(0x50000, 0, 64, 0.05, 1, 0x60000, 0x70000, None) == 2
     assert lib.qlora_dropout_mask(0x50000, 16, 64, 0.05, 1, None, 0x70000, None) == 1
     assert lib.qlora_dropout_mask(0x50008, 16, 64, 0.05, 1, 0x60000, 0x70000, None) == 3
+
+
+def test_projection_set_validation_before_any_launch():
+    lib = qlora.lib()
+    n_outs = (ctypes.c_int64 * 3)(512, 256, 256)
+    assert lib.qlora_linear_set_workspace_bytes(16, 3, n_outs, 256, 8) > 0
+    assert lib.qlora_linear_set_workspace_bytes(4, 3, n_outs, 256, 8) == 0  # few-token: per linear
+    assert lib.qlora_linear_set_workspace_bytes(16, 5, n_outs, 256, 8) == 0
+    assert lib.qlora_linear_set_workspace_bytes(16, 3, n_outs, 100, 8) == 0
+    ws = lib.qlora_linear_set_workspace_bytes(16, 3, n_outs, 256, 8)
+    ws_big = lib.qlora_linear_set_workspace_bytes(2048, 3, n_outs, 256, 8)
+    assert ws_big > ws
+    qs = (qlora.NF4WeightStruct * 3)(_fake_weight(512, 256), _fake_weight(256, 256), _fake_weight(256, 256))
+    ptrs = lambda *v: (ctypes.c_void_p * len(v))(*v)
+    B, Y = ptrs(0x70000, 0x71000, 0x72000), ptrs(0x80000, 0x81000, 0x82000)
+    fwd = lambda T=16, count=3, q=qs, b=B, y=Y, wsb=ws, a=0x60000: lib.qlora_linear_set_fwd(
+        0x50000, T, count, q, a, b, 8, 2.0, y, None, 0x90000, wsb, None)
+    assert fwd(wsb=ws - 1) == 4
+    assert fwd(T=4) == 2 and fwd(count=0) == 2 and fwd(count=5) == 2
+    assert fwd(a=0x60008) == 3
+    assert fwd(b=ptrs(0x70000, None, 0x72000)) == 1
+    odd = (qlora.NF4WeightStruct * 3)(_fake_weight(512, 256), _fake_weight(256, 320), _fake_weight(256, 256))
+    assert fwd(q=odd) == 2  # members must share n_in
+    mixed = (qlora.NF4WeightStruct * 3)(_fake_weight(512, 256), _fake_weight(256, 256), _fake_weight(256, 256))
+    mixed[1].flags = qlora.QLORA_NF4_FP32_CONSTANTS
+    assert fwd(q=mixed) == 8  # and the storage form
+    G = ptrs(0xA0000, 0xA1000, 0xA2000)
+    assert lib.qlora_linear_set_bwd(ptrs(0xB0000, 0xB1000, 0xB2000), 0x50000, 16, 3, qs, 0x60000, B, 8, 2.0,
+                                    None, None, 0xC0000, G, 0x90000, ws - 1, None) == 4

@@ -1,0 +1,100 @@
+"""GPU parity of projection sets (linears sharing their input, run as one fused GEMM per
+direction): every member's y, the summed grad_x, grad_A_set and every grad_B against the fp64
+oracle within the normwise bar; a one-member set bit-identical to the single-linear calls."""
+
+import numpy as np
+import pytest
+
+import oracle
+from bit_quantized_finetuning_quant_amd import qlora, workloads
+from helpers import NORMWISE_TOL, announce, bf16_to_f64, dev_bf16, dev_f32, host, host_bits, normwise_rel
+
+pytestmark = pytest.mark.gpu
+
+
+def _members(n_outs, n_in, T, r, seed):
+    cases = [workloads.custom_case(n, n_in, T, r, 16.0, seed=seed + 17 * i) for i, n in enumerate(n_outs)]
+    x = cases[0].x
+    for c in cases:
+        c.x = x
+    return cases
+
+
+def _run_set(cases, need_u=True, double_quant=True):
+    torch = __import__("torch")
+    s = cases[0].scale
+    qs = [qlora.quantize(dev_f32(c.w), double_quant=double_quant) for c in cases]
+    x = dev_bf16(cases[0].x)
+    a_set = dev_bf16(np.concatenate([c.a for c in cases], axis=0))
+    bs = [dev_bf16(c.b) for c in cases]
+    dys = [dev_bf16(c.dy) for c in cases]
+    ys, u = qlora.linear_set_fwd(x, qs, a_set, bs, s)
+    gx, ga, gbs = qlora.linear_set_bwd(dys, x, qs, a_set, bs, s, u=u if need_u else None)
+    torch.cuda.synchronize()
+    return qs, ys, u, gx, ga, gbs
+
+
+def _check(cases, need_u=True, double_quant=True):
+    s = cases[0].scale
+    qs, ys, u, gx, ga, gbs = _run_set(cases, need_u, double_quant)
+    r = cases[0].a.shape[0]
+    gx_ref = 0.0
+    errs = {}
+    for i, (c, q) in enumerate(zip(cases, qs)):
+        ref = oracle.quantize(c.w, c.n_out, c.n_in, double_quant=double_quant)
+        wh = oracle.dequantize(ref)
+        assert np.array_equal(host_bits(qlora.dequantize(q)), wh)
+        y_ref, u_ref = oracle.forward(c.x, wh, c.a, c.b, s)
+        g = oracle.backward(c.dy, c.x, wh, c.a, c.b, s)
+        gx_ref = gx_ref + g[0]
+        errs[f"y{i}"] = normwise_rel(bf16_to_f64(host_bits(ys[i])), y_ref)
+        errs[f"u{i}"] = normwise_rel(bf16_to_f64(host_bits(u))[:, i * r:(i + 1) * r], u_ref)
+        errs[f"grad_A{i}"] = normwise_rel(host(ga)[i * r:(i + 1) * r], g[1])
+        errs[f"grad_B{i}"] = normwise_rel(host(gbs[i]), g[2])
+    errs["grad_x"] = normwise_rel(bf16_to_f64(host_bits(gx)), gx_ref)
+    for k, e in errs.items():
+        assert e <= NORMWISE_TOL, (k, e)
+    return errs
+
+
+@pytest.mark.parametrize("n_outs,n_in,T,r", [((320, 192, 256), 320, 300, 24), ((77, 130, 64), 192, 259, 5),
+                                             ((1000, 640), 640, 513, 64), ((128, 128, 128, 128), 128, 17, 16),
+                                             ((64, 128), 128, 40, 4)])
+def test_sets_against_the_oracle(n_outs, n_in, T, r):
+    announce(f"set n_outs={n_outs} n_in={n_in} T={T} r={r}")
+    cases = _members(n_outs, n_in, T, r, seed=T + r)
+    _check(cases)
+    _check(cases, need_u=False)
+
+
+def test_set_with_fp32_constants():
+    announce("set fp32 constants n_outs=(256, 320) n_in=256 T=130 r=8")
+    _check(_members((256, 320), 256, 130, 8, seed=5), double_quant=False)
+
+
+def test_one_member_set_equals_the_single_linear_calls():
+    torch = __import__("torch")
+    announce("set of one member vs single linear, 300x320 T=200 r=24")
+    (c,) = _members((300,), 320, 200, 24, seed=11)
+    q = qlora.quantize(dev_f32(c.w))
+    x, a, b, dy = dev_bf16(c.x), dev_bf16(c.a), dev_bf16(c.b), dev_bf16(c.dy)
+    y0, u0 = qlora.linear_fwd(x, q, a, b, c.scale)
+    g0 = qlora.linear_bwd(dy, x, q, a, b, c.scale, u=u0)
+    (y1,), u1 = qlora.linear_set_fwd(x, [q], a, [b], c.scale)
+    g1x, g1a, (g1b,) = qlora.linear_set_bwd([dy], x, [q], a, [b], c.scale, u=u1)
+    torch.cuda.synchronize()
+    for t0, t1 in zip((y0, u0) + tuple(g0), (y1, u1, g1x, g1a, g1b)):
+        assert np.array_equal(host(t0), host(t1))
+
+
+def test_7b_attention_projections_T2048():
+    """q, k, v of LLaMA-7B (3 x 4096 x 4096, r = 64, 2048 tokens) as one set, in full."""
+    announce("set 7b q/k/v T=2048 full")
+    errs = _check(_members((4096, 4096, 4096), 4096, 2048, 64, seed=2))
+    print("7b q/k/v set normwise errors:", errs)
+
+
+def test_7b_gate_up_T512():
+    announce("set 7b gate/up T=512 full")
+    errs = _check(_members((11008, 11008), 4096, 512, 64, seed=3))
+    print("7b gate/up set normwise errors:", errs)
