@@ -218,6 +218,55 @@ class LayerSet:
                           workspace=self.ws)
 
 
+class FusedLayer:
+    """fwd + bwd through a decoder layer's linears as projection sets: members of a group share
+    their input (q/k/v; o; gate/up; down), one fused GEMM per group and direction."""
+
+    GROUPS = (("q", "k", "v"), ("o",), ("gate", "up"), ("down",))
+
+    def __init__(self, torch, qlora, shapes, tokens, weight, pad_rows=False, seed=0):
+        g = torch.Generator(device="cuda")
+        g.manual_seed(seed)
+        by_name = {name: (n, k) for name, n, k in shapes}
+        r = 64
+        bf, f32 = torch.bfloat16, torch.float32
+        self.groups, self.flops = [], 0
+        ws_bytes = 0
+        for names in self.GROUPS:
+            k = by_name[names[0]][1]
+            qs = []
+            for name in names:
+                n = by_name[name][0]
+                w = torch.empty((n, k), dtype=torch.float32, device="cuda")
+                weight(g, n, k, w)
+                qs.append(qlora.quantize(w))
+                del w
+                self.flops += linear_flops(tokens, n, k, r)
+            x = _bf16_normal(torch, g, (tokens, k), 1.0)
+            if pad_rows:
+                x.view(tokens // 512, 512, k)[:, 512 - 26:] = 0
+            a_set = _bf16_normal(torch, g, (len(names) * r, k), 0.01)
+            bs = [_bf16_normal(torch, g, (q.n_out, r), 0.01) for q in qs]
+            dys = [_bf16_normal(torch, g, (tokens, q.n_out), 1.0) for q in qs]
+            o = dict(ys=[torch.empty((tokens, q.n_out), dtype=bf, device="cuda") for q in qs],
+                     u=torch.empty((tokens, len(names) * r), dtype=bf, device="cuda"),
+                     gx=torch.empty((tokens, k), dtype=bf, device="cuda"),
+                     ga=torch.empty((len(names) * r, k), dtype=f32, device="cuda"),
+                     gbs=[torch.empty((q.n_out, r), dtype=f32, device="cuda") for q in qs])
+            self.groups.append((qs, x, a_set, bs, dys, o))
+            ws_bytes = max(ws_bytes, qlora.linear_set_workspace_bytes(tokens, [q.n_out for q in qs], k, r))
+        self.ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+        self.qlora = qlora
+        torch.cuda.synchronize()
+
+    def __call__(self):
+        ql = self.qlora
+        for qs, x, a_set, bs, dys, o in self.groups:
+            ql.linear_set_fwd(x, qs, a_set, bs, 0.25, ys=o["ys"], u_out=o["u"], workspace=self.ws)
+            ql.linear_set_bwd(dys, x, qs, a_set, bs, 0.25, u=o["u"], grad_x=o["gx"], grad_A_set=o["ga"],
+                              grad_Bs=o["gbs"], workspace=self.ws)
+
+
 def extra_layers(torch, qlora, workloads, steps):
     out = {}
     normal = lambda g, n, k, w: w.normal_(0.0, 0.02, generator=g)
@@ -234,6 +283,17 @@ def extra_layers(torch, qlora, workloads, steps):
                     "ms_per_layer_step": t / n * 1e3, "tokens": tokens, "r": 64, "alpha": 16,
                     "linears": [list(s) for s in shapes], "flops_per_layer_step": ls.flops, "steps": n}
         del ls
+        torch.cuda.empty_cache()
+        log(f"extra: {tag} as projection sets")
+        fl = FusedLayer(torch, qlora, shapes, tokens, weight, pad_rows=pad, seed=len(tag) + 100)
+        for _ in range(2):
+            fl()
+        t, _ = time_region(torch, fl, n)
+        out[tag + "_sets"] = {"TFLOP/s": fl.flops * n / t / 1e12,
+                              "frac_mfma": fl.flops * n / t / 1e12 / PEAK_BF16_TFLOPS,
+                              "ms_per_layer_step": t / n * 1e3, "groups": [list(g) for g in FusedLayer.GROUPS],
+                              "flops_per_layer_step": fl.flops, "steps": n}
+        del fl
         torch.cuda.empty_cache()
     return out
 
@@ -498,7 +558,7 @@ def main():
                          "path, rotating over more than 1 GB of distinct packed weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--extra-only", choices=["adamw", "dropout"], default=None,
+    ap.add_argument("--extra-only", choices=["adamw", "dropout", "layers"], default=None,
                     help="run only this extra measurement and print its JSON (for profiling it alone)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before the steps, copy 256 MiB device to device three times (untimed): the "
@@ -525,6 +585,9 @@ def main():
         print(json.dumps(extra_adamw(torch, qlora, workloads, args.steps)), flush=True)
         return
     dev_bf16, dev_f32 = dev_helpers(torch)
+    if args.extra_only == "layers":
+        print(json.dumps(extra_layers(torch, qlora, workloads, args.steps)), flush=True)
+        return
     if args.extra_only == "dropout":
         case = workloads.attn7b_case(2048)
         print(json.dumps(extra_dropout(torch, qlora, case, dev_bf16, dev_f32, args.steps)), flush=True)
