@@ -373,6 +373,19 @@ def extra_measurements(torch, qlora, steps):
     out["dequant_bulk"] = {"GB/s": bytes_deq / t / 1e9, "frac_hbm": bytes_deq / t / 1e9 / PEAK_HBM_GBS,
                            "bytes_per_param": (packed + 2 * N * K) / (N * K),
                            "shape": [N, K], "weights_rotated": nw}
+    # the same weights eight to a launch (qlora_dequantize_many)
+    outs8 = [torch.empty((N, K), dtype=torch.bfloat16, device="cuda") for _ in range(8)]
+
+    def deq_many():
+        for i in range(0, nw - nw % 8, 8):
+            qlora.dequantize_many(weights[i:i + 8], outs=outs8)
+
+    deq_many()
+    t, _ = time_region(torch, deq_many, reps)
+    bytes_many = reps * (nw - nw % 8) * (packed + 2 * N * K)
+    out["dequant_bulk_8_per_launch"] = {"GB/s": bytes_many / t / 1e9, "frac_hbm": bytes_many / t / 1e9 / PEAK_HBM_GBS,
+                                        "shape": [N, K], "weights_rotated": nw - nw % 8}
+    del outs8
     # few-token path, T = 1, rotating weights
     rng = np.random.default_rng(2)
     bits = lambda a: torch.from_numpy(a.astype(np.float32)).to(torch.bfloat16).cuda()
@@ -558,7 +571,7 @@ def main():
                          "path, rotating over more than 1 GB of distinct packed weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--extra-only", choices=["adamw", "dropout", "layers"], default=None,
+    ap.add_argument("--extra-only", choices=["adamw", "dropout", "layers", "bulk"], default=None,
                     help="run only this extra measurement and print its JSON (for profiling it alone)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before the steps, copy 256 MiB device to device three times (untimed): the "
@@ -585,6 +598,11 @@ def main():
         print(json.dumps(extra_adamw(torch, qlora, workloads, args.steps)), flush=True)
         return
     dev_bf16, dev_f32 = dev_helpers(torch)
+    if args.extra_only == "bulk":
+        out = {"bulk_65b": extra_bulk_65b(torch, qlora, workloads)}
+        out.update(extra_measurements(torch, qlora, args.steps))
+        print(json.dumps(out), flush=True)
+        return
     if args.extra_only == "layers":
         print(json.dumps(extra_layers(torch, qlora, workloads, args.steps)), flush=True)
         return

@@ -247,6 +247,23 @@ qlora_status qlora_dequantize(const qlora_nf4_weight *q, uint16_t *w_bf16, void 
   return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP;
 }
 
+qlora_status qlora_dequantize_many(const qlora_nf4_weight *q, int count, uint16_t *const *w_bf16, void *stream) {
+  if (!q || !w_bf16) return QLORA_ERR_NULL;
+  if (count < 1 || count > kMaxDequantSet) return QLORA_ERR_SHAPE;
+  DequantSet set{};
+  set.count = count;
+  for (int i = 0; i < count; ++i) {
+    const qlora_status s = check_weight(&q[i]);
+    if (s != QLORA_OK) return s;
+    if (!w_bf16[i]) return QLORA_ERR_NULL;
+    if (!aligned16(w_bf16[i])) return QLORA_ERR_ALIGN;
+    set.w[i] = qweight(&q[i]);
+    set.out[i] = w_bf16[i];
+  }
+  hipError_t e = launch_dequantize_set(set, tables().cb, (hipStream_t)stream);
+  return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP;
+}
+
 qlora_status qlora_linear_fwd(const uint16_t *x, int64_t T, const qlora_nf4_weight *q, const uint16_t *A,
                               const uint16_t *B, int r, float scale, uint16_t *y, uint16_t *u_out, void *ws,
                               size_t ws_bytes, void *stream) {

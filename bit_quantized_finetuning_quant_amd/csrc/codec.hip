@@ -12,6 +12,8 @@
 //   double_quantize   one workgroup per 256-block group: fp32 scale, e4m3 codes
 //   dequantize_bf16   streaming decode to bf16 (HBM bound)
 
+#include <algorithm>
+
 #include "common.hpp"
 #include "launch.hpp"
 
@@ -252,46 +254,86 @@ __global__ __launch_bounds__(256) void double_quantize(const float *__restrict__
   if (b < nblocks) q_out[b] = (s2 > 0.f) ? (uint8_t)e4m3_rne((double)d / (double)s2) : (uint8_t)0;
 }
 
-// One thread decodes 8 consecutive elements (4 code bytes) per pass.  kDQ:
-// FP8 constants with group scales and a mean; otherwise s2 holds the fp32
-// block constants themselves.
+// Streaming decode of one or several weights in one launch.  Each weight's
+// 8-element chunks are grouped in passes of 1024; a workgroup takes one pass at
+// a time (grid-stride over the passes of all the weights, a pass never spans
+// two weights).  Load j of every lane reads the 4 code bytes of chunk
+// base + 256 j + lane, so each load and each 16-byte store instruction of a
+// wave covers one contiguous run (256 B of codes, 1 KiB of output); all four
+// chunks' codes and constants are loaded before any is decoded.  The output is
+// written with non-temporal stores (it is not read back here).  Measured: 6.9
+// TB/s for a 22016 x 8192 weight against 5.0 TB/s for one chunk per thread with
+// 4-byte loads and ordinary stores.  kDQ is the storage form of every weight
+// of the launch (a runtime switch costs a quarter of the throughput); without
+// double quantization s2 holds the fp32 block constants (no mean, no FP8).
+constexpr int kDeqPass = 1024;  // chunks per pass
+
 template <bool kDQ>
-__global__ __launch_bounds__(256) void dequantize_bf16(const uint8_t *__restrict__ codes,
-                                                       const uint8_t *__restrict__ fp8,
-                                                       const float *__restrict__ s2,
-                                                       const float *__restrict__ mu_p, int64_t numel,
-                                                       uint16_t *__restrict__ out, Codebook cb) {
+__global__ __launch_bounds__(256) void dequantize_bf16(DequantSet set, int64_t passes, Codebook cb) {
+  typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
   __shared__ float lut[16];
   if (threadIdx.x < 16) lut[threadIdx.x] = cb.v[threadIdx.x];
   __syncthreads();
-  const float mu = kDQ ? *mu_p : 0.f;
-  const int64_t nchunks = (numel + 7) >> 3;
-  const int64_t codes_bytes = (numel + 1) >> 1;
-  for (int64_t c = (int64_t)blockIdx.x * 256 + threadIdx.x; c < nchunks; c += (int64_t)gridDim.x * 256) {
-    const int64_t e0 = c << 3;
-    const bool full = e0 + 8 <= numel;
-    uint32_t packed;
-    if (full) {
-      packed = *(const uint32_t *)(codes + (c << 2));
-    } else {
-      packed = 0x77777777u;
-      for (int i = 0; i < 4; ++i)
-        if ((c << 2) + i < codes_bytes) packed = (packed & ~(0xFFu << (8 * i))) | ((uint32_t)codes[(c << 2) + i] << (8 * i));
+  // grid-stride over the passes (the workgroups in flight cover one contiguous
+  // window of memory); passes only increase, so the weight's pointers and mean
+  // are reloaded only when a workgroup crosses into the next weight
+  QWeight w = set.w[0];
+  uint16_t *out = set.out[0];
+  int64_t pass0 = 0, next = -1, numel = 0, nchunks = 0, codes_bytes = 0;
+  float mu = 0.f;
+  for (int64_t ps = blockIdx.x; ps < passes; ps += gridDim.x) {
+    if (ps >= next) {
+      int mi = 0;
+      for (int i = 1; i < set.count; ++i)
+        if (ps >= set.pass0[i]) mi = i;
+      w = set.w[mi];
+      out = set.out[mi];
+      pass0 = set.pass0[mi];
+      next = mi + 1 < set.count ? set.pass0[mi + 1] : passes;
+      numel = w.n_out * w.n_in;
+      nchunks = (numel + 7) >> 3;
+      codes_bytes = (numel + 1) >> 1;
+      mu = kDQ ? *w.mu : 0.f;
     }
-    const int64_t blk = e0 >> 6;
-    const float ch = kDQ ? decode_constant(fp8[blk], s2[blk >> 8], mu) : s2[blk];
-    u32x4 o;
+    const int64_t base = (ps - pass0) * kDeqPass;
+    uint32_t pk[4];
+    float ch[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float lo = decode_product(lut[(packed >> (8 * i)) & 15u], ch);
-      const float hi = decode_product(lut[(packed >> (8 * i + 4)) & 15u], ch);
-      o[i] = pack_bf16x2(lo, hi);
+    for (int j = 0; j < 4; ++j) {
+      const int64_t c = base + j * 256 + threadIdx.x;
+      uint32_t packed = 0x77777777u;
+      int64_t blk = 0;
+      if (c < nchunks) {
+        if ((c << 3) + 8 <= numel) {
+          packed = *(const uint32_t *)(w.codes + (c << 2));
+        } else {
+          for (int i = 0; i < 4; ++i)
+            if ((c << 2) + i < codes_bytes)
+              packed = (packed & ~(0xFFu << (8 * i))) | ((uint32_t)w.codes[(c << 2) + i] << (8 * i));
+        }
+        blk = (c << 3) >> 6;
+      }
+      pk[j] = packed;
+      ch[j] = kDQ ? decode_constant(w.fp8[blk], w.s2[blk >> 8], mu) : w.s2[blk];
     }
-    if (full) {
-      *(u32x4 *)(out + e0) = o;
-    } else {
-      for (int i = 0; i < 8; ++i)
-        if (e0 + i < numel) out[e0 + i] = (uint16_t)(o[i >> 1] >> (16 * (i & 1)));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int64_t c = base + j * 256 + threadIdx.x;
+      if (c >= nchunks) continue;
+      const int64_t e0 = c << 3;
+      u32x4v o;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float lo = decode_product(lut[(pk[j] >> (8 * i)) & 15u], ch[j]);
+        const float hi = decode_product(lut[(pk[j] >> (8 * i + 4)) & 15u], ch[j]);
+        o[i] = pack_bf16x2(lo, hi);
+      }
+      if (e0 + 8 <= numel) {
+        __builtin_nontemporal_store(o, (u32x4v *)(out + e0));
+      } else {
+        for (int i = 0; i < 8; ++i)
+          if (e0 + i < numel) out[e0 + i] = (uint16_t)(o[i >> 1] >> (16 * (i & 1)));
+      }
     }
   }
 }
@@ -323,15 +365,47 @@ hipError_t launch_quantize(const void *w, bool bf16_src, bool dq, int64_t numel,
   return hipGetLastError();
 }
 
-hipError_t launch_dequantize(const QWeight &w, uint16_t *out, const Codebook &cb, hipStream_t st) {
-  const int64_t numel = w.n_out * w.n_in;
-  const int64_t nchunks = (numel + 7) / 8;
-  const int g = grid_for(nchunks, 256, 256 * 32);
-  if (w.dq)
-    dequantize_bf16<true><<<g, 256, 0, st>>>(w.codes, w.fp8, w.s2, w.mu, numel, out, cb);
+// One launch per storage form present in the set.
+static hipError_t launch_dequantize_form(const DequantSet &set_in, bool dq, const Codebook &cb, hipStream_t st) {
+  DequantSet set{};
+  for (int i = 0; i < set_in.count; ++i)
+    if (set_in.w[i].dq == dq) {
+      set.w[set.count] = set_in.w[i];
+      set.out[set.count] = set_in.out[i];
+      ++set.count;
+    }
+  if (set.count == 0) return hipSuccess;
+  int64_t passes = 0;
+  for (int i = 0; i < set.count; ++i) {
+    set.pass0[i] = passes;
+    const int64_t nchunks = (set.w[i].n_out * set.w[i].n_in + 7) / 8;
+    passes += (nchunks + kDeqPass - 1) / kDeqPass;
+  }
+  for (int i = set.count; i < kMaxDequantSet; ++i) {
+    set.w[i] = set.w[0];
+    set.out[i] = set.out[0];
+    set.pass0[i] = passes;
+  }
+  const int g = (int)std::min<int64_t>(passes, 8192);
+  if (dq)
+    dequantize_bf16<true><<<g, 256, 0, st>>>(set, passes, cb);
   else
-    dequantize_bf16<false><<<g, 256, 0, st>>>(w.codes, w.fp8, w.s2, w.mu, numel, out, cb);
+    dequantize_bf16<false><<<g, 256, 0, st>>>(set, passes, cb);
   return hipGetLastError();
+}
+
+hipError_t launch_dequantize_set(const DequantSet &set, const Codebook &cb, hipStream_t st) {
+  if (set.count < 1 || set.count > kMaxDequantSet) return hipErrorInvalidValue;
+  const hipError_t e = launch_dequantize_form(set, true, cb, st);
+  return e != hipSuccess ? e : launch_dequantize_form(set, false, cb, st);
+}
+
+hipError_t launch_dequantize(const QWeight &w, uint16_t *out, const Codebook &cb, hipStream_t st) {
+  DequantSet s{};
+  s.count = 1;
+  s.w[0] = w;
+  s.out[0] = out;
+  return launch_dequantize_set(s, cb, st);
 }
 
 }  // namespace qlora

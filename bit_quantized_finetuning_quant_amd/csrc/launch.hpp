@@ -35,6 +35,16 @@ hipError_t launch_quantize(const void *w, bool bf16_src, bool dq, int64_t numel,
 
 hipError_t launch_dequantize(const QWeight &w, uint16_t *out, const Codebook &cb, hipStream_t st);
 
+// Several weights decoded in one launch (codec.hip); pass0 is set by the launcher.
+constexpr int kMaxDequantSet = 8;
+struct DequantSet {
+  int count;
+  QWeight w[kMaxDequantSet];
+  uint16_t *out[kMaxDequantSet];
+  int64_t pass0[kMaxDequantSet];
+};
+hipError_t launch_dequantize_set(const DequantSet &set, const Codebook &cb, hipStream_t st);
+
 // Few-token path (gemv.hip): 1 <= T <= kGemvMaxT.  `part` is fp32 scratch of
 // gemv_part_floats(T, N, K, r) floats.  launch_gemv_fwd with y == nullptr only
 // computes u; launch_gemv_bwd with grad_x == nullptr skips the weight pass.

@@ -48,6 +48,7 @@ _SIGNATURES = {
     "qlora_version": (ctypes.c_char_p, []),
     "qlora_quantize": (ctypes.c_int, [_P, ctypes.c_int, _P, _P, _SZ, _P]),
     "qlora_dequantize": (ctypes.c_int, [_P, _P, _P]),
+    "qlora_dequantize_many": (ctypes.c_int, [_P, ctypes.c_int, _P, _P]),
     "qlora_linear_fwd": (ctypes.c_int, [_P, _I64, _P, _P, _P, ctypes.c_int, ctypes.c_float, _P, _P, _P, _SZ, _P]),
     "qlora_linear_bwd": (ctypes.c_int, [_P, _P, _I64, _P, _P, _P, ctypes.c_int, ctypes.c_float, _P, _P, _P, _P,
                                         _P, _SZ, _P]),
@@ -232,6 +233,17 @@ def dequantize(q: NF4Weight, out=None, stream=None):
     st = q.struct()
     _check(lib().qlora_dequantize(ctypes.byref(st), _ptr(y), _stream(stream)), "qlora_dequantize")
     return y
+
+
+def dequantize_many(qs, outs=None, stream=None):
+    """Decode several packed weights (up to 8) in one launch; returns the bf16 tensors."""
+    torch = _torch()
+    outs = outs if outs is not None else [torch.empty((q.n_out, q.n_in), dtype=torch.bfloat16, device=q.codes.device)
+                                          for q in qs]
+    st = (NF4WeightStruct * len(qs))(*[q.struct() for q in qs])
+    ptrs = (ctypes.c_void_p * len(outs))(*[_ptr(o) for o in outs])
+    _check(lib().qlora_dequantize_many(st, len(qs), ptrs, _stream(stream)), "qlora_dequantize_many")
+    return outs
 
 
 def linear_workspace(tokens: int, n_out: int, n_in: int, r: int, device="cuda"):

@@ -146,6 +146,13 @@ qlora_status qlora_quantize(const void *w, qlora_dtype w_dtype, const qlora_nf4_
  * This is the same decode the fused linear calls apply on the fly.           */
 qlora_status qlora_dequantize(const qlora_nf4_weight *q, uint16_t *w_bf16, void *stream);
 
+/* The same decode for count = 1..8 weights in one launch (for instance the
+ * seven linears of a decoder layer, streamed back to bf16 layer by layer, the
+ * 16-bit copy existing only for the layer in use: "qlora" entry, section
+ * "a ideia").  q[i] -> w_bf16[i]; either storage form, mixed freely.         */
+qlora_status qlora_dequantize_many(const qlora_nf4_weight *q, int count, uint16_t *const *w_bf16,
+                                   void *stream);
+
 /* Forward of the adapted linear layer for T tokens:
  *   u = x A^T                      (bf16, [T x r]; written to u_out if non-NULL)
  *   y = bf16( x W_hat^T + scale * u B^T )          [T x n_out]

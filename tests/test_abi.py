@@ -200,3 +200,15 @@ def test_projection_set_validation_before_any_launch():
     G = ptrs(0xA0000, 0xA1000, 0xA2000)
     assert lib.qlora_linear_set_bwd(ptrs(0xB0000, 0xB1000, 0xB2000), 0x50000, 16, 3, qs, 0x60000, B, 8, 2.0,
                                     None, None, 0xC0000, G, 0x90000, ws - 1, None) == 4
+
+
+def test_dequantize_many_validation():
+    lib = qlora.lib()
+    ws = (qlora.NF4WeightStruct * 2)(_fake_weight(), _fake_weight())
+    outs = (ctypes.c_void_p * 2)(0x80000, 0x90000)
+    assert lib.qlora_dequantize_many(ws, 0, outs, None) == 2
+    assert lib.qlora_dequantize_many(ws, 9, outs, None) == 2
+    assert lib.qlora_dequantize_many(None, 2, outs, None) == 1
+    assert lib.qlora_dequantize_many(ws, 2, (ctypes.c_void_p * 2)(0x80000, 0x90002), None) == 3
+    bad = (qlora.NF4WeightStruct * 2)(_fake_weight(), _fake_weight(0, 256))
+    assert lib.qlora_dequantize_many(bad, 2, outs, None) == 2

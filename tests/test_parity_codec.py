@@ -123,3 +123,38 @@ def test_quantize_is_deterministic():
     q2 = _gpu_quantize(w)
     for a, b in ((q1.codes, q2.codes), (q1.absmax_fp8, q2.absmax_fp8), (q1.absmax_scale, q2.absmax_scale)):
         assert np.array_equal(host(a), host(b))
+
+
+def test_dequantize_many_bit_exact():
+    """Several weights of mixed shapes and both storage forms decoded in one launch equal the
+    oracle's decode of each."""
+    announce("codec dequantize_many (5 weights, ragged, mixed storage forms)")
+    shapes = [(37, 101), (64, 1024), (1, 63), (129, 192), (300, 320)]
+    rng = np.random.default_rng(77)
+    ws = [(rng.standard_normal(s) * 0.02).astype(np.float32) for s in shapes]
+    forms = [True, False, True, False, True]
+    qs = [qlora.quantize(dev_f32(w), double_quant=dq) for w, dq in zip(ws, forms)]
+    outs = qlora.dequantize_many(qs)
+    for w, dq, o, (n, k) in zip(ws, forms, outs, shapes):
+        ref = oracle.quantize(w, n, k, double_quant=dq)
+        assert np.array_equal(host_bits(o), oracle.dequantize(ref)), (n, k, dq)
+
+
+def test_dequantize_many_65b_layer_sampled():
+    """The seven 65B linears of one layer in one launch, each checked against the single-weight
+    call bit for bit (the single call is checked against the oracle elsewhere)."""
+    torch = __import__("torch")
+    announce("codec dequantize_many 65B layer (7 weights)")
+    g = torch.Generator(device="cuda")
+    g.manual_seed(9)
+    qs = []
+    for _, n, k in workloads.SHAPES_65B:
+        w = torch.empty((n, k), dtype=torch.float32, device="cuda").normal_(0.0, 0.02, generator=g)
+        qs.append(qlora.quantize(w))
+        del w
+    outs = qlora.dequantize_many(qs)
+    for q, o in zip(qs, outs):
+        single = qlora.dequantize(q)
+        torch.cuda.synchronize()
+        assert torch.equal(single.view(torch.int16), o.view(torch.int16))
+        del single
