@@ -350,6 +350,44 @@ def extra_bulk_65b(torch, qlora, workloads, layers=80):
     return res
 
 
+def extra_gemv_65b(torch, qlora, workloads, steps):
+    """One token through the seven LLaMA-65B linears (fwd + bwd each, r = 64): 418 MB of packed
+    weights per layer step, beyond the last-level cache, so every step reads them from HBM."""
+    r = 64
+    g = torch.Generator(device="cuda")
+    g.manual_seed(165)
+    bits = lambda shape, std: (torch.randn(shape, generator=g, device="cuda") * std).to(torch.bfloat16)
+    items, step_bytes = [], 0
+    for _, n, k in workloads.SHAPES_65B:
+        w = torch.empty((n, k), dtype=torch.float32, device="cuda").normal_(0.0, 0.02, generator=g)
+        q = qlora.quantize(w)
+        del w
+        packed = qlora.nf4_bytes(n, k)
+        bf, f32 = torch.bfloat16, torch.float32
+        items.append(dict(q=q, x=bits((1, k), 1.0), dy=bits((1, n), 1.0), a=bits((r, k), 0.01), b=bits((n, r), 0.01),
+                          y=torch.empty((1, n), dtype=bf, device="cuda"), u=torch.empty((1, r), dtype=bf, device="cuda"),
+                          gx=torch.empty((1, k), dtype=bf, device="cuda"), ga=torch.empty((r, k), dtype=f32, device="cuda"),
+                          gb=torch.empty((n, r), dtype=f32, device="cuda"), ws=qlora.linear_workspace(1, n, k, r)))
+        # as the 4096^2 line: the weight and the adapters twice, adapter gradients, the vectors
+        step_bytes += 2 * packed + 2 * 2 * r * (n + k) + 4 * r * (n + k) + 2 * (2 * n + 3 * k)
+    torch.cuda.synchronize()
+
+    def layer():
+        for d in items:
+            qlora.linear_fwd(d["x"], d["q"], d["a"], d["b"], 0.25, y=d["y"], u_out=d["u"], workspace=d["ws"])
+            qlora.linear_bwd(d["dy"], d["x"], d["q"], d["a"], d["b"], 0.25, u=d["u"], grad_x=d["gx"], grad_A=d["ga"],
+                             grad_B=d["gb"], workspace=d["ws"])
+
+    layer()
+    n = max(5, steps // 5)
+    t, _ = time_region(torch, layer, n)
+    res = {"gemv_T1_65b_layer": {"GB/s": step_bytes * n / t / 1e9, "frac_hbm": step_bytes * n / t / 1e9 / PEAK_HBM_GBS,
+                                 "us_per_layer_fwd_bwd": t / n * 1e6, "bytes_per_layer_step": step_bytes, "r": r}}
+    del items
+    torch.cuda.empty_cache()
+    return res
+
+
 def extra_measurements(torch, qlora, steps):
     out = {}
     N = K = 4096
@@ -571,7 +609,7 @@ def main():
                          "path, rotating over more than 1 GB of distinct packed weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--extra-only", choices=["adamw", "dropout", "layers", "bulk"], default=None,
+    ap.add_argument("--extra-only", choices=["adamw", "dropout", "layers", "bulk", "gemv"], default=None,
                     help="run only this extra measurement and print its JSON (for profiling it alone)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before the steps, copy 256 MiB device to device three times (untimed): the "
@@ -602,6 +640,9 @@ def main():
         out = {"bulk_65b": extra_bulk_65b(torch, qlora, workloads)}
         out.update(extra_measurements(torch, qlora, args.steps))
         print(json.dumps(out), flush=True)
+        return
+    if args.extra_only == "gemv":
+        print(json.dumps(extra_gemv_65b(torch, qlora, workloads, args.steps)), flush=True)
         return
     if args.extra_only == "layers":
         print(json.dumps(extra_layers(torch, qlora, workloads, args.steps)), flush=True)
@@ -658,6 +699,7 @@ def main():
         extra = extra_layers(torch, qlora, workloads, args.steps)
         extra["bulk_65b"] = extra_bulk_65b(torch, qlora, workloads)
         extra.update(extra_measurements(torch, qlora, args.steps))
+        extra.update(extra_gemv_65b(torch, qlora, workloads, args.steps))
         extra.update(extra_adamw(torch, qlora, workloads, args.steps))
         extra.update(extra_dropout(torch, qlora, case, dev_bf16, dev_f32, args.steps))
         result["extra"] = extra
