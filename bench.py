@@ -576,7 +576,7 @@ def roofline_of(timing, T, N, K, r, packed):
         "gemv_fwd": ("hbm", packed + 2 * T * K + 2 * r * K),
         "gemv_bwd": ("hbm", packed + 2 * T * N + 2 * r * N + 2 * T * r + 4 * r * N),
     }
-    live = {k: v for k, v in timing.items() if v[0] > 0}
+    live = {k: v for k, v in timing.items() if v[0] > 0 and k in units}
     dom = max(live, key=lambda k: live[k][1])
     n_launch, ms = live[dom]
     avg_s = ms / n_launch / 1e3
