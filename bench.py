@@ -452,6 +452,32 @@ def extra_measurements(torch, qlora, steps):
     out["gemv_T1_fwd_bwd"] = {"GB/s": reps * nw * step_bytes / t / 1e9,
                               "frac_hbm": reps * nw * step_bytes / t / 1e9 / PEAK_HBM_GBS,
                               "us_per_fwd_bwd": t / (reps * nw) * 1e6, "shape": [N, K], "r": r}
+    # the same steps captured in one HIP graph and replayed (launch cost off the host)
+    graphs = []
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for q in weights[:16]:
+            qlora.linear_fwd(x, q, A, B, 0.25, y=y, u_out=u, workspace=ws)
+            qlora.linear_bwd(dy, x, q, A, B, 0.25, u=u, grad_x=gx, grad_A=ga, grad_B=gb, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    gr = torch.cuda.CUDAGraph()  # the steps over all the weights in one graph
+    with torch.cuda.graph(gr):
+        for q in weights:
+            qlora.linear_fwd(x, q, A, B, 0.25, y=y, u_out=u, workspace=ws)
+            qlora.linear_bwd(dy, x, q, A, B, 0.25, u=u, grad_x=gx, grad_A=ga, grad_B=gb, workspace=ws)
+    graphs.append(gr)
+
+    def gemv_graphs():
+        for gr in graphs:
+            gr.replay()
+
+    gemv_graphs()
+    t, _ = time_region(torch, gemv_graphs, reps)
+    out["gemv_T1_fwd_bwd_graph"] = {"GB/s": reps * nw * step_bytes / t / 1e9,
+                                    "frac_hbm": reps * nw * step_bytes / t / 1e9 / PEAK_HBM_GBS,
+                                    "us_per_fwd_bwd": t / (reps * nw) * 1e6, "shape": [N, K], "r": r}
+    del graphs
     del weights
     # quantize one fp32 weight (reads 4 B/param, writes the packed format)
     w = torch.empty((N, K), dtype=torch.float32, device="cuda").normal_(0, 0.02)

@@ -731,9 +731,17 @@ hipError_t gemv_bwd_impl(const uint16_t *dy, const uint16_t *xa, const QWeight &
   float *gx_part = part, *v_part = part + g.chunks * T * K;
   const size_t lds = bwd_lds_bytes(T);
   const void *fn = T == 1 ? (const void *)gemv_bwd_main_t1 : (const void *)gemv_bwd_main<T>;
+  // the attribute is set once per device and token count (the size depends on T only), so
+  // calls under stream capture make no attribute call
+  static bool lds_set[64][kGemvMaxT + 1] = {};
+  int dev = 0;
   if (lds > 64 * 1024) {
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (!lds_set[dev][T]) {
+      const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+      if (e != hipSuccess) return e;
+      lds_set[dev][T] = true;
+    }
   }
   const unsigned grid = (unsigned)(nf4_wgs + g.bparts);  // adapter workgroups first
   TimedLaunch tl;
