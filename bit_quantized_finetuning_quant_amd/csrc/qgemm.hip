@@ -544,14 +544,29 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
   __shared__ float lut[16];
 
   const int tid = threadIdx.x;
-  const int64_t m0 = (int64_t)blockIdx.x * QBM;
+  // Tile of this workgroup.  Workgroups go to the 8 XCDs round robin by linear
+  // id, and each XCD has its own L2.  When the grid allows it, XCD k takes a
+  // block of R/4 row tiles x C/2 column tiles (rows fastest, so the row tiles
+  // that share a weight tile run together): each activation row tile is then
+  // read by 2 XCDs and each weight tile by 4, against 1 and 8 for the plain
+  // order (whose weight re-reads dominate the traffic).
+  int64_t bx = blockIdx.x, by = blockIdx.y;
+  {
+    const int64_t R = gridDim.x, C = gridDim.y;
+    if (R % 4 == 0 && C % 2 == 0) {
+      const int64_t id = bx + by * R, xcd = id % 8, slot = id / 8, rb = R / 4;
+      bx = (xcd / 2) * rb + slot % rb;
+      by = (xcd % 2) * (C / 2) + slot / rb;
+    }
+  }
+  const int64_t m0 = bx * QBM;
   int mf = 0;  // forward: the member of this column tile
   if (!kTransW)
     for (int i = 1; i < set.count; ++i)
-      if ((int64_t)blockIdx.y >= set_member(set, i).tile0) mf = i;
+      if (by >= set_member(set, i).tile0) mf = i;
   const QgemmMember fm = set_member(set, mf);
   const int64_t Ncols = kTransW ? set.m[0].w.n_in : fm.w.n_out;
-  const int64_t c0 = ((int64_t)blockIdx.y - (kTransW ? 0 : fm.tile0)) * QBN;
+  const int64_t c0 = (by - (kTransW ? 0 : fm.tile0)) * QBN;
   const uint16_t *la_t = kTransW ? la : la + (int64_t)mf * r;
   const uint16_t *lb_t = kTransW ? lb : fm.lb;
   uint16_t *out = kTransW ? gx : fm.out;
