@@ -134,7 +134,7 @@ bool device_address(const void *p, void **dev) {
 }
 
 // A projection set: 1..kMaxSetMembers members sharing n_in and the storage
-// form, T above the few-token limit, adapter rank r per member.
+// form, adapter rank r per member.
 qlora_status check_set(int64_t T, int count, const qlora_nf4_weight *q, int r, float scale, int64_t *N) {
   if (!q) return QLORA_ERR_NULL;
   if (count < 1 || count > kMaxSetMembers) return QLORA_ERR_SHAPE;
@@ -145,7 +145,6 @@ qlora_status check_set(int64_t T, int count, const qlora_nf4_weight *q, int r, f
     if (q[i].flags != q[0].flags) return QLORA_ERR_VALUE;
     N[i] = q[i].n_out;
   }
-  if (T <= kGemvMaxT) return QLORA_ERR_SHAPE;
   if (T * (int64_t)count * r > kMaxNumel) return QLORA_ERR_SHAPE;
   return QLORA_OK;
 }
@@ -369,7 +368,7 @@ qlora_status qlora_linear_bwd_dropout(const uint16_t *dy, const uint16_t *x, int
 }
 
 size_t qlora_linear_set_workspace_bytes(int64_t T, int count, const int64_t *n_out, int64_t n_in, int r) {
-  if (!n_out || count < 1 || count > kMaxSetMembers || T <= kGemvMaxT || T > kMaxNumel) return 0;
+  if (!n_out || count < 1 || count > kMaxSetMembers || T < 1 || T > kMaxNumel) return 0;
   if (n_in % kBlock != 0 || r < 1 || r > 256) return 0;
   for (int i = 0; i < count; ++i)
     if (!shape_ok(n_out[i], n_in)) return 0;

@@ -794,4 +794,44 @@ hipError_t launch_gemv_bwd(int64_t T, const uint16_t *dy, const uint16_t *xa, co
   }
 }
 
+// ---------------------------------------------------------------------------
+// Few-token projection sets: the members run one by one; these move u between
+// the set's [T x count r] layout and per-member [T x r] blocks, and add the
+// members' grad_x.
+
+namespace {
+
+__global__ __launch_bounds__(256) void copy_rows_u16(const uint16_t *__restrict__ src, int64_t ld_src,
+                                                     uint16_t *__restrict__ dst, int64_t ld_dst, int64_t rows,
+                                                     int64_t cols) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < rows * cols; i += (int64_t)gridDim.x * 256)
+    dst[(i / cols) * ld_dst + i % cols] = src[(i / cols) * ld_src + i % cols];
+}
+
+// out = bf16(sum over members of the bf16 inputs, added in member order in fp32)
+__global__ __launch_bounds__(256) void sum_bf16(SumInputs in, int64_t n, uint16_t *__restrict__ out) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    float s = 0.f;
+    for (int m = 0; m < in.count; ++m) s += bf(in.p[m][i]);
+    out[i] = to_bf16(s);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_copy_rows(const uint16_t *src, int64_t ld_src, uint16_t *dst, int64_t ld_dst, int64_t rows,
+                            int64_t cols, hipStream_t st) {
+  const int64_t n = rows * cols;
+  if (n <= 0) return hipSuccess;
+  copy_rows_u16<<<(unsigned)std::min<int64_t>(cdiv(n, 256), 1024), 256, 0, st>>>(src, ld_src, dst, ld_dst, rows,
+                                                                                    cols);
+  return hipGetLastError();
+}
+
+hipError_t launch_sum_bf16(const SumInputs &in, int64_t n, uint16_t *out, hipStream_t st) {
+  if (n <= 0) return hipSuccess;
+  sum_bf16<<<(unsigned)std::min<int64_t>(cdiv(n, 256), 1024), 256, 0, st>>>(in, n, out);
+  return hipGetLastError();
+}
+
 }  // namespace qlora

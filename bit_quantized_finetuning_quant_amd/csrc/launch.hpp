@@ -176,14 +176,26 @@ struct AdamwScalars {
 hipError_t launch_adamw(float *param, uint16_t *param_bf16, const float *grad, float *exp_avg, float *exp_avg_sq,
                         int64_t n, const AdamwScalars &s, hipStream_t st);
 
+// Few-token sets (gemv.hip helpers): a strided 2-D copy of bf16 rows, and the
+// sum of up to kMaxSetMembers bf16 arrays (fp32 adds in member order, one bf16
+// rounding).
+struct SumInputs {
+  int count;
+  const uint16_t *p[kMaxSetMembers];
+};
+hipError_t launch_copy_rows(const uint16_t *src, int64_t ld_src, uint16_t *dst, int64_t ld_dst, int64_t rows,
+                            int64_t cols, hipStream_t st);
+hipError_t launch_sum_bf16(const SumInputs &in, int64_t n, uint16_t *out, hipStream_t st);
+
 // Projection sets (linear.hip): members share x [T x K] and the adapter
 // rank r; A_set [count r x K] holds the members' A back to back, u_set and
-// v_set are [T x count r].  T > kGemvMaxT.
+// v_set are [T x count r].  For T <= kGemvMaxT the members run one by one on
+// the few-token path, with per-member u and grad_x blocks in the workspace.
 struct SetPlan {
   int64_t T, K;
   int r, count;
   int64_t N[kMaxSetMembers];
-  size_t off_u, off_v, off_part, total;
+  size_t off_u, off_v, off_part, off_um, off_gx, total;
 };
 SetPlan plan_linear_set(int64_t T, int count, const int64_t *N, int64_t K, int r);
 hipError_t launch_linear_set_fwd(const SetPlan &p, const uint16_t *x, const QWeight *w, const uint16_t *A_set,

@@ -218,15 +218,71 @@ SetPlan plan_linear_set(int64_t T, int count, const int64_t *N, int64_t K, int r
   p.off_v = off;
   off += uv;
   p.off_part = off;
-  off += align256(lora_set_part_floats(T, count, N, K, r) * 4);
+  if (T <= kGemvMaxT) {  // members one by one: the largest member's scratch, one u block, count grad_x blocks
+    size_t part = 0;
+    for (int i = 0; i < count; ++i) part = std::max(part, gemv_part_floats(T, N[i], K, r));
+    off += align256(part * 4);
+    p.off_um = off;
+    off += align256((size_t)T * r * 2);
+    p.off_gx = off;
+    off += (size_t)count * align256((size_t)T * K * 2);
+  } else {
+    off += align256(lora_set_part_floats(T, count, N, K, r) * 4);
+    p.off_um = p.off_gx = off;
+  }
   p.total = off;
   return p;
+}
+
+// Few-token sets: each member on the few-token path.  u moves between the
+// set's [T x count r] layout and one [T x r] block; grad_x is the fp32 sum,
+// in member order, of the members' bf16 terms (one more bf16 rounding).
+static hipError_t set_fwd_few(const SetPlan &p, const uint16_t *x, const QWeight *w, const uint16_t *A_set,
+                              const uint16_t *const *B, float scale, uint16_t *const *y, uint16_t *u, char *ws,
+                              const Codebook &cb, hipStream_t st) {
+  float *part = (float *)(ws + p.off_part);
+  uint16_t *um = (uint16_t *)(ws + p.off_um);
+  const int64_t rt = (int64_t)p.count * p.r;
+  for (int i = 0; i < p.count; ++i) {
+    hipError_t e = launch_gemv_fwd(p.T, x, x, w[i], A_set + (int64_t)i * p.r * p.K, B[i], p.r, scale, 1.0f, y[i], um,
+                                   part, cb, st);
+    if (e == hipSuccess) e = launch_copy_rows(um, p.r, u + (int64_t)i * p.r, rt, p.T, p.r, st);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+static hipError_t set_bwd_few(const SetPlan &p, const uint16_t *const *dy, const uint16_t *x, const QWeight *w,
+                              const uint16_t *A_set, const uint16_t *const *B, float scale, const uint16_t *u,
+                              uint16_t *grad_x, float *grad_A_set, float *const *grad_B, char *ws, const Codebook &cb,
+                              hipStream_t st) {
+  float *part = (float *)(ws + p.off_part);
+  uint16_t *um = (uint16_t *)(ws + p.off_um);
+  const int64_t rt = (int64_t)p.count * p.r;
+  const size_t gx_bytes = align256((size_t)p.T * p.K * 2);
+  SumInputs sum{};
+  sum.count = p.count;
+  for (int i = 0; i < p.count; ++i) {
+    const uint16_t *A = A_set + (int64_t)i * p.r * p.K;
+    hipError_t e = u ? launch_copy_rows(u + (int64_t)i * p.r, rt, um, p.r, p.T, p.r, st)
+                     : launch_gemv_fwd(p.T, x, x, w[i], A, B[i], p.r, scale, 1.0f, nullptr, um, part, cb, st);
+    if (e != hipSuccess) return e;
+    uint16_t *gx = nullptr;
+    if (grad_x) gx = p.count == 1 ? grad_x : (uint16_t *)(ws + p.off_gx + (size_t)i * gx_bytes);
+    sum.p[i] = gx;
+    e = launch_gemv_bwd(p.T, dy[i], x, w[i], A, B[i], p.r, scale, scale, nullptr, um, gx, grad_A_set + (int64_t)i * p.r * p.K,
+                        grad_B[i], part, cb, st);
+    if (e != hipSuccess) return e;
+  }
+  if (!grad_x || p.count == 1) return hipSuccess;
+  return launch_sum_bf16(sum, p.T * p.K, grad_x, st);
 }
 
 hipError_t launch_linear_set_fwd(const SetPlan &p, const uint16_t *x, const QWeight *w, const uint16_t *A_set,
                                  const uint16_t *const *B, float scale, uint16_t *const *y, uint16_t *u_out, char *ws,
                                  const Codebook &cb, hipStream_t st) {
   uint16_t *u = u_out ? u_out : (uint16_t *)(ws + p.off_u);
+  if (p.T <= kGemvMaxT) return set_fwd_few(p, x, w, A_set, B, scale, y, u, ws, cb, st);
   float *part = (float *)(ws + p.off_part);
   const int64_t rt = (int64_t)p.count * p.r;
   // u_set = x A_set^T: one product for every member's u
@@ -251,6 +307,7 @@ hipError_t launch_linear_set_bwd(const SetPlan &p, const uint16_t *const *dy, co
                                  const uint16_t *A_set, const uint16_t *const *B, float scale, const uint16_t *u,
                                  uint16_t *grad_x, float *grad_A_set, float *const *grad_B, char *ws,
                                  const Codebook &cb, hipStream_t st) {
+  if (p.T <= kGemvMaxT) return set_bwd_few(p, dy, x, w, A_set, B, scale, u, grad_x, grad_A_set, grad_B, ws, cb, st);
   float *part = (float *)(ws + p.off_part);
   uint16_t *v = (uint16_t *)(ws + p.off_v);
   const int64_t rt = (int64_t)p.count * p.r;

@@ -177,7 +177,8 @@ def test_projection_set_validation_before_any_launch():
     lib = qlora.lib()
     n_outs = (ctypes.c_int64 * 3)(512, 256, 256)
     assert lib.qlora_linear_set_workspace_bytes(16, 3, n_outs, 256, 8) > 0
-    assert lib.qlora_linear_set_workspace_bytes(4, 3, n_outs, 256, 8) == 0  # few-token: per linear
+    assert lib.qlora_linear_set_workspace_bytes(4, 3, n_outs, 256, 8) > 0  # few-token: members one by one
+    assert lib.qlora_linear_set_workspace_bytes(0, 3, n_outs, 256, 8) == 0
     assert lib.qlora_linear_set_workspace_bytes(16, 5, n_outs, 256, 8) == 0
     assert lib.qlora_linear_set_workspace_bytes(16, 3, n_outs, 100, 8) == 0
     ws = lib.qlora_linear_set_workspace_bytes(16, 3, n_outs, 256, 8)
@@ -189,7 +190,7 @@ def test_projection_set_validation_before_any_launch():
     fwd = lambda T=16, count=3, q=qs, b=B, y=Y, wsb=ws, a=0x60000: lib.qlora_linear_set_fwd(
         0x50000, T, count, q, a, b, 8, 2.0, y, None, 0x90000, wsb, None)
     assert fwd(wsb=ws - 1) == 4
-    assert fwd(T=4) == 2 and fwd(count=0) == 2 and fwd(count=5) == 2
+    assert fwd(T=0) == 2 and fwd(count=0) == 2 and fwd(count=5) == 2
     assert fwd(a=0x60008) == 3
     assert fwd(b=ptrs(0x70000, None, 0x72000)) == 1
     odd = (qlora.NF4WeightStruct * 3)(_fake_weight(512, 256), _fake_weight(256, 320), _fake_weight(256, 256))

@@ -67,6 +67,30 @@ def test_sets_against_the_oracle(n_outs, n_in, T, r):
     _check(cases, need_u=False)
 
 
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
+def test_few_token_sets_against_the_oracle(T):
+    """T <= 4: the members run one by one on the few-token kernels; same layouts, same bar."""
+    announce(f"few-token set n_outs=(256, 192, 320) n_in=384 T={T} r=16")
+    cases = _members((256, 192, 320), 384, T, 16, seed=40 + T)
+    _check(cases)
+    _check(cases, need_u=False)
+
+
+def test_few_token_one_member_set_equals_the_single_linear_calls():
+    torch = __import__("torch")
+    announce("few-token set of one member vs single linear, 300x320 T=3 r=24")
+    (c,) = _members((300,), 320, 3, 24, seed=12)
+    q = qlora.quantize(dev_f32(c.w))
+    x, a, b, dy = dev_bf16(c.x), dev_bf16(c.a), dev_bf16(c.b), dev_bf16(c.dy)
+    y0, u0 = qlora.linear_fwd(x, q, a, b, c.scale)
+    g0 = qlora.linear_bwd(dy, x, q, a, b, c.scale, u=u0)
+    (y1,), u1 = qlora.linear_set_fwd(x, [q], a, [b], c.scale)
+    g1x, g1a, (g1b,) = qlora.linear_set_bwd([dy], x, [q], a, [b], c.scale, u=u1)
+    torch.cuda.synchronize()
+    for t0, t1 in zip((y0, u0) + tuple(g0), (y1, u1, g1x, g1a, g1b)):
+        assert np.array_equal(host(t0), host(t1))
+
+
 def test_set_with_fp32_constants():
     announce("set fp32 constants n_outs=(256, 320) n_in=256 T=130 r=8")
     _check(_members((256, 320), 256, 130, 8, seed=5), double_quant=False)
