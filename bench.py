@@ -490,6 +490,30 @@ def extra_measurements(torch, qlora, steps):
     return out
 
 
+def extra_library_reference(torch, qlora, case, dev_bf16, dev_f32, steps, fused_fwd_us=None):
+    """Context for the fused forward GEMM: the vendor library's plain bf16 GEMM (torch.matmul,
+    hipBLASLt) of the same activation with the decoded weight, x W_hat^T (no adapter term), and the
+    library's time plus one bulk dequantization (the unfused alternative).  Not part of any path of
+    this library."""
+    T, N, K = case.tokens, case.n_out, case.n_in
+    q = qlora.quantize(dev_f32(case.w))
+    w_hat = qlora.dequantize(q)
+    x = dev_bf16(case.x)
+    for _ in range(5):
+        torch.matmul(x, w_hat.t())
+        qlora.dequantize(q, out=w_hat)
+    reps = max(10, steps)
+    t_mm, _ = time_region(torch, lambda: torch.matmul(x, w_hat.t()), reps)
+    t_dq, _ = time_region(torch, lambda: qlora.dequantize(q, out=w_hat), reps)
+    mm_us, dq_us = t_mm / reps * 1e6, t_dq / reps * 1e6
+    out = {"library_gemm_us": mm_us, "library_gemm_TFLOP/s": 2 * T * N * K / (mm_us * 1e-6) / 1e12,
+           "library_gemm_frac_mfma": 2 * T * N * K / (mm_us * 1e-6) / 1e12 / PEAK_BF16_TFLOPS,
+           "dequant_us": dq_us, "dequant_plus_library_us": dq_us + mm_us, "shape": [T, N, K]}
+    if fused_fwd_us is not None:
+        out["fused_fwd_us"] = fused_fwd_us
+    return {"library_reference_7b_attn_T2048": out}
+
+
 def extra_dropout(torch, qlora, case, dev_bf16, dev_f32, steps):
     """The headline step with LoRA dropout 0.05 (mask regenerated in the forward and in the
     backward), against the same step without it."""
@@ -635,7 +659,7 @@ def main():
                          "path, rotating over more than 1 GB of distinct packed weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--extra-only", choices=["adamw", "dropout", "layers", "bulk", "gemv"], default=None,
+    ap.add_argument("--extra-only", choices=["adamw", "dropout", "layers", "bulk", "gemv", "library"], default=None,
                     help="run only this extra measurement and print its JSON (for profiling it alone)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before the steps, copy 256 MiB device to device three times (untimed): the "
@@ -676,6 +700,10 @@ def main():
     if args.extra_only == "dropout":
         case = workloads.attn7b_case(2048)
         print(json.dumps(extra_dropout(torch, qlora, case, dev_bf16, dev_f32, args.steps)), flush=True)
+        return
+    if args.extra_only == "library":
+        case = workloads.attn7b_case(2048)
+        print(json.dumps(extra_library_reference(torch, qlora, case, dev_bf16, dev_f32, args.steps)), flush=True)
         return
     tokens = 2048 if args.workload == "7b_attn" else 1
     log(f"generating the 7B projection workload (4096x4096, T={tokens}, r=64)")
@@ -728,6 +756,10 @@ def main():
         extra.update(extra_gemv_65b(torch, qlora, workloads, args.steps))
         extra.update(extra_adamw(torch, qlora, workloads, args.steps))
         extra.update(extra_dropout(torch, qlora, case, dev_bf16, dev_f32, args.steps))
+        fwd = roofline.get("other_kernels", {}).get("qgemm_fwd", {}).get("avg_us")
+        if roofline.get("kernel") == "qgemm_fwd":
+            fwd = roofline.get("avg_us")
+        extra.update(extra_library_reference(torch, qlora, case, dev_bf16, dev_f32, args.steps, fwd))
         result["extra"] = extra
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on host cores")

@@ -93,8 +93,9 @@ __device__ __forceinline__ u32x4 frag(const uint16_t *lds, int base, int kk, int
 __host__ __device__ constexpr int64_t cdiv_d(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 // Contraction steps fetched at once: 4 (a group of 256) or, when a split is
-// exactly 512 long, all 8 of it, so that the whole split arrives in one round
-// trip (128 KB per workgroup in flight, 147 KB of LDS).
+// exactly 512 long and the launch fits one round of workgroups, all 8 of it,
+// so that the whole split arrives in one round trip (128 KB per workgroup in
+// flight, 147 KB of LDS).
 
 template <bool kAT, bool kBT, bool kBf16Out, bool kFull, int kGroupSteps>
 __device__ __forceinline__ void lora_body(const uint16_t *__restrict__ P, int64_t ldp,
@@ -319,12 +320,16 @@ int64_t problem_blocks(const LoraProblem &pr) { return lora_tiles(pr.M, pr.Nc) *
 int64_t problem_quads(const LoraProblem &pr) { return pr.S > 1 ? lora_tiles(pr.M, pr.Nc) * (LT * LT / 4) : 0; }
 
 // Launches one product (nb == nullptr) or two of the same operand forms; the
-// two must agree on the group length (8 when a split is exactly 512 long).
+// two must agree on the split length.  A split of exactly 512 is fetched in
+// one round trip (8 steps, 147 KB of LDS: one workgroup per CU) when the
+// launch fits one round of 256 workgroups; a larger launch (the two gradient
+// products) fetches groups of 4 steps, two workgroups per CU, so that all of
+// it is resident at once.
 template <bool kAT, bool kBT, bool kBf16Out>
 hipError_t launch_pair(const LoraProblem &a, const LoraProblem *nb, hipStream_t st) {
   const LoraProblem b = nb ? *nb : a;
   const int64_t wa = problem_blocks(a), wb = nb ? problem_blocks(b) : 0;
-  const bool whole = a.chunk == LT * 8;
+  const bool whole = a.chunk == LT * 8 && wa + wb <= 256;
   if (whole)
     lora_gemm<kAT, kBT, kBf16Out, 8><<<(unsigned)(wa + wb), 256, 0, st>>>(a, b, wa);
   else

@@ -312,16 +312,22 @@ struct Producer {
 //   - fetch the codes of stage k+5,
 //   - form the products of stage k+2 (levels read at the previous step) and
 //     write them to LDS.
-// Code sets rotate by three and level sets by two (unrolled by six).
+// Code sets rotate by three and level sets by two (unrolled by six).  The
+// caller fetches the codes of stages 0, 1 and 2 (fetch_first_codes), so that
+// their latency can overlap other work.
+template <bool kTransW, bool kDQ>
+__device__ __forceinline__ void fetch_first_codes(const Producer<kTransW, kDQ> &p, int64_t nk, Stage &c0, Stage &c1,
+                                                  Stage &c2) {
+  p.template load_w<true>(0, c0);
+  p.template load_w<true>(min((int64_t)1, nk - 1), c1);
+  p.template load_w<true>(min((int64_t)2, nk - 1), c2);
+}
+
 template <bool kTransW, bool kDQ>
 __device__ __forceinline__ void producer_loop_full(const Producer<kTransW, kDQ> &p, int64_t nk, uint16_t (*sb)[QBN * QLD],
-                                                   const float *lut) {
+                                                   const float *lut, Stage &c0, Stage &c1, Stage &c2) {
   auto st = [nk](int64_t k) { return min(k, nk - 1); };
-  Stage c0, c1, c2;
   Levels l0, l1;
-  p.template load_w<true>(0, c0);
-  p.template load_w<true>(st(1), c1);
-  p.template load_w<true>(st(2), c2);
   p.read_levels(c0, lut, l0);
   p.store_w(l0, sb[0]);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
@@ -489,34 +495,73 @@ __device__ __forceinline__ u32x4 load_b_frag(const uint16_t *B, int wn, int lane
 // the left factor la [M x r] (row stride ld_la) as an activation tile, the right factor as a
 // weight tile (forward: lb = B [Ncols x r], rows = output columns; grad_x:
 // lb = A [r x Ncols], rows = the rank).  All 512 threads stage with 16-byte
-// loads where the rank allows it.
+// loads where the rank allows it, every load of a chunk issued before the
+// first LDS store (one memory round trip per chunk).
 template <bool kTransW>
 __device__ __forceinline__ void stage_lora(const uint16_t *la, int64_t ld_la, const uint16_t *lb, int r, int j0, int64_t M,
                                            int64_t Ncols, int64_t m0, int64_t c0, int tid, uint16_t *sa_dst,
                                            uint16_t *sb_dst) {
   const bool vec = (r % 8) == 0 && (ld_la % 8) == 0;
-  for (int idx = tid; idx < QBM * 8; idx += 512) {  // 256 rows x 8 chunks
-    const int row = idx >> 3, ch = idx & 7;
+  constexpr int kA = QBM * 8 / 512, kB = 2;  // per thread: 256 rows x 8 chunks; 1024 chunks of the right factor
+  u32x4 va[kA], vb[kB];
+#pragma unroll
+  for (int it = 0; it < kA; ++it) {
+    const int idx = tid + 512 * it, row = idx >> 3, ch = idx & 7;
     const int64_t grow = m0 + row;
-    const u32x4 v = grow < M ? ld8(la + grow * ld_la, j0 + 8 * ch, r, vec) : u32x4{0u, 0u, 0u, 0u};
-    *(u32x4 *)&sa_dst[act_off(row, ch)] = v;
+    va[it] = grow < M ? ld8(la + grow * ld_la, j0 + 8 * ch, r, vec) : u32x4{0u, 0u, 0u, 0u};
   }
   if (!kTransW) {
-    for (int idx = tid; idx < QBN * 8; idx += 512) {  // 128 output columns x 8 chunks of the rank
-      const int row = idx >> 3, ch = idx & 7;
+#pragma unroll
+    for (int it = 0; it < kB; ++it) {  // 128 output columns x 8 chunks of the rank
+      const int idx = tid + 512 * it, row = idx >> 3, ch = idx & 7;
       const int64_t col = c0 + row;
-      const u32x4 v = col < Ncols ? ld8(lb + col * r, j0 + 8 * ch, r, vec) : u32x4{0u, 0u, 0u, 0u};
-      *(u32x4 *)&sb_dst[row * QLD + 8 * ch] = v;
+      vb[it] = col < Ncols ? ld8(lb + col * r, j0 + 8 * ch, r, vec) : u32x4{0u, 0u, 0u, 0u};
     }
   } else {
     const bool cvec = (Ncols % 8) == 0;
-    for (int idx = tid; idx < 64 * 16; idx += 512) {  // 64 rank rows x 16 chunks of 8 columns
-      const int jr = idx >> 4, ch = idx & 15;
+#pragma unroll
+    for (int it = 0; it < kB; ++it) {  // 64 rank rows x 16 chunks of 8 columns
+      const int idx = tid + 512 * it, jr = idx >> 4, ch = idx & 15;
       const int j = j0 + jr;
-      const u32x4 v = j < r ? ld8(lb + (int64_t)j * Ncols, c0 + 8 * ch, Ncols, cvec) : u32x4{0u, 0u, 0u, 0u};
-      *(u32x4 *)&sb_dst[jr * TLD + 8 * ch] = v;
+      vb[it] = j < r ? ld8(lb + (int64_t)j * Ncols, c0 + 8 * ch, Ncols, cvec) : u32x4{0u, 0u, 0u, 0u};
     }
   }
+#pragma unroll
+  for (int it = 0; it < kA; ++it) {
+    const int idx = tid + 512 * it;
+    *(u32x4 *)&sa_dst[act_off(idx >> 3, idx & 7)] = va[it];
+  }
+#pragma unroll
+  for (int it = 0; it < kB; ++it) {
+    const int idx = tid + 512 * it;
+    if (!kTransW)
+      *(u32x4 *)&sb_dst[(idx >> 3) * QLD + 8 * (idx & 7)] = vb[it];
+    else
+      *(u32x4 *)&sb_dst[(idx >> 4) * TLD + 8 * (idx & 15)] = vb[it];
+  }
+}
+
+// The producer state of member mi of a set (mu: the member's tensor mean,
+// loaded by the caller).
+template <bool kTransW, bool kDQ>
+__device__ __forceinline__ Producer<kTransW, kDQ> member_producer(const QgemmMember &mm, const uint16_t *x, int64_t M,
+                                                                  int64_t m0, int64_t c0, int tid, float mu) {
+  Producer<kTransW, kDQ> p;
+  const int64_t Kc = kTransW ? mm.w.n_out : mm.w.n_in;
+  p.act = kTransW ? mm.act : x;
+  p.M = M;
+  p.Kc = Kc;
+  p.m0 = m0;
+  p.c0 = c0;
+  p.K = mm.w.n_in;
+  p.N = mm.w.n_out;
+  p.kblk_row = mm.w.n_in / kBlock;
+  p.w = mm.w;
+  p.mu = mu;
+  p.ptid = tid - 256;
+  p.act_vec = (Kc % 8) == 0;
+  p.init_addressing();
+  return p;
 }
 
 __device__ __forceinline__ QgemmMember set_member(const QgemmSet &s, int i) {
@@ -578,13 +623,49 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
   if (tid < 16) lut[tid] = cb.v[tid];
   __syncthreads();
 
-  // LoRA term first, scaled: acc = scale * la lb^T, staged chunk by chunk in
-  // activation stage 2 and weight stage 1 (the loop's last barrier ends their
-  // use before the pipeline starts); the consumer waves multiply, everyone
-  // stages.
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, lhi = lane >> 5;
+  const int cw = __builtin_amdgcn_readfirstlane(wave);  // consumer wave: DMA rows [64 cw, 64 cw + 64)
+  const int64_t dma_row0 = m0 + 64 * cw;
+
+  // The pipeline's first memory accesses go out before the LoRA term, so that
+  // their latency overlaps its staging: for full tiles of the first member the
+  // producers fetch the codes of stages 0-2 and the consumers start the
+  // activation DMA of stages 0 and 1 (stage 2's buffer still holds the LoRA
+  // staging).
+  const QgemmMember m_first = set_member(set, m_begin);
+  const int64_t Kc_first = kTransW ? m_first.w.n_out : m_first.w.n_in;
+  const int64_t nk_first = (Kc_first + QBK - 1) / QBK;
+  const bool full_first = (m0 + QBM <= M) && (c0 + QBN <= Ncols) && (Kc_first % QBK == 0);
+  Stage pre0, pre1, pre2;
+  uint32_t dma_off_first[2] = {0u, 0u};
+  // every member's tensor mean, fetched with the first codes
+  float mu0 = 0.f, mu1 = 0.f, mu2 = 0.f, mu3 = 0.f;
+  if (tid >= 256) {
+    if (kDQ) {
+      mu0 = *set_member(set, m_begin).w.mu;
+      if (m_begin + 1 < m_end) mu1 = *set_member(set, m_begin + 1).w.mu;
+      if (m_begin + 2 < m_end) mu2 = *set_member(set, m_begin + 2).w.mu;
+      if (m_begin + 3 < m_end) mu3 = *set_member(set, m_begin + 3).w.mu;
+    }
+    if (full_first)
+      fetch_first_codes(member_producer<kTransW, kDQ>(m_first, x, M, m0, c0, tid, 0.f), nk_first, pre0, pre1, pre2);
+  } else if (full_first) {
+    const uint16_t *act = kTransW ? m_first.act : x;
+    dma_off_first[0] = dma_lane_offset(lane, Kc_first, 0);
+    dma_off_first[1] = dma_lane_offset(lane, Kc_first, 1);
+    dma_act(act, Kc_first, dma_row0, 0, dma_off_first, sa[0] + 64 * cw * 64);
+    dma_act(act, Kc_first, dma_row0, min((int64_t)1, nk_first - 1), dma_off_first, sa[1] + 64 * cw * 64);
+  }
+
+  // LoRA term first, scaled: acc = scale * la lb^T, staged chunk by chunk in
+  // activation stage 2 and weight stage 1; the consumer waves multiply,
+  // everyone stages.  The producers skip the last chunk's closing barrier:
+  // while the consumers multiply it they decode stage 0 into weight stage 0,
+  // and their "stage 0 ready" barrier pairs with the consumers' closing one
+  // (which the consumers' first member then does not repeat), so the stage 1
+  // writes into weight stage 1 start only after the LoRA term is read.
   f32x16 acc[4][2];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -594,9 +675,17 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
   for (int j0 = 0; j0 < r; j0 += QBK) {
     stage_lora<kTransW>(la_t, set.ld_la, lb_t, r, j0, M, Ncols, m0, c0, tid, sa[2], sb[1]);
+    // every wave's early DMA of stages 0 and 1 has landed before the barrier
+    // (the staging's loads, issued after them, have returned already); naming
+    // the lane offsets keeps their registers untouched until then
+    if (tid < 256) asm volatile("s_waitcnt vmcnt(0)" ::"v"(dma_off_first[0]), "v"(dma_off_first[1]) : "memory");
     __syncthreads();
-    if (tid < 256) consumer_slices<kTransW>(sa[2], sb[1], wm, wn, lane, acc);
-    __syncthreads();
+    if (tid < 256) {
+      consumer_slices<kTransW>(sa[2], sb[1], wm, wn, lane, acc);
+      __syncthreads();
+    } else if (j0 + QBK < r) {
+      __syncthreads();
+    }
   }
   if (tid < 256) {
     if (kTransW && kDrop) {
@@ -635,32 +724,22 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
       const int64_t nk = (Kc + QBK - 1) / QBK;
       const bool full = (m0 + QBM <= M) && (c0 + QBN <= Ncols) && (Kc % QBK == 0);
       if (mi > m_begin) wg_barrier();  // the previous member's pipeline has drained
-      Producer<kTransW, kDQ> p;
-      p.act = kTransW ? mm.act : x;
-      p.M = M;
-      p.Kc = Kc;
-      p.m0 = m0;
-      p.c0 = c0;
-      p.K = mm.w.n_in;
-      p.N = mm.w.n_out;
-      p.kblk_row = mm.w.n_in / kBlock;
-      p.w = mm.w;
-      p.mu = kDQ ? *mm.w.mu : 0.f;
-      p.ptid = tid - 256;
-      p.act_vec = (Kc % 8) == 0;
-      p.init_addressing();
-      if (full)
-        producer_loop_full(p, nk, sb, lut);
-      else
+      const int mo = mi - m_begin;
+      const float mu = mo == 0 ? mu0 : mo == 1 ? mu1 : mo == 2 ? mu2 : mu3;
+      const Producer<kTransW, kDQ> p = member_producer<kTransW, kDQ>(mm, x, M, m0, c0, tid, mu);
+      if (full) {
+        if (mi > m_begin) fetch_first_codes(p, nk, pre0, pre1, pre2);  // the first member's went out early
+        producer_loop_full(p, nk, sb, lut, pre0, pre1, pre2);
+      } else {
         producer_loop_partial(p, nk, sa, sb, lut);
+      }
     }
     return;
   }
 
   // -------------------------------------------------------------- consumers
-  // full tiles: stages 0, 1 and 2 of the activation ring
-  const int cw = __builtin_amdgcn_readfirstlane(wave);
-  const int64_t dma_row0 = m0 + 64 * cw;
+  // full tiles: stages 0, 1 and 2 of the activation ring (the first member's
+  // stages 0 and 1 went out before the LoRA term)
   for (int mi = m_begin; mi < m_end; ++mi) {
   const QgemmMember mm = set_member(set, mi);
   const uint16_t *act = kTransW ? mm.act : x;
@@ -670,12 +749,14 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
   if (mi > m_begin) wg_barrier();  // every wave is done with the previous member's LDS stages
   const uint32_t dma_lane_off[2] = {dma_lane_offset(lane, Kc, 0), dma_lane_offset(lane, Kc, 1)};
   if (full) {
-    dma_act(act, Kc, dma_row0, 0, dma_lane_off, sa[0] + 64 * cw * 64);
-    dma_act(act, Kc, dma_row0, min((int64_t)1, nk - 1), dma_lane_off, sa[1] + 64 * cw * 64);
+    if (mi > m_begin) {
+      dma_act(act, Kc, dma_row0, 0, dma_lane_off, sa[0] + 64 * cw * 64);
+      dma_act(act, Kc, dma_row0, min((int64_t)1, nk - 1), dma_lane_off, sa[1] + 64 * cw * 64);
+    }
     dma_act(act, Kc, dma_row0, min((int64_t)2, nk - 1), dma_lane_off, sa[2] + 64 * cw * 64);
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(16, 0));  // stage 0 has landed
   }
-  wg_barrier();  // stage 0 ready
+  if (mi > m_begin) wg_barrier();  // stage 0 ready (the first member's: at the LoRA term's last barrier)
   StageFrags f;
 #pragma unroll
   for (int kk = 0; kk < QBK / 16; ++kk) {
