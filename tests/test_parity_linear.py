@@ -57,7 +57,7 @@ def test_tiny_case_scale_alpha_and_recomputed_u():
 
 
 @pytest.mark.parametrize("shape", [(300, 320, 300, 24), (128, 64, 1, 8), (77, 192, 259, 5),
-                                   (1000, 640, 513, 64), (256, 128, 17, 256)])
+                                   (1000, 640, 513, 64), (256, 128, 17, 256), (256, 256, 512, 160)])
 def test_ragged_multi_tile_shapes(shape):
     n_out, n_in, T, r = shape
     announce(f"linear ragged n_out={n_out} n_in={n_in} T={T} r={r}")

@@ -59,7 +59,7 @@ def _check(cases, need_u=True, double_quant=True):
 
 @pytest.mark.parametrize("n_outs,n_in,T,r", [((320, 192, 256), 320, 300, 24), ((77, 130, 64), 192, 259, 5),
                                              ((1000, 640), 640, 513, 64), ((128, 128, 128, 128), 128, 17, 16),
-                                             ((64, 128), 128, 40, 4)])
+                                             ((64, 128), 128, 40, 4), ((256, 128), 256, 256, 96)])
 def test_sets_against_the_oracle(n_outs, n_in, T, r):
     announce(f"set n_outs={n_outs} n_in={n_in} T={T} r={r}")
     cases = _members(n_outs, n_in, T, r, seed=T + r)
