@@ -17,11 +17,13 @@
 //     stage k+2 from global memory straight into a 3-stage LDS ring with
 //     global_load_lds_dwordx4, so no register ever holds it;
 //   waves 4-7 (producers) fetch the packed weight codes several steps ahead
-//     into registers, look each code's level up in a 16-entry table in LDS,
-//     multiply it by the block constant in fp32 and round to bf16 (the weight
-//     tile is decoded once per workgroup and shared by all 256 activation
-//     rows), and write the next weight stage to LDS.  For partial tiles they
-//     also carry the activation tile, masked, through registers.
+//     into registers and decode them (the weight tile is decoded once per
+//     workgroup and shared by all 256 activation rows): full tiles build each
+//     block's 16 values bf16(fl32(level * constant)) as register byte tables
+//     and select with v_perm_b32; partial tiles look the levels up in a
+//     16-entry table in LDS and multiply.  They write the next weight stage to
+//     LDS; for partial tiles they also carry the activation tile, masked,
+//     through registers.
 // One consumer and one producer wave share each SIMD, so the decode's vector
 // ALU work issues alongside the matrix-core work.  One workgroup barrier per
 // contraction step; both roles execute the same number of barriers.  The DMA
@@ -139,8 +141,7 @@ struct Stage {
   float s2;
 };
 
-// The 32 levels of a stage's codes and its block constant, read one step
-// before the products that use them.
+// The 32 levels of a stage's codes and its block constant (partial tiles).
 struct Levels {
   float lv[32];
   float ch;
@@ -226,8 +227,8 @@ struct Producer {
     }
   }
 
-  // The levels of a stage's 32 codes from the 16-entry table in LDS, and its
-  // block constant.  Each byte of the masked words (c << 2) & 0x3C3C3C3C and
+  // Partial tiles: the levels of a stage's 32 codes from the 16-entry table
+  // in LDS, and its block constant.  Each byte of the masked words (c << 2) & 0x3C3C3C3C and
   // (c >> 2) & 0x3C3C3C3C is four times a code (even and odd elements), i.e.
   // the byte offset of its level, so one extract per code forms its address.
   __device__ __forceinline__ void read_levels(const Stage &s, const float *lut, Levels &L) const {
@@ -247,44 +248,25 @@ struct Producer {
     L.ch = kDQ ? decode_constant(s.q, s.s2, mu) : s.s2;
   }
 
-  // Levels of word v (8 codes) of a stage.
-  __device__ __forceinline__ void read_word(const Stage &s, int v, const float *lut, Levels &L) const {
-    const char *base = (const char *)lut;
-    uint32_t ev = (s.code[v] << 2) & 0x3C3C3C3Cu, od = (s.code[v] >> 2) & 0x3C3C3C3Cu;
-    asm("" : "+v"(ev), "+v"(od));
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      L.lv[8 * v + 2 * k] = *(const float *)(base + __builtin_amdgcn_ubfe(ev, 8 * k, 8));
-      L.lv[8 * v + 2 * k + 1] = *(const float *)(base + __builtin_amdgcn_ubfe(od, 8 * k, 8));
-    }
-  }
-
-  // Products of word v of a stage, rounded to bf16, as one 16-byte store.
-  __device__ __forceinline__ void write_word(const Levels &L, int v, uint16_t *sb) const {
+  // Full tiles: the decoded stage straight from its codes into LDS, with no
+  // table in memory: the block's 16 decoded values are built in registers as
+  // byte tables and each code selects its bf16 value with v_perm_b32
+  // (decode_table / decode_word; bit-identical to the product form).  Four
+  // 16-byte stores.
+  __device__ __forceinline__ void write_rt(const Stage &s, const Codebook &cb, uint16_t *sb) const {
+    const float ch = kDQ ? decode_constant(s.q, s.s2, mu) : s.s2;
+    const DecodeTable t = decode_table(cb, ch);
     uint16_t *dst = kTransW ? &sb[(ptid >> 2) * TLD + 32 * (ptid & 3)] : &sb[(ptid >> 1) * QLD + 32 * (ptid & 1)];
-    u32x4 o;
-#pragma unroll
-    for (int d = 0; d < 4; ++d)
-      o[d] = pack_bf16x2(decode_product(L.lv[8 * v + 2 * d], L.ch), decode_product(L.lv[8 * v + 2 * d + 1], L.ch));
-    *(u32x4 *)&dst[8 * v] = o;
-  }
-
-  // One steady-state decode step: the levels of the next stage (codes in
-  // `next`) word by word, each group of eight reads followed by the products
-  // of a word of the current stage, so that at most nine LDS operations are
-  // in flight (the counter tracks fifteen) and the products cover the reads'
-  // latency.
-  __device__ __forceinline__ void step_decode(const Stage &next, const float *lut, Levels &Lnext,
-                                              const Levels &Lcur, uint16_t *sb) const {
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
-      read_word(next, v, lut, Lnext);
-      write_word(Lcur, v, sb);
+      uint32_t o[4];
+      decode_word(s.code[v], t, o);
+      *(u32x4 *)&dst[8 * v] = u32x4{o[0], o[1], o[2], o[3]};
     }
-    Lnext.ch = kDQ ? decode_constant(next.q, next.s2, mu) : next.s2;
   }
 
-  // The decoded stage into LDS: fl32 products rounded to bf16, 16-byte stores.
+  // Partial tiles: the decoded stage into LDS, fl32 products rounded to bf16,
+  // 16-byte stores.
   __device__ __forceinline__ void store_w(const Levels &L, uint16_t *sb) const {
     uint16_t *dst = kTransW ? &sb[(ptid >> 2) * TLD + 32 * (ptid & 3)] : &sb[(ptid >> 1) * QLD + 32 * (ptid & 1)];
 #pragma unroll
@@ -306,15 +288,13 @@ struct Producer {
 // over their register sets with no conditions inside, so each set keeps fixed
 // registers.
 //
-// Full tiles: at step k the producers
-//   - read the levels of stage k+3 from the LDS table (codes fetched two
-//     steps earlier), to be used at the next step,
-//   - fetch the codes of stage k+5,
-//   - form the products of stage k+2 (levels read at the previous step) and
-//     write them to LDS.
-// Code sets rotate by three and level sets by two (unrolled by six).  The
-// caller fetches the codes of stages 0, 1 and 2 (fetch_first_codes), so that
-// their latency can overlap other work.
+// Full tiles: at step k the producers decode stage k+2 from its codes (fetched
+// three steps earlier) into LDS, then fetch the codes of stage k+5 into the
+// same registers.  Code sets rotate by three (unrolled by three).  The caller
+// fetches the codes of stages 0, 1 and 2 (fetch_first_codes), so that their
+// latency can overlap other work.  The decode reads no memory: with the level
+// table in LDS the producers' level reads (32 KB per step) competed with the
+// consumers' fragment reads.
 template <bool kTransW, bool kDQ>
 __device__ __forceinline__ void fetch_first_codes(const Producer<kTransW, kDQ> &p, int64_t nk, Stage &c0, Stage &c1,
                                                   Stage &c2) {
@@ -325,45 +305,32 @@ __device__ __forceinline__ void fetch_first_codes(const Producer<kTransW, kDQ> &
 
 template <bool kTransW, bool kDQ>
 __device__ __forceinline__ void producer_loop_full(const Producer<kTransW, kDQ> &p, int64_t nk, uint16_t (*sb)[QBN * QLD],
-                                                   const float *lut, Stage &c0, Stage &c1, Stage &c2) {
+                                                   Stage &c0, Stage &c1, Stage &c2, const Codebook &cb) {
   auto st = [nk](int64_t k) { return min(k, nk - 1); };
-  Levels l0, l1;
-  p.read_levels(c0, lut, l0);
-  p.store_w(l0, sb[0]);
+  p.write_rt(c0, cb, sb[0]);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
   wg_barrier();  // stage 0 ready
-  p.read_levels(c1, lut, l1);
-  p.store_w(l1, sb[1]);
-  p.read_levels(c2, lut, l0);  // stage 2, used at step 0
+  p.write_rt(c1, cb, sb[1]);
   p.template load_w<true>(st(3), c0);
   p.template load_w<true>(st(4), c1);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
-  wg_barrier();  // stage 1 ready; the consumers hold stage 0 in registers
-  // step K_: LCUR = levels of stage K_+2, LNEXT <- levels of stage K_+3 (codes
-  // in CREAD), CLOAD (codes of stage K_+2, levels already read) <- stage K_+5
-#define QGEMM_PRODUCER_STEP(K_, LCUR, LNEXT, CREAD, CLOAD)                           \
+  wg_barrier();  // stage 1 ready
+#define QGEMM_PRODUCER_STEP(K_, CUR)                                                   \
   if ((K_) < nk) {                                                                    \
-    p.template load_w<true>(st((K_) + 5), CLOAD);                                     \
+    p.write_rt(CUR, cb, sb[(K_) & 1]);                                                \
     __builtin_amdgcn_sched_barrier(0);                                                \
-    p.step_decode(CREAD, lut, LNEXT, LCUR, sb[(K_) & 1]);                             \
-    __builtin_amdgcn_sched_barrier(0);                                                \
+    p.template load_w<true>(st((K_) + 5), CUR);                                       \
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));                                   \
     wg_barrier();                                                                     \
   }
   int64_t kt = 0;
-  for (; kt + 6 <= nk; kt += 6) {
-    QGEMM_PRODUCER_STEP(kt, l0, l1, c0, c2)
-    QGEMM_PRODUCER_STEP(kt + 1, l1, l0, c1, c0)
-    QGEMM_PRODUCER_STEP(kt + 2, l0, l1, c2, c1)
-    QGEMM_PRODUCER_STEP(kt + 3, l1, l0, c0, c2)
-    QGEMM_PRODUCER_STEP(kt + 4, l0, l1, c1, c0)
-    QGEMM_PRODUCER_STEP(kt + 5, l1, l0, c2, c1)
+  for (; kt + 3 <= nk; kt += 3) {
+    QGEMM_PRODUCER_STEP(kt, c2)
+    QGEMM_PRODUCER_STEP(kt + 1, c0)
+    QGEMM_PRODUCER_STEP(kt + 2, c1)
   }
-  QGEMM_PRODUCER_STEP(kt, l0, l1, c0, c2)
-  QGEMM_PRODUCER_STEP(kt + 1, l1, l0, c1, c0)
-  QGEMM_PRODUCER_STEP(kt + 2, l0, l1, c2, c1)
-  QGEMM_PRODUCER_STEP(kt + 3, l1, l0, c0, c2)
-  QGEMM_PRODUCER_STEP(kt + 4, l0, l1, c1, c0)
+  QGEMM_PRODUCER_STEP(kt, c2)
+  QGEMM_PRODUCER_STEP(kt + 1, c0)
 #undef QGEMM_PRODUCER_STEP
 }
 
@@ -619,7 +586,7 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
   // full (per member): every row, column and contraction step of the tile is
   // in range and activation rows are 16-byte aligned
 
-  // Level table for the producers' decode.
+  // Level table for the producers' decode of partial tiles.
   if (tid < 16) lut[tid] = cb.v[tid];
   __syncthreads();
 
@@ -729,7 +696,7 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
       const Producer<kTransW, kDQ> p = member_producer<kTransW, kDQ>(mm, x, M, m0, c0, tid, mu);
       if (full) {
         if (mi > m_begin) fetch_first_codes(p, nk, pre0, pre1, pre2);  // the first member's went out early
-        producer_loop_full(p, nk, sb, lut, pre0, pre1, pre2);
+        producer_loop_full(p, nk, sb, pre0, pre1, pre2, cb);
       } else {
         producer_loop_partial(p, nk, sa, sb, lut);
       }
