@@ -105,8 +105,11 @@ __device__ __forceinline__ void decode_word(uint32_t c, const DecodeTable &t, ui
   const uint32_t c4 = c >> 4;
   // bytes of c: even codes n0, n2, n4, n6 in bits 0..3; bytes of c4: odd codes
   const uint32_t se = c & 0x07070707u, so = c4 & 0x07070707u;
-  const uint32_t xe = c & 0x08080808u, xo = c4 & 0x08080808u;
-  const uint32_t me = (xe << 5) - (xe >> 3), mo = (xo << 5) - (xo >> 3);  // 0x08 -> 0xFF per byte
+  // 0xFF in byte b where bit 3 of code b is set: v_perm selectors 8..11 give 0xFF or 0x00 from the
+  // top bit of bytes 1, 3, 5, 7 of {S0, S1}; the shifts bring bit 3 (even codes) or bit 7 (odd
+  // codes) of byte b there
+  const uint32_t me = __builtin_amdgcn_perm(c << 4, c << 12, 0x0B090A08u);
+  const uint32_t mo = __builtin_amdgcn_perm(c, c << 8, 0x0B090A08u);
   const uint32_t le = table_bytes(t.lo, se, me), he = table_bytes(t.hi, se, me);
   const uint32_t lq = table_bytes(t.lo, so, mo), hq = table_bytes(t.hi, so, mo);
   const uint32_t x0 = __builtin_amdgcn_perm(he, le, 0x05010400u);  // t[n0] | t[n2] << 16
