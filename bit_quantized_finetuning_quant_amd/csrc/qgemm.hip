@@ -14,7 +14,7 @@
 // Workgroup = 8 waves on a 256 x 128 output tile, contraction step 64:
 //   waves 0-3 (consumers) each own a 128 x 64 sub-tile: they read LDS, issue
 //     v_mfma_f32_32x32x16_bf16, and (full tiles) move the activation tile of
-//     stage k+2 from global memory straight into a 3-stage LDS ring with
+//     stage k+3 from global memory straight into a 3-stage LDS ring with
 //     global_load_lds_dwordx4, so no register ever holds it;
 //   waves 4-7 (producers) fetch the packed weight codes several steps ahead
 //     into registers and decode them (the weight tile is decoded once per
