@@ -47,9 +47,15 @@ def log(msg):
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def source_sha(name):
-    p = os.path.join(ROOT, "bit_quantized_finetuning_quant_amd", "csrc", name)
-    return hashlib.sha256(open(p, "rb").read()).hexdigest()[:16]
+# the sources the fused GEMM is compiled from
+QGEMM_SOURCES = ("qgemm.hip", "common.hpp", "launch.hpp")
+
+
+def source_sha(names):
+    h = hashlib.sha256()
+    for name in names:
+        h.update(open(os.path.join(ROOT, "bit_quantized_finetuning_quant_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
 
 
 def measured_traffic(kernel_tag):
@@ -63,7 +69,7 @@ def measured_traffic(kernel_tag):
         if ":" in line and not line.startswith("#"):
             k, v = line.split(":", 1)
             fields[k.strip()] = v.strip()
-    if fields.get("source_sha") != source_sha("qgemm.hip"):
+    if fields.get("source_sha") != source_sha(QGEMM_SOURCES):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
