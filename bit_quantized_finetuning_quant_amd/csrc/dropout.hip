@@ -31,6 +31,17 @@ namespace {
 constexpr uint64_t kPhiloxM0 = 0xD2E7470EE14C6C93ull, kPhiloxM1 = 0xCA5A826395121157ull;
 constexpr uint64_t kPhiloxW0 = 0x9E3779B97F4A7C15ull, kPhiloxW1 = 0xBB67AE8584CAA73Bull;
 
+// hi:lo = m * c (128 bits) from four 32 x 32 -> 64 products, each a v_mad_u64_u32 with the
+// running partial sum as its addend (no sum overflows 64 bits).
+__device__ __forceinline__ void mulhilo64(uint64_t m, uint64_t c, uint64_t &hi, uint64_t &lo) {
+  const uint32_t ml = (uint32_t)m, mh = (uint32_t)(m >> 32), cl = (uint32_t)c, ch = (uint32_t)(c >> 32);
+  const uint64_t p0 = (uint64_t)ml * cl;
+  const uint64_t t = (uint64_t)ml * ch + (p0 >> 32);
+  const uint64_t u = (uint64_t)mh * cl + (uint32_t)t;
+  lo = (u << 32) | (uint32_t)p0;
+  hi = (uint64_t)mh * ch + ((t >> 32) + (u >> 32));
+}
+
 __device__ __forceinline__ void philox4x64_10(uint64_t c0, uint64_t k0, uint64_t k1, uint64_t (&o)[4]) {
   uint64_t c1 = 0, c2 = 0, c3 = 0;
 #pragma unroll
@@ -39,8 +50,9 @@ __device__ __forceinline__ void philox4x64_10(uint64_t c0, uint64_t k0, uint64_t
       k0 += kPhiloxW0;
       k1 += kPhiloxW1;
     }
-    const uint64_t hi0 = __umul64hi(kPhiloxM0, c0), lo0 = kPhiloxM0 * c0;
-    const uint64_t hi1 = __umul64hi(kPhiloxM1, c2), lo1 = kPhiloxM1 * c2;
+    uint64_t hi0, lo0, hi1, lo1;
+    mulhilo64(kPhiloxM0, c0, hi0, lo0);
+    mulhilo64(kPhiloxM1, c2, hi1, lo1);
     const uint64_t n0 = hi1 ^ c1 ^ k0, n2 = hi0 ^ c3 ^ k1;
     c0 = n0;
     c1 = lo1;
