@@ -76,6 +76,13 @@ def test_few_token_sets_against_the_oracle(T):
     _check(cases, need_u=False)
 
 
+def test_few_token_set_of_four_members_rank_256():
+    announce("few-token set n_outs=(128, 64, 192, 128) n_in=256 T=4 r=256")
+    cases = _members((128, 64, 192, 128), 256, 4, 256, seed=77)
+    _check(cases)
+    _check(cases, need_u=False)
+
+
 def test_few_token_one_member_set_equals_the_single_linear_calls():
     torch = __import__("torch")
     announce("few-token set of one member vs single linear, 300x320 T=3 r=24")
