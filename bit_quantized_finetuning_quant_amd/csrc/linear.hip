@@ -27,8 +27,6 @@ namespace qlora {
 // ---------------------------------------------------------------------------
 // host side
 
-static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
 // ---- diagnostics: HIP events around the main kernel launches (events are
 // pooled, so a timed launch costs two event records and no event creation)
 namespace {

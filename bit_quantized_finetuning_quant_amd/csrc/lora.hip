@@ -90,8 +90,6 @@ __device__ __forceinline__ u32x4 frag(const uint16_t *lds, int base, int kk, int
   return u32x4{l2.x, l2.y, h2.x, h2.y};
 }
 
-__host__ __device__ constexpr int64_t cdiv_d(int64_t a, int64_t b) { return (a + b - 1) / b; }
-
 // Contraction steps fetched at once: 4 (a group of 256) or, when a split is
 // exactly 512 long and the launch fits one round of workgroups, all 8 of it,
 // so that the whole split arrives in one round trip (128 KB per workgroup in
