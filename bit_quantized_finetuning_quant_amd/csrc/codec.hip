@@ -208,12 +208,18 @@ __global__ __launch_bounds__(256) void mean_from_bins(const unsigned long long *
   }
   const int L = 32 * top + (32 - __clz(q[top]));
   const int s = max(L - 24, 64);
-  auto bit = [&](int i) -> uint32_t { return (i < 0 || i >= 384) ? 0u : (q[i >> 5] >> (i & 31)) & 1u; };
-  uint32_t m = 0;
-  for (int i = 0; i < 25; ++i) m |= bit(s + i) << i;
-  const uint32_t guard = bit(s - 1);
-  bool sticky = rem != 0;
-  for (int i = 0; i < s - 1 && !sticky; ++i) sticky = bit(i) != 0;
+  // the quotient's bits from bit i up (i >= 0), zero past the top limb
+  auto bits_from = [&](int i) -> uint64_t {
+    const int wi = i >> 5, bi = i & 31;
+    const uint64_t lo = wi < 12 ? q[wi] : 0u, mid = wi + 1 < 12 ? q[wi + 1] : 0u, hi = wi + 2 < 12 ? q[wi + 2] : 0u;
+    return ((lo | (mid << 32)) >> bi) | (bi ? hi << (64 - bi) : 0ull);
+  };
+  uint32_t m = (uint32_t)(bits_from(s) & 0x1FFFFFFull);  // bits s .. s + 24
+  const uint32_t guard = (uint32_t)(bits_from(s - 1) & 1ull);
+  // sticky: any bit below s - 1, or a nonzero remainder
+  const int sb_w = (s - 1) >> 5, sb_b = (s - 1) & 31;
+  bool sticky = rem != 0 || (sb_b && (q[sb_w] & ((1u << sb_b) - 1u)) != 0u);
+  for (int k = 0; k < sb_w && !sticky; ++k) sticky = q[k] != 0u;
   if (guard && (sticky || (m & 1u))) ++m;
   *mu = __uint_as_float(((uint32_t)(s - 64) << 23) + m);
 }
