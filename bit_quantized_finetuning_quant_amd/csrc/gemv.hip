@@ -143,6 +143,22 @@ struct FwdTile {
   UnitLoad L[kSteps];
 };
 
+// The weights of one forward pass: up to kMaxSetMembers linears that share x, their rows
+// concatenated (a single linear is a set of one).  Member m's rows start at 64-row block block0[m]
+// (every member but the last has a multiple of 64 rows); block0[m] is past every block for
+// m >= count.  y[m] and B[m] are its output and right factor.
+struct GemvFwdSet {
+  int count;
+  QWeight w[kMaxSetMembers];
+  int64_t block0[kMaxSetMembers + 1];
+  const uint16_t *B[kMaxSetMembers];
+  uint16_t *y[kMaxSetMembers];
+};
+
+__device__ __forceinline__ int fwd_member(const GemvFwdSet &s, int64_t p) {
+  return (p >= s.block0[1] ? 1 : 0) + (p >= s.block0[2] ? 1 : 0) + (p >= s.block0[3] ? 1 : 0);
+}
+
 template <int kSteps>
 __device__ __forceinline__ void fwd_load(const QWeight &w, int64_t n, int64_t unit0, int64_t U, int64_t kblk_row,
                                          FwdTile<kSteps> &f) {
@@ -190,19 +206,23 @@ __device__ __forceinline__ void fwd_store(const f32x4 &acc, float *dst, int64_t 
 
 template <int kUnits>
 __global__ __launch_bounds__(256) void gemv_fwd_main(const uint16_t *__restrict__ x,
-                                                     const uint16_t *__restrict__ xa, int T, QWeight w,
-                                                     const uint16_t *__restrict__ A, int r, float *__restrict__ y_part,
-                                                     float *__restrict__ u_part, int64_t spans, int64_t ablocks,
-                                                     Codebook cb) {
+                                                     const uint16_t *__restrict__ xa, int T, GemvFwdSet set,
+                                                     int64_t Ntot, const uint16_t *__restrict__ A, int r,
+                                                     float *__restrict__ y_part, float *__restrict__ u_part,
+                                                     int64_t spans, int64_t ablocks, Codebook cb) {
   typedef FwdShape<kUnits> S;
   constexpr int kSteps = S::kSteps, kXStride = S::kXStride, kASlice = S::kASlice;
   extern __shared__ __attribute__((aligned(16))) uint16_t xs[];  // [T][kXStride]
   __shared__ float lut[16];
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t K = w.n_in, N = w.n_out, U = K / 32, kblk_row = K / kBlock;
+  const int64_t K = set.w[0].n_in, U = K / 32, kblk_row = K / kBlock;
   const bool a_rows = (int64_t)blockIdx.x < ablocks;
   const int64_t blk = a_rows ? (int64_t)blockIdx.x : (int64_t)blockIdx.x - ablocks;
-  const int64_t span = blk % spans, p = blk / spans;
+  const int64_t span = blk % spans, pg = blk / spans;
+  // the member of this row block, and the block within it
+  const int m = a_rows ? 0 : fwd_member(set, pg);
+  const QWeight w = set.w[m];
+  const int64_t p = a_rows ? pg : pg - set.block0[m], N = w.n_out;
   const int64_t col0 = span * kUnits * 32;
   const int rl = lane & 15, g = lane >> 4;
   const int64_t unit0 = span * kUnits + g;
@@ -245,7 +265,13 @@ __global__ __launch_bounds__(256) void gemv_fwd_main(const uint16_t *__restrict_
     fwd_store(acc, u_part + span * T * r, r, row0 + rl, T, g);
     return;
   }
-  fwd_store(fwd_tile(f, w.dq ? *w.mu : 0.f, lut, xrow), y_part + span * T * N, N, row0 + rl, T, g);
+  const f32x4 acc = fwd_tile(f, w.dq ? *w.mu : 0.f, lut, xrow);
+  if (row0 + rl < rows) {  // concatenated row index, row stride Ntot
+    float *dst = y_part + span * T * Ntot + set.block0[m] * kFwdRows + row0 + rl;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * g + i < T) dst[(int64_t)(4 * g + i) * Ntot] = acc[i];
+  }
 }
 
 // Sum of `count` fp32 values p[0], p[stride], ... in index order, fetched
@@ -275,16 +301,22 @@ __device__ __forceinline__ float strided_sum(const float *p, int64_t stride, int
 template <int T>
 __global__ __launch_bounds__(256) void gemv_fwd_finish(const float *__restrict__ y_part,
                                                        const float *__restrict__ u_part, int64_t spans,
-                                                       const uint16_t *__restrict__ B, int r, float scale,
-                                                       float u_scale, int64_t N, uint16_t *__restrict__ y,
-                                                       uint16_t *__restrict__ u_out) {
+                                                       GemvFwdSet set, int r, int ld_u, float scale,
+                                                       float u_scale, int64_t Ntot, uint16_t *__restrict__ u_out) {
   __shared__ float us[T * 256];
   __shared__ float tmp[1024];
   __shared__ float red[4][T][64];
   const int tid = threadIdx.x;
   const int q = __builtin_amdgcn_readfirstlane(tid >> 6), c = tid & 63;
-  const int64_t n = (int64_t)blockIdx.x * 64 + c;
+  // this workgroup's member (Ntot = 0: u only, member 0) and its 64 rows
+  const int m = Ntot > 0 ? fwd_member(set, blockIdx.x) : 0;
+  const int64_t pl = (int64_t)blockIdx.x - set.block0[m];
+  const int64_t N = Ntot > 0 ? set.w[m].n_out : 0;
+  const uint16_t *__restrict__ B = set.B[m];
+  uint16_t *__restrict__ y = set.y[m];
+  const int64_t n = pl * 64 + c;
   const int64_t nc = n < N ? n : (N > 0 ? N - 1 : 0);
+  const int64_t gc = set.block0[m] * 64 + nc;  // row in the concatenated partials
   const bool vec = (r & 7) == 0;
   const int nch = r / 8;
   const uint16_t *brow = B + nc * r;
@@ -296,7 +328,7 @@ __global__ __launch_bounds__(256) void gemv_fwd_finish(const float *__restrict__
 #pragma unroll
     for (int i = 0; i < kYB; ++i)
 #pragma unroll
-      for (int t = 0; t < T; ++t) yp[i][t] = y_part[(min((int64_t)(q + 4 * i), spans - 1) * T + t) * N + nc];
+      for (int t = 0; t < T; ++t) yp[i][t] = y_part[(min((int64_t)(q + 4 * i), spans - 1) * T + t) * Ntot + gc];
     if (vec) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) b[i] = *(const u32x4 *)(brow + 8 * min(q + 4 * i, nch - 1));
@@ -304,10 +336,12 @@ __global__ __launch_bounds__(256) void gemv_fwd_finish(const float *__restrict__
   }
   const int E = T * r, S = E >= 256 ? 1 : 256 / E;
   const int64_t per = (spans + S - 1) / S;
+  // the member's u columns m r .. m r + r - 1 of the [span][t][ld_u] partials
+  const int64_t ustride = (int64_t)T * ld_u;
   for (int idx = tid; idx < E * S; idx += 256) {
     const int e = idx % E, sl = idx / E;
     const int64_t cnt = max((int64_t)0, min(per, (spans - sl + S - 1) / S));
-    tmp[idx] = strided_sum(u_part + sl * (int64_t)E + e, (int64_t)S * E, cnt);
+    tmp[idx] = strided_sum(u_part + sl * ustride + (int64_t)(e / r) * ld_u + m * r + e % r, (int64_t)S * ustride, cnt);
   }
   __syncthreads();
   for (int e = tid; e < E; e += 256) {
@@ -315,7 +349,7 @@ __global__ __launch_bounds__(256) void gemv_fwd_finish(const float *__restrict__
     for (int sl = 0; sl < S; ++sl) s += tmp[sl * E + e];
     const uint16_t h = to_bf16(s * u_scale);
     us[e] = bf(h);
-    if (blockIdx.x == 0) u_out[e] = h;
+    if (pl == 0) u_out[(e / r) * ld_u + m * r + e % r] = h;
   }
   if (N == 0) return;
   __syncthreads();
@@ -331,7 +365,7 @@ __global__ __launch_bounds__(256) void gemv_fwd_finish(const float *__restrict__
 #pragma unroll
     for (int i = 0; i < kYB; ++i)
 #pragma unroll
-      for (int t = 0; t < T; ++t) yp[i][t] = y_part[(min(s0 + 4 * kYB + 4 * i, spans - 1) * T + t) * N + nc];
+      for (int t = 0; t < T; ++t) yp[i][t] = y_part[(min(s0 + 4 * kYB + 4 * i, spans - 1) * T + t) * Ntot + gc];
   }
   if (vec) {
     for (int c0 = q;; c0 += 32) {
@@ -696,28 +730,68 @@ size_t bwd_lds_bytes(int T) {
   return std::max(tree, adapter);
 }
 
+constexpr int64_t kNoBlock = INT64_MAX / 4;  // block0 past every block
+
+// The forward of a set: Ntot concatenated rows (rows == false: u only, from A [r_total x K]); u
+// [T x r_total] holds every member's u (member m: columns m r ..).
 template <int T>
-hipError_t gemv_fwd_impl(const uint16_t *x, const uint16_t *xa, const QWeight &w, const uint16_t *A, const uint16_t *B,
-                         int r, float scale, float u_scale, uint16_t *y, uint16_t *u, float *part, const Codebook &cb,
-                         hipStream_t st) {
-  const int64_t N = w.n_out;
-  const GemvGeometry g = geometry(N, w.n_in, r);
-  const bool rows = y != nullptr;
+hipError_t gemv_fwd_run(const uint16_t *x, const uint16_t *xa, const GemvFwdSet &set, int64_t Ntot, bool rows,
+                        const uint16_t *A, int r, int r_total, float scale, float u_scale, uint16_t *u, float *part,
+                        const Codebook &cb, hipStream_t st) {
+  const GemvGeometry g = geometry(Ntot, set.w[0].n_in, r_total);
   const int64_t fblocks = rows ? g.fblocks : 0;
-  float *y_part = part, *u_part = part + g.fspans * T * N;
+  float *y_part = part, *u_part = part + g.fspans * T * Ntot;
   const size_t lds = (size_t)T * (g.funits * 32 + 8) * 2;
   const unsigned grid = (unsigned)(fblocks + g.ablocks);
   TimedLaunch tl;
   const bool timed = rows && timing_begin(st, tl, kTimedGemvFwd);
   if (g.funits == kFwdUnitsSmall)
-    gemv_fwd_main<kFwdUnitsSmall><<<grid, 256, lds, st>>>(x, xa, T, w, A, r, y_part, u_part, g.fspans, g.ablocks, cb);
+    gemv_fwd_main<kFwdUnitsSmall><<<grid, 256, lds, st>>>(x, xa, T, set, Ntot, A, r_total, y_part, u_part, g.fspans,
+                                                          g.ablocks, cb);
   else
-    gemv_fwd_main<kFwdUnitsLarge><<<grid, 256, lds, st>>>(x, xa, T, w, A, r, y_part, u_part, g.fspans, g.ablocks, cb);
+    gemv_fwd_main<kFwdUnitsLarge><<<grid, 256, lds, st>>>(x, xa, T, set, Ntot, A, r_total, y_part, u_part, g.fspans,
+                                                          g.ablocks, cb);
   if (timed) timing_end(st, tl);
-  const int64_t out_rows = rows ? N : 0;
+  const int64_t out_rows = rows ? Ntot : 0;
   const unsigned fg = (unsigned)std::max<int64_t>(1, cdiv(out_rows, 64));
-  gemv_fwd_finish<T><<<fg, 256, 0, st>>>(y_part, u_part, g.fspans, B, r, scale, u_scale, out_rows, y, u);
+  gemv_fwd_finish<T><<<fg, 256, 0, st>>>(y_part, u_part, g.fspans, set, r, r_total, scale, u_scale, out_rows, u);
   return hipGetLastError();
+}
+
+template <int T>
+hipError_t gemv_fwd_impl(const uint16_t *x, const uint16_t *xa, const QWeight &w, const uint16_t *A, const uint16_t *B,
+                         int r, float scale, float u_scale, uint16_t *y, uint16_t *u, float *part, const Codebook &cb,
+                         hipStream_t st) {
+  GemvFwdSet set{};
+  set.count = 1;
+  set.w[0] = w;
+  set.B[0] = B;
+  set.y[0] = y;
+  set.block0[0] = 0;
+  for (int i = 1; i <= kMaxSetMembers; ++i) set.block0[i] = kNoBlock;
+  for (int i = 1; i < kMaxSetMembers; ++i) set.w[i] = w;
+  return gemv_fwd_run<T>(x, xa, set, w.n_out, y != nullptr, A, r, r, scale, u_scale, u, part, cb, st);
+}
+
+template <int T>
+hipError_t gemv_fwd_set_impl(const uint16_t *x, const QWeight *w, int count, const uint16_t *A_set,
+                             const uint16_t *const *B, int r, float scale, uint16_t *const *y, uint16_t *u_set,
+                             float *part, const Codebook &cb, hipStream_t st) {
+  GemvFwdSet set{};
+  set.count = count;
+  int64_t blocks = 0, Ntot = 0;
+  for (int i = 0; i < kMaxSetMembers; ++i) {
+    set.w[i] = w[i < count ? i : 0];
+    set.B[i] = i < count ? B[i] : B[0];
+    set.y[i] = i < count ? y[i] : y[0];
+    set.block0[i] = i < count ? blocks : kNoBlock;
+    if (i < count) {
+      blocks += cdiv(w[i].n_out, kFwdRows);
+      Ntot += w[i].n_out;
+    }
+  }
+  set.block0[kMaxSetMembers] = kNoBlock;
+  return gemv_fwd_run<T>(x, x, set, Ntot, true, A_set, r, count * r, scale, 1.0f, u_set, part, cb, st);
 }
 
 template <int T>
@@ -761,6 +835,24 @@ hipError_t gemv_bwd_impl(const uint16_t *dy, const uint16_t *xa, const QWeight &
 }  // namespace
 
 bool gemv_applies(int64_t T, int64_t K) { return T >= 1 && T <= kGemvMaxT && K % 64 == 0; }
+
+bool gemv_set_fusable(const int64_t *N, int count) {
+  for (int i = 0; i + 1 < count; ++i)
+    if (N[i] % kFwdRows != 0) return false;
+  return true;
+}
+
+hipError_t launch_gemv_fwd_set(int64_t T, const uint16_t *x, const QWeight *w, int count, const uint16_t *A_set,
+                               const uint16_t *const *B, int r, float scale, uint16_t *const *y, uint16_t *u_set,
+                               float *part, const Codebook &cb, hipStream_t st) {
+  switch (T) {
+    case 1: return gemv_fwd_set_impl<1>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 2: return gemv_fwd_set_impl<2>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 3: return gemv_fwd_set_impl<3>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 4: return gemv_fwd_set_impl<4>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 size_t gemv_part_floats(int64_t T, int64_t N, int64_t K, int r) {
   const GemvGeometry g = geometry(N, K, r);

@@ -57,6 +57,13 @@ size_t gemv_part_floats(int64_t T, int64_t N, int64_t K, int r);
 hipError_t launch_gemv_fwd(int64_t T, const uint16_t *x, const uint16_t *xa, const QWeight &w, const uint16_t *A,
                            const uint16_t *B, int r, float scale, float u_scale, uint16_t *y, uint16_t *u,
                            float *part, const Codebook &cb, hipStream_t st);
+// Few-token forward of a projection set in one pass over the members' concatenated rows (every
+// member but the last a multiple of 64 rows: gemv_set_fusable); u_set [T x count r].  `part` holds
+// gemv_part_floats(T, sum of n_out, K, count r) floats.
+bool gemv_set_fusable(const int64_t *N, int count);
+hipError_t launch_gemv_fwd_set(int64_t T, const uint16_t *x, const QWeight *w, int count, const uint16_t *A_set,
+                               const uint16_t *const *B, int r, float scale, uint16_t *const *y, uint16_t *u_set,
+                               float *part, const Codebook &cb, hipStream_t st);
 hipError_t launch_gemv_bwd(int64_t T, const uint16_t *dy, const uint16_t *xa, const QWeight &w, const uint16_t *A,
                            const uint16_t *B, int r, float scale, float scale_ax, const uint32_t *keep,
                            const uint16_t *u, uint16_t *grad_x, float *grad_A, float *grad_B, float *part,

@@ -216,8 +216,10 @@ SetPlan plan_linear_set(int64_t T, int count, const int64_t *N, int64_t K, int r
   p.off_v = off;
   off += uv;
   p.off_part = off;
-  if (T <= kGemvMaxT) {  // members one by one: the largest member's scratch, one u block, count grad_x blocks
-    size_t part = 0;
+  if (T <= kGemvMaxT) {  // the fused forward's scratch or the largest member's, one u block, count grad_x blocks
+    int64_t ntot = 0;
+    for (int i = 0; i < count; ++i) ntot += N[i];
+    size_t part = gemv_part_floats(T, ntot, K, count * r);
     for (int i = 0; i < count; ++i) part = std::max(part, gemv_part_floats(T, N[i], K, r));
     off += align256(part * 4);
     p.off_um = off;
@@ -232,13 +234,18 @@ SetPlan plan_linear_set(int64_t T, int count, const int64_t *N, int64_t K, int r
   return p;
 }
 
-// Few-token sets: each member on the few-token path.  u moves between the
-// set's [T x count r] layout and one [T x r] block; grad_x is the fp32 sum,
-// in member order, of the members' bf16 terms (one more bf16 rounding).
+// Few-token sets.  The forward runs as one pass over the members' concatenated
+// rows when every member but the last has a multiple of 64 rows, else member by
+// member; the backward runs member by member.  Member by member, u moves
+// between the set's [T x count r] layout and one [T x r] block, and grad_x is
+// the fp32 sum, in member order, of the members' bf16 terms (one more bf16
+// rounding).
 static hipError_t set_fwd_few(const SetPlan &p, const uint16_t *x, const QWeight *w, const uint16_t *A_set,
                               const uint16_t *const *B, float scale, uint16_t *const *y, uint16_t *u, char *ws,
                               const Codebook &cb, hipStream_t st) {
   float *part = (float *)(ws + p.off_part);
+  if (gemv_set_fusable(p.N, p.count))
+    return launch_gemv_fwd_set(p.T, x, w, p.count, A_set, B, p.r, scale, y, u, part, cb, st);
   uint16_t *um = (uint16_t *)(ws + p.off_um);
   const int64_t rt = (int64_t)p.count * p.r;
   for (int i = 0; i < p.count; ++i) {

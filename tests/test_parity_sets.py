@@ -76,6 +76,15 @@ def test_few_token_sets_against_the_oracle(T):
     _check(cases, need_u=False)
 
 
+def test_few_token_set_with_unaligned_member():
+    """A member other than the last with a row count that is not a multiple of 64: the forward runs
+    member by member."""
+    announce("few-token set n_outs=(300, 256) n_in=256 T=2 r=8")
+    cases = _members((300, 256), 256, 2, 8, seed=78)
+    _check(cases)
+    _check(cases, need_u=False)
+
+
 def test_few_token_set_of_four_members_rank_256():
     announce("few-token set n_outs=(128, 64, 192, 128) n_in=256 T=4 r=256")
     cases = _members((128, 64, 192, 128), 256, 4, 256, seed=77)
