@@ -196,11 +196,13 @@ qlora_status qlora_linear_bwd(const uint16_t *dy, const uint16_t *x, int64_t T,
  * v_set [T x count r] the members' u / v side by side (member i: columns
  * i r ..).  B[i] [n_out_i x r], y[i] [T x n_out_i], dy[i] [T x n_out_i] and
  * grad_B[i] [n_out_i x r] are arrays of count device pointers; grad_x is the
- * gradient of x summed over the members (NULL skips it).  For T <= 4 the
- * members run one after another on the few-token kernels (the same results in
- * the same layouts; grad_x is then the fp32 sum of the members' bf16 terms,
- * rounded to bf16 once more).  No dropout here: each adapter draws its own
- * mask, so sets with dropout go per linear.                                 */
+ * gradient of x summed over the members (NULL skips it).  For T <= 4 the few-
+ * token kernels run the forward as one pass over the members' concatenated
+ * rows when every member but the last has a multiple of 64 rows (else member
+ * by member), and the backward member by member (grad_x is then the fp32 sum
+ * of the members' bf16 terms, rounded to bf16 once more); same layouts.  No
+ * dropout here: each adapter draws its own mask, so sets with dropout go per
+ * linear.                                                                   */
 size_t qlora_linear_set_workspace_bytes(int64_t T, int count, const int64_t *n_out, int64_t n_in, int r);
 
 qlora_status qlora_linear_set_fwd(const uint16_t *x, int64_t T, int count, const qlora_nf4_weight *q,
