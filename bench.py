@@ -484,6 +484,34 @@ def extra_measurements(torch, qlora, steps):
                                     "frac_hbm": reps * nw * step_bytes / t / 1e9 / PEAK_HBM_GBS,
                                     "us_per_fwd_bwd": t / (reps * nw) * 1e6, "shape": [N, K], "r": r}
     del graphs
+    # one token through q/k/v as a projection set (forward only, the decode step), against the
+    # three linears called one by one, over the same rotating weights
+    sets = [weights[i:i + 3] for i in range(0, nw - nw % 3, 3)]
+    A_set = bits(rng.standard_normal((3 * r, K)) * 0.01)
+    As = [A_set[i * r:(i + 1) * r].contiguous() for i in range(3)]
+    Bs = [B, B, B]
+    ys = [torch.empty((1, N), dtype=torch.bfloat16, device="cuda") for _ in range(3)]
+    u_set = torch.empty((1, 3 * r), dtype=torch.bfloat16, device="cuda")
+    ws_set = qlora.linear_set_workspace(1, [N, N, N], K, r)
+
+    def qkv_set():
+        for qs in sets:
+            qlora.linear_set_fwd(x, qs, A_set, Bs, 0.25, ys=ys, u_out=u_set, workspace=ws_set)
+
+    def qkv_one_by_one():
+        for qs in sets:
+            for i, q in enumerate(qs):
+                qlora.linear_fwd(x, q, As[i], B, 0.25, y=ys[i], u_out=u, workspace=ws)
+
+    qkv_set()
+    qkv_one_by_one()
+    t_set, _ = time_region(torch, qkv_set, reps)
+    t_one, _ = time_region(torch, qkv_one_by_one, reps)
+    set_bytes = 3 * fwd_bytes
+    out["gemv_T1_qkv_set_fwd"] = {"GB/s": reps * len(sets) * set_bytes / t_set / 1e9,
+                                  "frac_hbm": reps * len(sets) * set_bytes / t_set / 1e9 / PEAK_HBM_GBS,
+                                  "us_per_set_fwd": t_set / (reps * len(sets)) * 1e6,
+                                  "us_one_by_one": t_one / (reps * len(sets)) * 1e6, "shape": [3, N, K], "r": r}
     del weights
     # quantize one fp32 weight (reads 4 B/param, writes the packed format)
     w = torch.empty((N, K), dtype=torch.float32, device="cuda").normal_(0, 0.02)
