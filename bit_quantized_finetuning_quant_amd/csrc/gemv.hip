@@ -418,6 +418,24 @@ struct BwdGroup {
   float d[kRowsPerWave][T];
 };
 
+// The weights of one backward pass: up to kMaxSetMembers linears that share x, each with its dy,
+// B and grad_B (a single linear is a set of one).  Member m owns weight chunks chunk0[m] ..
+// chunk0[m + 1] - 1 and adapter workgroups part0[m] .. part0[m + 1] - 1; entries past the last
+// member are past every chunk and workgroup.
+struct GemvBwdSet {
+  int count;
+  QWeight w[kMaxSetMembers];
+  const uint16_t *dy[kMaxSetMembers];
+  const uint16_t *B[kMaxSetMembers];
+  float *grad_B[kMaxSetMembers];
+  int64_t chunk0[kMaxSetMembers + 1];
+  int64_t part0[kMaxSetMembers + 1];
+};
+
+__device__ __forceinline__ int bwd_member(const int64_t (&first)[kMaxSetMembers + 1], int64_t i) {
+  return (i >= first[1] ? 1 : 0) + (i >= first[2] ? 1 : 0) + (i >= first[3] ? 1 : 0);
+}
+
 template <int T>
 __device__ __forceinline__ void bwd_load(const QWeight &w, const uint16_t *dy, int64_t n0, int64_t unit,
                                          int64_t kblk_row, BwdGroup<T> &g) {
@@ -461,29 +479,34 @@ __device__ __forceinline__ void bwd_group(const BwdGroup<T> &g, float mu, const 
 // sums per token.  The waves' sums are added through LDS in a fixed tree
 // (halves added pairwise) and wave 0 writes the chunk's partial.
 template <int T>
-__device__ __forceinline__ void bwd_main_body(const uint16_t *__restrict__ dy, QWeight w,
-                                              const uint16_t *__restrict__ B, const uint16_t *__restrict__ u, int r,
+__device__ __forceinline__ void bwd_main_body(const GemvBwdSet &set, const uint16_t *__restrict__ u, int ld_u, int r,
                                               float scale, float *__restrict__ gx_part, float *__restrict__ v_part,
-                                              float *__restrict__ grad_B, int64_t spans, int64_t awgs, int groups,
-                                              int bsub, const Codebook &cb, float *smem, float *lut) {
+                                              int64_t spans, int64_t awgs, int groups, int bsub, const Codebook &cb,
+                                              float *smem, float *lut) {
   static_assert(T <= 4, "adapter partials hold at most two entries per thread");
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t K = w.n_in, N = w.n_out;
+  const int64_t K = set.w[0].n_in;
   if ((int64_t)blockIdx.x < awgs) {
-    // adapter rows [bid * bsub * 64, ...) of B, 64 at a time (r <= 256)
+    // adapter rows [b * bsub * 64, ...) of the member's B, 64 at a time (r <= 256); b is the
+    // workgroup's index within its member, bid its index among all adapter workgroups
     const int64_t bid = blockIdx.x;
+    const int m = bwd_member(set.part0, bid);
+    const int64_t b = bid - set.part0[m], N = set.w[m].n_out;
+    const uint16_t *__restrict__ dy = set.dy[m];
+    const uint16_t *__restrict__ B = set.B[m];
+    float *__restrict__ grad_B = set.grad_B[m];
     float *us = smem;                          // [T][r]
     float *ds = us + T * 256;                  // [T][64]
     uint16_t *bt = (uint16_t *)(ds + T * 64);  // [64][r]
     float *vt = (float *)(bt + kBRows * 256);  // [S][E]
     const int E = T * r, S = E >= kBwdThreads ? 1 : kBwdThreads / E;
-    for (int e = tid; e < T * r; e += kBwdThreads) us[e] = bf(u[e]);
+    for (int e = tid; e < T * r; e += kBwdThreads) us[e] = bf(u[(e / r) * ld_u + m * r + e % r]);
     constexpr int kV = (1024 + kBwdThreads - 1) / kBwdThreads;  // E * S <= max(E, threads) <= 1024
     float vacc[kV];  // entries idx = tid + kBwdThreads k of the [S][E] slices
 #pragma unroll
     for (int k = 0; k < kV; ++k) vacc[k] = 0.f;
     for (int sb = 0; sb < bsub; ++sb) {
-      const int64_t n0 = (bid * bsub + sb) * kBRows;
+      const int64_t n0 = (b * bsub + sb) * kBRows;
       if (n0 >= N) break;
       const int rows = (int)min((int64_t)kBRows, N - n0);
       __syncthreads();  // the previous block's tile is no longer read
@@ -537,11 +560,15 @@ __device__ __forceinline__ void bwd_main_body(const uint16_t *__restrict__ dy, Q
   __syncthreads();
   const int64_t U = K / 32, kblk_row = K / kBlock;
   const int64_t id = (int64_t)blockIdx.x - awgs;
-  const int64_t span = id % spans, chunk = id / spans;
+  const int64_t span = id % spans, chunk = id / spans;  // chunk among all members'
+  const int m = bwd_member(set.chunk0, chunk);
+  const QWeight w = set.w[m];
+  const uint16_t *__restrict__ dy = set.dy[m];
+  const int64_t N = w.n_out;
   const int64_t unit = span * kSpanUnits + lane;
   const bool valid = unit < U;
   const int64_t uc = valid ? unit : U - 1;
-  const int64_t n_base = (chunk * kBwdWaves + wave) * (int64_t)groups * kRowsPerWave;
+  const int64_t n_base = ((chunk - set.chunk0[m]) * kBwdWaves + wave) * (int64_t)groups * kRowsPerWave;
   const float mu = w.dq ? *w.mu : 0.f;
   float acc[T][32];
 #pragma unroll
@@ -583,27 +610,24 @@ __device__ __forceinline__ void bwd_main_body(const uint16_t *__restrict__ dy, Q
 }
 
 // One token fits in 128 registers, which keeps two workgroups on every CU.
-__global__ __launch_bounds__(kBwdThreads, 4) void gemv_bwd_main_t1(const uint16_t *__restrict__ dy, QWeight w,
-                                                           const uint16_t *__restrict__ B,
-                                                           const uint16_t *__restrict__ u, int r, float scale,
+__global__ __launch_bounds__(kBwdThreads, 4) void gemv_bwd_main_t1(GemvBwdSet set, const uint16_t *__restrict__ u,
+                                                           int ld_u, int r, float scale,
                                                            float *__restrict__ gx_part, float *__restrict__ v_part,
-                                                           float *__restrict__ grad_B, int64_t spans, int64_t awgs,
-                                                           int groups, int bsub, Codebook cb) {
+                                                           int64_t spans, int64_t awgs, int groups, int bsub,
+                                                           Codebook cb) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ float lut[16];
-  bwd_main_body<1>(dy, w, B, u, r, scale, gx_part, v_part, grad_B, spans, awgs, groups, bsub, cb, smem, lut);
+  bwd_main_body<1>(set, u, ld_u, r, scale, gx_part, v_part, spans, awgs, groups, bsub, cb, smem, lut);
 }
 
 template <int T>
-__global__ __launch_bounds__(kBwdThreads) void gemv_bwd_main(const uint16_t *__restrict__ dy, QWeight w,
-                                                     const uint16_t *__restrict__ B, const uint16_t *__restrict__ u,
+__global__ __launch_bounds__(kBwdThreads) void gemv_bwd_main(GemvBwdSet set, const uint16_t *__restrict__ u, int ld_u,
                                                      int r, float scale, float *__restrict__ gx_part,
-                                                     float *__restrict__ v_part, float *__restrict__ grad_B,
-                                                     int64_t spans, int64_t awgs, int groups, int bsub,
-                                                     Codebook cb) {
+                                                     float *__restrict__ v_part, int64_t spans, int64_t awgs,
+                                                     int groups, int bsub, Codebook cb) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ float lut[16];
-  bwd_main_body<T>(dy, w, B, u, r, scale, gx_part, v_part, grad_B, spans, awgs, groups, bsub, cb, smem, lut);
+  bwd_main_body<T>(set, u, ld_u, r, scale, gx_part, v_part, spans, awgs, groups, bsub, cb, smem, lut);
 }
 
 // Backward, pass 2: a workgroup per 64 columns; thread (jg, c) = (tid / 64,
@@ -614,12 +638,15 @@ __global__ __launch_bounds__(kBwdThreads) void gemv_bwd_main(const uint16_t *__r
 // partials of each thread, x) is issued before v is reduced.
 template <int T>
 __global__ __launch_bounds__(256) void gemv_bwd_finish(const float *__restrict__ gx_part, int64_t chunks,
-                                                       const float *__restrict__ v_part, int64_t vparts,
+                                                       const float *__restrict__ v_part, GemvBwdSet set,
                                                        const uint16_t *__restrict__ x, const uint16_t *__restrict__ A,
                                                        int r, int64_t K, float scale, const uint32_t *__restrict__ keep,
                                                        uint16_t *__restrict__ grad_x, float *__restrict__ grad_A) {
+  // r is a member's rank; A and grad_A have rt = count r rows (member m: rows m r ..), and v
+  // [T x rt] is member m's adapter partials summed in its columns
+  const int rt = set.count * r;
   __shared__ float tmp[1024];
-  __shared__ float vs[T * 256];
+  __shared__ float vs[T * 256 * kMaxSetMembers];
   __shared__ float red[4][T][64];
   const int tid = threadIdx.x;
   const int jg = __builtin_amdgcn_readfirstlane(tid >> 6), c = tid & 63;
@@ -630,7 +657,7 @@ __global__ __launch_bounds__(256) void gemv_bwd_finish(const float *__restrict__
 #pragma unroll
   for (int t = 0; t < T; ++t) xv[t] = bf(x[t * K + cc]);
 #pragma unroll
-  for (int i = 0; i < kFinBatch; ++i) a[i] = bf(A[(int64_t)min(jg + 4 * i, r - 1) * K + cc]);
+  for (int i = 0; i < kFinBatch; ++i) a[i] = bf(A[(int64_t)min(jg + 4 * i, rt - 1) * K + cc]);
   if (grad_x) {
 #pragma unroll
     for (int i = 0; i < kFinBatch; ++i)
@@ -638,19 +665,22 @@ __global__ __launch_bounds__(256) void gemv_bwd_finish(const float *__restrict__
       for (int t = 0; t < T; ++t) gv[i][t] = gx_part[(min((int64_t)(jg + 4 * i), chunks - 1) * T + t) * K + cc];
   }
   const int E = T * r, S = E >= 256 ? 1 : 256 / E;
-  const int64_t per = (vparts + S - 1) / S;
-  for (int idx = tid; idx < E * S; idx += 256) {
-    const int e = idx % E, sl = idx / E;
-    const int64_t cnt = max((int64_t)0, min(per, (vparts - sl + S - 1) / S));
-    tmp[idx] = strided_sum(v_part + sl * (int64_t)E + e, (int64_t)S * E, cnt);
+  for (int mm = 0; mm < set.count; ++mm) {
+    const int64_t p0 = set.part0[mm], vparts = set.part0[mm + 1] - p0;
+    const int64_t per = (vparts + S - 1) / S;
+    for (int idx = tid; idx < E * S; idx += 256) {
+      const int e = idx % E, sl = idx / E;
+      const int64_t cnt = max((int64_t)0, min(per, (vparts - sl + S - 1) / S));
+      tmp[idx] = strided_sum(v_part + (p0 + sl) * (int64_t)E + e, (int64_t)S * E, cnt);
+    }
+    __syncthreads();
+    for (int e = tid; e < E; e += 256) {
+      float s = 0.f;
+      for (int sl = 0; sl < S; ++sl) s += tmp[sl * E + e];
+      vs[(e / r) * rt + mm * r + e % r] = s;
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  for (int e = tid; e < E; e += 256) {
-    float s = 0.f;
-    for (int sl = 0; sl < S; ++sl) s += tmp[sl * E + e];
-    vs[e] = s;
-  }
-  __syncthreads();
   float g[T], lora[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) g[t] = lora[t] = 0.f;
@@ -658,19 +688,19 @@ __global__ __launch_bounds__(256) void gemv_bwd_finish(const float *__restrict__
 #pragma unroll
     for (int i = 0; i < kFinBatch; ++i) {
       const int j = j0 + 4 * i;
-      if (j < r) {
+      if (j < rt) {
         float ga = 0.f;
 #pragma unroll
         for (int t = 0; t < T; ++t) {
-          lora[t] = __builtin_fmaf(vs[t * r + j], a[i], lora[t]);
-          ga = __builtin_fmaf(vs[t * r + j], xv[t], ga);
+          lora[t] = __builtin_fmaf(vs[t * rt + j], a[i], lora[t]);
+          ga = __builtin_fmaf(vs[t * rt + j], xv[t], ga);
         }
         if (valid) grad_A[(int64_t)j * K + col] = scale * ga;
       }
     }
-    if (j0 + 4 * kFinBatch >= r) break;
+    if (j0 + 4 * kFinBatch >= rt) break;
 #pragma unroll
-    for (int i = 0; i < kFinBatch; ++i) a[i] = bf(A[(int64_t)min(j0 + 4 * kFinBatch + 4 * i, r - 1) * K + cc]);
+    for (int i = 0; i < kFinBatch; ++i) a[i] = bf(A[(int64_t)min(j0 + 4 * kFinBatch + 4 * i, rt - 1) * K + cc]);
   }
   if (grad_x) {
     for (int64_t c0 = jg;; c0 += 4 * kFinBatch) {
@@ -794,15 +824,43 @@ hipError_t gemv_fwd_set_impl(const uint16_t *x, const QWeight *w, int count, con
   return gemv_fwd_run<T>(x, x, set, Ntot, true, A_set, r, count * r, scale, 1.0f, u_set, part, cb, st);
 }
 
+// Work split of a backward set: the geometry of the concatenated rows decides the rows per wave
+// and the adapter blocks per workgroup; each member then takes whole chunks and adapter
+// workgroups of its own.
+struct BwdSplit {
+  GemvGeometry g;
+  int64_t chunks, parts;
+};
+
+static BwdSplit bwd_split(GemvBwdSet &set, int64_t K, int r) {
+  int64_t ntot = 0;
+  for (int i = 0; i < set.count; ++i) ntot += set.w[i].n_out;
+  BwdSplit b;
+  b.g = geometry(ntot, K, r);
+  const int64_t chunk_rows = (int64_t)kBwdWaves * b.g.groups * kRowsPerWave;
+  b.chunks = 0;
+  b.parts = 0;
+  for (int i = 0; i <= kMaxSetMembers; ++i) {
+    set.chunk0[i] = i <= set.count ? b.chunks : kNoBlock;
+    set.part0[i] = i <= set.count ? b.parts : kNoBlock;
+    if (i < set.count) {
+      b.chunks += cdiv(set.w[i].n_out, chunk_rows);
+      b.parts += cdiv(cdiv(set.w[i].n_out, kBRows), b.g.bsub);
+    }
+  }
+  // lookups compare against entries 1 .. 3: a member past the last never matches
+  for (int i = set.count + 1; i <= kMaxSetMembers; ++i) set.chunk0[i] = set.part0[i] = kNoBlock;
+  return b;
+}
+
 template <int T>
-hipError_t gemv_bwd_impl(const uint16_t *dy, const uint16_t *xa, const QWeight &w, const uint16_t *A,
-                         const uint16_t *B, int r, float scale, float scale_ax, const uint32_t *keep, const uint16_t *u,
-                         uint16_t *grad_x, float *grad_A, float *grad_B, float *part, const Codebook &cb,
-                         hipStream_t st) {
-  const int64_t N = w.n_out, K = w.n_in;
-  const GemvGeometry g = geometry(N, K, r);
-  const int64_t nf4_wgs = grad_x ? g.bspans * g.chunks : 0;
-  float *gx_part = part, *v_part = part + g.chunks * T * K;
+hipError_t gemv_bwd_run(GemvBwdSet &set, const uint16_t *xa, const uint16_t *A, int r, float scale, float scale_ax,
+                        const uint32_t *keep, const uint16_t *u, int ld_u, uint16_t *grad_x, float *grad_A,
+                        float *part, const Codebook &cb, hipStream_t st) {
+  const int64_t K = set.w[0].n_in;
+  const BwdSplit b = bwd_split(set, K, r);
+  const int64_t nf4_wgs = grad_x ? b.g.bspans * b.chunks : 0;
+  float *gx_part = part, *v_part = part + b.chunks * T * K;
   const size_t lds = bwd_lds_bytes(T);
   const void *fn = T == 1 ? (const void *)gemv_bwd_main_t1 : (const void *)gemv_bwd_main<T>;
   // the attribute is set once per device and token count (the size depends on T only), so
@@ -817,19 +875,52 @@ hipError_t gemv_bwd_impl(const uint16_t *dy, const uint16_t *xa, const QWeight &
       lds_set[dev][T] = true;
     }
   }
-  const unsigned grid = (unsigned)(nf4_wgs + g.bparts);  // adapter workgroups first
+  const unsigned grid = (unsigned)(nf4_wgs + b.parts);  // adapter workgroups first
   TimedLaunch tl;
   const bool timed = grad_x && timing_begin(st, tl, kTimedGemvBwd);
   if (T == 1)
-    gemv_bwd_main_t1<<<grid, kBwdThreads, lds, st>>>(dy, w, B, u, r, scale, gx_part, v_part, grad_B, g.bspans, g.bparts,
-                                             (int)g.groups, (int)g.bsub, cb);
+    gemv_bwd_main_t1<<<grid, kBwdThreads, lds, st>>>(set, u, ld_u, r, scale, gx_part, v_part, b.g.bspans, b.parts,
+                                                     (int)b.g.groups, (int)b.g.bsub, cb);
   else
-    gemv_bwd_main<T><<<grid, kBwdThreads, lds, st>>>(dy, w, B, u, r, scale, gx_part, v_part, grad_B, g.bspans, g.bparts,
-                                             (int)g.groups, (int)g.bsub, cb);
+    gemv_bwd_main<T><<<grid, kBwdThreads, lds, st>>>(set, u, ld_u, r, scale, gx_part, v_part, b.g.bspans, b.parts,
+                                                     (int)b.g.groups, (int)b.g.bsub, cb);
   if (timed) timing_end(st, tl);
-  gemv_bwd_finish<T><<<(unsigned)cdiv(K, 64), 256, 0, st>>>(gx_part, g.chunks, v_part, g.bparts, xa, A, r, K,
-                                                            scale_ax, keep, grad_x, grad_A);
+  gemv_bwd_finish<T><<<(unsigned)cdiv(K, 64), 256, 0, st>>>(gx_part, b.chunks, v_part, set, xa, A, r, K, scale_ax,
+                                                            keep, grad_x, grad_A);
   return hipGetLastError();
+}
+
+template <int T>
+hipError_t gemv_bwd_impl(const uint16_t *dy, const uint16_t *xa, const QWeight &w, const uint16_t *A,
+                         const uint16_t *B, int r, float scale, float scale_ax, const uint32_t *keep, const uint16_t *u,
+                         uint16_t *grad_x, float *grad_A, float *grad_B, float *part, const Codebook &cb,
+                         hipStream_t st) {
+  GemvBwdSet set{};
+  set.count = 1;
+  for (int i = 0; i < kMaxSetMembers; ++i) {
+    set.w[i] = w;
+    set.dy[i] = dy;
+    set.B[i] = B;
+    set.grad_B[i] = grad_B;
+  }
+  return gemv_bwd_run<T>(set, xa, A, r, scale, scale_ax, keep, u, r, grad_x, grad_A, part, cb, st);
+}
+
+template <int T>
+hipError_t gemv_bwd_set_impl(const uint16_t *const *dy, const uint16_t *x, const QWeight *w, int count,
+                             const uint16_t *A_set, const uint16_t *const *B, int r, float scale, const uint16_t *u_set,
+                             uint16_t *grad_x, float *grad_A_set, float *const *grad_B, float *part,
+                             const Codebook &cb, hipStream_t st) {
+  GemvBwdSet set{};
+  set.count = count;
+  for (int i = 0; i < kMaxSetMembers; ++i) {
+    const int k = i < count ? i : 0;
+    set.w[i] = w[k];
+    set.dy[i] = dy[k];
+    set.B[i] = B[k];
+    set.grad_B[i] = grad_B[k];
+  }
+  return gemv_bwd_run<T>(set, x, A_set, r, scale, scale, nullptr, u_set, count * r, grad_x, grad_A_set, part, cb, st);
 }
 
 }  // namespace
@@ -850,6 +941,34 @@ hipError_t launch_gemv_fwd_set(int64_t T, const uint16_t *x, const QWeight *w, i
     case 2: return gemv_fwd_set_impl<2>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
     case 3: return gemv_fwd_set_impl<3>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
     case 4: return gemv_fwd_set_impl<4>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+size_t gemv_set_part_floats(int64_t T, const int64_t *N, int count, int64_t K, int r) {
+  GemvBwdSet set{};
+  set.count = count;
+  int64_t ntot = 0;
+  for (int i = 0; i < count; ++i) {
+    set.w[i].n_out = N[i];
+    ntot += N[i];
+  }
+  const BwdSplit b = bwd_split(set, K, r);
+  const GemvGeometry gf = geometry(ntot, K, count * r);
+  const size_t fwd = (size_t)(gf.fspans * T * (ntot + (int64_t)count * r));
+  const size_t bwd = (size_t)(b.chunks * T * K + b.parts * T * r);
+  return std::max(fwd, bwd);
+}
+
+hipError_t launch_gemv_bwd_set(int64_t T, const uint16_t *const *dy, const uint16_t *x, const QWeight *w, int count,
+                               const uint16_t *A_set, const uint16_t *const *B, int r, float scale,
+                               const uint16_t *u_set, uint16_t *grad_x, float *grad_A_set, float *const *grad_B,
+                               float *part, const Codebook &cb, hipStream_t st) {
+  switch (T) {
+    case 1: return gemv_bwd_set_impl<1>(dy, x, w, count, A_set, B, r, scale, u_set, grad_x, grad_A_set, grad_B, part, cb, st);
+    case 2: return gemv_bwd_set_impl<2>(dy, x, w, count, A_set, B, r, scale, u_set, grad_x, grad_A_set, grad_B, part, cb, st);
+    case 3: return gemv_bwd_set_impl<3>(dy, x, w, count, A_set, B, r, scale, u_set, grad_x, grad_A_set, grad_B, part, cb, st);
+    case 4: return gemv_bwd_set_impl<4>(dy, x, w, count, A_set, B, r, scale, u_set, grad_x, grad_A_set, grad_B, part, cb, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -887,9 +1006,8 @@ hipError_t launch_gemv_bwd(int64_t T, const uint16_t *dy, const uint16_t *xa, co
 }
 
 // ---------------------------------------------------------------------------
-// Few-token projection sets: the members run one by one; these move u between
-// the set's [T x count r] layout and per-member [T x r] blocks, and add the
-// members' grad_x.
+// Few-token projection sets whose forward runs member by member: u moves
+// between the set's [T x count r] layout and one [T x r] block.
 
 namespace {
 
@@ -900,15 +1018,6 @@ __global__ __launch_bounds__(256) void copy_rows_u16(const uint16_t *__restrict_
     dst[(i / cols) * ld_dst + i % cols] = src[(i / cols) * ld_src + i % cols];
 }
 
-// out = bf16(sum over members of the bf16 inputs, added in member order in fp32)
-__global__ __launch_bounds__(256) void sum_bf16(SumInputs in, int64_t n, uint16_t *__restrict__ out) {
-  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
-    float s = 0.f;
-    for (int m = 0; m < in.count; ++m) s += bf(in.p[m][i]);
-    out[i] = to_bf16(s);
-  }
-}
-
 }  // namespace
 
 hipError_t launch_copy_rows(const uint16_t *src, int64_t ld_src, uint16_t *dst, int64_t ld_dst, int64_t rows,
@@ -917,12 +1026,6 @@ hipError_t launch_copy_rows(const uint16_t *src, int64_t ld_src, uint16_t *dst, 
   if (n <= 0) return hipSuccess;
   copy_rows_u16<<<(unsigned)std::min<int64_t>(cdiv(n, 256), 1024), 256, 0, st>>>(src, ld_src, dst, ld_dst, rows,
                                                                                     cols);
-  return hipGetLastError();
-}
-
-hipError_t launch_sum_bf16(const SumInputs &in, int64_t n, uint16_t *out, hipStream_t st) {
-  if (n <= 0) return hipSuccess;
-  sum_bf16<<<(unsigned)std::min<int64_t>(cdiv(n, 256), 1024), 256, 0, st>>>(in, n, out);
   return hipGetLastError();
 }
 

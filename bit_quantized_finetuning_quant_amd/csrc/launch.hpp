@@ -64,6 +64,14 @@ bool gemv_set_fusable(const int64_t *N, int count);
 hipError_t launch_gemv_fwd_set(int64_t T, const uint16_t *x, const QWeight *w, int count, const uint16_t *A_set,
                                const uint16_t *const *B, int r, float scale, uint16_t *const *y, uint16_t *u_set,
                                float *part, const Codebook &cb, hipStream_t st);
+// Few-token backward of a projection set in one pass over every member's rows: grad_x summed over
+// the members, grad_A_set [count r x K], grad_B[i]; u_set and v [T x count r].  `part` holds
+// gemv_set_part_floats(T, n_out, count, K, r) floats (which also covers launch_gemv_fwd_set).
+size_t gemv_set_part_floats(int64_t T, const int64_t *N, int count, int64_t K, int r);
+hipError_t launch_gemv_bwd_set(int64_t T, const uint16_t *const *dy, const uint16_t *x, const QWeight *w, int count,
+                               const uint16_t *A_set, const uint16_t *const *B, int r, float scale,
+                               const uint16_t *u_set, uint16_t *grad_x, float *grad_A_set, float *const *grad_B,
+                               float *part, const Codebook &cb, hipStream_t st);
 hipError_t launch_gemv_bwd(int64_t T, const uint16_t *dy, const uint16_t *xa, const QWeight &w, const uint16_t *A,
                            const uint16_t *B, int r, float scale, float scale_ax, const uint32_t *keep,
                            const uint16_t *u, uint16_t *grad_x, float *grad_A, float *grad_B, float *part,
@@ -183,26 +191,19 @@ struct AdamwScalars {
 hipError_t launch_adamw(float *param, uint16_t *param_bf16, const float *grad, float *exp_avg, float *exp_avg_sq,
                         int64_t n, const AdamwScalars &s, hipStream_t st);
 
-// Few-token sets (gemv.hip helpers): a strided 2-D copy of bf16 rows, and the
-// sum of up to kMaxSetMembers bf16 arrays (fp32 adds in member order, one bf16
-// rounding).
-struct SumInputs {
-  int count;
-  const uint16_t *p[kMaxSetMembers];
-};
+// Few-token sets (gemv.hip helper): a strided 2-D copy of bf16 rows.
 hipError_t launch_copy_rows(const uint16_t *src, int64_t ld_src, uint16_t *dst, int64_t ld_dst, int64_t rows,
                             int64_t cols, hipStream_t st);
-hipError_t launch_sum_bf16(const SumInputs &in, int64_t n, uint16_t *out, hipStream_t st);
 
 // Projection sets (linear.hip): members share x [T x K] and the adapter
 // rank r; A_set [count r x K] holds the members' A back to back, u_set and
-// v_set are [T x count r].  For T <= kGemvMaxT the members run one by one on
-// the few-token path, with per-member u and grad_x blocks in the workspace.
+// v_set are [T x count r].  For T <= kGemvMaxT the few-token kernels run the
+// set (a [T x r] u block in the workspace for the member-by-member forward).
 struct SetPlan {
   int64_t T, K;
   int r, count;
   int64_t N[kMaxSetMembers];
-  size_t off_u, off_v, off_part, off_um, off_gx, total;
+  size_t off_u, off_v, off_part, off_um, total;
 };
 SetPlan plan_linear_set(int64_t T, int count, const int64_t *N, int64_t K, int r);
 hipError_t launch_linear_set_fwd(const SetPlan &p, const uint16_t *x, const QWeight *w, const uint16_t *A_set,

@@ -216,19 +216,15 @@ SetPlan plan_linear_set(int64_t T, int count, const int64_t *N, int64_t K, int r
   p.off_v = off;
   off += uv;
   p.off_part = off;
-  if (T <= kGemvMaxT) {  // the fused forward's scratch or the largest member's, one u block, count grad_x blocks
-    int64_t ntot = 0;
-    for (int i = 0; i < count; ++i) ntot += N[i];
-    size_t part = gemv_part_floats(T, ntot, K, count * r);
+  if (T <= kGemvMaxT) {  // the set passes' scratch or the largest member's, and one u block
+    size_t part = gemv_set_part_floats(T, N, count, K, r);
     for (int i = 0; i < count; ++i) part = std::max(part, gemv_part_floats(T, N[i], K, r));
     off += align256(part * 4);
     p.off_um = off;
     off += align256((size_t)T * r * 2);
-    p.off_gx = off;
-    off += (size_t)count * align256((size_t)T * K * 2);
   } else {
     off += align256(lora_set_part_floats(T, count, N, K, r) * 4);
-    p.off_um = p.off_gx = off;
+    p.off_um = off;
   }
   p.total = off;
   return p;
@@ -236,10 +232,9 @@ SetPlan plan_linear_set(int64_t T, int count, const int64_t *N, int64_t K, int r
 
 // Few-token sets.  The forward runs as one pass over the members' concatenated
 // rows when every member but the last has a multiple of 64 rows, else member by
-// member; the backward runs member by member.  Member by member, u moves
-// between the set's [T x count r] layout and one [T x r] block, and grad_x is
-// the fp32 sum, in member order, of the members' bf16 terms (one more bf16
-// rounding).
+// member (u moves between the set's [T x count r] layout and one [T x r]
+// block); the backward is one pass over every member's rows, which sums grad_x
+// over the members in its fp32 partials.
 static hipError_t set_fwd_few(const SetPlan &p, const uint16_t *x, const QWeight *w, const uint16_t *A_set,
                               const uint16_t *const *B, float scale, uint16_t *const *y, uint16_t *u, char *ws,
                               const Codebook &cb, hipStream_t st) {
@@ -262,25 +257,18 @@ static hipError_t set_bwd_few(const SetPlan &p, const uint16_t *const *dy, const
                               uint16_t *grad_x, float *grad_A_set, float *const *grad_B, char *ws, const Codebook &cb,
                               hipStream_t st) {
   float *part = (float *)(ws + p.off_part);
-  uint16_t *um = (uint16_t *)(ws + p.off_um);
-  const int64_t rt = (int64_t)p.count * p.r;
-  const size_t gx_bytes = align256((size_t)p.T * p.K * 2);
-  SumInputs sum{};
-  sum.count = p.count;
-  for (int i = 0; i < p.count; ++i) {
-    const uint16_t *A = A_set + (int64_t)i * p.r * p.K;
-    hipError_t e = u ? launch_copy_rows(u + (int64_t)i * p.r, rt, um, p.r, p.T, p.r, st)
-                     : launch_gemv_fwd(p.T, x, x, w[i], A, B[i], p.r, scale, 1.0f, nullptr, um, part, cb, st);
-    if (e != hipSuccess) return e;
-    uint16_t *gx = nullptr;
-    if (grad_x) gx = p.count == 1 ? grad_x : (uint16_t *)(ws + p.off_gx + (size_t)i * gx_bytes);
-    sum.p[i] = gx;
-    e = launch_gemv_bwd(p.T, dy[i], x, w[i], A, B[i], p.r, scale, scale, nullptr, um, gx, grad_A_set + (int64_t)i * p.r * p.K,
-                        grad_B[i], part, cb, st);
-    if (e != hipSuccess) return e;
+  if (!u) {  // recompute u_set member by member (u only), through one [T x r] block
+    uint16_t *um = (uint16_t *)(ws + p.off_um), *us = (uint16_t *)(ws + p.off_u);
+    const int64_t rt = (int64_t)p.count * p.r;
+    for (int i = 0; i < p.count; ++i) {
+      hipError_t e = launch_gemv_fwd(p.T, x, x, w[i], A_set + (int64_t)i * p.r * p.K, B[i], p.r, scale, 1.0f, nullptr, um,
+                                     part, cb, st);
+      if (e == hipSuccess) e = launch_copy_rows(um, p.r, us + (int64_t)i * p.r, rt, p.T, p.r, st);
+      if (e != hipSuccess) return e;
+    }
+    u = us;
   }
-  if (!grad_x || p.count == 1) return hipSuccess;
-  return launch_sum_bf16(sum, p.T * p.K, grad_x, st);
+  return launch_gemv_bwd_set(p.T, dy, x, w, p.count, A_set, B, p.r, scale, u, grad_x, grad_A_set, grad_B, part, cb, st);
 }
 
 hipError_t launch_linear_set_fwd(const SetPlan &p, const uint16_t *x, const QWeight *w, const uint16_t *A_set,

@@ -199,8 +199,8 @@ qlora_status qlora_linear_bwd(const uint16_t *dy, const uint16_t *x, int64_t T,
  * gradient of x summed over the members (NULL skips it).  For T <= 4 the few-
  * token kernels run the forward as one pass over the members' concatenated
  * rows when every member but the last has a multiple of 64 rows (else member
- * by member), and the backward member by member (grad_x is then the fp32 sum
- * of the members' bf16 terms, rounded to bf16 once more); same layouts.  No
+ * by member), and the backward as one pass over every member's rows (grad_x
+ * summed over the members in fp32, rounded to bf16 once); same layouts.  No
  * dropout here: each adapter draws its own mask, so sets with dropout go per
  * linear.                                                                   */
 size_t qlora_linear_set_workspace_bytes(int64_t T, int count, const int64_t *n_out, int64_t n_in, int r);

@@ -177,7 +177,7 @@ def test_projection_set_validation_before_any_launch():
     lib = qlora.lib()
     n_outs = (ctypes.c_int64 * 3)(512, 256, 256)
     assert lib.qlora_linear_set_workspace_bytes(16, 3, n_outs, 256, 8) > 0
-    assert lib.qlora_linear_set_workspace_bytes(4, 3, n_outs, 256, 8) > 0  # few-token: members one by one
+    assert lib.qlora_linear_set_workspace_bytes(4, 3, n_outs, 256, 8) > 0  # few-token set kernels
     assert lib.qlora_linear_set_workspace_bytes(0, 3, n_outs, 256, 8) == 0
     assert lib.qlora_linear_set_workspace_bytes(16, 5, n_outs, 256, 8) == 0
     assert lib.qlora_linear_set_workspace_bytes(16, 3, n_outs, 100, 8) == 0

@@ -69,7 +69,8 @@ def test_sets_against_the_oracle(n_outs, n_in, T, r):
 
 @pytest.mark.parametrize("T", [1, 2, 3, 4])
 def test_few_token_sets_against_the_oracle(T):
-    """T <= 4: the members run one by one on the few-token kernels; same layouts, same bar."""
+    """T <= 4: the few-token kernels run the set (the forward over the concatenated rows, the
+    backward over every member's rows and adapter blocks in one pass); same layouts, same bar."""
     announce(f"few-token set n_outs=(256, 192, 320) n_in=384 T={T} r=16")
     cases = _members((256, 192, 320), 384, T, 16, seed=40 + T)
     _check(cases)
@@ -78,7 +79,7 @@ def test_few_token_sets_against_the_oracle(T):
 
 def test_few_token_set_with_unaligned_member():
     """A member other than the last with a row count that is not a multiple of 64: the forward runs
-    member by member."""
+    member by member, the backward still as one pass."""
     announce("few-token set n_outs=(300, 256) n_in=256 T=2 r=8")
     cases = _members((300, 256), 256, 2, 8, seed=78)
     _check(cases)
