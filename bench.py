@@ -512,6 +512,30 @@ def extra_measurements(torch, qlora, steps):
                                   "frac_hbm": reps * len(sets) * set_bytes / t_set / 1e9 / PEAK_HBM_GBS,
                                   "us_per_set_fwd": t_set / (reps * len(sets)) * 1e6,
                                   "us_one_by_one": t_one / (reps * len(sets)) * 1e6, "shape": [3, N, K], "r": r}
+    # and back through the set (grad_x summed over q/k/v), against the three backwards one by one
+    ga_set = torch.empty((3 * r, K), dtype=torch.float32, device="cuda")
+    gbs = [torch.empty((N, r), dtype=torch.float32, device="cuda") for _ in range(3)]
+    dys = [dy, dy, dy]
+
+    def qkv_set_bwd():
+        for qs in sets:
+            qlora.linear_set_bwd(dys, x, qs, A_set, Bs, 0.25, u=u_set, grad_x=gx, grad_A_set=ga_set, grad_Bs=gbs,
+                                 workspace=ws_set)
+
+    def qkv_bwd_one_by_one():
+        for qs in sets:
+            for i, q in enumerate(qs):
+                qlora.linear_bwd(dy, x, q, As[i], B, 0.25, u=u, grad_x=gx, grad_A=ga, grad_B=gbs[i], workspace=ws)
+
+    qkv_set_bwd()
+    qkv_bwd_one_by_one()
+    t_set, _ = time_region(torch, qkv_set_bwd, reps)
+    t_one, _ = time_region(torch, qkv_bwd_one_by_one, reps)
+    set_bytes = 3 * bwd_bytes
+    out["gemv_T1_qkv_set_bwd"] = {"GB/s": reps * len(sets) * set_bytes / t_set / 1e9,
+                                  "frac_hbm": reps * len(sets) * set_bytes / t_set / 1e9 / PEAK_HBM_GBS,
+                                  "us_per_set_bwd": t_set / (reps * len(sets)) * 1e6,
+                                  "us_one_by_one": t_one / (reps * len(sets)) * 1e6, "shape": [3, N, K], "r": r}
     del weights
     # quantize one fp32 weight (reads 4 B/param, writes the packed format)
     w = torch.empty((N, K), dtype=torch.float32, device="cuda").normal_(0, 0.02)

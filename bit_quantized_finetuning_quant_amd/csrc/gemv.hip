@@ -478,7 +478,7 @@ __device__ __forceinline__ void bwd_group(const BwdGroup<T> &g, float mu, const 
 // (chunk * kBwdWaves + w) * groups * kRowsPerWave and accumulates 32 column
 // sums per token.  The waves' sums are added through LDS in a fixed tree
 // (halves added pairwise) and wave 0 writes the chunk's partial.
-template <int T>
+template <int T, bool Multi>
 __device__ __forceinline__ void bwd_main_body(const GemvBwdSet &set, const uint16_t *__restrict__ u, int ld_u, int r,
                                               float scale, float *__restrict__ gx_part, float *__restrict__ v_part,
                                               int64_t spans, int64_t awgs, int groups, int bsub, const Codebook &cb,
@@ -490,7 +490,7 @@ __device__ __forceinline__ void bwd_main_body(const GemvBwdSet &set, const uint1
     // adapter rows [b * bsub * 64, ...) of the member's B, 64 at a time (r <= 256); b is the
     // workgroup's index within its member, bid its index among all adapter workgroups
     const int64_t bid = blockIdx.x;
-    const int m = bwd_member(set.part0, bid);
+    const int m = Multi ? bwd_member(set.part0, bid) : 0;
     const int64_t b = bid - set.part0[m], N = set.w[m].n_out;
     const uint16_t *__restrict__ dy = set.dy[m];
     const uint16_t *__restrict__ B = set.B[m];
@@ -561,7 +561,7 @@ __device__ __forceinline__ void bwd_main_body(const GemvBwdSet &set, const uint1
   const int64_t U = K / 32, kblk_row = K / kBlock;
   const int64_t id = (int64_t)blockIdx.x - awgs;
   const int64_t span = id % spans, chunk = id / spans;  // chunk among all members'
-  const int m = bwd_member(set.chunk0, chunk);
+  const int m = Multi ? bwd_member(set.chunk0, chunk) : 0;
   const QWeight w = set.w[m];
   const uint16_t *__restrict__ dy = set.dy[m];
   const int64_t N = w.n_out;
@@ -609,7 +609,9 @@ __device__ __forceinline__ void bwd_main_body(const GemvBwdSet &set, const uint1
   }
 }
 
-// One token fits in 128 registers, which keeps two workgroups on every CU.
+// One token fits in 128 registers, which keeps two workgroups on every CU.  Multi: more than one
+// member (a single linear reads member 0 without the lookup).
+template <bool Multi>
 __global__ __launch_bounds__(kBwdThreads, 4) void gemv_bwd_main_t1(GemvBwdSet set, const uint16_t *__restrict__ u,
                                                            int ld_u, int r, float scale,
                                                            float *__restrict__ gx_part, float *__restrict__ v_part,
@@ -617,17 +619,17 @@ __global__ __launch_bounds__(kBwdThreads, 4) void gemv_bwd_main_t1(GemvBwdSet se
                                                            Codebook cb) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ float lut[16];
-  bwd_main_body<1>(set, u, ld_u, r, scale, gx_part, v_part, spans, awgs, groups, bsub, cb, smem, lut);
+  bwd_main_body<1, Multi>(set, u, ld_u, r, scale, gx_part, v_part, spans, awgs, groups, bsub, cb, smem, lut);
 }
 
-template <int T>
+template <int T, bool Multi>
 __global__ __launch_bounds__(kBwdThreads) void gemv_bwd_main(GemvBwdSet set, const uint16_t *__restrict__ u, int ld_u,
                                                      int r, float scale, float *__restrict__ gx_part,
                                                      float *__restrict__ v_part, int64_t spans, int64_t awgs,
                                                      int groups, int bsub, Codebook cb) {
   extern __shared__ __attribute__((aligned(16))) float smem[];
   __shared__ float lut[16];
-  bwd_main_body<T>(set, u, ld_u, r, scale, gx_part, v_part, spans, awgs, groups, bsub, cb, smem, lut);
+  bwd_main_body<T, Multi>(set, u, ld_u, r, scale, gx_part, v_part, spans, awgs, groups, bsub, cb, smem, lut);
 }
 
 // Backward, pass 2: a workgroup per 64 columns; thread (jg, c) = (tid / 64,
@@ -853,7 +855,7 @@ static BwdSplit bwd_split(GemvBwdSet &set, int64_t K, int r) {
   return b;
 }
 
-template <int T>
+template <int T, bool Multi>
 hipError_t gemv_bwd_run(GemvBwdSet &set, const uint16_t *xa, const uint16_t *A, int r, float scale, float scale_ax,
                         const uint32_t *keep, const uint16_t *u, int ld_u, uint16_t *grad_x, float *grad_A,
                         float *part, const Codebook &cb, hipStream_t st) {
@@ -862,8 +864,8 @@ hipError_t gemv_bwd_run(GemvBwdSet &set, const uint16_t *xa, const uint16_t *A, 
   const int64_t nf4_wgs = grad_x ? b.g.bspans * b.chunks : 0;
   float *gx_part = part, *v_part = part + b.chunks * T * K;
   const size_t lds = bwd_lds_bytes(T);
-  const void *fn = T == 1 ? (const void *)gemv_bwd_main_t1 : (const void *)gemv_bwd_main<T>;
-  // the attribute is set once per device and token count (the size depends on T only), so
+  const void *fn = T == 1 ? (const void *)gemv_bwd_main_t1<Multi> : (const void *)gemv_bwd_main<T, Multi>;
+  // the attribute is set once per device, token count and variant (the size depends on T only), so
   // calls under stream capture make no attribute call
   static bool lds_set[64][kGemvMaxT + 1] = {};
   int dev = 0;
@@ -879,10 +881,10 @@ hipError_t gemv_bwd_run(GemvBwdSet &set, const uint16_t *xa, const uint16_t *A, 
   TimedLaunch tl;
   const bool timed = grad_x && timing_begin(st, tl, kTimedGemvBwd);
   if (T == 1)
-    gemv_bwd_main_t1<<<grid, kBwdThreads, lds, st>>>(set, u, ld_u, r, scale, gx_part, v_part, b.g.bspans, b.parts,
+    gemv_bwd_main_t1<Multi><<<grid, kBwdThreads, lds, st>>>(set, u, ld_u, r, scale, gx_part, v_part, b.g.bspans, b.parts,
                                                      (int)b.g.groups, (int)b.g.bsub, cb);
   else
-    gemv_bwd_main<T><<<grid, kBwdThreads, lds, st>>>(set, u, ld_u, r, scale, gx_part, v_part, b.g.bspans, b.parts,
+    gemv_bwd_main<T, Multi><<<grid, kBwdThreads, lds, st>>>(set, u, ld_u, r, scale, gx_part, v_part, b.g.bspans, b.parts,
                                                      (int)b.g.groups, (int)b.g.bsub, cb);
   if (timed) timing_end(st, tl);
   gemv_bwd_finish<T><<<(unsigned)cdiv(K, 64), 256, 0, st>>>(gx_part, b.chunks, v_part, set, xa, A, r, K, scale_ax,
@@ -903,7 +905,7 @@ hipError_t gemv_bwd_impl(const uint16_t *dy, const uint16_t *xa, const QWeight &
     set.B[i] = B;
     set.grad_B[i] = grad_B;
   }
-  return gemv_bwd_run<T>(set, xa, A, r, scale, scale_ax, keep, u, r, grad_x, grad_A, part, cb, st);
+  return gemv_bwd_run<T, false>(set, xa, A, r, scale, scale_ax, keep, u, r, grad_x, grad_A, part, cb, st);
 }
 
 template <int T>
@@ -920,7 +922,10 @@ hipError_t gemv_bwd_set_impl(const uint16_t *const *dy, const uint16_t *x, const
     set.B[i] = B[k];
     set.grad_B[i] = grad_B[k];
   }
-  return gemv_bwd_run<T>(set, x, A_set, r, scale, scale, nullptr, u_set, count * r, grad_x, grad_A_set, part, cb, st);
+  return count > 1 ? gemv_bwd_run<T, true>(set, x, A_set, r, scale, scale, nullptr, u_set, count * r, grad_x,
+                                            grad_A_set, part, cb, st)
+                   : gemv_bwd_run<T, false>(set, x, A_set, r, scale, scale, nullptr, u_set, count * r, grad_x,
+                                            grad_A_set, part, cb, st);
 }
 
 }  // namespace
