@@ -77,6 +77,32 @@ def test_few_token_sets_against_the_oracle(T):
     _check(cases, need_u=False)
 
 
+@pytest.mark.parametrize("T", [1, 3])
+def test_few_token_set_backward_without_grad_x(T):
+    """Skipping grad_x leaves only the adapter workgroups: grad_A_set and every grad_B are the
+    same bits as in the call that also produces grad_x, and within the bar of the oracle."""
+    announce(f"few-token set without grad_x n_outs=(192, 256, 128) n_in=256 T={T} r=32")
+    cases = _members((192, 256, 128), 256, T, 32, seed=90 + T)
+    qs, ys, u, gx, ga, gbs = _run_set(cases)
+    s = cases[0].scale
+    x = dev_bf16(cases[0].x)
+    a_set = dev_bf16(np.concatenate([c.a for c in cases], axis=0))
+    bs = [dev_bf16(c.b) for c in cases]
+    dys = [dev_bf16(c.dy) for c in cases]
+    gx2, ga2, gbs2 = qlora.linear_set_bwd(dys, x, qs, a_set, bs, s, u=u, need_grad_x=False)
+    __import__("torch").cuda.synchronize()
+    assert gx2 is None
+    assert np.array_equal(host(ga2), host(ga))
+    for g2, g in zip(gbs2, gbs):
+        assert np.array_equal(host(g2), host(g))
+    r = 32
+    for i, c in enumerate(cases):
+        wh = oracle.dequantize(oracle.quantize(c.w, c.n_out, c.n_in))
+        g = oracle.backward(c.dy, c.x, wh, c.a, c.b, s)
+        assert normwise_rel(host(ga2)[i * r:(i + 1) * r], g[1]) <= NORMWISE_TOL
+        assert normwise_rel(host(gbs2[i]), g[2]) <= NORMWISE_TOL
+
+
 def test_few_token_set_with_unaligned_member():
     """A member other than the last with a row count that is not a multiple of 64: the forward runs
     member by member, the backward still as one pass."""
