@@ -7,6 +7,7 @@ of the square root and the eps.
 """
 
 import math
+from fractions import Fraction
 
 import numpy as np
 import pytest
@@ -148,3 +149,63 @@ def test_step_scalars_from_their_definitions():
     assert s1["decay"] == np.float32(1 - 1e-2 * 0.1)
     assert s1["c_m"] == np.float32(0.1) and s1["c_v"] == np.float32(1 - 0.999)
     assert s1["b1"] == np.float32(0.9) and s1["b2"] == np.float32(0.999)
+
+
+def _rn32_exact(q: Fraction) -> float:
+    """Round a positive rational to the nearest fp32 value, ties to even (normal range)."""
+    assert q > 0
+    e = q.numerator.bit_length() - q.denominator.bit_length()
+    while Fraction(2) ** e > q:
+        e -= 1
+    while Fraction(2) ** (e + 1) <= q:
+        e += 1
+    # q = m * 2^(e - 23) with 2^23 <= m < 2^24
+    m = q / Fraction(2) ** (e - 23)
+    n = m.numerator // m.denominator
+    rem = m - n
+    if rem > Fraction(1, 2) or (rem == Fraction(1, 2) and n % 2 == 1):
+        n += 1
+    return float(Fraction(n) * Fraction(2) ** (e - 23))
+
+
+def _rn32_sqrt_exact(q: Fraction) -> float:
+    """Round sqrt(q) of a positive rational to the nearest fp32 value, ties to even."""
+    assert q > 0
+    e = 0
+    while Fraction(4) ** e > q:
+        e -= 1
+    while Fraction(4) ** (e + 1) <= q:
+        e += 1
+    # sqrt(q) = s * 2^(e - 23) with 2^23 <= s < 2^24, s^2 = X
+    x = q / Fraction(4) ** (e - 23)
+    y = 4 * x  # (2 s)^2
+    t2 = math.isqrt(y.numerator // y.denominator)  # floor(2 s)
+    n = t2 // 2
+    if t2 % 2 == 1:  # s >= n + 1/2
+        if Fraction(t2 * t2) != y or n % 2 == 1:
+            n += 1
+    return float(Fraction(n) * Fraction(2) ** (e - 23))
+
+
+def test_step_scalars_equal_the_exact_values_rounded_once():
+    """step_size = RN32(lr / (1 - b1^t)) and bc2_sqrt = RN32(sqrt(1 - b2^t)) of the exact real
+    numbers the fp64 hyperparameters stand for, with b^t an exact rational power (no libm): the
+    oracle's fp64 evaluation must round to the same fp32 values at every step the tests run and
+    over a sweep of steps and hyperparameters.  A power taken at the wrong step, a missing
+    square root or a swapped beta fails it."""
+    from fractions import Fraction as F
+
+    cases = [(1e-2, 0.9, 0.999), (2e-4, 0.9, 0.999), (1e-2, 0.8, 0.99), (1e-3, 0.95, 0.9999), (3e-4, 0.5, 0.75)]
+    steps = list(range(1, 41)) + [63, 64, 100, 255, 999, 1000, 1001, 1002, 1003, 4096, 10000]
+    for lr, b1, b2 in cases:
+        fb1, fb2 = F(b1), F(b2)
+        p1, p2 = F(1), F(1)
+        t_prev = 0
+        for t in steps:
+            p1 *= fb1 ** (t - t_prev)
+            p2 *= fb2 ** (t - t_prev)
+            t_prev = t
+            s = oracle.step_scalars(t, lr, b1, b2, 1e-8, 0.0)
+            assert float(s["step_size"]) == _rn32_exact(F(lr) / (1 - p1)), (lr, b1, t)
+            assert float(s["bc2_sqrt"]) == _rn32_sqrt_exact(1 - p2), (b2, t)
+        assert float(oracle.step_scalars(1, lr, b1, b2, 1e-8, 0.1)["decay"]) == _rn32_exact(1 - F(lr) * F(0.1))

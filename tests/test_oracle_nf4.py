@@ -27,12 +27,51 @@ def _brute_code(x: float, c1: float, cb) -> int:
     return best[1]
 
 
+def _plain_absmax(flat) -> list:
+    """max |x| of every zero-padded 64-element block, over Python floats (independent of numpy)."""
+    vals = [float(v) for v in np.asarray(flat, np.float32).reshape(-1).tolist()]
+    vals += [0.0] * (-len(vals) % BLOCK)
+    return [max(abs(v) for v in vals[b:b + BLOCK]) for b in range(0, len(vals), BLOCK)]
+
+
 def _check_codes_brute(flat: np.ndarray):
+    """Codes by exact rational argmin, with the block constant formed independently of the oracle;
+    the oracle's own block constants must equal it."""
     cb = oracle.nf4_codebook()
+    c1_plain = _plain_absmax(flat)
     c1 = oracle.block_absmax(flat)
+    assert [float(v) for v in c1.tolist()] == c1_plain
     codes = oracle.nearest_codes(flat, c1).reshape(-1)
     for i, x in enumerate(flat.tolist()):
-        assert codes[i] == _brute_code(x, float(c1[i // BLOCK]), cb), (i, x, float(c1[i // BLOCK]))
+        assert codes[i] == _brute_code(x, c1_plain[i // BLOCK], cb), (i, x, c1_plain[i // BLOCK])
+
+
+def test_block_absmax_is_the_largest_magnitude():
+    """The block constant is the largest magnitude of the block ("qlora" entry, section "como
+    funciona"), also where that element is negative, and padding never raises it."""
+    rng = np.random.default_rng(13)
+    blocks = (rng.standard_normal((6, BLOCK)) * 0.02).astype(np.float32)
+    # the largest magnitude of every block is a negative element; one block is all negative,
+    # one holds a single non-zero (negative) element, one is -0 and +0 only
+    for b in range(6):
+        blocks[b, (7 * b) % BLOCK] = np.float32(-0.5 - 0.125 * b)
+    blocks[1] = -np.abs(blocks[1])
+    blocks[2] = 0.0
+    blocks[2, 33] = np.float32(-3e-39)  # subnormal
+    blocks[3] = -0.0
+    blocks[3, ::2] = 0.0
+    flat = blocks.reshape(-1)
+    want = _plain_absmax(flat)
+    assert want[0] == 0.5 and want[2] == float(np.float32(3e-39)) and want[3] == 0.0
+    assert [float(v) for v in oracle.block_absmax(flat).tolist()] == want
+    _check_codes_brute(flat)
+    codes = oracle.nearest_codes(flat, oracle.block_absmax(flat))
+    for b in (0, 1, 2, 4, 5):
+        assert codes[b, int(np.argmin(blocks[b]))] == 0  # the negative absmax element maps to -1
+    # a ragged tail: 64 + 10 elements, the tail block padded with zeros that do not count
+    tail = np.concatenate([blocks[0], np.array([-0.25] + [0.01] * 9, np.float32)])
+    assert [float(v) for v in oracle.block_absmax(tail).tolist()] == _plain_absmax(tail) == [0.5, 0.25]
+    _check_codes_brute(tail)
 
 
 def test_nearest_code_brute_force_random():
