@@ -160,6 +160,74 @@ def _ptr(t) -> int:
     return 0 if t is None else int(t.data_ptr())
 
 
+# The C ABI takes plain pointers and cannot check the extent of a buffer, so every tensor is
+# checked here before a call: dtype, contiguity, exact shape, and the device of the packed
+# weight.  A wrong tensor raises ValueError and nothing is launched.
+_DT = {}  # dtype sets of the checks, filled on first use (torch is imported lazily)
+
+
+def _dtypes():
+    if not _DT:
+        torch = _torch()
+        _DT.update(tensor=torch.Tensor, bf16=(torch.bfloat16, torch.int16), f32=(torch.float32,))
+    return _DT
+
+
+class _Args:
+    """Checks of one call's tensors: dtype, exact shape and contiguity as each is named, then
+    (done) that every one of them is on the packed weight's CUDA device."""
+
+    __slots__ = ("device", "named")
+
+    def __init__(self, device):
+        self.device = device
+        self.named = []
+
+    def _check(self, t, name: str, shape, kind: str) -> None:
+        dt = _dtypes()
+        if not isinstance(t, dt["tensor"]):
+            raise ValueError(f"{name} must be a tensor")
+        if t.dtype not in dt[kind]:
+            raise ValueError(f"{name} must be {' or '.join(str(d) for d in dt[kind])}, not {t.dtype}")
+        if t.shape != shape:
+            raise ValueError(f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+        self.named.append((name, t))
+
+    def bf16(self, t, name: str, shape) -> None:
+        self._check(t, name, shape, "bf16")
+
+    def f32(self, t, name: str, shape) -> None:
+        self._check(t, name, shape, "f32")
+
+    def done(self) -> None:
+        dev = self.device
+        for name, t in self.named:
+            if t.device != dev or dev.type != "cuda":
+                raise ValueError(f"{name} must be on {dev}, not {t.device}")
+
+
+def _workspace(ws, device, need: int) -> int:
+    """Checks a caller's workspace (a contiguous uint8 CUDA tensor of at least `need` bytes)."""
+    torch = _torch()
+    if not isinstance(ws, torch.Tensor) or ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous 1-D uint8 tensor")
+    if ws.device.type != "cuda" or ws.device != device:
+        raise ValueError(f"workspace must be on {device}, not {ws.device}")
+    if ws.numel() < need:
+        raise ValueError(f"workspace holds {ws.numel()} bytes, the call needs {need}")
+    return ws.numel()
+
+
+def _weight_device(q) -> "object":
+    """The device of a packed weight (every call's tensors must be on it)."""
+    dev = q.codes.device
+    if dev.type != "cuda":
+        raise ValueError(f"the packed weight must be on a CUDA device, not {dev}")
+    return dev
+
+
 @dataclass
 class NF4Weight:
     """Device buffers of a packed weight (allocated by torch, owned by this object).
@@ -212,12 +280,16 @@ def quantize(w, out: NF4Weight = None, workspace=None, stream=None, double_quant
     if dtype is None:
         raise ValueError("w must be float32 or bfloat16")
     n_out, n_in = w.shape
+    if w.device.type != "cuda":
+        raise ValueError(f"w must be on a CUDA device, not {w.device}")
     q = out if out is not None else NF4Weight.empty(n_out, n_in, w.device, double_quant=double_quant)
+    if (q.n_out, q.n_in) != (n_out, n_in) or _weight_device(q) != w.device:
+        raise ValueError("out must be a packed weight of w's shape on w's device")
     wsb = quantize_workspace_bytes(n_out, n_in)
     ws = workspace if workspace is not None else torch.empty(wsb, dtype=torch.uint8, device=w.device)
+    wsn = _workspace(ws, w.device, wsb)
     st = q.struct()
-    _check(lib().qlora_quantize(_ptr(w), dtype, ctypes.byref(st), _ptr(ws), ws.numel() * ws.element_size(),
-                                _stream(stream)), "qlora_quantize")
+    _check(lib().qlora_quantize(_ptr(w), dtype, ctypes.byref(st), _ptr(ws), wsn, _stream(stream)), "qlora_quantize")
     q.last_workspace = ws
     return q
 
@@ -229,7 +301,11 @@ def status_read(workspace, stream=None) -> int:
 
 def dequantize(q: NF4Weight, out=None, stream=None):
     torch = _torch()
-    y = out if out is not None else torch.empty((q.n_out, q.n_in), dtype=torch.bfloat16, device=q.codes.device)
+    dev = _weight_device(q)
+    y = out if out is not None else torch.empty((q.n_out, q.n_in), dtype=torch.bfloat16, device=dev)
+    chk = _Args(dev)
+    chk.bf16(y, "out", (q.n_out, q.n_in))
+    chk.done()
     st = q.struct()
     _check(lib().qlora_dequantize(ctypes.byref(st), _ptr(y), _stream(stream)), "qlora_dequantize")
     return y
@@ -240,6 +316,11 @@ def dequantize_many(qs, outs=None, stream=None):
     torch = _torch()
     outs = outs if outs is not None else [torch.empty((q.n_out, q.n_in), dtype=torch.bfloat16, device=q.codes.device)
                                           for q in qs]
+    _check_list(outs, len(qs), "outs")
+    for i, (q, o) in enumerate(zip(qs, outs)):
+        chk = _Args(_weight_device(q))
+        chk.bf16(o, f"outs[{i}]", (q.n_out, q.n_in))
+        chk.done()
     st = (NF4WeightStruct * len(qs))(*[q.struct() for q in qs])
     ptrs = (ctypes.c_void_p * len(outs))(*[_ptr(o) for o in outs])
     _check(lib().qlora_dequantize_many(st, len(qs), ptrs, _stream(stream)), "qlora_dequantize_many")
@@ -256,35 +337,72 @@ def linear_fwd(x, q: NF4Weight, A, B, scale: float, y=None, u_out=None, save_u=T
                stream=None):
     """y = x W_hat^T + scale (x A^T) B^T (bf16); returns (y, u or None)."""
     torch = _torch()
-    T = x.shape[0]
-    r = A.shape[0]
-    y = y if y is not None else torch.empty((T, q.n_out), dtype=torch.bfloat16, device=x.device)
+    T, r = _linear_dims(x, A, q)
+    dev = _weight_device(q)
+    chk = _Args(dev)
+    chk.bf16(x, "x", (T, q.n_in))
+    chk.bf16(A, "A", (r, q.n_in))
+    chk.bf16(B, "B", (q.n_out, r))
+    y = y if y is not None else torch.empty((T, q.n_out), dtype=torch.bfloat16, device=dev)
+    chk.bf16(y, "y", (T, q.n_out))
     if save_u and u_out is None:
-        u_out = torch.empty((T, r), dtype=torch.bfloat16, device=x.device)
-    ws = workspace if workspace is not None else linear_workspace(T, q.n_out, q.n_in, r, x.device)
+        u_out = torch.empty((T, r), dtype=torch.bfloat16, device=dev)
+    if u_out is not None:
+        chk.bf16(u_out, "u_out", (T, r))
+    chk.done()
+    ws = workspace if workspace is not None else linear_workspace(T, q.n_out, q.n_in, r, dev)
+    wsb = _workspace(ws, dev, linear_workspace_bytes(T, q.n_out, q.n_in, r))
     st = q.struct()
     _check(lib().qlora_linear_fwd(_ptr(x), T, ctypes.byref(st), _ptr(A), _ptr(B), r, float(scale), _ptr(y),
-                                  _ptr(u_out), _ptr(ws), ws.numel(), _stream(stream)), "qlora_linear_fwd")
+                                  _ptr(u_out), _ptr(ws), wsb, _stream(stream)), "qlora_linear_fwd")
     return y, u_out
+
+
+def _linear_dims(x, A, q):
+    """(T, r) of a linear call from x [T x n_in] and A [r x n_in]."""
+    if x.dim() != 2 or A.dim() != 2:
+        raise ValueError("x and A must be 2-D")
+    return int(x.shape[0]), int(A.shape[0])
+
+
+def _check_bwd(dy, x, q, A, B, u, chk):
+    T, r = _linear_dims(x, A, q)
+    chk.bf16(dy, "dy", (T, q.n_out))
+    chk.bf16(x, "x", (T, q.n_in))
+    chk.bf16(A, "A", (r, q.n_in))
+    chk.bf16(B, "B", (q.n_out, r))
+    if u is not None:
+        chk.bf16(u, "u", (T, r))
+    return T, r
+
+
+def _check_grads(grad_x, grad_A, grad_B, T, r, q, chk):
+    if grad_x is not None:
+        chk.bf16(grad_x, "grad_x", (T, q.n_in))
+    chk.f32(grad_A, "grad_A", (r, q.n_in))
+    chk.f32(grad_B, "grad_B", (q.n_out, r))
+    chk.done()
 
 
 def linear_bwd(dy, x, q: NF4Weight, A, B, scale: float, u=None, need_grad_x=True, grad_x=None, grad_A=None,
                grad_B=None, workspace=None, stream=None):
     """Returns (grad_x bf16 or None, grad_A fp32, grad_B fp32)."""
     torch = _torch()
-    T = x.shape[0]
-    r = A.shape[0]
-    dev = x.device
+    dev = _weight_device(q)
+    chk = _Args(dev)
+    T, r = _check_bwd(dy, x, q, A, B, u, chk)
     if need_grad_x and grad_x is None:
         grad_x = torch.empty((T, q.n_in), dtype=torch.bfloat16, device=dev)
     if not need_grad_x:
         grad_x = None
     grad_A = grad_A if grad_A is not None else torch.empty((r, q.n_in), dtype=torch.float32, device=dev)
     grad_B = grad_B if grad_B is not None else torch.empty((q.n_out, r), dtype=torch.float32, device=dev)
+    _check_grads(grad_x, grad_A, grad_B, T, r, q, chk)
     ws = workspace if workspace is not None else linear_workspace(T, q.n_out, q.n_in, r, dev)
+    wsb = _workspace(ws, dev, linear_workspace_bytes(T, q.n_out, q.n_in, r))
     st = q.struct()
     _check(lib().qlora_linear_bwd(_ptr(dy), _ptr(x), T, ctypes.byref(st), _ptr(A), _ptr(B), r, float(scale),
-                                  _ptr(u), _ptr(grad_x), _ptr(grad_A), _ptr(grad_B), _ptr(ws), ws.numel(),
+                                  _ptr(u), _ptr(grad_x), _ptr(grad_A), _ptr(grad_B), _ptr(ws), wsb,
                                   _stream(stream)), "qlora_linear_bwd")
     return grad_x, grad_A, grad_B
 
@@ -326,14 +444,24 @@ def linear_fwd_dropout(x, q: NF4Weight, A, B, scale: float, p: float, seed: int,
                        workspace=None, stream=None):
     """linear_fwd with LoRA dropout of probability p on the adapter input (mask from seed)."""
     torch = _torch()
-    T, r = x.shape[0], A.shape[0]
-    y = y if y is not None else torch.empty((T, q.n_out), dtype=torch.bfloat16, device=x.device)
+    T, r = _linear_dims(x, A, q)
+    dev = _weight_device(q)
+    chk = _Args(dev)
+    chk.bf16(x, "x", (T, q.n_in))
+    chk.bf16(A, "A", (r, q.n_in))
+    chk.bf16(B, "B", (q.n_out, r))
+    y = y if y is not None else torch.empty((T, q.n_out), dtype=torch.bfloat16, device=dev)
+    chk.bf16(y, "y", (T, q.n_out))
     if save_u and u_out is None:
-        u_out = torch.empty((T, r), dtype=torch.bfloat16, device=x.device)
-    ws = workspace if workspace is not None else linear_dropout_workspace(T, q.n_out, q.n_in, r, x.device)
+        u_out = torch.empty((T, r), dtype=torch.bfloat16, device=dev)
+    if u_out is not None:
+        chk.bf16(u_out, "u_out", (T, r))
+    chk.done()
+    ws = workspace if workspace is not None else linear_dropout_workspace(T, q.n_out, q.n_in, r, dev)
+    wsb = _workspace(ws, dev, linear_dropout_workspace_bytes(T, q.n_out, q.n_in, r))
     st = q.struct()
     _check(lib().qlora_linear_fwd_dropout(_ptr(x), T, ctypes.byref(st), _ptr(A), _ptr(B), r, float(scale), float(p),
-                                          int(seed), _ptr(y), _ptr(u_out), _ptr(ws), ws.numel(), _stream(stream)),
+                                          int(seed), _ptr(y), _ptr(u_out), _ptr(ws), wsb, _stream(stream)),
            "qlora_linear_fwd_dropout")
     return y, u_out
 
@@ -342,25 +470,34 @@ def linear_bwd_dropout(dy, x, q: NF4Weight, A, B, scale: float, p: float, seed: 
                        grad_x=None, grad_A=None, grad_B=None, workspace=None, stream=None):
     """linear_bwd with the forward's dropout mask (same p and seed)."""
     torch = _torch()
-    T, r, dev = x.shape[0], A.shape[0], x.device
+    dev = _weight_device(q)
+    chk = _Args(dev)
+    T, r = _check_bwd(dy, x, q, A, B, u, chk)
     if need_grad_x and grad_x is None:
         grad_x = torch.empty((T, q.n_in), dtype=torch.bfloat16, device=dev)
     if not need_grad_x:
         grad_x = None
     grad_A = grad_A if grad_A is not None else torch.empty((r, q.n_in), dtype=torch.float32, device=dev)
     grad_B = grad_B if grad_B is not None else torch.empty((q.n_out, r), dtype=torch.float32, device=dev)
+    _check_grads(grad_x, grad_A, grad_B, T, r, q, chk)
     ws = workspace if workspace is not None else linear_dropout_workspace(T, q.n_out, q.n_in, r, dev)
+    wsb = _workspace(ws, dev, linear_dropout_workspace_bytes(T, q.n_out, q.n_in, r))
     st = q.struct()
     _check(lib().qlora_linear_bwd_dropout(_ptr(dy), _ptr(x), T, ctypes.byref(st), _ptr(A), _ptr(B), r, float(scale),
                                           float(p), int(seed), _ptr(u), _ptr(grad_x), _ptr(grad_A), _ptr(grad_B),
-                                          _ptr(ws), ws.numel(), _stream(stream)), "qlora_linear_bwd_dropout")
+                                          _ptr(ws), wsb, _stream(stream)), "qlora_linear_bwd_dropout")
     return grad_x, grad_A, grad_B
 
 
 def dropout_mask(x, p: float, seed: int, stream=None):
     """(keep_words [ceil(T/32) x K] int32, x_drop [T x K] bf16) for a [T x K] bf16 tensor."""
     torch = _torch()
+    if x.dim() != 2:
+        raise ValueError("x must be 2-D")
     T, K = x.shape
+    chk = _Args(x.device)
+    chk.bf16(x, "x", (T, K))
+    chk.done()
     keep = torch.empty(((T + 31) // 32, K), dtype=torch.int32, device=x.device)
     xd = torch.empty((T, K), dtype=torch.bfloat16, device=x.device)
     _check(lib().qlora_dropout_mask(_ptr(x), T, K, float(p), int(seed), _ptr(keep), _ptr(xd), _stream(stream)),
@@ -387,36 +524,87 @@ def linear_set_fwd(x, qs, A_set, Bs, scale: float, ys=None, u_out=None, save_u=T
     """Projection set forward: y_i = x W_hat_i^T + scale (x A_i^T) B_i^T for every member, with
     A_set [count r x n_in] the members' A matrices back to back.  Returns (ys, u_set or None)."""
     torch = _torch()
-    T, count = x.shape[0], len(qs)
-    r = A_set.shape[0] // count
-    ys = ys if ys is not None else [torch.empty((T, q.n_out), dtype=torch.bfloat16, device=x.device) for q in qs]
+    T, count, r, dev, chk = _set_dims(x, qs, A_set)
+    _check_list(Bs, count, "Bs")
+    for i, (q, b) in enumerate(zip(qs, Bs)):
+        chk.bf16(b, f"Bs[{i}]", (q.n_out, r))
+    ys = ys if ys is not None else [torch.empty((T, q.n_out), dtype=torch.bfloat16, device=dev) for q in qs]
+    _check_list(ys, count, "ys")
+    for i, (q, y) in enumerate(zip(qs, ys)):
+        chk.bf16(y, f"ys[{i}]", (T, q.n_out))
     if save_u and u_out is None:
-        u_out = torch.empty((T, count * r), dtype=torch.bfloat16, device=x.device)
-    ws = workspace if workspace is not None else linear_set_workspace(T, [q.n_out for q in qs], qs[0].n_in, r,
-                                                                      x.device)
+        u_out = torch.empty((T, count * r), dtype=torch.bfloat16, device=dev)
+    if u_out is not None:
+        chk.bf16(u_out, "u_out", (T, count * r))
+    chk.done()
+    n_outs = [q.n_out for q in qs]
+    ws = workspace if workspace is not None else linear_set_workspace(T, n_outs, qs[0].n_in, r, dev)
+    wsb = _workspace(ws, dev, linear_set_workspace_bytes(T, n_outs, qs[0].n_in, r))
     st = (NF4WeightStruct * count)(*[q.struct() for q in qs])
     _check(lib().qlora_linear_set_fwd(_ptr(x), T, count, st, _ptr(A_set), _ptrs(Bs), r, float(scale), _ptrs(ys),
-                                      _ptr(u_out), _ptr(ws), ws.numel(), _stream(stream)), "qlora_linear_set_fwd")
+                                      _ptr(u_out), _ptr(ws), wsb, _stream(stream)), "qlora_linear_set_fwd")
     return ys, u_out
+
+
+def _check_list(ts, count: int, name: str) -> None:
+    if len(ts) != count:
+        raise ValueError(f"{name} must hold {count} tensors, not {len(ts)}")
+
+
+def _set_dims(x, qs, A_set):
+    """(T, count, r, device, checker) of a projection-set call; A_set must hold count whole [r x n_in] blocks."""
+    count = len(qs)
+    if count < 1:
+        raise ValueError("a projection set needs at least one member")
+    dev = _weight_device(qs[0])
+    for i, q in enumerate(qs):
+        if q.n_in != qs[0].n_in:
+            raise ValueError(f"member {i} has n_in {q.n_in}, member 0 has {qs[0].n_in}")
+        if _weight_device(q) != dev:
+            raise ValueError(f"member {i} is on {q.codes.device}, member 0 on {dev}")
+    if x.dim() != 2 or A_set.dim() != 2:
+        raise ValueError("x and A_set must be 2-D")
+    if A_set.shape[0] % count:
+        raise ValueError(f"A_set has {A_set.shape[0]} rows, not a multiple of the {count} members")
+    T, r = int(x.shape[0]), int(A_set.shape[0]) // count
+    chk = _Args(dev)
+    chk.bf16(x, "x", (T, qs[0].n_in))
+    chk.bf16(A_set, "A_set", (count * r, qs[0].n_in))
+    return T, count, r, dev, chk
 
 
 def linear_set_bwd(dys, x, qs, A_set, Bs, scale: float, u=None, need_grad_x=True, grad_x=None, grad_A_set=None,
                    grad_Bs=None, workspace=None, stream=None):
     """Projection set backward: (grad_x summed over the members or None, grad_A_set, [grad_B_i])."""
     torch = _torch()
-    T, count, dev = x.shape[0], len(qs), x.device
-    r = A_set.shape[0] // count
+    T, count, r, dev, chk = _set_dims(x, qs, A_set)
+    _check_list(dys, count, "dys")
+    _check_list(Bs, count, "Bs")
+    for i, (q, d, b) in enumerate(zip(qs, dys, Bs)):
+        chk.bf16(d, f"dys[{i}]", (T, q.n_out))
+        chk.bf16(b, f"Bs[{i}]", (q.n_out, r))
+    if u is not None:
+        chk.bf16(u, "u", (T, count * r))
     if need_grad_x and grad_x is None:
         grad_x = torch.empty((T, qs[0].n_in), dtype=torch.bfloat16, device=dev)
     if not need_grad_x:
         grad_x = None
+    if grad_x is not None:
+        chk.bf16(grad_x, "grad_x", (T, qs[0].n_in))
     grad_A_set = grad_A_set if grad_A_set is not None else torch.empty((count * r, qs[0].n_in), dtype=torch.float32,
                                                                        device=dev)
+    chk.f32(grad_A_set, "grad_A_set", (count * r, qs[0].n_in))
     grad_Bs = grad_Bs if grad_Bs is not None else [torch.empty((q.n_out, r), dtype=torch.float32, device=dev)
                                                    for q in qs]
-    ws = workspace if workspace is not None else linear_set_workspace(T, [q.n_out for q in qs], qs[0].n_in, r, dev)
+    _check_list(grad_Bs, count, "grad_Bs")
+    for i, (q, g) in enumerate(zip(qs, grad_Bs)):
+        chk.f32(g, f"grad_Bs[{i}]", (q.n_out, r))
+    chk.done()
+    n_outs = [q.n_out for q in qs]
+    ws = workspace if workspace is not None else linear_set_workspace(T, n_outs, qs[0].n_in, r, dev)
+    wsb = _workspace(ws, dev, linear_set_workspace_bytes(T, n_outs, qs[0].n_in, r))
     st = (NF4WeightStruct * count)(*[q.struct() for q in qs])
     _check(lib().qlora_linear_set_bwd(_ptrs(dys), _ptr(x), T, count, st, _ptr(A_set), _ptrs(Bs), r, float(scale),
-                                      _ptr(u), _ptr(grad_x), _ptr(grad_A_set), _ptrs(grad_Bs), _ptr(ws), ws.numel(),
+                                      _ptr(u), _ptr(grad_x), _ptr(grad_A_set), _ptrs(grad_Bs), _ptr(ws), wsb,
                                       _stream(stream)), "qlora_linear_set_bwd")
     return grad_x, grad_A_set, grad_Bs

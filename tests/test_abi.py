@@ -213,3 +213,81 @@ def test_dequantize_many_validation():
     assert lib.qlora_dequantize_many(ws, 2, (ctypes.c_void_p * 2)(0x80000, 0x90002), None) == 3
     bad = (qlora.NF4WeightStruct * 2)(_fake_weight(), _fake_weight(0, 256))
     assert lib.qlora_dequantize_many(bad, 2, outs, None) == 2
+
+
+def test_binding_checks_every_tensor_before_a_call():
+    """The binding refuses a tensor of the wrong dtype, shape, layout or device before the C ABI
+    is reached (the ABI takes plain pointers and cannot check buffer extents).  CPU tensors never
+    reach the library: with every shape right, the device check is what refuses them."""
+    torch = pytest.importorskip("torch")
+    from bit_quantized_finetuning_quant_amd import qlora
+
+    n_out, n_in, T, r = 128, 64, 5, 8
+    q = qlora.NF4Weight.empty(n_out, n_in, device="cpu")
+    bf = lambda *s: torch.zeros(s, dtype=torch.bfloat16)
+    f32 = lambda *s: torch.zeros(s, dtype=torch.float32)
+    x, a, b, dy = bf(T, n_in), bf(r, n_in), bf(n_out, r), bf(T, n_out)
+
+    def refuses(fn, match):
+        with pytest.raises(ValueError, match=match):
+            fn()
+
+    # the packed weight itself must be on a CUDA device
+    refuses(lambda: qlora.linear_fwd(x, q, a, b, 0.5), "CUDA device")
+    refuses(lambda: qlora.dequantize(q), "CUDA device")
+
+    class _Dev:  # a packed weight that claims a CUDA device, so each tensor check is reached
+        type = "cuda"
+
+        def __eq__(self, other):
+            return other is self
+
+        def __ne__(self, other):
+            return other is not self
+
+        def __repr__(self):
+            return "cuda:0"
+
+    class _Codes:
+        device = _Dev()  # one device object: members compare equal, CPU tensors do not
+
+    qc = qlora.NF4Weight(n_out, n_in, _Codes(), None, None, None)
+    outs = dict(y=bf(T, n_out), u_out=bf(T, r))
+    grads = dict(grad_x=bf(T, n_in), grad_A=f32(r, n_in), grad_B=f32(n_out, r))
+    fwd = lambda x_=x, a_=a, b_=b, **kw: qlora.linear_fwd(x_, qc, a_, b_, 0.5, **{**outs, **kw})
+    bwd = lambda dy_=dy, x_=x, **kw: qlora.linear_bwd(dy_, x_, qc, a, b, 0.5, **{**grads, **kw})
+    refuses(lambda: fwd(x_=bf(T, n_in + 8)), r"x must have shape \(5, 64\)")
+    refuses(lambda: fwd(x_=x.float()), "x must be")
+    refuses(lambda: fwd(a_=bf(r, n_in - 1)), "A must have shape")
+    refuses(lambda: fwd(b_=bf(r, n_out).t()), "B must be contiguous")
+    refuses(lambda: fwd(b_=bf(n_out + 1, r)), "B must have shape")
+    refuses(lambda: fwd(y=bf(T, n_out - 1)), "y must have shape")
+    refuses(lambda: fwd(u_out=bf(T, r + 1)), "u_out must have shape")
+    refuses(lambda: fwd(), "x must be on cuda:0, not cpu")  # every shape right: the device decides
+    refuses(lambda: bwd(dy_=bf(T, n_out + 1)), "dy must have shape")
+    refuses(lambda: bwd(u=bf(T, r + 1)), "u must have shape")
+    refuses(lambda: bwd(grad_A=bf(r, n_in)), "grad_A must be")
+    refuses(lambda: bwd(grad_B=f32(r, n_out)), "grad_B must have shape")
+    refuses(lambda: bwd(grad_x=f32(T, n_in)), "grad_x must be")
+    refuses(lambda: bwd(), "dy must be on cuda:0")
+    refuses(lambda: qlora.linear_bwd_dropout(dy, bf(T + 1, n_in), qc, a, b, 0.5, 0.1, 1), "dy must have")
+    refuses(lambda: qlora.linear_fwd_dropout(x, qc, a, b.float(), 0.5, 0.1, 1), "B must be")
+    # projection sets: A_set must hold whole [r x n_in] blocks, one per member
+    qs = [qc, qc]
+    sfwd = lambda a_set, bs, **kw: qlora.linear_set_fwd(x, qs, a_set, bs, 0.5, **kw)
+    refuses(lambda: sfwd(bf(2 * r + 1, n_in), [b, b]), "multiple of the 2 members")
+    refuses(lambda: sfwd(bf(2 * r, n_in), [b]), "Bs must hold 2")
+    refuses(lambda: sfwd(bf(2 * r, n_in), [b, bf(n_out, r + 1)]), r"Bs\[1\] must have shape")
+    refuses(lambda: sfwd(bf(2 * r, n_in), [b, b], ys=[bf(T, n_out)] * 2, u_out=bf(T, r)), "u_out must have")
+    refuses(lambda: sfwd(bf(2 * r, n_in), [b, b], ys=[bf(T, n_out)] * 2, u_out=bf(T, 2 * r)), "x must be on")
+    q2 = qlora.NF4Weight(n_out, n_in + 64, _Codes(), None, None, None)
+    refuses(lambda: qlora.linear_set_fwd(x, [qc, q2], bf(2 * r, n_in), [b, b], 0.5), "member 1 has n_in")
+    refuses(lambda: qlora.linear_set_bwd([dy, dy], x, qs, bf(2 * r + 1, n_in), [b, b], 0.5), "multiple of the 2")
+    refuses(lambda: qlora.linear_set_bwd([dy], x, qs, bf(2 * r, n_in), [b, b], 0.5), "dys must hold 2")
+    # a workspace must be a uint8 CUDA tensor: its byte count is what the ABI is told
+    with pytest.raises(ValueError, match="workspace must be a contiguous 1-D uint8"):
+        qlora._workspace(torch.zeros(16, dtype=torch.float32), torch.device("cpu"), 8)
+    with pytest.raises(ValueError, match="workspace must be on"):
+        qlora._workspace(torch.zeros(16, dtype=torch.uint8), torch.device("cuda:0"), 8)
+    # quantize: the source must be on a CUDA device
+    refuses(lambda: qlora.quantize(f32(n_out, n_in)), "w must be on a CUDA device")
