@@ -22,7 +22,8 @@
  *     current HIP device), 16-byte aligned, row-major and densely packed.
  *     bf16 tensors are passed as uint16_t bit patterns.
  *   - The caller owns every buffer, including the workspace.  The library
- *     allocates and frees no device memory and keeps no mutable global state.
+ *     allocates and frees no device memory.  Its only mutable global state is
+ *     the timing diagnostics (qlora_kernel_timing_*, not thread-safe).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls validate
  *     their arguments on the host, enqueue kernels on `stream` and return
  *     without waiting.  Buffers must stay alive until the stream has run the
@@ -122,7 +123,9 @@ const char *qlora_version(void);
 
 /* ---- device calls (enqueue on `stream`) ---------------------------------- */
 
-/* Quantize W (fp32 or bf16, [q->n_out x q->n_in], device) into *q.
+/* Quantize W (fp32 or bf16, [q->n_out x q->n_in], device) into *q: blockwise
+ * NF4 with one absmax constant per 64 elements, the constants quantized again
+ * to FP8 in groups of 256 ("qlora" entry, section "como funciona"):
  *   c1_b  = max |x| over block b (exact);
  *   code  = index of the NF4 level nearest to the exact real x / c1_b, ties
  *           toward the level of smaller magnitude (c1_b = 0 gives code 7);
@@ -139,7 +142,9 @@ const char *qlora_version(void);
 qlora_status qlora_quantize(const void *w, qlora_dtype w_dtype, const qlora_nf4_weight *q,
                             void *ws, size_t ws_bytes, void *stream);
 
-/* Dequantize *q to bf16 w_bf16 [n_out x n_in] (device):
+/* Dequantize *q to bf16 w_bf16 [n_out x n_in] (device), the decode that every
+ * use of the weight applies ("qlora" entry, section "a ideia": the 4-bit
+ * weight is dequantized to BFloat16 when it is used):
  *   c1hat_b = fl32(fl32(e4m3(q_b) * s2_g) + mu)     (no fused multiply-add;
  *             c1hat_b = c1_b with QLORA_NF4_FP32_CONSTANTS)
  *   w_hat   = bf16_round_nearest_even(fl32(CB[code] * c1hat_b))
@@ -153,7 +158,10 @@ qlora_status qlora_dequantize(const qlora_nf4_weight *q, uint16_t *w_bf16, void 
 qlora_status qlora_dequantize_many(const qlora_nf4_weight *q, int count, uint16_t *const *w_bf16,
                                    void *stream);
 
-/* Forward of the adapted linear layer for T tokens:
+/* Forward of the adapted linear layer for T tokens: the 4-bit weight decoded
+ * to BFloat16 inside the product ("qlora" entry, section "a ideia") plus the
+ * LoRA path W' = W + s.B.A (nexusinovation tutorial, section "LoRA: O Padrão
+ * Ouro de Eficiência"):
  *   u = x A^T                      (bf16, [T x r]; written to u_out if non-NULL)
  *   y = bf16( x W_hat^T + scale * u B^T )          [T x n_out]
  * x [T x n_in] bf16, A [r x n_in] bf16, B [n_out x r] bf16, all device.
@@ -165,7 +173,9 @@ qlora_status qlora_linear_fwd(const uint16_t *x, int64_t T, const qlora_nf4_weig
                               uint16_t *y, uint16_t *u_out, void *ws, size_t ws_bytes,
                               void *stream);
 
-/* Backward of the adapted linear layer (the weight is frozen):
+/* Backward of the adapted linear layer: the gradient passes through the
+ * frozen 4-bit weight into the 16-bit adapters only ("qlora" entry, section
+ * "a ideia"):
  *   v      = dy B                                   (bf16, internal)
  *   grad_x = bf16( dy W_hat + scale * v A )         [T x n_in]   (skipped if NULL)
  *   grad_A = scale * v^T x                          [r x n_in]   fp32
