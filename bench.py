@@ -175,8 +175,10 @@ def _student_t_weight(torch, g, n, k, out):
     out.div_(torch.sqrt(chi / 5.0)).mul_(0.02)
     del chi, z
     flat = out.view(-1)
-    idx = torch.randint(0, flat.numel(), (round(0.001 * flat.numel()),), device="cuda", generator=g)
+    # exactly round(0.001 numel) distinct positions (drawn without replacement)
+    idx = torch.randperm(flat.numel(), device="cuda", generator=g)[:round(0.001 * flat.numel())]
     flat[idx] *= 20.0
+    del idx
 
 
 class LayerSet:
@@ -548,6 +550,61 @@ def extra_measurements(torch, qlora, steps):
     return out
 
 
+CROSSOVER_TOKENS = (1, 2, 4, 8, 16, 32, 64, 128, 256)
+
+
+def extra_crossover(torch, qlora, steps):
+    """fwd + bwd of one linear by token count, at the 7B projection (4096 x 4096, rotating over
+    1.1 GB of distinct packed weights) and at the 65B gate shape (22016 x 8192, rotating over 12
+    weights, 1.1 GB), r = 64.  For each T: time per fwd + bwd, GB/s of the algorithmic bytes
+    (the packed weight read by each direction, activations, adapters and outputs), TFLOP/s of
+    4TNK + 6Tr(N + K), and the fraction of the better of the two rooflines that time reaches
+    (roofline time = max(bytes / 8 TB/s, flops / bf16 MFMA peak))."""
+    out = {}
+    r = 64
+    g = torch.Generator(device="cuda")
+    g.manual_seed(77)
+    for name, N, K in (("7b_attn", 4096, 4096), ("65b_gate", 22016, 8192)):
+        packed = qlora.nf4_bytes(N, K)
+        weights = rotating_weights(torch, qlora, N, K, 1.1e9)
+        A = _bf16_normal(torch, g, (r, K), 0.01)
+        B = _bf16_normal(torch, g, (N, r), 0.01)
+        rows = []
+        for T in CROSSOVER_TOKENS:
+            x = _bf16_normal(torch, g, (T, K), 1.0)
+            dy = _bf16_normal(torch, g, (T, N), 1.0)
+            y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
+            u = torch.empty((T, r), dtype=torch.bfloat16, device="cuda")
+            gx = torch.empty((T, K), dtype=torch.bfloat16, device="cuda")
+            ga = torch.empty((r, K), dtype=torch.float32, device="cuda")
+            gb = torch.empty((N, r), dtype=torch.float32, device="cuda")
+            ws = qlora.linear_workspace(T, N, K, r)
+
+            def run():
+                for q in weights:
+                    qlora.linear_fwd(x, q, A, B, 0.25, y=y, u_out=u, workspace=ws)
+                    qlora.linear_bwd(dy, x, q, A, B, 0.25, u=u, grad_x=gx, grad_A=ga, grad_B=gb, workspace=ws)
+
+            run()
+            reps = max(2, steps // 10)
+            t, _ = time_region(torch, run, reps)
+            per = t / (reps * len(weights))
+            flops = linear_flops(T, N, K, r)
+            # fwd: W, x, A, B in, y, u out; bwd: W, dy, x, A, B, u in, grad_x, grad_A, grad_B out
+            nbytes = (2 * packed + 2 * T * (2 * K + 2 * N + 2 * r) + 2 * 2 * r * (N + K) + 4 * r * (N + K)
+                      + 2 * T * K)
+            roof = max(nbytes / (PEAK_HBM_GBS * 1e9), flops / (PEAK_BF16_TFLOPS * 1e12))
+            rows.append({"T": T, "us": per * 1e6, "GB/s": nbytes / per / 1e9, "TFLOP/s": flops / per / 1e12,
+                         "roofline_us": roof * 1e6, "frac_of_roofline": roof / per,
+                         "bound": "hbm" if nbytes / (PEAK_HBM_GBS * 1e9) >= flops / (PEAK_BF16_TFLOPS * 1e12)
+                         else "mfma"})
+            del x, dy, y, u, gx, ga, gb, ws
+        out[f"crossover_{name}"] = {"shape": [N, K], "r": r, "weights_rotated": len(weights), "by_tokens": rows}
+        del weights, A, B
+        torch.cuda.empty_cache()
+    return out
+
+
 def extra_library_reference(torch, qlora, case, dev_bf16, dev_f32, steps, fused_fwd_us=None):
     """Context for the fused forward GEMM: the vendor library's plain bf16 GEMM (torch.matmul,
     hipBLASLt) of the same activation with the decoded weight, x W_hat^T (no adapter term), and the
@@ -717,7 +774,8 @@ def main():
                          "path, rotating over more than 1 GB of distinct packed weights")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true")
-    ap.add_argument("--extra-only", choices=["adamw", "dropout", "layers", "bulk", "gemv", "library"], default=None,
+    ap.add_argument("--extra-only", choices=["adamw", "dropout", "layers", "bulk", "gemv", "library", "crossover"],
+                    default=None,
                     help="run only this extra measurement and print its JSON (for profiling it alone)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before the steps, copy 256 MiB device to device three times (untimed): the "
@@ -748,6 +806,9 @@ def main():
         out = {"bulk_65b": extra_bulk_65b(torch, qlora, workloads)}
         out.update(extra_measurements(torch, qlora, args.steps))
         print(json.dumps(out), flush=True)
+        return
+    if args.extra_only == "crossover":
+        print(json.dumps(extra_crossover(torch, qlora, args.steps)), flush=True)
         return
     if args.extra_only == "gemv":
         print(json.dumps(extra_gemv_65b(torch, qlora, workloads, args.steps)), flush=True)
@@ -812,6 +873,7 @@ def main():
         extra["bulk_65b"] = extra_bulk_65b(torch, qlora, workloads)
         extra.update(extra_measurements(torch, qlora, args.steps))
         extra.update(extra_gemv_65b(torch, qlora, workloads, args.steps))
+        extra.update(extra_crossover(torch, qlora, args.steps))
         extra.update(extra_adamw(torch, qlora, workloads, args.steps))
         extra.update(extra_dropout(torch, qlora, case, dev_bf16, dev_f32, args.steps))
         fwd = roofline.get("other_kernels", {}).get("qgemm_fwd", {}).get("avg_us")
