@@ -6,6 +6,7 @@
 
 #include <algorithm>
 #include <cmath>
+#include <mutex>
 
 #include "../../include/qlora.h"
 #include "common.hpp"
@@ -149,6 +150,48 @@ qlora_status check_set(int64_t T, int count, const qlora_nf4_weight *q, int r, f
   return QLORA_OK;
 }
 
+// ---- scratch of the forward without a caller workspace --------------------
+// For callers that cannot allocate (graph capture, serving loops): a fixed
+// device array, one copy per GPU for the life of the process.  In host code
+// its name stands for a host-side shadow, not a device address, so host code
+// only ever uses the address hipGetSymbolAddress returns for the current
+// device (looked up on the first call on that device and kept).
+constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+qlora_status noalloc_scratch(void **out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();
+    return QLORA_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return QLORA_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return QLORA_OK;
+}
+
+// Bytes of a linear workspace the forward touches: u (when the caller does not
+// take it) and the partial sums of its own adapter product, at the offsets of
+// the linear plan.
+size_t forward_scratch_bytes(const LinearPlan &p) {
+  const size_t part = gemv_applies(p.T, p.K) ? gemv_part_floats(p.T, p.N, p.K, p.r)
+                                             : lora_part_floats(p.T, p.r, p.K);
+  return p.off_part + part * 4;
+}
+
 }  // namespace
 
 extern "C" {
@@ -213,6 +256,7 @@ const char *qlora_status_string(qlora_status s) {
     case QLORA_ERR_NONFINITE: return "NaN or Inf in the quantized weight";
     case QLORA_ERR_VALUE: return "a scalar argument is not finite or out of range";
     case QLORA_ERR_MEMORY: return "a buffer is not reachable by the GPU (pageable host memory?)";
+    case QLORA_ERR_SCRATCH: return "the call needs more scratch than the library's fixed array holds";
   }
   return "unknown status";
 }
@@ -274,6 +318,26 @@ qlora_status qlora_linear_fwd(const uint16_t *x, int64_t T, const qlora_nf4_weig
     return QLORA_ERR_ALIGN;
   const LinearPlan p = plan_linear(T, q->n_out, q->n_in, r);
   if (ws_bytes < p.total) return QLORA_ERR_WORKSPACE;
+  hipError_t e = launch_linear_fwd(p, x, qweight(q), A, B, scale, y, u_out, (char *)ws, tables().cb,
+                                   (hipStream_t)stream);
+  return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP;
+}
+
+size_t qlora_linear_fwd_noalloc_max_bytes(void) { return kNoAllocScratchBytes; }
+
+qlora_status qlora_linear_fwd_noalloc(const uint16_t *x, int64_t T, const qlora_nf4_weight *q, const uint16_t *A,
+                                      const uint16_t *B, int r, float scale, uint16_t *y, uint16_t *u_out,
+                                      void *stream) {
+  qlora_status s = check_linear(T, q, r, scale);
+  if (s != QLORA_OK) return s;
+  if (!x || !A || !B || !y) return QLORA_ERR_NULL;
+  if (!aligned16(x) || !aligned16(A) || !aligned16(B) || !aligned16(y) || (u_out && !aligned16(u_out)))
+    return QLORA_ERR_ALIGN;
+  const LinearPlan p = plan_linear(T, q->n_out, q->n_in, r);
+  if (forward_scratch_bytes(p) > kNoAllocScratchBytes) return QLORA_ERR_SCRATCH;
+  void *ws = nullptr;
+  s = noalloc_scratch(&ws);
+  if (s != QLORA_OK) return s;
   hipError_t e = launch_linear_fwd(p, x, qweight(q), A, B, scale, y, u_out, (char *)ws, tables().cb,
                                    (hipStream_t)stream);
   return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP;

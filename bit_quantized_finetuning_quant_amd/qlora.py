@@ -17,7 +17,7 @@ QLORA_F32, QLORA_BF16 = 0, 1
 QLORA_NF4_FP32_CONSTANTS = 1
 STATUS_NAMES = {0: "QLORA_OK", 1: "QLORA_ERR_NULL", 2: "QLORA_ERR_SHAPE", 3: "QLORA_ERR_ALIGN",
                 4: "QLORA_ERR_WORKSPACE", 5: "QLORA_ERR_DTYPE", 6: "QLORA_ERR_HIP",
-                7: "QLORA_ERR_NONFINITE", 8: "QLORA_ERR_VALUE", 9: "QLORA_ERR_MEMORY"}
+                7: "QLORA_ERR_NONFINITE", 8: "QLORA_ERR_VALUE", 9: "QLORA_ERR_MEMORY", 10: "QLORA_ERR_SCRATCH"}
 
 
 class QloraError(RuntimeError):
@@ -52,6 +52,8 @@ _SIGNATURES = {
     "qlora_linear_fwd": (ctypes.c_int, [_P, _I64, _P, _P, _P, ctypes.c_int, ctypes.c_float, _P, _P, _P, _SZ, _P]),
     "qlora_linear_bwd": (ctypes.c_int, [_P, _P, _I64, _P, _P, _P, ctypes.c_int, ctypes.c_float, _P, _P, _P, _P,
                                         _P, _SZ, _P]),
+    "qlora_linear_fwd_noalloc_max_bytes": (_SZ, []),
+    "qlora_linear_fwd_noalloc": (ctypes.c_int, [_P, _I64, _P, _P, _P, ctypes.c_int, ctypes.c_float, _P, _P, _P]),
     "qlora_linear_set_workspace_bytes": (_SZ, [_I64, ctypes.c_int, _P, _I64, ctypes.c_int]),
     "qlora_linear_set_fwd": (ctypes.c_int, [_P, _I64, ctypes.c_int, _P, _P, _P, ctypes.c_int, ctypes.c_float, _P, _P,
                                             _P, _SZ, _P]),
@@ -356,6 +358,30 @@ def linear_fwd(x, q: NF4Weight, A, B, scale: float, y=None, u_out=None, save_u=T
     _check(lib().qlora_linear_fwd(_ptr(x), T, ctypes.byref(st), _ptr(A), _ptr(B), r, float(scale), _ptr(y),
                                   _ptr(u_out), _ptr(ws), wsb, _stream(stream)), "qlora_linear_fwd")
     return y, u_out
+
+
+def linear_fwd_noalloc(x, q: NF4Weight, A, B, scale: float, y, u_out=None, stream=None):
+    """linear_fwd on the library's fixed per-GPU scratch array instead of a workspace (for callers
+    that cannot allocate): y (and u_out, if given) are the caller's; nothing is allocated here.
+    Calls that may overlap in time on one GPU share the array and must be ordered."""
+    T, r = _linear_dims(x, A, q)
+    dev = _weight_device(q)
+    chk = _Args(dev)
+    chk.bf16(x, "x", (T, q.n_in))
+    chk.bf16(A, "A", (r, q.n_in))
+    chk.bf16(B, "B", (q.n_out, r))
+    chk.bf16(y, "y", (T, q.n_out))
+    if u_out is not None:
+        chk.bf16(u_out, "u_out", (T, r))
+    chk.done()
+    st = q.struct()
+    _check(lib().qlora_linear_fwd_noalloc(_ptr(x), T, ctypes.byref(st), _ptr(A), _ptr(B), r, float(scale), _ptr(y),
+                                          _ptr(u_out), _stream(stream)), "qlora_linear_fwd_noalloc")
+    return y, u_out
+
+
+def linear_fwd_noalloc_max_bytes() -> int:
+    return int(lib().qlora_linear_fwd_noalloc_max_bytes())
 
 
 def _linear_dims(x, A, q):

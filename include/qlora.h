@@ -23,7 +23,9 @@
  *     bf16 tensors are passed as uint16_t bit patterns.
  *   - The caller owns every buffer, including the workspace.  The library
  *     allocates and frees no device memory.  Its only mutable global state is
- *     the timing diagnostics (qlora_kernel_timing_*, not thread-safe).
+ *     the timing diagnostics (qlora_kernel_timing_*, not thread-safe) and the
+ *     per-device scratch array of qlora_linear_fwd_noalloc (with the cache of
+ *     its device addresses).
  *   - `stream` is a hipStream_t (NULL = the default stream).  Calls validate
  *     their arguments on the host, enqueue kernels on `stream` and return
  *     without waiting.  Buffers must stay alive until the stream has run the
@@ -55,7 +57,8 @@ typedef enum {
   QLORA_ERR_HIP = 6,        /* the HIP runtime reported an error at launch          */
   QLORA_ERR_NONFINITE = 7,  /* (deferred) NaN or Inf met while quantizing           */
   QLORA_ERR_VALUE = 8,      /* a scalar argument is not finite or out of range      */
-  QLORA_ERR_MEMORY = 9      /* a buffer is neither device nor pinned host memory    */
+  QLORA_ERR_MEMORY = 9,     /* a buffer is neither device nor pinned host memory    */
+  QLORA_ERR_SCRATCH = 10    /* the call needs more than the fixed scratch array     */
 } qlora_status;
 
 typedef enum { QLORA_F32 = 0, QLORA_BF16 = 1 } qlora_dtype;
@@ -172,6 +175,25 @@ qlora_status qlora_linear_fwd(const uint16_t *x, int64_t T, const qlora_nf4_weig
                               const uint16_t *A, const uint16_t *B, int r, float scale,
                               uint16_t *y, uint16_t *u_out, void *ws, size_t ws_bytes,
                               void *stream);
+
+/* qlora_linear_fwd without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same computation, kernels, shape rules and
+ * errors as qlora_linear_fwd (results bit-identical to it), plus
+ * QLORA_ERR_SCRATCH, returned before anything is enqueued, when the call needs
+ * more scratch than the library's fixed array holds (the partial sums of
+ * u = x A^T, and u itself when u_out is NULL; qlora_linear_fwd_noalloc_max_bytes
+ * gives the limit).  The array is a device global of the library: every GPU the
+ * library runs on holds one copy of it until the process ends, and every call on
+ * that GPU shares it, so two calls that may overlap in time on one GPU race
+ * (order them on one stream).  Nothing in it has to start at zero: each call
+ * writes every scratch value it reads.  The call allocates nothing and runs on
+ * the current HIP device, which must be the one that owns `stream` and the
+ * buffers.                                                                  */
+size_t qlora_linear_fwd_noalloc_max_bytes(void);
+qlora_status qlora_linear_fwd_noalloc(const uint16_t *x, int64_t T, const qlora_nf4_weight *q,
+                                      const uint16_t *A, const uint16_t *B, int r, float scale,
+                                      uint16_t *y, uint16_t *u_out, void *stream);
 
 /* Backward of the adapted linear layer: the gradient passes through the
  * frozen 4-bit weight into the 16-bit adapters only ("qlora" entry, section

@@ -291,3 +291,22 @@ def test_binding_checks_every_tensor_before_a_call():
         qlora._workspace(torch.zeros(16, dtype=torch.uint8), torch.device("cuda:0"), 8)
     # quantize: the source must be on a CUDA device
     refuses(lambda: qlora.quantize(f32(n_out, n_in)), "w must be on a CUDA device")
+
+
+def test_noalloc_forward_refuses_what_its_scratch_cannot_hold():
+    """The forward without a workspace checks its scratch need on the host and refuses a call
+    that would not fit before touching the GPU (the buffers here are never dereferenced)."""
+    from bit_quantized_finetuning_quant_amd import qlora
+
+    lib = qlora.lib()
+    limit = lib.qlora_linear_fwd_noalloc_max_bytes()
+    assert limit == 16 << 20
+    fake = 1 << 20  # 16-byte aligned, never dereferenced
+    # u alone: T x r bf16 beyond the limit (T = 65536, r = 256: 32 MiB)
+    st = qlora.NF4WeightStruct(4096, 4096, fake, fake, fake, fake, 0)
+    rc = lib.qlora_linear_fwd_noalloc(fake, 65536, ctypes.byref(st), fake, fake, 256, 1.0, fake, 0, None)
+    assert rc == 10 and "scratch" in qlora.status_string(rc)
+    # argument errors come first, as in qlora_linear_fwd
+    assert lib.qlora_linear_fwd_noalloc(0, 16, ctypes.byref(st), fake, fake, 8, 1.0, fake, 0, None) == 1
+    assert lib.qlora_linear_fwd_noalloc(fake, 16, ctypes.byref(st), fake, fake, 0, 1.0, fake, 0, None) == 2
+    assert lib.qlora_linear_fwd_noalloc(fake + 2, 16, ctypes.byref(st), fake, fake, 8, 1.0, fake, 0, None) == 3
