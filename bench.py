@@ -691,10 +691,17 @@ def extra_adamw(torch, qlora, workloads, steps):
     return out
 
 
-def cpu_baseline(case, budget_s=12.0):
-    """The oracle (dequantize + fp64 forward + backward) timed on this host's cores."""
-    import oracle
-
+def host_info():
+    """CPU model, the cores this process may use, and the BLAS thread count numpy's oracle runs on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     try:
         from threadpoolctl import threadpool_info
 
@@ -702,6 +709,47 @@ def cpu_baseline(case, budget_s=12.0):
                       default=1)
     except Exception:  # pragma: no cover
         threads = 1
+    return {"cpu_model": model, "host_cpus": len(os.sched_getaffinity(0)), "blas_threads": int(threads)}
+
+
+def gpu_clocks():
+    """Current shader (sclk) and memory (mclk) clocks as rocm-smi reports them (None if unavailable)."""
+    import subprocess
+
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True, timeout=20)
+        d = json.loads(out.stdout)
+    except Exception:
+        return None
+    card = next(iter(d.values()), {}) if isinstance(d, dict) else {}
+    pick = lambda key: next((v for k, v in card.items() if key in k.lower()), None)
+    return {"sclk": pick("sclk"), "mclk": pick("mclk"), "fclk": pick("fclk")}
+
+
+def _time_oracle_steps(oracle, case, wh, budget_s, max_steps):
+    """Whole fwd + bwd steps of the oracle on a decoded weight until the budget is spent."""
+    steps, t0 = 0, time.perf_counter()
+    while True:
+        oracle.forward(case.x, wh, case.a, case.b, case.scale)
+        oracle.backward(case.dy, case.x, wh, case.a, case.b, case.scale)
+        steps += 1
+        el = time.perf_counter() - t0
+        if el >= budget_s or steps >= max_steps:
+            return steps, el
+
+
+def cpu_baseline(case, workloads, budget_s=6.0):
+    """The oracle (NF4 decode + fp64 forward + backward, and the codec) timed on this host's cores.
+
+    `value` is the headline workload's unit (the 7B projection at 2048 tokens: NF4 decode + fp64
+    fwd + bwd per step, TFLOP/s); `breakdown` adds bounded samples of the other workloads: the
+    tiny case in full, each 7B decoder linear once on its first 512 tokens, the 65B q projection
+    once on 1024 tokens (the other six 65B linears scale with their flops), and the oracle's
+    quantize + dequantize of that 65B tensor with the stated extrapolation to one layer and to the
+    80-layer store.  About 25 s of host work in all."""
+    import oracle
+
+    info = host_info()
     ref = oracle.quantize(case.w, case.n_out, case.n_in)
     steps, t0 = 0, time.perf_counter()
     while True:
@@ -713,9 +761,59 @@ def cpu_baseline(case, budget_s=12.0):
         if el >= budget_s or steps >= 20:
             break
     flops = linear_flops(case.tokens, case.n_out, case.n_in, case.r) * steps
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{steps} full step(s) of {case.name} (NF4 decode + fp64 fwd + bwd), {el:.1f} s",
-            "host_cpus": len(os.sched_getaffinity(0))}
+    br = {}
+    # tiny case, everything: quantize, decode, fwd, bwd
+    tc = workloads.tiny_case()
+    t0 = time.perf_counter()
+    q = oracle.quantize(tc.w, tc.n_out, tc.n_in)
+    wt = oracle.dequantize(q)
+    oracle.forward(tc.x, wt, tc.a, tc.b, tc.scale)
+    oracle.backward(tc.dy, tc.x, wt, tc.a, tc.b, tc.scale)
+    br["tiny_full_s"] = time.perf_counter() - t0
+    # each 7B decoder linear once on 512 tokens (decode + fwd + bwd)
+    rows, t_all, f_all = [], 0.0, 0
+    for c in workloads.layer7b_cases(512):
+        qc = oracle.quantize(c.w, c.n_out, c.n_in)
+        t0 = time.perf_counter()
+        whc = oracle.dequantize(qc)
+        oracle.forward(c.x, whc, c.a, c.b, c.scale)
+        oracle.backward(c.dy, c.x, whc, c.a, c.b, c.scale)
+        dt = time.perf_counter() - t0
+        f = linear_flops(c.tokens, c.n_out, c.n_in, c.r)
+        rows.append({"linear": c.name, "s": dt, "TFLOP/s": f / dt / 1e12})
+        t_all += dt
+        f_all += f
+    br["7b_layer_per_linear"] = rows
+    br["7b_layer_TFLOP/s"] = f_all / t_all / 1e12
+    # the 65B q projection on 1024 tokens
+    c = next(workloads.layer65b_cases(1024, names=("q",)))
+    t0 = time.perf_counter()
+    qc = oracle.quantize(c.w, c.n_out, c.n_in)
+    t_quant = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    whc = oracle.dequantize(qc)
+    t_deq = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    oracle.forward(c.x, whc, c.a, c.b, c.scale)
+    oracle.backward(c.dy, c.x, whc, c.a, c.b, c.scale)
+    dt = time.perf_counter() - t0 + t_deq
+    f = linear_flops(c.tokens, c.n_out, c.n_in, c.r)
+    per_layer_flops = sum(linear_flops(c.tokens, n, k, 64) for _, n, k in workloads.SHAPES_65B)
+    br["65b_q_linear"] = {"tokens": c.tokens, "s": dt, "TFLOP/s": f / dt / 1e12,
+                          "layer_s_at_4096_tokens_extrapolated_by_flops": dt * per_layer_flops / f * 4096 / c.tokens}
+    # the codec on that tensor (fp32 source, N(0,0.02) Student-t mix): quantize and dequantize
+    n = c.n_out * c.n_in
+    layer_params = sum(nn * kk for _, nn, kk in workloads.SHAPES_65B)
+    br["65b_codec_one_tensor"] = {"params": n, "quantize_s": t_quant, "dequantize_s": t_deq,
+                                  "quantize_GB/s": (4 * n + 0.515869 * n) / t_quant / 1e9,
+                                  "dequantize_GB/s": 2.515869 * n / t_deq / 1e9,
+                                  "layer_quantize_s_extrapolated": t_quant * layer_params / n,
+                                  "store_quantize_s_extrapolated_x80": 80 * t_quant * layer_params / n}
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": info["blas_threads"], "kind": "oracle",
+            "sample": f"{steps} full step(s) of {case.name} (NF4 decode + fp64 fwd + bwd), {el:.1f} s; "
+                      "breakdown: the tiny case in full, each 7B decoder linear once, the 65B q projection "
+                      "once (other 65B linears by flops), the codec on one 65B tensor (x layer, x 80)",
+            **info, "breakdown": br}
 
 
 class RotatingStep:
@@ -865,6 +963,7 @@ def main():
         "config": {"workload": f"7b_attn_T{T}", "n_out": N, "n_in": K, "tokens": T, "r": r, "alpha": 16,
                    "flops_per_step": flops, "parallelism": "single GPU"},
         "roofline": roofline,
+        "clocks": gpu_clocks(),
     }
     if not args.no_extra and tokens > 1:
         log("extra measurements: layer sets, bulk 65B store, bulk dequant, T=1 path, quantize, adapter AdamW, "
@@ -883,7 +982,7 @@ def main():
         result["extra"] = extra
     if not args.no_cpu_baseline:
         log("cpu baseline: oracle on host cores")
-        result["cpu_baseline"] = cpu_baseline(case)
+        result["cpu_baseline"] = cpu_baseline(case, workloads)
     print(json.dumps(result), flush=True)
 
 

@@ -156,7 +156,7 @@ qlora_status check_set(int64_t T, int count, const qlora_nf4_weight *q, int r, f
 // its name stands for a host-side shadow, not a device address, so host code
 // only ever uses the address hipGetSymbolAddress returns for the current
 // device (looked up on the first call on that device and kept).
-constexpr size_t kNoAllocScratchBytes = (size_t)16 << 20;
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
 static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
 
 constexpr int kMaxDevices = 64;
@@ -184,12 +184,13 @@ qlora_status noalloc_scratch(void **out) {
 }
 
 // Bytes of a linear workspace the forward touches: u (when the caller does not
-// take it) and the partial sums of its own adapter product, at the offsets of
-// the linear plan.
+// take it), the partial sums of its own adapter product and, when its fused
+// GEMM splits the contraction, the split partials, at the offsets of the
+// linear plan.
 size_t forward_scratch_bytes(const LinearPlan &p) {
-  const size_t part = gemv_applies(p.T, p.K) ? gemv_part_floats(p.T, p.N, p.K, p.r)
-                                             : lora_part_floats(p.T, p.r, p.K);
-  return p.off_part + part * 4;
+  if (gemv_applies(p.T, p.K)) return p.off_part + gemv_part_floats(p.T, p.N, p.K, p.r) * 4;
+  const size_t qsplit = qgemm_split_floats(p.T, p.N, p.K);
+  return std::max(p.off_part + lora_part_floats(p.T, p.r, p.K) * 4, qsplit ? p.off_qpart + qsplit * 4 : 0);
 }
 
 }  // namespace

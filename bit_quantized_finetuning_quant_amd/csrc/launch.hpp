@@ -82,7 +82,7 @@ struct LinearPlan {
   int64_t T, N, K;
   int r;
   bool dropout;
-  size_t off_status, off_u, off_v, off_part, off_keep, off_xd, total;
+  size_t off_status, off_u, off_v, off_part, off_qpart, off_keep, off_xd, total;
 };
 
 // LoRA dropout of one linear call (dropout.hip): the mask of the adapter input
@@ -128,9 +128,19 @@ struct QgemmSet {
 // forward: x shared, la = u_set (member i reads columns [i r, i r + r)); grad_x:
 // gx = sum over members of dy_i W_hat_i + keep (.) (scale * la lb^T) with la =
 // v_set, lb = A_set and r the total rank.
+// part: fp32 scratch for a split contraction (qgemm_split_floats of the shape; nullptr: never split).
 hipError_t launch_qgemm_set(bool trans_w, const QgemmSet &set, int64_t M, const uint16_t *x, const uint16_t *la,
                             const uint16_t *lb, int r, float scale, uint16_t *gx, const Codebook &cb, hipStream_t st,
-                            const uint32_t *keep = nullptr);
+                            const uint32_t *keep = nullptr, float *part = nullptr);
+
+// Split contraction of a single linear's fused GEMM (out [M x Ncols], contraction Kc): `splits`
+// workgroups per output tile, `steps` contraction steps of 64 each (splits == 1: none).
+struct QgemmSplit {
+  int splits;
+  int64_t steps;
+};
+QgemmSplit qgemm_split(int64_t M, int64_t Ncols, int64_t Kc);
+size_t qgemm_split_floats(int64_t M, int64_t Ncols, int64_t Kc);
 
 // Adapter products of a projection set (lora.hip); each product has its own
 // region of `part`, lora_set_part_floats in all.
@@ -145,7 +155,7 @@ hipError_t launch_lora_set_grads(const uint16_t *v_set, const uint16_t *x, const
 // qgemm.hip); keep (dropout words, [ceil(M/32)][Ncols]) may be nullptr.
 hipError_t launch_qgemm(bool trans_w, const uint16_t *act, int64_t M, int64_t Ncols, int64_t Kc, const QWeight &w,
                         const uint16_t *la, const uint16_t *lb, int r, float scale, uint16_t *out,
-                        const Codebook &cb, hipStream_t st, const uint32_t *keep = nullptr);
+                        const Codebook &cb, hipStream_t st, const uint32_t *keep = nullptr, float *part = nullptr);
 
 LinearPlan plan_linear(int64_t T, int64_t N, int64_t K, int r, bool dropout = false);
 

@@ -107,6 +107,11 @@ LinearPlan plan_linear(int64_t T, int64_t N, int64_t K, int r, bool dropout) {
   off += align256((size_t)T * r * 2);
   p.off_part = off;
   off += align256(part * 4);
+  // split contraction of the fused GEMMs (few tokens or a narrow output): fp32 partial tiles of the
+  // forward (y) or of grad_x, whichever needs more
+  p.off_qpart = off;
+  if (!gemv_applies(T, K))
+    off += align256(std::max(qgemm_split_floats(T, N, K), qgemm_split_floats(T, K, N)) * 4);
   // dropout: keep words [ceil(T/32)][K] and the dropped-out input [T x K] bf16
   p.off_keep = p.off_xd = 0;
   if (dropout) {
@@ -151,7 +156,7 @@ hipError_t launch_linear_fwd(const LinearPlan &p, const uint16_t *x, const QWeig
   if (e != hipSuccess) return e;
   TimedLaunch tl;
   const bool timed = timing_begin(st, tl, kTimedQgemmFwd);
-  e = launch_qgemm(false, x, p.T, p.N, p.K, w, u, B, p.r, scale, y, cb, st);
+  e = launch_qgemm(false, x, p.T, p.N, p.K, w, u, B, p.r, scale, y, cb, st, nullptr, (float *)(ws + p.off_qpart));
   if (timed) timing_end(st, tl);
   return e != hipSuccess ? e : hipGetLastError();
 }
@@ -189,7 +194,8 @@ hipError_t launch_linear_bwd(const LinearPlan &p, const uint16_t *dy, const uint
   if (grad_x) {  // grad_x = dy W_hat + keep (.) (s / (1 - p)) v A
     TimedLaunch tl;
     const bool timed = timing_begin(st, tl, kTimedQgemmDx);
-    e = launch_qgemm(true, dy, p.T, p.K, p.N, w, v, A, p.r, scale_ax, grad_x, cb, st, ai.keep);
+    e = launch_qgemm(true, dy, p.T, p.K, p.N, w, v, A, p.r, scale_ax, grad_x, cb, st, ai.keep,
+                     (float *)(ws + p.off_qpart));
     if (timed) timing_end(st, tl);
     if (e != hipSuccess) return e;
   }

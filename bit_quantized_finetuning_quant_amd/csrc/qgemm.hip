@@ -123,13 +123,69 @@ __device__ __forceinline__ uint32_t dma_lane_offset(int lane, int64_t Kc, int pa
   return (uint32_t)((row * Kc + 8 * chunk) * 2);
 }
 
-__device__ __forceinline__ void dma_act(const uint16_t *act, int64_t Kc, int64_t row0, int64_t kt,
-                                        const uint32_t (&lane_off)[2], uint16_t *dst, int j0 = 0, int nj = 8) {
-  const char *base = (const char *)(act + row0 * Kc + kt * QBK);
-  const uint32_t l0 = lds_addr(dst);
+// The activation DMA of one consumer wave cw: rows [64 cw, 64 cw + 64) of the
+// tile, DMA j moving rows 8 j .. 8 j + 7 of them.  kClamp (a launch whose token
+// count is not a multiple of QBM): lane rows at or past the tile's last valid
+// row read that row instead, so every address stays inside the activation and
+// the full-tile pipeline runs for any number of rows; the epilogue never
+// stores those rows.  Without kClamp the per-lane offset takes the two
+// loop-invariant values above; with it the offset is formed per DMA from the
+// lane's row (three vector instructions).
+template <bool kClamp>
+struct ActDma {
+  const char *base;   // kClamp: element (m0, first step) of the activation; else that of row m0 + 64 cw
+  int64_t row_bytes;  // 2 Kc
+  uint32_t off[2];    // !kClamp: lane offsets by the parity of j
+  int lane_row, pos, last_row;  // kClamp: tile row of the lane at j = 0, its chunk slot, last valid row
+
+  __device__ __forceinline__ void init(const uint16_t *act, int64_t Kc, int64_t M, int64_t m0, int64_t kstep0,
+                                       int cw, int lane) {
+    row_bytes = 2 * Kc;
+    base = (const char *)(act + m0 * Kc + kstep0 * QBK);
+    if (!kClamp) {
+      base += 64 * cw * row_bytes;
+      off[0] = dma_lane_offset(lane, Kc, 0);
+      off[1] = dma_lane_offset(lane, Kc, 1);
+    } else {
+      lane_row = 64 * cw + (lane >> 3);
+      pos = lane & 7;
+      last_row = (int)min((int64_t)QBM, M - m0) - 1;
+    }
+  }
+
+  // DMAs j0 .. j0 + nj - 1 of stage kt into dst (this wave's 64 rows of an LDS stage).  The base
+  // and the row length are wave-uniform; readfirstlane keeps them in scalar registers where the
+  // compiler cannot see that (an object set up under a branch on the wave index).
+  __device__ __forceinline__ void issue(int64_t kt, uint16_t *dst, int j0 = 0, int nj = 8) const {
+    const uint32_t l0 = lds_addr(dst);
+    // (readfirstlane returns a signed int: each half goes through uint32_t, so the low word is not
+    // sign-extended into the high one)
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+    const uint64_t bu = ((uint64_t)hi << 32) | (uint64_t)lo;
+    const int64_t row_bytes = (int64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)this->row_bytes);
+    const char *sb = (const char *)(uintptr_t)bu + kt * (QBK * 2);
 #pragma unroll
-  for (int j = j0; j < j0 + nj; ++j) dma16(base + (int64_t)(16 * j) * Kc, lane_off[j & 1], l0 + 8 * j * 64 * 2);
-}
+    for (int j = j0; j < j0 + nj; ++j) {
+      if (!kClamp) {
+        dma16(sb + (int64_t)(8 * j) * row_bytes, off[j & 1], l0 + 8 * j * 64 * 2);
+      } else {
+        const int row = lane_row + 8 * j;
+        const int chunk = pos ^ ((row >> 1) & 7);
+        dma16(sb, (uint32_t)min(row, last_row) * (uint32_t)row_bytes + 16u * (uint32_t)chunk, l0 + 8 * j * 64 * 2);
+      }
+    }
+  }
+
+  // every DMA of this wave has landed; the offsets a DMA reads stay untouched until then
+  __device__ __forceinline__ void wait_all() const {
+    if (!kClamp)
+      asm volatile("s_waitcnt vmcnt(0)" ::"v"(off[0]), "v"(off[1]) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::"v"(lane_row), "v"(pos) : "memory");
+  }
+};
 
 // One stage of a producer lane: its 32 weight codes (one weight row, 32
 // consecutive n_in positions) with the block's FP8 constant and group scale,
@@ -157,10 +213,11 @@ struct Producer {
   float mu;
   int ptid;
   bool act_vec;
+  int64_t kstep0;  // first contraction step of this workgroup's split
 
   // Partial tiles: the activation tile goes through registers with masking.
   __device__ __forceinline__ void load_act(int64_t kt, Stage &s) const {
-    const int64_t k0 = kt * QBK;
+    const int64_t k0 = (kstep0 + kt) * QBK;
     const int a_row = ptid >> 3, a_col = 8 * (ptid & 7);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -187,10 +244,10 @@ struct Producer {
   __device__ __forceinline__ void init_addressing() {
     const int64_t n = kTransW ? (ptid >> 2) : c0 + (ptid >> 1);
     const int64_t col = kTransW ? c0 + 32 * (ptid & 3) : 32 * (ptid & 1);
-    code0 = w.codes + n * (K / 2) + col / 2;
     code_step = kTransW ? QBK * (K / 2) : QBK / 2;
-    blk0 = n * kblk_row + col / kBlock;
     blk_step = kTransW ? QBK * kblk_row : 1;
+    code0 = w.codes + n * (K / 2) + col / 2 + kstep0 * code_step;
+    blk0 = n * kblk_row + col / kBlock + kstep0 * blk_step;
   }
 
   template <bool kFull>
@@ -207,7 +264,7 @@ struct Producer {
       }
       return;
     }
-    const int64_t k0 = kt * QBK;
+    const int64_t k0 = (kstep0 + kt) * QBK;
     const int64_t n = kTransW ? k0 + (ptid >> 2) : c0 + (ptid >> 1);
     const int64_t col = kTransW ? c0 + 32 * (ptid & 3) : k0 + 32 * (ptid & 1);
     if (n < N && col < K) {
@@ -512,7 +569,8 @@ __device__ __forceinline__ void stage_lora(const uint16_t *la, int64_t ld_la, co
 // loaded by the caller).
 template <bool kTransW, bool kDQ>
 __device__ __forceinline__ Producer<kTransW, kDQ> member_producer(const QgemmMember &mm, const uint16_t *x, int64_t M,
-                                                                  int64_t m0, int64_t c0, int tid, float mu) {
+                                                                  int64_t m0, int64_t c0, int tid, float mu,
+                                                                  int64_t kstep0) {
   Producer<kTransW, kDQ> p;
   const int64_t Kc = kTransW ? mm.w.n_out : mm.w.n_in;
   p.act = kTransW ? mm.act : x;
@@ -527,6 +585,7 @@ __device__ __forceinline__ Producer<kTransW, kDQ> member_producer(const QgemmMem
   p.mu = mu;
   p.ptid = tid - 256;
   p.act_vec = (Kc % 8) == 0;
+  p.kstep0 = kstep0;
   p.init_addressing();
   return p;
 }
@@ -546,11 +605,18 @@ __device__ __forceinline__ QgemmMember set_member(const QgemmSet &s, int i) {
 //     the adapter term uses la = v_set, lb = A_set and r = the set's total
 //     rank; out = grad_x.
 // kDrop (grad_x only): the adapter term is masked by the LoRA dropout words.
-template <bool kTransW, bool kDQ, bool kDrop>
+// kClamp: M is not a multiple of QBM; the last row tile's missing rows read a
+// valid row (ActDma) and are never stored, so it runs the full-tile pipeline.
+// Split contraction (single linear only; part != nullptr): workgroup z of the
+// grid's third dimension contracts steps [z split_steps, (z + 1) split_steps)
+// and writes its fp32 tile to part[z][M][Ncols]; split 0 also carries the
+// adapter term; qgemm_split_reduce adds the splits in order.
+template <bool kTransW, bool kDQ, bool kDrop, bool kClamp>
 __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const uint16_t *__restrict__ x,
                                                 const uint16_t *__restrict__ la, const uint16_t *__restrict__ lb,
                                                 int r, float scale, uint16_t *__restrict__ gx, Codebook cb,
-                                                const uint32_t *__restrict__ keep) {
+                                                const uint32_t *__restrict__ keep, float *__restrict__ part,
+                                                int64_t split_steps) {
   __shared__ __attribute__((aligned(16))) uint16_t sa[kActStages][QBM * 64];
   __shared__ __attribute__((aligned(16))) uint16_t sb[2][QBN * QLD];  // = 64 * TLD
   __shared__ float lut[16];
@@ -583,8 +649,17 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
   const uint16_t *lb_t = kTransW ? lb : fm.lb;
   uint16_t *out = kTransW ? gx : fm.out;
   const int m_begin = kTransW ? 0 : mf, m_end = kTransW ? set.count : mf + 1;
-  // full (per member): every row, column and contraction step of the tile is
-  // in range and activation rows are 16-byte aligned
+  // full (per member): every column and contraction step of the tile is in
+  // range (and, without kClamp, every row)
+  const bool rows_ok = kClamp || m0 + QBM <= M;
+  // this workgroup's contraction steps (a split, or all of them) and its rank
+  // of the adapter term (only split 0 adds it)
+  const int64_t kstep0 = part ? (int64_t)blockIdx.z * split_steps : 0;
+  const int r_eff = blockIdx.z == 0 ? r : 0;
+  auto member_steps = [&](int64_t Kc) {
+    const int64_t nk = (Kc + QBK - 1) / QBK;
+    return part ? min(split_steps, nk - kstep0) : nk;
+  };
 
   // Level table for the producers' decode of partial tiles.
   if (tid < 16) lut[tid] = cb.v[tid];
@@ -594,7 +669,6 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
   const int wm = wave >> 1, wn = wave & 1;
   const int l32 = lane & 31, lhi = lane >> 5;
   const int cw = __builtin_amdgcn_readfirstlane(wave);  // consumer wave: DMA rows [64 cw, 64 cw + 64)
-  const int64_t dma_row0 = m0 + 64 * cw;
 
   // The pipeline's first memory accesses go out before the LoRA term, so that
   // their latency overlaps its staging: for full tiles of the first member the
@@ -603,10 +677,10 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
   // staging).
   const QgemmMember m_first = set_member(set, m_begin);
   const int64_t Kc_first = kTransW ? m_first.w.n_out : m_first.w.n_in;
-  const int64_t nk_first = (Kc_first + QBK - 1) / QBK;
-  const bool full_first = (m0 + QBM <= M) && (c0 + QBN <= Ncols) && (Kc_first % QBK == 0);
+  const int64_t nk_first = member_steps(Kc_first);
+  const bool full_first = rows_ok && (c0 + QBN <= Ncols) && (Kc_first % QBK == 0);
   Stage pre0, pre1, pre2;
-  uint32_t dma_off_first[2] = {0u, 0u};
+  ActDma<kClamp> dma_first;
   // every member's tensor mean, fetched with the first codes
   float mu0 = 0.f, mu1 = 0.f, mu2 = 0.f, mu3 = 0.f;
   if (tid >= 256) {
@@ -617,13 +691,13 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
       if (m_begin + 3 < m_end) mu3 = *set_member(set, m_begin + 3).w.mu;
     }
     if (full_first)
-      fetch_first_codes(member_producer<kTransW, kDQ>(m_first, x, M, m0, c0, tid, 0.f), nk_first, pre0, pre1, pre2);
+      fetch_first_codes(member_producer<kTransW, kDQ>(m_first, x, M, m0, c0, tid, 0.f, kstep0), nk_first, pre0, pre1,
+                        pre2);
   } else if (full_first) {
     const uint16_t *act = kTransW ? m_first.act : x;
-    dma_off_first[0] = dma_lane_offset(lane, Kc_first, 0);
-    dma_off_first[1] = dma_lane_offset(lane, Kc_first, 1);
-    dma_act(act, Kc_first, dma_row0, 0, dma_off_first, sa[0] + 64 * cw * 64);
-    dma_act(act, Kc_first, dma_row0, min((int64_t)1, nk_first - 1), dma_off_first, sa[1] + 64 * cw * 64);
+    dma_first.init(act, Kc_first, M, m0, kstep0, cw, lane);
+    dma_first.issue(0, sa[0] + 64 * cw * 64);
+    dma_first.issue(min((int64_t)1, nk_first - 1), sa[1] + 64 * cw * 64);
   }
 
   // LoRA term first, scaled: acc = scale * la lb^T, staged chunk by chunk in
@@ -640,20 +714,23 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-  for (int j0 = 0; j0 < r; j0 += QBK) {
+  for (int j0 = 0; j0 < r_eff; j0 += QBK) {
     stage_lora<kTransW>(la_t, set.ld_la, lb_t, r, j0, M, Ncols, m0, c0, tid, sa[2], sb[1]);
     // every wave's early DMA of stages 0 and 1 has landed before the barrier
     // (the staging's loads, issued after them, have returned already); naming
     // the lane offsets keeps their registers untouched until then
-    if (tid < 256) asm volatile("s_waitcnt vmcnt(0)" ::"v"(dma_off_first[0]), "v"(dma_off_first[1]) : "memory");
+    if (tid < 256) dma_first.wait_all();
     __syncthreads();
     if (tid < 256) {
       consumer_slices<kTransW>(sa[2], sb[1], wm, wn, lane, acc);
       __syncthreads();
-    } else if (j0 + QBK < r) {
+    } else if (j0 + QBK < r_eff) {
       __syncthreads();
     }
   }
+  // no adapter term (a split past the first): the early DMA has landed before
+  // the consumers' "stage 0 ready" barrier below
+  if (r_eff == 0 && tid < 256) dma_first.wait_all();
   if (tid < 256) {
     if (kTransW && kDrop) {
       // LoRA dropout (grad_x): the adapter term of (row, column) is kept where
@@ -688,12 +765,12 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
     for (int mi = m_begin; mi < m_end; ++mi) {
       const QgemmMember mm = set_member(set, mi);
       const int64_t Kc = kTransW ? mm.w.n_out : mm.w.n_in;
-      const int64_t nk = (Kc + QBK - 1) / QBK;
-      const bool full = (m0 + QBM <= M) && (c0 + QBN <= Ncols) && (Kc % QBK == 0);
+      const int64_t nk = member_steps(Kc);
+      const bool full = rows_ok && (c0 + QBN <= Ncols) && (Kc % QBK == 0);
       if (mi > m_begin) wg_barrier();  // the previous member's pipeline has drained
       const int mo = mi - m_begin;
       const float mu = mo == 0 ? mu0 : mo == 1 ? mu1 : mo == 2 ? mu2 : mu3;
-      const Producer<kTransW, kDQ> p = member_producer<kTransW, kDQ>(mm, x, M, m0, c0, tid, mu);
+      const Producer<kTransW, kDQ> p = member_producer<kTransW, kDQ>(mm, x, M, m0, c0, tid, mu, kstep0);
       if (full) {
         if (mi > m_begin) fetch_first_codes(p, nk, pre0, pre1, pre2);  // the first member's went out early
         producer_loop_full(p, nk, sb, pre0, pre1, pre2, cb);
@@ -711,19 +788,22 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
   const QgemmMember mm = set_member(set, mi);
   const uint16_t *act = kTransW ? mm.act : x;
   const int64_t Kc = kTransW ? mm.w.n_out : mm.w.n_in;
-  const int64_t nk = (Kc + QBK - 1) / QBK;
-  const bool full = (m0 + QBM <= M) && (c0 + QBN <= Ncols) && (Kc % QBK == 0);
+  const int64_t nk = member_steps(Kc);
+  const bool full = rows_ok && (c0 + QBN <= Ncols) && (Kc % QBK == 0);
   if (mi > m_begin) wg_barrier();  // every wave is done with the previous member's LDS stages
-  const uint32_t dma_lane_off[2] = {dma_lane_offset(lane, Kc, 0), dma_lane_offset(lane, Kc, 1)};
+  ActDma<kClamp> dma;
+  dma.init(act, Kc, M, m0, kstep0, cw, lane);
   if (full) {
     if (mi > m_begin) {
-      dma_act(act, Kc, dma_row0, 0, dma_lane_off, sa[0] + 64 * cw * 64);
-      dma_act(act, Kc, dma_row0, min((int64_t)1, nk - 1), dma_lane_off, sa[1] + 64 * cw * 64);
+      dma.issue(0, sa[0] + 64 * cw * 64);
+      dma.issue(min((int64_t)1, nk - 1), sa[1] + 64 * cw * 64);
     }
-    dma_act(act, Kc, dma_row0, min((int64_t)2, nk - 1), dma_lane_off, sa[2] + 64 * cw * 64);
+    dma.issue(min((int64_t)2, nk - 1), sa[2] + 64 * cw * 64);
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(16, 0));  // stage 0 has landed
   }
-  if (mi > m_begin) wg_barrier();  // stage 0 ready (the first member's: at the LoRA term's last barrier)
+  // stage 0 ready (the first member's: at the LoRA term's last barrier, when
+  // there is an adapter term)
+  if (mi > m_begin || r_eff == 0) wg_barrier();
   StageFrags f;
 #pragma unroll
   for (int kk = 0; kk < QBK / 16; ++kk) {
@@ -765,7 +845,7 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
         acc[i][0] = mfma(f.a[kk][i], f.b[kk][0], acc[i][0]);
         __builtin_amdgcn_sched_barrier(0);
         if (kk > 0 && i < 2) f.b[kk - 1][i] = load_b_frag<kTransW>(nb, wn, lane, kk - 1, i);
-        if (i >= 2 && full) dma_act(act, Kc, dma_row0, dma_kt, dma_lane_off, dma_dst, 2 * kk + i - 2, 1);
+        if (i >= 2 && full) dma.issue(dma_kt, dma_dst, 2 * kk + i - 2, 1);
         __builtin_amdgcn_sched_barrier(0);
         acc[i][1] = mfma(f.a[kk][i], f.b[kk][1], acc[i][1]);
         __builtin_amdgcn_sched_barrier(0);
@@ -784,8 +864,26 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
   // No LDS-DMA may still be writing when the next member's stages start or the
   // workgroup's LDS is released; the wait names the lane offsets so that their
   // registers stay untouched until then.
-  asm volatile("s_waitcnt vmcnt(0)" ::"v"(dma_lane_off[0]), "v"(dma_lane_off[1]) : "memory");
+  dma.wait_all();
   }  // members
+
+  if (part) {
+    // a split: the fp32 tile goes straight from the accumulators to part[z]
+    // (each store instruction covers 32 consecutive columns of two rows)
+    float *pz = part + (int64_t)blockIdx.z * M * Ncols;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int64_t col = c0 + wn * 64 + j * 32 + l32;
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int64_t row = m0 + wm * 128 + i * 32 + 8 * (q >> 2) + 4 * lhi + (q & 3);
+          if (row < M && col < Ncols) pz[row * Ncols + col] = acc[i][j][q];
+        }
+      }
+    return;
+  }
 
   // Epilogue through LDS: the tile is rounded to bf16 into [256][136] (the
   // activation ring's storage), then written out as 16-byte row chunks.  The
@@ -819,47 +917,135 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
   }
 }
 
+// The splits of a grid: sum over the splits, in split order, rounded to bf16
+// once (8 columns per thread; Ncols is a multiple of QBN here).
+__global__ __launch_bounds__(256) void qgemm_split_reduce(const float *__restrict__ part, int S, int64_t M,
+                                                          int64_t Ncols, uint16_t *__restrict__ out) {
+  const int64_t n8 = M * Ncols / 8, zs = M * Ncols / 4;  // zs: one split in float4 units
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+    const f32x4 *p = (const f32x4 *)part + 2 * i;
+    f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
+    for (int z0 = 0; z0 < S; z0 += 4) {
+      f32x4 v[4][2];
+#pragma unroll
+      for (int z = 0; z < 4; ++z) {
+        const bool in = z0 + z < S;
+        v[z][0] = in ? p[(int64_t)(z0 + z) * zs] : f32x4{0.f, 0.f, 0.f, 0.f};
+        v[z][1] = in ? p[(int64_t)(z0 + z) * zs + 1] : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll
+      for (int z = 0; z < 4; ++z)
+        if (z0 + z < S) {
+          a += v[z][0];
+          b += v[z][1];
+        }
+    }
+    *(u32x4 *)&out[8 * i] = u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                                  pack_bf16x2(b[2], b[3])};
+  }
+}
+
+template <bool kTransW, bool kDQ, bool kDrop>
+void launch_ws(bool clamp, dim3 g, hipStream_t st, const QgemmSet &s, int64_t M, const uint16_t *x,
+               const uint16_t *la, const uint16_t *lb, int r, float scale, uint16_t *gx, const Codebook &cb,
+               const uint32_t *keep, float *part, int64_t split_steps) {
+  if (clamp)
+    qgemm_ws<kTransW, kDQ, kDrop, true><<<g, 512, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, keep, part,
+                                                            split_steps);
+  else
+    qgemm_ws<kTransW, kDQ, kDrop, false><<<g, 512, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, keep, part,
+                                                             split_steps);
+}
+
 }  // namespace
+
+// A single linear whose tile grid fills the 256 CUs poorly (few tokens, or a
+// tile count just past a multiple of 256) splits its contraction.  One
+// workgroup runs per CU, so a launch of W workgroups takes ceil(W / 256)
+// rounds, each as long as one workgroup: about 4 steps of set-up and epilogue
+// plus its contraction steps (64 wide, about 1 us each at full occupancy).
+// The split count minimises that estimate plus the reduction's reading of the
+// fp32 partials (at about 4 GB per ms), with at least 4 steps per split.  Only
+// shapes whose tiles are full in columns and contraction split, so every
+// workgroup runs the full-tile pipeline.
+QgemmSplit qgemm_split(int64_t M, int64_t Ncols, int64_t Kc) {
+  QgemmSplit sp{1, 0};
+  if (M < 1 || Ncols % QBN != 0 || Kc % QBK != 0) return sp;
+  const int64_t tiles = (M + QBM - 1) / QBM * (Ncols / QBN), nk = Kc / QBK;
+  double best = 0.0;
+  for (int64_t S = 1; S <= std::min<int64_t>(64, nk / 4) || S == 1; ++S) {
+    const int64_t steps = (nk + S - 1) / S, splits = (nk + steps - 1) / steps;
+    if (splits != S) continue;
+    const double rounds = (double)((tiles * S + 255) / 256);
+    const double reduce_us = S > 1 ? (double)S * M * Ncols * 4.0 / 4e6 + 3.0 : 0.0;
+    const double cost = rounds * (4.0 + (double)steps) + reduce_us;
+    if (S == 1 || cost < best) {
+      best = cost;
+      sp = S > 1 ? QgemmSplit{(int)S, steps} : QgemmSplit{1, 0};
+    }
+  }
+  return sp;
+}
+
+size_t qgemm_split_floats(int64_t M, int64_t Ncols, int64_t Kc) {
+  const QgemmSplit sp = qgemm_split(M, Ncols, Kc);
+  return sp.splits > 1 ? (size_t)sp.splits * M * Ncols : 0;
+}
 
 hipError_t launch_qgemm_set(bool trans_w, const QgemmSet &set, int64_t M, const uint16_t *x, const uint16_t *la,
                             const uint16_t *lb, int r, float scale, uint16_t *gx, const Codebook &cb, hipStream_t st,
-                            const uint32_t *keep) {
+                            const uint32_t *keep, float *part) {
   if (set.count < 1 || set.count > kMaxSetMembers) return hipErrorInvalidValue;
   QgemmSet s = set;
-  int64_t ytiles = 0;
+  int64_t ytiles = 0, kc_max = 0;
   if (!trans_w) {
     for (int i = 0; i < s.count; ++i) {
       s.m[i].tile0 = ytiles;
       ytiles += (s.m[i].w.n_out + QBN - 1) / QBN;
     }
+    kc_max = s.m[0].w.n_in;
   } else {
     ytiles = (s.m[0].w.n_in + QBN - 1) / QBN;
+    for (int i = 0; i < s.count; ++i) kc_max = std::max(kc_max, s.m[i].w.n_out);
   }
   for (int i = s.count; i < kMaxSetMembers; ++i) s.m[i] = s.m[0];
-  const dim3 g((unsigned)((M + QBM - 1) / QBM), (unsigned)ytiles);
+  // the last row tile's missing rows read a valid row (byte offsets within a
+  // tile stay below 2^32)
+  const bool clamp = (M % QBM) != 0 && kc_max < ((int64_t)1 << 22);
+  const int64_t Ncols = trans_w ? s.m[0].w.n_in : s.m[0].w.n_out;
+  QgemmSplit sp{1, 0};
+  if (part && s.count == 1) sp = qgemm_split(M, Ncols, kc_max);
+  float *pz = sp.splits > 1 ? part : nullptr;
+  const dim3 g((unsigned)((M + QBM - 1) / QBM), (unsigned)ytiles, (unsigned)sp.splits);
   const bool dq = s.m[0].w.dq;
   if (!trans_w) {  // the forward never takes a dropout mask
     if (dq)
-      qgemm_ws<false, true, false><<<g, 512, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, nullptr);
+      launch_ws<false, true, false>(clamp, g, st, s, M, x, la, lb, r, scale, gx, cb, nullptr, pz, sp.steps);
     else
-      qgemm_ws<false, false, false><<<g, 512, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, nullptr);
+      launch_ws<false, false, false>(clamp, g, st, s, M, x, la, lb, r, scale, gx, cb, nullptr, pz, sp.steps);
   } else if (keep) {
     if (dq)
-      qgemm_ws<true, true, true><<<g, 512, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, keep);
+      launch_ws<true, true, true>(clamp, g, st, s, M, x, la, lb, r, scale, gx, cb, keep, pz, sp.steps);
     else
-      qgemm_ws<true, false, true><<<g, 512, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, keep);
+      launch_ws<true, false, true>(clamp, g, st, s, M, x, la, lb, r, scale, gx, cb, keep, pz, sp.steps);
   } else {
     if (dq)
-      qgemm_ws<true, true, false><<<g, 512, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, nullptr);
+      launch_ws<true, true, false>(clamp, g, st, s, M, x, la, lb, r, scale, gx, cb, nullptr, pz, sp.steps);
     else
-      qgemm_ws<true, false, false><<<g, 512, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, nullptr);
+      launch_ws<true, false, false>(clamp, g, st, s, M, x, la, lb, r, scale, gx, cb, nullptr, pz, sp.steps);
+  }
+  if (pz) {
+    uint16_t *out = trans_w ? gx : s.m[0].out;
+    int64_t blocks = (M * Ncols / 8 + 255) / 256;
+    if (blocks > 2048) blocks = 2048;
+    qgemm_split_reduce<<<(unsigned)blocks, 256, 0, st>>>(pz, sp.splits, M, Ncols, out);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_qgemm(bool trans_w, const uint16_t *act, int64_t M, int64_t Ncols, int64_t Kc, const QWeight &w,
                         const uint16_t *la, const uint16_t *lb, int r, float scale, uint16_t *out,
-                        const Codebook &cb, hipStream_t st, const uint32_t *keep) {
+                        const Codebook &cb, hipStream_t st, const uint32_t *keep, float *part) {
   (void)Ncols;
   (void)Kc;
   QgemmSet s{};
@@ -868,11 +1054,11 @@ hipError_t launch_qgemm(bool trans_w, const uint16_t *act, int64_t M, int64_t Nc
   s.m[0].w = w;
   if (trans_w) {
     s.m[0].act = act;
-    return launch_qgemm_set(true, s, M, nullptr, la, lb, r, scale, out, cb, st, keep);
+    return launch_qgemm_set(true, s, M, nullptr, la, lb, r, scale, out, cb, st, keep, part);
   }
   s.m[0].lb = lb;
   s.m[0].out = out;
-  return launch_qgemm_set(false, s, M, act, la, nullptr, r, scale, nullptr, cb, st, nullptr);
+  return launch_qgemm_set(false, s, M, act, la, nullptr, r, scale, nullptr, cb, st, nullptr, part);
 }
 
 }  // namespace qlora

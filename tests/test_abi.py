@@ -300,9 +300,9 @@ def test_noalloc_forward_refuses_what_its_scratch_cannot_hold():
 
     lib = qlora.lib()
     limit = lib.qlora_linear_fwd_noalloc_max_bytes()
-    assert limit == 16 << 20
+    assert limit == 64 << 20
     fake = 1 << 20  # 16-byte aligned, never dereferenced
-    # u alone: T x r bf16 beyond the limit (T = 65536, r = 256: 32 MiB)
+    # u and v: T x r bf16 each (T = 65536, r = 256: 32 MiB each), past the limit
     st = qlora.NF4WeightStruct(4096, 4096, fake, fake, fake, fake, 0)
     rc = lib.qlora_linear_fwd_noalloc(fake, 65536, ctypes.byref(st), fake, fake, 256, 1.0, fake, 0, None)
     assert rc == 10 and "scratch" in qlora.status_string(rc)

@@ -64,7 +64,8 @@ def _check(case, p, seed, need_u=True):
     return errs
 
 
-@pytest.mark.parametrize("shape", [(300, 320, 300, 24), (1000, 640, 513, 64), (77, 192, 259, 5), (256, 128, 17, 256)])
+@pytest.mark.parametrize("shape", [(300, 320, 300, 24), (1000, 640, 513, 64), (77, 192, 259, 5), (256, 128, 17, 256),
+                                   (512, 2048, 40, 16), (1024, 1024, 300, 64)])
 def test_fused_gemm_path(shape):
     n_out, n_in, T, r = shape
     announce(f"dropout linear n_out={n_out} n_in={n_in} T={T} r={r}")

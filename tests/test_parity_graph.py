@@ -11,21 +11,23 @@ from helpers import announce, dev_bf16, dev_f32, host
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("T", [1, 3, 300])
-def test_captured_step_replays_equal_eager(T):
+@pytest.mark.parametrize("T,N,K", [(1, 512, 320), (3, 512, 320), (300, 512, 320), (40, 512, 2048)])
+def test_captured_step_replays_equal_eager(T, N, K):
+    """T = 40 at 512 x 2048 splits the contraction of both fused GEMMs (a reduction kernel after
+    each), and its 40 rows run clamped in a 256-row tile."""
     torch = __import__("torch")
-    announce(f"graph capture fwd+bwd 512x320 T={T} r=16")
-    case = workloads.custom_case(512, 320, T, 16, 16.0, seed=50 + T)
+    announce(f"graph capture fwd+bwd {N}x{K} T={T} r=16")
+    case = workloads.custom_case(N, K, T, 16, 16.0, seed=50 + T)
     q = qlora.quantize(dev_f32(case.w))
     a, b = dev_bf16(case.a), dev_bf16(case.b)
     x, dy = dev_bf16(case.x), dev_bf16(case.dy)
     bf, f32 = torch.bfloat16, torch.float32
-    y = torch.empty((T, 512), dtype=bf, device="cuda")
+    y = torch.empty((T, N), dtype=bf, device="cuda")
     u = torch.empty((T, 16), dtype=bf, device="cuda")
-    gx = torch.empty((T, 320), dtype=bf, device="cuda")
-    ga = torch.empty((16, 320), dtype=f32, device="cuda")
-    gb = torch.empty((512, 16), dtype=f32, device="cuda")
-    ws = qlora.linear_workspace(T, 512, 320, 16)
+    gx = torch.empty((T, K), dtype=bf, device="cuda")
+    ga = torch.empty((16, K), dtype=f32, device="cuda")
+    gb = torch.empty((N, 16), dtype=f32, device="cuda")
+    ws = qlora.linear_workspace(T, N, K, 16)
 
     def step():
         qlora.linear_fwd(x, q, a, b, case.scale, y=y, u_out=u, workspace=ws)
@@ -41,8 +43,8 @@ def test_captured_step_replays_equal_eager(T):
         step()
     rng = np.random.default_rng(T)
     for rep in range(3):
-        xs = workloads.to_bf16_bits(rng.standard_normal((T, 320)).astype(np.float32))
-        dys = workloads.to_bf16_bits(rng.standard_normal((T, 512)).astype(np.float32))
+        xs = workloads.to_bf16_bits(rng.standard_normal((T, K)).astype(np.float32))
+        dys = workloads.to_bf16_bits(rng.standard_normal((T, N)).astype(np.float32))
         x.copy_(dev_bf16(xs))
         dy.copy_(dev_bf16(dys))
         g.replay()

@@ -65,6 +65,20 @@ def test_ragged_multi_tile_shapes(shape):
     _check_case(case)
 
 
+@pytest.mark.parametrize("shape", [(512, 2048, 40, 16), (1024, 1024, 300, 64), (4096, 4096, 64, 64),
+                                   (2048, 8192, 8, 8), (256, 4096, 5, 32), (1408, 1024, 129, 64)])
+def test_split_contraction_and_clamped_rows(shape):
+    """Token counts that are not a multiple of the 256-row tile run the full-tile pipeline with the
+    missing rows clamped to a valid row; grids too small to fill the chip split the contraction
+    (fp32 partial tiles added in split order).  Shapes: splits in both directions, clamped rows,
+    T = 5 (just past the few-token path), the 7B projection at T = 64."""
+    n_out, n_in, T, r = shape
+    announce(f"linear split/clamp n_out={n_out} n_in={n_in} T={T} r={r}")
+    case = workloads.custom_case(n_out, n_in, T, r, 16.0, seed=n_out + 7 * T)
+    _check_case(case)
+    _check_case(case, scale=1.5, need_u=False)
+
+
 @pytest.mark.parametrize("shape", [(300, 320, 1, 24), (77, 192, 2, 5), (64, 64, 2, 256), (1000, 11008, 1, 64),
                                    (11008, 4096, 2, 64), (130, 2112, 3, 13), (515, 4160, 4, 64), (8, 64, 4, 1)])
 def test_few_token_path(shape):
