@@ -279,8 +279,11 @@ def extra_layers(torch, qlora, workloads, steps):
     out = {}
     normal = lambda g, n, k, w: w.normal_(0.0, 0.02, generator=g)
     student = lambda g, n, k, w: _student_t_weight(torch, g, n, k, w)
+    # layers_65b_T512: one GPU's share of the 65B layer under 8-way data parallelism (4096 tokens split
+    # over 8 GPUs: every GPU holds the whole packed layer and runs 512 tokens)
     for tag, shapes, tokens, weight, pad in (("layers_7b", workloads.SHAPES_7B, 2048, normal, False),
-                                             ("layers_65b", workloads.SHAPES_65B, 4096, student, True)):
+                                             ("layers_65b", workloads.SHAPES_65B, 4096, student, True),
+                                             ("layers_65b_T512", workloads.SHAPES_65B, 512, student, True)):
         log(f"extra: {tag} ({len(shapes)} linears, {tokens} tokens)")
         ls = LayerSet(torch, qlora, shapes, tokens, weight, pad_rows=pad, seed=len(tag))
         for _ in range(2):
