@@ -66,9 +66,10 @@ constexpr int64_t kMaxNumel = (int64_t)1 << 37;
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
-bool shape_ok(int64_t n_out, int64_t n_in) {
-  return n_out > 0 && n_in > 0 && n_out <= kMaxNumel && n_in <= kMaxNumel && n_out * n_in <= kMaxNumel;
-}
+// a * b <= kMaxNumel for positive a, b, without forming a product that could overflow
+bool product_ok(int64_t a, int64_t b) { return a > 0 && b > 0 && a <= kMaxNumel / b; }
+
+bool shape_ok(int64_t n_out, int64_t n_in) { return product_ok(n_out, n_in); }
 
 bool double_quantized(const qlora_nf4_weight *q) { return (q->flags & QLORA_NF4_FP32_CONSTANTS) == 0u; }
 
@@ -93,7 +94,7 @@ qlora_status check_linear(int64_t T, const qlora_nf4_weight *q, int r, float sca
   qlora_status s = check_weight(q);
   if (s != QLORA_OK) return s;
   if (T < 1 || T > kMaxNumel || q->n_in % kBlock != 0 || r < 1 || r > 256) return QLORA_ERR_SHAPE;
-  if (T * q->n_in > kMaxNumel || T * q->n_out > kMaxNumel) return QLORA_ERR_SHAPE;
+  if (!product_ok(T, q->n_in) || !product_ok(T, q->n_out)) return QLORA_ERR_SHAPE;
   if (!std::isfinite(scale)) return QLORA_ERR_VALUE;
   return QLORA_OK;
 }
@@ -146,7 +147,7 @@ qlora_status check_set(int64_t T, int count, const qlora_nf4_weight *q, int r, f
     if (q[i].flags != q[0].flags) return QLORA_ERR_VALUE;
     N[i] = q[i].n_out;
   }
-  if (T * (int64_t)count * r > kMaxNumel) return QLORA_ERR_SHAPE;
+  if (!product_ok(T, (int64_t)count * r)) return QLORA_ERR_SHAPE;
   return QLORA_OK;
 }
 
@@ -229,14 +230,19 @@ size_t qlora_quantize_workspace_bytes(int64_t n_out, int64_t n_in) {
   return 256 + kQuantizeBinBytes + (size_t)nb * 4;
 }
 
+// the shapes every linear call accepts (check_linear), for the size helpers
+bool linear_shape_ok(int64_t T, int64_t n_out, int64_t n_in, int r) {
+  return shape_ok(n_out, n_in) && n_in % kBlock == 0 && r >= 1 && r <= 256 && product_ok(T, n_in) &&
+         product_ok(T, n_out);
+}
+
 size_t qlora_linear_workspace_bytes(int64_t T, int64_t n_out, int64_t n_in, int r) {
-  if (T < 1 || !shape_ok(n_out, n_in) || n_in % kBlock != 0 || r < 1 || r > 256) return 0;
+  if (!linear_shape_ok(T, n_out, n_in, r)) return 0;
   return plan_linear(T, n_out, n_in, r).total;
 }
 
 size_t qlora_linear_dropout_workspace_bytes(int64_t T, int64_t n_out, int64_t n_in, int r) {
-  if (T < 1 || !shape_ok(n_out, n_in) || n_in % kBlock != 0 || r < 1 || r > 256) return 0;
-  if (T * n_in > kMaxNumel) return 0;
+  if (!linear_shape_ok(T, n_out, n_in, r)) return 0;
   return plan_linear(T, n_out, n_in, r, true).total;
 }
 
@@ -246,7 +252,11 @@ void qlora_nf4_codebook(float out[16]) {
 }
 
 const char *qlora_status_string(qlora_status s) {
-  switch (s) {
+  // C callers and bindings may pass any integer: read the code as one (loading an enum object that
+  // holds a value outside the enumeration is undefined in C++)
+  int code;
+  memcpy(&code, &s, sizeof code);
+  switch (code) {
     case QLORA_OK: return "ok";
     case QLORA_ERR_NULL: return "a required pointer is NULL";
     case QLORA_ERR_SHAPE: return "a dimension is out of range";
@@ -270,13 +280,15 @@ qlora_status qlora_quantize(const void *w, qlora_dtype w_dtype, const qlora_nf4_
   if (s != QLORA_OK) return s;
   if (!w || !ws) return QLORA_ERR_NULL;
   if (!aligned16(w) || !aligned16(ws)) return QLORA_ERR_ALIGN;
-  if (w_dtype != QLORA_F32 && w_dtype != QLORA_BF16) return QLORA_ERR_DTYPE;
+  int dtype;  // read as an integer: a caller may pass any value (see qlora_status_string)
+  memcpy(&dtype, &w_dtype, sizeof dtype);
+  if (dtype != QLORA_F32 && dtype != QLORA_BF16) return QLORA_ERR_DTYPE;
   if (ws_bytes < qlora_quantize_workspace_bytes(q->n_out, q->n_in)) return QLORA_ERR_WORKSPACE;
   char *base = (char *)ws;
   // without double quantization the block constants go straight to absmax_scale
   const bool dq = double_quantized(q);
   float *c1 = dq ? (float *)(base + 256 + kQuantizeBinBytes) : q->absmax_scale;
-  hipError_t e = launch_quantize(w, w_dtype == QLORA_BF16, dq, q->n_out * q->n_in, q->codes, q->absmax_fp8,
+  hipError_t e = launch_quantize(w, dtype == QLORA_BF16, dq, q->n_out * q->n_in, q->codes, q->absmax_fp8,
                                  q->absmax_scale, q->absmax_mean, (uint32_t *)base,
                                  (unsigned long long *)(base + 256), c1, tables().mid, (hipStream_t)stream);
   return e == hipSuccess ? QLORA_OK : QLORA_ERR_HIP;
@@ -434,9 +446,9 @@ qlora_status qlora_linear_bwd_dropout(const uint16_t *dy, const uint16_t *x, int
 
 size_t qlora_linear_set_workspace_bytes(int64_t T, int count, const int64_t *n_out, int64_t n_in, int r) {
   if (!n_out || count < 1 || count > kMaxSetMembers || T < 1 || T > kMaxNumel) return 0;
-  if (n_in % kBlock != 0 || r < 1 || r > 256) return 0;
+  if (n_in % kBlock != 0 || r < 1 || r > 256 || !product_ok(T, (int64_t)count * r)) return 0;
   for (int i = 0; i < count; ++i)
-    if (!shape_ok(n_out[i], n_in)) return 0;
+    if (!linear_shape_ok(T, n_out[i], n_in, r)) return 0;
   return plan_linear_set(T, count, n_out, n_in, r).total;
 }
 
@@ -487,7 +499,7 @@ qlora_status qlora_linear_set_bwd(const uint16_t *const *dy, const uint16_t *x, 
 
 qlora_status qlora_dropout_mask(const uint16_t *x, int64_t T, int64_t K, double dropout_p, uint64_t seed,
                                 uint32_t *keep_words, uint16_t *x_drop, void *stream) {
-  if (T < 1 || K < 1 || K % 8 != 0 || T > kMaxNumel || K > kMaxNumel || T * K > kMaxNumel) return QLORA_ERR_SHAPE;
+  if (K % 8 != 0 || !product_ok(T, K)) return QLORA_ERR_SHAPE;
   Dropout d;
   if (!make_dropout(dropout_p, seed, &d)) return QLORA_ERR_VALUE;
   if (!x || !keep_words || !x_drop) return QLORA_ERR_NULL;
