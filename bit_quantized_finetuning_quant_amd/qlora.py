@@ -8,6 +8,7 @@ fallback: if the library is missing, every call raises.
 
 import ctypes
 import os
+import threading
 from dataclasses import dataclass
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -175,11 +176,50 @@ def _dtypes():
     return _DT
 
 
+_TRUST = threading.local()
+
+
+class trusted_calls:
+    """Context manager: inside it the calls of this thread skip the per-tensor checks below (about
+    1 us of host time per tensor, which is most of a few-token step's launch cost).  For loops that
+    repeat calls on tensors already checked once (the same shapes, dtypes and device)."""
+
+    def __enter__(self):
+        self.prev = getattr(_TRUST, "on", False)
+        _TRUST.on = True
+        return self
+
+    def __exit__(self, *exc):
+        _TRUST.on = self.prev
+        return False
+
+
+class _NoChecks:
+    __slots__ = ()
+
+    def bf16(self, t, name, shape):
+        pass
+
+    def f32(self, t, name, shape):
+        pass
+
+    def done(self):
+        pass
+
+
+_NO_CHECKS = _NoChecks()
+
+
 class _Args:
     """Checks of one call's tensors: dtype, exact shape and contiguity as each is named, then
     (done) that every one of them is on the packed weight's CUDA device."""
 
     __slots__ = ("device", "named")
+
+    def __new__(cls, device):
+        if getattr(_TRUST, "on", False):
+            return _NO_CHECKS
+        return super().__new__(cls)
 
     def __init__(self, device):
         self.device = device
@@ -210,13 +250,16 @@ class _Args:
                 raise ValueError(f"{name} must be on {dev}, not {t.device}")
 
 
-def _workspace(ws, device, need: int) -> int:
-    """Checks a caller's workspace (a contiguous uint8 CUDA tensor of at least `need` bytes)."""
+def _workspace(ws, device, need) -> int:
+    """Checks a caller's workspace (a contiguous uint8 CUDA tensor of at least need() bytes)."""
+    if getattr(_TRUST, "on", False):
+        return ws.numel()
     torch = _torch()
     if not isinstance(ws, torch.Tensor) or ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous():
         raise ValueError("workspace must be a contiguous 1-D uint8 tensor")
     if ws.device.type != "cuda" or ws.device != device:
         raise ValueError(f"workspace must be on {device}, not {ws.device}")
+    need = need()
     if ws.numel() < need:
         raise ValueError(f"workspace holds {ws.numel()} bytes, the call needs {need}")
     return ws.numel()
@@ -289,7 +332,7 @@ def quantize(w, out: NF4Weight = None, workspace=None, stream=None, double_quant
         raise ValueError("out must be a packed weight of w's shape on w's device")
     wsb = quantize_workspace_bytes(n_out, n_in)
     ws = workspace if workspace is not None else torch.empty(wsb, dtype=torch.uint8, device=w.device)
-    wsn = _workspace(ws, w.device, wsb)
+    wsn = _workspace(ws, w.device, lambda: wsb)
     st = q.struct()
     _check(lib().qlora_quantize(_ptr(w), dtype, ctypes.byref(st), _ptr(ws), wsn, _stream(stream)), "qlora_quantize")
     q.last_workspace = ws
@@ -353,7 +396,7 @@ def linear_fwd(x, q: NF4Weight, A, B, scale: float, y=None, u_out=None, save_u=T
         chk.bf16(u_out, "u_out", (T, r))
     chk.done()
     ws = workspace if workspace is not None else linear_workspace(T, q.n_out, q.n_in, r, dev)
-    wsb = _workspace(ws, dev, linear_workspace_bytes(T, q.n_out, q.n_in, r))
+    wsb = _workspace(ws, dev, lambda: linear_workspace_bytes(T, q.n_out, q.n_in, r))
     st = q.struct()
     _check(lib().qlora_linear_fwd(_ptr(x), T, ctypes.byref(st), _ptr(A), _ptr(B), r, float(scale), _ptr(y),
                                   _ptr(u_out), _ptr(ws), wsb, _stream(stream)), "qlora_linear_fwd")
@@ -425,7 +468,7 @@ def linear_bwd(dy, x, q: NF4Weight, A, B, scale: float, u=None, need_grad_x=True
     grad_B = grad_B if grad_B is not None else torch.empty((q.n_out, r), dtype=torch.float32, device=dev)
     _check_grads(grad_x, grad_A, grad_B, T, r, q, chk)
     ws = workspace if workspace is not None else linear_workspace(T, q.n_out, q.n_in, r, dev)
-    wsb = _workspace(ws, dev, linear_workspace_bytes(T, q.n_out, q.n_in, r))
+    wsb = _workspace(ws, dev, lambda: linear_workspace_bytes(T, q.n_out, q.n_in, r))
     st = q.struct()
     _check(lib().qlora_linear_bwd(_ptr(dy), _ptr(x), T, ctypes.byref(st), _ptr(A), _ptr(B), r, float(scale),
                                   _ptr(u), _ptr(grad_x), _ptr(grad_A), _ptr(grad_B), _ptr(ws), wsb,
@@ -484,7 +527,7 @@ def linear_fwd_dropout(x, q: NF4Weight, A, B, scale: float, p: float, seed: int,
         chk.bf16(u_out, "u_out", (T, r))
     chk.done()
     ws = workspace if workspace is not None else linear_dropout_workspace(T, q.n_out, q.n_in, r, dev)
-    wsb = _workspace(ws, dev, linear_dropout_workspace_bytes(T, q.n_out, q.n_in, r))
+    wsb = _workspace(ws, dev, lambda: linear_dropout_workspace_bytes(T, q.n_out, q.n_in, r))
     st = q.struct()
     _check(lib().qlora_linear_fwd_dropout(_ptr(x), T, ctypes.byref(st), _ptr(A), _ptr(B), r, float(scale), float(p),
                                           int(seed), _ptr(y), _ptr(u_out), _ptr(ws), wsb, _stream(stream)),
@@ -507,7 +550,7 @@ def linear_bwd_dropout(dy, x, q: NF4Weight, A, B, scale: float, p: float, seed: 
     grad_B = grad_B if grad_B is not None else torch.empty((q.n_out, r), dtype=torch.float32, device=dev)
     _check_grads(grad_x, grad_A, grad_B, T, r, q, chk)
     ws = workspace if workspace is not None else linear_dropout_workspace(T, q.n_out, q.n_in, r, dev)
-    wsb = _workspace(ws, dev, linear_dropout_workspace_bytes(T, q.n_out, q.n_in, r))
+    wsb = _workspace(ws, dev, lambda: linear_dropout_workspace_bytes(T, q.n_out, q.n_in, r))
     st = q.struct()
     _check(lib().qlora_linear_bwd_dropout(_ptr(dy), _ptr(x), T, ctypes.byref(st), _ptr(A), _ptr(B), r, float(scale),
                                           float(p), int(seed), _ptr(u), _ptr(grad_x), _ptr(grad_A), _ptr(grad_B),
@@ -565,7 +608,7 @@ def linear_set_fwd(x, qs, A_set, Bs, scale: float, ys=None, u_out=None, save_u=T
     chk.done()
     n_outs = [q.n_out for q in qs]
     ws = workspace if workspace is not None else linear_set_workspace(T, n_outs, qs[0].n_in, r, dev)
-    wsb = _workspace(ws, dev, linear_set_workspace_bytes(T, n_outs, qs[0].n_in, r))
+    wsb = _workspace(ws, dev, lambda: linear_set_workspace_bytes(T, n_outs, qs[0].n_in, r))
     st = (NF4WeightStruct * count)(*[q.struct() for q in qs])
     _check(lib().qlora_linear_set_fwd(_ptr(x), T, count, st, _ptr(A_set), _ptrs(Bs), r, float(scale), _ptrs(ys),
                                       _ptr(u_out), _ptr(ws), wsb, _stream(stream)), "qlora_linear_set_fwd")
@@ -628,7 +671,7 @@ def linear_set_bwd(dys, x, qs, A_set, Bs, scale: float, u=None, need_grad_x=True
     chk.done()
     n_outs = [q.n_out for q in qs]
     ws = workspace if workspace is not None else linear_set_workspace(T, n_outs, qs[0].n_in, r, dev)
-    wsb = _workspace(ws, dev, linear_set_workspace_bytes(T, n_outs, qs[0].n_in, r))
+    wsb = _workspace(ws, dev, lambda: linear_set_workspace_bytes(T, n_outs, qs[0].n_in, r))
     st = (NF4WeightStruct * count)(*[q.struct() for q in qs])
     _check(lib().qlora_linear_set_bwd(_ptrs(dys), _ptr(x), T, count, st, _ptr(A_set), _ptrs(Bs), r, float(scale),
                                       _ptr(u), _ptr(grad_x), _ptr(grad_A_set), _ptrs(grad_Bs), _ptr(ws), wsb,

@@ -286,9 +286,9 @@ def test_binding_checks_every_tensor_before_a_call():
     refuses(lambda: qlora.linear_set_bwd([dy], x, qs, bf(2 * r, n_in), [b, b], 0.5), "dys must hold 2")
     # a workspace must be a uint8 CUDA tensor: its byte count is what the ABI is told
     with pytest.raises(ValueError, match="workspace must be a contiguous 1-D uint8"):
-        qlora._workspace(torch.zeros(16, dtype=torch.float32), torch.device("cpu"), 8)
+        qlora._workspace(torch.zeros(16, dtype=torch.float32), torch.device("cpu"), lambda: 8)
     with pytest.raises(ValueError, match="workspace must be on"):
-        qlora._workspace(torch.zeros(16, dtype=torch.uint8), torch.device("cuda:0"), 8)
+        qlora._workspace(torch.zeros(16, dtype=torch.uint8), torch.device("cuda:0"), lambda: 8)
     # quantize: the source must be on a CUDA device
     refuses(lambda: qlora.quantize(f32(n_out, n_in)), "w must be on a CUDA device")
 
@@ -310,3 +310,22 @@ def test_noalloc_forward_refuses_what_its_scratch_cannot_hold():
     assert lib.qlora_linear_fwd_noalloc(0, 16, ctypes.byref(st), fake, fake, 8, 1.0, fake, 0, None) == 1
     assert lib.qlora_linear_fwd_noalloc(fake, 16, ctypes.byref(st), fake, fake, 0, 1.0, fake, 0, None) == 2
     assert lib.qlora_linear_fwd_noalloc(fake + 2, 16, ctypes.byref(st), fake, fake, 8, 1.0, fake, 0, None) == 3
+
+
+def test_trusted_calls_skip_the_checks_only_inside_the_block():
+    """trusted_calls() turns the per-tensor checks off for the current thread inside the block only."""
+    torch = pytest.importorskip("torch")
+    from bit_quantized_finetuning_quant_amd import qlora
+
+    dev = torch.device("cpu")
+    assert isinstance(qlora._Args(dev), qlora._Args)
+    with qlora.trusted_calls():
+        assert qlora._Args(dev) is qlora._NO_CHECKS
+        with qlora.trusted_calls():
+            pass
+        assert qlora._Args(dev) is qlora._NO_CHECKS
+    assert isinstance(qlora._Args(dev), qlora._Args)
+    q = qlora.NF4Weight.empty(128, 64, device="cpu")
+    with pytest.raises(ValueError):
+        qlora.linear_fwd(torch.zeros((5, 64), dtype=torch.bfloat16), q, torch.zeros((8, 64), dtype=torch.bfloat16),
+                         torch.zeros((128, 8), dtype=torch.bfloat16), 0.5)
