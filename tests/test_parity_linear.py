@@ -24,11 +24,24 @@ def _run(case, scale=None, need_u=True):
     return q, y, u, gx, ga, gb
 
 
-def _check_case(case, scale=None, need_u=True):
+_DECODED = {}
+
+
+def _oracle_decode(w, key=None):
+    """The oracle's dequantized weight (cached by `key` for cases that share one weight)."""
+    if key is not None and key in _DECODED:
+        return _DECODED[key]
+    wh = oracle.dequantize(oracle.quantize(w, w.shape[0], w.shape[1]))
+    if key is not None:
+        _DECODED.clear()
+        _DECODED[key] = wh
+    return wh
+
+
+def _check_case(case, scale=None, need_u=True, weight_key=None):
     s = case.scale if scale is None else scale
     q, y, u, gx, ga, gb = _run(case, s, need_u)
-    ref = oracle.quantize(case.w, case.n_out, case.n_in)
-    wh = oracle.dequantize(ref)
+    wh = _oracle_decode(case.w, weight_key)
     assert np.array_equal(host_bits(qlora.dequantize(q)), wh)
     y_ref, u_ref = oracle.forward(case.x, wh, case.a, case.b, s)
     gx_ref, ga_ref, gb_ref = oracle.backward(case.dy, case.x, wh, case.a, case.b, s)
@@ -77,6 +90,16 @@ def test_split_contraction_and_clamped_rows(shape):
     case = workloads.custom_case(n_out, n_in, T, r, 16.0, seed=n_out + 7 * T)
     _check_case(case)
     _check_case(case, scale=1.5, need_u=False)
+
+
+@pytest.mark.parametrize("T", [1, 2, 4, 8, 16, 32, 64, 128, 256])
+def test_7b_projection_every_token_count_of_the_sweep(T):
+    """The 7B projection (4096 x 4096, r = 64) at every token count the benchmark sweeps: the
+    few-token kernels up to 4 tokens, then the fused GEMM with clamped rows and split
+    contractions."""
+    announce(f"linear 7b_attn T={T} (sweep)")
+    case = workloads.custom_case(4096, 4096, T, 64, 16.0, seed=900)  # one weight; x, dy drawn per T
+    _check_case(case, weight_key=("sweep", 900))
 
 
 @pytest.mark.parametrize("shape", [(300, 320, 1, 24), (77, 192, 2, 5), (64, 64, 2, 256), (1000, 11008, 1, 64),
