@@ -138,12 +138,16 @@ struct ActDma {
   uint32_t off[2];    // !kClamp: lane offsets by the parity of j
   int lane_row, pos, last_row;  // kClamp: tile row of the lane at j = 0, its chunk slot, last valid row
 
+  // Every input but the lane is wave-uniform.  The base goes through readfirstlane once here, so it
+  // stays in scalar registers also where the object is set up under a branch on the wave index
+  // (each half through uint32_t: readfirstlane returns a signed int, which must not be
+  // sign-extended into the other half).
   __device__ __forceinline__ void init(const uint16_t *act, int64_t Kc, int64_t M, int64_t m0, int64_t kstep0,
                                        int cw, int lane) {
     row_bytes = 2 * Kc;
-    base = (const char *)(act + m0 * Kc + kstep0 * QBK);
+    const char *b = (const char *)(act + m0 * Kc + kstep0 * QBK);
     if (!kClamp) {
-      base += 64 * cw * row_bytes;
+      b += 64 * cw * row_bytes;
       off[0] = dma_lane_offset(lane, Kc, 0);
       off[1] = dma_lane_offset(lane, Kc, 1);
     } else {
@@ -151,21 +155,16 @@ struct ActDma {
       pos = lane & 7;
       last_row = (int)min((int64_t)QBM, M - m0) - 1;
     }
+    const uint64_t u = (uint64_t)(uintptr_t)b;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(u >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)u);
+    base = (const char *)(uintptr_t)(((uint64_t)hi << 32) | (uint64_t)lo);
   }
 
-  // DMAs j0 .. j0 + nj - 1 of stage kt into dst (this wave's 64 rows of an LDS stage).  The base
-  // and the row length are wave-uniform; readfirstlane keeps them in scalar registers where the
-  // compiler cannot see that (an object set up under a branch on the wave index).
+  // DMAs j0 .. j0 + nj - 1 of stage kt into dst (this wave's 64 rows of an LDS stage)
   __device__ __forceinline__ void issue(int64_t kt, uint16_t *dst, int j0 = 0, int nj = 8) const {
     const uint32_t l0 = lds_addr(dst);
-    // (readfirstlane returns a signed int: each half goes through uint32_t, so the low word is not
-    // sign-extended into the high one)
-    const uint64_t b = (uint64_t)(uintptr_t)base;
-    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
-    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
-    const uint64_t bu = ((uint64_t)hi << 32) | (uint64_t)lo;
-    const int64_t row_bytes = (int64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)this->row_bytes);
-    const char *sb = (const char *)(uintptr_t)bu + kt * (QBK * 2);
+    const char *sb = base + kt * (QBK * 2);
 #pragma unroll
     for (int j = j0; j < j0 + nj; ++j) {
       if (!kClamp) {
