@@ -29,19 +29,11 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-// e4m3 ("fn") byte -> its exact value: bias 7, 3 mantissa bits, exponent
-// field 0 = subnormal m * 2^-9.  NaN patterns never occur in stored data.
-__device__ __forceinline__ float e4m3_to_f32(uint32_t b) {
-  // Branch-free: both the normal and the subnormal encodings are formed and
-  // one is selected, and the sign is OR-ed in (a divergent branch here would
-  // make the compiler drain outstanding loads at the join).
-  const uint32_t e = (b >> 3) & 0xFu;
-  const uint32_t m = b & 7u;
-  const uint32_t normal = ((e + 120u) << 23) | (m << 20);
-  const uint32_t subnormal = __float_as_uint((float)m * 0x1p-9f);  // exact
-  const uint32_t mag = e ? normal : subnormal;
-  return __uint_as_float(mag | ((b & 0x80u) << 24));
-}
+// e4m3 ("fn") byte -> its exact value (bias 7, 3 mantissa bits, exponent
+// field 0 = subnormal m * 2^-9; 0x7F and 0xFF are NaN, which stored data
+// never holds).  gfx950's v_cvt_f32_fp8 reads the OCP e4m3 format; every
+// e4m3 value is an fp32 value, so the conversion is exact.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t b) { return __builtin_amdgcn_cvt_f32_fp8((int)b, 0); }
 
 // Block constant decode: fl32(fl32(e4m3(q) * s2) + mu), two roundings.  The
 // multiply and the add must not be contracted into one fused multiply-add
@@ -66,29 +58,24 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 }
 
 // Decode without a memory lookup.  The 16 decoded values of one block,
-// t[k] = bf16_rne(fl32(CB[k] * c1hat)), are built once per block in registers
-// as byte tables: lo[j] holds the low bytes of t[4j .. 4j+3], hi[j] the high
-// bytes.  A code then selects its two bytes with v_perm_b32 (which picks
-// bytes 0..7 of the 64-bit pair {S0, S1}, S1 the low word): one permute
-// over each half of a table and a per-byte select on the code's bit 3.
-// Every decoded value is computed exactly as in the lookup form, so the two
-// are bit-identical.
+// t[k] = bf16_rne(fl32(CB[k] * c1hat)), are held in registers as byte
+// tables: lo[j] holds the low bytes of t[4j .. 4j+3], hi[j] the high bytes.
+// A code then selects its two bytes with v_perm_b32 (which picks bytes 0..7
+// of the 64-bit pair {S0, S1}, S1 the low word): one permute over each half
+// of a table and a per-byte select on the code's bit 3.  Every decoded value
+// is computed exactly as in the lookup form, so the two are bit-identical.
 struct DecodeTable {
   uint32_t lo[4], hi[4];
 };
 
-__device__ __forceinline__ DecodeTable decode_table(const Codebook &cb, float c1hat) {
-  uint32_t p[8];  // p[m] = t[2m] | t[2m+1] << 16
+// lo[j] and hi[j] of 8 consecutive levels from their 4 packed bf16 pairs
+// p[m] = t[2m] | t[2m+1] << 16.
+__device__ __forceinline__ void table_half(const uint32_t (&p)[4], uint32_t (&lo)[2], uint32_t (&hi)[2]) {
 #pragma unroll
-  for (int m = 0; m < 8; ++m)
-    p[m] = pack_bf16x2(decode_product(cb.v[2 * m], c1hat), decode_product(cb.v[2 * m + 1], c1hat));
-  DecodeTable t;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    t.lo[j] = __builtin_amdgcn_perm(p[2 * j + 1], p[2 * j], 0x06040200u);
-    t.hi[j] = __builtin_amdgcn_perm(p[2 * j + 1], p[2 * j], 0x07050301u);
+  for (int j = 0; j < 2; ++j) {
+    lo[j] = __builtin_amdgcn_perm(p[2 * j + 1], p[2 * j], 0x06040200u);
+    hi[j] = __builtin_amdgcn_perm(p[2 * j + 1], p[2 * j], 0x07050301u);
   }
-  return t;
 }
 
 // Byte b of the result is byte (code_b) of a 16-byte table, for four codes

@@ -109,6 +109,11 @@ __device__ __forceinline__ void dma16(const char *sbase, uint32_t voff, uint32_t
 }
 #pragma clang diagnostic pop
 
+// The value held by the other lane of an adjacent pair (DPP quad_perm [1, 0, 3, 2]).
+__device__ __forceinline__ uint32_t pair_swap(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, true);
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void *p) { return (uint32_t)(uintptr_t)(lptr_t *)p; }
 
 // Full tiles: consumer wave cw (0..3) moves rows [64 cw, 64 cw + 64) of the
@@ -305,18 +310,39 @@ struct Producer {
   }
 
   // Full tiles: the decoded stage straight from its codes into LDS, with no
-  // table in memory: the block's 16 decoded values are built in registers as
+  // table in memory: the block's 16 decoded values are held in registers as
   // byte tables and each code selects its bf16 value with v_perm_b32
-  // (decode_table / decode_word; bit-identical to the product form).  Four
-  // 16-byte stores.
+  // (decode_word; bit-identical to the product form).  The two lanes of an
+  // adjacent pair decode the two halves of one block, so they share its
+  // tables: each builds those of 8 levels (the odd lane levels 8..15) and
+  // takes the other 8 from its partner with a DPP swap.  A lane's tables
+  // thus list its own levels first, and the odd lane's codes select with
+  // bit 3 flipped.  Four 16-byte stores.
   __device__ __forceinline__ void write_rt(const Stage &s, const Codebook &cb, uint16_t *sb) const {
     const float ch = kDQ ? decode_constant(s.q, s.s2, mu) : s.s2;
-    const DecodeTable t = decode_table(cb, ch);
+    const bool odd = ptid & 1;
+    uint32_t p[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const float l0 = odd ? cb.v[8 + 2 * m] : cb.v[2 * m], l1 = odd ? cb.v[9 + 2 * m] : cb.v[2 * m + 1];
+      p[m] = pack_bf16x2(decode_product(l0, ch), decode_product(l1, ch));
+    }
+    DecodeTable t;
+    uint32_t lo[2], hi[2];
+    table_half(p, lo, hi);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      t.lo[j] = lo[j];
+      t.hi[j] = hi[j];
+      t.lo[2 + j] = pair_swap(lo[j]);
+      t.hi[2 + j] = pair_swap(hi[j]);
+    }
+    const uint32_t flip = odd ? 0x88888888u : 0u;
     uint16_t *dst = kTransW ? &sb[(ptid >> 2) * TLD + 32 * (ptid & 3)] : &sb[(ptid >> 1) * QLD + 32 * (ptid & 1)];
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       uint32_t o[4];
-      decode_word(s.code[v], t, o);
+      decode_word(s.code[v] ^ flip, t, o);
       *(u32x4 *)&dst[8 * v] = u32x4{o[0], o[1], o[2], o[3]};
     }
   }
@@ -604,18 +630,22 @@ __device__ __forceinline__ QgemmMember set_member(const QgemmSet &s, int i) {
 //     the adapter term uses la = v_set, lb = A_set and r = the set's total
 //     rank; out = grad_x.
 // kDrop (grad_x only): the adapter term is masked by the LoRA dropout words.
-// kClamp: M is not a multiple of QBM; the last row tile's missing rows read a
-// valid row (ActDma) and are never stored, so it runs the full-tile pipeline.
+// kFull: every tile of the grid is full in columns and contraction steps, and
+// in rows unless kClamp; the partial-tile path is not compiled in.
+// kClamp (with kFull only): M is not a multiple of QBM; the last row tile's
+// missing rows read a valid row (ActDma) and are never stored, so it runs the
+// full-tile pipeline.
 // Split contraction (single linear only; part != nullptr): workgroup z of the
 // grid's third dimension contracts steps [z split_steps, (z + 1) split_steps)
 // and writes its fp32 tile to part[z][M][Ncols]; split 0 also carries the
 // adapter term; qgemm_split_reduce adds the splits in order.
-template <bool kTransW, bool kDQ, bool kDrop, bool kClamp>
+template <bool kTransW, bool kDQ, bool kDrop, bool kClamp, bool kFull>
 __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const uint16_t *__restrict__ x,
                                                 const uint16_t *__restrict__ la, const uint16_t *__restrict__ lb,
                                                 int r, float scale, uint16_t *__restrict__ gx, Codebook cb,
                                                 const uint32_t *__restrict__ keep, float *__restrict__ part,
                                                 int64_t split_steps) {
+  static_assert(kFull || !kClamp, "clamped rows only on grids of full tiles");
   __shared__ __attribute__((aligned(16))) uint16_t sa[kActStages][QBM * 64];
   __shared__ __attribute__((aligned(16))) uint16_t sb[2][QBN * QLD];  // = 64 * TLD
   __shared__ float lut[16];
@@ -650,7 +680,7 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
   const int m_begin = kTransW ? 0 : mf, m_end = kTransW ? set.count : mf + 1;
   // full (per member): every column and contraction step of the tile is in
   // range (and, without kClamp, every row)
-  const bool rows_ok = kClamp || m0 + QBM <= M;
+  const bool rows_ok = kFull || m0 + QBM <= M;
   // this workgroup's contraction steps (a split, or all of them) and its rank
   // of the adapter term (only split 0 adds it)
   const int64_t kstep0 = part ? (int64_t)blockIdx.z * split_steps : 0;
@@ -661,8 +691,10 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
   };
 
   // Level table for the producers' decode of partial tiles.
-  if (tid < 16) lut[tid] = cb.v[tid];
-  __syncthreads();
+  if (!kFull) {
+    if (tid < 16) lut[tid] = cb.v[tid];
+    __syncthreads();
+  }
 
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -677,7 +709,7 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
   const QgemmMember m_first = set_member(set, m_begin);
   const int64_t Kc_first = kTransW ? m_first.w.n_out : m_first.w.n_in;
   const int64_t nk_first = member_steps(Kc_first);
-  const bool full_first = rows_ok && (c0 + QBN <= Ncols) && (Kc_first % QBK == 0);
+  const bool full_first = kFull || (rows_ok && (c0 + QBN <= Ncols) && (Kc_first % QBK == 0));
   Stage pre0, pre1, pre2;
   ActDma<kClamp> dma_first;
   // every member's tensor mean, fetched with the first codes
@@ -765,7 +797,7 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
       const QgemmMember mm = set_member(set, mi);
       const int64_t Kc = kTransW ? mm.w.n_out : mm.w.n_in;
       const int64_t nk = member_steps(Kc);
-      const bool full = rows_ok && (c0 + QBN <= Ncols) && (Kc % QBK == 0);
+      const bool full = kFull || (rows_ok && (c0 + QBN <= Ncols) && (Kc % QBK == 0));
       if (mi > m_begin) wg_barrier();  // the previous member's pipeline has drained
       const int mo = mi - m_begin;
       const float mu = mo == 0 ? mu0 : mo == 1 ? mu1 : mo == 2 ? mu2 : mu3;
@@ -773,7 +805,7 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
       if (full) {
         if (mi > m_begin) fetch_first_codes(p, nk, pre0, pre1, pre2);  // the first member's went out early
         producer_loop_full(p, nk, sb, pre0, pre1, pre2, cb);
-      } else {
+      } else if (!kFull) {
         producer_loop_partial(p, nk, sa, sb, lut);
       }
     }
@@ -788,7 +820,7 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
   const uint16_t *act = kTransW ? mm.act : x;
   const int64_t Kc = kTransW ? mm.w.n_out : mm.w.n_in;
   const int64_t nk = member_steps(Kc);
-  const bool full = rows_ok && (c0 + QBN <= Ncols) && (Kc % QBK == 0);
+  const bool full = kFull || (rows_ok && (c0 + QBN <= Ncols) && (Kc % QBK == 0));
   if (mi > m_begin) wg_barrier();  // every wave is done with the previous member's LDS stages
   ActDma<kClamp> dma;
   dma.init(act, Kc, M, m0, kstep0, cw, lane);
@@ -944,16 +976,23 @@ __global__ __launch_bounds__(256) void qgemm_split_reduce(const float *__restric
   }
 }
 
+// Tiles of a grid: any (some may be partial), all full, or all full with the
+// last row tile's missing rows clamped.
+enum class Tiles { kAny, kFull, kFullClamped };
+
 template <bool kTransW, bool kDQ, bool kDrop>
-void launch_ws(bool clamp, dim3 g, hipStream_t st, const QgemmSet &s, int64_t M, const uint16_t *x,
+void launch_ws(Tiles tiles, dim3 g, hipStream_t st, const QgemmSet &s, int64_t M, const uint16_t *x,
                const uint16_t *la, const uint16_t *lb, int r, float scale, uint16_t *gx, const Codebook &cb,
                const uint32_t *keep, float *part, int64_t split_steps) {
-  if (clamp)
-    qgemm_ws<kTransW, kDQ, kDrop, true><<<g, 512, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, keep, part,
-                                                            split_steps);
+  if (tiles == Tiles::kFullClamped)
+    qgemm_ws<kTransW, kDQ, kDrop, true, true><<<g, 512, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, keep, part,
+                                                                  split_steps);
+  else if (tiles == Tiles::kFull)
+    qgemm_ws<kTransW, kDQ, kDrop, false, true><<<g, 512, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, keep, part,
+                                                                   split_steps);
   else
-    qgemm_ws<kTransW, kDQ, kDrop, false><<<g, 512, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, keep, part,
-                                                             split_steps);
+    qgemm_ws<kTransW, kDQ, kDrop, false, false><<<g, 512, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, keep,
+                                                                    part, split_steps);
 }
 
 }  // namespace
@@ -1008,10 +1047,21 @@ hipError_t launch_qgemm_set(bool trans_w, const QgemmSet &set, int64_t M, const 
     for (int i = 0; i < s.count; ++i) kc_max = std::max(kc_max, s.m[i].w.n_out);
   }
   for (int i = s.count; i < kMaxSetMembers; ++i) s.m[i] = s.m[0];
-  // the last row tile's missing rows read a valid row (byte offsets within a
-  // tile stay below 2^32)
-  const bool clamp = (M % QBM) != 0 && kc_max < ((int64_t)1 << 22);
   const int64_t Ncols = trans_w ? s.m[0].w.n_in : s.m[0].w.n_out;
+  // Every tile full in columns and contraction steps: the grid runs the
+  // full-tile pipeline only, with the last row tile's missing rows reading a
+  // valid row when M is not a multiple of QBM (byte offsets within a tile
+  // stay below 2^32).
+  bool cols_k_full = true;
+  for (int i = 0; i < s.count; ++i) {
+    const int64_t nc = trans_w ? s.m[0].w.n_in : s.m[i].w.n_out, kc = trans_w ? s.m[i].w.n_out : s.m[i].w.n_in;
+    cols_k_full = cols_k_full && nc % QBN == 0 && kc % QBK == 0;
+  }
+  Tiles tiles = Tiles::kAny;
+  if (cols_k_full && M % QBM == 0)
+    tiles = Tiles::kFull;
+  else if (cols_k_full && kc_max < ((int64_t)1 << 22))
+    tiles = Tiles::kFullClamped;
   QgemmSplit sp{1, 0};
   if (part && s.count == 1) sp = qgemm_split(M, Ncols, kc_max);
   float *pz = sp.splits > 1 ? part : nullptr;
@@ -1019,19 +1069,19 @@ hipError_t launch_qgemm_set(bool trans_w, const QgemmSet &set, int64_t M, const 
   const bool dq = s.m[0].w.dq;
   if (!trans_w) {  // the forward never takes a dropout mask
     if (dq)
-      launch_ws<false, true, false>(clamp, g, st, s, M, x, la, lb, r, scale, gx, cb, nullptr, pz, sp.steps);
+      launch_ws<false, true, false>(tiles, g, st, s, M, x, la, lb, r, scale, gx, cb, nullptr, pz, sp.steps);
     else
-      launch_ws<false, false, false>(clamp, g, st, s, M, x, la, lb, r, scale, gx, cb, nullptr, pz, sp.steps);
+      launch_ws<false, false, false>(tiles, g, st, s, M, x, la, lb, r, scale, gx, cb, nullptr, pz, sp.steps);
   } else if (keep) {
     if (dq)
-      launch_ws<true, true, true>(clamp, g, st, s, M, x, la, lb, r, scale, gx, cb, keep, pz, sp.steps);
+      launch_ws<true, true, true>(tiles, g, st, s, M, x, la, lb, r, scale, gx, cb, keep, pz, sp.steps);
     else
-      launch_ws<true, false, true>(clamp, g, st, s, M, x, la, lb, r, scale, gx, cb, keep, pz, sp.steps);
+      launch_ws<true, false, true>(tiles, g, st, s, M, x, la, lb, r, scale, gx, cb, keep, pz, sp.steps);
   } else {
     if (dq)
-      launch_ws<true, true, false>(clamp, g, st, s, M, x, la, lb, r, scale, gx, cb, nullptr, pz, sp.steps);
+      launch_ws<true, true, false>(tiles, g, st, s, M, x, la, lb, r, scale, gx, cb, nullptr, pz, sp.steps);
     else
-      launch_ws<true, false, false>(clamp, g, st, s, M, x, la, lb, r, scale, gx, cb, nullptr, pz, sp.steps);
+      launch_ws<true, false, false>(tiles, g, st, s, M, x, la, lb, r, scale, gx, cb, nullptr, pz, sp.steps);
   }
   if (pz) {
     uint16_t *out = trans_w ? gx : s.m[0].out;
