@@ -49,6 +49,7 @@ constexpr int QBM = 256, QBN = 128, QBK = 64;
 constexpr int QLD = 72, TLD = 144;
 static_assert(128 * QLD == 64 * TLD, "both weight-tile layouts fill the same LDS stage");
 constexpr int kActStages = 3;                            // activation tile LDS ring
+constexpr int kWStages = 3;                              // weight tile LDS ring
 
 typedef __attribute__((address_space(1))) const void gptr_t;
 typedef __attribute__((address_space(3))) void lptr_t;
@@ -397,9 +398,9 @@ __device__ __forceinline__ void producer_loop_full(const Producer<kTransW, kDQ> 
   p.template load_w<true>(st(4), c1);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
   wg_barrier();  // stage 1 ready
-#define QGEMM_PRODUCER_STEP(K_, CUR)                                                   \
+#define QGEMM_PRODUCER_STEP(K_, CUR, BUF)                                              \
   if ((K_) < nk) {                                                                    \
-    p.write_rt(CUR, cb, sb[(K_) & 1]);                                                \
+    p.write_rt(CUR, cb, sb[BUF]);                                                     \
     __builtin_amdgcn_sched_barrier(0);                                                \
     p.template load_w<true>(st((K_) + 5), CUR);                                       \
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));                                   \
@@ -407,12 +408,12 @@ __device__ __forceinline__ void producer_loop_full(const Producer<kTransW, kDQ> 
   }
   int64_t kt = 0;
   for (; kt + 3 <= nk; kt += 3) {
-    QGEMM_PRODUCER_STEP(kt, c2)
-    QGEMM_PRODUCER_STEP(kt + 1, c0)
-    QGEMM_PRODUCER_STEP(kt + 2, c1)
+    QGEMM_PRODUCER_STEP(kt, c2, 2)
+    QGEMM_PRODUCER_STEP(kt + 1, c0, 0)
+    QGEMM_PRODUCER_STEP(kt + 2, c1, 1)
   }
-  QGEMM_PRODUCER_STEP(kt, c2)
-  QGEMM_PRODUCER_STEP(kt + 1, c0)
+  QGEMM_PRODUCER_STEP(kt, c2, 2)
+  QGEMM_PRODUCER_STEP(kt + 1, c0, 0)
 #undef QGEMM_PRODUCER_STEP
 }
 
@@ -434,7 +435,7 @@ __device__ __forceinline__ void producer_loop_partial(const Producer<kTransW, kD
   auto store = [&](const Stage &c, int64_t k) {
     p.read_levels(c, lut, l);
     p.store_act(c, sa[k % kActStages]);
-    p.store_w(l, sb[k & 1]);
+    p.store_w(l, sb[k % kWStages]);
   };
   load(0, c0);
   load(st(1), c1);
@@ -647,7 +648,7 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
                                                 int64_t split_steps) {
   static_assert(kFull || !kClamp, "clamped rows only on grids of full tiles");
   __shared__ __attribute__((aligned(16))) uint16_t sa[kActStages][QBM * 64];
-  __shared__ __attribute__((aligned(16))) uint16_t sb[2][QBN * QLD];  // = 64 * TLD
+  __shared__ __attribute__((aligned(16))) uint16_t sb[kWStages][QBN * QLD];  // = 64 * TLD
   __shared__ float lut[16];
 
   const int tid = threadIdx.x;
@@ -861,13 +862,19 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
   // ring goes by DMA into the buffer of stage k (read during step k-1).  At the
   // last step the loads read a stage nobody uses.  Exactly 8 DMAs per step, so
   // waiting for at most 8 outstanding before the barrier means stage k+2 has
-  // landed; every read of stage k+1 has returned by then too.
+  // landed; every read of stage k+1 has returned by then too, except the last
+  // B fragments: the weight ring is three stages deep, so the producers
+  // overwrite their stage only at step k+2.
+  static_assert(kWStages == kActStages, "one ring index serves both rings");
+  // LDS instructions of the B fragments read after the last MFMA: one 16-byte
+  // read per fragment, or two 8-byte transpose reads
+  constexpr int kBReadOps = kTransW ? 4 : 2;
   int ring = 0;  // kt % kActStages, kept by rotation (a 64-bit remainder costs the scalar unit dozens of instructions)
   for (int64_t kt = 0; kt < nk; ++kt) {
     const int ring1 = ring + 1 == kActStages ? 0 : ring + 1;
     uint16_t *dma_dst = sa[ring] + 64 * cw * 64;
     const int64_t dma_kt = min(kt + 3, nk - 1);
-    const uint16_t *na = sa[ring1], *nb = sb[(kt + 1) & 1];
+    const uint16_t *na = sa[ring1], *nb = sb[ring1];
     ring = ring1;
 #pragma unroll
     for (int kk = 0; kk < QBK / 16; ++kk) {
@@ -886,10 +893,12 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) f.b[QBK / 16 - 1][j] = load_b_frag<kTransW>(nb, wn, lane, QBK / 16 - 1, j);
+    // These last B reads (kBReadOps LDS instructions) may still be in flight
+    // at the barrier: their weight stage is overwritten only at step k+2.
     if (full)
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm(8, 0));
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(8, kBReadOps));
     else
-      __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+      __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, kBReadOps));
     wg_barrier();
   }
   // No LDS-DMA may still be writing when the next member's stages start or the
