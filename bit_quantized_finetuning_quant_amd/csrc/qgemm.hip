@@ -592,10 +592,10 @@ __device__ __forceinline__ void stage_lora(const uint16_t *la, int64_t ld_la, co
 }
 
 // The producer state of member mi of a set (mu: the member's tensor mean,
-// loaded by the caller).
+// loaded by the caller; ptid: the lane's index among the 256 decoding lanes).
 template <bool kTransW, bool kDQ>
 __device__ __forceinline__ Producer<kTransW, kDQ> member_producer(const QgemmMember &mm, const uint16_t *x, int64_t M,
-                                                                  int64_t m0, int64_t c0, int tid, float mu,
+                                                                  int64_t m0, int64_t c0, int ptid, float mu,
                                                                   int64_t kstep0) {
   Producer<kTransW, kDQ> p;
   const int64_t Kc = kTransW ? mm.w.n_out : mm.w.n_in;
@@ -609,7 +609,7 @@ __device__ __forceinline__ Producer<kTransW, kDQ> member_producer(const QgemmMem
   p.kblk_row = mm.w.n_in / kBlock;
   p.w = mm.w;
   p.mu = mu;
-  p.ptid = tid - 256;
+  p.ptid = ptid;
   p.act_vec = (Kc % 8) == 0;
   p.kstep0 = kstep0;
   p.init_addressing();
@@ -723,7 +723,7 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
       if (m_begin + 3 < m_end) mu3 = *set_member(set, m_begin + 3).w.mu;
     }
     if (full_first)
-      fetch_first_codes(member_producer<kTransW, kDQ>(m_first, x, M, m0, c0, tid, 0.f, kstep0), nk_first, pre0, pre1,
+      fetch_first_codes(member_producer<kTransW, kDQ>(m_first, x, M, m0, c0, tid - 256, 0.f, kstep0), nk_first, pre0, pre1,
                         pre2);
   } else if (full_first) {
     const uint16_t *act = kTransW ? m_first.act : x;
@@ -802,7 +802,7 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
       if (mi > m_begin) wg_barrier();  // the previous member's pipeline has drained
       const int mo = mi - m_begin;
       const float mu = mo == 0 ? mu0 : mo == 1 ? mu1 : mo == 2 ? mu2 : mu3;
-      const Producer<kTransW, kDQ> p = member_producer<kTransW, kDQ>(mm, x, M, m0, c0, tid, mu, kstep0);
+      const Producer<kTransW, kDQ> p = member_producer<kTransW, kDQ>(mm, x, M, m0, c0, tid - 256, mu, kstep0);
       if (full) {
         if (mi > m_begin) fetch_first_codes(p, nk, pre0, pre1, pre2);  // the first member's went out early
         producer_loop_full(p, nk, sb, pre0, pre1, pre2, cb);
@@ -985,6 +985,192 @@ __global__ __launch_bounds__(256) void qgemm_split_reduce(const float *__restric
   }
 }
 
+// ---------------------------------------------------------------------------
+// Few-token tiles.  With a few dozen tokens a 256-row tile is mostly padding:
+// its matrix work is wasted and the step time is the decode, which only the
+// four producer waves of qgemm_ws do.  qgemm_sm takes 64 x 128 output tiles
+// in workgroups of four waves, two workgroups per CU, and every wave both
+// decodes (the producer lane mapping of qgemm_ws: one unit of 32 codes per
+// lane and step, the same register byte tables) and multiplies (tile rows
+// 0..63, columns 32 w .. 32 w + 31), so that two waves per SIMD issue decode
+// instructions.  The activation tile (64 x 64 per step) goes through
+// registers into LDS, rows at or past M reading row M - 1 (never stored).
+// Every load is an ordinary compiler-tracked load, so the waits the compiler
+// places are exact.  Pipeline over a three-stage LDS ring: at step k the
+// waves multiply stage k and write stage k+2 (codes and activation loaded
+// three steps earlier into one of three register sets, which then fetches
+// stage k+5).  Single linears whose tiles are full in columns and
+// contraction, without a dropout mask; a split contraction (blockIdx.z) as in
+// qgemm_ws.
+constexpr int SBM = 64;  // rows (tokens) of a few-token tile
+
+// Codes and activation of one stage for one lane: its unit of the weight tile
+// and two 16-byte chunks of the activation tile (row tid / 4, chunks
+// 2 (tid % 4) and 2 (tid % 4) + 1).
+struct SmStage {
+  Stage w;
+  u32x4 a0, a1;
+};
+
+// The 8 MFMAs of one stage for wave w: A fragments of rows 0..63 (two 32-row
+// halves), the B fragment of columns 32 w .. 32 w + 31.
+template <bool kTransW>
+__device__ __forceinline__ void sm_stage_mfma(const uint16_t *A, const uint16_t *B, int w, int lane,
+                                              f32x16 (&acc)[2]) {
+  u32x4 a[QBK / 16][2], b[QBK / 16];
+#pragma unroll
+  for (int kk = 0; kk < QBK / 16; ++kk) {
+    a[kk][0] = load_a_frag(A, 0, lane, kk, 0);
+    a[kk][1] = load_a_frag(A, 0, lane, kk, 1);
+    b[kk] = load_b_frag<kTransW>(B, w >> 1, lane, kk, w & 1);
+  }
+#pragma unroll
+  for (int kk = 0; kk < QBK / 16; ++kk) {
+    acc[0] = mfma(a[kk][0], b[kk], acc[0]);
+    acc[1] = mfma(a[kk][1], b[kk], acc[1]);
+  }
+}
+
+template <bool kTransW, bool kDQ>
+__global__ __launch_bounds__(256, 2) void qgemm_sm(QgemmSet set, int64_t M, const uint16_t *__restrict__ x,
+                                                   const uint16_t *__restrict__ la, const uint16_t *__restrict__ lb,
+                                                   int r, float scale, uint16_t *__restrict__ gx, Codebook cb,
+                                                   float *__restrict__ part, int64_t split_steps) {
+  __shared__ __attribute__((aligned(16))) uint16_t sa[3][SBM * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t sb[3][QBN * QLD];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, lhi = lane >> 5;
+  const QgemmMember mm = set.m[0];
+  const int64_t Ncols = kTransW ? mm.w.n_in : mm.w.n_out, Kc = kTransW ? mm.w.n_out : mm.w.n_in;
+  const int64_t m0 = (int64_t)blockIdx.x * SBM, c0 = (int64_t)blockIdx.y * QBN;
+  const uint16_t *act = kTransW ? mm.act : x;
+  const uint16_t *lb_t = kTransW ? lb : mm.lb;
+  uint16_t *out = kTransW ? gx : mm.out;
+  const int64_t kstep0 = part ? (int64_t)blockIdx.z * split_steps : 0;
+  const int64_t nk = part ? min(split_steps, Kc / QBK - kstep0) : Kc / QBK;
+  const int r_eff = blockIdx.z == 0 ? r : 0;
+  const float mu = kDQ ? *mm.w.mu : 0.f;
+  const Producer<kTransW, kDQ> p = member_producer<kTransW, kDQ>(mm, x, M, m0, c0, tid, mu, kstep0);
+
+  // this lane's activation row (clamped) and chunk pair
+  const int arow = tid >> 2, ach = 2 * (tid & 3);
+  const uint16_t *asrc = act + min(m0 + arow, M - 1) * Kc + kstep0 * QBK + 8 * ach;
+  auto st = [nk](int64_t k) { return min(k, nk - 1); };
+  auto load = [&](int64_t k, SmStage &c) {
+    p.template load_w<true>(k, c.w);
+    c.a0 = *(const u32x4 *)(asrc + k * QBK);
+    c.a1 = *(const u32x4 *)(asrc + k * QBK + 8);
+  };
+  auto store = [&](const SmStage &c, int buf) {
+    p.write_rt(c.w, cb, sb[buf]);
+    *(u32x4 *)&sa[buf][act_off(arow, ach)] = c.a0;
+    *(u32x4 *)&sa[buf][act_off(arow, ach + 1)] = c.a1;
+  };
+
+  SmStage s0, s1, s2;
+  load(0, s0);
+  load(st(1), s1);
+  load(st(2), s2);
+
+  f32x16 acc[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[i][q] = 0.f;
+  // LoRA term (first split only): scale * la lb^T, one 64-wide chunk of the
+  // rank at a time through stage 2 of both rings (zero past r and past M)
+  const bool lvec = (r % 8) == 0 && (set.ld_la % 8) == 0;
+  for (int j0 = 0; j0 < r_eff; j0 += QBK) {
+    u32x4 va[2], vb[4];
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {  // 64 rows x 8 chunks of the rank
+      const int idx = tid + 256 * it, row = idx >> 3, ch = idx & 7;
+      const int64_t grow = m0 + row;
+      va[it] = grow < M ? ld8(la + grow * set.ld_la, j0 + 8 * ch, r, lvec) : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int idx = tid + 256 * it;
+      if (!kTransW) {  // 128 output columns x 8 chunks of the rank
+        const int row = idx >> 3, ch = idx & 7;
+        vb[it] = ld8(lb_t + (c0 + row) * r, j0 + 8 * ch, r, lvec);
+      } else {  // 64 rank rows x 16 chunks of 8 columns
+        const int jr = idx >> 4, ch = idx & 15;
+        vb[it] = j0 + jr < r ? *(const u32x4 *)(lb_t + (int64_t)(j0 + jr) * Ncols + c0 + 8 * ch)
+                             : u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+#pragma unroll
+    for (int it = 0; it < 2; ++it) {
+      const int idx = tid + 256 * it;
+      *(u32x4 *)&sa[2][act_off(idx >> 3, idx & 7)] = va[it];
+    }
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const int idx = tid + 256 * it;
+      if (!kTransW)
+        *(u32x4 *)&sb[2][(idx >> 3) * QLD + 8 * (idx & 7)] = vb[it];
+      else
+        *(u32x4 *)&sb[2][(idx >> 4) * TLD + 8 * (idx & 15)] = vb[it];
+    }
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    wg_barrier();
+    sm_stage_mfma<kTransW>(sa[2], sb[2], w, lane, acc);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    wg_barrier();  // stage 2 of the rings is free again
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) acc[i][q] *= scale;
+
+  store(s0, 0);
+  load(st(3), s0);
+  store(s1, 1);
+  load(st(4), s1);
+  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+  wg_barrier();  // stages 0 and 1 ready
+#define QGEMM_SM_STEP(K_, CUR, BUF, NEXT)                                              \
+  if ((K_) < nk) {                                                                    \
+    sm_stage_mfma<kTransW>(sa[BUF], sb[BUF], w, lane, acc);                           \
+    store(CUR, NEXT);                                                                 \
+    load(st((K_) + 5), CUR);                                                          \
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));                                   \
+    wg_barrier();                                                                     \
+  }
+  int64_t kt = 0;
+  for (; kt + 3 <= nk; kt += 3) {
+    QGEMM_SM_STEP(kt, s2, 0, 2)
+    QGEMM_SM_STEP(kt + 1, s0, 1, 0)
+    QGEMM_SM_STEP(kt + 2, s1, 2, 1)
+  }
+  QGEMM_SM_STEP(kt, s2, 0, 2)
+  QGEMM_SM_STEP(kt + 1, s0, 1, 0)
+#undef QGEMM_SM_STEP
+
+  // element q of acc[i]: tile row 32 i + 8 (q / 4) + 4 (lane / 32) + q % 4, column 32 w + lane % 32
+  const int64_t col = c0 + 32 * w + l32;
+  if (part) {
+    float *pz = part + (int64_t)blockIdx.z * M * Ncols;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int64_t row = m0 + 32 * i + 8 * (q >> 2) + 4 * lhi + (q & 3);
+        if (row < M) pz[row * Ncols + col] = acc[i][q];
+      }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int64_t row = m0 + 32 * i + 8 * (q >> 2) + 4 * lhi + (q & 3);
+      __bf16 h = (__bf16)acc[i][q];
+      if (row < M) out[row * Ncols + col] = __builtin_bit_cast(uint16_t, h);
+    }
+}
+
 // Tiles of a grid: any (some may be partial), all full, or all full with the
 // last row tile's missing rows clamped.
 enum class Tiles { kAny, kFull, kFullClamped };
@@ -1034,9 +1220,39 @@ QgemmSplit qgemm_split(int64_t M, int64_t Ncols, int64_t Kc) {
   return sp;
 }
 
+// Few-token tiles (qgemm_sm) for launches of at most this many tokens.
+constexpr int64_t kSmMaxRows = 64;
+
+// The split of a few-token launch: the same estimate with two workgroups per
+// CU (512 at once), each step about 0.7 us with the other workgroup of its CU
+// running alongside.
+QgemmSplit qgemm_sm_split(int64_t M, int64_t Ncols, int64_t Kc) {
+  QgemmSplit sp{1, 0};
+  if (M < 1 || Ncols % QBN != 0 || Kc % QBK != 0) return sp;
+  const int64_t tiles = (M + SBM - 1) / SBM * (Ncols / QBN), nk = Kc / QBK;
+  double best = 0.0;
+  for (int64_t S = 1; S <= std::min<int64_t>(64, nk / 4) || S == 1; ++S) {
+    const int64_t steps = (nk + S - 1) / S, splits = (nk + steps - 1) / steps;
+    if (splits != S) continue;
+    const double rounds = (double)((tiles * S + 511) / 512);
+    const double reduce_us = S > 1 ? (double)S * M * Ncols * 4.0 / 4e6 + 3.0 : 0.0;
+    const double cost = rounds * (4.0 + (double)steps) * 0.7 + reduce_us;
+    if (S == 1 || cost < best) {
+      best = cost;
+      sp = S > 1 ? QgemmSplit{(int)S, steps} : QgemmSplit{1, 0};
+    }
+  }
+  return sp;
+}
+
 size_t qgemm_split_floats(int64_t M, int64_t Ncols, int64_t Kc) {
   const QgemmSplit sp = qgemm_split(M, Ncols, Kc);
-  return sp.splits > 1 ? (size_t)sp.splits * M * Ncols : 0;
+  size_t f = sp.splits > 1 ? (size_t)sp.splits * M * Ncols : 0;
+  if (M <= kSmMaxRows) {
+    const QgemmSplit ss = qgemm_sm_split(M, Ncols, Kc);
+    if (ss.splits > 1) f = std::max(f, (size_t)ss.splits * M * Ncols);
+  }
+  return f;
 }
 
 hipError_t launch_qgemm_set(bool trans_w, const QgemmSet &set, int64_t M, const uint16_t *x, const uint16_t *la,
@@ -1066,6 +1282,31 @@ hipError_t launch_qgemm_set(bool trans_w, const QgemmSet &set, int64_t M, const 
     const int64_t nc = trans_w ? s.m[0].w.n_in : s.m[i].w.n_out, kc = trans_w ? s.m[i].w.n_out : s.m[i].w.n_in;
     cols_k_full = cols_k_full && nc % QBN == 0 && kc % QBK == 0;
   }
+  const bool dq = s.m[0].w.dq;
+  if (s.count == 1 && cols_k_full && M <= kSmMaxRows && !keep) {
+    // few tokens: qgemm_sm
+    const QgemmSplit sp = part ? qgemm_sm_split(M, Ncols, kc_max) : QgemmSplit{1, 0};
+    float *pz = sp.splits > 1 ? part : nullptr;
+    const dim3 g((unsigned)((M + SBM - 1) / SBM), (unsigned)(Ncols / QBN), (unsigned)sp.splits);
+    if (trans_w) {
+      if (dq)
+        qgemm_sm<true, true><<<g, 256, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, pz, sp.steps);
+      else
+        qgemm_sm<true, false><<<g, 256, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, pz, sp.steps);
+    } else {
+      if (dq)
+        qgemm_sm<false, true><<<g, 256, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, pz, sp.steps);
+      else
+        qgemm_sm<false, false><<<g, 256, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, pz, sp.steps);
+    }
+    if (pz) {
+      uint16_t *out = trans_w ? gx : s.m[0].out;
+      int64_t blocks = (M * Ncols / 8 + 255) / 256;
+      if (blocks > 2048) blocks = 2048;
+      qgemm_split_reduce<<<(unsigned)blocks, 256, 0, st>>>(pz, sp.splits, M, Ncols, out);
+    }
+    return hipGetLastError();
+  }
   Tiles tiles = Tiles::kAny;
   if (cols_k_full && M % QBM == 0)
     tiles = Tiles::kFull;
@@ -1075,7 +1316,6 @@ hipError_t launch_qgemm_set(bool trans_w, const QgemmSet &set, int64_t M, const 
   if (part && s.count == 1) sp = qgemm_split(M, Ncols, kc_max);
   float *pz = sp.splits > 1 ? part : nullptr;
   const dim3 g((unsigned)((M + QBM - 1) / QBM), (unsigned)ytiles, (unsigned)sp.splits);
-  const bool dq = s.m[0].w.dq;
   if (!trans_w) {  // the forward never takes a dropout mask
     if (dq)
       launch_ws<false, true, false>(tiles, g, st, s, M, x, la, lb, r, scale, gx, cb, nullptr, pz, sp.steps);
