@@ -1223,9 +1223,11 @@ QgemmSplit qgemm_split(int64_t M, int64_t Ncols, int64_t Kc) {
 // Few-token tiles (qgemm_sm) for launches of at most this many tokens.
 constexpr int64_t kSmMaxRows = 64;
 
-// The split of a few-token launch: the same estimate with two workgroups per
-// CU (512 at once), each step about 0.7 us with the other workgroup of its CU
-// running alongside.
+// The split of a few-token launch: two workgroups run per CU (512 at once);
+// the estimate is rounds x (about 4 steps of set-up + steps per split) at
+// about 0.9 us a step, plus the fp32 partials written and read back at about
+// 2 bytes per ps and a few us for the reduction's launch (fitted to split
+// sweeps at 4096 x 4096, 11008 x 4096 and 22016 x 8192 with 16 and 64 tokens).
 QgemmSplit qgemm_sm_split(int64_t M, int64_t Ncols, int64_t Kc) {
   QgemmSplit sp{1, 0};
   if (M < 1 || Ncols % QBN != 0 || Kc % QBK != 0) return sp;
@@ -1235,8 +1237,8 @@ QgemmSplit qgemm_sm_split(int64_t M, int64_t Ncols, int64_t Kc) {
     const int64_t steps = (nk + S - 1) / S, splits = (nk + steps - 1) / steps;
     if (splits != S) continue;
     const double rounds = (double)((tiles * S + 511) / 512);
-    const double reduce_us = S > 1 ? (double)S * M * Ncols * 4.0 / 4e6 + 3.0 : 0.0;
-    const double cost = rounds * (4.0 + (double)steps) * 0.7 + reduce_us;
+    const double reduce_us = S > 1 ? (double)S * M * Ncols * 4.0 / 2e6 + 3.0 : 0.0;
+    const double cost = rounds * (4.0 + (double)steps) * 0.9 + reduce_us;
     if (S == 1 || cost < best) {
       best = cost;
       sp = S > 1 ? QgemmSplit{(int)S, steps} : QgemmSplit{1, 0};
