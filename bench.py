@@ -566,24 +566,27 @@ def extra_measurements(torch, qlora, steps):
 CROSSOVER_TOKENS = (1, 2, 4, 8, 16, 32, 64, 128, 256)
 
 
-def extra_crossover(torch, qlora, steps):
+def extra_crossover(torch, qlora, steps, tokens=None, shapes=None):
     """fwd + bwd of one linear by token count, at the 7B projection (4096 x 4096, rotating over
     1.1 GB of distinct packed weights) and at the 65B gate shape (22016 x 8192, rotating over 12
     weights, 1.1 GB), r = 64.  For each T: time per fwd + bwd, GB/s of the algorithmic bytes
     (the packed weight read by each direction, activations, adapters and outputs), TFLOP/s of
     4TNK + 6Tr(N + K), and the fraction of the better of the two rooflines that time reaches
-    (roofline time = max(bytes / 8 TB/s, flops / bf16 MFMA peak))."""
+    (roofline time = max(bytes / 8 TB/s, flops / bf16 MFMA peak)).  `tokens` and `shapes` restrict
+    the sweep (to profile one case alone)."""
     out = {}
     r = 64
     g = torch.Generator(device="cuda")
     g.manual_seed(77)
     for name, N, K in (("7b_attn", 4096, 4096), ("65b_gate", 22016, 8192)):
+        if shapes and name not in shapes:
+            continue
         packed = qlora.nf4_bytes(N, K)
         weights = rotating_weights(torch, qlora, N, K, 1.1e9)
         A = _bf16_normal(torch, g, (r, K), 0.01)
         B = _bf16_normal(torch, g, (N, r), 0.01)
         rows = []
-        for T in CROSSOVER_TOKENS:
+        for T in (tokens or CROSSOVER_TOKENS):
             x = _bf16_normal(torch, g, (T, K), 1.0)
             dy = _bf16_normal(torch, g, (T, N), 1.0)
             y = torch.empty((T, N), dtype=torch.bfloat16, device="cuda")
@@ -888,6 +891,10 @@ def main():
     ap.add_argument("--extra-only", choices=["adamw", "dropout", "layers", "bulk", "gemv", "library", "crossover"],
                     default=None,
                     help="run only this extra measurement and print its JSON (for profiling it alone)")
+    ap.add_argument("--crossover-tokens", type=int, nargs="+", default=None,
+                    help="with --extra-only crossover: only these token counts")
+    ap.add_argument("--crossover-shapes", nargs="+", choices=["7b_attn", "65b_gate"], default=None,
+                    help="with --extra-only crossover: only these shapes")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="before the steps, copy 256 MiB device to device three times (untimed): the "
                          "reference kernel that scales the HBM byte counters of a profiled run")
@@ -919,7 +926,8 @@ def main():
         print(json.dumps(out), flush=True)
         return
     if args.extra_only == "crossover":
-        print(json.dumps(extra_crossover(torch, qlora, args.steps)), flush=True)
+        print(json.dumps(extra_crossover(torch, qlora, args.steps, args.crossover_tokens, args.crossover_shapes)),
+              flush=True)
         return
     if args.extra_only == "gemv":
         print(json.dumps(extra_gemv_65b(torch, qlora, workloads, args.steps)), flush=True)
