@@ -7,8 +7,9 @@ A = 0 make y row t equal to column k_t of the dequantized weight, and one-hot dy
 make grad_x row t equal to row n_t: a single product is exact in fp32, so the result must equal
 the oracle's dequantized BF16 weight bit for bit ("qlora" entry, sections "a ideia" and "como
 funciona": the 4-bit weight is dequantized to BFloat16 on every use).  Together the calls cover
-every element of every weight, in both storage forms.  T = 64 runs the few-token tiles (64 x 128,
-every wave decoding, split contraction); T = 256 and 512 the 256 x 128 tiles.
+every element of every weight, in both storage forms.  T = 40 and 64 run the few-token tiles
+(64 x 128, every wave decoding, split contraction; at T = 40 rows 40..63 read row 39 and are never
+stored); T = 256 and 512 the 256 x 128 tiles.
 """
 
 import numpy as np
@@ -39,7 +40,7 @@ def _zeros(*shape):
 
 
 @pytest.mark.parametrize("double_quant", [True, False])
-@pytest.mark.parametrize("T", [64, 256, 512])
+@pytest.mark.parametrize("T", [40, 64, 256, 512])
 def test_single_linear_every_element(T, double_quant):
     announce(f"full-tile one-hot {N_OUT}x{N_IN} T={T} double_quant={double_quant}")
     w, rng = _weight(300 + T + double_quant)
@@ -48,10 +49,11 @@ def test_single_linear_every_element(T, double_quant):
     bits = workloads.to_bf16_bits
     b_rand = dev_bf16(bits((rng.standard_normal((N_OUT, R)) * 0.01).astype(np.float32)))
     a_rand = dev_bf16(bits((rng.standard_normal((R, N_IN)) * 0.01).astype(np.float32)))
-    # forward: the columns of W_hat, every column once over the calls
+    # forward: the columns of W_hat, every column at least once over the calls
     cols = rng.permutation(N_IN)
-    for part in range(N_IN // T):
-        ks = cols[part * T:(part + 1) * T]
+    for part in range(-(-N_IN // T)):
+        ks = cols[(part * T) % N_IN:][:T]
+        ks = np.concatenate([ks, cols[:T - ks.size]])
         y, _ = qlora.linear_fwd(dev_bf16(_one_hot(T, N_IN, ks)), q, dev_bf16(_zeros(R, N_IN)), b_rand, 0.5)
         assert np.array_equal(host_bits(y), wh[:, ks].T), ("forward", part)
     # grad_x: the rows of W_hat, every row once over the calls
