@@ -232,6 +232,16 @@ SetPlan plan_linear_set(int64_t T, int count, const int64_t *N, int64_t K, int r
     off += align256(lora_set_part_floats(T, count, N, K, r) * 4);
     p.off_um = off;
   }
+  // grad_x of a set whose members share n_out may split its contraction (each
+  // split contracts the same range of every member): its fp32 partial tiles
+  p.off_qpart = 0;
+  bool same_n = T > kGemvMaxT;
+  for (int i = 1; i < count; ++i) same_n = same_n && N[i] == N[0];
+  const size_t qsplit = same_n ? qgemm_split_floats(T, K, N[0]) : 0;
+  if (qsplit) {
+    p.off_qpart = off;
+    off += align256(qsplit * 4);
+  }
   p.total = off;
   return p;
 }
@@ -330,7 +340,8 @@ hipError_t launch_linear_set_bwd(const SetPlan &p, const uint16_t *const *dy, co
     }
     TimedLaunch tl;
     const bool timed = timing_begin(st, tl, kTimedQgemmDx);
-    e = launch_qgemm_set(true, s, p.T, nullptr, v, A_set, (int)rt, scale, grad_x, cb, st);
+    e = launch_qgemm_set(true, s, p.T, nullptr, v, A_set, (int)rt, scale, grad_x, cb, st, nullptr,
+                         p.off_qpart ? (float *)(ws + p.off_qpart) : nullptr);
     if (timed) timing_end(st, tl);
     if (e != hipSuccess) return e;
   }

@@ -636,10 +636,11 @@ __device__ __forceinline__ QgemmMember set_member(const QgemmSet &s, int i) {
 // kClamp (with kFull only): M is not a multiple of QBM; the last row tile's
 // missing rows read a valid row (ActDma) and are never stored, so it runs the
 // full-tile pipeline.
-// Split contraction (single linear only; part != nullptr): workgroup z of the
-// grid's third dimension contracts steps [z split_steps, (z + 1) split_steps)
-// and writes its fp32 tile to part[z][M][Ncols]; split 0 also carries the
-// adapter term; qgemm_split_reduce adds the splits in order.
+// Split contraction (a single linear, or grad_x of a set whose members share
+// n_out; part != nullptr): workgroup z of the grid's third dimension contracts
+// steps [z split_steps, (z + 1) split_steps) of every member and writes its
+// fp32 tile to part[z][M][Ncols]; split 0 also carries the adapter term;
+// qgemm_split_reduce adds the splits in order.
 template <bool kTransW, bool kDQ, bool kDrop, bool kClamp, bool kFull>
 __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const uint16_t *__restrict__ x,
                                                 const uint16_t *__restrict__ la, const uint16_t *__restrict__ lb,
@@ -1314,8 +1315,12 @@ hipError_t launch_qgemm_set(bool trans_w, const QgemmSet &set, int64_t M, const 
     tiles = Tiles::kFull;
   else if (cols_k_full && kc_max < ((int64_t)1 << 22))
     tiles = Tiles::kFullClamped;
+  // A split contracts the same range of steps of every member, so a set splits
+  // only in grad_x and only when its members share n_out.
+  bool same_kc = true;
+  for (int i = 1; i < s.count; ++i) same_kc = same_kc && s.m[i].w.n_out == s.m[0].w.n_out;
   QgemmSplit sp{1, 0};
-  if (part && s.count == 1) sp = qgemm_split(M, Ncols, kc_max);
+  if (part && (s.count == 1 || (trans_w && same_kc))) sp = qgemm_split(M, Ncols, kc_max);
   float *pz = sp.splits > 1 ? part : nullptr;
   const dim3 g((unsigned)((M + QBM - 1) / QBM), (unsigned)ytiles, (unsigned)sp.splits);
   if (!trans_w) {  // the forward never takes a dropout mask
