@@ -31,8 +31,46 @@ __device__ __forceinline__ float next_down(float f) {
   return __uint_as_float((u & 0x80000000u) ? u + 1u : u - 1u);
 }
 
+// Threshold j of a block with constant c1: x is above midpoint j of the
+// levels exactly when x > tau_j (fp32 compare).  tau_j is the fp32 rounding
+// down of the exact product M_j c1 (exact in fp64: M_j has at most 26
+// significant bits, c1 24); an exact tie on the negative side (j < 7) counts
+// as above (toward zero), so tau_j moves one step further down there.
+__device__ __forceinline__ float threshold(double m, double c1, int j) {
+  const double t = m * c1;  // exact in fp64
+  float f = (float)t;
+  const double fd = (double)f;
+  if (fd > t || (fd == t && j < 7)) f = next_down(f);
+  return f;
+}
+
+// The 15 thresholds of a block.
+struct Thresholds {
+  float t[15];
+};
+
+// The number of thresholds below x, #{j : x > tau_j}, for non-decreasing
+// tau_0..tau_14 (M_j increases with j, c1 >= 0, and rounding down keeps the
+// order): four steps of a binary search, each comparing x with the one
+// threshold the previous steps select.  The candidates are selected as values
+// (a conditional between two array elements would be a conditional address,
+// which puts the array in scratch memory).
+__device__ __forceinline__ float pick(bool c, float a, float b) { return c ? a : b; }
+
+__device__ __forceinline__ uint32_t code_of(float x, const Thresholds &tau) {
+  const float *t = tau.t;
+  const bool b3 = x > t[7];
+  const bool b2 = x > pick(b3, t[11], t[3]);
+  const bool b1 = x > pick(b3, pick(b2, t[13], t[9]), pick(b2, t[5], t[1]));
+  const float u = pick(b3, pick(b2, pick(b1, t[14], t[12]), pick(b1, t[10], t[8])),
+                       pick(b2, pick(b1, t[6], t[4]), pick(b1, t[2], t[0])));
+  const bool b0 = x > u;
+  return 8u * b3 + 4u * b2 + 2u * b1 + (uint32_t)b0;
+}
+
 // 8 lanes own one 64-element block (8 elements each); a 256-thread workgroup
-// covers 32 blocks per pass and strides over the tensor.
+// covers 32 blocks per pass and strides over the tensor.  Lane s of a block
+// forms thresholds s and s + 8 and the 8 lanes exchange them.
 template <bool kBf16Src>
 __global__ __launch_bounds__(256) void quantize_blocks(const void *__restrict__ src, int64_t numel,
                                                        int64_t nblocks, uint8_t *__restrict__ codes,
@@ -40,9 +78,12 @@ __global__ __launch_bounds__(256) void quantize_blocks(const void *__restrict__ 
                                                        unsigned long long *__restrict__ bins,
                                                        uint32_t *__restrict__ status, Midpoints mid) {
   __shared__ unsigned long long sbins[256];
+  __shared__ double smid[16];
   sbins[threadIdx.x] = 0ull;
+  if (threadIdx.x < 15) smid[threadIdx.x] = mid.m[threadIdx.x];
   __syncthreads();
   const int sub = threadIdx.x & 7;
+  const double m_lo = smid[sub], m_hi = sub < 7 ? smid[sub + 8] : 0.0;
   bool bad = false;
   for (int64_t b = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3); b < nblocks; b += (int64_t)gridDim.x * 32) {
     const int64_t e0 = b * kBlock + sub * 8;
@@ -84,26 +125,16 @@ __global__ __launch_bounds__(256) void quantize_blocks(const void *__restrict__ 
     am = max(am, (uint32_t)__shfl_xor((int)am, 4, 8));
     if (am >= 0x7F800000u) bad = true;
     const float c1 = __uint_as_float(am);
-    // thresholds: x is above midpoint j exactly when x > tau_j (fp32 compare)
     const double cd = (double)c1;
-    float tau[15];
+    const float t_lo = threshold(m_lo, cd, sub), t_hi = threshold(m_hi, cd, sub + 8);
+    Thresholds tau;
 #pragma unroll
-    for (int j = 0; j < 15; ++j) {
-      const double t = mid.m[j] * cd;  // exact in fp64
-      float f = (float)t;
-      const double fd = (double)f;
-      // round down; an exact tie on the negative side counts as "above" (toward zero)
-      if (fd > t || (fd == t && j < 7)) f = next_down(f);
-      tau[j] = f;
-    }
+    for (int j = 0; j < 8; ++j) tau.t[j] = __shfl(t_lo, j, 8);
+#pragma unroll
+    for (int j = 8; j < 15; ++j) tau.t[j] = __shfl(t_hi, j - 8, 8);
     uint32_t packed = 0u;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t c = 0u;
-#pragma unroll
-      for (int j = 0; j < 15; ++j) c += (x[i] > tau[j]) ? 1u : 0u;
-      packed |= c << (4 * i);
-    }
+    for (int i = 0; i < 8; ++i) packed |= code_of(x[i], tau) << (4 * i);
     const int64_t byte0 = e0 >> 1;
     if (byte0 + 4 <= codes_bytes) {
       *(uint32_t *)(codes + byte0) = packed;
