@@ -989,32 +989,29 @@ __global__ __launch_bounds__(256) void qgemm_split_reduce(const float *__restric
 // ---------------------------------------------------------------------------
 // Few-token tiles.  With a few dozen tokens a 256-row tile is mostly padding:
 // its matrix work is wasted and the step time is the decode, which only the
-// four producer waves of qgemm_ws do.  qgemm_sm takes 64 x 128 output tiles
-// in workgroups of four waves, two workgroups per CU, and every wave both
-// decodes (the producer lane mapping of qgemm_ws: one unit of 32 codes per
-// lane and step, the same register byte tables) and multiplies (tile rows
-// 0..63, columns 32 w .. 32 w + 31), so that two waves per SIMD issue decode
-// instructions.  The activation tile (64 x 64 per step) goes through
-// registers into LDS, rows at or past M reading row M - 1 (never stored).
-// Every load is an ordinary compiler-tracked load, so the waits the compiler
-// places are exact.  Pipeline over a three-stage LDS ring: at step k the
-// waves multiply stage k and write stage k+2 (codes and activation loaded
-// three steps earlier into one of three register sets, which then fetches
-// stage k+5).  Single linears whose tiles are full in columns and
-// contraction, without a dropout mask; a split contraction (blockIdx.z) as in
-// qgemm_ws.
-constexpr int SBM = 64;  // rows (tokens) of a few-token tile
-
-// Codes and activation of one stage for one lane: its unit of the weight tile
-// and two 16-byte chunks of the activation tile (row tid / 4, chunks
-// 2 (tid % 4) and 2 (tid % 4) + 1).
+// four producer waves of qgemm_ws do.  qgemm_sm takes kRows x 128 output tiles
+// (kRows = 64 or 128) in workgroups of four waves, two workgroups per CU, and
+// every wave both decodes (the producer lane mapping of qgemm_ws: one unit of
+// 32 codes per lane and step, the same register byte tables) and multiplies
+// (tile rows 0..kRows-1, columns 32 w .. 32 w + 31), so that two waves per
+// SIMD issue decode instructions.  The activation tile (kRows x 64 per step)
+// goes through registers into LDS, rows at or past M reading row M - 1 (never
+// stored).  Every load is an ordinary compiler-tracked load, so the waits the
+// compiler places are exact.  Codes and activation are loaded three steps
+// ahead of their LDS store into one of three register sets.  With 64 rows the
+// LDS ring has three stages (stage k multiplied while stage k+2 is written,
+// 78 KB); with 128 rows two (stage k+1 written, 68 KB), so that two
+// workgroups still fit a CU.  Single linears whose tiles are full in columns
+// and contraction, without a dropout mask; a split contraction (blockIdx.z)
+// as in qgemm_ws.
 struct SmStage {
   Stage w;
-  u32x4 a0, a1;
+  u32x4 a0, a1;  // row tid / 4, chunks 2 (tid % 4) and 2 (tid % 4) + 1
+  u32x4 a2, a3;  // 128-row tiles: the same chunks of row tid / 4 + 64
 };
 
-// The 8 MFMAs of one stage for wave w: A fragments of rows 0..63 (two 32-row
-// halves), the B fragment of columns 32 w .. 32 w + 31.
+// The 8 MFMAs of one stage of a 64-row tile for wave w: A fragments of rows
+// 0..63 (two 32-row halves), the B fragment of columns 32 w .. 32 w + 31.
 template <bool kTransW>
 __device__ __forceinline__ void sm_stage_mfma(const uint16_t *A, const uint16_t *B, int w, int lane,
                                               f32x16 (&acc)[2]) {
@@ -1032,18 +1029,40 @@ __device__ __forceinline__ void sm_stage_mfma(const uint16_t *A, const uint16_t 
   }
 }
 
-template <bool kTransW, bool kDQ>
+// The 16 MFMAs of one stage of a 128-row tile: the fragments of slice kk+1
+// read while slice kk multiplies (registers for two slices).
+template <bool kTransW>
+__device__ __forceinline__ void sm_stage_mfma(const uint16_t *A, const uint16_t *B, int w, int lane,
+                                              f32x16 (&acc)[4]) {
+  u32x4 a[2][4], b[2];
+  auto frags = [&](int kk, u32x4 (&fa)[4], u32x4 &fb) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[i] = load_a_frag(A, 0, lane, kk, i);
+    fb = load_b_frag<kTransW>(B, w >> 1, lane, kk, w & 1);
+  };
+  frags(0, a[0], b[0]);
+#pragma unroll
+  for (int kk = 0; kk < QBK / 16; ++kk) {
+    if (kk + 1 < QBK / 16) frags(kk + 1, a[(kk + 1) & 1], b[(kk + 1) & 1]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] = mfma(a[kk & 1][i], b[kk & 1], acc[i]);
+  }
+}
+
+template <bool kTransW, bool kDQ, int kRows>
 __global__ __launch_bounds__(256, 2) void qgemm_sm(QgemmSet set, int64_t M, const uint16_t *__restrict__ x,
                                                    const uint16_t *__restrict__ la, const uint16_t *__restrict__ lb,
                                                    int r, float scale, uint16_t *__restrict__ gx, Codebook cb,
                                                    float *__restrict__ part, int64_t split_steps) {
-  __shared__ __attribute__((aligned(16))) uint16_t sa[3][SBM * 64];
-  __shared__ __attribute__((aligned(16))) uint16_t sb[3][QBN * QLD];
+  constexpr int kSt = kRows == 64 ? 3 : 2;  // LDS stages
+  constexpr int kTiles = kRows / 32;        // 32-row MFMA tiles; also 16-byte activation chunks per thread
+  __shared__ __attribute__((aligned(16))) uint16_t sa[kSt][kRows * 64];
+  __shared__ __attribute__((aligned(16))) uint16_t sb[kSt][QBN * QLD];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, lhi = lane >> 5;
   const QgemmMember mm = set.m[0];
   const int64_t Ncols = kTransW ? mm.w.n_in : mm.w.n_out, Kc = kTransW ? mm.w.n_out : mm.w.n_in;
-  const int64_t m0 = (int64_t)blockIdx.x * SBM, c0 = (int64_t)blockIdx.y * QBN;
+  const int64_t m0 = (int64_t)blockIdx.x * kRows, c0 = (int64_t)blockIdx.y * QBN;
   const uint16_t *act = kTransW ? mm.act : x;
   const uint16_t *lb_t = kTransW ? lb : mm.lb;
   uint16_t *out = kTransW ? gx : mm.out;
@@ -1053,19 +1072,28 @@ __global__ __launch_bounds__(256, 2) void qgemm_sm(QgemmSet set, int64_t M, cons
   const float mu = kDQ ? *mm.w.mu : 0.f;
   const Producer<kTransW, kDQ> p = member_producer<kTransW, kDQ>(mm, x, M, m0, c0, tid, mu, kstep0);
 
-  // this lane's activation row (clamped) and chunk pair
+  // this lane's activation rows (clamped) and chunk pair
   const int arow = tid >> 2, ach = 2 * (tid & 3);
   const uint16_t *asrc = act + min(m0 + arow, M - 1) * Kc + kstep0 * QBK + 8 * ach;
+  const uint16_t *asrc2 = act + min(m0 + arow + 64, M - 1) * Kc + kstep0 * QBK + 8 * ach;
   auto st = [nk](int64_t k) { return min(k, nk - 1); };
   auto load = [&](int64_t k, SmStage &c) {
     p.template load_w<true>(k, c.w);
     c.a0 = *(const u32x4 *)(asrc + k * QBK);
     c.a1 = *(const u32x4 *)(asrc + k * QBK + 8);
+    if (kRows == 128) {
+      c.a2 = *(const u32x4 *)(asrc2 + k * QBK);
+      c.a3 = *(const u32x4 *)(asrc2 + k * QBK + 8);
+    }
   };
   auto store = [&](const SmStage &c, int buf) {
     p.write_rt(c.w, cb, sb[buf]);
     *(u32x4 *)&sa[buf][act_off(arow, ach)] = c.a0;
     *(u32x4 *)&sa[buf][act_off(arow, ach + 1)] = c.a1;
+    if (kRows == 128) {
+      *(u32x4 *)&sa[buf][act_off(arow + 64, ach)] = c.a2;
+      *(u32x4 *)&sa[buf][act_off(arow + 64, ach + 1)] = c.a3;
+    }
   };
 
   SmStage s0, s1, s2;
@@ -1073,18 +1101,19 @@ __global__ __launch_bounds__(256, 2) void qgemm_sm(QgemmSet set, int64_t M, cons
   load(st(1), s1);
   load(st(2), s2);
 
-  f32x16 acc[2];
+  f32x16 acc[kTiles];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kTiles; ++i)
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[i][q] = 0.f;
   // LoRA term (first split only): scale * la lb^T, one 64-wide chunk of the
-  // rank at a time through stage 2 of both rings (zero past r and past M)
+  // rank at a time through the last LDS stage (zero past r and past M)
+  constexpr int kL = kSt - 1;
   const bool lvec = (r % 8) == 0 && (set.ld_la % 8) == 0;
   for (int j0 = 0; j0 < r_eff; j0 += QBK) {
-    u32x4 va[2], vb[4];
+    u32x4 va[kTiles], vb[4];
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {  // 64 rows x 8 chunks of the rank
+    for (int it = 0; it < kTiles; ++it) {  // kRows rows x 8 chunks of the rank
       const int idx = tid + 256 * it, row = idx >> 3, ch = idx & 7;
       const int64_t grow = m0 + row;
       va[it] = grow < M ? ld8(la + grow * set.ld_la, j0 + 8 * ch, r, lvec) : u32x4{0u, 0u, 0u, 0u};
@@ -1102,59 +1131,86 @@ __global__ __launch_bounds__(256, 2) void qgemm_sm(QgemmSet set, int64_t M, cons
       }
     }
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
+    for (int it = 0; it < kTiles; ++it) {
       const int idx = tid + 256 * it;
-      *(u32x4 *)&sa[2][act_off(idx >> 3, idx & 7)] = va[it];
+      *(u32x4 *)&sa[kL][act_off(idx >> 3, idx & 7)] = va[it];
     }
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
       const int idx = tid + 256 * it;
       if (!kTransW)
-        *(u32x4 *)&sb[2][(idx >> 3) * QLD + 8 * (idx & 7)] = vb[it];
+        *(u32x4 *)&sb[kL][(idx >> 3) * QLD + 8 * (idx & 7)] = vb[it];
       else
-        *(u32x4 *)&sb[2][(idx >> 4) * TLD + 8 * (idx & 15)] = vb[it];
+        *(u32x4 *)&sb[kL][(idx >> 4) * TLD + 8 * (idx & 15)] = vb[it];
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
     wg_barrier();
-    sm_stage_mfma<kTransW>(sa[2], sb[2], w, lane, acc);
+    sm_stage_mfma<kTransW>(sa[kL], sb[kL], w, lane, acc);
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
-    wg_barrier();  // stage 2 of the rings is free again
+    wg_barrier();  // the last stage is free again
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kTiles; ++i)
 #pragma unroll
     for (int q = 0; q < 16; ++q) acc[i][q] *= scale;
 
-  store(s0, 0);
-  load(st(3), s0);
-  store(s1, 1);
-  load(st(4), s1);
-  __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
-  wg_barrier();  // stages 0 and 1 ready
+  int64_t kt = 0;
+  if constexpr (kSt == 3) {
+    // at step k: multiply stage k, write stage k+2 (its set then fetches k+5)
+    store(s0, 0);
+    load(st(3), s0);
+    store(s1, 1);
+    load(st(4), s1);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    wg_barrier();  // stages 0 and 1 ready
 #define QGEMM_SM_STEP(K_, CUR, BUF, NEXT)                                              \
   if ((K_) < nk) {                                                                    \
-    sm_stage_mfma<kTransW>(sa[BUF], sb[BUF], w, lane, acc);                           \
+    sm_stage_mfma<kTransW>(sa[BUF], sb[BUF], w, lane, acc);                   \
     store(CUR, NEXT);                                                                 \
     load(st((K_) + 5), CUR);                                                          \
     __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));                                   \
     wg_barrier();                                                                     \
   }
-  int64_t kt = 0;
-  for (; kt + 3 <= nk; kt += 3) {
+    for (; kt + 3 <= nk; kt += 3) {
+      QGEMM_SM_STEP(kt, s2, 0, 2)
+      QGEMM_SM_STEP(kt + 1, s0, 1, 0)
+      QGEMM_SM_STEP(kt + 2, s1, 2, 1)
+    }
     QGEMM_SM_STEP(kt, s2, 0, 2)
     QGEMM_SM_STEP(kt + 1, s0, 1, 0)
-    QGEMM_SM_STEP(kt + 2, s1, 2, 1)
-  }
-  QGEMM_SM_STEP(kt, s2, 0, 2)
-  QGEMM_SM_STEP(kt + 1, s0, 1, 0)
 #undef QGEMM_SM_STEP
+  } else {
+    // at step k: multiply stage k, write stage k+1 into the other stage (its set
+    // then fetches k+4)
+    store(s0, 0);
+    load(st(3), s0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));
+    wg_barrier();  // stage 0 ready
+#define QGEMM_SM_STEP(K_, CUR)                                                         \
+  if ((K_) < nk) {                                                                    \
+    const int buf = (int)((K_) & 1);                                                  \
+    sm_stage_mfma<kTransW>(sa[buf], sb[buf], w, lane, acc);                   \
+    store(CUR, buf ^ 1);                                                              \
+    load(st((K_) + 4), CUR);                                                          \
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(63, 0));                                   \
+    wg_barrier();                                                                     \
+  }
+    for (; kt + 3 <= nk; kt += 3) {
+      QGEMM_SM_STEP(kt, s1)
+      QGEMM_SM_STEP(kt + 1, s2)
+      QGEMM_SM_STEP(kt + 2, s0)
+    }
+    QGEMM_SM_STEP(kt, s1)
+    QGEMM_SM_STEP(kt + 1, s2)
+#undef QGEMM_SM_STEP
+  }
 
   // element q of acc[i]: tile row 32 i + 8 (q / 4) + 4 (lane / 32) + q % 4, column 32 w + lane % 32
   const int64_t col = c0 + 32 * w + l32;
   if (part) {
     float *pz = part + (int64_t)blockIdx.z * M * Ncols;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < kTiles; ++i)
 #pragma unroll
       for (int q = 0; q < 16; ++q) {
         const int64_t row = m0 + 32 * i + 8 * (q >> 2) + 4 * lhi + (q & 3);
@@ -1163,13 +1219,30 @@ __global__ __launch_bounds__(256, 2) void qgemm_sm(QgemmSet set, int64_t M, cons
     return;
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < kTiles; ++i)
 #pragma unroll
     for (int q = 0; q < 16; ++q) {
       const int64_t row = m0 + 32 * i + 8 * (q >> 2) + 4 * lhi + (q & 3);
       __bf16 h = (__bf16)acc[i][q];
       if (row < M) out[row * Ncols + col] = __builtin_bit_cast(uint16_t, h);
     }
+}
+
+template <int kRows>
+void launch_sm(bool trans_w, bool dq, dim3 g, hipStream_t st, const QgemmSet &s, int64_t M, const uint16_t *x,
+               const uint16_t *la, const uint16_t *lb, int r, float scale, uint16_t *gx, const Codebook &cb,
+               float *part, int64_t split_steps) {
+  if (trans_w) {
+    if (dq)
+      qgemm_sm<true, true, kRows><<<g, 256, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, part, split_steps);
+    else
+      qgemm_sm<true, false, kRows><<<g, 256, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, part, split_steps);
+  } else {
+    if (dq)
+      qgemm_sm<false, true, kRows><<<g, 256, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, part, split_steps);
+    else
+      qgemm_sm<false, false, kRows><<<g, 256, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, part, split_steps);
+  }
 }
 
 // Tiles of a grid: any (some may be partial), all full, or all full with the
@@ -1221,8 +1294,10 @@ QgemmSplit qgemm_split(int64_t M, int64_t Ncols, int64_t Kc) {
   return sp;
 }
 
-// Few-token tiles (qgemm_sm) for launches of at most this many tokens.
-constexpr int64_t kSmMaxRows = 64;
+// Few-token tiles (qgemm_sm) for launches of at most this many tokens: 64-row
+// tiles up to 64 tokens, 128-row tiles above.
+constexpr int64_t kSmMaxRows = 128;
+constexpr int sm_rows(int64_t M) { return M <= 64 ? 64 : 128; }
 
 // The split of a few-token launch: two workgroups run per CU (512 at once);
 // the estimate is rounds x (about 4 steps of set-up + steps per split) at
@@ -1232,7 +1307,8 @@ constexpr int64_t kSmMaxRows = 64;
 QgemmSplit qgemm_sm_split(int64_t M, int64_t Ncols, int64_t Kc) {
   QgemmSplit sp{1, 0};
   if (M < 1 || Ncols % QBN != 0 || Kc % QBK != 0) return sp;
-  const int64_t tiles = (M + SBM - 1) / SBM * (Ncols / QBN), nk = Kc / QBK;
+  const int rows = sm_rows(M);
+  const int64_t tiles = (M + rows - 1) / rows * (Ncols / QBN), nk = Kc / QBK;
   double best = 0.0;
   for (int64_t S = 1; S <= std::min<int64_t>(64, nk / 4) || S == 1; ++S) {
     const int64_t steps = (nk + S - 1) / S, splits = (nk + steps - 1) / steps;
@@ -1290,18 +1366,12 @@ hipError_t launch_qgemm_set(bool trans_w, const QgemmSet &set, int64_t M, const 
     // few tokens: qgemm_sm
     const QgemmSplit sp = part ? qgemm_sm_split(M, Ncols, kc_max) : QgemmSplit{1, 0};
     float *pz = sp.splits > 1 ? part : nullptr;
-    const dim3 g((unsigned)((M + SBM - 1) / SBM), (unsigned)(Ncols / QBN), (unsigned)sp.splits);
-    if (trans_w) {
-      if (dq)
-        qgemm_sm<true, true><<<g, 256, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, pz, sp.steps);
-      else
-        qgemm_sm<true, false><<<g, 256, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, pz, sp.steps);
-    } else {
-      if (dq)
-        qgemm_sm<false, true><<<g, 256, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, pz, sp.steps);
-      else
-        qgemm_sm<false, false><<<g, 256, 0, st>>>(s, M, x, la, lb, r, scale, gx, cb, pz, sp.steps);
-    }
+    const int rows = sm_rows(M);
+    const dim3 g((unsigned)((M + rows - 1) / rows), (unsigned)(Ncols / QBN), (unsigned)sp.splits);
+    if (rows == 64)
+      launch_sm<64>(trans_w, dq, g, st, s, M, x, la, lb, r, scale, gx, cb, pz, sp.steps);
+    else
+      launch_sm<128>(trans_w, dq, g, st, s, M, x, la, lb, r, scale, gx, cb, pz, sp.steps);
     if (pz) {
       uint16_t *out = trans_w ? gx : s.m[0].out;
       int64_t blocks = (M * Ncols / 8 + 255) / 256;

@@ -7,9 +7,9 @@ A = 0 make y row t equal to column k_t of the dequantized weight, and one-hot dy
 make grad_x row t equal to row n_t: a single product is exact in fp32, so the result must equal
 the oracle's dequantized BF16 weight bit for bit ("qlora" entry, sections "a ideia" and "como
 funciona": the 4-bit weight is dequantized to BFloat16 on every use).  Together the calls cover
-every element of every weight, in both storage forms.  T = 40 and 64 run the few-token tiles
-(64 x 128, every wave decoding, split contraction; at T = 40 rows 40..63 read row 39 and are never
-stored); T = 256 and 512 the 256 x 128 tiles.
+every element of every weight, in both storage forms.  T = 40 and 64 run the 64-row few-token
+tiles (every wave decoding, split contraction; at T = 40 rows 40..63 read row 39 and are never
+stored), T = 128 the 128-row few-token tiles; T = 256 and 512 the 256 x 128 tiles.
 """
 
 import numpy as np
@@ -40,7 +40,7 @@ def _zeros(*shape):
 
 
 @pytest.mark.parametrize("double_quant", [True, False])
-@pytest.mark.parametrize("T", [40, 64, 256, 512])
+@pytest.mark.parametrize("T", [40, 64, 128, 256, 512])
 def test_single_linear_every_element(T, double_quant):
     announce(f"full-tile one-hot {N_OUT}x{N_IN} T={T} double_quant={double_quant}")
     w, rng = _weight(300 + T + double_quant)

@@ -93,12 +93,13 @@ def test_split_contraction_and_clamped_rows(shape):
 
 
 @pytest.mark.parametrize("shape", [(256, 512, 24, 5), (512, 1024, 64, 96), (384, 640, 7, 200),
-                                   (128, 64, 33, 64)])
+                                   (128, 64, 33, 64), (256, 512, 100, 5), (512, 1024, 128, 96),
+                                   (384, 640, 65, 200)])
 def test_few_token_tiles_ranks(shape):
-    """The 64-row few-token tiles (5 to 64 tokens, every tile full in columns and contraction) with
-    ranks that are not a multiple of 8 (element-wise adapter loads) and ranks that take two to four
-    64-wide adapter chunks; the last shape's forward contracts a single step (its grad_x, 64 columns
-    wide, runs the 256-row tiles)."""
+    """The few-token tiles (64 rows for 5 to 64 tokens, 128 rows for 65 to 128; every tile full in
+    columns and contraction) with ranks that are not a multiple of 8 (element-wise adapter loads)
+    and ranks that take two to four 64-wide adapter chunks; the fourth shape's forward contracts a
+    single step (its grad_x, 64 columns wide, runs the 256-row tiles)."""
     n_out, n_in, T, r = shape
     announce(f"linear few-token tiles n_out={n_out} n_in={n_in} T={T} r={r}")
     case = workloads.custom_case(n_out, n_in, T, r, 16.0, seed=n_out + 11 * T + r)
