@@ -45,8 +45,10 @@ __device__ __forceinline__ u32x4 ld8(const uint16_t *row, int64_t c, int64_t nco
 
 // Tile rows [r0, r0 + 64) x columns [c0, c0 + 64) of a row-major [nrows x ld]
 // bf16 matrix (columns >= ncols and rows >= nrows read as zero); thread t
-// fetches row t/4, columns 16 (t%4) .. +15.  kFull: the tile is known to be in
-// range and 16-byte aligned, so the loads are unconditional.
+// fetches columns 8 (t%8) .. +7 of rows t/8 and t/8 + 32, so that each wave's
+// load covers 8 whole 128-byte rows (a load that covers half of each of 16
+// lines moves about half as many bytes per cycle from L2).  kFull: the tile is
+// known to be in range and 16-byte aligned, so the loads are unconditional.
 struct TileRegs {
   u32x4 v[2];
 };
@@ -54,22 +56,22 @@ struct TileRegs {
 template <bool kFull>
 __device__ __forceinline__ void load_tile(const uint16_t *src, int64_t ld, int64_t nrows, int64_t ncols,
                                           int64_t r0, int64_t c0, bool vec, int tid, TileRegs &t) {
-  const int64_t row = r0 + (tid >> 2);
-  const int64_t col = c0 + 16 * (tid & 3);
+  const int64_t row = r0 + (tid >> 3);
+  const int64_t col = c0 + 8 * (tid & 7);
   if (kFull) {
     const uint16_t *p = src + row * ld + col;
     t.v[0] = *(const u32x4 *)p;
-    t.v[1] = *(const u32x4 *)(p + 8);
+    t.v[1] = *(const u32x4 *)(p + 32 * ld);
     return;
   }
 #pragma unroll
   for (int h = 0; h < 2; ++h)
-    t.v[h] = (row < nrows) ? ld8(src + row * ld, col + 8 * h, ncols, vec) : u32x4{0u, 0u, 0u, 0u};
+    t.v[h] = (row + 32 * h < nrows) ? ld8(src + (row + 32 * h) * ld, col, ncols, vec) : u32x4{0u, 0u, 0u, 0u};
 }
 
 __device__ __forceinline__ void store_tile(const TileRegs &t, uint16_t *lds, int tid) {
 #pragma unroll
-  for (int h = 0; h < 2; ++h) *(u32x4 *)&lds[(tid >> 2) * LLD + 16 * (tid & 3) + 8 * h] = t.v[h];
+  for (int h = 0; h < 2; ++h) *(u32x4 *)&lds[((tid >> 3) + 32 * h) * LLD + 8 * (tid & 7)] = t.v[h];
 }
 
 // MFMA operand fragment for output rows/cols [base, base + 32), contraction

@@ -107,6 +107,20 @@ def test_few_token_tiles_ranks(shape):
     _check_case(case, scale=0.75, need_u=False)
 
 
+@pytest.mark.parametrize("shape", [(3100, 1024, 2049, 24), (2560, 1536, 1024, 64), (1536, 2048, 704, 96),
+                                   (3000, 1216, 300, 5)])
+def test_adapter_products_at_long_token_counts(shape):
+    """The adapter products over 300 to 2049 tokens with ragged token counts, ranks and widths:
+    u and v with partial 64 x 64 tiles in both dimensions, v and the gradients with contraction
+    lengths (n_out and T) that are not whole 256-wide split chunks, and the gradients of a rank of 5
+    (adapter rows not 16-byte aligned).  The second shape has full tiles throughout."""
+    n_out, n_in, T, r = shape
+    announce(f"linear long-token adapter products n_out={n_out} n_in={n_in} T={T} r={r}")
+    case = workloads.custom_case(n_out, n_in, T, r, 16.0, seed=n_out + 3 * T + r)
+    _check_case(case)
+    _check_case(case, scale=0.5, need_u=False)
+
+
 @pytest.mark.parametrize("T", [1, 2, 4, 8, 16, 32, 64, 128, 256])
 def test_7b_projection_every_token_count_of_the_sweep(T):
     """The 7B projection (4096 x 4096, r = 64) at every token count the benchmark sweeps: the
