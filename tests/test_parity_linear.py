@@ -205,6 +205,29 @@ def test_deterministic():
         assert np.array_equal(host(t1), host(t2))
 
 
+def test_grid_size_does_not_change_the_bits():
+    """LDS-race audit: the same rows through the fused GEMM in launches of 256 and of 512
+    workgroups (2048 and 4096 tokens at 4096 x 4096: whole 256 x 128 tiles, no contraction split,
+    so every output element is summed in the same order) are bit-identical, forward and grad_x,
+    and a second run of each launch repeats its bits.  The adapter terms are zero (B = 0 for the
+    forward, A = 0 for grad_x), so that only the fused GEMM decides the bits; a race on its LDS
+    rings would show as a difference between the two schedules."""
+    announce("linear grid-size audit 4096x4096 T=2048/4096")
+    case = workloads.custom_case(4096, 4096, 4096, 64, 16.0, seed=4242)
+    q = qlora.quantize(dev_f32(case.w))
+    x, dy = dev_bf16(case.x), dev_bf16(case.dy)
+    a, b = dev_bf16(case.a), dev_bf16(case.b)
+    a0, b0 = dev_bf16(np.zeros_like(case.a)), dev_bf16(np.zeros_like(case.b))
+    y_all = host_bits(qlora.linear_fwd(x, q, a, b0, 0.5)[0])
+    gx_all = host_bits(qlora.linear_bwd(dy, x, q, a0, b, 0.5)[0])
+    assert np.array_equal(host_bits(qlora.linear_fwd(x, q, a, b0, 0.5)[0]), y_all)
+    for half in (slice(0, 2048), slice(2048, 4096)):
+        y, _ = qlora.linear_fwd(x[half].contiguous(), q, a, b0, 0.5)
+        gx, _, _ = qlora.linear_bwd(dy[half].contiguous(), x[half].contiguous(), q, a0, b, 0.5)
+        assert np.array_equal(host_bits(y), y_all[half]), ("forward", half)
+        assert np.array_equal(host_bits(gx), gx_all[half]), ("grad_x", half)
+
+
 def test_7b_projection_T2048():
     """4096 x 4096 weight, r = 64, alpha = 16, 2048 tokens (batch 4 x seq 512): the full
     outputs against the fp64 oracle."""
