@@ -124,6 +124,10 @@ struct QgemmSet {
   int count;
   int64_t ld_la;  // row stride of the adapter left factor (u_set or v_set)
   QgemmMember m[kMaxSetMembers];
+  // columns of a split's fp32 partial tiles (set by launch_qgemm_set): grad_x
+  // n_in; forward the members' column tiles side by side (tile t at columns
+  // [128 t, 128 t + 128))
+  int64_t part_cols;
 };
 // forward: x shared, la = u_set (member i reads columns [i r, i r + r)); grad_x:
 // gx = sum over members of dy_i W_hat_i + keep (.) (scale * la lb^T) with la =

@@ -233,11 +233,19 @@ SetPlan plan_linear_set(int64_t T, int count, const int64_t *N, int64_t K, int r
     p.off_um = off;
   }
   // grad_x of a set whose members share n_out may split its contraction (each
-  // split contracts the same range of every member): its fp32 partial tiles
+  // split contracts the same range of every member), and so may the forward
+  // when every member's n_out is whole 128-column tiles (or the set has one
+  // member): their fp32 partial tiles
   p.off_qpart = 0;
-  bool same_n = T > kGemvMaxT;
-  for (int i = 1; i < count; ++i) same_n = same_n && N[i] == N[0];
-  const size_t qsplit = same_n ? qgemm_split_floats(T, K, N[0]) : 0;
+  bool same_n = T > kGemvMaxT, tiles_n = T > kGemvMaxT;
+  int64_t n_all = 0;
+  for (int i = 0; i < count; ++i) {
+    same_n = same_n && N[i] == N[0];
+    tiles_n = tiles_n && (count == 1 || N[i] % 128 == 0);
+    n_all += N[i];
+  }
+  const size_t qsplit = std::max(same_n ? qgemm_split_floats(T, K, N[0]) : 0,
+                                 tiles_n ? qgemm_split_floats(T, n_all, K) : 0);
   if (qsplit) {
     p.off_qpart = off;
     off += align256(qsplit * 4);
@@ -307,7 +315,8 @@ hipError_t launch_linear_set_fwd(const SetPlan &p, const uint16_t *x, const QWei
   }
   TimedLaunch tl;
   const bool timed = timing_begin(st, tl, kTimedQgemmFwd);
-  e = launch_qgemm_set(false, s, p.T, x, u, nullptr, p.r, scale, nullptr, cb, st);
+  e = launch_qgemm_set(false, s, p.T, x, u, nullptr, p.r, scale, nullptr, cb, st, nullptr,
+                       p.off_qpart ? (float *)(ws + p.off_qpart) : nullptr);
   if (timed) timing_end(st, tl);
   return e;
 }

@@ -636,11 +636,11 @@ __device__ __forceinline__ QgemmMember set_member(const QgemmSet &s, int i) {
 // kClamp (with kFull only): M is not a multiple of QBM; the last row tile's
 // missing rows read a valid row (ActDma) and are never stored, so it runs the
 // full-tile pipeline.
-// Split contraction (a single linear, or grad_x of a set whose members share
-// n_out; part != nullptr): workgroup z of the grid's third dimension contracts
-// steps [z split_steps, (z + 1) split_steps) of every member and writes its
-// fp32 tile to part[z][M][Ncols]; split 0 also carries the adapter term;
-// qgemm_split_reduce adds the splits in order.
+// Split contraction (part != nullptr): workgroup z of the grid's third
+// dimension contracts steps [z split_steps, (z + 1) split_steps) of every
+// member and writes its fp32 tile to part[z][M][set.part_cols] (forward: a
+// member's column c at column 128 tile0 + c); split 0 also carries the adapter
+// term; qgemm_split_reduce adds the splits in order.
 template <bool kTransW, bool kDQ, bool kDrop, bool kClamp, bool kFull>
 __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const uint16_t *__restrict__ x,
                                                 const uint16_t *__restrict__ la, const uint16_t *__restrict__ lb,
@@ -911,7 +911,8 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
   if (part) {
     // a split: the fp32 tile goes straight from the accumulators to part[z]
     // (each store instruction covers 32 consecutive columns of two rows)
-    float *pz = part + (int64_t)blockIdx.z * M * Ncols;
+    const int64_t pcols = set.part_cols;
+    float *pz = part + (int64_t)blockIdx.z * M * pcols + (kTransW ? 0 : fm.tile0 * QBN);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -920,7 +921,7 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
 #pragma unroll
         for (int q = 0; q < 16; ++q) {
           const int64_t row = m0 + wm * 128 + i * 32 + 8 * (q >> 2) + 4 * lhi + (q & 3);
-          if (row < M && col < Ncols) pz[row * Ncols + col] = acc[i][j][q];
+          if (row < M && col < Ncols) pz[row * pcols + col] = acc[i][j][q];
         }
       }
     return;
@@ -960,10 +961,30 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
 
 // The splits of a grid: sum over the splits, in split order, rounded to bf16
 // once (8 columns per thread; Ncols is a multiple of QBN here).
+// The outputs of a split launch: one, or a forward set's members, whose
+// columns [col0[i], col0[i] + ncols[i]) of the partial tiles go to out[i]
+// [M x ncols[i]].
+struct SplitOut {
+  int count;
+  int64_t col0[kMaxSetMembers], ncols[kMaxSetMembers];
+  uint16_t *out[kMaxSetMembers];
+};
+
 __global__ __launch_bounds__(256) void qgemm_split_reduce(const float *__restrict__ part, int S, int64_t M,
-                                                          int64_t Ncols, uint16_t *__restrict__ out) {
+                                                          int64_t Ncols, SplitOut so) {
   const int64_t n8 = M * Ncols / 8, zs = M * Ncols / 4;  // zs: one split in float4 units
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+    // destination of these 8 columns (members' column ranges are multiples of 8)
+    uint16_t *dst;
+    if (so.count == 1) {
+      dst = so.out[0] + 8 * i;
+    } else {
+      const int64_t row = (8 * i) / Ncols, col = 8 * i - row * Ncols;
+      int m = 0;
+      for (int k = 1; k < so.count; ++k)
+        if (col >= so.col0[k]) m = k;
+      dst = so.out[m] + row * so.ncols[m] + (col - so.col0[m]);
+    }
     const f32x4 *p = (const f32x4 *)part + 2 * i;
     f32x4 a = {0.f, 0.f, 0.f, 0.f}, b = {0.f, 0.f, 0.f, 0.f};
     for (int z0 = 0; z0 < S; z0 += 4) {
@@ -981,9 +1002,18 @@ __global__ __launch_bounds__(256) void qgemm_split_reduce(const float *__restric
           b += v[z][1];
         }
     }
-    *(u32x4 *)&out[8 * i] = u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
-                                  pack_bf16x2(b[2], b[3])};
+    *(u32x4 *)dst = u32x4{pack_bf16x2(a[0], a[1]), pack_bf16x2(a[2], a[3]), pack_bf16x2(b[0], b[1]),
+                          pack_bf16x2(b[2], b[3])};
   }
+}
+
+SplitOut split_out(uint16_t *out, int64_t ncols) {
+  SplitOut so{};
+  so.count = 1;
+  so.col0[0] = 0;
+  so.ncols[0] = ncols;
+  so.out[0] = out;
+  return so;
 }
 
 // ---------------------------------------------------------------------------
@@ -1376,7 +1406,7 @@ hipError_t launch_qgemm_set(bool trans_w, const QgemmSet &set, int64_t M, const 
       uint16_t *out = trans_w ? gx : s.m[0].out;
       int64_t blocks = (M * Ncols / 8 + 255) / 256;
       if (blocks > 2048) blocks = 2048;
-      qgemm_split_reduce<<<(unsigned)blocks, 256, 0, st>>>(pz, sp.splits, M, Ncols, out);
+      qgemm_split_reduce<<<(unsigned)blocks, 256, 0, st>>>(pz, sp.splits, M, Ncols, split_out(out, Ncols));
     }
     return hipGetLastError();
   }
@@ -1385,12 +1415,16 @@ hipError_t launch_qgemm_set(bool trans_w, const QgemmSet &set, int64_t M, const 
     tiles = Tiles::kFull;
   else if (cols_k_full && kc_max < ((int64_t)1 << 22))
     tiles = Tiles::kFullClamped;
-  // A split contracts the same range of steps of every member, so a set splits
-  // only in grad_x and only when its members share n_out.
+  // A split contracts the same range of steps of every member: grad_x of a set
+  // splits only when its members share n_out; a forward set (members share
+  // n_in) when every member's columns are whole tiles, its partial tiles side
+  // by side.
   bool same_kc = true;
   for (int i = 1; i < s.count; ++i) same_kc = same_kc && s.m[i].w.n_out == s.m[0].w.n_out;
+  const int64_t pcols = trans_w || s.count == 1 ? Ncols : ytiles * QBN;
+  s.part_cols = pcols;
   QgemmSplit sp{1, 0};
-  if (part && (s.count == 1 || (trans_w && same_kc))) sp = qgemm_split(M, Ncols, kc_max);
+  if (part && (s.count == 1 || (trans_w && same_kc) || (!trans_w && cols_k_full))) sp = qgemm_split(M, pcols, kc_max);
   float *pz = sp.splits > 1 ? part : nullptr;
   const dim3 g((unsigned)((M + QBM - 1) / QBM), (unsigned)ytiles, (unsigned)sp.splits);
   if (!trans_w) {  // the forward never takes a dropout mask
@@ -1410,10 +1444,18 @@ hipError_t launch_qgemm_set(bool trans_w, const QgemmSet &set, int64_t M, const 
       launch_ws<true, false, false>(tiles, g, st, s, M, x, la, lb, r, scale, gx, cb, nullptr, pz, sp.steps);
   }
   if (pz) {
-    uint16_t *out = trans_w ? gx : s.m[0].out;
-    int64_t blocks = (M * Ncols / 8 + 255) / 256;
+    SplitOut so = split_out(trans_w ? gx : s.m[0].out, Ncols);
+    if (!trans_w && s.count > 1) {
+      so.count = s.count;
+      for (int i = 0; i < s.count; ++i) {
+        so.col0[i] = s.m[i].tile0 * QBN;
+        so.ncols[i] = s.m[i].w.n_out;
+        so.out[i] = s.m[i].out;
+      }
+    }
+    int64_t blocks = (M * pcols / 8 + 255) / 256;
     if (blocks > 2048) blocks = 2048;
-    qgemm_split_reduce<<<(unsigned)blocks, 256, 0, st>>>(pz, sp.splits, M, Ncols, out);
+    qgemm_split_reduce<<<(unsigned)blocks, 256, 0, st>>>(pz, sp.splits, M, pcols, so);
   }
   return hipGetLastError();
 }

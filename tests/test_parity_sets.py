@@ -60,7 +60,8 @@ def _check(cases, need_u=True, double_quant=True):
 @pytest.mark.parametrize("n_outs,n_in,T,r", [((320, 192, 256), 320, 300, 24), ((77, 130, 64), 192, 259, 5),
                                              ((1000, 640), 640, 513, 64), ((128, 128, 128, 128), 128, 17, 16),
                                              ((64, 128), 128, 40, 4), ((256, 128), 256, 256, 96),
-                                             ((512, 512, 512), 1024, 40, 16), ((1000, 700, 1300), 896, 2050, 24)])
+                                             ((512, 512, 512), 1024, 40, 16), ((1000, 700, 1300), 896, 2050, 24),
+                                             ((1024, 512, 768), 2048, 300, 32)])
 def test_sets_against_the_oracle(n_outs, n_in, T, r):
     announce(f"set n_outs={n_outs} n_in={n_in} T={T} r={r}")
     cases = _members(n_outs, n_in, T, r, seed=T + r)
@@ -140,10 +141,14 @@ def test_set_with_fp32_constants():
     _check(_members((256, 320), 256, 130, 8, seed=5), double_quant=False)
 
 
-def test_one_member_set_equals_the_single_linear_calls():
+@pytest.mark.parametrize("n_out,n_in,T,r", [(300, 320, 200, 24), (2048, 2048, 256, 64), (1024, 4096, 64, 16)])
+def test_one_member_set_equals_the_single_linear_calls(n_out, n_in, T, r):
+    """A one-member set runs the single linear's kernels, splits included (the second shape splits
+    the contraction of both directions on 256-row tiles, the third on the few-token tiles), so
+    every output is bit-identical."""
     torch = __import__("torch")
-    announce("set of one member vs single linear, 300x320 T=200 r=24")
-    (c,) = _members((300,), 320, 200, 24, seed=11)
+    announce(f"set of one member vs single linear, {n_out}x{n_in} T={T} r={r}")
+    (c,) = _members((n_out,), n_in, T, r, seed=11 + T)
     q = qlora.quantize(dev_f32(c.w))
     x, a, b, dy = dev_bf16(c.x), dev_bf16(c.a), dev_bf16(c.b), dev_bf16(c.dy)
     y0, u0 = qlora.linear_fwd(x, q, a, b, c.scale)
