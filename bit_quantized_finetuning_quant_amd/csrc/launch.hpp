@@ -217,7 +217,7 @@ struct SetPlan {
   int64_t T, K;
   int r, count;
   int64_t N[kMaxSetMembers];
-  size_t off_u, off_v, off_part, off_um, off_qpart, total;  // off_qpart: 0 when grad_x never splits
+  size_t off_u, off_v, off_part, off_um, off_qpart, total;  // off_qpart: 0 when neither direction splits
 };
 SetPlan plan_linear_set(int64_t T, int count, const int64_t *N, int64_t K, int r);
 hipError_t launch_linear_set_fwd(const SetPlan &p, const uint16_t *x, const QWeight *w, const uint16_t *A_set,
