@@ -143,7 +143,9 @@ struct QgemmSplit {
   int splits;
   int64_t steps;
 };
-QgemmSplit qgemm_split(int64_t M, int64_t Ncols, int64_t Kc);
+QgemmSplit qgemm_split(int64_t M, int64_t Ncols, int64_t Kc, double *cost = nullptr);
+// fp32 scratch of a set's grad_x run member by member at a few tokens (0: never)
+size_t qgemm_set_dx_member_floats(int64_t M, int count, const int64_t *n_out, int64_t n_in);
 size_t qgemm_split_floats(int64_t M, int64_t Ncols, int64_t Kc);
 
 // Adapter products of a projection set (lora.hip); each product has its own

@@ -244,8 +244,12 @@ SetPlan plan_linear_set(int64_t T, int count, const int64_t *N, int64_t K, int r
     tiles_n = tiles_n && (count == 1 || N[i] % 128 == 0);
     n_all += N[i];
   }
-  const size_t qsplit = std::max(same_n ? qgemm_split_floats(T, K, N[0]) : 0,
-                                 tiles_n ? qgemm_split_floats(T, n_all, K) : 0);
+  size_t qsplit = std::max(same_n ? qgemm_split_floats(T, K, N[0]) : 0,
+                           tiles_n ? qgemm_split_floats(T, n_all, K) : 0);
+  // at a few tokens a set may run member by member on the few-token tiles
+  if (tiles_n)
+    for (int i = 0; i < count; ++i) qsplit = std::max(qsplit, qgemm_split_floats(T, N[i], K));
+  if (T > kGemvMaxT && count > 1) qsplit = std::max(qsplit, qgemm_set_dx_member_floats(T, count, N, K));
   if (qsplit) {
     p.off_qpart = off;
     off += align256(qsplit * 4);

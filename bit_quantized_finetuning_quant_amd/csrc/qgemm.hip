@@ -959,8 +959,6 @@ __global__ __launch_bounds__(512) void qgemm_ws(QgemmSet set, int64_t M, const u
   }
 }
 
-// The splits of a grid: sum over the splits, in split order, rounded to bf16
-// once (8 columns per thread; Ncols is a multiple of QBN here).
 // The outputs of a split launch: one, or a forward set's members, whose
 // columns [col0[i], col0[i] + ncols[i]) of the partial tiles go to out[i]
 // [M x ncols[i]].
@@ -970,6 +968,9 @@ struct SplitOut {
   uint16_t *out[kMaxSetMembers];
 };
 
+// The splits of a grid: sum over the splits, in split order, rounded to bf16
+// once (8 columns per thread; Ncols, the partial tiles' width, is a multiple
+// of QBN here).
 __global__ __launch_bounds__(256) void qgemm_split_reduce(const float *__restrict__ part, int S, int64_t M,
                                                           int64_t Ncols, SplitOut so) {
   const int64_t n8 = M * Ncols / 8, zs = M * Ncols / 4;  // zs: one split in float4 units
@@ -1305,8 +1306,9 @@ void launch_ws(Tiles tiles, dim3 g, hipStream_t st, const QgemmSet &s, int64_t M
 // fp32 partials (at about 4 GB per ms), with at least 4 steps per split.  Only
 // shapes whose tiles are full in columns and contraction split, so every
 // workgroup runs the full-tile pipeline.
-QgemmSplit qgemm_split(int64_t M, int64_t Ncols, int64_t Kc) {
+QgemmSplit qgemm_split(int64_t M, int64_t Ncols, int64_t Kc, double *cost) {
   QgemmSplit sp{1, 0};
+  if (cost) *cost = 1e30;
   if (M < 1 || Ncols % QBN != 0 || Kc % QBK != 0) return sp;
   const int64_t tiles = (M + QBM - 1) / QBM * (Ncols / QBN), nk = Kc / QBK;
   double best = 0.0;
@@ -1321,6 +1323,7 @@ QgemmSplit qgemm_split(int64_t M, int64_t Ncols, int64_t Kc) {
       sp = S > 1 ? QgemmSplit{(int)S, steps} : QgemmSplit{1, 0};
     }
   }
+  if (cost) *cost = best;
   return sp;
 }
 
@@ -1334,8 +1337,9 @@ constexpr int sm_rows(int64_t M) { return M <= 64 ? 64 : 128; }
 // about 0.9 us a step, plus the fp32 partials written and read back at about
 // 2 bytes per ps and a few us for the reduction's launch (fitted to split
 // sweeps at 4096 x 4096, 11008 x 4096 and 22016 x 8192 with 16 and 64 tokens).
-QgemmSplit qgemm_sm_split(int64_t M, int64_t Ncols, int64_t Kc) {
+QgemmSplit qgemm_sm_split(int64_t M, int64_t Ncols, int64_t Kc, double *cost = nullptr) {
   QgemmSplit sp{1, 0};
+  if (cost) *cost = 1e30;
   if (M < 1 || Ncols % QBN != 0 || Kc % QBK != 0) return sp;
   const int rows = sm_rows(M);
   const int64_t tiles = (M + rows - 1) / rows * (Ncols / QBN), nk = Kc / QBK;
@@ -1351,6 +1355,7 @@ QgemmSplit qgemm_sm_split(int64_t M, int64_t Ncols, int64_t Kc) {
       sp = S > 1 ? QgemmSplit{(int)S, steps} : QgemmSplit{1, 0};
     }
   }
+  if (cost) *cost = best;
   return sp;
 }
 
@@ -1360,6 +1365,18 @@ size_t qgemm_split_floats(int64_t M, int64_t Ncols, int64_t Kc) {
   if (M <= kSmMaxRows) {
     const QgemmSplit ss = qgemm_sm_split(M, Ncols, Kc);
     if (ss.splits > 1) f = std::max(f, (size_t)ss.splits * M * Ncols);
+  }
+  return f;
+}
+
+// grad_x of a set at a few tokens, member by member: the fp32 partial tiles of
+// every member's splits (at least one each), side by side along z.
+size_t qgemm_set_dx_member_floats(int64_t M, int count, const int64_t *n_out, int64_t n_in) {
+  if (M > kSmMaxRows || n_in % QBN != 0) return 0;
+  size_t f = 0;
+  for (int i = 0; i < count; ++i) {
+    if (n_out[i] % QBK != 0) return 0;
+    f += (size_t)std::max(1, qgemm_sm_split(M, n_in, n_out[i]).splits) * M * n_in;
   }
   return f;
 }
@@ -1409,6 +1426,73 @@ hipError_t launch_qgemm_set(bool trans_w, const QgemmSet &set, int64_t M, const 
       qgemm_split_reduce<<<(unsigned)blocks, 256, 0, st>>>(pz, sp.splits, M, Ncols, split_out(out, Ncols));
     }
     return hipGetLastError();
+  }
+  // grad_x of a set at a few tokens: each member on the few-token tiles, every
+  // split of every member writing its fp32 partial tile (a member's first
+  // split adds its share s v_i A_i of the adapter term), and one reduction over
+  // all of them; against one launch of 256-row tiles contracting over every
+  // member, by the split cost models (about 5 us per extra launch).
+  if (trans_w && s.count > 1 && cols_k_full && M <= kSmMaxRows && part && !keep) {
+    int64_t kc_all = 0;
+    for (int i = 0; i < s.count; ++i) kc_all += s.m[i].w.n_out;
+    double c_set = 0.0, c_members = 5.0 * (s.count - 1);
+    qgemm_split(M, Ncols, kc_all, &c_set);
+    QgemmSplit spm[kMaxSetMembers];
+    for (int i = 0; i < s.count; ++i) {
+      double c = 0.0;
+      spm[i] = qgemm_sm_split(M, Ncols, s.m[i].w.n_out, &c);
+      c_members += c;
+    }
+    if (c_members < c_set) {
+      const int rows = sm_rows(M), rm = r / s.count;  // every member's rank
+      int64_t z = 0;
+      for (int i = 0; i < s.count; ++i) {
+        QgemmSet one{};
+        one.count = 1;
+        one.ld_la = s.ld_la;
+        one.m[0] = s.m[i];
+        one.part_cols = Ncols;
+        const int S = spm[i].splits;
+        const int64_t steps = S > 1 ? spm[i].steps : s.m[i].w.n_out / QBK;
+        const dim3 g((unsigned)((M + rows - 1) / rows), (unsigned)(Ncols / QBN), (unsigned)S);
+        const uint16_t *la_i = la + (int64_t)i * rm, *lb_i = lb + (int64_t)i * rm * Ncols;
+        float *pz = part + z * M * Ncols;
+        if (rows == 64)
+          launch_sm<64>(true, dq, g, st, one, M, x, la_i, lb_i, rm, scale, gx, cb, pz, steps);
+        else
+          launch_sm<128>(true, dq, g, st, one, M, x, la_i, lb_i, rm, scale, gx, cb, pz, steps);
+        z += S;
+      }
+      int64_t blocks = (M * Ncols / 8 + 255) / 256;
+      if (blocks > 2048) blocks = 2048;
+      qgemm_split_reduce<<<(unsigned)blocks, 256, 0, st>>>(part, (int)z, M, Ncols, split_out(gx, Ncols));
+      return hipGetLastError();
+    }
+  }
+  // A forward set at a few tokens: each member on the few-token tiles (one
+  // launch and reduction per member, about 5 us each) can beat one launch of
+  // all the members on 256-row tiles; the split cost models decide.
+  if (!trans_w && s.count > 1 && cols_k_full && M <= kSmMaxRows && part) {
+    double c_set = 0.0, c_members = 5.0 * (s.count - 1);
+    qgemm_split(M, ytiles * QBN, kc_max, &c_set);
+    for (int i = 0; i < s.count; ++i) {
+      double c = 0.0;
+      qgemm_sm_split(M, s.m[i].w.n_out, kc_max, &c);
+      c_members += c;
+    }
+    if (c_members < c_set) {
+      for (int i = 0; i < s.count; ++i) {
+        QgemmSet one{};
+        one.count = 1;
+        one.ld_la = s.ld_la;
+        one.m[0] = s.m[i];
+        one.m[0].tile0 = 0;
+        const hipError_t e =
+            launch_qgemm_set(false, one, M, x, la + (int64_t)i * r, lb, r, scale, gx, cb, st, nullptr, part);
+        if (e != hipSuccess) return e;
+      }
+      return hipSuccess;
+    }
   }
   Tiles tiles = Tiles::kAny;
   if (cols_k_full && M % QBM == 0)

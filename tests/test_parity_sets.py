@@ -160,6 +160,18 @@ def test_one_member_set_equals_the_single_linear_calls(n_out, n_in, T, r):
         assert np.array_equal(host(t0), host(t1))
 
 
+@pytest.mark.parametrize("n_outs,n_in,T,r", [((4096, 4096), 8192, 16, 32), ((4096, 8192), 4096, 40, 24)])
+def test_few_token_set_member_by_member(n_outs, n_in, T, r):
+    """Sets at a few tokens whose members are large enough that the split cost models run them
+    member by member on the few-token tiles: the first shape in both directions (forward: each
+    member with its own split and reduction, the adapter term from its columns of u_set; grad_x:
+    every member's splits as fp32 partial tiles, its share of s v_set A_set in its first split,
+    one reduction over all of them), the second in the forward only (members of different widths,
+    40 tokens: clamped rows, rank 24); against the oracle."""
+    announce(f"set {n_outs} x {n_in} T={T} r={r} (member by member)")
+    _check(_members(n_outs, n_in, T, r, seed=41 + T))
+
+
 def test_7b_attention_projections_T2048():
     """q, k, v of LLaMA-7B (3 x 4096 x 4096, r = 64, 2048 tokens) as one set, in full."""
     announce("set 7b q/k/v T=2048 full")
