@@ -1,7 +1,8 @@
-// Few-token (T <= 4) QLoRA linear layer for gfx950.  With so few tokens the
-// work per weight element is a handful of flops, so reading the 4-bit weight
-// from HBM is the bound: every weight byte is read once, decoded once and used
-// for all T tokens with vector ALU dot products.
+// Few-token QLoRA linear layer for gfx950 (forward T <= 16, backward T <= 4).
+// With so few tokens the work per weight element is a handful of flops, so
+// reading the 4-bit weight from HBM is the bound: every weight byte is read
+// once, decoded once and used for all T tokens (the forward's matrix tile pads
+// the tokens to 16; the backward's vector ALU dot products cost per token).
 //
 // Method ("qlora" encyclopedia entry, tonho.wtf, section "a ideia"): the weight
 // is dequantized to BFloat16 as it is used; gradients reach only the LoRA
@@ -304,7 +305,7 @@ __global__ __launch_bounds__(256) void gemv_fwd_finish(const float *__restrict__
                                                        GemvFwdSet set, int r, int ld_u, float scale,
                                                        float u_scale, int64_t Ntot, uint16_t *__restrict__ u_out) {
   __shared__ float us[T * 256];
-  __shared__ float tmp[1024];
+  __shared__ float tmp[T * 256 > 1024 ? T * 256 : 1024];  // E S <= max(E, 256) entries, E = T r <= 256 T
   __shared__ float red[4][T][64];
   const int tid = threadIdx.x;
   const int q = __builtin_amdgcn_readfirstlane(tid >> 6), c = tid & 63;
@@ -321,7 +322,7 @@ __global__ __launch_bounds__(256) void gemv_fwd_finish(const float *__restrict__
   const int nch = r / 8;
   const uint16_t *brow = B + nc * r;
   // first batch of this thread's partials and B chunks
-  constexpr int kYB = kFinBatch / 2;
+  constexpr int kYB = T <= 4 ? kFinBatch / 2 : (T <= 8 ? 4 : 2);  // span partials a thread holds per batch
   float yp[kYB][T];
   u32x4 b[8];
   if (N > 0) {
@@ -931,6 +932,7 @@ hipError_t gemv_bwd_set_impl(const uint16_t *const *dy, const uint16_t *x, const
 }  // namespace
 
 bool gemv_applies(int64_t T, int64_t K) { return T >= 1 && T <= kGemvMaxT && K % 64 == 0; }
+bool gemv_fwd_applies(int64_t T, int64_t K) { return T >= 1 && T <= kGemvFwdMaxT && K % 64 == 0; }
 
 bool gemv_set_fusable(const int64_t *N, int count) {
   for (int i = 0; i + 1 < count; ++i)
@@ -946,6 +948,18 @@ hipError_t launch_gemv_fwd_set(int64_t T, const uint16_t *x, const QWeight *w, i
     case 2: return gemv_fwd_set_impl<2>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
     case 3: return gemv_fwd_set_impl<3>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
     case 4: return gemv_fwd_set_impl<4>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 5: return gemv_fwd_set_impl<5>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 6: return gemv_fwd_set_impl<6>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 7: return gemv_fwd_set_impl<7>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 8: return gemv_fwd_set_impl<8>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 9: return gemv_fwd_set_impl<9>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 10: return gemv_fwd_set_impl<10>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 11: return gemv_fwd_set_impl<11>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 12: return gemv_fwd_set_impl<12>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 13: return gemv_fwd_set_impl<13>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 14: return gemv_fwd_set_impl<14>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 15: return gemv_fwd_set_impl<15>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 16: return gemv_fwd_set_impl<16>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -953,16 +967,17 @@ hipError_t launch_gemv_fwd_set(int64_t T, const uint16_t *x, const QWeight *w, i
 size_t gemv_set_part_floats(int64_t T, const int64_t *N, int count, int64_t K, int r) {
   GemvBwdSet set{};
   set.count = count;
-  int64_t ntot = 0;
-  for (int i = 0; i < count; ++i) {
-    set.w[i].n_out = N[i];
-    ntot += N[i];
-  }
+  for (int i = 0; i < count; ++i) set.w[i].n_out = N[i];
   const BwdSplit b = bwd_split(set, K, r);
-  const GemvGeometry gf = geometry(ntot, K, count * r);
-  const size_t fwd = (size_t)(gf.fspans * T * (ntot + (int64_t)count * r));
   const size_t bwd = (size_t)(b.chunks * T * K + b.parts * T * r);
-  return std::max(fwd, bwd);
+  return std::max(gemv_set_fwd_part_floats(T, N, count, K, r), bwd);
+}
+
+size_t gemv_set_fwd_part_floats(int64_t T, const int64_t *N, int count, int64_t K, int r) {
+  int64_t ntot = 0;
+  for (int i = 0; i < count; ++i) ntot += N[i];
+  const GemvGeometry gf = geometry(ntot, K, count * r);
+  return (size_t)(gf.fspans * T * (ntot + (int64_t)count * r));
 }
 
 hipError_t launch_gemv_bwd_set(int64_t T, const uint16_t *const *dy, const uint16_t *x, const QWeight *w, int count,
@@ -980,9 +995,13 @@ hipError_t launch_gemv_bwd_set(int64_t T, const uint16_t *const *dy, const uint1
 
 size_t gemv_part_floats(int64_t T, int64_t N, int64_t K, int r) {
   const GemvGeometry g = geometry(N, K, r);
-  const size_t fwd = (size_t)(g.fspans * T * (N + r));
   const size_t bwd = (size_t)(g.chunks * T * K + g.bparts * T * r);
-  return std::max(fwd, bwd);
+  return std::max(gemv_fwd_part_floats(T, N, K, r), bwd);
+}
+
+size_t gemv_fwd_part_floats(int64_t T, int64_t N, int64_t K, int r) {
+  const GemvGeometry g = geometry(N, K, r);
+  return (size_t)(g.fspans * T * (N + r));
 }
 
 hipError_t launch_gemv_fwd(int64_t T, const uint16_t *x, const uint16_t *xa, const QWeight &w, const uint16_t *A,
@@ -993,6 +1012,18 @@ hipError_t launch_gemv_fwd(int64_t T, const uint16_t *x, const uint16_t *xa, con
     case 2: return gemv_fwd_impl<2>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
     case 3: return gemv_fwd_impl<3>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
     case 4: return gemv_fwd_impl<4>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 5: return gemv_fwd_impl<5>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 6: return gemv_fwd_impl<6>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 7: return gemv_fwd_impl<7>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 8: return gemv_fwd_impl<8>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 9: return gemv_fwd_impl<9>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 10: return gemv_fwd_impl<10>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 11: return gemv_fwd_impl<11>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 12: return gemv_fwd_impl<12>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 13: return gemv_fwd_impl<13>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 14: return gemv_fwd_impl<14>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 15: return gemv_fwd_impl<15>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 16: return gemv_fwd_impl<16>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
     default: return hipErrorInvalidValue;
   }
 }

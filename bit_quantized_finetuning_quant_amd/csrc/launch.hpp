@@ -45,12 +45,17 @@ struct DequantSet {
 };
 hipError_t launch_dequantize_set(const DequantSet &set, const Codebook &cb, hipStream_t st);
 
-// Few-token path (gemv.hip): 1 <= T <= kGemvMaxT.  `part` is fp32 scratch of
-// gemv_part_floats(T, N, K, r) floats.  launch_gemv_fwd with y == nullptr only
-// computes u; launch_gemv_bwd with grad_x == nullptr skips the weight pass.
+// Few-token path (gemv.hip): the forward for 1 <= T <= kGemvFwdMaxT (its
+// matrix tile pads the tokens to 16), the backward for 1 <= T <= kGemvMaxT.
+// `part` is fp32 scratch of gemv_part_floats(T, N, K, r) floats, or
+// gemv_fwd_part_floats for a forward alone.  launch_gemv_fwd with y == nullptr
+// only computes u; launch_gemv_bwd with grad_x == nullptr skips the weight pass.
 constexpr int64_t kGemvMaxT = 4;
-bool gemv_applies(int64_t T, int64_t K);
+constexpr int64_t kGemvFwdMaxT = 16;
+bool gemv_applies(int64_t T, int64_t K);      // both directions
+bool gemv_fwd_applies(int64_t T, int64_t K);  // the forward
 size_t gemv_part_floats(int64_t T, int64_t N, int64_t K, int r);
+size_t gemv_fwd_part_floats(int64_t T, int64_t N, int64_t K, int r);
 // The adapter input xa (x, or the dropped-out x) feeds u = u_scale * xa A^T
 // and grad_A = scale_ax * v^T xa; scale_ax also scales the adapter term of
 // grad_x, which `keep` (nullptr: no dropout) masks element by element.
@@ -66,8 +71,10 @@ hipError_t launch_gemv_fwd_set(int64_t T, const uint16_t *x, const QWeight *w, i
                                float *part, const Codebook &cb, hipStream_t st);
 // Few-token backward of a projection set in one pass over every member's rows: grad_x summed over
 // the members, grad_A_set [count r x K], grad_B[i]; u_set and v [T x count r].  `part` holds
-// gemv_set_part_floats(T, n_out, count, K, r) floats (which also covers launch_gemv_fwd_set).
+// gemv_set_part_floats(T, n_out, count, K, r) floats (which also covers launch_gemv_fwd_set;
+// gemv_set_fwd_part_floats covers it alone).
 size_t gemv_set_part_floats(int64_t T, const int64_t *N, int count, int64_t K, int r);
+size_t gemv_set_fwd_part_floats(int64_t T, const int64_t *N, int count, int64_t K, int r);
 hipError_t launch_gemv_bwd_set(int64_t T, const uint16_t *const *dy, const uint16_t *x, const QWeight *w, int count,
                                const uint16_t *A_set, const uint16_t *const *B, int r, float scale,
                                const uint16_t *u_set, uint16_t *grad_x, float *grad_A_set, float *const *grad_B,
@@ -213,8 +220,9 @@ hipError_t launch_copy_rows(const uint16_t *src, int64_t ld_src, uint16_t *dst, 
 
 // Projection sets (linear.hip): members share x [T x K] and the adapter
 // rank r; A_set [count r x K] holds the members' A back to back, u_set and
-// v_set are [T x count r].  For T <= kGemvMaxT the few-token kernels run the
-// set (a [T x r] u block in the workspace for the member-by-member forward).
+// v_set are [T x count r].  The few-token kernels run the set's forward for
+// T <= kGemvFwdMaxT and its backward for T <= kGemvMaxT (a [T x r] u block in
+// the workspace for a member-by-member forward).
 struct SetPlan {
   int64_t T, K;
   int r, count;

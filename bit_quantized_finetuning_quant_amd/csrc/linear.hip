@@ -97,7 +97,10 @@ LinearPlan plan_linear(int64_t T, int64_t N, int64_t K, int r, bool dropout) {
   for (const auto &sh : shapes) part = std::max(part, lora_part_floats(sh[0], sh[1], sh[2]));
   // grad_A and grad_B are formed together
   part = std::max(part, lora_part_floats(r, K, T) + lora_part_floats(N, r, T));
-  if (gemv_applies(T, K)) part = std::max(part, gemv_part_floats(T, N, K, r));
+  if (gemv_applies(T, K))
+    part = std::max(part, gemv_part_floats(T, N, K, r));
+  else if (gemv_fwd_applies(T, K))  // the forward on the few-token kernels, the backward on the GEMMs
+    part = std::max(part, gemv_fwd_part_floats(T, N, K, r));
   size_t off = 0;
   p.off_status = off;  // status word (never written by the linear calls)
   off = 256;
@@ -149,7 +152,7 @@ hipError_t launch_linear_fwd(const LinearPlan &p, const uint16_t *x, const QWeig
   float *part = (float *)(ws + p.off_part);
   const AdapterInput ai = adapter_input(p, x, ws, d, st);
   if (ai.err != hipSuccess) return ai.err;
-  if (gemv_applies(p.T, p.K))
+  if (gemv_fwd_applies(p.T, p.K))
     return launch_gemv_fwd(p.T, x, ai.xa, w, A, B, p.r, scale, ai.inv_keep, y, u, part, cb, st);
   // u = bf16((1 / (1 - p)) xa A^T): the factor is exactly 1 without dropout
   hipError_t e = launch_lora(LoraKind::kU, ai.xa, p.K, A, p.K, p.T, p.r, p.K, ai.inv_keep, u, part, st);
@@ -228,6 +231,12 @@ SetPlan plan_linear_set(int64_t T, int count, const int64_t *N, int64_t K, int r
     off += align256(part * 4);
     p.off_um = off;
     off += align256((size_t)T * r * 2);
+  } else if (T <= kGemvFwdMaxT) {  // few-token forward passes, the adapter products of the backward
+    size_t part = std::max(lora_set_part_floats(T, count, N, K, r), gemv_set_fwd_part_floats(T, N, count, K, r));
+    for (int i = 0; i < count; ++i) part = std::max(part, gemv_fwd_part_floats(T, N[i], K, r));
+    off += align256(part * 4);
+    p.off_um = off;
+    off += align256((size_t)T * r * 2);
   } else {
     off += align256(lora_set_part_floats(T, count, N, K, r) * 4);
     p.off_um = off;
@@ -258,11 +267,11 @@ SetPlan plan_linear_set(int64_t T, int count, const int64_t *N, int64_t K, int r
   return p;
 }
 
-// Few-token sets.  The forward runs as one pass over the members' concatenated
-// rows when every member but the last has a multiple of 64 rows, else member by
-// member (u moves between the set's [T x count r] layout and one [T x r]
-// block); the backward is one pass over every member's rows, which sums grad_x
-// over the members in its fp32 partials.
+// Few-token sets.  The forward (T <= kGemvFwdMaxT) runs as one pass over the
+// members' concatenated rows when every member but the last has a multiple of
+// 64 rows, else member by member (u moves between the set's [T x count r]
+// layout and one [T x r] block); the backward (T <= kGemvMaxT) is one pass over
+// every member's rows, which sums grad_x over the members in its fp32 partials.
 static hipError_t set_fwd_few(const SetPlan &p, const uint16_t *x, const QWeight *w, const uint16_t *A_set,
                               const uint16_t *const *B, float scale, uint16_t *const *y, uint16_t *u, char *ws,
                               const Codebook &cb, hipStream_t st) {
@@ -303,7 +312,7 @@ hipError_t launch_linear_set_fwd(const SetPlan &p, const uint16_t *x, const QWei
                                  const uint16_t *const *B, float scale, uint16_t *const *y, uint16_t *u_out, char *ws,
                                  const Codebook &cb, hipStream_t st) {
   uint16_t *u = u_out ? u_out : (uint16_t *)(ws + p.off_u);
-  if (p.T <= kGemvMaxT) return set_fwd_few(p, x, w, A_set, B, scale, y, u, ws, cb, st);
+  if (gemv_fwd_applies(p.T, p.K)) return set_fwd_few(p, x, w, A_set, B, scale, y, u, ws, cb, st);
   float *part = (float *)(ws + p.off_part);
   const int64_t rt = (int64_t)p.count * p.r;
   // u_set = x A_set^T: one product for every member's u

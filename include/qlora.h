@@ -228,11 +228,12 @@ qlora_status qlora_linear_bwd(const uint16_t *dy, const uint16_t *x, int64_t T,
  * v_set [T x count r] the members' u / v side by side (member i: columns
  * i r ..).  B[i] [n_out_i x r], y[i] [T x n_out_i], dy[i] [T x n_out_i] and
  * grad_B[i] [n_out_i x r] are arrays of count device pointers; grad_x is the
- * gradient of x summed over the members (NULL skips it).  For T <= 4 the few-
- * token kernels run the forward as one pass over the members' concatenated
- * rows when every member but the last has a multiple of 64 rows (else member
- * by member), and the backward as one pass over every member's rows (grad_x
- * summed over the members in fp32, rounded to bf16 once); same layouts.  No
+ * gradient of x summed over the members (NULL skips it).  The few-token
+ * kernels run the forward for T <= 16 as one pass over the members'
+ * concatenated rows when every member but the last has a multiple of 64 rows
+ * (else member by member), and the backward for T <= 4 as one pass over every
+ * member's rows (grad_x summed over the members in fp32, rounded to bf16
+ * once); same layouts.  No
  * dropout here: each adapter draws its own mask, so sets with dropout go per
  * linear.                                                                   */
 size_t qlora_linear_set_workspace_bytes(int64_t T, int count, const int64_t *n_out, int64_t n_in, int r);
@@ -330,7 +331,7 @@ qlora_status qlora_adamw_step(float *param, uint16_t *param_bf16, const float *g
 enum {
   QLORA_TIMED_QGEMM_FWD = 0, /* dequant-fused GEMM, forward: x W_hat^T (+ LoRA)       */
   QLORA_TIMED_QGEMM_DX = 1,  /* dequant-fused GEMM, grad_x: dy W_hat (+ LoRA)         */
-  QLORA_TIMED_GEMV_FWD = 2,  /* few-token forward, weight pass (T <= 4)                */
+  QLORA_TIMED_GEMV_FWD = 2,  /* few-token forward, weight pass (T <= 16)               */
   QLORA_TIMED_GEMV_BWD = 3,  /* few-token backward, weight and adapter pass (T <= 4)   */
   QLORA_TIMED_ADAMW = 4,     /* adapter AdamW update, whole 4096-element tiles          */
   QLORA_TIMED_KINDS = 5

@@ -124,8 +124,8 @@ def test_adapter_products_at_long_token_counts(shape):
 @pytest.mark.parametrize("T", [1, 2, 4, 8, 16, 32, 64, 128, 256])
 def test_7b_projection_every_token_count_of_the_sweep(T):
     """The 7B projection (4096 x 4096, r = 64) at every token count the benchmark sweeps: the
-    few-token kernels up to 4 tokens, then the fused GEMM with clamped rows and split
-    contractions."""
+    few-token kernels up to 4 tokens (the forward up to 16), then the fused GEMM with clamped rows
+    and split contractions."""
     announce(f"linear 7b_attn T={T} (sweep)")
     case = workloads.custom_case(4096, 4096, T, 64, 16.0, seed=900)  # one weight; x, dy drawn per T
     _check_case(case, weight_key=("sweep", 900))
@@ -139,6 +139,19 @@ def test_few_token_path(shape):
     n_out, n_in, T, r = shape
     announce(f"linear few-token n_out={n_out} n_in={n_in} T={T} r={r}")
     case = workloads.custom_case(n_out, n_in, T, r, 16.0, seed=n_out + 3 * T)
+    _check_case(case)
+    _check_case(case, scale=1.5, need_u=False)
+
+
+@pytest.mark.parametrize("shape", [(300, 320, 5, 24), (77, 192, 6, 5), (64, 64, 16, 256), (1000, 11008, 9, 64),
+                                   (130, 2112, 12, 13), (515, 4160, 16, 64), (8, 64, 16, 1), (4096, 4096, 7, 64)])
+def test_few_token_forward_up_to_16_tokens(shape):
+    """From 5 to 16 tokens the forward runs the few-token kernels (their matrix tile pads the
+    tokens to 16) and the backward the fused GEMM: ragged row groups and spans, ranks 1 to 256 (the
+    largest T r the forward's reduction holds), against the oracle."""
+    n_out, n_in, T, r = shape
+    announce(f"linear few-token forward n_out={n_out} n_in={n_in} T={T} r={r}")
+    case = workloads.custom_case(n_out, n_in, T, r, 16.0, seed=n_out + 7 * T + r)
     _check_case(case)
     _check_case(case, scale=1.5, need_u=False)
 
@@ -158,12 +171,14 @@ def test_backward_without_grad_x(T):
     assert normwise_rel(host(gb), gb_ref) <= NORMWISE_TOL
 
 
-def test_one_hot_rows_return_decoded_weight_bit_exactly():
+@pytest.mark.parametrize("T", [40, 16])
+def test_one_hot_rows_return_decoded_weight_bit_exactly(T):
     """x rows one-hot with A = 0: y row t is column k_t of W_hat; dy rows one-hot with B = 0:
     grad_x row t is row n_t of W_hat.  A single product is exact in fp32, so this checks the
-    in-kernel decode and layout independently of summation order."""
-    announce("linear one-hot 384x320 T=40")
-    n_out, n_in, T, r = 384, 320, 40, 16
+    in-kernel decode and layout independently of summation order: at 40 tokens both directions on
+    the few-token tiles, at 16 the forward on the few-token kernels' matrix tile."""
+    announce(f"linear one-hot 384x320 T={T}")
+    n_out, n_in, r = 384, 320, 16
     rng = np.random.default_rng(7)
     w = (rng.standard_normal((n_out, n_in)) * 0.02).astype(np.float32)
     ks = rng.integers(0, n_in, T)
