@@ -291,24 +291,29 @@ __device__ __forceinline__ float strided_sum(const float *p, int64_t stride, int
   return s;
 }
 
-// Forward, pass 2: a workgroup per 64 output rows (N may be 0: u only).
-// u = bf16(sum of the span partials of u): with E = T r entries, slice sl of
-// S = 256 / E thread groups sums spans sl, sl + S, ... and the slices are
-// added in order.  Thread (q, c) = (tid / 64, tid % 64) owns row
-// n = 64 blockIdx.x + c and its quarter q of the rest: span partials q,
-// q + 4, ... and the 8-wide rank chunks q, q + 4, ... of s u B^T; the four
-// quarters are added in order.  Every load that does not need u is issued
-// before u is reduced, so that one memory round trip covers them.
-template <int T>
+// Forward, pass 2: a workgroup per 64 output rows (N may be 0: u only) and
+// per group of TG tokens (blockIdx.y: tokens TG blockIdx.y .. + TG - 1 of T;
+// one group for T <= 4, groups of 4 above).  u = bf16(sum of the span partials
+// of u): with E = TG r entries, slice sl of S = 256 / E thread groups sums
+// spans sl, sl + S, ... and the slices are added in order.  Thread (q, c) =
+// (tid / 64, tid % 64) owns row n = 64 blockIdx.x + c and its quarter q of the
+// rest: span partials q, q + 4, ... and the 8-wide rank chunks q, q + 4, ... of
+// s u B^T; the four quarters are added in order.  Every load that does not
+// need u is issued before u is reduced, so that one memory round trip covers
+// them.  Tokens of the last group past T read token T - 1 and are never stored.
+template <int TG>
 __global__ __launch_bounds__(256) void gemv_fwd_finish(const float *__restrict__ y_part,
                                                        const float *__restrict__ u_part, int64_t spans,
                                                        GemvFwdSet set, int r, int ld_u, float scale,
-                                                       float u_scale, int64_t Ntot, uint16_t *__restrict__ u_out) {
-  __shared__ float us[T * 256];
-  __shared__ float tmp[T * 256 > 1024 ? T * 256 : 1024];  // E S <= max(E, 256) entries, E = T r <= 256 T
-  __shared__ float red[4][T][64];
+                                                       float u_scale, int64_t Ntot, int T,
+                                                       uint16_t *__restrict__ u_out) {
+  __shared__ float us[TG * 256];
+  __shared__ float tmp[1024];  // E S <= max(E, 256) entries, E = TG r <= 1024
+  __shared__ float red[4][TG][64];
   const int tid = threadIdx.x;
   const int q = __builtin_amdgcn_readfirstlane(tid >> 6), c = tid & 63;
+  const int t0 = TG * (int)blockIdx.y;
+  auto tok = [&](int t) { return min(t0 + t, T - 1); };  // token of group position t (clamped)
   // this workgroup's member (Ntot = 0: u only, member 0) and its 64 rows
   const int m = Ntot > 0 ? fwd_member(set, blockIdx.x) : 0;
   const int64_t pl = (int64_t)blockIdx.x - set.block0[m];
@@ -322,27 +327,27 @@ __global__ __launch_bounds__(256) void gemv_fwd_finish(const float *__restrict__
   const int nch = r / 8;
   const uint16_t *brow = B + nc * r;
   // first batch of this thread's partials and B chunks
-  constexpr int kYB = T <= 4 ? kFinBatch / 2 : (T <= 8 ? 4 : 2);  // span partials a thread holds per batch
-  float yp[kYB][T];
+  constexpr int kYB = kFinBatch / 2;
+  float yp[kYB][TG];
   u32x4 b[8];
   if (N > 0) {
 #pragma unroll
     for (int i = 0; i < kYB; ++i)
 #pragma unroll
-      for (int t = 0; t < T; ++t) yp[i][t] = y_part[(min((int64_t)(q + 4 * i), spans - 1) * T + t) * Ntot + gc];
+      for (int t = 0; t < TG; ++t) yp[i][t] = y_part[(min((int64_t)(q + 4 * i), spans - 1) * T + tok(t)) * Ntot + gc];
     if (vec) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) b[i] = *(const u32x4 *)(brow + 8 * min(q + 4 * i, nch - 1));
     }
   }
-  const int E = T * r, S = E >= 256 ? 1 : 256 / E;
+  const int E = TG * r, S = E >= 256 ? 1 : 256 / E;
   const int64_t per = (spans + S - 1) / S;
   // the member's u columns m r .. m r + r - 1 of the [span][t][ld_u] partials
   const int64_t ustride = (int64_t)T * ld_u;
   for (int idx = tid; idx < E * S; idx += 256) {
     const int e = idx % E, sl = idx / E;
     const int64_t cnt = max((int64_t)0, min(per, (spans - sl + S - 1) / S));
-    tmp[idx] = strided_sum(u_part + sl * ustride + (int64_t)(e / r) * ld_u + m * r + e % r, (int64_t)S * ustride, cnt);
+    tmp[idx] = strided_sum(u_part + sl * ustride + (int64_t)tok(e / r) * ld_u + m * r + e % r, (int64_t)S * ustride, cnt);
   }
   __syncthreads();
   for (int e = tid; e < E; e += 256) {
@@ -350,23 +355,23 @@ __global__ __launch_bounds__(256) void gemv_fwd_finish(const float *__restrict__
     for (int sl = 0; sl < S; ++sl) s += tmp[sl * E + e];
     const uint16_t h = to_bf16(s * u_scale);
     us[e] = bf(h);
-    if (pl == 0) u_out[(e / r) * ld_u + m * r + e % r] = h;
+    if (pl == 0 && t0 + e / r < T) u_out[(t0 + e / r) * ld_u + m * r + e % r] = h;
   }
   if (N == 0) return;
   __syncthreads();
-  float ys[T], lora[T];
+  float ys[TG], lora[TG];
 #pragma unroll
-  for (int t = 0; t < T; ++t) ys[t] = lora[t] = 0.f;
+  for (int t = 0; t < TG; ++t) ys[t] = lora[t] = 0.f;
   for (int64_t s0 = q;; s0 += 4 * kYB) {
 #pragma unroll
     for (int i = 0; i < kYB; ++i)
 #pragma unroll
-      for (int t = 0; t < T; ++t) ys[t] += s0 + 4 * i < spans ? yp[i][t] : 0.f;
+      for (int t = 0; t < TG; ++t) ys[t] += s0 + 4 * i < spans ? yp[i][t] : 0.f;
     if (s0 + 4 * kYB >= spans) break;
 #pragma unroll
     for (int i = 0; i < kYB; ++i)
 #pragma unroll
-      for (int t = 0; t < T; ++t) yp[i][t] = y_part[(min(s0 + 4 * kYB + 4 * i, spans - 1) * T + t) * Ntot + gc];
+      for (int t = 0; t < TG; ++t) yp[i][t] = y_part[(min(s0 + 4 * kYB + 4 * i, spans - 1) * T + tok(t)) * Ntot + gc];
   }
   if (vec) {
     for (int c0 = q;; c0 += 32) {
@@ -377,7 +382,7 @@ __global__ __launch_bounds__(256) void gemv_fwd_finish(const float *__restrict__
 #pragma unroll
           for (int e = 0; e < 4; ++e)
 #pragma unroll
-            for (int t = 0; t < T; ++t) {
+            for (int t = 0; t < TG; ++t) {
               lora[t] = __builtin_fmaf(us[t * r + 8 * ch + 2 * e], bf16_lo(b[i][e]), lora[t]);
               lora[t] = __builtin_fmaf(us[t * r + 8 * ch + 2 * e + 1], bf16_hi(b[i][e]), lora[t]);
             }
@@ -397,17 +402,18 @@ __global__ __launch_bounds__(256) void gemv_fwd_finish(const float *__restrict__
         const int j = j0 + 4 * i;
         if (j < r) {
 #pragma unroll
-          for (int t = 0; t < T; ++t) lora[t] = __builtin_fmaf(us[t * r + j], bs[i], lora[t]);
+          for (int t = 0; t < TG; ++t) lora[t] = __builtin_fmaf(us[t * r + j], bs[i], lora[t]);
         }
       }
     }
   }
 #pragma unroll
-  for (int t = 0; t < T; ++t) red[q][t][c] = ys[t] + scale * lora[t];
+  for (int t = 0; t < TG; ++t) red[q][t][c] = ys[t] + scale * lora[t];
   __syncthreads();
   if (q == 0 && n < N) {
 #pragma unroll
-    for (int t = 0; t < T; ++t) y[t * N + n] = to_bf16(red[0][t][c] + red[1][t][c] + red[2][t][c] + red[3][t][c]);
+    for (int t = 0; t < TG; ++t)
+      if (t0 + t < T) y[(t0 + t) * N + n] = to_bf16(red[0][t][c] + red[1][t][c] + red[2][t][c] + red[3][t][c]);
   }
 }
 
@@ -787,7 +793,9 @@ hipError_t gemv_fwd_run(const uint16_t *x, const uint16_t *xa, const GemvFwdSet 
   if (timed) timing_end(st, tl);
   const int64_t out_rows = rows ? Ntot : 0;
   const unsigned fg = (unsigned)std::max<int64_t>(1, cdiv(out_rows, 64));
-  gemv_fwd_finish<T><<<fg, 256, 0, st>>>(y_part, u_part, g.fspans, set, r, r_total, scale, u_scale, out_rows, u);
+  constexpr int TG = T <= 4 ? T : 4;  // tokens per finishing workgroup
+  gemv_fwd_finish<TG><<<dim3(fg, (unsigned)((T + TG - 1) / TG)), 256, 0, st>>>(y_part, u_part, g.fspans, set, r, r_total,
+                                                                               scale, u_scale, out_rows, (int)T, u);
   return hipGetLastError();
 }
 
