@@ -939,7 +939,9 @@ hipError_t gemv_bwd_set_impl(const uint16_t *const *dy, const uint16_t *x, const
 
 }  // namespace
 
-bool gemv_applies(int64_t T, int64_t K) { return T >= 1 && T <= kGemvMaxT && K % 64 == 0; }
+bool gemv_bwd_applies(int64_t T, int64_t K, int count) {
+  return T >= 1 && T <= (count == 1 ? kGemvLinearBwdMaxT : kGemvMaxT) && K % 64 == 0;
+}
 bool gemv_fwd_applies(int64_t T, int64_t K) { return T >= 1 && T <= kGemvFwdMaxT && K % 64 == 0; }
 
 bool gemv_set_fusable(const int64_t *N, int count) {

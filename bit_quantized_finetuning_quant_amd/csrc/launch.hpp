@@ -46,14 +46,18 @@ struct DequantSet {
 hipError_t launch_dequantize_set(const DequantSet &set, const Codebook &cb, hipStream_t st);
 
 // Few-token path (gemv.hip): the forward for 1 <= T <= kGemvFwdMaxT (its
-// matrix tile pads the tokens to 16), the backward for 1 <= T <= kGemvMaxT.
-// `part` is fp32 scratch of gemv_part_floats(T, N, K, r) floats, or
-// gemv_fwd_part_floats for a forward alone.  launch_gemv_fwd with y == nullptr
-// only computes u; launch_gemv_bwd with grad_x == nullptr skips the weight pass.
+// matrix tile pads the tokens to 16), the backward of a single linear for
+// 1 <= T <= kGemvLinearBwdMaxT and of a projection set for 1 <= T <= kGemvMaxT
+// (its dot products cost per token; beyond these counts the fused GEMM's
+// backward is faster).  `part` is fp32 scratch of gemv_part_floats(T, N, K, r)
+// floats, or gemv_fwd_part_floats for a forward alone.  launch_gemv_fwd with
+// y == nullptr only computes u; launch_gemv_bwd with grad_x == nullptr skips
+// the weight pass.
 constexpr int64_t kGemvMaxT = 4;
+constexpr int64_t kGemvLinearBwdMaxT = 2;
 constexpr int64_t kGemvFwdMaxT = 16;
-bool gemv_applies(int64_t T, int64_t K);      // both directions
-bool gemv_fwd_applies(int64_t T, int64_t K);  // the forward
+bool gemv_fwd_applies(int64_t T, int64_t K);             // the forward
+bool gemv_bwd_applies(int64_t T, int64_t K, int count);  // the backward of `count` linears sharing x
 size_t gemv_part_floats(int64_t T, int64_t N, int64_t K, int r);
 size_t gemv_fwd_part_floats(int64_t T, int64_t N, int64_t K, int r);
 // The adapter input xa (x, or the dropped-out x) feeds u = u_scale * xa A^T
@@ -221,8 +225,8 @@ hipError_t launch_copy_rows(const uint16_t *src, int64_t ld_src, uint16_t *dst, 
 // Projection sets (linear.hip): members share x [T x K] and the adapter
 // rank r; A_set [count r x K] holds the members' A back to back, u_set and
 // v_set are [T x count r].  The few-token kernels run the set's forward for
-// T <= kGemvFwdMaxT and its backward for T <= kGemvMaxT (a [T x r] u block in
-// the workspace for a member-by-member forward).
+// T <= kGemvFwdMaxT and its backward where gemv_bwd_applies (a [T x r] u block
+// in the workspace for a member-by-member forward).
 struct SetPlan {
   int64_t T, K;
   int r, count;

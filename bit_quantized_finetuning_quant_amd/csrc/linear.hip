@@ -97,7 +97,7 @@ LinearPlan plan_linear(int64_t T, int64_t N, int64_t K, int r, bool dropout) {
   for (const auto &sh : shapes) part = std::max(part, lora_part_floats(sh[0], sh[1], sh[2]));
   // grad_A and grad_B are formed together
   part = std::max(part, lora_part_floats(r, K, T) + lora_part_floats(N, r, T));
-  if (gemv_applies(T, K))
+  if (gemv_bwd_applies(T, K, 1))
     part = std::max(part, gemv_part_floats(T, N, K, r));
   else if (gemv_fwd_applies(T, K))  // the forward on the few-token kernels, the backward on the GEMMs
     part = std::max(part, gemv_fwd_part_floats(T, N, K, r));
@@ -113,7 +113,7 @@ LinearPlan plan_linear(int64_t T, int64_t N, int64_t K, int r, bool dropout) {
   // split contraction of the fused GEMMs (few tokens or a narrow output): fp32 partial tiles of the
   // forward (y) or of grad_x, whichever needs more
   p.off_qpart = off;
-  if (!gemv_applies(T, K))
+  if (!gemv_bwd_applies(T, K, 1))
     off += align256(std::max(qgemm_split_floats(T, N, K), qgemm_split_floats(T, K, N)) * 4);
   // dropout: keep words [ceil(T/32)][K] and the dropped-out input [T x K] bf16
   p.off_keep = p.off_xd = 0;
@@ -175,7 +175,7 @@ hipError_t launch_linear_bwd(const LinearPlan &p, const uint16_t *dy, const uint
   // grad_A and the adapter term of grad_x carry s / (1 - p); grad_B = s dy^T u
   const float scale_ax = scale * ai.inv_keep;
   hipError_t e;
-  if (gemv_applies(p.T, p.K)) {
+  if (gemv_bwd_applies(p.T, p.K, 1)) {
     if (!u) {  // recompute u = (1 / (1 - p)) xa A^T
       uint16_t *uw = (uint16_t *)(ws + p.off_u);
       e = launch_gemv_fwd(p.T, x, ai.xa, w, A, B, p.r, scale, ai.inv_keep, nullptr, uw, part, cb, st);
@@ -225,28 +225,27 @@ SetPlan plan_linear_set(int64_t T, int count, const int64_t *N, int64_t K, int r
   p.off_v = off;
   off += uv;
   p.off_part = off;
-  if (T <= kGemvMaxT) {  // the set passes' scratch or the largest member's, and one u block
-    size_t part = gemv_set_part_floats(T, N, count, K, r);
-    for (int i = 0; i < count; ++i) part = std::max(part, gemv_part_floats(T, N[i], K, r));
-    off += align256(part * 4);
-    p.off_um = off;
-    off += align256((size_t)T * r * 2);
-  } else if (T <= kGemvFwdMaxT) {  // few-token forward passes, the adapter products of the backward
-    size_t part = std::max(lora_set_part_floats(T, count, N, K, r), gemv_set_fwd_part_floats(T, N, count, K, r));
+  const bool fwd_few = gemv_fwd_applies(T, K), bwd_few = gemv_bwd_applies(T, K, count);
+  size_t part = 0;
+  if (fwd_few) {  // the few-token forward: the set pass's span partials or the largest member's
+    part = gemv_set_fwd_part_floats(T, N, count, K, r);
     for (int i = 0; i < count; ++i) part = std::max(part, gemv_fwd_part_floats(T, N[i], K, r));
-    off += align256(part * 4);
-    p.off_um = off;
-    off += align256((size_t)T * r * 2);
-  } else {
-    off += align256(lora_set_part_floats(T, count, N, K, r) * 4);
-    p.off_um = off;
   }
+  if (bwd_few) {  // the few-token backward pass
+    part = std::max(part, gemv_set_part_floats(T, N, count, K, r));
+    for (int i = 0; i < count; ++i) part = std::max(part, gemv_part_floats(T, N[i], K, r));
+  }
+  if (!fwd_few || !bwd_few)  // the adapter products of the direction(s) on the fused GEMM
+    part = std::max(part, lora_set_part_floats(T, count, N, K, r));
+  off += align256(part * 4);
+  p.off_um = off;
+  if (fwd_few || bwd_few) off += align256((size_t)T * r * 2);  // one [T x r] u block
   // grad_x of a set whose members share n_out may split its contraction (each
   // split contracts the same range of every member), and so may the forward
   // when every member's n_out is whole 128-column tiles (or the set has one
   // member): their fp32 partial tiles
   p.off_qpart = 0;
-  bool same_n = T > kGemvMaxT, tiles_n = T > kGemvMaxT;
+  bool same_n = !bwd_few, tiles_n = !fwd_few;
   int64_t n_all = 0;
   for (int i = 0; i < count; ++i) {
     same_n = same_n && N[i] == N[0];
@@ -258,7 +257,7 @@ SetPlan plan_linear_set(int64_t T, int count, const int64_t *N, int64_t K, int r
   // at a few tokens a set may run member by member on the few-token tiles
   if (tiles_n)
     for (int i = 0; i < count; ++i) qsplit = std::max(qsplit, qgemm_split_floats(T, N[i], K));
-  if (T > kGemvMaxT && count > 1) qsplit = std::max(qsplit, qgemm_set_dx_member_floats(T, count, N, K));
+  if (!bwd_few && count > 1) qsplit = std::max(qsplit, qgemm_set_dx_member_floats(T, count, N, K));
   if (qsplit) {
     p.off_qpart = off;
     off += align256(qsplit * 4);
@@ -270,8 +269,9 @@ SetPlan plan_linear_set(int64_t T, int count, const int64_t *N, int64_t K, int r
 // Few-token sets.  The forward (T <= kGemvFwdMaxT) runs as one pass over the
 // members' concatenated rows when every member but the last has a multiple of
 // 64 rows, else member by member (u moves between the set's [T x count r]
-// layout and one [T x r] block); the backward (T <= kGemvMaxT) is one pass over
-// every member's rows, which sums grad_x over the members in its fp32 partials.
+// layout and one [T x r] block); the backward (gemv_bwd_applies) is one pass
+// over every member's rows, which sums grad_x over the members in its fp32
+// partials.
 static hipError_t set_fwd_few(const SetPlan &p, const uint16_t *x, const QWeight *w, const uint16_t *A_set,
                               const uint16_t *const *B, float scale, uint16_t *const *y, uint16_t *u, char *ws,
                               const Codebook &cb, hipStream_t st) {
@@ -338,7 +338,8 @@ hipError_t launch_linear_set_bwd(const SetPlan &p, const uint16_t *const *dy, co
                                  const uint16_t *A_set, const uint16_t *const *B, float scale, const uint16_t *u,
                                  uint16_t *grad_x, float *grad_A_set, float *const *grad_B, char *ws,
                                  const Codebook &cb, hipStream_t st) {
-  if (p.T <= kGemvMaxT) return set_bwd_few(p, dy, x, w, A_set, B, scale, u, grad_x, grad_A_set, grad_B, ws, cb, st);
+  if (gemv_bwd_applies(p.T, p.K, p.count))
+    return set_bwd_few(p, dy, x, w, A_set, B, scale, u, grad_x, grad_A_set, grad_B, ws, cb, st);
   float *part = (float *)(ws + p.off_part);
   uint16_t *v = (uint16_t *)(ws + p.off_v);
   const int64_t rt = (int64_t)p.count * p.r;

@@ -231,9 +231,9 @@ qlora_status qlora_linear_bwd(const uint16_t *dy, const uint16_t *x, int64_t T,
  * gradient of x summed over the members (NULL skips it).  The few-token
  * kernels run the forward for T <= 16 as one pass over the members'
  * concatenated rows when every member but the last has a multiple of 64 rows
- * (else member by member), and the backward for T <= 4 as one pass over every
- * member's rows (grad_x summed over the members in fp32, rounded to bf16
- * once); same layouts.  No
+ * (else member by member), and the backward for T <= 4 (T <= 2 for a set of
+ * one, as for a single linear) as one pass over every member's rows (grad_x
+ * summed over the members in fp32, rounded to bf16 once); same layouts.  No
  * dropout here: each adapter draws its own mask, so sets with dropout go per
  * linear.                                                                   */
 size_t qlora_linear_set_workspace_bytes(int64_t T, int count, const int64_t *n_out, int64_t n_in, int r);
@@ -332,7 +332,7 @@ enum {
   QLORA_TIMED_QGEMM_FWD = 0, /* dequant-fused GEMM, forward: x W_hat^T (+ LoRA)       */
   QLORA_TIMED_QGEMM_DX = 1,  /* dequant-fused GEMM, grad_x: dy W_hat (+ LoRA)         */
   QLORA_TIMED_GEMV_FWD = 2,  /* few-token forward, weight pass (T <= 16)               */
-  QLORA_TIMED_GEMV_BWD = 3,  /* few-token backward, weight and adapter pass (T <= 4)   */
+  QLORA_TIMED_GEMV_BWD = 3,  /* few-token backward, weight and adapter pass (T <= 2; sets T <= 4) */
   QLORA_TIMED_ADAMW = 4,     /* adapter AdamW update, whole 4096-element tiles          */
   QLORA_TIMED_KINDS = 5
 };

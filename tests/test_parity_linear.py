@@ -124,7 +124,7 @@ def test_adapter_products_at_long_token_counts(shape):
 @pytest.mark.parametrize("T", [1, 2, 4, 8, 16, 32, 64, 128, 256])
 def test_7b_projection_every_token_count_of_the_sweep(T):
     """The 7B projection (4096 x 4096, r = 64) at every token count the benchmark sweeps: the
-    few-token kernels up to 4 tokens (the forward up to 16), then the fused GEMM with clamped rows
+    few-token kernels up to 2 tokens (the forward up to 16), then the fused GEMM with clamped rows
     and split contractions."""
     announce(f"linear 7b_attn T={T} (sweep)")
     case = workloads.custom_case(4096, 4096, T, 64, 16.0, seed=900)  # one weight; x, dy drawn per T
@@ -134,8 +134,9 @@ def test_7b_projection_every_token_count_of_the_sweep(T):
 @pytest.mark.parametrize("shape", [(300, 320, 1, 24), (77, 192, 2, 5), (64, 64, 2, 256), (1000, 11008, 1, 64),
                                    (11008, 4096, 2, 64), (130, 2112, 3, 13), (515, 4160, 4, 64), (8, 64, 4, 1)])
 def test_few_token_path(shape):
-    """T <= 4 runs the HBM-bound few-token kernels; same bar as the GEMM path.  The shapes cover
-    ragged row groups and spans, r not a multiple of 8, and the largest adapter rank."""
+    """T <= 4 runs the HBM-bound few-token kernels in the forward, T <= 2 in the backward too (3 and
+    4 tokens go back through the fused GEMM); same bar as the GEMM path.  The shapes cover ragged
+    row groups and spans, r not a multiple of 8, and the largest adapter rank."""
     n_out, n_in, T, r = shape
     announce(f"linear few-token n_out={n_out} n_in={n_in} T={T} r={r}")
     case = workloads.custom_case(n_out, n_in, T, r, 16.0, seed=n_out + 3 * T)

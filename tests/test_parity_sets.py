@@ -71,9 +71,9 @@ def test_sets_against_the_oracle(n_outs, n_in, T, r):
 
 @pytest.mark.parametrize("T", [1, 2, 3, 4, 8, 16])
 def test_few_token_sets_against_the_oracle(T):
-    """T <= 4: the few-token kernels run the set (the forward over the concatenated rows, the
-    backward over every member's rows and adapter blocks in one pass); at 8 and 16 tokens the
-    forward still, the backward on the fused GEMM; same layouts, same bar."""
+    """T <= 4: the few-token kernels run a set of several members (the forward over the
+    concatenated rows, the backward over every member's rows and adapter blocks in one pass); at 8
+    and 16 tokens the forward still, the backward on the fused GEMM; same layouts, same bar."""
     announce(f"few-token set n_outs=(256, 192, 320) n_in=384 T={T} r=16")
     cases = _members((256, 192, 320), 384, T, 16, seed=40 + T)
     _check(cases)
