@@ -41,7 +41,9 @@ constexpr int kSpanUnits = 64;   // backward: units per span (one per lane)
 constexpr int kRowsPerWave = 4;  // backward: rows of one group
 constexpr int kBwdWaves = 8;     // waves of a backward workgroup
 constexpr int kBwdThreads = kBwdWaves * 64;
-constexpr int64_t kBwdTargetWaves = 2048;  // backward: waves the row split aims for
+// backward: waves the row split aims for; from 2 tokens the dot products per weight double and
+// fewer, longer row chunks (half the chunk partials to add) pay
+constexpr int64_t kBwdTargetWavesT1 = 2048, kBwdTargetWaves = 1024;
 constexpr int kBRows = 64;       // rows of B staged at a time by an adapter workgroup
 constexpr int kFwdRows = 64;     // forward: rows per workgroup (16 per wave)
 // Forward span (units per workgroup): short spans give small weights enough
@@ -739,14 +741,14 @@ __global__ __launch_bounds__(256) void gemv_bwd_finish(const float *__restrict__
 
 // Work split of one call.  The backward takes enough rows per wave that the
 // chunk partials stay small next to the weight, and no more than keeps about
-// kBwdTargetWaves waves in flight.
+// kBwdTargetWaves (one token: kBwdTargetWavesT1) waves in flight.
 struct GemvGeometry {
   int64_t funits, fspans, fblocks, ablocks;  // forward: span units, spans, weight and A workgroups
   int64_t bspans, groups, chunks;         // backward weight pass
   int64_t bsub, bparts;                   // backward adapter workgroups
 };
 
-GemvGeometry geometry(int64_t N, int64_t K, int r) {
+GemvGeometry geometry(int64_t T, int64_t N, int64_t K, int r) {
   GemvGeometry g;
   const int64_t short_span_waves = cdiv(K / 32, kFwdUnitsSmall) * cdiv(N, 16);
   g.funits = short_span_waves <= kFwdShortSpanWaves ? kFwdUnitsSmall : kFwdUnitsLarge;
@@ -754,7 +756,7 @@ GemvGeometry geometry(int64_t N, int64_t K, int r) {
   g.fblocks = g.fspans * cdiv(N, kFwdRows);
   g.ablocks = g.fspans * cdiv(r, kFwdRows);
   g.bspans = cdiv(K / 32, kSpanUnits);
-  const int64_t rows_per_wave = g.bspans * N / kBwdTargetWaves;
+  const int64_t rows_per_wave = g.bspans * N / (T == 1 ? kBwdTargetWavesT1 : kBwdTargetWaves);
   g.groups = std::max<int64_t>(1, std::min<int64_t>(4, rows_per_wave / kRowsPerWave));
   g.chunks = cdiv(N, kBwdWaves * g.groups * kRowsPerWave);
   const int64_t blocks = cdiv(N, kBRows);
@@ -777,7 +779,7 @@ template <int T>
 hipError_t gemv_fwd_run(const uint16_t *x, const uint16_t *xa, const GemvFwdSet &set, int64_t Ntot, bool rows,
                         const uint16_t *A, int r, int r_total, float scale, float u_scale, uint16_t *u, float *part,
                         const Codebook &cb, hipStream_t st) {
-  const GemvGeometry g = geometry(Ntot, set.w[0].n_in, r_total);
+  const GemvGeometry g = geometry(T, Ntot, set.w[0].n_in, r_total);
   const int64_t fblocks = rows ? g.fblocks : 0;
   float *y_part = part, *u_part = part + g.fspans * T * Ntot;
   const size_t lds = (size_t)T * (g.funits * 32 + 8) * 2;
@@ -843,11 +845,11 @@ struct BwdSplit {
   int64_t chunks, parts;
 };
 
-static BwdSplit bwd_split(GemvBwdSet &set, int64_t K, int r) {
+static BwdSplit bwd_split(int64_t T, GemvBwdSet &set, int64_t K, int r) {
   int64_t ntot = 0;
   for (int i = 0; i < set.count; ++i) ntot += set.w[i].n_out;
   BwdSplit b;
-  b.g = geometry(ntot, K, r);
+  b.g = geometry(T, ntot, K, r);
   const int64_t chunk_rows = (int64_t)kBwdWaves * b.g.groups * kRowsPerWave;
   b.chunks = 0;
   b.parts = 0;
@@ -869,7 +871,7 @@ hipError_t gemv_bwd_run(GemvBwdSet &set, const uint16_t *xa, const uint16_t *A, 
                         const uint32_t *keep, const uint16_t *u, int ld_u, uint16_t *grad_x, float *grad_A,
                         float *part, const Codebook &cb, hipStream_t st) {
   const int64_t K = set.w[0].n_in;
-  const BwdSplit b = bwd_split(set, K, r);
+  const BwdSplit b = bwd_split(T, set, K, r);
   const int64_t nf4_wgs = grad_x ? b.g.bspans * b.chunks : 0;
   float *gx_part = part, *v_part = part + b.chunks * T * K;
   const size_t lds = bwd_lds_bytes(T);
@@ -978,7 +980,7 @@ size_t gemv_set_part_floats(int64_t T, const int64_t *N, int count, int64_t K, i
   GemvBwdSet set{};
   set.count = count;
   for (int i = 0; i < count; ++i) set.w[i].n_out = N[i];
-  const BwdSplit b = bwd_split(set, K, r);
+  const BwdSplit b = bwd_split(T, set, K, r);
   const size_t bwd = (size_t)(b.chunks * T * K + b.parts * T * r);
   return std::max(gemv_set_fwd_part_floats(T, N, count, K, r), bwd);
 }
@@ -986,7 +988,7 @@ size_t gemv_set_part_floats(int64_t T, const int64_t *N, int count, int64_t K, i
 size_t gemv_set_fwd_part_floats(int64_t T, const int64_t *N, int count, int64_t K, int r) {
   int64_t ntot = 0;
   for (int i = 0; i < count; ++i) ntot += N[i];
-  const GemvGeometry gf = geometry(ntot, K, count * r);
+  const GemvGeometry gf = geometry(T, ntot, K, count * r);
   return (size_t)(gf.fspans * T * (ntot + (int64_t)count * r));
 }
 
@@ -1004,13 +1006,13 @@ hipError_t launch_gemv_bwd_set(int64_t T, const uint16_t *const *dy, const uint1
 }
 
 size_t gemv_part_floats(int64_t T, int64_t N, int64_t K, int r) {
-  const GemvGeometry g = geometry(N, K, r);
+  const GemvGeometry g = geometry(T, N, K, r);
   const size_t bwd = (size_t)(g.chunks * T * K + g.bparts * T * r);
   return std::max(gemv_fwd_part_floats(T, N, K, r), bwd);
 }
 
 size_t gemv_fwd_part_floats(int64_t T, int64_t N, int64_t K, int r) {
-  const GemvGeometry g = geometry(N, K, r);
+  const GemvGeometry g = geometry(T, N, K, r);
   return (size_t)(g.fspans * T * (N + r));
 }
 
