@@ -189,7 +189,7 @@ qlora_status noalloc_scratch(void **out) {
 // GEMM splits the contraction, the split partials, at the offsets of the
 // linear plan.
 size_t forward_scratch_bytes(const LinearPlan &p) {
-  if (gemv_fwd_applies(p.T, p.K)) return p.off_part + gemv_fwd_part_floats(p.T, p.N, p.K, p.r) * 4;
+  if (gemv_fwd_applies(p.T, p.N, p.K)) return p.off_part + gemv_fwd_part_floats(p.T, p.N, p.K, p.r) * 4;
   const size_t qsplit = qgemm_split_floats(p.T, p.N, p.K);
   return std::max(p.off_part + lora_part_floats(p.T, p.r, p.K) * 4, qsplit ? p.off_qpart + qsplit * 4 : 0);
 }

@@ -1,8 +1,9 @@
-// Few-token QLoRA linear layer for gfx950 (forward T <= 16, backward T <= 4).
+// Few-token QLoRA linear layer for gfx950 (forward T <= 32, backward T <= 4).
 // With so few tokens the work per weight element is a handful of flops, so
 // reading the 4-bit weight from HBM is the bound: every weight byte is read
-// once, decoded once and used for all T tokens (the forward's matrix tile pads
-// the tokens to 16; the backward's vector ALU dot products cost per token).
+// once, decoded once and used for all T tokens (the forward's matrix tiles pad
+// the tokens to 16, one or two tiles; the backward's vector ALU dot products
+// cost per token).
 //
 // Method ("qlora" encyclopedia entry, tonho.wtf, section "a ideia"): the weight
 // is dequantized to BFloat16 as it is used; gradients reach only the LoRA
@@ -14,8 +15,9 @@
 // codes (half an NF4 block).
 //
 //   gemv_fwd_main    workgroup = (span of 8 or 32 units, 64 rows): x W_hat^T on
-//                    v_mfma_f32_16x16x32_bf16 with the tokens padded to 16; a
-//                    lane decodes one unit per step straight into the B operand.
+//                    v_mfma_f32_16x16x32_bf16 with the tokens padded to 16 (one
+//                    or two token tiles); a lane decodes one unit per step
+//                    straight into the B operand of every token tile.
 //                    The first workgroups do the same for the rows of A
 //                    (partial u).
 //   gemv_fwd_finish  y = sum of span partials + s u B^T, u = bf16(sum of partials)
@@ -51,6 +53,11 @@ constexpr int kFwdRows = 64;     // forward: rows per workgroup (16 per wave)
 // long spans, which keep the span partials and per-workgroup set-up few.
 constexpr int kFwdUnitsSmall = 8, kFwdUnitsLarge = 32;
 constexpr int64_t kFwdShortSpanWaves = 8192;  // short spans while they give at most this many waves
+// Above 16 tokens (two tiles of 16 per decoded unit) the forward pays only while its x tile leaves
+// room for several workgroups per CU: with the long spans of large weights 32 tokens take 66 KB of
+// LDS per workgroup and run slower than the fused GEMM's few-token tiles (22016 x 8192: 157.7 ->
+// 171.5 us per fwd+bwd, against 61 -> 50 us at 4096^2 and 17 tokens).
+constexpr size_t kFwdTwoTileMaxLds = 40 * 1024;
 template <int kUnits>
 struct FwdShape {
   static constexpr int kSteps = kUnits / 4;
@@ -169,21 +176,24 @@ __device__ __forceinline__ void fwd_load(const QWeight &w, int64_t n, int64_t un
   for (int st = 0; st < kSteps; ++st) load_unit(w, n, min(unit0 + 4 * st, U - 1), kblk_row, f.L[st]);
 }
 
-template <int kSteps>
-__device__ __forceinline__ f32x4 fwd_tile(const FwdTile<kSteps> &f, float mu, const float *lut,
-                                          const uint16_t *xrow) {
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+// kTT tiles of 16 tokens (xrow[h]: this lane's token row of tile h) share
+// each decoded unit.
+template <int kSteps, int kTT>
+__device__ __forceinline__ void fwd_tile(const FwdTile<kSteps> &f, float mu, const float *lut,
+                                         const uint16_t *const (&xrow)[kTT], f32x4 (&acc)[kTT]) {
+#pragma unroll
+  for (int h = 0; h < kTT; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int st = 0; st < kSteps; ++st) {
     uint32_t wv[16];
     decode_unit(f.L[st].c, decode_constant(f.L[st].q, f.L[st].s2, mu), lut, wv);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const u32x4 xa = *(const u32x4 *)(xrow + 128 * st + 8 * j);
-      acc = mfma16(xa, u32x4{wv[4 * j], wv[4 * j + 1], wv[4 * j + 2], wv[4 * j + 3]}, acc);
+      const u32x4 wj = u32x4{wv[4 * j], wv[4 * j + 1], wv[4 * j + 2], wv[4 * j + 3]};
+#pragma unroll
+      for (int h = 0; h < kTT; ++h) acc[h] = mfma16(*(const u32x4 *)(xrow[h] + 128 * st + 8 * j), wj, acc[h]);
     }
   }
-  return acc;
 }
 
 // Rows of A: the same tile with bf16 values read directly, in slices of at
@@ -199,15 +209,18 @@ __device__ __forceinline__ void a_load(const uint16_t *A, int64_t K, int64_t n, 
   }
 }
 
-__device__ __forceinline__ void fwd_store(const f32x4 &acc, float *dst, int64_t rows, int64_t row, int T, int g) {
+__device__ __forceinline__ void fwd_store(const f32x4 &acc, float *dst, int64_t rows, int64_t row, int T, int g,
+                                          int h) {
   if (row < rows) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (4 * g + i < T) dst[(int64_t)(4 * g + i) * rows + row] = acc[i];
+    for (int i = 0; i < 4; ++i) {
+      const int t = 16 * h + 4 * g + i;
+      if (t < T) dst[(int64_t)t * rows + row] = acc[i];
+    }
   }
 }
 
-template <int kUnits>
+template <int kUnits, int kTT>
 __global__ __launch_bounds__(256) void gemv_fwd_main(const uint16_t *__restrict__ x,
                                                      const uint16_t *__restrict__ xa, int T, GemvFwdSet set,
                                                      int64_t Ntot, const uint16_t *__restrict__ A, int r,
@@ -251,30 +264,33 @@ __global__ __launch_bounds__(256) void gemv_fwd_main(const uint16_t *__restrict_
   }
   __syncthreads();
   if (!active) return;
-  const uint16_t *xrow = xs + min(rl, T - 1) * kXStride + 32 * g;
-  if (a_rows) {
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  const uint16_t *xrow[kTT];
 #pragma unroll
-    for (int h = 0; h < kSteps / kASlice; ++h) {
-      if (h > 0) a_load<kASlice>(A, K, n, unit0, U, h, av);
+  for (int h = 0; h < kTT; ++h) xrow[h] = xs + min(16 * h + rl, T - 1) * kXStride + 32 * g;
+  f32x4 acc[kTT];
+  if (a_rows) {
+#pragma unroll
+    for (int h = 0; h < kTT; ++h) acc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int sl = 0; sl < kSteps / kASlice; ++sl) {
+      if (sl > 0) a_load<kASlice>(A, K, n, unit0, U, sl, av);
 #pragma unroll
       for (int st = 0; st < kASlice; ++st)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const u32x4 xa = *(const u32x4 *)(xrow + 128 * (st + h * kASlice) + 8 * j);
-          acc = mfma16(xa, av[st][j], acc);
-        }
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int h = 0; h < kTT; ++h)
+            acc[h] = mfma16(*(const u32x4 *)(xrow[h] + 128 * (st + sl * kASlice) + 8 * j), av[st][j], acc[h]);
     }
-    fwd_store(acc, u_part + span * T * r, r, row0 + rl, T, g);
+#pragma unroll
+    for (int h = 0; h < kTT; ++h) fwd_store(acc[h], u_part + span * T * r, r, row0 + rl, T, g, h);
     return;
   }
-  const f32x4 acc = fwd_tile(f, w.dq ? *w.mu : 0.f, lut, xrow);
-  if (row0 + rl < rows) {  // concatenated row index, row stride Ntot
-    float *dst = y_part + span * T * Ntot + set.block0[m] * kFwdRows + row0 + rl;
+  fwd_tile(f, w.dq ? *w.mu : 0.f, lut, xrow, acc);
+  // concatenated row index, row stride Ntot
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (4 * g + i < T) dst[(int64_t)(4 * g + i) * Ntot] = acc[i];
-  }
+  for (int h = 0; h < kTT; ++h)
+    fwd_store(acc[h], y_part + span * T * Ntot + set.block0[m] * kFwdRows, Ntot, row0 + rl, T, g, h);
 }
 
 // Sum of `count` fp32 values p[0], p[stride], ... in index order, fetched
@@ -784,14 +800,17 @@ hipError_t gemv_fwd_run(const uint16_t *x, const uint16_t *xa, const GemvFwdSet 
   float *y_part = part, *u_part = part + g.fspans * T * Ntot;
   const size_t lds = (size_t)T * (g.funits * 32 + 8) * 2;
   const unsigned grid = (unsigned)(fblocks + g.ablocks);
+  constexpr int kTT = (T + 15) / 16;  // tiles of 16 tokens
+  // the x tile is at most 40 KB above 16 tokens (gemv_fwd_applies), within the default LDS limit
+  if (lds > kFwdTwoTileMaxLds && T > 16) return hipErrorInvalidValue;
   TimedLaunch tl;
   const bool timed = rows && timing_begin(st, tl, kTimedGemvFwd);
   if (g.funits == kFwdUnitsSmall)
-    gemv_fwd_main<kFwdUnitsSmall><<<grid, 256, lds, st>>>(x, xa, T, set, Ntot, A, r_total, y_part, u_part, g.fspans,
-                                                          g.ablocks, cb);
+    gemv_fwd_main<kFwdUnitsSmall, kTT><<<grid, 256, lds, st>>>(x, xa, T, set, Ntot, A, r_total, y_part, u_part,
+                                                               g.fspans, g.ablocks, cb);
   else
-    gemv_fwd_main<kFwdUnitsLarge><<<grid, 256, lds, st>>>(x, xa, T, set, Ntot, A, r_total, y_part, u_part, g.fspans,
-                                                          g.ablocks, cb);
+    gemv_fwd_main<kFwdUnitsLarge, kTT><<<grid, 256, lds, st>>>(x, xa, T, set, Ntot, A, r_total, y_part, u_part,
+                                                               g.fspans, g.ablocks, cb);
   if (timed) timing_end(st, tl);
   const int64_t out_rows = rows ? Ntot : 0;
   const unsigned fg = (unsigned)std::max<int64_t>(1, cdiv(out_rows, 64));
@@ -944,7 +963,12 @@ hipError_t gemv_bwd_set_impl(const uint16_t *const *dy, const uint16_t *x, const
 bool gemv_bwd_applies(int64_t T, int64_t K, int count) {
   return T >= 1 && T <= (count == 1 ? kGemvLinearBwdMaxT : kGemvMaxT) && K % 64 == 0;
 }
-bool gemv_fwd_applies(int64_t T, int64_t K) { return T >= 1 && T <= kGemvFwdMaxT && K % 64 == 0; }
+bool gemv_fwd_applies(int64_t T, int64_t N, int64_t K) {
+  if (T < 1 || T > kGemvFwdMaxT || K % 64 != 0) return false;
+  if (T <= 16) return true;
+  const GemvGeometry g = geometry(T, N, K, 0);
+  return (size_t)T * (g.funits * 32 + 8) * 2 <= kFwdTwoTileMaxLds;
+}
 
 bool gemv_set_fusable(const int64_t *N, int count) {
   for (int i = 0; i + 1 < count; ++i)
@@ -972,6 +996,22 @@ hipError_t launch_gemv_fwd_set(int64_t T, const uint16_t *x, const QWeight *w, i
     case 14: return gemv_fwd_set_impl<14>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
     case 15: return gemv_fwd_set_impl<15>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
     case 16: return gemv_fwd_set_impl<16>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 17: return gemv_fwd_set_impl<17>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 18: return gemv_fwd_set_impl<18>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 19: return gemv_fwd_set_impl<19>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 20: return gemv_fwd_set_impl<20>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 21: return gemv_fwd_set_impl<21>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 22: return gemv_fwd_set_impl<22>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 23: return gemv_fwd_set_impl<23>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 24: return gemv_fwd_set_impl<24>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 25: return gemv_fwd_set_impl<25>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 26: return gemv_fwd_set_impl<26>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 27: return gemv_fwd_set_impl<27>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 28: return gemv_fwd_set_impl<28>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 29: return gemv_fwd_set_impl<29>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 30: return gemv_fwd_set_impl<30>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 31: return gemv_fwd_set_impl<31>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 32: return gemv_fwd_set_impl<32>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1036,6 +1076,22 @@ hipError_t launch_gemv_fwd(int64_t T, const uint16_t *x, const uint16_t *xa, con
     case 14: return gemv_fwd_impl<14>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
     case 15: return gemv_fwd_impl<15>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
     case 16: return gemv_fwd_impl<16>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 17: return gemv_fwd_impl<17>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 18: return gemv_fwd_impl<18>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 19: return gemv_fwd_impl<19>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 20: return gemv_fwd_impl<20>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 21: return gemv_fwd_impl<21>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 22: return gemv_fwd_impl<22>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 23: return gemv_fwd_impl<23>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 24: return gemv_fwd_impl<24>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 25: return gemv_fwd_impl<25>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 26: return gemv_fwd_impl<26>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 27: return gemv_fwd_impl<27>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 28: return gemv_fwd_impl<28>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 29: return gemv_fwd_impl<29>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 30: return gemv_fwd_impl<30>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 31: return gemv_fwd_impl<31>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 32: return gemv_fwd_impl<32>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
     default: return hipErrorInvalidValue;
   }
 }

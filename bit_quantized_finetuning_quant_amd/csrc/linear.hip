@@ -99,7 +99,7 @@ LinearPlan plan_linear(int64_t T, int64_t N, int64_t K, int r, bool dropout) {
   part = std::max(part, lora_part_floats(r, K, T) + lora_part_floats(N, r, T));
   if (gemv_bwd_applies(T, K, 1))
     part = std::max(part, gemv_part_floats(T, N, K, r));
-  else if (gemv_fwd_applies(T, K))  // the forward on the few-token kernels, the backward on the GEMMs
+  else if (gemv_fwd_applies(T, N, K))  // the forward on the few-token kernels, the backward on the GEMMs
     part = std::max(part, gemv_fwd_part_floats(T, N, K, r));
   size_t off = 0;
   p.off_status = off;  // status word (never written by the linear calls)
@@ -152,7 +152,7 @@ hipError_t launch_linear_fwd(const LinearPlan &p, const uint16_t *x, const QWeig
   float *part = (float *)(ws + p.off_part);
   const AdapterInput ai = adapter_input(p, x, ws, d, st);
   if (ai.err != hipSuccess) return ai.err;
-  if (gemv_fwd_applies(p.T, p.K))
+  if (gemv_fwd_applies(p.T, p.N, p.K))
     return launch_gemv_fwd(p.T, x, ai.xa, w, A, B, p.r, scale, ai.inv_keep, y, u, part, cb, st);
   // u = bf16((1 / (1 - p)) xa A^T): the factor is exactly 1 without dropout
   hipError_t e = launch_lora(LoraKind::kU, ai.xa, p.K, A, p.K, p.T, p.r, p.K, ai.inv_keep, u, part, st);
@@ -225,7 +225,10 @@ SetPlan plan_linear_set(int64_t T, int count, const int64_t *N, int64_t K, int r
   p.off_v = off;
   off += uv;
   p.off_part = off;
-  const bool fwd_few = gemv_fwd_applies(T, K), bwd_few = gemv_bwd_applies(T, K, count);
+  int64_t ntot = 0;
+  for (int i = 0; i < count; ++i) ntot += N[i];
+  p.fwd_few = gemv_fwd_applies(T, ntot, K);
+  const bool fwd_few = p.fwd_few, bwd_few = gemv_bwd_applies(T, K, count);
   size_t part = 0;
   if (fwd_few) {  // the few-token forward: the set pass's span partials or the largest member's
     part = gemv_set_fwd_part_floats(T, N, count, K, r);
@@ -312,7 +315,7 @@ hipError_t launch_linear_set_fwd(const SetPlan &p, const uint16_t *x, const QWei
                                  const uint16_t *const *B, float scale, uint16_t *const *y, uint16_t *u_out, char *ws,
                                  const Codebook &cb, hipStream_t st) {
   uint16_t *u = u_out ? u_out : (uint16_t *)(ws + p.off_u);
-  if (gemv_fwd_applies(p.T, p.K)) return set_fwd_few(p, x, w, A_set, B, scale, y, u, ws, cb, st);
+  if (p.fwd_few) return set_fwd_few(p, x, w, A_set, B, scale, y, u, ws, cb, st);
   float *part = (float *)(ws + p.off_part);
   const int64_t rt = (int64_t)p.count * p.r;
   // u_set = x A_set^T: one product for every member's u

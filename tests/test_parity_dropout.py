@@ -75,7 +75,7 @@ def test_fused_gemm_path(shape):
 
 
 @pytest.mark.parametrize("shape", [(300, 320, 1, 24), (77, 192, 2, 5), (130, 2112, 3, 13), (515, 4160, 4, 64),
-                                   (300, 320, 8, 24), (515, 4160, 16, 64)])
+                                   (300, 320, 8, 24), (515, 4160, 16, 64), (300, 320, 27, 24)])
 def test_few_token_path(shape):
     n_out, n_in, T, r = shape
     announce(f"dropout few-token n_out={n_out} n_in={n_in} T={T} r={r}")

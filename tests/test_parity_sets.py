@@ -69,11 +69,12 @@ def test_sets_against_the_oracle(n_outs, n_in, T, r):
     _check(cases, need_u=False)
 
 
-@pytest.mark.parametrize("T", [1, 2, 3, 4, 8, 16])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 8, 16, 29])
 def test_few_token_sets_against_the_oracle(T):
     """T <= 4: the few-token kernels run a set of several members (the forward over the
-    concatenated rows, the backward over every member's rows and adapter blocks in one pass); at 8
-    and 16 tokens the forward still, the backward on the fused GEMM; same layouts, same bar."""
+    concatenated rows, the backward over every member's rows and adapter blocks in one pass); at 8,
+    16 and 29 tokens (two token tiles) the forward still, the backward on the fused GEMM; same
+    layouts, same bar."""
     announce(f"few-token set n_outs=(256, 192, 320) n_in=384 T={T} r=16")
     cases = _members((256, 192, 320), 384, T, 16, seed=40 + T)
     _check(cases)
@@ -163,16 +164,16 @@ def test_one_member_set_equals_the_single_linear_calls(n_out, n_in, T, r):
         assert np.array_equal(host(t0), host(t1))
 
 
-@pytest.mark.parametrize("n_outs,n_in,T,r", [((4096, 4096), 8192, 24, 32), ((4096, 4096), 8192, 16, 32),
-                                             ((4096, 8192), 4096, 40, 24)])
+@pytest.mark.parametrize("n_outs,n_in,T,r", [((4096, 4096), 8192, 48, 32), ((4096, 4096), 8192, 16, 32),
+                                             ((4096, 4096), 8192, 24, 32), ((4096, 8192), 4096, 40, 24)])
 def test_few_token_set_member_by_member(n_outs, n_in, T, r):
     """Sets at a few tokens whose members are large enough that the split cost models run them
     member by member on the few-token tiles: the first shape in both directions (forward: each
     member with its own split and reduction, the adapter term from its columns of u_set; grad_x:
     every member's splits as fp32 partial tiles, its share of s v_set A_set in its first split,
-    one reduction over all of them), the second the same grad_x after a forward on the few-token
-    kernels, the third in the forward only (members of different widths, 40 tokens: clamped rows,
-    rank 24); against the oracle."""
+    one reduction over all of them), the second and third the same grad_x after a forward on the
+    few-token kernels (one and two tiles of 16 tokens), the fourth in the forward only (members of
+    different widths, 40 tokens: clamped rows, rank 24); against the oracle."""
     announce(f"set {n_outs} x {n_in} T={T} r={r} (member by member)")
     _check(_members(n_outs, n_in, T, r, seed=41 + T))
 

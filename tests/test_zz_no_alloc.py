@@ -2,7 +2,8 @@
 against the forward with one (qlora_linear_fwd): the same kernels on the same inputs, so y and u
 must be bit-identical, and both within the normwise bar of the fp64 oracle.  Two calls in a row
 share the library's scratch array, the second on a smaller input (the few-token path), a third
-goes back to the first shape and a fourth runs 12 tokens (the few-token forward above 4 tokens)."""
+goes back to the first shape, a fourth runs 12 tokens (the few-token forward above 4 tokens) and a
+fifth 28 (its two tiles of 16 tokens)."""
 
 import numpy as np
 import pytest
@@ -46,6 +47,8 @@ def test_noalloc_forward_matches_the_workspace_forward_on_consecutive_calls():
     _compare(big, save_u=False)
     announce("noalloc fwd 512x1024 T=12 r=16 (few-token forward, u saved)")
     _compare(workloads.custom_case(512, 1024, 12, 16, 16.0, seed=73), save_u=True)
+    announce("noalloc fwd 512x1024 T=28 r=16 (few-token forward, two token tiles)")
+    _compare(workloads.custom_case(512, 1024, 28, 16, 16.0, seed=74), save_u=False)
 
 
 def test_noalloc_forward_7b_projection():
