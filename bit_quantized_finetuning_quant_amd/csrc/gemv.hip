@@ -53,11 +53,11 @@ constexpr int kFwdRows = 64;     // forward: rows per workgroup (16 per wave)
 // long spans, which keep the span partials and per-workgroup set-up few.
 constexpr int kFwdUnitsSmall = 8, kFwdUnitsLarge = 32;
 constexpr int64_t kFwdShortSpanWaves = 8192;  // short spans while they give at most this many waves
-// Above 16 tokens (two tiles of 16 per decoded unit) the forward pays only while its x tile leaves
-// room for several workgroups per CU: with the long spans of large weights 32 tokens take 66 KB of
-// LDS per workgroup and run slower than the fused GEMM's few-token tiles (22016 x 8192: 157.7 ->
-// 171.5 us per fwd+bwd, against 61 -> 50 us at 4096^2 and 17 tokens).
-constexpr size_t kFwdTwoTileMaxLds = 40 * 1024;
+// Above 16 tokens (two to four tiles of 16 per decoded unit) the forward pays only while its x tile
+// leaves room for several workgroups per CU: with the long spans of large weights 32 tokens take
+// 66 KB of LDS per workgroup and run slower than the fused GEMM's few-token tiles (22016 x 8192:
+// 157.7 -> 171.5 us per fwd+bwd, against 61 -> 50 us at 4096^2 and 17 tokens).
+constexpr size_t kFwdMultiTileMaxLds = 40 * 1024;
 template <int kUnits>
 struct FwdShape {
   static constexpr int kSteps = kUnits / 4;
@@ -802,15 +802,20 @@ hipError_t gemv_fwd_run(const uint16_t *x, const uint16_t *xa, const GemvFwdSet 
   const unsigned grid = (unsigned)(fblocks + g.ablocks);
   constexpr int kTT = (T + 15) / 16;  // tiles of 16 tokens
   // the x tile is at most 40 KB above 16 tokens (gemv_fwd_applies), within the default LDS limit
-  if (lds > kFwdTwoTileMaxLds && T > 16) return hipErrorInvalidValue;
+  if (lds > kFwdMultiTileMaxLds && T > 16) return hipErrorInvalidValue;
   TimedLaunch tl;
   const bool timed = rows && timing_begin(st, tl, kTimedGemvFwd);
-  if (g.funits == kFwdUnitsSmall)
+  if (g.funits == kFwdUnitsSmall) {
     gemv_fwd_main<kFwdUnitsSmall, kTT><<<grid, 256, lds, st>>>(x, xa, T, set, Ntot, A, r_total, y_part, u_part,
                                                                g.fspans, g.ablocks, cb);
-  else
-    gemv_fwd_main<kFwdUnitsLarge, kTT><<<grid, 256, lds, st>>>(x, xa, T, set, Ntot, A, r_total, y_part, u_part,
-                                                               g.fspans, g.ablocks, cb);
+  } else {
+    // long spans hold at most 19 tokens in 40 KB
+    if constexpr (kTT <= 2)
+      gemv_fwd_main<kFwdUnitsLarge, kTT><<<grid, 256, lds, st>>>(x, xa, T, set, Ntot, A, r_total, y_part, u_part,
+                                                                 g.fspans, g.ablocks, cb);
+    else
+      return hipErrorInvalidValue;
+  }
   if (timed) timing_end(st, tl);
   const int64_t out_rows = rows ? Ntot : 0;
   const unsigned fg = (unsigned)std::max<int64_t>(1, cdiv(out_rows, 64));
@@ -967,7 +972,7 @@ bool gemv_fwd_applies(int64_t T, int64_t N, int64_t K) {
   if (T < 1 || T > kGemvFwdMaxT || K % 64 != 0) return false;
   if (T <= 16) return true;
   const GemvGeometry g = geometry(T, N, K, 0);
-  return (size_t)T * (g.funits * 32 + 8) * 2 <= kFwdTwoTileMaxLds;
+  return (size_t)T * (g.funits * 32 + 8) * 2 <= kFwdMultiTileMaxLds;
 }
 
 bool gemv_set_fusable(const int64_t *N, int count) {
@@ -1012,6 +1017,38 @@ hipError_t launch_gemv_fwd_set(int64_t T, const uint16_t *x, const QWeight *w, i
     case 30: return gemv_fwd_set_impl<30>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
     case 31: return gemv_fwd_set_impl<31>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
     case 32: return gemv_fwd_set_impl<32>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 33: return gemv_fwd_set_impl<33>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 34: return gemv_fwd_set_impl<34>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 35: return gemv_fwd_set_impl<35>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 36: return gemv_fwd_set_impl<36>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 37: return gemv_fwd_set_impl<37>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 38: return gemv_fwd_set_impl<38>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 39: return gemv_fwd_set_impl<39>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 40: return gemv_fwd_set_impl<40>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 41: return gemv_fwd_set_impl<41>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 42: return gemv_fwd_set_impl<42>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 43: return gemv_fwd_set_impl<43>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 44: return gemv_fwd_set_impl<44>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 45: return gemv_fwd_set_impl<45>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 46: return gemv_fwd_set_impl<46>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 47: return gemv_fwd_set_impl<47>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 48: return gemv_fwd_set_impl<48>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 49: return gemv_fwd_set_impl<49>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 50: return gemv_fwd_set_impl<50>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 51: return gemv_fwd_set_impl<51>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 52: return gemv_fwd_set_impl<52>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 53: return gemv_fwd_set_impl<53>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 54: return gemv_fwd_set_impl<54>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 55: return gemv_fwd_set_impl<55>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 56: return gemv_fwd_set_impl<56>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 57: return gemv_fwd_set_impl<57>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 58: return gemv_fwd_set_impl<58>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 59: return gemv_fwd_set_impl<59>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 60: return gemv_fwd_set_impl<60>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 61: return gemv_fwd_set_impl<61>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 62: return gemv_fwd_set_impl<62>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 63: return gemv_fwd_set_impl<63>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
+    case 64: return gemv_fwd_set_impl<64>(x, w, count, A_set, B, r, scale, y, u_set, part, cb, st);
     default: return hipErrorInvalidValue;
   }
 }
@@ -1092,6 +1129,38 @@ hipError_t launch_gemv_fwd(int64_t T, const uint16_t *x, const uint16_t *xa, con
     case 30: return gemv_fwd_impl<30>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
     case 31: return gemv_fwd_impl<31>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
     case 32: return gemv_fwd_impl<32>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 33: return gemv_fwd_impl<33>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 34: return gemv_fwd_impl<34>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 35: return gemv_fwd_impl<35>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 36: return gemv_fwd_impl<36>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 37: return gemv_fwd_impl<37>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 38: return gemv_fwd_impl<38>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 39: return gemv_fwd_impl<39>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 40: return gemv_fwd_impl<40>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 41: return gemv_fwd_impl<41>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 42: return gemv_fwd_impl<42>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 43: return gemv_fwd_impl<43>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 44: return gemv_fwd_impl<44>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 45: return gemv_fwd_impl<45>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 46: return gemv_fwd_impl<46>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 47: return gemv_fwd_impl<47>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 48: return gemv_fwd_impl<48>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 49: return gemv_fwd_impl<49>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 50: return gemv_fwd_impl<50>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 51: return gemv_fwd_impl<51>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 52: return gemv_fwd_impl<52>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 53: return gemv_fwd_impl<53>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 54: return gemv_fwd_impl<54>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 55: return gemv_fwd_impl<55>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 56: return gemv_fwd_impl<56>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 57: return gemv_fwd_impl<57>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 58: return gemv_fwd_impl<58>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 59: return gemv_fwd_impl<59>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 60: return gemv_fwd_impl<60>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 61: return gemv_fwd_impl<61>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 62: return gemv_fwd_impl<62>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 63: return gemv_fwd_impl<63>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
+    case 64: return gemv_fwd_impl<64>(x, xa, w, A, B, r, scale, u_scale, y, u, part, cb, st);
     default: return hipErrorInvalidValue;
   }
 }

@@ -46,7 +46,7 @@ struct DequantSet {
 hipError_t launch_dequantize_set(const DequantSet &set, const Codebook &cb, hipStream_t st);
 
 // Few-token path (gemv.hip): the forward for 1 <= T <= kGemvFwdMaxT (its
-// matrix tiles pad the tokens to 16 or 32), the backward of a single linear for
+// matrix tiles pad the tokens to a multiple of 16), the backward of a single linear for
 // 1 <= T <= kGemvLinearBwdMaxT and of a projection set for 1 <= T <= kGemvMaxT
 // (its dot products cost per token; beyond these counts the fused GEMM's
 // backward is faster).  `part` is fp32 scratch of gemv_part_floats(T, N, K, r)
@@ -55,7 +55,7 @@ hipError_t launch_dequantize_set(const DequantSet &set, const Codebook &cb, hipS
 // the weight pass.
 constexpr int64_t kGemvMaxT = 4;
 constexpr int64_t kGemvLinearBwdMaxT = 2;
-constexpr int64_t kGemvFwdMaxT = 32;
+constexpr int64_t kGemvFwdMaxT = 64;
 bool gemv_fwd_applies(int64_t T, int64_t N, int64_t K);  // the forward over N rows (a set: all members' rows)
 bool gemv_bwd_applies(int64_t T, int64_t K, int count);  // the backward of `count` linears sharing x
 size_t gemv_part_floats(int64_t T, int64_t N, int64_t K, int r);

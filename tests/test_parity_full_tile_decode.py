@@ -7,9 +7,11 @@ A = 0 make y row t equal to column k_t of the dequantized weight, and one-hot dy
 make grad_x row t equal to row n_t: a single product is exact in fp32, so the result must equal
 the oracle's dequantized BF16 weight bit for bit ("qlora" entry, sections "a ideia" and "como
 funciona": the 4-bit weight is dequantized to BFloat16 on every use).  Together the calls cover
-every element of every weight, in both storage forms.  T = 40 and 64 run the 64-row few-token
-tiles (every wave decoding, split contraction; at T = 40 rows 40..63 read row 39 and are never
-stored), T = 128 the 128-row few-token tiles; T = 256 and 512 the 256 x 128 tiles.
+every element of every weight, in both storage forms.  T = 40 and 64 run grad_x on the 64-row
+few-token tiles (every wave decoding, split contraction; at T = 40 rows 40..63 read row 39 and are
+never stored) and, on this shape, the forward on the few-token kernels' matrix tiles (three and four
+tiles of 16 tokens); a weight with long forward spans keeps the forward on the 64-row tiles; T = 128
+runs the 128-row few-token tiles, T = 256 and 512 the 256 x 128 tiles.
 """
 
 import numpy as np
@@ -37,6 +39,26 @@ def _one_hot(T, width, idx):
 
 def _zeros(*shape):
     return np.zeros(shape, np.uint16)
+
+
+@pytest.mark.parametrize("T", [40, 64])
+def test_forward_on_the_few_token_tiles_every_column(T):
+    """4096 x 8256 (every tile full; forward spans long enough that its 40- or 64-token x tile would
+    not fit the few-token kernels' limit): the forward runs the fused GEMM's 64-row few-token tiles,
+    and one-hot rows cover every column of the weight."""
+    n_out, n_in = 4096, 8256
+    announce(f"few-token tiles one-hot forward {n_out}x{n_in} T={T}")
+    w, rng = _weight(700 + T, n_out, n_in)
+    q = qlora.quantize(dev_f32(w))
+    wh = oracle.dequantize(oracle.quantize(w, n_out, n_in))
+    b_rand = dev_bf16(workloads.to_bf16_bits((rng.standard_normal((n_out, R)) * 0.01).astype(np.float32)))
+    a_zero = dev_bf16(_zeros(R, n_in))
+    cols = rng.permutation(n_in)
+    for part in range(-(-n_in // T)):
+        ks = cols[(part * T) % n_in:][:T]
+        ks = np.concatenate([ks, cols[:T - ks.size]])
+        y, _ = qlora.linear_fwd(dev_bf16(_one_hot(T, n_in, ks)), q, a_zero, b_rand, 0.5)
+        assert np.array_equal(host_bits(y), wh[:, ks].T), ("forward", part)
 
 
 @pytest.mark.parametrize("double_quant", [True, False])

@@ -147,13 +147,15 @@ def test_few_token_path(shape):
 @pytest.mark.parametrize("shape", [(300, 320, 5, 24), (77, 192, 6, 5), (64, 64, 16, 256), (1000, 11008, 9, 64),
                                    (130, 2112, 12, 13), (515, 4160, 16, 64), (8, 64, 16, 1), (4096, 4096, 7, 64),
                                    (300, 320, 17, 24), (77, 192, 31, 5), (64, 64, 32, 256), (515, 4160, 32, 64),
-                                   (1000, 11008, 24, 64), (8192, 8192, 19, 16), (8192, 8192, 32, 16)])
-def test_few_token_forward_up_to_32_tokens(shape):
-    """From 5 to 32 tokens the forward runs the few-token kernels (their matrix tiles pad the
-    tokens to 16, or to 32 with two tiles per decoded unit) and the backward the fused GEMM: ragged
-    row groups, spans and token tiles, ranks 1 to 256 (the largest T r the forward's reduction
-    holds), long spans at 19 tokens (a 39 KB x tile) and at 32 (whose 66 KB x tile sends the
-    forward to the fused GEMM), against the oracle."""
+                                   (1000, 11008, 24, 64), (8192, 8192, 19, 16), (8192, 8192, 32, 16),
+                                   (300, 320, 33, 24), (77, 192, 47, 5), (515, 4160, 64, 64), (4096, 4096, 40, 64),
+                                   (64, 64, 64, 256)])
+def test_few_token_forward_up_to_64_tokens(shape):
+    """From 5 to 64 tokens the forward runs the few-token kernels (their matrix tiles pad the
+    tokens to a multiple of 16, up to four tiles per decoded unit) and the backward the fused GEMM:
+    ragged row groups, spans and token tiles, ranks 1 to 256 (the largest T r the forward's
+    reduction holds), long spans at 19 tokens (a 39 KB x tile) and at 32 (whose 66 KB x tile sends
+    the forward to the fused GEMM), against the oracle."""
     n_out, n_in, T, r = shape
     announce(f"linear few-token forward n_out={n_out} n_in={n_in} T={T} r={r}")
     case = workloads.custom_case(n_out, n_in, T, r, 16.0, seed=n_out + 7 * T + r)
@@ -180,8 +182,9 @@ def test_backward_without_grad_x(T):
 def test_one_hot_rows_return_decoded_weight_bit_exactly(T):
     """x rows one-hot with A = 0: y row t is column k_t of W_hat; dy rows one-hot with B = 0:
     grad_x row t is row n_t of W_hat.  A single product is exact in fp32, so this checks the
-    in-kernel decode and layout independently of summation order: at 40 tokens both directions on
-    the few-token tiles, at 16 and 32 the forward on the few-token kernels' matrix tiles."""
+    in-kernel decode and layout independently of summation order: at 40 tokens grad_x on the
+    fused GEMM's few-token tiles, and at 16, 32 and 40 the forward on the few-token kernels' matrix
+    tiles."""
     announce(f"linear one-hot 384x320 T={T}")
     n_out, n_in, r = 384, 320, 16
     rng = np.random.default_rng(7)
