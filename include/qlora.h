@@ -229,7 +229,7 @@ qlora_status qlora_linear_bwd(const uint16_t *dy, const uint16_t *x, int64_t T,
  * i r ..).  B[i] [n_out_i x r], y[i] [T x n_out_i], dy[i] [T x n_out_i] and
  * grad_B[i] [n_out_i x r] are arrays of count device pointers; grad_x is the
  * gradient of x summed over the members (NULL skips it).  The few-token
- * kernels run the forward for T <= 16 (and up to 32 while the tokens' x tile
+ * kernels run the forward for T <= 16 (and up to 64 while the tokens' x tile
  * stays within 40 KB of LDS, which the shorter spans of smaller weights
  * allow) as one pass over the members' concatenated rows when every member
  * but the last has a multiple of 64 rows (else member by member), and the
@@ -333,7 +333,7 @@ qlora_status qlora_adamw_step(float *param, uint16_t *param_bf16, const float *g
 enum {
   QLORA_TIMED_QGEMM_FWD = 0, /* dequant-fused GEMM, forward: x W_hat^T (+ LoRA)       */
   QLORA_TIMED_QGEMM_DX = 1,  /* dequant-fused GEMM, grad_x: dy W_hat (+ LoRA)         */
-  QLORA_TIMED_GEMV_FWD = 2,  /* few-token forward, weight pass (T <= 16, to 32 by shape) */
+  QLORA_TIMED_GEMV_FWD = 2,  /* few-token forward, weight pass (T <= 16, to 64 by shape) */
   QLORA_TIMED_GEMV_BWD = 3,  /* few-token backward, weight and adapter pass (T <= 2; sets T <= 4) */
   QLORA_TIMED_ADAMW = 4,     /* adapter AdamW update, whole 4096-element tiles          */
   QLORA_TIMED_KINDS = 5
