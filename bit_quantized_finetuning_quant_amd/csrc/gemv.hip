@@ -965,8 +965,13 @@ hipError_t gemv_bwd_set_impl(const uint16_t *const *dy, const uint16_t *x, const
 
 }  // namespace
 
-bool gemv_bwd_applies(int64_t T, int64_t K, int count) {
-  return T >= 1 && T <= (count == 1 ? kGemvLinearBwdMaxT : kGemvMaxT) && K % 64 == 0;
+// A single linear's backward runs here up to 2 tokens, and up to 4 when the weight is small: with
+// the row split of two and more tokens the few-token pass beats the fused GEMM's backward at 4096^2
+// (3 tokens 45.2 -> 39.2 us per fwd+bwd, 4 tokens 46.6 -> 42.9) but not at 22016 x 8192 (4 tokens
+// 124 -> 135 us).
+bool gemv_bwd_applies(int64_t T, int64_t N, int64_t K, int count) {
+  const int64_t max_t = count > 1 || N * K <= kGemvSmallWeight ? kGemvMaxT : kGemvLinearBwdMaxT;
+  return T >= 1 && T <= max_t && K % 64 == 0;
 }
 bool gemv_fwd_applies(int64_t T, int64_t N, int64_t K) {
   if (T < 1 || T > kGemvFwdMaxT || K % 64 != 0) return false;

@@ -47,7 +47,8 @@ hipError_t launch_dequantize_set(const DequantSet &set, const Codebook &cb, hipS
 
 // Few-token path (gemv.hip): the forward for 1 <= T <= kGemvFwdMaxT (its
 // matrix tiles pad the tokens to a multiple of 16), the backward of a single linear for
-// 1 <= T <= kGemvLinearBwdMaxT and of a projection set for 1 <= T <= kGemvMaxT
+// 1 <= T <= kGemvLinearBwdMaxT (to kGemvMaxT for weights of at most
+// kGemvSmallWeight elements) and of a projection set for 1 <= T <= kGemvMaxT
 // (its dot products cost per token; beyond these counts the fused GEMM's
 // backward is faster).  `part` is fp32 scratch of gemv_part_floats(T, N, K, r)
 // floats, or gemv_fwd_part_floats for a forward alone.  launch_gemv_fwd with
@@ -55,9 +56,10 @@ hipError_t launch_dequantize_set(const DequantSet &set, const Codebook &cb, hipS
 // the weight pass.
 constexpr int64_t kGemvMaxT = 4;
 constexpr int64_t kGemvLinearBwdMaxT = 2;
+constexpr int64_t kGemvSmallWeight = (int64_t)4096 * 4096;
 constexpr int64_t kGemvFwdMaxT = 64;
 bool gemv_fwd_applies(int64_t T, int64_t N, int64_t K);  // the forward over N rows (a set: all members' rows)
-bool gemv_bwd_applies(int64_t T, int64_t K, int count);  // the backward of `count` linears sharing x
+bool gemv_bwd_applies(int64_t T, int64_t N, int64_t K, int count);  // the backward of `count` linears sharing x, N rows in all
 size_t gemv_part_floats(int64_t T, int64_t N, int64_t K, int r);
 size_t gemv_fwd_part_floats(int64_t T, int64_t N, int64_t K, int r);
 // The adapter input xa (x, or the dropped-out x) feeds u = u_scale * xa A^T
@@ -233,6 +235,7 @@ struct SetPlan {
   int64_t N[kMaxSetMembers];
   size_t off_u, off_v, off_part, off_um, off_qpart, total;  // off_qpart: 0 when neither direction splits
   bool fwd_few;  // the forward on the few-token kernels (gemv_fwd_applies over all members' rows)
+  bool bwd_few;  // the backward on the few-token kernels (gemv_bwd_applies over all members' rows)
 };
 SetPlan plan_linear_set(int64_t T, int count, const int64_t *N, int64_t K, int r);
 hipError_t launch_linear_set_fwd(const SetPlan &p, const uint16_t *x, const QWeight *w, const uint16_t *A_set,

@@ -97,7 +97,7 @@ LinearPlan plan_linear(int64_t T, int64_t N, int64_t K, int r, bool dropout) {
   for (const auto &sh : shapes) part = std::max(part, lora_part_floats(sh[0], sh[1], sh[2]));
   // grad_A and grad_B are formed together
   part = std::max(part, lora_part_floats(r, K, T) + lora_part_floats(N, r, T));
-  if (gemv_bwd_applies(T, K, 1))
+  if (gemv_bwd_applies(T, N, K, 1))
     part = std::max(part, gemv_part_floats(T, N, K, r));
   else if (gemv_fwd_applies(T, N, K))  // the forward on the few-token kernels, the backward on the GEMMs
     part = std::max(part, gemv_fwd_part_floats(T, N, K, r));
@@ -113,7 +113,7 @@ LinearPlan plan_linear(int64_t T, int64_t N, int64_t K, int r, bool dropout) {
   // split contraction of the fused GEMMs (few tokens or a narrow output): fp32 partial tiles of the
   // forward (y) or of grad_x, whichever needs more
   p.off_qpart = off;
-  if (!gemv_bwd_applies(T, K, 1))
+  if (!gemv_bwd_applies(T, N, K, 1))
     off += align256(std::max(qgemm_split_floats(T, N, K), qgemm_split_floats(T, K, N)) * 4);
   // dropout: keep words [ceil(T/32)][K] and the dropped-out input [T x K] bf16
   p.off_keep = p.off_xd = 0;
@@ -175,7 +175,7 @@ hipError_t launch_linear_bwd(const LinearPlan &p, const uint16_t *dy, const uint
   // grad_A and the adapter term of grad_x carry s / (1 - p); grad_B = s dy^T u
   const float scale_ax = scale * ai.inv_keep;
   hipError_t e;
-  if (gemv_bwd_applies(p.T, p.K, 1)) {
+  if (gemv_bwd_applies(p.T, p.N, p.K, 1)) {
     if (!u) {  // recompute u = (1 / (1 - p)) xa A^T
       uint16_t *uw = (uint16_t *)(ws + p.off_u);
       e = launch_gemv_fwd(p.T, x, ai.xa, w, A, B, p.r, scale, ai.inv_keep, nullptr, uw, part, cb, st);
@@ -228,7 +228,8 @@ SetPlan plan_linear_set(int64_t T, int count, const int64_t *N, int64_t K, int r
   int64_t ntot = 0;
   for (int i = 0; i < count; ++i) ntot += N[i];
   p.fwd_few = gemv_fwd_applies(T, ntot, K);
-  const bool fwd_few = p.fwd_few, bwd_few = gemv_bwd_applies(T, K, count);
+  p.bwd_few = gemv_bwd_applies(T, ntot, K, count);
+  const bool fwd_few = p.fwd_few, bwd_few = p.bwd_few;
   size_t part = 0;
   if (fwd_few) {  // the few-token forward: the set pass's span partials or the largest member's
     part = gemv_set_fwd_part_floats(T, N, count, K, r);
@@ -341,7 +342,7 @@ hipError_t launch_linear_set_bwd(const SetPlan &p, const uint16_t *const *dy, co
                                  const uint16_t *A_set, const uint16_t *const *B, float scale, const uint16_t *u,
                                  uint16_t *grad_x, float *grad_A_set, float *const *grad_B, char *ws,
                                  const Codebook &cb, hipStream_t st) {
-  if (gemv_bwd_applies(p.T, p.K, p.count))
+  if (p.bwd_few)
     return set_bwd_few(p, dy, x, w, A_set, B, scale, u, grad_x, grad_A_set, grad_B, ws, cb, st);
   float *part = (float *)(ws + p.off_part);
   uint16_t *v = (uint16_t *)(ws + p.off_v);

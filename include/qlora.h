@@ -233,7 +233,8 @@ qlora_status qlora_linear_bwd(const uint16_t *dy, const uint16_t *x, int64_t T,
  * stays within 40 KB of LDS, which the shorter spans of smaller weights
  * allow) as one pass over the members' concatenated rows when every member
  * but the last has a multiple of 64 rows (else member by member), and the
- * backward for T <= 4 (T <= 2 for a set of one, as for a single linear) as
+ * backward for T <= 4 (for a set of one as for a single linear: T <= 2, or
+ * T <= 4 for weights of at most 4096 x 4096 elements) as
  * one pass over every member's rows (grad_x summed over the members in fp32,
  * rounded to bf16 once); same layouts.  No
  * dropout here: each adapter draws its own mask, so sets with dropout go per
@@ -334,7 +335,7 @@ enum {
   QLORA_TIMED_QGEMM_FWD = 0, /* dequant-fused GEMM, forward: x W_hat^T (+ LoRA)       */
   QLORA_TIMED_QGEMM_DX = 1,  /* dequant-fused GEMM, grad_x: dy W_hat (+ LoRA)         */
   QLORA_TIMED_GEMV_FWD = 2,  /* few-token forward, weight pass (T <= 16, to 64 by shape) */
-  QLORA_TIMED_GEMV_BWD = 3,  /* few-token backward, weight and adapter pass (T <= 2; sets T <= 4) */
+  QLORA_TIMED_GEMV_BWD = 3,  /* few-token backward, weight and adapter pass (T <= 2, or 4 by shape; sets T <= 4) */
   QLORA_TIMED_ADAMW = 4,     /* adapter AdamW update, whole 4096-element tiles          */
   QLORA_TIMED_KINDS = 5
 };

@@ -121,11 +121,11 @@ def test_adapter_products_at_long_token_counts(shape):
     _check_case(case, scale=0.5, need_u=False)
 
 
-@pytest.mark.parametrize("T", [1, 2, 4, 8, 16, 32, 64, 128, 256])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 8, 16, 32, 64, 128, 256])
 def test_7b_projection_every_token_count_of_the_sweep(T):
     """The 7B projection (4096 x 4096, r = 64) at every token count the benchmark sweeps: the
-    few-token kernels up to 2 tokens (the forward up to 16), then the fused GEMM with clamped rows
-    and split contractions."""
+    few-token kernels up to 4 tokens (a weight this small; the forward up to 64), then the fused
+    GEMM with clamped rows and split contractions."""
     announce(f"linear 7b_attn T={T} (sweep)")
     case = workloads.custom_case(4096, 4096, T, 64, 16.0, seed=900)  # one weight; x, dy drawn per T
     _check_case(case, weight_key=("sweep", 900))
