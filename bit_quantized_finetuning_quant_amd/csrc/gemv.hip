@@ -968,9 +968,14 @@ hipError_t gemv_bwd_set_impl(const uint16_t *const *dy, const uint16_t *x, const
 // A single linear's backward runs here up to 2 tokens, and up to 4 when the weight is small: with
 // the row split of two and more tokens the few-token pass beats the fused GEMM's backward at 4096^2
 // (3 tokens 45.2 -> 39.2 us per fwd+bwd, 4 tokens 46.6 -> 42.9) but not at 22016 x 8192 (4 tokens
-// 124 -> 135 us).
+// 124 -> 135 us).  A projection set's one pass over all its members' rows runs up to 4 tokens, and
+// up to 3 once the members hold more than 128 M weights in all (q/k/v of 3 x 8192^2, backward alone
+// at 4 tokens: 119.6 us here against 108.6 on the fused GEMM; gate/up of 2 x 11008 x 4096 even).
+constexpr int64_t kGemvLargeSet = (int64_t)128 << 20;
+
 bool gemv_bwd_applies(int64_t T, int64_t N, int64_t K, int count) {
-  const int64_t max_t = count > 1 || N * K <= kGemvSmallWeight ? kGemvMaxT : kGemvLinearBwdMaxT;
+  int64_t max_t = count > 1 || N * K <= kGemvSmallWeight ? kGemvMaxT : kGemvLinearBwdMaxT;
+  if (count > 1 && N * K > kGemvLargeSet) max_t = 3;
   return T >= 1 && T <= max_t && K % 64 == 0;
 }
 bool gemv_fwd_applies(int64_t T, int64_t N, int64_t K) {

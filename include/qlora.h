@@ -233,8 +233,9 @@ qlora_status qlora_linear_bwd(const uint16_t *dy, const uint16_t *x, int64_t T,
  * stays within 40 KB of LDS, which the shorter spans of smaller weights
  * allow) as one pass over the members' concatenated rows when every member
  * but the last has a multiple of 64 rows (else member by member), and the
- * backward for T <= 4 (for a set of one as for a single linear: T <= 2, or
- * T <= 4 for weights of at most 4096 x 4096 elements) as
+ * backward for T <= 4 (T <= 3 for sets above 128 M weights in all; for a set
+ * of one as for a single linear: T <= 2, or T <= 4 for weights of at most
+ * 4096 x 4096 elements) as
  * one pass over every member's rows (grad_x summed over the members in fp32,
  * rounded to bf16 once); same layouts.  No
  * dropout here: each adapter draws its own mask, so sets with dropout go per

@@ -178,6 +178,14 @@ def test_few_token_set_member_by_member(n_outs, n_in, T, r):
     _check(_members(n_outs, n_in, T, r, seed=41 + T))
 
 
+@pytest.mark.parametrize("T", [3, 4])
+def test_large_set_at_three_and_four_tokens(T):
+    """Two 8192 x 8192 members (134 M weights in all): the backward on the few-token pass at 3
+    tokens and on the fused GEMM at 4 (sets above 128 M weights), against the oracle."""
+    announce(f"set (8192, 8192) x 8192 T={T} r=16")
+    _check(_members((8192, 8192), 8192, T, 16, seed=90 + T))
+
+
 def test_7b_attention_projections_T2048():
     """q, k, v of LLaMA-7B (3 x 4096 x 4096, r = 64, 2048 tokens) as one set, in full."""
     announce("set 7b q/k/v T=2048 full")
